@@ -1,0 +1,367 @@
+/*
+ * rownorm_oracle.c -- plain, slow, obviously correct fp64 CPU reference for row-wise
+ * LayerNorm, RMSNorm and fused residual-add + RMSNorm.
+ *
+ * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg may load this library. The GPU product path never calls it, links it or shares
+ * code with it: no headers, helpers, tables or constants are common to the two.
+ *
+ * Every quantity is computed in IEEE double precision, sequentially, row by row, in the
+ * order the definitions state. Inputs arrive as raw I/O-dtype bit patterns (fp32, fp16
+ * or bf16) and are decoded exactly; outputs are fp64 (y, mean, rstd) plus, for the fused
+ * op, the residual stream rounded once to the I/O dtype.
+ *
+ * Sources (pages' titles and sections; see the function comments for which step follows
+ * which passage):
+ *   [WALK]  "LayerNorm CUDA walkthrough" (lpnh.cn/news/2756757): section 1 (definition of
+ *           mean, biased variance, y), section 6 (two-pass or Welford for stability),
+ *           section 2 / 7 (gamma and beta optional).
+ *   [OPS]   "05 LLM Ops" lesson (smarter.xin/posts/cb29461c): section 2 LayerNorm and the
+ *           "Welford recurrence" paragraph (delta, mean and M2 updates, var = M2/n);
+ *           section 3 RMSNorm formula.
+ *   [FUSED] "CUDA fused RMSNorm kernel" (diycv.top/archives/cuda-fused-rmsnorm-kernel):
+ *           section 0.3 (RMSNorm = x / sqrt(mean(x^2) + eps), residual_out = x + residual),
+ *           section 3.2 (fp32 accumulation; the sum x + residual is first rounded to the
+ *           I/O dtype and the rounded value is the one squared and returned).
+ *   [LLM]   "LayerNorm vs RMSNorm in LLM inference engines" (lpnh.cn/news/2853107),
+ *           section 2.1 (y = gamma * (x - mean) / sqrt(var + eps) + beta;
+ *           y = gamma * x / sqrt(mean(x^2) + eps)).
+ *
+ * Readings where the pages are silent (each is also listed in the design notes):
+ *   - variance is the biased 1/N form; eps is added inside the square root;
+ *   - rstd = 1 / sqrt(var + eps) for LayerNorm and 1 / sqrt(mean(x^2) + eps) for RMSNorm;
+ *   - a null gamma / weight means 1, a null beta means 0;
+ *   - rounding to fp16 / bf16 / fp32 is IEEE round-to-nearest, ties to even, with
+ *     overflow to infinity (the pages do not name a rounding mode).
+ *
+ * Pins: tests/test_oracle.py checks this file against exact rational arithmetic on tiny
+ * rows, torch's CPU float64 layer_norm / rms_norm, closed forms for N = 1 and N = 2, the
+ * invariants of the definitions, and (for the codec) every fp16 / bf16 bit pattern.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* I/O dtype codes of this library (defined here, independently of the product). */
+enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
+
+/* Error codes. */
+enum { ORC_OK = 0, ORC_EARG = 1, ORC_EWELFORD = 2, ORC_ENOMEM = 3 };
+
+/* ---------------------------------------------------------------------------------- */
+/* IEEE binary formats, from their definition: 1 sign bit, `e` exponent bits with bias */
+/* 2^(e-1) - 1, `m` stored fraction bits; all-ones exponent encodes inf / NaN; zero    */
+/* exponent encodes zero and subnormals with quantum 2^(1 - bias - m).                 */
+/* ---------------------------------------------------------------------------------- */
+
+static int fmt_bits(int dtype, int* m, int* e) {
+    switch (dtype) {
+    case ORC_F32: *m = 23; *e = 8; return 0;
+    case ORC_F16: *m = 10; *e = 5; return 0;
+    case ORC_BF16: *m = 7; *e = 8; return 0;
+    default: return -1;
+    }
+}
+
+static int dtype_size(int dtype) { return dtype == ORC_F32 ? 4 : 2; }
+
+/* Exact value of a bit pattern. */
+double orc_decode(int dtype, uint32_t bits) {
+    int m, e;
+    if (fmt_bits(dtype, &m, &e)) return NAN;
+    const uint32_t emask = (1u << e) - 1u;
+    const int bias = (1 << (e - 1)) - 1;
+    const uint32_t sign = (bits >> (m + e)) & 1u;
+    const uint32_t E = (bits >> m) & emask;
+    const uint32_t M = bits & ((1u << m) - 1u);
+    double v;
+    if (E == emask) {
+        v = (M == 0) ? INFINITY : NAN;
+    } else if (E == 0) {
+        v = ldexp((double)M, 1 - bias - m);
+    } else {
+        v = ldexp((double)M + ldexp(1.0, m), (int)E - bias - m);
+    }
+    return sign ? -v : v;
+}
+
+/* Round a double to the nearest representable value of the format, ties to even,
+ * overflowing to infinity; return its bit pattern. One rounding step: the exact binary
+ * value of `v` is scaled by a power of two so that the format's quantum at |v| becomes 1,
+ * split into integer and fraction (both exact), and the integer part is bumped when the
+ * fraction is above one half, or exactly one half with an odd integer part. */
+uint32_t orc_encode(int dtype, double v) {
+    int m, e;
+    if (fmt_bits(dtype, &m, &e)) return 0;
+    const uint32_t emask = (1u << e) - 1u;
+    const int bias = (1 << (e - 1)) - 1;
+    const int emin = 1 - bias; /* exponent of the smallest normal */
+    const uint32_t sign = signbit(v) ? (1u << (m + e)) : 0u;
+    if (isnan(v)) return sign | (emask << m) | (1u << (m - 1)); /* quiet NaN */
+    double a = fabs(v);
+    if (isinf(a)) return sign | (emask << m);
+    if (a == 0.0) return sign;
+
+    int ex;
+    (void)frexp(a, &ex); /* a in [2^(ex-1), 2^ex) */
+    int k = ex - 1;      /* binade exponent: a in [2^k, 2^(k+1)) */
+    if (k < emin) k = emin; /* subnormal range: the quantum stays 2^(emin - m) */
+    const double n = ldexp(a, m - k); /* a / quantum, exact */
+    double r = floor(n);
+    const double frac = n - r; /* exact */
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+
+    const double one = ldexp(1.0, m); /* implicit leading bit */
+    if (k == emin && r < one) {
+        return sign | (uint32_t)r; /* subnormal (or zero) */
+    }
+    if (r == 2.0 * one) { /* rounded up into the next binade */
+        r = one;
+        k += 1;
+    }
+    const int E = k + bias;
+    if (E >= (int)emask) return sign | (emask << m); /* overflow */
+    return sign | ((uint32_t)E << m) | (uint32_t)(r - one);
+}
+
+static double load_elem(int dtype, const void* p, int64_t i) {
+    if (dtype == ORC_F32) {
+        uint32_t b;
+        memcpy(&b, (const char*)p + 4 * i, 4);
+        return orc_decode(dtype, b);
+    }
+    uint16_t h;
+    memcpy(&h, (const char*)p + 2 * i, 2);
+    return orc_decode(dtype, h);
+}
+
+static void store_elem(int dtype, void* p, int64_t i, uint32_t bits) {
+    if (dtype == ORC_F32) {
+        memcpy((char*)p + 4 * i, &bits, 4);
+    } else {
+        uint16_t h = (uint16_t)bits;
+        memcpy((char*)p + 2 * i, &h, 2);
+    }
+}
+
+void orc_decode_array(int dtype, const void* src, double* dst, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) dst[i] = load_elem(dtype, src, i);
+}
+
+void orc_encode_array(int dtype, const double* src, void* dst, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) store_elem(dtype, dst, i, orc_encode(dtype, src[i]));
+}
+
+/* ---------------------------------------------------------------------------------- */
+/* Row statistics.                                                                     */
+/* ---------------------------------------------------------------------------------- */
+
+/* Two-pass moments ([WALK] section 1 and 6; [OPS] section 2 "naive" variant): the mean is
+ * the plain sum over N, then the biased variance is the mean of squared deviations from
+ * it. */
+double orc_twopass_var(const double* x, int64_t n, double* mean_out) {
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i) s += x[i];
+    const double mean = s / (double)n;
+    double ss = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        const double d = x[i] - mean;
+        ss += d * d;
+    }
+    if (mean_out) *mean_out = mean;
+    return ss / (double)n;
+}
+
+/* Welford's online recurrence ([OPS] "Welford recurrence"): with delta = x_k - mean_{k-1},
+ * mean_k = mean_{k-1} + delta / k and M2_k = M2_{k-1} + delta * (x_k - mean_k); the
+ * variance is M2_n / n. */
+double orc_welford_var(const double* x, int64_t n, double* mean_out) {
+    double mean = 0.0, m2 = 0.0;
+    for (int64_t k = 1; k <= n; ++k) {
+        const double xk = x[k - 1];
+        const double delta = xk - mean;
+        mean += delta / (double)k;
+        m2 += delta * (xk - mean);
+    }
+    if (mean_out) *mean_out = mean;
+    return m2 / (double)n;
+}
+
+/* The two variance routes must agree; a disagreement means a bug (or an input outside
+ * what fp64 can resolve) and the oracle refuses to answer. The bound is far above fp64
+ * rounding (about N * 2^-53 relative) and far below any error a GPU kernel may make. */
+static int variances_agree(double var_tp, double var_w, double mean) {
+    if (var_tp == var_w) return 1;
+    const double tol = 1e-9 * fabs(var_tp) + 1e-20 * mean * mean;
+    return fabs(var_tp - var_w) <= tol;
+}
+
+/* ---------------------------------------------------------------------------------- */
+/* Per-row operations.                                                                 */
+/* ---------------------------------------------------------------------------------- */
+
+typedef struct {
+    int op; /* 0 = LayerNorm, 1 = RMSNorm, 2 = fused add + RMSNorm */
+    int dtype;
+    const void* x;
+    const void* residual;
+    const void* gamma; /* gamma or weight; nullable */
+    const void* beta;  /* nullable */
+    int64_t rows, N;
+    double eps;
+    double* y;            /* [rows, N] fp64, nullable */
+    double* mean;         /* [rows], nullable (LayerNorm) */
+    double* rstd;         /* [rows], nullable */
+    void* residual_out;   /* [rows, N] I/O dtype, nullable (fused) */
+    int64_t r0, r1;
+    int status;
+} job_t;
+
+/* LayerNorm of one row ([WALK] section 1; [LLM] section 2.1):
+ * mean = (1/N) sum x_j; var = (1/N) sum (x_j - mean)^2; rstd = 1/sqrt(var + eps);
+ * y_j = (x_j - mean) * rstd * gamma_j + beta_j. */
+static int ln_row(const job_t* jb, const double* xr, const double* g, const double* b, int64_t r) {
+    const int64_t N = jb->N;
+    double mean_tp, mean_w;
+    const double var = orc_twopass_var(xr, N, &mean_tp);
+    const double var_w = orc_welford_var(xr, N, &mean_w);
+    if (!variances_agree(var, var_w, mean_tp)) return ORC_EWELFORD;
+    const double rstd = 1.0 / sqrt(var + jb->eps);
+    if (jb->mean) jb->mean[r] = mean_tp;
+    if (jb->rstd) jb->rstd[r] = rstd;
+    if (jb->y) {
+        double* yr = jb->y + r * N;
+        for (int64_t j = 0; j < N; ++j) {
+            const double gj = g ? g[j] : 1.0;
+            const double bj = b ? b[j] : 0.0;
+            yr[j] = (xr[j] - mean_tp) * rstd * gj + bj;
+        }
+    }
+    return ORC_OK;
+}
+
+/* RMSNorm of one row ([FUSED] section 0.3; [OPS] section 3; [LLM] section 2.1):
+ * ms = (1/N) sum x_j^2; rstd = 1/sqrt(ms + eps); y_j = x_j * rstd * w_j. */
+static void rms_row(const job_t* jb, const double* xr, const double* w, int64_t r) {
+    const int64_t N = jb->N;
+    double ss = 0.0;
+    for (int64_t j = 0; j < N; ++j) ss += xr[j] * xr[j];
+    const double rstd = 1.0 / sqrt(ss / (double)N + jb->eps);
+    if (jb->rstd) jb->rstd[r] = rstd;
+    if (jb->y) {
+        double* yr = jb->y + r * N;
+        for (int64_t j = 0; j < N; ++j) yr[j] = xr[j] * rstd * (w ? w[j] : 1.0);
+    }
+}
+
+static void* run_rows(void* arg) {
+    job_t* jb = (job_t*)arg;
+    const int64_t N = jb->N;
+    double* xr = (double*)malloc(sizeof(double) * (size_t)N);
+    double* rr = jb->op == 2 ? (double*)malloc(sizeof(double) * (size_t)N) : NULL;
+    double* g = jb->gamma ? (double*)malloc(sizeof(double) * (size_t)N) : NULL;
+    double* b = jb->beta ? (double*)malloc(sizeof(double) * (size_t)N) : NULL;
+    if (!xr || (jb->op == 2 && !rr) || (jb->gamma && !g) || (jb->beta && !b)) {
+        jb->status = ORC_ENOMEM;
+        goto done;
+    }
+    if (g) orc_decode_array(jb->dtype, jb->gamma, g, N);
+    if (b) orc_decode_array(jb->dtype, jb->beta, b, N);
+    for (int64_t r = jb->r0; r < jb->r1; ++r) {
+        orc_decode_array(jb->dtype, (const char*)jb->x + r * N * dtype_size(jb->dtype), xr, N);
+        if (jb->op == 0) {
+            int st = ln_row(jb, xr, g, b, r);
+            if (st != ORC_OK) {
+                jb->status = st;
+                goto done;
+            }
+        } else if (jb->op == 1) {
+            rms_row(jb, xr, g, r);
+        } else {
+            /* Fused ([FUSED] sections 0.3 and 3.2): residual_out = x + residual, the exact
+             * sum rounded once to the I/O dtype; the RMSNorm uses that rounded value. */
+            orc_decode_array(jb->dtype, (const char*)jb->residual + r * N * dtype_size(jb->dtype), rr, N);
+            for (int64_t j = 0; j < N; ++j) {
+                const uint32_t t = orc_encode(jb->dtype, xr[j] + rr[j]);
+                if (jb->residual_out) store_elem(jb->dtype, jb->residual_out, r * N + j, t);
+                xr[j] = orc_decode(jb->dtype, t);
+            }
+            rms_row(jb, xr, g, r);
+        }
+    }
+done:
+    free(xr);
+    free(rr);
+    free(g);
+    free(b);
+    return NULL;
+}
+
+/* Split rows into contiguous ranges, one per thread (nthreads <= 1: the calling thread). */
+static int run_job(const job_t* proto, int nthreads) {
+    if (proto->rows < 0 || proto->N <= 0 || !proto->x || !(proto->eps >= 0.0)) return ORC_EARG;
+    if (fmt_bits(proto->dtype, &(int){0}, &(int){0})) return ORC_EARG;
+    if (proto->op == 2 && !proto->residual) return ORC_EARG;
+    if (proto->rows == 0) return ORC_OK;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > proto->rows) nthreads = (int)proto->rows;
+    job_t* jobs = (job_t*)calloc((size_t)nthreads, sizeof(job_t));
+    pthread_t* th = (pthread_t*)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !th) {
+        free(jobs);
+        free(th);
+        return ORC_ENOMEM;
+    }
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = *proto;
+        jobs[t].r0 = proto->rows * t / nthreads;
+        jobs[t].r1 = proto->rows * (t + 1) / nthreads;
+        jobs[t].status = ORC_OK;
+    }
+    int started = 0;
+    for (int t = 1; t < nthreads; ++t) {
+        if (pthread_create(&th[t], NULL, run_rows, &jobs[t]) != 0) break;
+        started = t;
+    }
+    run_rows(&jobs[0]);
+    /* Rows of threads that failed to start are done here, serially. */
+    for (int t = started + 1; t < nthreads; ++t) run_rows(&jobs[t]);
+    for (int t = 1; t <= started; ++t) pthread_join(th[t], NULL);
+    int st = ORC_OK;
+    for (int t = 0; t < nthreads; ++t)
+        if (jobs[t].status != ORC_OK) st = jobs[t].status;
+    free(jobs);
+    free(th);
+    return st;
+}
+
+/* LayerNorm forward over x[rows, N]. y [rows, N], mean and rstd [rows] are fp64 and each
+ * nullable; gamma / beta are I/O-dtype [N] and nullable. Returns an ORC_* code. */
+int orc_layer_norm(int dtype, const void* x, const void* gamma, const void* beta, int64_t rows,
+                   int64_t N, double eps, double* y, double* mean, double* rstd, int nthreads) {
+    job_t jb = {0};
+    jb.op = 0; jb.dtype = dtype; jb.x = x; jb.gamma = gamma; jb.beta = beta;
+    jb.rows = rows; jb.N = N; jb.eps = eps; jb.y = y; jb.mean = mean; jb.rstd = rstd;
+    return run_job(&jb, nthreads);
+}
+
+/* RMSNorm forward over x[rows, N]; weight I/O-dtype [N], nullable. */
+int orc_rms_norm(int dtype, const void* x, const void* weight, int64_t rows, int64_t N, double eps,
+                 double* y, double* rstd, int nthreads) {
+    job_t jb = {0};
+    jb.op = 1; jb.dtype = dtype; jb.x = x; jb.gamma = weight;
+    jb.rows = rows; jb.N = N; jb.eps = eps; jb.y = y; jb.rstd = rstd;
+    return run_job(&jb, nthreads);
+}
+
+/* Fused residual add + RMSNorm; residual_out is I/O-dtype [rows, N], nullable. */
+int orc_fused_add_rms_norm(int dtype, const void* x, const void* residual, const void* weight,
+                           int64_t rows, int64_t N, double eps, double* y, void* residual_out,
+                           double* rstd, int nthreads) {
+    job_t jb = {0};
+    jb.op = 2; jb.dtype = dtype; jb.x = x; jb.residual = residual; jb.gamma = weight;
+    jb.rows = rows; jb.N = N; jb.eps = eps; jb.y = y; jb.residual_out = residual_out; jb.rstd = rstd;
+    return run_job(&jb, nthreads);
+}
