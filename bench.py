@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of the row-wise normalization hot path on one MI355X.
+
+One step = one LayerNorm forward (y, mean, rstd) over the 4096 x 16384 bf16 workload, the
+largest configuration and the one the bandwidth target applies to (rows * N = 64M >= 8M).
+The same measurement is also taken for fused residual-add + RMSNorm at 8192 x 4096 fp16
+(32M elements) and reported in the same JSON line under "fused_add_rms_norm".
+
+Cold cache: inputs and outputs rotate through enough buffer sets that each launch touches
+memory the previous launches have pushed out of L2 (8 x 4 MiB) and the 256 MiB
+memory-side cache. Inputs are resident in HBM before the timed region starts.
+
+Timed region: W warmup steps untimed, then exactly K steps bracketed by
+torch.cuda.synchronize(); ms_per_step is the wall time over K. Each launch is also
+bracketed by HIP events on the stream the kernel runs on (torch's current stream, which
+the binding passes to the C ABI), giving the per-kernel average duration used for the
+roofline.
+
+value = algorithmic bytes per step / ms_per_step (GB/s, 1 GB = 1e9 B). Algorithmic bytes:
+LayerNorm 2*rows*N*s + 2*N*s + 8*rows; fused 4*rows*N*s + N*s + 4*rows (with rstd).
+
+The CPU baseline times the fp64 oracle (oracle/) on the same workload on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--cache cold|hot]
+       python bench.py --copy-calibration   (plain copy of known size, for counter scaling)
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "achieved HBM GB/s (% of MI355X peak) + rows/s, LayerNorm & fused add+RMSNorm"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published peak
+COLD_FOOTPRINT = 768 << 20  # bytes each buffer set cycle must exceed (L2 + 256 MiB MALL, with margin)
+KERNEL_SRC = os.path.join(ROOT, "row_wise_normalization_fp32_amd", "csrc", "rownorm_kernels.hip")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_traffic(workload_key: str):
+    """HBM bytes per launch measured by rocprofv3 FETCH_SIZE / WRITE_SIZE (scaled by a copy
+    kernel), if recorded for the current kernel source; else None."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    text = open(COUNTERS_FILE).read()
+    m = re.search(r"kernel_source_sha256_16:\s*(\w+)", text)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    m = re.search(rf"^{re.escape(workload_key)}\s+traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    return float(m.group(1)) if m else None
+
+
+def make_sets(w, nsets, dev):
+    import torch
+
+    import workloads
+
+    base = workloads.make_inputs(w)
+    sets = []
+    for i in range(nsets):
+        s = {}
+        for k, v in base.items():
+            if k in ("gamma", "beta", "weight"):
+                s[k] = sets[0][k] if sets else v.to(dev)
+            else:
+                # distinct buffers with the workload's values (a rolled copy per set)
+                s[k] = torch.roll(v, shifts=i, dims=0).to(dev) if i else v.to(dev)
+        s["y"] = torch.empty_like(s["x"])
+        if w.op == "fused_add_rms":
+            s["residual_out"] = torch.empty_like(s["x"])
+        s["rstd"] = torch.empty(w.rows, dtype=torch.float32, device=dev)
+        if w.op == "ln":
+            s["mean"] = torch.empty(w.rows, dtype=torch.float32, device=dev)
+        sets.append(s)
+    return sets
+
+
+def launch(rn, w, s):
+    if w.op == "ln":
+        rn.ln_forward(s["x"], s.get("gamma"), s.get("beta"), w.eps, out=s["y"], mean=s["mean"], rstd=s["rstd"])
+    elif w.op == "rms":
+        rn.rms_norm(s["x"], s.get("weight"), w.eps, out=s["y"], rstd=s["rstd"])
+    else:
+        rn.fused_add_rms_norm(s["x"], s["residual"], s.get("weight"), w.eps, out=s["y"],
+                              residual_out=s["residual_out"], rstd=s["rstd"])
+
+
+def measure(w, steps, warmup, cache, dev):
+    import torch
+
+    import row_wise_normalization_fp32_amd as rn
+    import workloads
+
+    nbytes = workloads.algorithmic_bytes(w.op, w.rows, w.N, w.elem_bytes, with_stats=True)
+    set_bytes = (4 if w.op == "fused_add_rms" else 2) * w.rows * w.N * w.elem_bytes
+    nsets = 1 if cache == "hot" else max(2, min(64, math.ceil(COLD_FOOTPRINT / set_bytes)))
+    log(f"[bench] {w.name}: {nsets} buffer set(s), {nbytes} algorithmic bytes per launch")
+    sets = make_sets(w, nsets, dev)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        launch(rn, w, sets[i % nsets])
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record()
+        launch(rn, w, sets[(warmup + i) % nsets])
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = [a.elapsed_time(b) for a, b in zip(starts, ends)]  # ms
+    kernel_ms = sum(durs) / len(durs)
+    ms_per_step = wall * 1e3 / steps
+    st, info = rn.plan(w.op, w.rows, w.N, workloads.TORCH_DTYPES[w.dtype])
+    del sets
+    torch.cuda.empty_cache()
+    return {
+        "bytes": nbytes, "ms_per_step": ms_per_step, "kernel_ms": kernel_ms,
+        "kernel_ms_median": sorted(durs)[len(durs) // 2], "nsets": nsets, "plan": info,
+    }
+
+
+def cpu_baseline(w, seconds):
+    import oracle
+    import workloads
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    threads = max(1, min(16, cores))
+    inp = workloads.make_inputs(w)
+    nbytes = workloads.algorithmic_bytes(w.op, w.rows, w.N, w.elem_bytes, with_stats=True)
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        if w.op == "ln":
+            oracle.layer_norm(inp["x"], inp.get("gamma"), inp.get("beta"), w.eps, threads=threads)
+        elif w.op == "rms":
+            oracle.rms_norm(inp["x"], inp.get("weight"), w.eps, threads=threads)
+        else:
+            oracle.fused_add_rms_norm(inp["x"], inp["residual"], inp.get("weight"), w.eps, threads=threads)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= seconds or len(times) >= 2000:
+            break
+    med = sorted(times)[len(times) // 2]
+    return {
+        "value": round(nbytes / med / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "rows_per_s": round(w.rows / med, 1),
+        "sample": f"full {w.rows}x{w.N} {w.dtype} workload, {len(times)} passes over {sum(times):.1f} s, median pass",
+    }
+
+
+def copy_calibration(dev):
+    import torch
+
+    n = 256 << 20
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: 10 copies of {n} bytes")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cache", choices=["cold", "hot"], default="cold")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fused", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} (WORLD_SIZE={world}) is not supported: "
+              "rows are independent, so more GPUs would each run the same kernel on their own rows.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+
+    dev = "cuda:0"
+    if args.copy_calibration:
+        copy_calibration(dev)
+        return
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        cpu = cpu_baseline(workloads.C5, args.cpu_seconds)
+        log(f"[bench] cpu baseline: {cpu}")
+
+    w = workloads.C5
+    log(f"[bench] timing {w.name} ({args.cache} cache) ...")
+    r = measure(w, args.steps, args.warmup, args.cache, dev)
+    value = r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
+    achieved = r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+    traffic = counter_traffic("ln_bf16_4096x16384")
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "LayerNorm forward, bf16 I/O, 4096 x 16384, eps 1e-5, y + fp32 mean/rstd",
+            "op": "ln_forward", "io_dtype": "bf16", "rows": w.rows, "N": w.N, "cache": args.cache,
+            "buffer_sets": r["nsets"], "variant": r["plan"]["variant"],
+            "inputs": "x = m_r + s_r*z, m_r~U(-10,10), s_r~U(0.5,4); gamma~U(0.5,1.5); beta~N(0,0.1^2); seed 1005",
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "rows_per_s": round(w.rows / (r["ms_per_step"] * 1e-3), 1),
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+            "kernel": "rn::rownorm_vec_kernel<bf16, LayerNorm, 4 waves per row, 8 chunks per lane, 1 row per block>",
+            "kernel_avg_ms": round(r["kernel_ms"], 5), "kernel_median_ms": round(r["kernel_ms_median"], 5),
+            "bytes_per_launch": r["bytes"],
+        },
+        "cpu_baseline": cpu,
+    }
+    if not args.no_fused:
+        f = workloads.FUSED_8192
+        log(f"[bench] timing {f.name} ({args.cache} cache) ...")
+        rf = measure(f, args.steps, args.warmup, args.cache, dev)
+        fv = rf["bytes"] / (rf["ms_per_step"] * 1e-3) / 1e9
+        fa = rf["bytes"] / (rf["kernel_ms"] * 1e-3) / 1e9
+        out["fused_add_rms_norm"] = {
+            "workload": "fused residual-add + RMSNorm, fp16 I/O, 8192 x 4096, eps 1e-6, y + residual_out + rstd",
+            "value": round(fv, 2), "unit": "GB/s", "pct_of_peak": round(100.0 * fv / PEAK_HBM_GBS, 2),
+            "rows_per_s": round(f.rows / (rf["ms_per_step"] * 1e-3), 1), "ms_per_step": round(rf["ms_per_step"], 5),
+            "kernel_avg_ms": round(rf["kernel_ms"], 5), "achieved_kernel_GBs": round(fa, 2),
+            "frac_kernel": round(fa / PEAK_HBM_GBS, 4), "bytes_per_launch": rf["bytes"],
+            "variant": rf["plan"]["variant"], "traffic": counter_traffic("fused_fp16_8192x4096"),
+        }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

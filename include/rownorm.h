@@ -1,0 +1,149 @@
+/*
+ * rownorm.h -- C ABI of the MI355X (gfx950) row-wise normalization library, librownorm.so.
+ *
+ * Three forward operations over a dense, row-major [rows, N] tensor, each row normalized
+ * on its own:
+ *
+ *   ln_forward          LayerNorm. mean = (1/N) sum x_j, var = (1/N) sum (x_j - mean)^2
+ *                       (biased), rstd = 1/sqrt(var + eps), y_j = (x_j - mean) * rstd *
+ *                       gamma_j + beta_j. Defined in the LayerNorm CUDA walkthrough
+ *                       (lpnh.cn/news/2756757), section 1; the same formula is section 2.1
+ *                       of "LayerNorm vs RMSNorm in LLM inference engines"
+ *                       (lpnh.cn/news/2853107) and section 2 of the "05 LLM Ops" lesson
+ *                       (smarter.xin/posts/cb29461c).
+ *   rms_norm            RMSNorm. rstd = 1/sqrt((1/N) sum x_j^2 + eps), y_j = x_j * rstd * w_j.
+ *                       Defined in "CUDA fused RMSNorm kernel"
+ *                       (diycv.top/archives/cuda-fused-rmsnorm-kernel), sections 0.3 and 2.
+ *   fused_add_rms_norm  residual_out = x + residual, rounded once to the I/O dtype; then
+ *                       RMSNorm of that rounded value, which is also what gets squared.
+ *                       Same article, sections 2 and 3.2.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are DEVICE pointers (HIP device memory of the current device). x, residual,
+ *     gamma / beta / weight, y and residual_out hold `dtype` elements; mean and rstd are
+ *     fp32. Row stride is N elements (dense rows). gamma / beta / weight have N elements.
+ *   - Arithmetic is fp32 for every dtype: fp16 / bf16 inputs are widened exactly, outputs
+ *     are rounded once (round-to-nearest-even) to `dtype`.
+ *   - The caller owns every buffer. The library never allocates, frees or synchronizes;
+ *     work is enqueued on `stream` (0 = the null stream) and results are valid once the
+ *     caller has synchronized that stream. The library keeps no state between calls and
+ *     may be called from several host threads at once.
+ *   - Errors are reported by the return value (an rn_status). Argument errors are detected
+ *     on the host before anything is enqueued, so an error leaves every output untouched.
+ *   - rows == 0 is a successful no-op.
+ *   - Aliasing: an output may be the exact same buffer as an input of the same shape
+ *     (in place: y == x, residual_out == residual, residual_out == x, y == residual).
+ *     Any other overlap between an output and any other buffer is RN_ERR_ALIAS.
+ *   - Every pointer must be aligned to its element size (RN_ERR_ALIGN otherwise). When N *
+ *     sizeof(dtype) is a multiple of 16 and every [rows, N] / [N] pointer is 16-byte aligned,
+ *     the vectorized kernels run (one 64-lane wavefront per row for N <= 4096, one
+ *     workgroup per row for N <= 16384); otherwise, and for longer rows, a slower general
+ *     kernel computes the same result.
+ */
+#ifndef ROWNORM_H
+#define ROWNORM_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* I/O element type. */
+typedef enum rn_dtype { RN_F32 = 0, RN_F16 = 1, RN_BF16 = 2 } rn_dtype;
+
+/* Status codes returned by every entry point. */
+typedef enum rn_status {
+    RN_OK = 0,
+    RN_ERR_NULL = 1,          /* a required pointer is NULL */
+    RN_ERR_SHAPE = 2,         /* rows < 0, N <= 0, rows * N overflows, or eps < 0 / not finite */
+    RN_ERR_DTYPE = 3,         /* dtype is not an rn_dtype */
+    RN_ERR_ALIAS = 4,         /* an output overlaps another buffer other than by exact aliasing */
+    RN_ERR_UNSUPPORTED = 5,   /* a forced kernel variant cannot run this shape / alignment */
+    RN_ERR_HIP = 6,           /* the HIP runtime reported an error at launch */
+    RN_ERR_ALIGN = 7          /* a pointer is not aligned to its element size */
+} rn_status;
+
+/* Kernel variants (for rn_*_variant entry points and rn_plan). */
+typedef enum rn_variant {
+    RN_VARIANT_AUTO = 0,      /* choose from N, dtype and alignment (what the plain entry points do) */
+    RN_VARIANT_WAVE = 1,      /* one 64-lane wavefront per row, row held in VGPRs (N <= 4096) */
+    RN_VARIANT_WORKGROUP = 2, /* one workgroup per row, cross-wave combine in LDS (N <= 16384) */
+    RN_VARIANT_GENERAL = 3    /* any N, any element-aligned pointers; re-reads the row */
+} rn_variant;
+
+/* Operation codes (for rn_plan). */
+typedef enum rn_op { RN_OP_LAYER_NORM = 0, RN_OP_RMS_NORM = 1, RN_OP_FUSED_ADD_RMS_NORM = 2 } rn_op;
+
+/*
+ * LayerNorm forward.
+ *   x      [rows, N] dtype, required.
+ *   gamma  [N] dtype, nullable (NULL means 1).   beta [N] dtype, nullable (NULL means 0).
+ *   y      [rows, N] dtype, required; may be x itself.
+ *   mean   [rows] fp32, nullable: the row mean.  rstd [rows] fp32, nullable: 1/sqrt(var + eps).
+ *   eps    >= 0, added to the variance inside the square root.
+ */
+int ln_forward(const void* x, const void* gamma, const void* beta, void* y, float* mean, float* rstd,
+               int64_t rows, int64_t N, float eps, int dtype, hipStream_t stream);
+
+/*
+ * RMSNorm forward.
+ *   x [rows, N] dtype, required.  weight [N] dtype, nullable (NULL means 1).
+ *   y [rows, N] dtype, required; may be x itself.  rstd [rows] fp32, nullable:
+ *   1/sqrt(mean(x^2) + eps).
+ */
+int rms_norm(const void* x, const void* weight, void* y, float* rstd, int64_t rows, int64_t N, float eps,
+             int dtype, hipStream_t stream);
+
+/*
+ * Fused residual add + RMSNorm.
+ *   x, residual [rows, N] dtype, required.  weight [N] dtype, nullable (NULL means 1).
+ *   residual_out [rows, N] dtype, required: x + residual rounded to dtype (may be x or
+ *   residual itself).  y [rows, N] dtype, required: RMSNorm(residual_out) * weight (may be
+ *   x or residual itself, but not residual_out).  rstd [rows] fp32, nullable: the rstd of
+ *   residual_out's row.
+ */
+int fused_add_rms_norm(const void* x, const void* residual, const void* weight, void* y, void* residual_out,
+                       float* rstd, int64_t rows, int64_t N, float eps, int dtype, hipStream_t stream);
+
+/* Same as the three entry points above, with the kernel variant forced (RN_VARIANT_AUTO
+ * behaves exactly like the plain entry point). A forced variant that cannot run the given
+ * shape / alignment returns RN_ERR_UNSUPPORTED before anything is enqueued. Used by tests
+ * to reach every kernel and by benchmarks to compare them. */
+int ln_forward_variant(const void* x, const void* gamma, const void* beta, void* y, float* mean, float* rstd,
+                       int64_t rows, int64_t N, float eps, int dtype, hipStream_t stream, int variant);
+int rms_norm_variant(const void* x, const void* weight, void* y, float* rstd, int64_t rows, int64_t N, float eps,
+                     int dtype, hipStream_t stream, int variant);
+int fused_add_rms_norm_variant(const void* x, const void* residual, const void* weight, void* y,
+                               void* residual_out, float* rstd, int64_t rows, int64_t N, float eps, int dtype,
+                               hipStream_t stream, int variant);
+
+/* Launch plan chosen for a call, computed on the host only (no HIP call is made), with the
+ * same validation as the entry points. Pointers are only inspected for NULL, alignment and
+ * overlap, never dereferenced. */
+typedef struct rn_plan_info {
+    int variant;           /* rn_variant actually used */
+    int waves_per_row;     /* wavefronts cooperating on one row */
+    int rows_per_block;    /* rows one workgroup processes per iteration */
+    int block_threads;     /* workgroup size */
+    int chunks_per_lane;   /* 16-byte chunks each lane holds (vectorized variants) */
+    int64_t grid_blocks;   /* workgroups launched */
+} rn_plan_info;
+
+int rn_plan(int op, const void* x, const void* residual, const void* gamma, const void* beta, const void* y,
+            const void* residual_out, const void* mean, const void* rstd, int64_t rows, int64_t N, float eps,
+            int dtype, int variant, rn_plan_info* out);
+
+/* Static string naming a status code ("RN_OK", ...); "unknown status" otherwise. */
+const char* rn_status_string(int status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int rn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROWNORM_H */

@@ -1,0 +1,77 @@
+"""Comparison of GPU outputs with the oracle, at the tolerances the parity tests use.
+
+* fp32 outputs: max |y_gpu - y_ref| <= 1e-4 (absolute), y_ref in fp64.
+* fp16 / bf16 outputs: at most 2 output ulps from round(y_ref), the oracle's single
+  round-to-nearest-even of the fp64 result. The ulp is taken at max(|y_ref|, 2^-14): for
+  fp16 that is exactly the format's own spacing (its subnormal spacing is 2^-24); for bf16
+  it floors the spacing at 2^-21, because an fp32-accumulating kernel cannot promise 2 bf16
+  ulps where the LayerNorm affine term cancels to nearly 0.
+* mean: |mean_gpu - mean_ref| <= 1e-5 * max(|mean_ref|, sigma_ref), sigma_ref = sqrt(var);
+  rstd: |rstd_gpu / rstd_ref - 1| <= 1e-5.
+* residual_out: bit-exact.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+
+FP32_ABS_TOL = 1e-4
+ULP_TOL = 2.0
+STAT_REL_TOL = 1e-5
+MANT_BITS = {"fp16": 10, "bf16": 7}
+_NAME = {torch.float32: "fp32", torch.float16: "fp16", torch.bfloat16: "bf16"}
+
+
+def dtype_name(t: torch.Tensor) -> str:
+    return _NAME[t.dtype]
+
+
+def ulp_distance(got: np.ndarray, ref64: np.ndarray, dtype: str) -> np.ndarray:
+    """|got - round(ref)| in ulps of the I/O dtype at max(|ref|, 2^-14)."""
+    ref_r = oracle.round_to(ref64, dtype)
+    mag = np.maximum(np.abs(ref64), 2.0 ** -14)
+    ulp = np.exp2(np.floor(np.log2(mag)) - MANT_BITS[dtype])
+    return np.abs(got - ref_r) / ulp
+
+
+def check_y(y_gpu: torch.Tensor, y_ref: np.ndarray, what: str = "y") -> float:
+    """Assert the tolerance for y; return the worst error (abs for fp32, ulps otherwise)."""
+    dt = dtype_name(y_gpu)
+    got = y_gpu.detach().cpu().double().numpy().reshape(y_ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
+    if dt == "fp32":
+        err = float(np.abs(got - y_ref).max()) if got.size else 0.0
+        assert err <= FP32_ABS_TOL, f"{what}: max abs error {err:.3g} > {FP32_ABS_TOL}"
+        return err
+    d = ulp_distance(got, y_ref, dt)
+    err = float(d.max()) if d.size else 0.0
+    assert err <= ULP_TOL, f"{what}: max ulp distance {err} > {ULP_TOL} (count {(d > ULP_TOL).sum()})"
+    return err
+
+
+def check_mean(mean_gpu: torch.Tensor, mean_ref: np.ndarray, rstd_ref: np.ndarray, eps: float):
+    got = mean_gpu.detach().cpu().double().numpy().reshape(-1)
+    var = np.maximum(1.0 / rstd_ref ** 2 - eps, 0.0)
+    scale = np.maximum(np.abs(mean_ref), np.sqrt(var))
+    err = np.abs(got - mean_ref)
+    bad = err > STAT_REL_TOL * scale
+    assert not bad.any(), f"mean: {bad.sum()} rows off, worst {float((err / np.maximum(scale, 1e-300)).max()):.3g}"
+
+
+def check_rstd(rstd_gpu: torch.Tensor, rstd_ref: np.ndarray):
+    got = rstd_gpu.detach().cpu().double().numpy().reshape(-1)
+    rel = np.abs(got / rstd_ref - 1.0)
+    worst = float(rel.max()) if rel.size else 0.0
+    assert worst <= STAT_REL_TOL, f"rstd: worst relative error {worst:.3g}"
+
+
+def check_bits_equal(a: torch.Tensor, ref_bits: np.ndarray, what: str):
+    dt = dtype_name(a)
+    t = a.detach().cpu().contiguous()
+    bits = t.view(torch.int32).numpy().view(np.uint32) if dt == "fp32" else t.view(torch.int16).numpy().view(np.uint16)
+    bits = bits.reshape(ref_bits.shape)
+    diff = bits != ref_bits
+    assert not diff.any(), f"{what}: {int(diff.sum())} elements differ from the correctly rounded sum"

@@ -1,0 +1,162 @@
+"""CPU-side tests of the C ABI (no GPU needed, no kernel is launched).
+
+* librownorm.so loads and exports every function include/rownorm.h declares;
+* rn_plan's validation and variant choice (a host-only function);
+* the entry points reject bad arguments before touching HIP.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import row_wise_normalization_fp32_amd as rn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rownorm.h")
+
+OK, NULL, SHAPE, DTYPE, ALIAS, UNSUP, HIP, ALIGN = range(8)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+    assert names, "no declarations parsed"
+    return names
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(rn.LIB_PATH)
+    names = _declared_functions()
+    for n in ("ln_forward", "rms_norm", "fused_add_rms_norm", "rn_plan", "rn_status_string"):
+        assert n in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_status_strings_and_version():
+    for code, name in rn.STATUS.items():
+        assert rn._lib.rn_status_string(code).decode() == name
+    assert rn._lib.rn_status_string(99).decode() == "unknown status"
+    assert rn.version() == 10000
+
+
+@pytest.mark.parametrize("op,dtype,rows,N,variant,V", [
+    ("ln", torch.float32, 64, 1024, "wave", 4),          # C1
+    ("ln", torch.float32, 128, 4096, "wave", 16),        # C2
+    ("rms", torch.float16, 2048, 4096, "wave", 8),       # C3
+    ("fused_add_rms", torch.float16, 256, 4096, "wave", 8),   # C4
+    ("fused_add_rms", torch.bfloat16, 256, 4096, "wave", 8),  # C4
+    ("ln", torch.bfloat16, 4096, 16384, "workgroup", 8),  # C5
+    ("ln", torch.float32, 16, 16384, "workgroup", 16),
+    ("rms", torch.bfloat16, 16, 32768, "workgroup", 16),
+    ("ln", torch.float32, 16, 16388, "general", 0),       # beyond a workgroup's registers
+    ("ln", torch.float32, 16, 1000, "wave", 4),           # ragged: 250 chunks
+    ("ln", torch.float16, 16, 1001, "general", 0),        # not a whole number of 16-byte chunks
+    ("rms", torch.float32, 3, 1, "general", 0),
+])
+def test_plan_variant_choice(op, dtype, rows, N, variant, V):
+    st, info = rn.plan(op, rows, N, dtype)
+    assert st == OK
+    assert info["variant"] == variant
+    assert info["chunks_per_lane"] == V
+    if variant == "wave":
+        assert info["block_threads"] == 256 and info["rows_per_block"] == 4
+        assert info["grid_blocks"] == (rows + 3) // 4
+    elif variant == "workgroup":
+        assert info["block_threads"] == 256 and info["waves_per_row"] == 4 and info["grid_blocks"] == rows
+    else:
+        assert info["grid_blocks"] == rows
+
+
+def test_plan_grid_is_capped():
+    st, info = rn.plan("rms", 1 << 23, 64, torch.float16)
+    assert st == OK and info["grid_blocks"] == 1 << 20
+
+
+def test_plan_misaligned_pointer_takes_general_path():
+    st, info = rn.plan("ln", 8, 1024, torch.float32, ptrs={"x": (1 << 40) + 4})
+    assert st == OK and info["variant"] == "general"
+    st, _ = rn.plan("ln", 8, 1024, torch.float32, ptrs={"x": (1 << 40) + 4}, variant="wave")
+    assert st == UNSUP
+
+
+def test_plan_forced_variants():
+    assert rn.plan("ln", 4, 4096, torch.float32, variant="workgroup")[1]["variant"] == "workgroup"
+    assert rn.plan("ln", 4, 8192, torch.float16, variant="wave")[1]["chunks_per_lane"] == 16
+    assert rn.plan("ln", 4, 8192, torch.float32, variant="wave")[0] == UNSUP
+    assert rn.plan("ln", 4, 64, torch.float32, variant="general")[1]["variant"] == "general"
+    assert rn.plan("ln", 4, 64, torch.float32, variant=7)[0] == UNSUP
+
+
+def test_plan_argument_errors():
+    f32 = torch.float32
+    assert rn.plan("ln", -1, 64, f32)[0] == SHAPE
+    assert rn.plan("ln", 4, 0, f32)[0] == SHAPE
+    assert rn.plan("ln", 4, 64, f32, eps=-1.0)[0] == SHAPE
+    assert rn.plan("ln", 4, 64, f32, eps=float("nan"))[0] == SHAPE
+    assert rn.plan("ln", 4, 64, f32, eps=float("inf"))[0] == SHAPE
+    assert rn.plan("ln", 1 << 40, 1 << 30, f32)[0] == SHAPE  # rows * N * 4 overflows
+    assert rn.plan("ln", 4, 64, f32, ptrs={"x": None})[0] == NULL
+    assert rn.plan("ln", 4, 64, f32, ptrs={"y": None})[0] == NULL
+    assert rn.plan("fused_add_rms", 4, 64, f32, ptrs={"residual": None})[0] == NULL
+    assert rn.plan("fused_add_rms", 4, 64, f32, ptrs={"residual_out": None})[0] == NULL
+    assert rn.plan("ln", 4, 64, f32, ptrs={"x": (1 << 40) + 2})[0] == ALIGN
+    assert rn.plan("ln", 4, 64, torch.float16, ptrs={"x": (1 << 40) + 1})[0] == ALIGN
+    assert rn.plan("ln", 4, 64, f32, ptrs={"mean": (1 << 44) + 2})[0] == ALIGN
+
+
+def test_plan_zero_rows_is_a_noop_even_without_buffers():
+    st, info = rn.plan("ln", 0, 64, torch.float32, ptrs={"x": None, "y": None})
+    assert st == OK and info["grid_blocks"] == 0
+
+
+def test_plan_aliasing_rules():
+    f32 = torch.float32
+    base = 1 << 40
+    rows, N = 4, 64
+    nbytes = rows * N * 4
+    far = base + (1 << 30)
+    # exact in-place is allowed
+    assert rn.plan("ln", rows, N, f32, ptrs={"x": base, "y": base})[0] == OK
+    assert rn.plan("rms", rows, N, f32, ptrs={"x": base, "y": base})[0] == OK
+    assert rn.plan("fused_add_rms", rows, N, f32,
+                   ptrs={"x": base, "residual": far, "residual_out": far, "y": base})[0] == OK
+    assert rn.plan("fused_add_rms", rows, N, f32,
+                   ptrs={"x": base, "residual": far, "residual_out": base, "y": far})[0] == OK
+    # partial overlap of an output with an input
+    assert rn.plan("ln", rows, N, f32, ptrs={"x": base, "y": base + 256})[0] == ALIAS
+    # an output on top of a parameter vector
+    assert rn.plan("ln", rows, N, f32, ptrs={"x": base, "y": far, "gamma": far + 128})[0] == ALIAS
+    # two outputs on the same memory
+    assert rn.plan("fused_add_rms", rows, N, f32,
+                   ptrs={"x": base, "residual": base + nbytes, "residual_out": far, "y": far})[0] == ALIAS
+    assert rn.plan("ln", rows, N, f32, ptrs={"x": base, "y": far, "mean": far + nbytes,
+                                            "rstd": far + nbytes})[0] == ALIAS
+    assert rn.plan("ln", rows, N, f32, ptrs={"x": base, "y": far, "mean": base + 16})[0] == ALIAS
+    # inputs may overlap each other
+    assert rn.plan("ln", rows, N, f32, ptrs={"x": base, "y": far, "gamma": base, "beta": base})[0] == OK
+    # beta is not part of RMSNorm, so it is ignored there
+    assert rn.plan("rms", rows, N, f32, ptrs={"x": base, "y": far, "beta": far})[0] == OK
+
+
+def test_entry_points_reject_before_launch():
+    # Every call below fails validation, so no HIP call is made: safe without a GPU.
+    lib = rn._lib
+    assert lib.ln_forward(None, None, None, 0x1000, None, None, 4, 64, 1e-5, 0, None) == NULL
+    assert lib.ln_forward(0x1000, None, None, 0x100000, None, None, 4, 64, 1e-5, 9, None) == DTYPE
+    assert lib.ln_forward(0x1000, None, None, 0x100000, None, None, -3, 64, 1e-5, 0, None) == SHAPE
+    assert lib.rms_norm(0x1000, None, 0x1000 + 64, None, 4, 64, 1e-6, 0, None) == ALIAS
+    assert lib.fused_add_rms_norm(0x1000, None, None, 0x100000, 0x200000, None, 4, 64, 1e-6, 1, None) == NULL
+    assert lib.ln_forward_variant(0x1000, None, None, 0x100000, None, None, 4, 8192, 1e-5, 0, None, 1) == UNSUP
+    assert lib.ln_forward(None, None, None, None, None, None, 0, 64, 1e-5, 0, None) == OK
+
+
+def test_python_binding_rejects_cpu_tensors():
+    with pytest.raises(ValueError):
+        rn.ln_forward(torch.zeros(2, 8))
+    with pytest.raises(ValueError):
+        rn.rms_norm(torch.zeros(2, 8))

@@ -1,0 +1,258 @@
+"""GPU parity: the HIP library against the fp64 oracle, element by element.
+
+Every call goes through the C ABI (via the ctypes binding). Inputs come from the seeded
+generators in workloads.py; expected values come only from the oracle. Tolerances are
+stated in tests/_compare.py.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import row_wise_normalization_fp32_amd as rn
+import workloads
+from _compare import check_bits_equal, check_mean, check_rstd, check_y, dtype_name
+
+pytestmark = pytest.mark.gpu
+
+THREADS = min(16, os.cpu_count() or 1)
+DEV = "cuda:0"
+TD = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _gpu(inp):
+    return {k: v.to(DEV) for k, v in inp.items()}
+
+
+def run_gpu(w: workloads.Workload, inp, variant="auto", stats=True):
+    g = _gpu(inp)
+    if w.op == "ln":
+        out = rn.ln_forward(g["x"], g.get("gamma"), g.get("beta"), w.eps, return_stats=stats, variant=variant)
+        return (out if stats else (out, None, None))
+    if w.op == "rms":
+        y, rstd = rn.rms_norm(g["x"], g.get("weight"), w.eps, return_rstd=True, variant=variant)
+        return y, None, rstd
+    y, ro, rstd = rn.fused_add_rms_norm(g["x"], g["residual"], g.get("weight"), w.eps, return_rstd=True,
+                                        variant=variant)
+    return y, ro, rstd
+
+
+def run_oracle(w: workloads.Workload, inp):
+    if w.op == "ln":
+        return oracle.layer_norm(inp["x"], inp.get("gamma"), inp.get("beta"), w.eps, threads=THREADS)
+    if w.op == "rms":
+        return oracle.rms_norm(inp["x"], inp.get("weight"), w.eps, threads=THREADS)
+    return oracle.fused_add_rms_norm(inp["x"], inp["residual"], inp.get("weight"), w.eps, threads=THREADS)
+
+
+def check_case(w: workloads.Workload, variant="auto", inp=None):
+    inp = workloads.make_inputs(w) if inp is None else inp
+    ref = run_oracle(w, inp)
+    a, b, c = run_gpu(w, inp, variant)
+    torch.cuda.synchronize()
+    err = check_y(a, ref["y"])
+    if w.op == "ln":
+        check_mean(b, ref["mean"], ref["rstd"], w.eps)
+        check_rstd(c, ref["rstd"])
+    elif w.op == "rms":
+        check_rstd(c, ref["rstd"])
+    else:
+        check_bits_equal(b, ref["residual_out"], "residual_out")
+        check_rstd(c, ref["rstd"])
+    return err
+
+
+# ---------------------------------------------------------------------------------------
+# The six headline configurations at full size, in the launch configuration the
+# benchmark times (automatic variant choice).
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("w", workloads.CONFIGS, ids=[c.name for c in workloads.CONFIGS])
+def test_config_full_size(w):
+    check_case(w)
+
+
+def test_fused_large_shape():
+    check_case(workloads.FUSED_8192)
+
+
+# ---------------------------------------------------------------------------------------
+# Every kernel variant on shapes spanning several tiles and a ragged tail.
+# ---------------------------------------------------------------------------------------
+
+SHAPES = [(37, 1000), (5, 4096), (9, 2056), (3, 8)]
+
+
+@pytest.mark.parametrize("variant", ["wave", "workgroup", "general"])
+@pytest.mark.parametrize("op", ["ln", "rms", "fused_add_rms"])
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+def test_variants_agree_with_oracle(variant, op, dtype):
+    base = {"ln": workloads.C1, "rms": workloads.C3, "fused_add_rms": workloads.C4_FP16}[op]
+    for rows, N in SHAPES:
+        w = base.scaled(rows=rows, N=N, seed=500 + rows, dtype=dtype)
+        check_case(w, variant)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_workgroup_path_long_rows(dtype):
+    for rows, N in [(7, 16384), (6, 12296), (4, 8200)]:
+        check_case(workloads.C5.scaled(rows=rows, N=N, seed=600 + N, dtype=dtype))
+
+
+def test_workgroup_path_32k_bf16_rows():
+    check_case(workloads.C5.scaled(rows=5, N=32768, seed=601))
+
+
+def test_offset_rows_on_every_variant():
+    # The cancellation stress (row offsets up to +-1000) on each kernel.
+    for variant in ("wave", "workgroup", "general"):
+        check_case(workloads.C2.scaled(rows=16, seed=610), variant)
+    check_case(workloads.C2.scaled(rows=8, N=16384, seed=611))
+
+
+# ---------------------------------------------------------------------------------------
+# Edge cases.
+# ---------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N", [1, 2, 3, 7, 64, 255, 1023, 4097, 8191, 20000])
+def test_odd_widths(N):
+    for op, base in (("ln", workloads.C1), ("rms", workloads.C3), ("fused_add_rms", workloads.C4_BF16)):
+        check_case(base.scaled(rows=3, N=N, seed=700 + N))
+
+
+def test_zero_rows_is_a_noop():
+    x = torch.empty(0, 64, device=DEV)
+    y = rn.ln_forward(x)
+    assert y.shape == (0, 64)
+    y, ro = rn.fused_add_rms_norm(x, x.clone())
+    assert ro.shape == (0, 64)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_optional_parameters(dtype):
+    for with_g, with_b in [(False, False), (True, False), (False, True)]:
+        w = workloads.C1.scaled(rows=9, N=1024, seed=800, dtype=dtype, with_gamma=with_g, with_beta=with_b)
+        for variant in ("wave", "workgroup", "general"):
+            check_case(w, variant)
+    w = workloads.C3.scaled(rows=9, N=512, seed=801, dtype=dtype, with_gamma=False)
+    check_case(w)
+    w = workloads.C4_FP16.scaled(rows=9, N=512, seed=802, dtype=dtype, with_gamma=False)
+    check_case(w)
+
+
+def test_constant_rows_map_to_beta():
+    for dtype in ("fp32", "fp16", "bf16"):
+        for N in (1024, 16384):
+            w = workloads.C2.scaled(rows=6, N=N, seed=810, dtype=dtype, x_dist="constant")
+            inp = workloads.make_inputs(w)
+            g = _gpu(inp)
+            y, mean, rstd = rn.ln_forward(g["x"], g["gamma"], g["beta"], w.eps, return_stats=True)
+            torch.cuda.synchronize()
+            beta = g["beta"].expand_as(y)
+            assert torch.equal(y, beta), f"{dtype} N={N}: constant rows must give beta exactly"
+            assert torch.equal(mean, g["x"][:, 0].float())
+
+
+def test_misaligned_pointers_use_general_path():
+    w = workloads.C1.scaled(rows=5, N=1024, seed=820)
+    inp = workloads.make_inputs(w)
+    ref = run_oracle(w, inp)
+    buf = torch.empty(5 * 1024 + 1, device=DEV)
+    x = buf[1:].view(5, 1024)
+    x.copy_(inp["x"].to(DEV))
+    st, info = rn.plan("ln", 5, 1024, torch.float32, ptrs={"x": x.data_ptr()})
+    assert info["variant"] == "general"
+    y, mean, rstd = rn.ln_forward(x, inp["gamma"].to(DEV), inp["beta"].to(DEV), w.eps, return_stats=True)
+    torch.cuda.synchronize()
+    check_y(y, ref["y"])
+    check_rstd(rstd, ref["rstd"])
+
+
+@pytest.mark.parametrize("variant", ["wave", "workgroup", "general"])
+def test_in_place(variant):
+    w = workloads.C1.scaled(rows=11, N=2048, seed=830, dtype="bf16")
+    inp = workloads.make_inputs(w)
+    ref = run_oracle(w, inp)
+    g = _gpu(inp)
+    x = g["x"].clone()
+    y = rn.ln_forward(x, g["gamma"], g["beta"], w.eps, out=x, variant=variant)
+    torch.cuda.synchronize()
+    assert y.data_ptr() == x.data_ptr()
+    check_y(x, ref["y"])
+    # fused: residual_out written over residual, y over x
+    w = workloads.C4_BF16.scaled(rows=11, N=2048, seed=831)
+    inp = workloads.make_inputs(w)
+    ref = run_oracle(w, inp)
+    g = _gpu(inp)
+    x, r = g["x"].clone(), g["residual"].clone()
+    rn.fused_add_rms_norm(x, r, g["weight"], w.eps, out=x, residual_out=r, variant=variant)
+    torch.cuda.synchronize()
+    check_y(x, ref["y"])
+    check_bits_equal(r, ref["residual_out"], "residual_out in place")
+    # fused: residual_out written over x, y over residual
+    x, r = g["x"].clone(), g["residual"].clone()
+    rn.fused_add_rms_norm(x, r, g["weight"], w.eps, out=r, residual_out=x, variant=variant)
+    torch.cuda.synchronize()
+    check_y(r, ref["y"])
+    check_bits_equal(x, ref["residual_out"], "residual_out over x")
+
+
+def test_three_dimensional_input():
+    w = workloads.C3.scaled(rows=24, N=4096, seed=840)
+    inp = workloads.make_inputs(w)
+    ref = run_oracle(w, inp)
+    x3 = inp["x"].view(4, 6, 4096).to(DEV)
+    y = rn.rms_norm(x3, inp["weight"].to(DEV), w.eps)
+    torch.cuda.synchronize()
+    assert y.shape == (4, 6, 4096)
+    check_y(y.view(24, 4096), ref["y"])
+
+
+def test_outputs_fully_written_and_nothing_outside():
+    # Outputs are carved from a NaN-filled buffer with guard zones on both sides.
+    for variant in ("wave", "workgroup", "general"):
+        w = workloads.C4_FP16.scaled(rows=13, N=1000, seed=850)
+        inp = workloads.make_inputs(w)
+        g = _gpu(inp)
+        n = 13 * 1000
+        pad = 4096
+        buf = torch.full((2 * n + 3 * pad,), float("nan"), dtype=torch.float16, device=DEV)
+        y = buf[pad:pad + n].view(13, 1000)
+        ro = buf[2 * pad + n:2 * pad + 2 * n].view(13, 1000)
+        rstd = torch.full((13 + 2 * 64,), float("nan"), device=DEV)
+        rn.fused_add_rms_norm(g["x"], g["residual"], g["weight"], w.eps, out=y, residual_out=ro,
+                              rstd=rstd[64:64 + 13], variant=variant)
+        torch.cuda.synchronize()
+        assert not torch.isnan(y).any() and not torch.isnan(ro).any()
+        assert torch.isnan(buf[:pad]).all() and torch.isnan(buf[pad + n:2 * pad + n]).all()
+        assert torch.isnan(buf[2 * pad + 2 * n:]).all()
+        assert torch.isnan(rstd[:64]).all() and torch.isnan(rstd[64 + 13:]).all()
+        assert not torch.isnan(rstd[64:64 + 13]).any()
+
+
+def test_bitwise_deterministic_across_launches():
+    for w in (workloads.C2, workloads.C4_BF16, workloads.C5.scaled(rows=64)):
+        g = _gpu(workloads.make_inputs(w))
+        first = None
+        for _ in range(20):
+            outs = run_gpu(w, {k: v for k, v in g.items()})
+            torch.cuda.synchronize()
+            outs = [o.clone() for o in outs if o is not None]
+            if first is None:
+                first = outs
+            else:
+                for a, b in zip(first, outs):
+                    assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_argument_errors_reach_python():
+    x = torch.zeros(4, 64, device=DEV)
+    with pytest.raises(rn.RowNormError) as e:
+        rn.ln_forward(x, out=x[:, :64].clone().view(4, 64), eps=-1.0)
+    assert e.value.status == 2
+    with pytest.raises(rn.RowNormError) as e:
+        rn.ln_forward(torch.zeros(4, 8192, device=DEV), variant="wave")
+    assert e.value.status == 5
