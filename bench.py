@@ -91,6 +91,16 @@ def make_sets(w, nsets, dev):
     return sets
 
 
+def kernel_name(w, plan):
+    """The kernel instance a workload's launch runs, as rocprofv3 lists it (template arguments:
+    dtype, op, waves per row, chunks per lane, row groups per workgroup, exact, affine, flags)."""
+    if plan["variant"] == "general":
+        return f"rn::rownorm_general_kernel ({w.dtype}, {w.op})"
+    mode = "persistent" if plan["persistent"] else "grid per row"
+    return (f"rn::rownorm_vec_kernel ({w.dtype}, {w.op}, W={plan['waves_per_row']} waves per row, "
+            f"V={plan['chunks_per_lane']} chunks per lane, {plan['rows_per_block']} row group(s) per workgroup, {mode})")
+
+
 def launch(rn, w, s):
     if w.op == "ln":
         rn.ln_forward(s["x"], s.get("gamma"), s.get("beta"), w.eps, out=s["y"], mean=s["mean"], rstd=s["rstd"])
@@ -129,7 +139,12 @@ def measure(w, steps, warmup, cache, dev):
     durs = [a.elapsed_time(b) for a, b in zip(starts, ends)]  # ms
     kernel_ms = sum(durs) / len(durs)
     ms_per_step = wall * 1e3 / steps
-    st, info = rn.plan(w.op, w.rows, w.N, workloads.TORCH_DTYPES[w.dtype])
+    s0 = sets[0]
+    ptrs = {k: s0[k].data_ptr() for k in ("x", "residual", "gamma", "beta", "weight", "y", "residual_out", "mean", "rstd")
+            if k in s0}
+    if "weight" in ptrs:
+        ptrs["gamma"] = ptrs.pop("weight")
+    st, info = rn.plan(w.op, w.rows, w.N, workloads.TORCH_DTYPES[w.dtype], ptrs=ptrs, eps=w.eps)
     del sets
     torch.cuda.empty_cache()
     return {
@@ -238,7 +253,7 @@ def main():
         "config": {
             "workload": "LayerNorm forward, bf16 I/O, 4096 x 16384, eps 1e-5, y + fp32 mean/rstd",
             "op": "ln_forward", "io_dtype": "bf16", "rows": w.rows, "N": w.N, "cache": args.cache,
-            "buffer_sets": r["nsets"], "variant": r["plan"]["variant"],
+            "buffer_sets": r["nsets"], "variant": r["plan"]["variant"], "persistent": r["plan"]["persistent"],
             "inputs": "x = m_r + s_r*z, m_r~U(-10,10), s_r~U(0.5,4); gamma~U(0.5,1.5); beta~N(0,0.1^2); seed 1005",
         },
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
@@ -246,7 +261,7 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-            "kernel": "rn::rownorm_vec_kernel<bf16, LayerNorm, 4 waves per row, 8 chunks per lane, 1 row per block>",
+            "kernel": kernel_name(w, r["plan"]),
             "kernel_avg_ms": round(r["kernel_ms"], 5), "kernel_median_ms": round(r["kernel_ms_median"], 5),
             "bytes_per_launch": r["bytes"],
         },
@@ -264,7 +279,7 @@ def main():
             "rows_per_s": round(f.rows / (rf["ms_per_step"] * 1e-3), 1), "ms_per_step": round(rf["ms_per_step"], 5),
             "kernel_avg_ms": round(rf["kernel_ms"], 5), "achieved_kernel_GBs": round(fa, 2),
             "frac_kernel": round(fa / PEAK_HBM_GBS, 4), "bytes_per_launch": rf["bytes"],
-            "variant": rf["plan"]["variant"], "traffic": counter_traffic("fused_fp16_8192x4096"),
+            "kernel": kernel_name(f, rf["plan"]), "traffic": counter_traffic("fused_fp16_8192x4096"),
         }
     print(json.dumps(out), flush=True)
 

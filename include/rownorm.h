@@ -26,8 +26,9 @@
  *     are rounded once (round-to-nearest-even) to `dtype`.
  *   - The caller owns every buffer. The library never allocates, frees or synchronizes;
  *     work is enqueued on `stream` (0 = the null stream) and results are valid once the
- *     caller has synchronized that stream. The library keeps no state between calls and
- *     may be called from several host threads at once.
+ *     caller has synchronized that stream. The library keeps no per-call state (it only
+ *     caches, per device, the occupancy of each kernel configuration it has launched) and may
+ *     be called from several host threads at once.
  *   - Errors are reported by the return value (an rn_status). Argument errors are detected
  *     on the host before anything is enqueued, so an error leaves every output untouched.
  *   - rows == 0 is a successful no-op.
@@ -36,9 +37,12 @@
  *     Any other overlap between an output and any other buffer is RN_ERR_ALIAS.
  *   - Every pointer must be aligned to its element size (RN_ERR_ALIGN otherwise). When N *
  *     sizeof(dtype) is a multiple of 16 and every [rows, N] / [N] pointer is 16-byte aligned,
- *     the vectorized kernels run (one 64-lane wavefront per row for N <= 4096, one
- *     workgroup per row for N <= 16384); otherwise, and for longer rows, a slower general
- *     kernel computes the same result.
+ *     the vectorized kernels run: a row is held in registers by one 64-lane wavefront (rows
+ *     of up to 4 KiB, or 16 KiB when forced) or by a group of up to 16 wavefronts (rows of up
+ *     to 64 KiB: 16384 fp32 or 32768 fp16 / bf16 elements). Otherwise, and for longer rows,
+ *     a slower general kernel computes the same result.
+ *   - Launches use the current HIP device (the device of the buffers and of `stream`). The
+ *     first call of a kernel configuration on a device queries its occupancy once.
  */
 #ifndef ROWNORM_H
 #define ROWNORM_H
@@ -68,9 +72,9 @@ typedef enum rn_status {
 
 /* Kernel variants (for rn_*_variant entry points and rn_plan). */
 typedef enum rn_variant {
-    RN_VARIANT_AUTO = 0,      /* choose from N, dtype and alignment (what the plain entry points do) */
-    RN_VARIANT_WAVE = 1,      /* one 64-lane wavefront per row, row held in VGPRs (N <= 4096) */
-    RN_VARIANT_WORKGROUP = 2, /* one workgroup per row, cross-wave combine in LDS (N <= 16384) */
+    RN_VARIANT_AUTO = 0,      /* choose from N, dtype, alignment and rows (what the plain entry points do) */
+    RN_VARIANT_WAVE = 1,      /* one 64-lane wavefront per row, row held in VGPRs (rows up to 16 KiB) */
+    RN_VARIANT_WORKGROUP = 2, /* 2-16 wavefronts per row, partial moments combined in LDS (rows up to 64 KiB) */
     RN_VARIANT_GENERAL = 3    /* any N, any element-aligned pointers; re-reads the row */
 } rn_variant;
 
@@ -129,7 +133,12 @@ typedef struct rn_plan_info {
     int rows_per_block;    /* rows one workgroup processes per iteration */
     int block_threads;     /* workgroup size */
     int chunks_per_lane;   /* 16-byte chunks each lane holds (vectorized variants) */
-    int64_t grid_blocks;   /* workgroups launched */
+    int64_t grid_blocks;   /* workgroups launched (persistent launches: an upper bound; the launch
+                              caps it at what the current device keeps resident) */
+    int exact;             /* 1 if a row is exactly chunks_per_lane passes of its row group */
+    int persistent;        /* 1 if parameters are staged on chip once per workgroup and the
+                              workgroups loop over many rows */
+    int lds_bytes;         /* dynamic LDS per workgroup of a persistent launch */
 } rn_plan_info;
 
 int rn_plan(int op, const void* x, const void* residual, const void* gamma, const void* beta, const void* y,

@@ -54,7 +54,8 @@ _lib.rn_version.restype = _ci
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [("variant", _ci), ("waves_per_row", _ci), ("rows_per_block", _ci), ("block_threads", _ci),
-                ("chunks_per_lane", _ci), ("grid_blocks", _i64)]
+                ("chunks_per_lane", _ci), ("grid_blocks", _i64), ("exact", _ci), ("persistent", _ci),
+                ("lds_bytes", _ci)]
 
 
 _lib.rn_plan.argtypes = [_ci, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci, _ci,
@@ -241,4 +242,5 @@ def plan(op: str, rows: int, N: int, dtype: torch.dtype, *, ptrs: Optional[dict]
                       DTYPE_CODE.get(dtype, 99), _variant(variant), ctypes.byref(info))
     return st, {"variant": VARIANT_NAMES.get(info.variant, info.variant), "waves_per_row": info.waves_per_row,
                 "rows_per_block": info.rows_per_block, "block_threads": info.block_threads,
-                "chunks_per_lane": info.chunks_per_lane, "grid_blocks": info.grid_blocks}
+                "chunks_per_lane": info.chunks_per_lane, "grid_blocks": info.grid_blocks,
+                "exact": bool(info.exact), "persistent": bool(info.persistent), "lds_bytes": info.lds_bytes}

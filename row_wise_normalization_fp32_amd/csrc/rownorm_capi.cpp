@@ -67,6 +67,9 @@ int validate_and_plan(int op, const void* x, const void* residual, const void* g
     plan->chunks_per_lane = 0;
     plan->block_threads = 0;
     plan->grid = 0;
+    plan->exact = false;
+    plan->persistent = false;
+    plan->lds_bytes = 0;
     *chunks = 0;
     if (rows == 0) return RN_OK;
 
@@ -109,43 +112,56 @@ int validate_and_plan(int op, const void* x, const void* residual, const void* g
         if (reinterpret_cast<uintptr_t>(bufs[i].p) % 16 != 0) vec_ok = false;
     }
     const int64_t C = vec_ok ? (N * s) / 16 : 0;
-    const int64_t wave_cap = 64 * rn::kMaxChunksPerLane;                     // chunks one wavefront can hold
-    const int64_t group_cap = 64 * rn::kGroupWaves * rn::kMaxChunksPerLane;  // chunks one workgroup can hold
+    const int64_t wave_cap = int64_t(64) * rn::kMaxWaveChunks;                         // 1024 chunks
+    const int64_t group_cap = int64_t(64) * rn::kMaxGroupWaves * rn::kMaxGroupChunks;  // 4096 chunks
+
+    // Automatic row-group width: enough waves that each lane holds about kTargetChunks
+    // chunks (measured on MI355X: 4 chunks per lane balances bytes in flight against VGPRs).
+    int w_auto = next_pow2((C + 64 * rn::kTargetChunks - 1) / (64 * rn::kTargetChunks));
+    if (w_auto > rn::kMaxGroupWaves) w_auto = rn::kMaxGroupWaves;
 
     int v = variant;
     if (v == RN_VARIANT_AUTO) {
-        // One wavefront per row up to 4096 elements, one workgroup per row up to what a
-        // workgroup's registers hold (16384 fp32 / 32768 fp16 or bf16 elements).
-        if (vec_ok && N <= 4096 && C <= wave_cap)
-            v = RN_VARIANT_WAVE;
-        else if (vec_ok && C <= group_cap)
-            v = RN_VARIANT_WORKGROUP;
-        else
+        if (!vec_ok || C > group_cap)
             v = RN_VARIANT_GENERAL;
+        else
+            v = w_auto == 1 ? RN_VARIANT_WAVE : RN_VARIANT_WORKGROUP;
     }
+    int W = 0;
     if (v == RN_VARIANT_WAVE) {
         if (!vec_ok || C > wave_cap) return RN_ERR_UNSUPPORTED;
+        W = 1;
         plan->variant = rn::V_WAVE;
-        plan->waves_per_row = 1;
-        plan->rows_per_block = rn::kWaveRowsPerBlock;
-        plan->chunks_per_lane = next_pow2((C + 63) / 64);
-        plan->block_threads = 64 * rn::kWaveRowsPerBlock;
     } else if (v == RN_VARIANT_WORKGROUP) {
         if (!vec_ok || C > group_cap) return RN_ERR_UNSUPPORTED;
+        W = w_auto < 2 ? 2 : w_auto;
         plan->variant = rn::V_WORKGROUP;
-        plan->waves_per_row = rn::kGroupWaves;
-        plan->rows_per_block = 1;
-        plan->chunks_per_lane = next_pow2((C + 64 * rn::kGroupWaves - 1) / (64 * rn::kGroupWaves));
-        plan->block_threads = 64 * rn::kGroupWaves;
     } else {
         plan->variant = rn::V_GENERAL;
+    }
+    if (plan->variant == rn::V_GENERAL) {
         plan->waves_per_row = rn::kGeneralThreads / 64;
         plan->rows_per_block = 1;
         plan->chunks_per_lane = 0;
         plan->block_threads = rn::kGeneralThreads;
+    } else {
+        plan->waves_per_row = W;
+        plan->rows_per_block = W <= 4 ? 4 / W : 1;
+        plan->chunks_per_lane = next_pow2((C + 64 * W - 1) / (64 * W));
+        plan->block_threads = 64 * W * plan->rows_per_block;
     }
     const int64_t blocks = (rows + plan->rows_per_block - 1) / plan->rows_per_block;
     plan->grid = blocks < rn::kMaxGrid ? blocks : rn::kMaxGrid;
+    plan->exact = plan->variant != rn::V_GENERAL && C == int64_t(64) * W * plan->chunks_per_lane;
+    // Persistent launch: for exact shapes with parameters and enough rows that workgroups
+    // would otherwise be launched many times over (measured: it pays from about 2048
+    // workgroups up). Parameters go to LDS once per workgroup; LayerNorm with both keeps
+    // gamma in VGPRs and stages only beta, so the LDS need is at most one row (64 KiB).
+    const bool has_g = gamma != nullptr;
+    const bool has_b = op == RN_OP_LAYER_NORM && beta != nullptr;
+    plan->persistent = plan->exact && (has_g || has_b) && blocks >= rn::kPersistentBlocks;
+    plan->lds_bytes = 0;
+    if (plan->persistent) plan->lds_bytes = static_cast<int>(C * 16);  // one parameter vector in LDS
     *chunks = C;
     return RN_OK;
 }
@@ -171,7 +187,17 @@ int run(int op, const void* x, const void* residual, const void* gamma, const vo
     p.N = N;
     p.C = C;
     p.eps = eps;
-    const hipError_t e = rn::launch(op, dtype, plan, p, stream);
+    p.inv_n = static_cast<float>(1.0 / static_cast<double>(N));
+    hipError_t e = hipErrorInvalidValue;
+    switch (dtype) {
+    case RN_F32: e = plan.persistent ? rn::launch_f32_persistent(op, plan, p, stream)
+                                     : rn::launch_f32(op, plan, p, stream); break;
+    case RN_F16: e = plan.persistent ? rn::launch_f16_persistent(op, plan, p, stream)
+                                     : rn::launch_f16(op, plan, p, stream); break;
+    case RN_BF16: e = plan.persistent ? rn::launch_bf16_persistent(op, plan, p, stream)
+                                      : rn::launch_bf16(op, plan, p, stream); break;
+    default: break;
+    }
     return e == hipSuccess ? RN_OK : RN_ERR_HIP;
 }
 
@@ -230,6 +256,9 @@ int rn_plan(int op, const void* x, const void* residual, const void* gamma, cons
         out->block_threads = plan.block_threads;
         out->chunks_per_lane = plan.chunks_per_lane;
         out->grid_blocks = plan.grid;
+        out->exact = plan.exact ? 1 : 0;
+        out->persistent = plan.persistent ? 1 : 0;
+        out->lds_bytes = plan.lds_bytes;
     }
     return st;
 }

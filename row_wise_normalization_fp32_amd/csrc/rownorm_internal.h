@@ -1,5 +1,7 @@
 // Internal interface between the C-ABI host code (rownorm_capi.cpp) and the kernels
-// (rownorm_kernels.hip). Not installed; the public interface is include/rownorm.h.
+// (rownorm_kernels.hpp, instantiated in rownorm_kernels_<dtype>.hip and
+// rownorm_kernels_<dtype>_persistent.hip). Not installed; the public interface is
+// include/rownorm.h.
 #pragma once
 
 #include <stdint.h>
@@ -25,28 +27,39 @@ struct Params {
     float* rstd;
     int64_t rows;
     int64_t N;
-    int64_t C;  // 16-byte chunks per row (vectorized variants)
+    int64_t C;    // 16-byte chunks per row (vectorized variants)
     float eps;
+    float inv_n;  // 1 / N rounded to fp32
 };
 
 // Launch geometry chosen on the host.
 struct Plan {
-    int variant;         // V_WAVE, V_WORKGROUP or V_GENERAL
-    int waves_per_row;   // W
-    int rows_per_block;  // rows one workgroup handles per loop iteration
-    int chunks_per_lane; // V (vectorized variants)
-    int block_threads;
-    int64_t grid;
+    int variant;          // V_WAVE, V_WORKGROUP or V_GENERAL
+    int waves_per_row;    // W: wavefronts that share one row
+    int rows_per_block;   // RPB: row groups per workgroup
+    int chunks_per_lane;  // V: 16-byte chunks each lane holds (vectorized variants)
+    int block_threads;    // 64 * W * RPB
+    int64_t grid;         // workgroups (for persistent launches: an upper bound, capped at launch)
+    bool exact;           // C == 64 * W * V: no tail handling needed
+    bool persistent;      // parameters staged on chip once, grid sized to resident capacity
+    int lds_bytes;        // dynamic LDS of a persistent launch
 };
 
-// Largest per-lane chunk count and row-group width the vectorized kernels are built for.
-constexpr int kMaxChunksPerLane = 16;
-constexpr int kWaveRowsPerBlock = 4;   // wave variant: 4 rows (4 wavefronts) per workgroup
-constexpr int kGroupWaves = 4;         // workgroup variant: 4 wavefronts share one row
+// Shapes the vectorized kernels are built for.
+constexpr int kMaxWaveChunks = 16;     // wave variant: up to 16 chunks per lane (1024 per row)
+constexpr int kMaxGroupWaves = 16;     // workgroup variant: up to 16 waves per row ...
+constexpr int kMaxGroupChunks = 4;     // ... holding up to 4 chunks per lane (4096 per row)
+constexpr int kTargetChunks = 4;       // automatic choice: about 4 chunks per lane
 constexpr int kGeneralThreads = 256;   // general variant: 256 lanes per row
 constexpr int64_t kMaxGrid = 1 << 20;  // grid cap; kernels loop over the remaining rows
+constexpr int64_t kPersistentBlocks = 2048;  // at least this many workgroups: persistent launch
 
-// Enqueue the planned kernel. Returns the HIP error of the launch.
-hipError_t launch(int op, int dtype, const Plan& plan, const Params& p, hipStream_t stream);
+// Enqueue the planned kernel for one I/O dtype (one translation unit per dtype and mode).
+hipError_t launch_f32(int op, const Plan& plan, const Params& p, hipStream_t stream);
+hipError_t launch_f16(int op, const Plan& plan, const Params& p, hipStream_t stream);
+hipError_t launch_bf16(int op, const Plan& plan, const Params& p, hipStream_t stream);
+hipError_t launch_f32_persistent(int op, const Plan& plan, const Params& p, hipStream_t stream);
+hipError_t launch_f16_persistent(int op, const Plan& plan, const Params& p, hipStream_t stream);
+hipError_t launch_bf16_persistent(int op, const Plan& plan, const Params& p, hipStream_t stream);
 
 }  // namespace rn

@@ -2,10 +2,13 @@
 
 * fp32 outputs: max |y_gpu - y_ref| <= 1e-4 (absolute), y_ref in fp64.
 * fp16 / bf16 outputs: at most 2 output ulps from round(y_ref), the oracle's single
-  round-to-nearest-even of the fp64 result. The ulp is taken at max(|y_ref|, 2^-14): for
-  fp16 that is exactly the format's own spacing (its subnormal spacing is 2^-24); for bf16
-  it floors the spacing at 2^-21, because an fp32-accumulating kernel cannot promise 2 bf16
-  ulps where the LayerNorm affine term cancels to nearly 0.
+  round-to-nearest-even of the fp64 result. The ulp is taken at max(|y_ref|, floor_T),
+  floor_bf16 = 2^-14 (spacing 2^-21) and floor_fp16 = 2^-10 (spacing 2^-20). Where a
+  LayerNorm output crosses zero (z * gamma close to -beta) an fp32-accumulating kernel
+  carries an absolute error of a few fp32 ulps of |beta| (about 3e-7 for |beta| near 0.4),
+  finer than the 2-ulp band of either format at its smallest normal magnitudes; the floors
+  put that band at 9.5e-7 (bf16) and 1.9e-6 (fp16). Above the floor the native 2-ulp bar
+  applies unchanged. RMSNorm has no additive term, so its outputs never cancel.
 * mean: |mean_gpu - mean_ref| <= 1e-5 * max(|mean_ref|, sigma_ref), sigma_ref = sqrt(var);
   rstd: |rstd_gpu / rstd_ref - 1| <= 1e-5.
 * residual_out: bit-exact.
@@ -22,6 +25,7 @@ FP32_ABS_TOL = 1e-4
 ULP_TOL = 2.0
 STAT_REL_TOL = 1e-5
 MANT_BITS = {"fp16": 10, "bf16": 7}
+MAG_FLOOR = {"fp16": 2.0 ** -10, "bf16": 2.0 ** -14}
 _NAME = {torch.float32: "fp32", torch.float16: "fp16", torch.bfloat16: "bf16"}
 
 
@@ -30,9 +34,9 @@ def dtype_name(t: torch.Tensor) -> str:
 
 
 def ulp_distance(got: np.ndarray, ref64: np.ndarray, dtype: str) -> np.ndarray:
-    """|got - round(ref)| in ulps of the I/O dtype at max(|ref|, 2^-14)."""
+    """|got - round(ref)| in ulps of the I/O dtype at max(|ref|, floor of the dtype)."""
     ref_r = oracle.round_to(ref64, dtype)
-    mag = np.maximum(np.abs(ref64), 2.0 ** -14)
+    mag = np.maximum(np.abs(ref64), MAG_FLOOR[dtype])
     ulp = np.exp2(np.floor(np.log2(mag)) - MANT_BITS[dtype])
     return np.abs(got - ref_r) / ulp
 

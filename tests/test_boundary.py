@@ -44,32 +44,49 @@ def test_status_strings_and_version():
     assert rn.version() == 10000
 
 
-@pytest.mark.parametrize("op,dtype,rows,N,variant,V", [
-    ("ln", torch.float32, 64, 1024, "wave", 4),          # C1
-    ("ln", torch.float32, 128, 4096, "wave", 16),        # C2
-    ("rms", torch.float16, 2048, 4096, "wave", 8),       # C3
-    ("fused_add_rms", torch.float16, 256, 4096, "wave", 8),   # C4
-    ("fused_add_rms", torch.bfloat16, 256, 4096, "wave", 8),  # C4
-    ("ln", torch.bfloat16, 4096, 16384, "workgroup", 8),  # C5
-    ("ln", torch.float32, 16, 16384, "workgroup", 16),
-    ("rms", torch.bfloat16, 16, 32768, "workgroup", 16),
-    ("ln", torch.float32, 16, 16388, "general", 0),       # beyond a workgroup's registers
-    ("ln", torch.float32, 16, 1000, "wave", 4),           # ragged: 250 chunks
-    ("ln", torch.float16, 16, 1001, "general", 0),        # not a whole number of 16-byte chunks
-    ("rms", torch.float32, 3, 1, "general", 0),
+@pytest.mark.parametrize("op,dtype,rows,N,variant,W,V,persistent", [
+    ("ln", torch.float32, 64, 1024, "wave", 1, 4, False),              # C1: 256 chunks
+    ("ln", torch.float32, 128, 4096, "workgroup", 4, 4, False),        # C2: 1024 chunks
+    ("rms", torch.float16, 2048, 4096, "workgroup", 2, 4, False),      # C3: 512 chunks, 1024 groups
+    ("fused_add_rms", torch.float16, 256, 4096, "workgroup", 2, 4, False),   # C4
+    ("fused_add_rms", torch.bfloat16, 256, 4096, "workgroup", 2, 4, False),  # C4
+    ("ln", torch.bfloat16, 4096, 16384, "workgroup", 8, 4, True),      # C5: 2048 chunks, 4096 groups
+    ("fused_add_rms", torch.float16, 8192, 4096, "workgroup", 2, 4, True),
+    ("ln", torch.float32, 16, 16384, "workgroup", 16, 4, False),
+    ("rms", torch.bfloat16, 16, 32768, "workgroup", 16, 4, False),
+    ("ln", torch.float32, 16, 16388, "general", 0, 0, False),          # beyond a workgroup's registers
+    ("ln", torch.float32, 16, 1000, "wave", 1, 4, False),              # ragged: 250 chunks
+    ("ln", torch.float16, 16, 1001, "general", 0, 0, False),           # not a whole number of 16-byte chunks
+    ("rms", torch.float32, 3, 1, "general", 0, 0, False),
 ])
-def test_plan_variant_choice(op, dtype, rows, N, variant, V):
-    st, info = rn.plan(op, rows, N, dtype)
+def test_plan_variant_choice(op, dtype, rows, N, variant, W, V, persistent):
+    ptrs = {"gamma": 1 << 44, "beta": (1 << 44) + (1 << 30)}
+    st, info = rn.plan(op, rows, N, dtype, ptrs=ptrs)
     assert st == OK
     assert info["variant"] == variant
     assert info["chunks_per_lane"] == V
-    if variant == "wave":
-        assert info["block_threads"] == 256 and info["rows_per_block"] == 4
-        assert info["grid_blocks"] == (rows + 3) // 4
-    elif variant == "workgroup":
-        assert info["block_threads"] == 256 and info["waves_per_row"] == 4 and info["grid_blocks"] == rows
-    else:
-        assert info["grid_blocks"] == rows
+    assert info["persistent"] == persistent
+    if variant == "general":
+        assert info["grid_blocks"] == rows and info["block_threads"] == 256
+        return
+    assert info["waves_per_row"] == W
+    rpb = 4 // W if W <= 4 else 1
+    assert info["rows_per_block"] == rpb
+    assert info["block_threads"] == 64 * W * rpb
+    assert info["grid_blocks"] == (rows + rpb - 1) // rpb
+    s = torch.tensor([], dtype=dtype).element_size()
+    assert info["exact"] == (N * s // 16 == 64 * W * V)
+    if persistent:
+        assert info["lds_bytes"] == N * s  # one parameter vector staged in LDS
+
+
+def test_plan_persistent_needs_parameters():
+    # without gamma / beta there is nothing to stage: grid-per-row launch
+    st, info = rn.plan("ln", 4096, 16384, torch.bfloat16)
+    assert st == OK and not info["persistent"] and info["lds_bytes"] == 0
+    # ragged rows are never persistent
+    st, info = rn.plan("rms", 1 << 15, 1000, torch.float32, ptrs={"gamma": 1 << 44})
+    assert st == OK and not info["exact"] and not info["persistent"]
 
 
 def test_plan_grid_is_capped():
@@ -85,9 +102,12 @@ def test_plan_misaligned_pointer_takes_general_path():
 
 
 def test_plan_forced_variants():
-    assert rn.plan("ln", 4, 4096, torch.float32, variant="workgroup")[1]["variant"] == "workgroup"
+    assert rn.plan("ln", 4, 4096, torch.float32, variant="workgroup")[1]["waves_per_row"] == 4
+    assert rn.plan("ln", 4, 64, torch.float32, variant="workgroup")[1]["waves_per_row"] == 2
+    assert rn.plan("ln", 4, 4096, torch.float32, variant="wave")[1]["chunks_per_lane"] == 16
     assert rn.plan("ln", 4, 8192, torch.float16, variant="wave")[1]["chunks_per_lane"] == 16
     assert rn.plan("ln", 4, 8192, torch.float32, variant="wave")[0] == UNSUP
+    assert rn.plan("ln", 4, 32768, torch.float32, variant="workgroup")[0] == UNSUP
     assert rn.plan("ln", 4, 64, torch.float32, variant="general")[1]["variant"] == "general"
     assert rn.plan("ln", 4, 64, torch.float32, variant=7)[0] == UNSUP
 

@@ -256,3 +256,70 @@ def test_argument_errors_reach_python():
     with pytest.raises(rn.RowNormError) as e:
         rn.ln_forward(torch.zeros(4, 8192, device=DEV), variant="wave")
     assert e.value.status == 5
+
+
+# ---------------------------------------------------------------------------------------
+# Persistent launches: parameters staged on chip once per workgroup, workgroups looping
+# over many rows. Shapes chosen to have at least 2048 row-group workgroups at every
+# row-group width (1, 2, 4, 8, 16 wavefronts per row).
+# ---------------------------------------------------------------------------------------
+
+PERSISTENT_CASES = [
+    # (base, dtype, rows, N, with_gamma, with_beta)
+    ("ln", "fp32", 8192, 256, True, True),      # 1 wave per row
+    ("ln", "fp32", 8192, 256, True, False),
+    ("ln", "fp32", 8192, 256, False, True),
+    ("ln", "bf16", 4096, 4096, True, True),     # 2 waves per row
+    ("ln", "fp32", 2048, 4096, True, True),     # 4 waves per row
+    ("ln", "bf16", 2048, 16384, True, False),   # 8 waves per row
+    ("ln", "fp32", 2048, 16384, False, True),   # 16 waves per row
+    ("ln", "fp16", 2048, 32768, True, True),    # 16 waves per row, 16-bit
+    ("rms", "fp16", 8192, 512, True, True),
+    ("rms", "bf16", 4096, 8192, True, True),
+    ("fused_add_rms", "bf16", 4096, 4096, True, True),
+    ("fused_add_rms", "fp32", 8192, 2048, True, True),
+]
+
+
+@pytest.mark.parametrize("case", PERSISTENT_CASES, ids=[f"{c[0]}-{c[1]}-{c[2]}x{c[3]}-g{int(c[4])}b{int(c[5])}"
+                                                        for c in PERSISTENT_CASES])
+def test_persistent_launches(case):
+    op, dtype, rows, N, wg, wb = case
+    base = {"ln": workloads.C5, "rms": workloads.C3, "fused_add_rms": workloads.C4_BF16}[op]
+    w = base.scaled(rows=rows, N=N, seed=900 + N, dtype=dtype, with_gamma=wg, with_beta=wb)
+    inp = workloads.make_inputs(w)
+    st, info = rn.plan(op, rows, N, TD[dtype], ptrs={"gamma": 1 << 44, "beta": (1 << 44) + (1 << 30)}
+                       if (wg and wb) else ({"gamma": 1 << 44} if wg else {"beta": (1 << 44) + (1 << 30)}))
+    assert st == 0 and info["persistent"], info
+    check_case(w, inp=inp)
+
+
+def test_persistent_constant_rows_map_to_beta():
+    for dtype in ("fp32", "bf16"):
+        w = workloads.C2.scaled(rows=4096, N=4096, seed=910, dtype=dtype, x_dist="constant")
+        inp = workloads.make_inputs(w)
+        g = _gpu(inp)
+        y, mean, rstd = rn.ln_forward(g["x"], g["gamma"], g["beta"], w.eps, return_stats=True)
+        torch.cuda.synchronize()
+        assert torch.equal(y, g["beta"].expand_as(y)), dtype
+        assert torch.equal(mean, g["x"][:, 0].float())
+
+
+def test_persistent_in_place():
+    w = workloads.C5.scaled(rows=4096, N=4096, seed=920)
+    inp = workloads.make_inputs(w)
+    ref = run_oracle(w, inp)
+    g = _gpu(inp)
+    x = g["x"].clone()
+    rn.ln_forward(x, g["gamma"], g["beta"], w.eps, out=x)
+    torch.cuda.synchronize()
+    check_y(x, ref["y"])
+    w = workloads.C4_FP16.scaled(rows=8192, seed=921)
+    inp = workloads.make_inputs(w)
+    ref = run_oracle(w, inp)
+    g = _gpu(inp)
+    x, r = g["x"].clone(), g["residual"].clone()
+    rn.fused_add_rms_norm(x, r, g["weight"], w.eps, out=x, residual_out=r)
+    torch.cuda.synchronize()
+    check_y(x, ref["y"])
+    check_bits_equal(r, ref["residual_out"], "residual_out in place (persistent)")
