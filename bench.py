@@ -11,10 +11,10 @@ memory the previous launches have pushed out of L2 (8 x 4 MiB) and the 256 MiB
 memory-side cache. Inputs are resident in HBM before the timed region starts.
 
 Timed region: W warmup steps untimed, then exactly K steps bracketed by
-torch.cuda.synchronize(); ms_per_step is the wall time over K. Each launch is also
-bracketed by HIP events on the stream the kernel runs on (torch's current stream, which
-the binding passes to the C ABI), giving the per-kernel average duration used for the
-roofline.
+torch.cuda.synchronize(); ms_per_step is the wall time over K. Then the same K launches
+are repeated, each bracketed by HIP events on the stream the kernel runs on (torch's
+current stream, which the binding passes to the C ABI), giving the per-kernel average
+duration used for the roofline.
 
 value = algorithmic bytes per step / ms_per_step (GB/s, 1 GB = 1e9 B). Algorithmic bytes:
 LayerNorm 2*rows*N*s + 2*N*s + 8*rows; fused 4*rows*N*s + N*s + 4*rows (with rstd).
@@ -40,7 +40,8 @@ sys.path.insert(0, ROOT)
 METRIC = "achieved HBM GB/s (% of MI355X peak) + rows/s, LayerNorm & fused add+RMSNorm"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published peak
 COLD_FOOTPRINT = 768 << 20  # bytes each buffer set cycle must exceed (L2 + 256 MiB MALL, with margin)
-KERNEL_SRC = os.path.join(ROOT, "row_wise_normalization_fp32_amd", "csrc", "rownorm_kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "row_wise_normalization_fp32_amd", "csrc", f)
+               for f in ("rownorm_kernels.hpp", "rownorm_capi.cpp")]  # the kernels and the launch plan
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.txt")
 
 
@@ -49,8 +50,17 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Fingerprint of the code that decides the kernel: the sources with comments and
+    whitespace removed, so that only a change of the code itself invalidates a counter
+    record."""
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("".join(text.split()).encode())
+    return h.hexdigest()[:16]
 
 
 def counter_traffic(workload_key: str):
@@ -125,20 +135,25 @@ def measure(w, steps, warmup, cache, dev):
     torch.cuda.synchronize()
     for i in range(warmup):
         launch(rn, w, sets[i % nsets])
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    # Timed region: exactly `steps` steps, nothing else enqueued between them.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for i in range(steps):
+        launch(rn, w, sets[(warmup + i) % nsets])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / steps
+    # Per-kernel durations: the same launches again, each bracketed by HIP events on the
+    # stream the kernel runs on (torch's current stream, passed to the C ABI).
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for i in range(steps):
         starts[i].record()
         launch(rn, w, sets[(warmup + i) % nsets])
         ends[i].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     durs = [a.elapsed_time(b) for a, b in zip(starts, ends)]  # ms
     kernel_ms = sum(durs) / len(durs)
-    ms_per_step = wall * 1e3 / steps
     s0 = sets[0]
     ptrs = {k: s0[k].data_ptr() for k in ("x", "residual", "gamma", "beta", "weight", "y", "residual_out", "mean", "rstd")
             if k in s0}
@@ -183,6 +198,28 @@ def cpu_baseline(w, seconds):
         "rows_per_s": round(w.rows / med, 1),
         "sample": f"full {w.rows}x{w.N} {w.dtype} workload, {len(times)} passes over {sum(times):.1f} s, median pass",
     }
+
+
+def copy_reference(nbytes_each, steps, dev):
+    """GB/s of a plain device copy (torch -> the HIP runtime's copy kernel) moving the same
+    bytes as a LayerNorm launch (read nbytes_each, write nbytes_each), with the same buffer
+    rotation: the practical read+write ceiling on this GPU, for context."""
+    import torch
+
+    nsets = max(2, math.ceil(COLD_FOOTPRINT / (2 * nbytes_each)))
+    src = [torch.ones(nbytes_each // 2, dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
+    dst = [torch.empty_like(a) for a in src]
+    for i in range(5):
+        dst[i % nsets].copy_(src[i % nsets])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        dst[i % nsets].copy_(src[i % nsets])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes_each / (ms * 1e-3) / 1e9
 
 
 def copy_calibration(dev):
@@ -266,6 +303,12 @@ def main():
             "bytes_per_launch": r["bytes"],
         },
         "cpu_baseline": cpu,
+    }
+    cref = copy_reference(w.rows * w.N * w.elem_bytes, args.steps, dev)
+    out["copy_reference"] = {
+        "what": "plain device copy of the same bytes (x -> y) with the same buffer rotation",
+        "value": round(cref, 2), "unit": "GB/s", "frac_of_peak": round(cref / PEAK_HBM_GBS, 4),
+        "ln_value_over_copy": round(value / cref, 4),
     }
     if not args.no_fused:
         f = workloads.FUSED_8192

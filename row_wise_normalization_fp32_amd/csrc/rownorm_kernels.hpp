@@ -22,24 +22,27 @@
 //   * EXACT instances (the row is exactly V passes of the row group, true for every
 //     power-of-two width) carry no tail masking at all; the others clamp idle lanes'
 //     addresses into the row and zero their values.
+//   * Every load of a row is issued before any of its values is used (a scheduling
+//     barrier keeps the compiler from interleaving the first uses with the loads).
 //   * Cross-lane sums use DPP (quad_perm, row_half_mirror, row_mirror: each step adds a
 //     lane's value to its partner's, and every partner pair is symmetric, so all 16 lanes
 //     of a DPP row end with the same bits), then readlane of lanes 0/16/32/48 adds the
 //     four row sums in a fixed order. The result is wave-uniform and deterministic.
-//   * W > 1: each wavefront produces a (count, mean, M2) triple for its share of the row;
-//     the triples meet in LDS after one barrier and every lane folds them in the same
-//     fixed order with the pairwise Welford combine (count = na + nb, delta = mb - ma,
-//     mean = ma + delta * nb / n, M2 = M2a + M2b + delta^2 * na * nb / n; the "05 LLM Ops"
-//     lesson, smarter.xin, section "Welford combine function").
-//   * LayerNorm statistics are shifted: K = x[row, 0] is subtracted from every element
-//     before the sums, so the mean and the squared deviations are taken of small numbers.
-//     On rows whose mean is large next to their spread (the cancellation case of the
-//     walkthrough's section 6), plain fp32 sums lose the 1e-4 accuracy bar; the shift
-//     keeps about 1e-6. The normalization is then fma(fma(x - K, rstd, -m * rstd), gamma,
-//     beta) with m the mean of x - K; |m * rstd| is the z-score of K within its row, at
-//     most sqrt(N), so the folded form adds at most ~sqrt(N) * 2^-24 absolute error.
+//   * LayerNorm statistics: corrected two-pass (see VecRow::norm_row). A rough mean comes
+//     from a first pass (v_dot2 of packed fp16 / bf16 pairs with 1.0; for fp32 a pass
+//     shifted by K = x[row, 0]), one centered pass then gives the exact mean and M2.
+//   * W > 1: each wavefront produces a (count, mean - K, M2) triple for its share of the
+//     row; the triples meet in LDS after one barrier and every lane folds them in the same
+//     fixed pairwise tree (count = na + nb, delta = mb - ma, mean = ma + delta * nb / n,
+//     M2 = M2a + M2b + delta^2 * na * nb / n; the "05 LLM Ops" lesson, smarter.xin, section
+//     "Welford combine function"). With equal parts every scaling is by exactly 1/2.
 //   * gamma / beta / weight presence is a compile-time property (AFF flags), so absent
 //     parameters cost nothing.
+//   * Two launch modes. Grid per row: one workgroup per RPB rows, parameters loaded with
+//     each row. Persistent (many rows): a grid sized to the resident capacity, each
+//     workgroup loops over rows; the parameters are staged once (gamma in VGPRs and beta in
+//     LDS for LayerNorm, the weight in LDS otherwise), rows stream with non-temporal
+//     accesses, and LayerNorm keeps only the loaded row between statistics and output.
 //
 // General kernel (rownorm_general_kernel): any N and any element-aligned pointers. One
 // 256-lane workgroup per row; it reads the row up to three times (statistics, centered
