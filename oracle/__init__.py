@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for row-wise LayerNorm, RMSNorm and fused residual-add + RMSNorm.
+"""fp64 CPU oracle for row-wise LayerNorm, RMSNorm, fused residual-add + RMSNorm /
++ LayerNorm, softmax, and the LayerNorm / RMSNorm backward passes.
 
 TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
 leg of ``bench.py`` may import this package. It shares no code with the HIP library:
@@ -61,6 +62,18 @@ def _load():
     lib.orc_rms_norm.restype = ci
     lib.orc_fused_add_rms_norm.argtypes = [ci, vp, vp, vp, i64, i64, dbl, vp, vp, vp, ci]
     lib.orc_fused_add_rms_norm.restype = ci
+    lib.orc_fused_add_layer_norm.argtypes = [ci, vp, vp, vp, vp, i64, i64, dbl, vp, vp, vp, vp, ci]
+    lib.orc_fused_add_layer_norm.restype = ci
+    lib.orc_softmax.argtypes = [ci, vp, i64, i64, vp, vp, vp, ci]
+    lib.orc_softmax.restype = ci
+    lib.orc_layer_norm_row_f64.argtypes = [vp, vp, vp, i64, dbl, vp]
+    lib.orc_layer_norm_row_f64.restype = ci
+    lib.orc_rms_norm_row_f64.argtypes = [vp, vp, i64, dbl, vp]
+    lib.orc_rms_norm_row_f64.restype = ci
+    lib.orc_layer_norm_backward.argtypes = [ci, vp, vp, vp, vp, vp, i64, i64, dbl, vp, vp, vp]
+    lib.orc_layer_norm_backward.restype = ci
+    lib.orc_rms_norm_backward.argtypes = [ci, vp, vp, vp, vp, i64, i64, dbl, vp, vp]
+    lib.orc_rms_norm_backward.restype = ci
     _lib = lib
     return lib
 
@@ -95,6 +108,8 @@ def _check(st: int, what: str):
         raise OracleError(f"{what}: two-pass and Welford variances disagree")
     if st == 3:
         raise OracleError(f"{what}: out of memory")
+    if st == 4:
+        raise OracleError(f"{what}: plain and online softmax denominators disagree")
     if st != 0:
         raise OracleError(f"{what}: status {st}")
 
@@ -188,3 +203,100 @@ def fused_add_rms_norm(x, residual, weight=None, eps: float = 1e-6, threads: int
                                         _ptr(y), _ptr(ro), _ptr(rstd), int(threads))
     _check(st, "fused_add_rms_norm")
     return {"y": y, "residual_out": ro, "rstd": rstd}
+
+
+def fused_add_layer_norm(x, residual, gamma=None, beta=None, eps: float = 1e-5, threads: int = 1,
+                         want_y: bool = True) -> Dict[str, np.ndarray]:
+    """Fused residual add + LayerNorm; returns {"y", "mean", "rstd"} in fp64 and
+    "residual_out" as raw dtype bits."""
+    dt = dtype_name(x)
+    rows, N = x.reshape(-1, x.shape[-1]).shape
+    xb = _bits(x, dt)
+    rb = _bits(residual, dt)
+    gb = None if gamma is None else _bits(gamma, dt)
+    bb = None if beta is None else _bits(beta, dt)
+    y = np.empty((rows, N), dtype=np.float64) if want_y else None
+    ro = np.empty((rows, N), dtype=_BITS_NP[dt])
+    mean = np.empty(rows, dtype=np.float64)
+    rstd = np.empty(rows, dtype=np.float64)
+    st = _load().orc_fused_add_layer_norm(DTYPE_CODE[dt], _ptr(xb), _ptr(rb), _ptr(gb), _ptr(bb), rows, N,
+                                          float(eps), _ptr(y), _ptr(ro), _ptr(mean), _ptr(rstd), int(threads))
+    _check(st, "fused_add_layer_norm")
+    return {"y": y, "residual_out": ro, "mean": mean, "rstd": rstd}
+
+
+def softmax(x, threads: int = 1, want_y: bool = True) -> Dict[str, np.ndarray]:
+    """Row-wise softmax; returns {"y" [rows, N], "max" [rows], "sum" [rows]} in fp64, where
+    sum is the row's sum of exp(x - max)."""
+    dt = dtype_name(x)
+    rows, N = x.reshape(-1, x.shape[-1]).shape
+    xb = _bits(x, dt)
+    y = np.empty((rows, N), dtype=np.float64) if want_y else None
+    mx = np.empty(rows, dtype=np.float64)
+    sm = np.empty(rows, dtype=np.float64)
+    st = _load().orc_softmax(DTYPE_CODE[dt], _ptr(xb), rows, N, _ptr(y), _ptr(mx), _ptr(sm), int(threads))
+    _check(st, "softmax")
+    return {"y": y, "max": mx, "sum": sm}
+
+
+def layer_norm_row_f64(x: np.ndarray, gamma=None, beta=None, eps: float = 1e-5) -> np.ndarray:
+    """LayerNorm forward of one fp64 row (for derivative checks)."""
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    g = None if gamma is None else np.ascontiguousarray(gamma, dtype=np.float64)
+    b = None if beta is None else np.ascontiguousarray(beta, dtype=np.float64)
+    y = np.empty_like(a)
+    _check(_load().orc_layer_norm_row_f64(_ptr(a), _ptr(g), _ptr(b), a.size, float(eps), _ptr(y)), "ln row")
+    return y
+
+
+def rms_norm_row_f64(x: np.ndarray, weight=None, eps: float = 1e-6) -> np.ndarray:
+    """RMSNorm forward of one fp64 row (for derivative checks)."""
+    a = np.ascontiguousarray(x, dtype=np.float64)
+    w = None if weight is None else np.ascontiguousarray(weight, dtype=np.float64)
+    y = np.empty_like(a)
+    _check(_load().orc_rms_norm_row_f64(_ptr(a), _ptr(w), a.size, float(eps), _ptr(y)), "rms row")
+    return y
+
+
+def _stats_f32(a):
+    if a is None:
+        return None
+    if isinstance(a, torch.Tensor):
+        a = a.detach().cpu().contiguous().numpy()
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.float32:
+        raise TypeError("statistics must be float32")
+    return a
+
+
+def layer_norm_backward(dy, x, gamma=None, mean=None, rstd=None, eps: float = 1e-5) -> Dict[str, np.ndarray]:
+    """LayerNorm backward; mean / rstd (float32 [rows]) are the forward's statistics, used
+    exactly as given (both None: recomputed in fp64). Returns fp64 {"dx", "dgamma", "dbeta"}."""
+    dt = dtype_name(x)
+    rows, N = x.reshape(-1, x.shape[-1]).shape
+    xb, db = _bits(x, dt), _bits(dy, dt)
+    gb = None if gamma is None else _bits(gamma, dt)
+    m, r = _stats_f32(mean), _stats_f32(rstd)
+    dx = np.empty((rows, N), dtype=np.float64)
+    dg = np.empty(N, dtype=np.float64)
+    dbeta = np.empty(N, dtype=np.float64)
+    st = _load().orc_layer_norm_backward(DTYPE_CODE[dt], _ptr(db), _ptr(xb), _ptr(gb), _ptr(m), _ptr(r), rows, N,
+                                         float(eps), _ptr(dx), _ptr(dg), _ptr(dbeta))
+    _check(st, "layer_norm_backward")
+    return {"dx": dx, "dgamma": dg, "dbeta": dbeta}
+
+
+def rms_norm_backward(dy, x, weight=None, rstd=None, eps: float = 1e-6) -> Dict[str, np.ndarray]:
+    """RMSNorm backward; rstd (float32 [rows]) from the forward, used exactly (None:
+    recomputed in fp64). Returns fp64 {"dx", "dweight"}."""
+    dt = dtype_name(x)
+    rows, N = x.reshape(-1, x.shape[-1]).shape
+    xb, db = _bits(x, dt), _bits(dy, dt)
+    wb = None if weight is None else _bits(weight, dt)
+    r = _stats_f32(rstd)
+    dx = np.empty((rows, N), dtype=np.float64)
+    dw = np.empty(N, dtype=np.float64)
+    st = _load().orc_rms_norm_backward(DTYPE_CODE[dt], _ptr(db), _ptr(xb), _ptr(wb), _ptr(r), rows, N, float(eps),
+                                       _ptr(dx), _ptr(dw))
+    _check(st, "rms_norm_backward")
+    return {"dx": dx, "dweight": dw}

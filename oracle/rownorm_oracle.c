@@ -1,6 +1,7 @@
 /*
  * rownorm_oracle.c -- plain, slow, obviously correct fp64 CPU reference for row-wise
- * LayerNorm, RMSNorm and fused residual-add + RMSNorm.
+ * LayerNorm, RMSNorm, fused residual-add + RMSNorm / + LayerNorm, softmax, and the
+ * backward passes of LayerNorm and RMSNorm.
  *
  * TEST INFRASTRUCTURE. Only the tests, the smoke check and the benchmark's CPU-baseline
  * leg may load this library. The GPU product path never calls it, links it or shares
@@ -26,6 +27,12 @@
  *   [LLM]   "LayerNorm vs RMSNorm in LLM inference engines" (lpnh.cn/news/2853107),
  *           section 2.1 (y = gamma * (x - mean) / sqrt(var + eps) + beta;
  *           y = gamma * x / sqrt(mean(x^2) + eps)).
+ *   [SMAX]  the same "05 LLM Ops" lesson, section 1 "Softmax" (softmax(x_i) =
+ *           exp(x_i - m) / sum_j exp(x_j - m), m = max x) and "Online Softmax denominator
+ *           correction" (running max and denominator, rescaled by exp(m_old - m_new)).
+ *   [BN]    "BatchNorm CUDA implementation" (jianying88.com/news/30214), section 3.1:
+ *           gradients of a normalization by the chain rule (d xhat = dy * gamma, then
+ *           through the mean and the variance), dbeta = sum dy, dgamma = sum dy * xhat.
  *
  * Readings where the pages are silent (each is also listed in the design notes):
  *   - variance is the biased 1/N form; eps is added inside the square root;
@@ -36,7 +43,10 @@
  *
  * Pins: tests/test_oracle.py checks this file against exact rational arithmetic on tiny
  * rows, torch's CPU float64 layer_norm / rms_norm, closed forms for N = 1 and N = 2, the
- * invariants of the definitions, and (for the codec) every fp16 / bf16 bit pattern.
+ * invariants of the definitions, and (for the codec) every fp16 / bf16 bit pattern;
+ * softmax against 50-digit decimal arithmetic, scipy's float64 softmax and the logistic
+ * closed form; the backward passes against central differences of this file's own fp64
+ * forward rows, torch's float64 autograd, and the orthogonality invariants of dx.
  */
 #include <math.h>
 #include <pthread.h>
@@ -48,7 +58,7 @@
 enum { ORC_F32 = 0, ORC_F16 = 1, ORC_BF16 = 2 };
 
 /* Error codes. */
-enum { ORC_OK = 0, ORC_EARG = 1, ORC_EWELFORD = 2, ORC_ENOMEM = 3 };
+enum { ORC_OK = 0, ORC_EARG = 1, ORC_EWELFORD = 2, ORC_ENOMEM = 3, ORC_EONLINE = 4 };
 
 /* ---------------------------------------------------------------------------------- */
 /* IEEE binary formats, from their definition: 1 sign bit, `e` exponent bits with bias */
@@ -202,8 +212,10 @@ static int variances_agree(double var_tp, double var_w, double mean) {
 /* Per-row operations.                                                                 */
 /* ---------------------------------------------------------------------------------- */
 
+enum { OP_LN = 0, OP_RMS = 1, OP_FUSED_RMS = 2, OP_FUSED_LN = 3, OP_SOFTMAX = 4 };
+
 typedef struct {
-    int op; /* 0 = LayerNorm, 1 = RMSNorm, 2 = fused add + RMSNorm */
+    int op; /* OP_LN, OP_RMS, OP_FUSED_RMS, OP_FUSED_LN, OP_SOFTMAX */
     int dtype;
     const void* x;
     const void* residual;
@@ -212,8 +224,8 @@ typedef struct {
     int64_t rows, N;
     double eps;
     double* y;            /* [rows, N] fp64, nullable */
-    double* mean;         /* [rows], nullable (LayerNorm) */
-    double* rstd;         /* [rows], nullable */
+    double* mean;         /* [rows], nullable (LayerNorm); softmax: the row maximum */
+    double* rstd;         /* [rows], nullable; softmax: the row's sum of exp(x - max) */
     void* residual_out;   /* [rows, N] I/O dtype, nullable (fused) */
     int64_t r0, r1;
     int status;
@@ -256,14 +268,47 @@ static void rms_row(const job_t* jb, const double* xr, const double* w, int64_t 
     }
 }
 
+
+/* Softmax of one row ([SMAX] section 1): m = max_j x_j, d = sum_j exp(x_j - m),
+ * y_j = exp(x_j - m) / d. Independently, the single-pass online form of the same section
+ * ("denominator correction"): a running maximum m_k and denominator d_k, where a new
+ * element x_k gives m_k = max(m_{k-1}, x_k) and d_k = d_{k-1} * exp(m_{k-1} - m_k) +
+ * exp(x_k - m_k). Both must give the same maximum and, up to fp64 rounding, the same
+ * denominator, or the oracle refuses to answer. Rows are expected to hold finite values. */
+static int softmax_row(const job_t* jb, const double* xr, int64_t r) {
+    const int64_t N = jb->N;
+    double m = xr[0];
+    for (int64_t j = 1; j < N; ++j)
+        if (xr[j] > m) m = xr[j];
+    double d = 0.0;
+    for (int64_t j = 0; j < N; ++j) d += exp(xr[j] - m);
+
+    double mo = xr[0], dn = 1.0; /* online: after the first element */
+    for (int64_t k = 1; k < N; ++k) {
+        const double mk = xr[k] > mo ? xr[k] : mo;
+        dn = dn * exp(mo - mk) + exp(xr[k] - mk);
+        mo = mk;
+    }
+    if (mo != m || !(fabs(dn - d) <= 1e-12 * d)) return ORC_EONLINE;
+
+    if (jb->mean) jb->mean[r] = m;
+    if (jb->rstd) jb->rstd[r] = d;
+    if (jb->y) {
+        double* yr = jb->y + r * N;
+        for (int64_t j = 0; j < N; ++j) yr[j] = exp(xr[j] - m) / d;
+    }
+    return ORC_OK;
+}
+
 static void* run_rows(void* arg) {
     job_t* jb = (job_t*)arg;
     const int64_t N = jb->N;
     double* xr = (double*)malloc(sizeof(double) * (size_t)N);
-    double* rr = jb->op == 2 ? (double*)malloc(sizeof(double) * (size_t)N) : NULL;
+    const int fused = jb->op == OP_FUSED_RMS || jb->op == OP_FUSED_LN;
+    double* rr = fused ? (double*)malloc(sizeof(double) * (size_t)N) : NULL;
     double* g = jb->gamma ? (double*)malloc(sizeof(double) * (size_t)N) : NULL;
     double* b = jb->beta ? (double*)malloc(sizeof(double) * (size_t)N) : NULL;
-    if (!xr || (jb->op == 2 && !rr) || (jb->gamma && !g) || (jb->beta && !b)) {
+    if (!xr || (fused && !rr) || (jb->gamma && !g) || (jb->beta && !b)) {
         jb->status = ORC_ENOMEM;
         goto done;
     }
@@ -271,24 +316,27 @@ static void* run_rows(void* arg) {
     if (b) orc_decode_array(jb->dtype, jb->beta, b, N);
     for (int64_t r = jb->r0; r < jb->r1; ++r) {
         orc_decode_array(jb->dtype, (const char*)jb->x + r * N * dtype_size(jb->dtype), xr, N);
-        if (jb->op == 0) {
-            int st = ln_row(jb, xr, g, b, r);
-            if (st != ORC_OK) {
-                jb->status = st;
-                goto done;
-            }
-        } else if (jb->op == 1) {
-            rms_row(jb, xr, g, r);
-        } else {
+        if (fused) {
             /* Fused ([FUSED] sections 0.3 and 3.2): residual_out = x + residual, the exact
-             * sum rounded once to the I/O dtype; the RMSNorm uses that rounded value. */
+             * sum rounded once to the I/O dtype; the normalization uses that rounded value. */
             orc_decode_array(jb->dtype, (const char*)jb->residual + r * N * dtype_size(jb->dtype), rr, N);
             for (int64_t j = 0; j < N; ++j) {
                 const uint32_t t = orc_encode(jb->dtype, xr[j] + rr[j]);
                 if (jb->residual_out) store_elem(jb->dtype, jb->residual_out, r * N + j, t);
                 xr[j] = orc_decode(jb->dtype, t);
             }
+        }
+        int st = ORC_OK;
+        if (jb->op == OP_LN || jb->op == OP_FUSED_LN) {
+            st = ln_row(jb, xr, g, b, r);
+        } else if (jb->op == OP_SOFTMAX) {
+            st = softmax_row(jb, xr, r);
+        } else {
             rms_row(jb, xr, g, r);
+        }
+        if (st != ORC_OK) {
+            jb->status = st;
+            goto done;
         }
     }
 done:
@@ -303,7 +351,7 @@ done:
 static int run_job(const job_t* proto, int nthreads) {
     if (proto->rows < 0 || proto->N <= 0 || !proto->x || !(proto->eps >= 0.0)) return ORC_EARG;
     if (fmt_bits(proto->dtype, &(int){0}, &(int){0})) return ORC_EARG;
-    if (proto->op == 2 && !proto->residual) return ORC_EARG;
+    if ((proto->op == OP_FUSED_RMS || proto->op == OP_FUSED_LN) && !proto->residual) return ORC_EARG;
     if (proto->rows == 0) return ORC_OK;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > proto->rows) nthreads = (int)proto->rows;
@@ -342,7 +390,7 @@ static int run_job(const job_t* proto, int nthreads) {
 int orc_layer_norm(int dtype, const void* x, const void* gamma, const void* beta, int64_t rows,
                    int64_t N, double eps, double* y, double* mean, double* rstd, int nthreads) {
     job_t jb = {0};
-    jb.op = 0; jb.dtype = dtype; jb.x = x; jb.gamma = gamma; jb.beta = beta;
+    jb.op = OP_LN; jb.dtype = dtype; jb.x = x; jb.gamma = gamma; jb.beta = beta;
     jb.rows = rows; jb.N = N; jb.eps = eps; jb.y = y; jb.mean = mean; jb.rstd = rstd;
     return run_job(&jb, nthreads);
 }
@@ -351,7 +399,7 @@ int orc_layer_norm(int dtype, const void* x, const void* gamma, const void* beta
 int orc_rms_norm(int dtype, const void* x, const void* weight, int64_t rows, int64_t N, double eps,
                  double* y, double* rstd, int nthreads) {
     job_t jb = {0};
-    jb.op = 1; jb.dtype = dtype; jb.x = x; jb.gamma = weight;
+    jb.op = OP_RMS; jb.dtype = dtype; jb.x = x; jb.gamma = weight;
     jb.rows = rows; jb.N = N; jb.eps = eps; jb.y = y; jb.rstd = rstd;
     return run_job(&jb, nthreads);
 }
@@ -361,7 +409,166 @@ int orc_fused_add_rms_norm(int dtype, const void* x, const void* residual, const
                            int64_t rows, int64_t N, double eps, double* y, void* residual_out,
                            double* rstd, int nthreads) {
     job_t jb = {0};
-    jb.op = 2; jb.dtype = dtype; jb.x = x; jb.residual = residual; jb.gamma = weight;
+    jb.op = OP_FUSED_RMS; jb.dtype = dtype; jb.x = x; jb.residual = residual; jb.gamma = weight;
     jb.rows = rows; jb.N = N; jb.eps = eps; jb.y = y; jb.residual_out = residual_out; jb.rstd = rstd;
     return run_job(&jb, nthreads);
+}
+
+
+/* Fused residual add + LayerNorm: residual_out = round(x + residual) as for the fused
+ * RMSNorm, then the LayerNorm of that rounded row (the pre-norm residual path of [FUSED]
+ * section 2 with the normalization of [WALK] section 1). */
+int orc_fused_add_layer_norm(int dtype, const void* x, const void* residual, const void* gamma,
+                             const void* beta, int64_t rows, int64_t N, double eps, double* y,
+                             void* residual_out, double* mean, double* rstd, int nthreads) {
+    job_t jb = {0};
+    jb.op = OP_FUSED_LN; jb.dtype = dtype; jb.x = x; jb.residual = residual; jb.gamma = gamma;
+    jb.beta = beta; jb.rows = rows; jb.N = N; jb.eps = eps; jb.y = y; jb.residual_out = residual_out;
+    jb.mean = mean; jb.rstd = rstd;
+    return run_job(&jb, nthreads);
+}
+
+/* Row-wise softmax over x[rows, N]; y fp64 [rows, N], row_max and row_sum [rows] (the
+ * maximum and the sum of exp(x - max)), each nullable. */
+int orc_softmax(int dtype, const void* x, int64_t rows, int64_t N, double* y, double* row_max,
+                double* row_sum, int nthreads) {
+    job_t jb = {0};
+    jb.op = OP_SOFTMAX; jb.dtype = dtype; jb.x = x; jb.rows = rows; jb.N = N; jb.y = y;
+    jb.mean = row_max; jb.rstd = row_sum;
+    return run_job(&jb, nthreads);
+}
+
+/* fp64 rows, for derivative checks: the forward formulas above applied to one row of
+ * doubles (gamma / beta nullable). */
+int orc_layer_norm_row_f64(const double* x, const double* gamma, const double* beta, int64_t N,
+                           double eps, double* y) {
+    job_t jb = {0};
+    jb.op = OP_LN; jb.N = N; jb.eps = eps; jb.y = y;
+    if (N <= 0) return ORC_EARG;
+    return ln_row(&jb, x, gamma, beta, 0);
+}
+
+int orc_rms_norm_row_f64(const double* x, const double* weight, int64_t N, double eps, double* y) {
+    job_t jb = {0};
+    jb.op = OP_RMS; jb.N = N; jb.eps = eps; jb.y = y;
+    if (N <= 0) return ORC_EARG;
+    rms_row(&jb, x, weight, 0);
+    return ORC_OK;
+}
+
+/* ---------------------------------------------------------------------------------- */
+/* Backward passes.                                                                    */
+/* ---------------------------------------------------------------------------------- */
+
+/* LayerNorm backward over rows ([BN] section 3.1, with the reduction running along a row
+ * instead of over a channel). With xhat_j = (x_j - mean) * rstd and y_j = xhat_j * gamma_j +
+ * beta_j, the chain rule gives, for one row:
+ *   g_j     = dy_j * gamma_j                        (gradient reaching xhat_j)
+ *   dx_j    = rstd * (g_j - (1/N) sum_k g_k - xhat_j * (1/N) sum_k g_k * xhat_k)
+ * and, over all rows, dgamma_j = sum_r dy_rj * xhat_rj, dbeta_j = sum_r dy_rj.
+ * The gamma factor sits inside the row sums because gamma varies along the row (for a
+ * batch normalization it is constant over the reduced set and factors out).
+ * mean / rstd: the forward's fp32 statistics when given (their exact values are used), else
+ * computed here in fp64 (two-pass). Outputs are fp64 and each nullable; the column sums run
+ * sequentially over the rows in order. */
+int orc_layer_norm_backward(int dtype, const void* dy, const void* x, const void* gamma,
+                            const float* mean_in, const float* rstd_in, int64_t rows, int64_t N,
+                            double eps, double* dx, double* dgamma, double* dbeta) {
+    if (rows < 0 || N <= 0 || !dy || !x || !(eps >= 0.0)) return ORC_EARG;
+    if (fmt_bits(dtype, &(int){0}, &(int){0})) return ORC_EARG;
+    const size_t n = (size_t)N;
+    double* xr = (double*)malloc(sizeof(double) * n);
+    double* dr = (double*)malloc(sizeof(double) * n);
+    double* g = (double*)malloc(sizeof(double) * n);
+    int st = ORC_OK;
+    if (!xr || !dr || !g) {
+        st = ORC_ENOMEM;
+        goto out;
+    }
+    for (int64_t j = 0; j < N; ++j) g[j] = gamma ? load_elem(dtype, gamma, j) : 1.0;
+    if (dgamma) memset(dgamma, 0, sizeof(double) * n);
+    if (dbeta) memset(dbeta, 0, sizeof(double) * n);
+    for (int64_t r = 0; r < rows; ++r) {
+        orc_decode_array(dtype, (const char*)x + r * N * dtype_size(dtype), xr, N);
+        orc_decode_array(dtype, (const char*)dy + r * N * dtype_size(dtype), dr, N);
+        double mean, rstd;
+        if (mean_in && rstd_in) {
+            mean = (double)mean_in[r];
+            rstd = (double)rstd_in[r];
+        } else {
+            const double var = orc_twopass_var(xr, N, &mean);
+            rstd = 1.0 / sqrt(var + eps);
+        }
+        double sg = 0.0, sgx = 0.0;
+        for (int64_t j = 0; j < N; ++j) {
+            const double xh = (xr[j] - mean) * rstd;
+            const double gj = dr[j] * g[j];
+            sg += gj;
+            sgx += gj * xh;
+            if (dgamma) dgamma[j] += dr[j] * xh;
+            if (dbeta) dbeta[j] += dr[j];
+        }
+        if (dx) {
+            double* o = dx + r * N;
+            for (int64_t j = 0; j < N; ++j) {
+                const double xh = (xr[j] - mean) * rstd;
+                o[j] = rstd * (dr[j] * g[j] - sg / (double)N - xh * (sgx / (double)N));
+            }
+        }
+    }
+out:
+    free(xr);
+    free(dr);
+    free(g);
+    return st;
+}
+
+/* RMSNorm backward over rows, by the same chain rule: xhat_j = x_j * rstd,
+ * rstd = 1/sqrt((1/N) sum x^2 + eps), y_j = xhat_j * w_j:
+ *   g_j  = dy_j * w_j
+ *   dx_j = rstd * (g_j - xhat_j * (1/N) sum_k g_k * xhat_k)
+ * and dw_j = sum_r dy_rj * xhat_rj. rstd: the forward's fp32 value when given, else fp64. */
+int orc_rms_norm_backward(int dtype, const void* dy, const void* x, const void* weight,
+                          const float* rstd_in, int64_t rows, int64_t N, double eps, double* dx,
+                          double* dweight) {
+    if (rows < 0 || N <= 0 || !dy || !x || !(eps >= 0.0)) return ORC_EARG;
+    if (fmt_bits(dtype, &(int){0}, &(int){0})) return ORC_EARG;
+    const size_t n = (size_t)N;
+    double* xr = (double*)malloc(sizeof(double) * n);
+    double* dr = (double*)malloc(sizeof(double) * n);
+    double* w = (double*)malloc(sizeof(double) * n);
+    int st = ORC_OK;
+    if (!xr || !dr || !w) {
+        st = ORC_ENOMEM;
+        goto out;
+    }
+    for (int64_t j = 0; j < N; ++j) w[j] = weight ? load_elem(dtype, weight, j) : 1.0;
+    if (dweight) memset(dweight, 0, sizeof(double) * n);
+    for (int64_t r = 0; r < rows; ++r) {
+        orc_decode_array(dtype, (const char*)x + r * N * dtype_size(dtype), xr, N);
+        orc_decode_array(dtype, (const char*)dy + r * N * dtype_size(dtype), dr, N);
+        double rstd;
+        if (rstd_in) {
+            rstd = (double)rstd_in[r];
+        } else {
+            double ss = 0.0;
+            for (int64_t j = 0; j < N; ++j) ss += xr[j] * xr[j];
+            rstd = 1.0 / sqrt(ss / (double)N + eps);
+        }
+        double sgx = 0.0;
+        for (int64_t j = 0; j < N; ++j) {
+            const double xh = xr[j] * rstd;
+            sgx += dr[j] * w[j] * xh;
+            if (dweight) dweight[j] += dr[j] * xh;
+        }
+        if (dx) {
+            double* o = dx + r * N;
+            for (int64_t j = 0; j < N; ++j) o[j] = rstd * (dr[j] * w[j] - xr[j] * rstd * (sgx / (double)N));
+        }
+    }
+out:
+    free(xr);
+    free(dr);
+    free(w);
+    return st;
 }

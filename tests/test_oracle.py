@@ -415,3 +415,212 @@ def test_algorithmic_bytes_match_pages_figures():
         else:
             two_kernel = 3 * x_bytes + 2 * e["N"] * 4 + 2 * 2 * e["rows"] * 4
             assert abs(two_kernel / 2 ** 20 - e["total_mib_approx"]) < 1.0
+
+
+# ------------------------------------------------------------------------------------
+# Fused residual add + LayerNorm.
+# ------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+def test_fused_add_layer_norm_semantics(dtype):
+    w = workloads.FUSED_LN.scaled(rows=24, N=512, dtype=dtype)
+    inp = workloads.make_inputs(w)
+    out = oracle.fused_add_layer_norm(inp["x"], inp["residual"], inp["gamma"], inp["beta"], w.eps)
+    td = workloads.TORCH_DTYPES[dtype]
+    # residual_out: the exact sum rounded once (for 16-bit inputs fp32 addition then
+    # rounding is correctly rounded; for fp32 the exact sum is formed in fp64 and rounded).
+    if dtype == "fp32":
+        t = (inp["x"].double() + inp["residual"].double()).float()
+        bits = t.view(torch.int32).numpy().view(np.uint32)
+    else:
+        t = (inp["x"].float() + inp["residual"].float()).to(td)
+        bits = t.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(out["residual_out"], bits)
+    # y, mean, rstd: torch's float64 LayerNorm of the rounded stream
+    ref = F.layer_norm(t.double(), (w.N,), inp["gamma"].double(), inp["beta"].double(), w.eps).numpy()
+    assert np.allclose(out["y"], ref, rtol=1e-12, atol=1e-12)
+    td64 = t.double()
+    assert np.allclose(out["mean"], td64.mean(dim=1).numpy(), rtol=1e-13, atol=1e-13)
+    var = td64.var(dim=1, unbiased=False)
+    assert np.allclose(out["rstd"], (1 / torch.sqrt(var + w.eps)).numpy(), rtol=1e-12)
+    # the plain LayerNorm of the rounded stream is the same computation
+    plain = oracle.layer_norm(t, inp["gamma"], inp["beta"], w.eps)
+    assert np.array_equal(plain["y"], out["y"])
+
+
+def test_fused_add_layer_norm_uses_the_rounded_sum():
+    # bf16: x + residual is not representable; normalizing the unrounded sum differs
+    w = workloads.FUSED_LN.scaled(rows=16, N=256)
+    inp = workloads.make_inputs(w)
+    out = oracle.fused_add_layer_norm(inp["x"], inp["residual"], inp["gamma"], inp["beta"], w.eps)
+    exact = (inp["x"].double() + inp["residual"].double())
+    ref_unrounded = F.layer_norm(exact, (w.N,), inp["gamma"].double(), inp["beta"].double(), w.eps).numpy()
+    assert np.abs(out["y"] - ref_unrounded).max() > 1e-4
+
+
+# ------------------------------------------------------------------------------------
+# Softmax.
+# ------------------------------------------------------------------------------------
+
+def _exact_softmax(xs):
+    getcontext().prec = 50
+    d = [Decimal(v) for v in xs]
+    m = max(d)
+    e = [(v - m).exp() for v in d]
+    s = sum(e)
+    return [float(v / s) for v in e], float(s)
+
+
+@pytest.mark.parametrize("xs", [
+    [0.0], [1.0, 2.0], [-3.5, 0.25, 7.0], [1.0, 1.0, 1.0, 1.0, 1.0],
+    [100.0, -100.0, 0.5, 0.75, -0.125, 3.0, 2.0],
+])
+def test_softmax_matches_50_digit_arithmetic(xs):
+    x = torch.tensor([xs], dtype=torch.float32)
+    out = oracle.softmax(x)
+    ref, s = _exact_softmax(xs)
+    assert np.allclose(out["y"][0], ref, rtol=1e-15, atol=1e-300)
+    assert out["max"][0] == max(xs)
+    assert out["sum"][0] == pytest.approx(s, rel=1e-15)
+
+
+@pytest.mark.parametrize("dtype,rows,N", [("fp32", 8, 4096), ("fp16", 5, 333), ("bf16", 3, 1000)])
+def test_softmax_matches_scipy_float64(dtype, rows, N):
+    from scipy.special import softmax as sp_softmax
+
+    inp = workloads.make_inputs(workloads.SOFTMAX.scaled(rows=rows, N=N, dtype=dtype, seed=5))
+    out = oracle.softmax(inp["x"])
+    ref = sp_softmax(inp["x"].double().numpy(), axis=1)
+    assert np.allclose(out["y"], ref, rtol=1e-13, atol=0)
+    assert np.allclose(out["y"].sum(axis=1), 1.0, rtol=0, atol=1e-14)
+
+
+def test_softmax_closed_forms_and_invariants():
+    # two elements: the logistic function of the difference
+    x = torch.tensor([[2.0, -1.0], [0.0, 0.0], [-5.0, 5.0]], dtype=torch.float32)
+    y = oracle.softmax(x)["y"]
+    d = (x[:, 0] - x[:, 1]).double().numpy()
+    assert np.allclose(y[:, 0], 1 / (1 + np.exp(-d)), rtol=1e-15)
+    # constant rows: exactly 1 / N
+    c = torch.full((3, 12), 7.25)
+    assert np.all(oracle.softmax(c)["y"] == 1.0 / 12)
+    # shift invariance (the shift is exact in fp32 for these dyadic values)
+    z = torch.tensor([[0.5, -2.25, 3.0, 1.0, -0.75]])
+    a = oracle.softmax(z)["y"]
+    b = oracle.softmax(z + 64.0)["y"]
+    assert np.allclose(a, b, rtol=1e-15, atol=0)
+    # order is preserved and every output lies in (0, 1]
+    assert list(np.argsort(a[0])) == list(np.argsort(z[0].numpy()))
+    assert np.all(a > 0) and np.all(a <= 1)
+    # large logits do not overflow: the maximum is subtracted first
+    big = torch.tensor([[1000.0, 999.0, -1000.0]])
+    yb = oracle.softmax(big)["y"][0]
+    assert np.isfinite(yb).all() and yb[0] == pytest.approx(1 / (1 + math.exp(-1)), rel=1e-15)
+
+
+# ------------------------------------------------------------------------------------
+# Backward passes.
+# ------------------------------------------------------------------------------------
+
+def _central_difference(f, x, h):
+    """Gradient of the scalar function f at x by central differences, one coordinate at a time."""
+    g = np.empty_like(x)
+    for j in range(x.size):
+        xp = x.copy(); xp[j] += h
+        xm = x.copy(); xm[j] -= h
+        g[j] = (f(xp) - f(xm)) / (2 * h)
+    return g
+
+
+@pytest.mark.parametrize("N", [1, 2, 7, 40])
+def test_layer_norm_backward_is_the_derivative_of_the_forward(N):
+    rng = np.random.default_rng(N)
+    x = (3.0 + 2.0 * rng.standard_normal(N)).astype(np.float32)
+    g = rng.uniform(0.5, 1.5, N).astype(np.float32)
+    b = (0.1 * rng.standard_normal(N)).astype(np.float32)
+    dy = rng.standard_normal(N).astype(np.float32)
+    eps = 1e-3
+    out = oracle.layer_norm_backward(torch.from_numpy(dy[None]), torch.from_numpy(x[None]), torch.from_numpy(g),
+                                     eps=eps)
+    x64, g64, b64, dy64 = (a.astype(np.float64) for a in (x, g, b, dy))
+    loss = lambda xx: float(np.dot(dy64, oracle.layer_norm_row_f64(xx, g64, b64, eps)))
+    fd = _central_difference(loss, x64, 1e-5)
+    assert np.allclose(out["dx"][0], fd, rtol=1e-6, atol=1e-7)
+    loss_g = lambda gg: float(np.dot(dy64, oracle.layer_norm_row_f64(x64, gg, b64, eps)))
+    assert np.allclose(out["dgamma"], _central_difference(loss_g, g64, 1e-5), rtol=1e-6, atol=1e-7)
+    loss_b = lambda bb: float(np.dot(dy64, oracle.layer_norm_row_f64(x64, g64, bb, eps)))
+    assert np.allclose(out["dbeta"], _central_difference(loss_b, b64, 1e-5), rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("N", [1, 3, 40])
+def test_rms_norm_backward_is_the_derivative_of_the_forward(N):
+    rng = np.random.default_rng(100 + N)
+    x = rng.standard_normal(N).astype(np.float32)
+    w = rng.uniform(0.5, 1.5, N).astype(np.float32)
+    dy = rng.standard_normal(N).astype(np.float32)
+    eps = 1e-3
+    out = oracle.rms_norm_backward(torch.from_numpy(dy[None]), torch.from_numpy(x[None]), torch.from_numpy(w), eps=eps)
+    x64, w64, dy64 = (a.astype(np.float64) for a in (x, w, dy))
+    loss = lambda xx: float(np.dot(dy64, oracle.rms_norm_row_f64(xx, w64, eps)))
+    assert np.allclose(out["dx"][0], _central_difference(loss, x64, 1e-5), rtol=1e-6, atol=1e-7)
+    loss_w = lambda ww: float(np.dot(dy64, oracle.rms_norm_row_f64(x64, ww, eps)))
+    assert np.allclose(out["dweight"], _central_difference(loss_w, w64, 1e-5), rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_layer_norm_backward_matches_torch_autograd_float64(dtype):
+    w = workloads.LN_BWD.scaled(rows=6, N=300, dtype=dtype)
+    inp = workloads.make_inputs(w)
+    out = oracle.layer_norm_backward(inp["dy"], inp["x"], inp["gamma"], eps=w.eps)
+    x = inp["x"].double().requires_grad_(True)
+    g = inp["gamma"].double().requires_grad_(True)
+    b = inp["beta"].double().requires_grad_(True)
+    F.layer_norm(x, (w.N,), g, b, w.eps).backward(inp["dy"].double())
+    assert np.allclose(out["dx"], x.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(out["dgamma"], g.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert np.allclose(out["dbeta"], b.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_rms_norm_backward_matches_torch_autograd_float64():
+    w = workloads.RMS_BWD.scaled(rows=5, N=257)
+    inp = workloads.make_inputs(w)
+    out = oracle.rms_norm_backward(inp["dy"], inp["x"], inp["weight"], eps=w.eps)
+    x = inp["x"].double().requires_grad_(True)
+    wt = inp["weight"].double().requires_grad_(True)
+    F.rms_norm(x, (w.N,), wt, w.eps).backward(inp["dy"].double())
+    assert np.allclose(out["dx"], x.grad.numpy(), rtol=1e-10, atol=1e-12)
+    assert np.allclose(out["dweight"], wt.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_backward_invariants_and_given_statistics():
+    w = workloads.LN_BWD.scaled(rows=8, N=128, dtype="fp32")
+    inp = workloads.make_inputs(w)
+    out = oracle.layer_norm_backward(inp["dy"], inp["x"], inp["gamma"], eps=w.eps)
+    fwd = oracle.layer_norm(inp["x"], inp["gamma"], inp["beta"], w.eps)
+    scale = np.abs(out["dx"]).max()
+    # dx is orthogonal to the constant direction (for any eps) ...
+    assert np.abs(out["dx"].sum(axis=1)).max() < 1e-12 * scale * w.N
+    # ... and, with eps = 0, to xhat: sum_j xhat_j^2 = N exactly cancels the last term
+    z = oracle.layer_norm_backward(inp["dy"], inp["x"], inp["gamma"], eps=0.0)
+    f0 = oracle.layer_norm(inp["x"], None, None, 0.0)
+    xhat = (inp["x"].double().numpy() - f0["mean"][:, None]) * f0["rstd"][:, None]
+    assert np.abs((z["dx"] * xhat).sum(axis=1)).max() < 1e-12 * np.abs(z["dx"]).max() * w.N
+    # with eps > 0 the same sum is rstd * sum(g * xhat) * eps / (var + eps), not zero
+    assert np.abs((out["dx"] * xhat).sum(axis=1)).max() > 1e-9
+    # dbeta: the exact column sums of dy (small-integer multiples of fp32 values)
+    dyf = [[Fraction(float(v)) for v in row] for row in inp["dy"].tolist()]
+    for j in (0, 17, 127):
+        assert out["dbeta"][j] == float(sum(r[j] for r in dyf))
+    # the forward's fp32 statistics, given explicitly, are used as given: the result
+    # moves by about the statistics' rounding, no more
+    given = oracle.layer_norm_backward(inp["dy"], inp["x"], inp["gamma"],
+                                       mean=fwd["mean"].astype(np.float32), rstd=fwd["rstd"].astype(np.float32),
+                                       eps=w.eps)
+    d = np.abs(given["dx"] - out["dx"]).max()
+    assert 0 < d < 1e-5 * scale
+    # RMSNorm with eps = 0: dx is orthogonal to x
+    rw = workloads.RMS_BWD.scaled(rows=4, N=96, dtype="fp32")
+    ri = workloads.make_inputs(rw)
+    ro = oracle.rms_norm_backward(ri["dy"], ri["x"], ri["weight"], eps=0.0)
+    xs = ri["x"].double().numpy()
+    assert np.abs((ro["dx"] * xs).sum(axis=1)).max() < 1e-12 * np.abs(ro["dx"]).max() * rw.N * np.abs(xs).max()

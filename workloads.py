@@ -50,7 +50,7 @@ class Workload:
     """
 
     name: str
-    op: str  # "ln", "rms", "fused_add_rms"
+    op: str  # "ln", "rms", "fused_add_rms", "fused_add_ln", "softmax", "ln_bwd", "rms_bwd"
     dtype: str  # "fp32", "fp16", "bf16"
     rows: int
     N: int
@@ -64,6 +64,7 @@ class Workload:
     std_lo: float = 1.0
     std_hi: float = 1.0
     residual_scale: float = 2.0
+    dy_scale: float = 1.0  # backward: dy ~ N(0, dy_scale^2)
     param_lo: float = 0.5  # gamma / weight ~ U(param_lo, param_hi)
     param_hi: float = 1.5
     beta_scale: float = 0.1  # beta ~ N(0, beta_scale^2)
@@ -100,6 +101,23 @@ C5 = Workload("C5_ln_bf16_4096x16384", "ln", "bf16", 4096, 16384, 1e-5, 1005,
 
 CONFIGS = (C1, C2, C3, C4_FP16, C4_BF16, C5)
 
+# Fused residual add + LayerNorm: the fused config's shape and residual, LayerNorm
+# parameters and the row-wise input spread of the 16384-wide config.
+FUSED_LN = Workload("fused_ln_bf16_256x4096", "fused_add_ln", "bf16", 256, 4096, 1e-5, 1021,
+                    x_dist="row_mean_std", mean_range=10.0, std_lo=0.5, std_hi=4.0, residual_scale=2.0)
+FUSED_LN_8192 = FUSED_LN.scaled(rows=8192, seed=1121, name="fused_ln_bf16_8192x4096")
+
+# Softmax: the LLM-ops lesson's measured shape (batch 128 x sequence 4096, fp32 I/O) with
+# logits x = 2 z, and a 32M-element version of it for bandwidth.
+SOFTMAX = Workload("softmax_fp32_128x4096", "softmax", "fp32", 128, 4096, 0.0, 1031, x_scale=2.0)
+SOFTMAX_8192 = SOFTMAX.scaled(rows=8192, seed=1131, name="softmax_fp32_8192x4096")
+
+# Backward passes: LayerNorm over the 16384-wide config's rows, RMSNorm over the RMSNorm
+# config's rows; dy ~ N(0, 1).
+LN_BWD = Workload("ln_bwd_bf16_4096x16384", "ln_bwd", "bf16", 4096, 16384, 1e-5, 1041,
+                  x_dist="row_mean_std", mean_range=10.0, std_lo=0.5, std_hi=4.0)
+RMS_BWD = Workload("rms_bwd_fp16_2048x4096", "rms_bwd", "fp16", 2048, 4096, 1e-6, 1043)
+
 # Larger fused add+RMSNorm shape with the fused config's distributions: 8192 x 4096 is
 # 32M elements, past the 8M-element size where the bandwidth target applies.
 FUSED_8192 = C4_FP16.scaled(rows=8192, seed=1104, name="fused_fp16_8192x4096")
@@ -112,12 +130,15 @@ def _to_dtype(a: np.ndarray, dtype: str) -> torch.Tensor:
 def make_inputs(w: Workload) -> Dict[str, torch.Tensor]:
     """Draw the inputs of ``w`` as CPU tensors in the I/O dtype.
 
-    Keys: ``x`` [rows, N]; ``residual`` [rows, N] (fused op only); ``gamma`` and
-    ``beta`` [N] (LayerNorm; absent when disabled) or ``weight`` [N] (RMSNorm ops).
+    Keys: ``x`` [rows, N]; ``residual`` [rows, N] (fused ops); ``dy`` [rows, N]
+    (backward ops); ``gamma`` and ``beta`` [N] (LayerNorm ops; absent when disabled) or
+    ``weight`` [N] (RMSNorm ops); softmax has no parameters.
     """
     rng = np.random.Generator(np.random.PCG64(w.seed))
     out: Dict[str, torch.Tensor] = {}
-    if w.op == "ln":
+    if w.op == "softmax":
+        pass
+    elif w.op in ("ln", "fused_add_ln", "ln_bwd"):
         g = rng.uniform(w.param_lo, w.param_hi, size=w.N)
         b = w.beta_scale * rng.standard_normal(size=w.N)
         if w.with_gamma:
@@ -145,8 +166,10 @@ def make_inputs(w: Workload) -> Dict[str, torch.Tensor]:
     else:
         raise ValueError(f"unknown x_dist {w.x_dist!r}")
     out["x"] = _to_dtype(x, w.dtype)
-    if w.op == "fused_add_rms":
+    if w.op in ("fused_add_rms", "fused_add_ln"):
         out["residual"] = _to_dtype(w.residual_scale * rng.standard_normal(size=shape), w.dtype)
+    if w.op in ("ln_bwd", "rms_bwd"):
+        out["dy"] = _to_dtype(w.dy_scale * rng.standard_normal(size=shape), w.dtype)
     return out
 
 
@@ -157,7 +180,10 @@ def algorithmic_bytes(op: str, rows: int, N: int, elem_bytes: int, with_params: 
     LayerNorm: read x, write y, read gamma and beta once (+ 8 bytes per row for fp32
     mean and rstd when requested). RMSNorm: read x, write y, read weight once (+ 4
     bytes per row for rstd). Fused add + RMSNorm: read x and residual, write y and
-    residual_out, read weight once (+ 4 bytes per row for rstd).
+    residual_out, read weight once (+ 4 bytes per row for rstd). Fused add + LayerNorm:
+    the same with gamma and beta (+ 8 bytes per row). Softmax: read x, write y.
+    LayerNorm backward: read x, dy, gamma, mean and rstd, write dx, dgamma and dbeta;
+    RMSNorm backward: read x, dy, weight and rstd, write dx and dweight.
     """
     elems = rows * N * elem_bytes
     if op == "ln":
@@ -167,4 +193,12 @@ def algorithmic_bytes(op: str, rows: int, N: int, elem_bytes: int, with_params: 
         return 2 * elems + (N * elem_bytes if with_params else 0) + (4 * rows if with_stats else 0)
     if op == "fused_add_rms":
         return 4 * elems + (N * elem_bytes if with_params else 0) + (4 * rows if with_stats else 0)
+    if op == "fused_add_ln":
+        return 4 * elems + (2 * N * elem_bytes if with_params else 0) + (8 * rows if with_stats else 0)
+    if op == "softmax":
+        return 2 * elems
+    if op == "ln_bwd":
+        return 3 * elems + (3 if with_params else 2) * N * elem_bytes + 8 * rows
+    if op == "rms_bwd":
+        return 3 * elems + (2 if with_params else 1) * N * elem_bytes + 4 * rows
     raise ValueError(op)
