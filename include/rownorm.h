@@ -1,27 +1,34 @@
 /*
  * rownorm.h -- C ABI of the MI355X (gfx950) row-wise normalization library, librownorm.so.
  *
- * Three forward operations over a dense, row-major [rows, N] tensor, each row normalized
- * on its own:
+ * Forward operations over a row-major [rows, N] tensor, each row processed on its own:
  *
- *   ln_forward          LayerNorm. mean = (1/N) sum x_j, var = (1/N) sum (x_j - mean)^2
- *                       (biased), rstd = 1/sqrt(var + eps), y_j = (x_j - mean) * rstd *
- *                       gamma_j + beta_j. Defined in the LayerNorm CUDA walkthrough
- *                       (lpnh.cn/news/2756757), section 1; the same formula is section 2.1
- *                       of "LayerNorm vs RMSNorm in LLM inference engines"
- *                       (lpnh.cn/news/2853107) and section 2 of the "05 LLM Ops" lesson
- *                       (smarter.xin/posts/cb29461c).
- *   rms_norm            RMSNorm. rstd = 1/sqrt((1/N) sum x_j^2 + eps), y_j = x_j * rstd * w_j.
- *                       Defined in "CUDA fused RMSNorm kernel"
- *                       (diycv.top/archives/cuda-fused-rmsnorm-kernel), sections 0.3 and 2.
- *   fused_add_rms_norm  residual_out = x + residual, rounded once to the I/O dtype; then
- *                       RMSNorm of that rounded value, which is also what gets squared.
- *                       Same article, sections 2 and 3.2.
+ *   ln_forward            LayerNorm. mean = (1/N) sum x_j, var = (1/N) sum (x_j - mean)^2
+ *                         (biased), rstd = 1/sqrt(var + eps), y_j = (x_j - mean) * rstd *
+ *                         gamma_j + beta_j. Defined in the LayerNorm CUDA walkthrough
+ *                         (lpnh.cn/news/2756757), section 1; the same formula is section 2.1
+ *                         of "LayerNorm vs RMSNorm in LLM inference engines"
+ *                         (lpnh.cn/news/2853107) and section 2 of the "05 LLM Ops" lesson
+ *                         (smarter.xin/posts/cb29461c).
+ *   rms_norm              RMSNorm. rstd = 1/sqrt((1/N) sum x_j^2 + eps), y_j = x_j * rstd * w_j.
+ *                         Defined in "CUDA fused RMSNorm kernel"
+ *                         (diycv.top/archives/cuda-fused-rmsnorm-kernel), sections 0.3 and 2.
+ *   fused_add_rms_norm    residual_out = x + residual, rounded once to the I/O dtype; then
+ *                         RMSNorm of that rounded value, which is also what gets squared.
+ *                         Same article, sections 2 and 3.2.
+ *   fused_add_layer_norm  the same residual add, then LayerNorm of the rounded value (the
+ *                         pre-norm residual path of the same article, section 2, with the
+ *                         walkthrough's LayerNorm).
+ *   softmax_forward       y_j = exp(x_j - m) / sum_k exp(x_k - m), m = max_k x_k ("05 LLM Ops"
+ *                         lesson, section 1 "Softmax"; the per-part (max, sum) pairs are
+ *                         merged with the rescaling of its "Online Softmax" sections).
  *
  * Conventions shared by every entry point:
  *   - Pointers are DEVICE pointers (HIP device memory of the current device). x, residual,
- *     gamma / beta / weight, y and residual_out hold `dtype` elements; mean and rstd are
- *     fp32. Row stride is N elements (dense rows). gamma / beta / weight have N elements.
+ *     gamma / beta / weight, y and residual_out hold `dtype` elements; mean and rstd (softmax:
+ *     row_max and row_sum) are fp32. Rows are dense (stride N elements) except through
+ *     rn_forward_ex, which takes a row stride per [rows, N] tensor. gamma / beta / weight
+ *     have N elements.
  *   - Arithmetic is fp32 for every dtype: fp16 / bf16 inputs are widened exactly, outputs
  *     are rounded once (round-to-nearest-even) to `dtype`.
  *   - The caller owns every buffer. The library never allocates, frees or synchronizes;
@@ -32,15 +39,19 @@
  *   - Errors are reported by the return value (an rn_status). Argument errors are detected
  *     on the host before anything is enqueued, so an error leaves every output untouched.
  *   - rows == 0 is a successful no-op.
- *   - Aliasing: an output may be the exact same buffer as an input of the same shape
- *     (in place: y == x, residual_out == residual, residual_out == x, y == residual).
- *     Any other overlap between an output and any other buffer is RN_ERR_ALIAS.
+ *   - Aliasing: an output may be the exact same buffer as an input of the same shape and
+ *     row stride (in place: y == x, residual_out == residual, residual_out == x,
+ *     y == residual). Any other overlap between an output and any other buffer is
+ *     RN_ERR_ALIAS (also when strided rows would interleave without touching: the check is
+ *     on address ranges).
  *   - Every pointer must be aligned to its element size (RN_ERR_ALIGN otherwise). When N *
- *     sizeof(dtype) is a multiple of 16 and every [rows, N] / [N] pointer is 16-byte aligned,
- *     the vectorized kernels run: a row is held in registers by one 64-lane wavefront (rows
- *     of up to 4 KiB, or 16 KiB when forced) or by a group of up to 16 wavefronts (rows of up
- *     to 64 KiB: 16384 fp32 or 32768 fp16 / bf16 elements). Otherwise, and for longer rows,
- *     a slower general kernel computes the same result.
+ *     sizeof(dtype) and every row stride in bytes are multiples of 16 and every [rows, N] /
+ *     [N] pointer is 16-byte aligned, the vectorized kernels run: a row is held in registers
+ *     by one 64-lane wavefront (rows of up to 4 KiB, or 16 KiB when forced) or by a group of
+ *     up to 16 wavefronts (rows of up to 64 KiB: 16384 fp32 or 32768 fp16 / bf16 elements).
+ *     Otherwise rows of up to 16384 elements are held in registers one element per slot
+ *     (the element kernel, still one read of x), and longer rows take a general kernel
+ *     that reads the row up to three times.
  *   - Launches use the current HIP device (the device of the buffers and of `stream`). The
  *     first call of a kernel configuration on a device queries its occupancy once.
  */
@@ -75,11 +86,25 @@ typedef enum rn_variant {
     RN_VARIANT_AUTO = 0,      /* choose from N, dtype, alignment and rows (what the plain entry points do) */
     RN_VARIANT_WAVE = 1,      /* one 64-lane wavefront per row, row held in VGPRs (rows up to 16 KiB) */
     RN_VARIANT_WORKGROUP = 2, /* 2-16 wavefronts per row, partial moments combined in LDS (rows up to 64 KiB) */
-    RN_VARIANT_GENERAL = 3    /* any N, any element-aligned pointers; re-reads the row */
+    RN_VARIANT_GENERAL = 3,   /* any N, any element-aligned pointers; re-reads the row */
+    RN_VARIANT_ELEMENT = 4    /* rows up to 16384 elements held in VGPRs one element per slot;
+                                 any element-aligned pointers and strides */
 } rn_variant;
 
-/* Operation codes (for rn_plan). */
-typedef enum rn_op { RN_OP_LAYER_NORM = 0, RN_OP_RMS_NORM = 1, RN_OP_FUSED_ADD_RMS_NORM = 2 } rn_op;
+/* Operation codes (for rn_forward_ex and rn_plan). */
+typedef enum rn_op {
+    RN_OP_LAYER_NORM = 0,
+    RN_OP_RMS_NORM = 1,
+    RN_OP_FUSED_ADD_RMS_NORM = 2,
+    RN_OP_FUSED_ADD_LAYER_NORM = 3,
+    RN_OP_SOFTMAX = 4
+} rn_op;
+
+/* Row strides in elements of the [rows, N] tensors (row r starts at base + r * stride).
+ * 0 means dense (N). A non-zero stride must be >= N. Unused entries are ignored. */
+typedef struct rn_row_strides {
+    int64_t x, residual, y, residual_out;
+} rn_row_strides;
 
 /*
  * LayerNorm forward.
@@ -112,7 +137,42 @@ int rms_norm(const void* x, const void* weight, void* y, float* rstd, int64_t ro
 int fused_add_rms_norm(const void* x, const void* residual, const void* weight, void* y, void* residual_out,
                        float* rstd, int64_t rows, int64_t N, float eps, int dtype, hipStream_t stream);
 
-/* Same as the three entry points above, with the kernel variant forced (RN_VARIANT_AUTO
+/*
+ * Fused residual add + LayerNorm.
+ *   x, residual [rows, N] dtype, required.  gamma, beta [N] dtype, nullable (1 and 0).
+ *   residual_out [rows, N] dtype, required: x + residual rounded to dtype (may be x or
+ *   residual itself).  y [rows, N] dtype, required: LayerNorm(residual_out) (may be x or
+ *   residual itself, but not residual_out).  mean, rstd [rows] fp32, nullable: the
+ *   statistics of residual_out's row.
+ */
+int fused_add_layer_norm(const void* x, const void* residual, const void* gamma, const void* beta, void* y,
+                         void* residual_out, float* mean, float* rstd, int64_t rows, int64_t N, float eps,
+                         int dtype, hipStream_t stream);
+
+/*
+ * Row-wise softmax.
+ *   x [rows, N] dtype, required.  y [rows, N] dtype, required; may be x itself.
+ *   row_max [rows] fp32, nullable: max_j x_j.  row_sum [rows] fp32, nullable:
+ *   sum_j exp(x_j - row_max) (so log-sum-exp = row_max + log(row_sum)).
+ *   Rows are expected to hold finite values.
+ */
+int softmax_forward(const void* x, void* y, float* row_max, float* row_sum, int64_t rows, int64_t N, int dtype,
+                    hipStream_t stream);
+
+/*
+ * Any forward operation with explicit row strides and kernel variant.
+ *   op       an rn_op; arguments the operation does not use are ignored (softmax: gamma,
+ *            beta, residual, residual_out, eps; mean / rstd are row_max / row_sum).
+ *   strides  nullable (all rows dense); see rn_row_strides.
+ *   variant  an rn_variant; RN_VARIANT_AUTO chooses as the plain entry points do. A forced
+ *            variant that cannot run the shape / alignment returns RN_ERR_UNSUPPORTED.
+ * Unknown op codes return RN_ERR_SHAPE.
+ */
+int rn_forward_ex(int op, const void* x, const void* residual, const void* gamma, const void* beta, void* y,
+                  void* residual_out, float* mean, float* rstd, int64_t rows, int64_t N, float eps, int dtype,
+                  const rn_row_strides* strides, int variant, hipStream_t stream);
+
+/* Same as the first three entry points above, with the kernel variant forced (RN_VARIANT_AUTO
  * behaves exactly like the plain entry point). A forced variant that cannot run the given
  * shape / alignment returns RN_ERR_UNSUPPORTED before anything is enqueued. Used by tests
  * to reach every kernel and by benchmarks to compare them. */
@@ -132,7 +192,8 @@ typedef struct rn_plan_info {
     int waves_per_row;     /* wavefronts cooperating on one row */
     int rows_per_block;    /* rows one workgroup processes per iteration */
     int block_threads;     /* workgroup size */
-    int chunks_per_lane;   /* 16-byte chunks each lane holds (vectorized variants) */
+    int chunks_per_lane;   /* 16-byte chunks (vectorized variants) or elements (element variant)
+                              each lane holds */
     int64_t grid_blocks;   /* workgroups launched (persistent launches: an upper bound; the launch
                               caps it at what the current device keeps resident) */
     int exact;             /* 1 if a row is exactly chunks_per_lane passes of its row group */
@@ -143,7 +204,7 @@ typedef struct rn_plan_info {
 
 int rn_plan(int op, const void* x, const void* residual, const void* gamma, const void* beta, const void* y,
             const void* residual_out, const void* mean, const void* rstd, int64_t rows, int64_t N, float eps,
-            int dtype, int variant, rn_plan_info* out);
+            int dtype, int variant, const rn_row_strides* strides, rn_plan_info* out);
 
 /* Static string naming a status code ("RN_OK", ...); "unknown status" otherwise. */
 const char* rn_status_string(int status);

@@ -1,15 +1,18 @@
-"""Row-wise normalization on MI355X (gfx950): LayerNorm, RMSNorm, fused residual-add + RMSNorm.
+"""Row-wise normalization on MI355X (gfx950): LayerNorm, RMSNorm, fused residual-add +
+RMSNorm / + LayerNorm, and softmax.
 
 A thin binding over the C ABI of ``librownorm.so`` (declared in ``include/rownorm.h``):
-it checks devices, contiguity and dtypes, allocates outputs with torch, and passes device
-pointers and torch's current HIP stream. Every step of the computation runs in the HIP
-kernels of the library; there is no other implementation behind these functions. If the
-library is missing, importing this package raises ``ImportError``: build it with
-``python row_wise_normalization_fp32_amd/build.py``.
+it checks devices, layouts and dtypes, allocates outputs with torch, and passes device
+pointers, row strides and torch's current HIP stream. Every step of the computation runs
+in the HIP kernels of the library; there is no other implementation behind these
+functions. If the library is missing, importing this package raises ``ImportError``: build
+it with ``python row_wise_normalization_fp32_amd/build.py``.
 
-Function names follow the C ABI: ``ln_forward``, ``rms_norm``, ``fused_add_rms_norm``.
-Inputs of shape [..., N] are treated as [rows, N] with rows the product of the leading
-dimensions.
+Function names follow the C ABI: ``ln_forward``, ``rms_norm``, ``fused_add_rms_norm``,
+``fused_add_layer_norm``, ``softmax_forward``. Inputs of shape [..., N] are treated as
+[rows, N] with rows the product of the leading dimensions; they must be contiguous, except
+that a 2-D tensor may have a row stride larger than N (e.g. a column slice of a wider
+buffer), which the kernels read and write in place.
 """
 
 from __future__ import annotations
@@ -21,8 +24,8 @@ from typing import Optional, Tuple, Union
 import torch
 
 __all__ = [
-    "ln_forward", "rms_norm", "fused_add_rms_norm", "plan", "RowNormError", "LIB_PATH",
-    "VARIANTS", "STATUS", "version",
+    "ln_forward", "rms_norm", "fused_add_rms_norm", "fused_add_layer_norm", "softmax_forward", "plan",
+    "RowNormError", "LIB_PATH", "VARIANTS", "STATUS", "version",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -34,22 +37,10 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 _vp, _i64, _f32, _ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
-_lib.ln_forward_variant.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci, _vp, _ci]
-_lib.ln_forward_variant.restype = _ci
-_lib.rms_norm_variant.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci, _vp, _ci]
-_lib.rms_norm_variant.restype = _ci
-_lib.fused_add_rms_norm_variant.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci, _vp, _ci]
-_lib.fused_add_rms_norm_variant.restype = _ci
-_lib.ln_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci, _vp]
-_lib.ln_forward.restype = _ci
-_lib.rms_norm.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci, _vp]
-_lib.rms_norm.restype = _ci
-_lib.fused_add_rms_norm.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci, _vp]
-_lib.fused_add_rms_norm.restype = _ci
-_lib.rn_status_string.argtypes = [_ci]
-_lib.rn_status_string.restype = ctypes.c_char_p
-_lib.rn_version.argtypes = []
-_lib.rn_version.restype = _ci
+
+
+class RowStrides(ctypes.Structure):
+    _fields_ = [("x", _i64), ("residual", _i64), ("y", _i64), ("residual_out", _i64)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -58,14 +49,37 @@ class PlanInfo(ctypes.Structure):
                 ("lds_bytes", _ci)]
 
 
+_lib.rn_forward_ex.argtypes = [_ci, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci,
+                               ctypes.POINTER(RowStrides), _ci, _vp]
+_lib.rn_forward_ex.restype = _ci
+_lib.ln_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci, _vp]
+_lib.ln_forward.restype = _ci
+_lib.rms_norm.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci, _vp]
+_lib.rms_norm.restype = _ci
+_lib.fused_add_rms_norm.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci, _vp]
+_lib.fused_add_rms_norm.restype = _ci
+_lib.fused_add_layer_norm.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci, _vp]
+_lib.fused_add_layer_norm.restype = _ci
+_lib.softmax_forward.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _ci, _vp]
+_lib.softmax_forward.restype = _ci
+_lib.ln_forward_variant.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci, _vp, _ci]
+_lib.ln_forward_variant.restype = _ci
+_lib.rms_norm_variant.argtypes = [_vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci, _vp, _ci]
+_lib.rms_norm_variant.restype = _ci
+_lib.fused_add_rms_norm_variant.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci, _vp, _ci]
+_lib.fused_add_rms_norm_variant.restype = _ci
+_lib.rn_status_string.argtypes = [_ci]
+_lib.rn_status_string.restype = ctypes.c_char_p
+_lib.rn_version.argtypes = []
+_lib.rn_version.restype = _ci
 _lib.rn_plan.argtypes = [_ci, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci, _ci,
-                         ctypes.POINTER(PlanInfo)]
+                         ctypes.POINTER(RowStrides), ctypes.POINTER(PlanInfo)]
 _lib.rn_plan.restype = _ci
 
 DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
-VARIANTS = {"auto": 0, "wave": 1, "workgroup": 2, "general": 3}
+VARIANTS = {"auto": 0, "wave": 1, "workgroup": 2, "general": 3, "element": 4}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
-OPS = {"ln": 0, "rms": 1, "fused_add_rms": 2}
+OPS = {"ln": 0, "rms": 1, "fused_add_rms": 2, "fused_add_ln": 3, "softmax": 4}
 STATUS = {0: "RN_OK", 1: "RN_ERR_NULL", 2: "RN_ERR_SHAPE", 3: "RN_ERR_DTYPE", 4: "RN_ERR_ALIAS",
           5: "RN_ERR_UNSUPPORTED", 6: "RN_ERR_HIP", 7: "RN_ERR_ALIGN"}
 
@@ -90,7 +104,17 @@ def _variant(v: Union[str, int]) -> int:
     return VARIANTS[v] if isinstance(v, str) else int(v)
 
 
-def _check_matrix(name: str, t: torch.Tensor, ref: torch.Tensor):
+def _row_stride(name: str, t: torch.Tensor) -> int:
+    """Row stride (elements) of ``t`` seen as [rows, N]: N for contiguous tensors; a 2-D
+    tensor with unit column stride may have a larger row stride."""
+    if t.is_contiguous():
+        return 0
+    if t.dim() == 2 and t.stride(1) == 1 and t.stride(0) >= t.shape[1]:
+        return t.stride(0)
+    raise ValueError(f"{name} must be contiguous, or 2-D with unit column stride (rows may be padded)")
+
+
+def _check_matrix(name: str, t: torch.Tensor, ref: torch.Tensor) -> int:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.device != ref.device:
@@ -99,8 +123,7 @@ def _check_matrix(name: str, t: torch.Tensor, ref: torch.Tensor):
         raise TypeError(f"{name} has dtype {t.dtype}, expected {ref.dtype}")
     if t.shape != ref.shape:
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(ref.shape)}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous (dense rows)")
+    return _row_stride(name, t)
 
 
 def _check_vector(name: str, t: Optional[torch.Tensor], ref: torch.Tensor, dtype=None, n=None):
@@ -125,16 +148,38 @@ def _prep(x: torch.Tensor):
         raise TypeError(f"unsupported dtype {x.dtype}; use float32, float16 or bfloat16")
     if x.dim() < 1:
         raise ValueError("x must have at least one dimension")
-    if not x.is_contiguous():
-        raise ValueError("x must be contiguous (dense rows)")
+    ld = _row_stride("x", x)
     N = x.shape[-1]
     rows = x.numel() // N if N > 0 else 0
-    return rows, N
+    return rows, N, ld
 
 
 def _stream(x: torch.Tensor, stream) -> int:
     s = torch.cuda.current_stream(x.device) if stream is None else stream
     return s.cuda_stream
+
+
+def _stats(name, t, x, rows, want):
+    if not want:
+        return None
+    if t is None:
+        t = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _check_vector(name, t, x, torch.float32, rows)
+    return t
+
+
+def _call(op: str, what: str, x, residual, gamma, beta, y, ro, mean, rstd, rows, N, eps, strides, variant, stream):
+    st_obj = RowStrides(*strides)
+    with torch.cuda.device(x.device):
+        st = _lib.rn_forward_ex(OPS[op], _ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(ro),
+                                _ptr(mean), _ptr(rstd), rows, N, float(eps), DTYPE_CODE[x.dtype],
+                                ctypes.byref(st_obj), _variant(variant), _stream(x, stream))
+    if st != 0:
+        raise RowNormError(st, what)
+
+
+def _new_like(x: torch.Tensor) -> torch.Tensor:
+    return torch.empty(x.shape, dtype=x.dtype, device=x.device)
 
 
 def ln_forward(x: torch.Tensor, gamma: Optional[torch.Tensor] = None, beta: Optional[torch.Tensor] = None,
@@ -147,45 +192,31 @@ def ln_forward(x: torch.Tensor, gamma: Optional[torch.Tensor] = None, beta: Opti
     per-row statistics when ``return_stats`` is true or ``mean`` / ``rstd`` are given.
     ``out`` may be ``x`` itself (in place).
     """
-    rows, N = _prep(x)
+    rows, N, ldx = _prep(x)
     _check_vector("gamma", gamma, x)
     _check_vector("beta", beta, x)
-    y = torch.empty_like(x) if out is None else out
-    _check_matrix("out", y, x)
-    want_stats = return_stats or mean is not None or rstd is not None
-    if want_stats:
-        if mean is None:
-            mean = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-        if rstd is None:
-            rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-        _check_vector("mean", mean, x, torch.float32, rows)
-        _check_vector("rstd", rstd, x, torch.float32, rows)
-    with torch.cuda.device(x.device):
-        st = _lib.ln_forward_variant(_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), rows, N,
-                                     float(eps), DTYPE_CODE[x.dtype], _stream(x, stream), _variant(variant))
-    if st != 0:
-        raise RowNormError(st, "ln_forward")
-    return (y, mean, rstd) if want_stats else y
+    y = _new_like(x) if out is None else out
+    ldy = _check_matrix("out", y, x)
+    want = return_stats or mean is not None or rstd is not None
+    mean = _stats("mean", mean, x, rows, want)
+    rstd = _stats("rstd", rstd, x, rows, want)
+    _call("ln", "ln_forward", x, None, gamma, beta, y, None, mean, rstd, rows, N, eps, (ldx, 0, ldy, 0), variant,
+          stream)
+    return (y, mean, rstd) if want else y
 
 
 def rms_norm(x: torch.Tensor, weight: Optional[torch.Tensor] = None, eps: float = 1e-6, *,
              out: Optional[torch.Tensor] = None, rstd: Optional[torch.Tensor] = None, return_rstd: bool = False,
              variant: Union[str, int] = "auto", stream=None):
     """RMSNorm forward over the last dimension. Returns ``y`` or ``(y, rstd)``."""
-    rows, N = _prep(x)
+    rows, N, ldx = _prep(x)
     _check_vector("weight", weight, x)
-    y = torch.empty_like(x) if out is None else out
-    _check_matrix("out", y, x)
+    y = _new_like(x) if out is None else out
+    ldy = _check_matrix("out", y, x)
     want = return_rstd or rstd is not None
-    if want:
-        if rstd is None:
-            rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-        _check_vector("rstd", rstd, x, torch.float32, rows)
-    with torch.cuda.device(x.device):
-        st = _lib.rms_norm_variant(_ptr(x), _ptr(weight), _ptr(y), _ptr(rstd), rows, N, float(eps),
-                                   DTYPE_CODE[x.dtype], _stream(x, stream), _variant(variant))
-    if st != 0:
-        raise RowNormError(st, "rms_norm")
+    rstd = _stats("rstd", rstd, x, rows, want)
+    _call("rms", "rms_norm", x, None, weight, None, y, None, None, rstd, rows, N, eps, (ldx, 0, ldy, 0), variant,
+          stream)
     return (y, rstd) if want else y
 
 
@@ -198,48 +229,85 @@ def fused_add_rms_norm(x: torch.Tensor, residual: torch.Tensor, weight: Optional
     ``residual_out = x + residual`` rounded to the dtype; ``y = rms_norm(residual_out) *
     weight``. Returns ``(y, residual_out)`` or ``(y, residual_out, rstd)``.
     """
-    rows, N = _prep(x)
-    _check_matrix("residual", residual, x)
+    rows, N, ldx = _prep(x)
+    ldr = _check_matrix("residual", residual, x)
     _check_vector("weight", weight, x)
-    y = torch.empty_like(x) if out is None else out
-    ro = torch.empty_like(x) if residual_out is None else residual_out
-    _check_matrix("out", y, x)
-    _check_matrix("residual_out", ro, x)
+    y = _new_like(x) if out is None else out
+    ro = _new_like(x) if residual_out is None else residual_out
+    ldy = _check_matrix("out", y, x)
+    ldo = _check_matrix("residual_out", ro, x)
     want = return_rstd or rstd is not None
-    if want:
-        if rstd is None:
-            rstd = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-        _check_vector("rstd", rstd, x, torch.float32, rows)
-    with torch.cuda.device(x.device):
-        st = _lib.fused_add_rms_norm_variant(_ptr(x), _ptr(residual), _ptr(weight), _ptr(y), _ptr(ro), _ptr(rstd),
-                                             rows, N, float(eps), DTYPE_CODE[x.dtype], _stream(x, stream),
-                                             _variant(variant))
-    if st != 0:
-        raise RowNormError(st, "fused_add_rms_norm")
+    rstd = _stats("rstd", rstd, x, rows, want)
+    _call("fused_add_rms", "fused_add_rms_norm", x, residual, weight, None, y, ro, None, rstd, rows, N, eps,
+          (ldx, ldr, ldy, ldo), variant, stream)
     return (y, ro, rstd) if want else (y, ro)
 
 
+def fused_add_layer_norm(x: torch.Tensor, residual: torch.Tensor, gamma: Optional[torch.Tensor] = None,
+                         beta: Optional[torch.Tensor] = None, eps: float = 1e-5, *, out: Optional[torch.Tensor] = None,
+                         residual_out: Optional[torch.Tensor] = None, mean: Optional[torch.Tensor] = None,
+                         rstd: Optional[torch.Tensor] = None, return_stats: bool = False,
+                         variant: Union[str, int] = "auto", stream=None):
+    """Fused residual add + LayerNorm.
+
+    ``residual_out = x + residual`` rounded to the dtype; ``y = layer_norm(residual_out)``.
+    Returns ``(y, residual_out)`` or ``(y, residual_out, mean, rstd)``.
+    """
+    rows, N, ldx = _prep(x)
+    ldr = _check_matrix("residual", residual, x)
+    _check_vector("gamma", gamma, x)
+    _check_vector("beta", beta, x)
+    y = _new_like(x) if out is None else out
+    ro = _new_like(x) if residual_out is None else residual_out
+    ldy = _check_matrix("out", y, x)
+    ldo = _check_matrix("residual_out", ro, x)
+    want = return_stats or mean is not None or rstd is not None
+    mean = _stats("mean", mean, x, rows, want)
+    rstd = _stats("rstd", rstd, x, rows, want)
+    _call("fused_add_ln", "fused_add_layer_norm", x, residual, gamma, beta, y, ro, mean, rstd, rows, N, eps,
+          (ldx, ldr, ldy, ldo), variant, stream)
+    return (y, ro, mean, rstd) if want else (y, ro)
+
+
+def softmax_forward(x: torch.Tensor, *, out: Optional[torch.Tensor] = None, row_max: Optional[torch.Tensor] = None,
+                    row_sum: Optional[torch.Tensor] = None, return_stats: bool = False,
+                    variant: Union[str, int] = "auto", stream=None):
+    """Softmax over the last dimension. Returns ``y``, or ``(y, row_max, row_sum)`` with
+    row_sum = sum(exp(x - row_max)) (fp32)."""
+    rows, N, ldx = _prep(x)
+    y = _new_like(x) if out is None else out
+    ldy = _check_matrix("out", y, x)
+    want = return_stats or row_max is not None or row_sum is not None
+    row_max = _stats("row_max", row_max, x, rows, want)
+    row_sum = _stats("row_sum", row_sum, x, rows, want)
+    _call("softmax", "softmax_forward", x, None, None, None, y, None, row_max, row_sum, rows, N, 0.0,
+          (ldx, 0, ldy, 0), variant, stream)
+    return (y, row_max, row_sum) if want else y
+
+
 def plan(op: str, rows: int, N: int, dtype: torch.dtype, *, ptrs: Optional[dict] = None, eps: float = 1e-5,
-         variant: Union[str, int] = "auto") -> Tuple[int, dict]:
+         variant: Union[str, int] = "auto", strides: Optional[dict] = None) -> Tuple[int, dict]:
     """Host-only launch plan (no GPU needed). ``ptrs`` maps buffer names (x, residual,
     gamma, beta, y, residual_out, mean, rstd) to integer addresses; missing required
-    buffers default to 256-byte-aligned placeholders that never overlap. Returns
-    ``(status, info)``."""
+    buffers default to 256-byte-aligned placeholders that never overlap. ``strides`` maps
+    x / residual / y / residual_out to row strides in elements. Returns ``(status, info)``."""
     s = torch.tensor([], dtype=dtype).element_size()
-    span = max(1, rows * N * s)
+    ld = max([N] + list((strides or {}).values()))
+    span = max(1, rows * ld * s)
     base = 1 << 40
     step = ((span + 4095) // 4096 + 1) * 4096
     default = {"x": base, "residual": base + step, "y": base + 2 * step, "residual_out": base + 3 * step}
     p = dict(default)
-    if op != "fused_add_rms":
+    if op not in ("fused_add_rms", "fused_add_ln"):
         p.pop("residual")
         p.pop("residual_out")
     if ptrs:
         p.update(ptrs)
+    st_obj = RowStrides(**(strides or {}))
     info = PlanInfo()
     st = _lib.rn_plan(OPS[op], p.get("x"), p.get("residual"), p.get("gamma"), p.get("beta"), p.get("y"),
                       p.get("residual_out"), p.get("mean"), p.get("rstd"), rows, N, float(eps),
-                      DTYPE_CODE.get(dtype, 99), _variant(variant), ctypes.byref(info))
+                      DTYPE_CODE.get(dtype, 99), _variant(variant), ctypes.byref(st_obj), ctypes.byref(info))
     return st, {"variant": VARIANT_NAMES.get(info.variant, info.variant), "waves_per_row": info.waves_per_row,
                 "rows_per_block": info.rows_per_block, "block_threads": info.block_threads,
                 "chunks_per_lane": info.chunks_per_lane, "grid_blocks": info.grid_blocks,

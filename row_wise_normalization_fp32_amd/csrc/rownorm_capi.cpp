@@ -18,13 +18,14 @@ namespace {
 using rn::Params;
 using rn::Plan;
 
-constexpr int kVersion = 10000;  // 1.0.0
+constexpr int kVersion = 10100;  // 1.1.0
 
 struct Buf {
     const void* p;
-    int64_t bytes;
+    int64_t bytes;   // extent from p to the end of the last element
+    int64_t stride;  // row stride in elements ([rows, N] tensors), 0 otherwise
     bool out;
-    int role;  // 0 x, 1 residual, 2 gamma, 3 beta, 4 y, 5 residual_out, 6 mean, 7 rstd
+    int role;
 };
 
 enum { R_X, R_RES, R_G, R_B, R_Y, R_RO, R_MEAN, R_RSTD };
@@ -37,9 +38,8 @@ bool overlaps(const Buf& a, const Buf& b) {
 // Exact aliasing that the kernels support: an output row element is written by the lane
 // that read the same element of the input, after it read it.
 bool exact_alias_allowed(const Buf& out, const Buf& other) {
-    if (out.p != other.p || out.bytes != other.bytes) return false;
-    if (out.role == R_Y) return other.role == R_X || other.role == R_RES;
-    if (out.role == R_RO) return other.role == R_X || other.role == R_RES;
+    if (out.p != other.p || out.bytes != other.bytes || out.stride != other.stride) return false;
+    if (out.role == R_Y || out.role == R_RO) return other.role == R_X || other.role == R_RES;
     return false;
 }
 
@@ -49,18 +49,49 @@ int next_pow2(int64_t v) {
     return p;
 }
 
-int validate_and_plan(int op, const void* x, const void* residual, const void* gamma, const void* beta,
-                      const void* y, const void* residual_out, const void* mean, const void* rstd, int64_t rows,
-                      int64_t N, float eps, int dtype, int variant, Plan* plan, int64_t* chunks) {
-    if (dtype != RN_F32 && dtype != RN_F16 && dtype != RN_BF16) return RN_ERR_DTYPE;
-    if (op != RN_OP_LAYER_NORM && op != RN_OP_RMS_NORM && op != RN_OP_FUSED_ADD_RMS_NORM) return RN_ERR_SHAPE;
-    if (variant < RN_VARIANT_AUTO || variant > RN_VARIANT_GENERAL) return RN_ERR_UNSUPPORTED;
-    const int64_t s = dtype == RN_F32 ? 4 : 2;
+bool is_ln(int op) { return op == RN_OP_LAYER_NORM || op == RN_OP_FUSED_ADD_LAYER_NORM; }
+bool is_fused(int op) { return op == RN_OP_FUSED_ADD_RMS_NORM || op == RN_OP_FUSED_ADD_LAYER_NORM; }
+
+struct Args {
+    int op;
+    const void *x, *residual, *gamma, *beta;
+    const void *y, *residual_out, *mean, *rstd;
+    int64_t rows, N;
+    float eps;
+    int dtype;
+    int variant;
+    int64_t ldx, ldr, ldy, ldro;  // resolved row strides (elements)
+};
+
+// Validates the arguments (dropping pointers the operation does not use) and chooses the
+// kernel. On success *C is the number of 16-byte chunks per row (vectorized variants).
+int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_t* chunks) {
+    if (a.dtype != RN_F32 && a.dtype != RN_F16 && a.dtype != RN_BF16) return RN_ERR_DTYPE;
+    if (a.op < RN_OP_LAYER_NORM || a.op > RN_OP_SOFTMAX) return RN_ERR_SHAPE;
+    if (a.variant < RN_VARIANT_AUTO || a.variant > RN_VARIANT_ELEMENT) return RN_ERR_UNSUPPORTED;
+    const int64_t s = a.dtype == RN_F32 ? 4 : 2;
+    const int64_t rows = a.rows, N = a.N;
     if (rows < 0 || N <= 0) return RN_ERR_SHAPE;
-    if (!(eps >= 0.f) || !isfinite(eps)) return RN_ERR_SHAPE;
-    if (rows > 0 && N > INT64_MAX / s / rows) return RN_ERR_SHAPE;
+    if (!(a.eps >= 0.f) || !isfinite(a.eps)) return RN_ERR_SHAPE;
     if (N > (int64_t(1) << 40)) return RN_ERR_SHAPE;
-    const bool fused = op == RN_OP_FUSED_ADD_RMS_NORM;
+    a.ldx = a.ldr = a.ldy = a.ldro = N;
+    if (strides) {
+        const int64_t in[4] = {strides->x, strides->residual, strides->y, strides->residual_out};
+        int64_t* outp[4] = {&a.ldx, &a.ldr, &a.ldy, &a.ldro};
+        const bool used[4] = {true, is_fused(a.op), true, is_fused(a.op)};
+        for (int i = 0; i < 4; ++i) {
+            if (in[i] == 0 || !used[i]) continue;
+            if (in[i] < N || in[i] > (int64_t(1) << 40)) return RN_ERR_SHAPE;
+            *outp[i] = in[i];
+        }
+    }
+    // the largest extent, (rows - 1) * ld + N elements, must fit in 63 bits of bytes
+    const int64_t ldmax = a.ldx > a.ldr ? (a.ldx > a.ldy ? (a.ldx > a.ldro ? a.ldx : a.ldro) : (a.ldy > a.ldro ? a.ldy : a.ldro))
+                                        : (a.ldr > a.ldy ? (a.ldr > a.ldro ? a.ldr : a.ldro) : (a.ldy > a.ldro ? a.ldy : a.ldro));
+    if (rows > 0 && ldmax > INT64_MAX / s / rows) return RN_ERR_SHAPE;
+    const bool fused = is_fused(a.op);
+    const bool ln = is_ln(a.op);
+    const bool sm = a.op == RN_OP_SOFTMAX;
     plan->variant = rn::V_GENERAL;
     plan->waves_per_row = 0;
     plan->rows_per_block = 0;
@@ -73,29 +104,33 @@ int validate_and_plan(int op, const void* x, const void* residual, const void* g
     *chunks = 0;
     if (rows == 0) return RN_OK;
 
-    if (!x || !y) return RN_ERR_NULL;
-    if (fused && (!residual || !residual_out)) return RN_ERR_NULL;
-    if (op != RN_OP_LAYER_NORM) {
-        beta = nullptr;  // not part of these ops
-        mean = nullptr;
-    }
+    if (!a.x || !a.y) return RN_ERR_NULL;
+    if (fused && (!a.residual || !a.residual_out)) return RN_ERR_NULL;
+    if (!ln) a.beta = nullptr;
+    if (!ln && !sm) a.mean = nullptr;
+    if (sm) a.gamma = nullptr;
     if (!fused) {
-        residual = nullptr;
-        residual_out = nullptr;
+        a.residual = nullptr;
+        a.residual_out = nullptr;
     }
 
-    const int64_t mat = rows * N * s;
+    auto extent = [&](int64_t ld) { return ((rows - 1) * ld + N) * s; };
     const Buf bufs[] = {
-        {x, mat, false, R_X},           {residual, mat, false, R_RES}, {gamma, N * s, false, R_G},
-        {beta, N * s, false, R_B},      {y, mat, true, R_Y},           {residual_out, mat, true, R_RO},
-        {mean, rows * 4, true, R_MEAN}, {rstd, rows * 4, true, R_RSTD},
+        {a.x, extent(a.ldx), a.ldx, false, R_X},
+        {a.residual, extent(a.ldr), a.ldr, false, R_RES},
+        {a.gamma, N * s, 0, false, R_G},
+        {a.beta, N * s, 0, false, R_B},
+        {a.y, extent(a.ldy), a.ldy, true, R_Y},
+        {a.residual_out, extent(a.ldro), a.ldro, true, R_RO},
+        {a.mean, rows * 4, 0, true, R_MEAN},
+        {a.rstd, rows * 4, 0, true, R_RSTD},
     };
     const int nb = sizeof(bufs) / sizeof(bufs[0]);
     for (int i = 0; i < nb; ++i) {
         if (!bufs[i].p) continue;
-        const uintptr_t a = reinterpret_cast<uintptr_t>(bufs[i].p);
+        const uintptr_t ad = reinterpret_cast<uintptr_t>(bufs[i].p);
         const int64_t need = (bufs[i].role == R_MEAN || bufs[i].role == R_RSTD) ? 4 : s;
-        if (a % static_cast<uintptr_t>(need) != 0) return RN_ERR_ALIGN;
+        if (ad % static_cast<uintptr_t>(need) != 0) return RN_ERR_ALIGN;
     }
     for (int i = 0; i < nb; ++i) {
         if (!bufs[i].p || !bufs[i].out) continue;
@@ -105,27 +140,32 @@ int validate_and_plan(int op, const void* x, const void* residual, const void* g
         }
     }
 
-    // Vectorized variants need whole 16-byte chunks per row and 16-byte aligned tensors.
+    // Vectorized variants need whole 16-byte chunks per row, 16-byte aligned tensors and
+    // row strides that are whole chunks.
     bool vec_ok = (N * s) % 16 == 0;
     for (int i = 0; i < nb && vec_ok; ++i) {
         if (!bufs[i].p || bufs[i].role == R_MEAN || bufs[i].role == R_RSTD) continue;
         if (reinterpret_cast<uintptr_t>(bufs[i].p) % 16 != 0) vec_ok = false;
+        if ((bufs[i].stride * s) % 16 != 0) vec_ok = false;
     }
     const int64_t C = vec_ok ? (N * s) / 16 : 0;
     const int64_t wave_cap = int64_t(64) * rn::kMaxWaveChunks;                         // 1024 chunks
     const int64_t group_cap = int64_t(64) * rn::kMaxGroupWaves * rn::kMaxGroupChunks;  // 4096 chunks
+    const int64_t elem_cap = int64_t(64) * rn::kMaxGroupWaves * rn::kElemMaxPerLane;   // 16384 elements
 
     // Automatic row-group width: enough waves that each lane holds about kTargetChunks
     // chunks (measured on MI355X: 4 chunks per lane balances bytes in flight against VGPRs).
     int w_auto = next_pow2((C + 64 * rn::kTargetChunks - 1) / (64 * rn::kTargetChunks));
     if (w_auto > rn::kMaxGroupWaves) w_auto = rn::kMaxGroupWaves;
 
-    int v = variant;
+    int v = a.variant;
     if (v == RN_VARIANT_AUTO) {
-        if (!vec_ok || C > group_cap)
-            v = RN_VARIANT_GENERAL;
-        else
+        if (vec_ok && C <= group_cap)
             v = w_auto == 1 ? RN_VARIANT_WAVE : RN_VARIANT_WORKGROUP;
+        else if (N <= elem_cap)
+            v = RN_VARIANT_ELEMENT;
+        else
+            v = RN_VARIANT_GENERAL;
     }
     int W = 0;
     if (v == RN_VARIANT_WAVE) {
@@ -136,6 +176,9 @@ int validate_and_plan(int op, const void* x, const void* residual, const void* g
         if (!vec_ok || C > group_cap) return RN_ERR_UNSUPPORTED;
         W = w_auto < 2 ? 2 : w_auto;
         plan->variant = rn::V_WORKGROUP;
+    } else if (v == RN_VARIANT_ELEMENT) {
+        if (N > elem_cap) return RN_ERR_UNSUPPORTED;
+        plan->variant = rn::V_ELEMENT;
     } else {
         plan->variant = rn::V_GENERAL;
     }
@@ -144,6 +187,14 @@ int validate_and_plan(int op, const void* x, const void* residual, const void* g
         plan->rows_per_block = 1;
         plan->chunks_per_lane = 0;
         plan->block_threads = rn::kGeneralThreads;
+    } else if (plan->variant == rn::V_ELEMENT) {
+        // about kElemTarget elements per lane: W = 1 up to 512 elements, then 2, 4, 8, 16
+        int We = next_pow2((N + 64 * rn::kElemTarget - 1) / (64 * rn::kElemTarget));
+        if (We > rn::kMaxGroupWaves) We = rn::kMaxGroupWaves;
+        plan->waves_per_row = We;
+        plan->rows_per_block = We <= 4 ? 4 / We : 1;
+        plan->chunks_per_lane = next_pow2((N + 64 * We - 1) / (64 * We));
+        plan->block_threads = 64 * We * plan->rows_per_block;
     } else {
         plan->waves_per_row = W;
         plan->rows_per_block = W <= 4 ? 4 / W : 1;
@@ -152,53 +203,81 @@ int validate_and_plan(int op, const void* x, const void* residual, const void* g
     }
     const int64_t blocks = (rows + plan->rows_per_block - 1) / plan->rows_per_block;
     plan->grid = blocks < rn::kMaxGrid ? blocks : rn::kMaxGrid;
-    plan->exact = plan->variant != rn::V_GENERAL && C == int64_t(64) * W * plan->chunks_per_lane;
+    const bool vec = plan->variant == rn::V_WAVE || plan->variant == rn::V_WORKGROUP;
+    plan->exact = vec && C == int64_t(64) * W * plan->chunks_per_lane;
     // Persistent launch: for exact shapes with parameters and enough rows that workgroups
     // would otherwise be launched many times over (measured: it pays from about 2048
-    // workgroups up). Parameters go to LDS once per workgroup; LayerNorm with both keeps
-    // gamma in VGPRs and stages only beta, so the LDS need is at most one row (64 KiB).
-    const bool has_g = gamma != nullptr;
-    const bool has_b = op == RN_OP_LAYER_NORM && beta != nullptr;
-    plan->persistent = plan->exact && (has_g || has_b) && blocks >= rn::kPersistentBlocks;
+    // workgroups up). Parameters go to LDS once per workgroup; the LayerNorm ops with both
+    // keep gamma in VGPRs and stage only beta, so the LDS need is at most one row (64 KiB).
+    const bool has_params = a.gamma != nullptr || (ln && a.beta != nullptr);
+    plan->persistent = vec && plan->exact && has_params && blocks >= rn::kPersistentBlocks;
     plan->lds_bytes = 0;
     if (plan->persistent) plan->lds_bytes = static_cast<int>(C * 16);  // one parameter vector in LDS
     *chunks = C;
     return RN_OK;
 }
 
-int run(int op, const void* x, const void* residual, const void* gamma, const void* beta, void* y,
-        void* residual_out, float* mean, float* rstd, int64_t rows, int64_t N, float eps, int dtype,
-        hipStream_t stream, int variant) {
+int run(Args a, const rn_row_strides* strides, hipStream_t stream) {
     Plan plan;
     int64_t C = 0;
-    const int st = validate_and_plan(op, x, residual, gamma, beta, y, residual_out, mean, rstd, rows, N, eps, dtype,
-                                     variant, &plan, &C);
-    if (st != RN_OK || rows == 0) return st;
+    const int st = validate_and_plan(a, strides, &plan, &C);
+    if (st != RN_OK || a.rows == 0) return st;
+    const int64_t s = a.dtype == RN_F32 ? 4 : 2;
     Params p;
-    p.x = x;
-    p.residual = op == RN_OP_FUSED_ADD_RMS_NORM ? residual : nullptr;
-    p.gamma = gamma;
-    p.beta = op == RN_OP_LAYER_NORM ? beta : nullptr;
-    p.y = y;
-    p.residual_out = op == RN_OP_FUSED_ADD_RMS_NORM ? residual_out : nullptr;
-    p.mean = op == RN_OP_LAYER_NORM ? mean : nullptr;
-    p.rstd = rstd;
-    p.rows = rows;
-    p.N = N;
+    p.x = a.x;
+    p.residual = a.residual;
+    p.gamma = a.gamma;
+    p.beta = a.beta;
+    p.y = const_cast<void*>(a.y);
+    p.residual_out = const_cast<void*>(a.residual_out);
+    p.mean = static_cast<float*>(const_cast<void*>(a.mean));
+    p.rstd = static_cast<float*>(const_cast<void*>(a.rstd));
+    p.rows = a.rows;
+    p.N = a.N;
     p.C = C;
-    p.eps = eps;
-    p.inv_n = static_cast<float>(1.0 / static_cast<double>(N));
+    p.ldx = a.ldx;
+    p.ldr = a.ldr;
+    p.ldy = a.ldy;
+    p.ldro = a.ldro;
+    p.cx = a.ldx * s / 16;  // used only by the vectorized variants, where they are exact
+    p.cr = a.ldr * s / 16;
+    p.cy = a.ldy * s / 16;
+    p.cro = a.ldro * s / 16;
+    p.eps = a.eps;
+    p.inv_n = static_cast<float>(1.0 / static_cast<double>(a.N));
     hipError_t e = hipErrorInvalidValue;
-    switch (dtype) {
-    case RN_F32: e = plan.persistent ? rn::launch_f32_persistent(op, plan, p, stream)
-                                     : rn::launch_f32(op, plan, p, stream); break;
-    case RN_F16: e = plan.persistent ? rn::launch_f16_persistent(op, plan, p, stream)
-                                     : rn::launch_f16(op, plan, p, stream); break;
-    case RN_BF16: e = plan.persistent ? rn::launch_bf16_persistent(op, plan, p, stream)
-                                      : rn::launch_bf16(op, plan, p, stream); break;
+    switch (a.dtype) {
+    case RN_F32: e = plan.persistent ? rn::launch_f32_persistent(a.op, plan, p, stream)
+                                     : rn::launch_f32(a.op, plan, p, stream); break;
+    case RN_F16: e = plan.persistent ? rn::launch_f16_persistent(a.op, plan, p, stream)
+                                     : rn::launch_f16(a.op, plan, p, stream); break;
+    case RN_BF16: e = plan.persistent ? rn::launch_bf16_persistent(a.op, plan, p, stream)
+                                      : rn::launch_bf16(a.op, plan, p, stream); break;
     default: break;
     }
     return e == hipSuccess ? RN_OK : RN_ERR_HIP;
+}
+
+Args make_args(int op, const void* x, const void* residual, const void* gamma, const void* beta, const void* y,
+               const void* residual_out, const void* mean, const void* rstd, int64_t rows, int64_t N, float eps,
+               int dtype, int variant) {
+    Args a;
+    a.op = op;
+    a.x = x;
+    a.residual = residual;
+    a.gamma = gamma;
+    a.beta = beta;
+    a.y = y;
+    a.residual_out = residual_out;
+    a.mean = mean;
+    a.rstd = rstd;
+    a.rows = rows;
+    a.N = N;
+    a.eps = eps;
+    a.dtype = dtype;
+    a.variant = variant;
+    a.ldx = a.ldr = a.ldy = a.ldro = N;
+    return a;
 }
 
 }  // namespace
@@ -207,48 +286,68 @@ extern "C" {
 
 int ln_forward(const void* x, const void* gamma, const void* beta, void* y, float* mean, float* rstd, int64_t rows,
                int64_t N, float eps, int dtype, hipStream_t stream) {
-    return run(RN_OP_LAYER_NORM, x, nullptr, gamma, beta, y, nullptr, mean, rstd, rows, N, eps, dtype, stream,
-               RN_VARIANT_AUTO);
+    return run(make_args(RN_OP_LAYER_NORM, x, nullptr, gamma, beta, y, nullptr, mean, rstd, rows, N, eps, dtype,
+                         RN_VARIANT_AUTO), nullptr, stream);
 }
 
 int rms_norm(const void* x, const void* weight, void* y, float* rstd, int64_t rows, int64_t N, float eps, int dtype,
              hipStream_t stream) {
-    return run(RN_OP_RMS_NORM, x, nullptr, weight, nullptr, y, nullptr, nullptr, rstd, rows, N, eps, dtype, stream,
-               RN_VARIANT_AUTO);
+    return run(make_args(RN_OP_RMS_NORM, x, nullptr, weight, nullptr, y, nullptr, nullptr, rstd, rows, N, eps, dtype,
+                         RN_VARIANT_AUTO), nullptr, stream);
 }
 
 int fused_add_rms_norm(const void* x, const void* residual, const void* weight, void* y, void* residual_out,
                        float* rstd, int64_t rows, int64_t N, float eps, int dtype, hipStream_t stream) {
-    return run(RN_OP_FUSED_ADD_RMS_NORM, x, residual, weight, nullptr, y, residual_out, nullptr, rstd, rows, N, eps,
-               dtype, stream, RN_VARIANT_AUTO);
+    return run(make_args(RN_OP_FUSED_ADD_RMS_NORM, x, residual, weight, nullptr, y, residual_out, nullptr, rstd, rows,
+                         N, eps, dtype, RN_VARIANT_AUTO), nullptr, stream);
+}
+
+int fused_add_layer_norm(const void* x, const void* residual, const void* gamma, const void* beta, void* y,
+                         void* residual_out, float* mean, float* rstd, int64_t rows, int64_t N, float eps, int dtype,
+                         hipStream_t stream) {
+    return run(make_args(RN_OP_FUSED_ADD_LAYER_NORM, x, residual, gamma, beta, y, residual_out, mean, rstd, rows, N,
+                         eps, dtype, RN_VARIANT_AUTO), nullptr, stream);
+}
+
+int softmax_forward(const void* x, void* y, float* row_max, float* row_sum, int64_t rows, int64_t N, int dtype,
+                    hipStream_t stream) {
+    return run(make_args(RN_OP_SOFTMAX, x, nullptr, nullptr, nullptr, y, nullptr, row_max, row_sum, rows, N, 0.f,
+                         dtype, RN_VARIANT_AUTO), nullptr, stream);
+}
+
+int rn_forward_ex(int op, const void* x, const void* residual, const void* gamma, const void* beta, void* y,
+                  void* residual_out, float* mean, float* rstd, int64_t rows, int64_t N, float eps, int dtype,
+                  const rn_row_strides* strides, int variant, hipStream_t stream) {
+    return run(make_args(op, x, residual, gamma, beta, y, residual_out, mean, rstd, rows, N, eps, dtype, variant),
+               strides, stream);
 }
 
 int ln_forward_variant(const void* x, const void* gamma, const void* beta, void* y, float* mean, float* rstd,
                        int64_t rows, int64_t N, float eps, int dtype, hipStream_t stream, int variant) {
-    return run(RN_OP_LAYER_NORM, x, nullptr, gamma, beta, y, nullptr, mean, rstd, rows, N, eps, dtype, stream,
-               variant);
+    return run(make_args(RN_OP_LAYER_NORM, x, nullptr, gamma, beta, y, nullptr, mean, rstd, rows, N, eps, dtype,
+                         variant), nullptr, stream);
 }
 
 int rms_norm_variant(const void* x, const void* weight, void* y, float* rstd, int64_t rows, int64_t N, float eps,
                      int dtype, hipStream_t stream, int variant) {
-    return run(RN_OP_RMS_NORM, x, nullptr, weight, nullptr, y, nullptr, nullptr, rstd, rows, N, eps, dtype, stream,
-               variant);
+    return run(make_args(RN_OP_RMS_NORM, x, nullptr, weight, nullptr, y, nullptr, nullptr, rstd, rows, N, eps, dtype,
+                         variant), nullptr, stream);
 }
 
 int fused_add_rms_norm_variant(const void* x, const void* residual, const void* weight, void* y, void* residual_out,
                                float* rstd, int64_t rows, int64_t N, float eps, int dtype, hipStream_t stream,
                                int variant) {
-    return run(RN_OP_FUSED_ADD_RMS_NORM, x, residual, weight, nullptr, y, residual_out, nullptr, rstd, rows, N, eps,
-               dtype, stream, variant);
+    return run(make_args(RN_OP_FUSED_ADD_RMS_NORM, x, residual, weight, nullptr, y, residual_out, nullptr, rstd, rows,
+                         N, eps, dtype, variant), nullptr, stream);
 }
 
 int rn_plan(int op, const void* x, const void* residual, const void* gamma, const void* beta, const void* y,
             const void* residual_out, const void* mean, const void* rstd, int64_t rows, int64_t N, float eps,
-            int dtype, int variant, rn_plan_info* out) {
+            int dtype, int variant, const rn_row_strides* strides, rn_plan_info* out) {
     Plan plan;
     int64_t C = 0;
-    const int st = validate_and_plan(op, x, residual, gamma, beta, y, residual_out, mean, rstd, rows, N, eps, dtype,
-                                     variant, &plan, &C);
+    Args a = make_args(op, x, residual, gamma, beta, y, residual_out, mean, rstd, rows, N, eps, dtype, variant);
+    const int st = validate_and_plan(a, strides, &plan, &C);
     if (out) {
         out->variant = plan.variant;
         out->waves_per_row = plan.waves_per_row;

@@ -10,34 +10,37 @@
 
 namespace rn {
 
-enum Op { OP_LN = 0, OP_RMS = 1, OP_FUSED = 2 };
+enum Op { OP_LN = 0, OP_RMS = 1, OP_FUSED = 2, OP_FUSED_LN = 3, OP_SOFTMAX = 4 };
 enum Dt { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
-enum Variant { V_AUTO = 0, V_WAVE = 1, V_WORKGROUP = 2, V_GENERAL = 3 };
+enum Variant { V_AUTO = 0, V_WAVE = 1, V_WORKGROUP = 2, V_GENERAL = 3, V_ELEMENT = 4 };
 
 // Kernel arguments, passed by value. Pointers are device pointers; nullable ones are
 // documented in include/rownorm.h.
 struct Params {
     const void* x;
     const void* residual;
-    const void* gamma;  // gamma (LayerNorm) or weight (RMSNorm ops)
+    const void* gamma;  // gamma (LayerNorm ops) or weight (RMSNorm ops)
     const void* beta;
     void* y;
     void* residual_out;
-    float* mean;
-    float* rstd;
+    float* mean;  // softmax: the row maximum
+    float* rstd;  // softmax: the row's sum of exp(x - max)
     int64_t rows;
     int64_t N;
     int64_t C;    // 16-byte chunks per row (vectorized variants)
+    int64_t ldx, ldr, ldy, ldro;  // row strides in elements of x, residual, y, residual_out
+    int64_t cx, cr, cy, cro;      // the same in 16-byte chunks (vectorized variants)
     float eps;
     float inv_n;  // 1 / N rounded to fp32
 };
 
 // Launch geometry chosen on the host.
 struct Plan {
-    int variant;          // V_WAVE, V_WORKGROUP or V_GENERAL
+    int variant;          // V_WAVE, V_WORKGROUP, V_ELEMENT or V_GENERAL
     int waves_per_row;    // W: wavefronts that share one row
     int rows_per_block;   // RPB: row groups per workgroup
-    int chunks_per_lane;  // V: 16-byte chunks each lane holds (vectorized variants)
+    int chunks_per_lane;  // V: 16-byte chunks (vectorized variants) or elements (element
+                          // variant) each lane holds
     int block_threads;    // 64 * W * RPB
     int64_t grid;         // workgroups (for persistent launches: an upper bound, capped at launch)
     bool exact;           // C == 64 * W * V: no tail handling needed
@@ -51,6 +54,8 @@ constexpr int kMaxGroupWaves = 16;     // workgroup variant: up to 16 waves per 
 constexpr int kMaxGroupChunks = 4;     // ... holding up to 4 chunks per lane (4096 per row)
 constexpr int kTargetChunks = 4;       // automatic choice: about 4 chunks per lane
 constexpr int kGeneralThreads = 256;   // general variant: 256 lanes per row
+constexpr int kElemTarget = 8;         // element variant: about 8 elements per lane ...
+constexpr int kElemMaxPerLane = 16;    // ... at most 16 (with 16 waves: rows up to 16384)
 constexpr int64_t kMaxGrid = 1 << 20;  // grid cap; kernels loop over the remaining rows
 constexpr int64_t kPersistentBlocks = 2048;  // at least this many workgroups: persistent launch
 

@@ -52,6 +52,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "rownorm_internal.h"
 
 namespace rn {
@@ -206,11 +208,25 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
+// Maximum over the 64 lanes, by the same exchange pattern.
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x141>(v));
+    v = fmaxf(v, dpp<0x140>(v));
+    const float r0 = bit_cast<float>(__builtin_amdgcn_readlane(bit_cast<int>(v), 0));
+    const float r1 = bit_cast<float>(__builtin_amdgcn_readlane(bit_cast<int>(v), 16));
+    const float r2 = bit_cast<float>(__builtin_amdgcn_readlane(bit_cast<int>(v), 32));
+    const float r3 = bit_cast<float>(__builtin_amdgcn_readlane(bit_cast<int>(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 __device__ __forceinline__ float uniform(float v) {
     return bit_cast<float>(__builtin_amdgcn_readfirstlane(bit_cast<int>(v)));
 }
 
-// (count, mean, M2) of a part of a row; mean is relative to the row's shift K.
+// (count, mean, M2) of a part of a row; mean is relative to a reference point common to
+// the parts being combined.
 struct Moments {
     float n, m, m2;
 };
@@ -228,12 +244,43 @@ __device__ __forceinline__ Moments combine(const Moments& a, const Moments& b) {
 // 1 / sqrt(v) with the hardware reciprocal square root (error within about 1 ulp).
 __device__ __forceinline__ float inv_sqrt(float v) { return __builtin_amdgcn_rsqf(v); }
 
+// 2^v with the hardware exponential (v_exp_f32).
+__device__ __forceinline__ float exp2_hw(float v) { return __builtin_amdgcn_exp2f(v); }
+constexpr float kLog2e = 1.44269504088896340736f;           // log2(e) rounded to fp32
+constexpr float kLog2eLo = 1.92596298909109e-8f;            // log2(e) - kLog2e
+
+// e^u for u <= 0 (softmax's x - max), with a relative error of a few ulps for every u.
+// The hardware exponential takes a base-2 argument; its error, and the rounding of
+// u * log2(e), grow with the argument's magnitude (about |u| * 2^-23 relative). So the
+// product is formed exactly as hi + lo (fma for the rounding error of hi, plus the part of
+// log2(e) that fp32 drops), its integer part n is split off exactly, 2^(fraction) comes
+// from v_exp_f32 on [-0.5, 0.5], and ldexp applies 2^n without rounding (down to the
+// subnormal range). Arguments below -200 (including -inf, an empty part's maximum) give 0.
+__device__ __forceinline__ float exp_neg(float u) {
+    u = fmaxf(u, -200.f);
+    const float hi = u * kLog2e;
+    const float lo = fmaf(u, kLog2e, -hi) + u * kLog2eLo;
+    const float n = rintf(hi);
+    const float f = (hi - n) + lo;
+    return ldexpf(exp2_hw(f), static_cast<int>(n));
+}
+
 // Pairwise combine of two parts of equal size n: mean = (ma + mb) / 2,
 // M2 = M2a + M2b + (mb - ma)^2 * n / 2. Every scaling is by a power of two, so the only
 // roundings are those of the additions.
 __device__ __forceinline__ Moments combine_equal(const Moments& a, const Moments& b) {
     const float d = b.m - a.m;
     return Moments{a.n + b.n, 0.5f * (a.m + b.m), a.m2 + b.m2 + d * d * (0.5f * a.n)};
+}
+
+// Softmax partial state of a part of a row: its maximum and sum of exp(x - max).
+// Combining two parts rescales both sums to the larger maximum (the "05 LLM Ops" lesson,
+// smarter.xin, sections "Online Softmax denominator correction" and "merging (max, sum)
+// with decay").
+__device__ __forceinline__ void softmax_combine(float& m, float& s, float mb, float sb) {
+    const float M = fmaxf(m, mb);
+    s = s * exp_neg(m - M) + sb * exp_neg(mb - M);
+    m = M;
 }
 
 // Compile-time presence of the affine parameters.
@@ -265,6 +312,119 @@ __device__ __forceinline__ void st(u32x4* p, const u32x4& v) {
     }
 }
 
+// Properties of an operation.
+template <int OP>
+struct OpTraits {
+    static constexpr bool LN = OP == OP_LN || OP == OP_FUSED_LN;    // mean-centred statistics
+    static constexpr bool RES = OP == OP_FUSED || OP == OP_FUSED_LN;  // residual add first
+    static constexpr bool SM = OP == OP_SOFTMAX;
+    static constexpr bool RMS = OP == OP_RMS || OP == OP_FUSED;
+};
+
+// Per-wave LDS record of a row group: LayerNorm (n, rough mean a, mean - a, M2);
+// RMSNorm (sum of squares); softmax (max, sum).
+struct WavePart {
+    float v[4];
+};
+
+// ---------------------------------------------------------------------------------------
+// Row-group statistics shared by the vectorized and the element kernels. Each wave has
+// reduced its own part of the row; these combine the W parts after one workgroup barrier
+// (W == 1: nothing to combine). `part` is this row group's LDS area, double-buffered by
+// `buf` so that consecutive rows need one barrier each.
+// ---------------------------------------------------------------------------------------
+
+// LayerNorm: wave part (n_w, a_w, cw = mean_w - a_w, M2_w). Returns the row's mean relative
+// to this wave's a (rel), M2 and the row mean. The parts are put on a common reference
+// R = a_0 (wave 0's rough mean): m_w = (a_w - R) + cw, where a_w - R is exact whenever the
+// rough means are within a factor of two of each other (Sterbenz), then combined in a fixed
+// pairwise tree (equal parts) or left to right.
+template <int W, bool EQUAL>
+__device__ __forceinline__ void group_moments(WavePart (*part)[W > 1 ? W : 1], int& buf, int lane, int wr, float n_w,
+                                              float a_w, float cw, float m2w, float& rel, float& m2, float& mean) {
+    if constexpr (W == 1) {
+        rel = cw;
+        m2 = m2w;
+        mean = a_w + cw;
+    } else {
+        if (lane == 0) {
+            WavePart& q = part[buf][wr];
+            q.v[0] = n_w;
+            q.v[1] = a_w;
+            q.v[2] = cw;
+            q.v[3] = m2w;
+        }
+        __syncthreads();
+        const float R = part[buf][0].v[1];
+        auto load = [&](int w) {
+            const WavePart q = part[buf][w];
+            return Moments{q.v[0], (q.v[1] - R) + q.v[2], q.v[3]};
+        };
+        Moments acc;
+        if constexpr (EQUAL && (W & (W - 1)) == 0 && W <= 16) {
+            // The fixed pairwise tree ((0,1),(2,3)),((4,5),(6,7)),... across lanes: lane l
+            // holds part l, and at step s lane l combines with lane l + s (DPP: quad_perm
+            // for s = 1, 2, row_shl for s = 4, 8). Lane 0 ends with the row's moments.
+            const WavePart q = part[buf][lane < W ? lane : 0];
+            Moments m{q.v[0], (q.v[1] - R) + q.v[2], q.v[3]};
+            auto step = [&](auto ctrl) {
+                constexpr int C = decltype(ctrl)::value;
+                const Moments o{dpp<C>(m.n), dpp<C>(m.m), dpp<C>(m.m2)};
+                m = combine_equal(m, o);
+            };
+            step(std::integral_constant<int, 0xB1>{});                      // lane + 1
+            if constexpr (W > 2) step(std::integral_constant<int, 0x4E>{});  // lane + 2
+            if constexpr (W > 4) step(std::integral_constant<int, 0x104>{}); // row_shl:4
+            if constexpr (W > 8) step(std::integral_constant<int, 0x108>{}); // row_shl:8
+            acc = Moments{uniform(m.n), uniform(m.m), uniform(m.m2)};
+        } else {
+            acc = load(0);
+#pragma unroll
+            for (int w = 1; w < W; ++w) acc = combine(acc, load(w));
+        }
+        buf ^= 1;
+        rel = acc.m - (a_w - R);
+        m2 = acc.m2;
+        mean = R + acc.m;
+    }
+}
+
+template <int W>
+__device__ __forceinline__ float group_sum(WavePart (*part)[W > 1 ? W : 1], int& buf, int lane, int wr, float s) {
+    if constexpr (W == 1) {
+        return s;
+    } else {
+        if (lane == 0) part[buf][wr].v[0] = s;
+        __syncthreads();
+        float S = part[buf][0].v[0];
+#pragma unroll
+        for (int w = 1; w < W; ++w) S += part[buf][w].v[0];
+        buf ^= 1;
+        return S;
+    }
+}
+
+// Softmax: combine the waves' (max, sum) pairs, left to right; returns the row's max and sum.
+template <int W>
+__device__ __forceinline__ void group_softmax(WavePart (*part)[W > 1 ? W : 1], int& buf, int lane, int wr, float mw,
+                                              float sw, float& M, float& S) {
+    if constexpr (W == 1) {
+        M = mw;
+        S = sw;
+    } else {
+        if (lane == 0) {
+            part[buf][wr].v[0] = mw;
+            part[buf][wr].v[1] = sw;
+        }
+        __syncthreads();
+        M = part[buf][0].v[0];
+        S = part[buf][0].v[1];
+#pragma unroll
+        for (int w = 1; w < W; ++w) softmax_combine(M, S, part[buf][w].v[0], part[buf][w].v[1]);
+        buf ^= 1;
+    }
+}
+
 // ---------------------------------------------------------------------------------------
 // Vectorized kernels: one row group of W wavefronts holds a row in VGPRs.
 // ---------------------------------------------------------------------------------------
@@ -272,12 +432,13 @@ __device__ __forceinline__ void st(u32x4* p, const u32x4& v) {
 template <int DT, int OP, int W, int V, bool EXACT, int AFF, int FL>
 struct VecRow {
     using IO = Io<DT>;
+    using OT = OpTraits<OP>;
     static constexpr int E = IO::E;
     static constexpr int LANES = 64 * W;
     static constexpr int WS = W > 1 ? W : 1;
-    static constexpr bool HG = (AFF & AFF_G) != 0;                 // gamma / weight present
-    static constexpr bool HB = OP == OP_LN && (AFF & AFF_B) != 0;  // beta present
-    static constexpr int NR = OP == OP_FUSED ? V : 1;              // residual registers
+    static constexpr bool HG = !OT::SM && (AFF & AFF_G) != 0;  // gamma / weight present
+    static constexpr bool HB = OT::LN && (AFF & AFF_B) != 0;   // beta present
+    static constexpr int NR = OT::RES ? V : 1;                 // residual registers
     static constexpr int NG = HG ? V : 1;
     static constexpr int NB = HB ? V : 1;
 
@@ -288,19 +449,14 @@ struct VecRow {
     }
     __device__ static __forceinline__ bool valid(int i, int t, int Ci) { return EXACT || i * LANES + t < Ci; }
 
-    // LayerNorm's common reference point K = x[row, 0] is loaded with the row when the row
-    // spans several waves (with one wave, lane 0 already holds it).
-    static constexpr bool LOAD_K = OP == OP_LN && W > 1;
-
-    // a1: issue every load of the row (and of the residual, and K).
+    // a1: issue every load of the row (and of the residual). Row strides are in chunks.
     __device__ static __forceinline__ void load_row(const Params& p, int64_t row, int t, int Ci, u32x4 (&xv)[V],
-                                                    u32x4 (&rv)[NR], float& K) {
-        if constexpr (LOAD_K) K = IO::load1(p.x, row * p.N);
-        const u32x4* xr = static_cast<const u32x4*>(p.x) + row * p.C;
+                                                    u32x4 (&rv)[NR]) {
+        const u32x4* xr = static_cast<const u32x4*>(p.x) + row * p.cx;
 #pragma unroll
         for (int i = 0; i < V; ++i) xv[i] = ld<FL>(xr + chunk(i, t, Ci));
-        if constexpr (OP == OP_FUSED) {
-            const u32x4* rr = static_cast<const u32x4*>(p.residual) + row * p.C;
+        if constexpr (OT::RES) {
+            const u32x4* rr = static_cast<const u32x4*>(p.residual) + row * p.cr;
 #pragma unroll
             for (int i = 0; i < V; ++i) rv[i] = ld<FL>(rr + chunk(i, t, Ci));
         }
@@ -318,30 +474,32 @@ struct VecRow {
     // Where the epilogue takes gamma / beta / weight from.
     enum { PARAMS_REG = 0, PARAMS_LDS = 2 };
 
-    // a2-a7 for one row whose chunks are in xv / rv. `part` is the workgroup's LDS
-    // exchange area (double-buffered by `buf`), used when W > 1. Parameters come from gv /
-    // bv (PARAMS_REG) or are read from LDS at `lds` (PARAMS_LDS: gamma chunks then beta
+    // a2-a7 for one row whose chunks are in xv / rv. Parameters come from gv / bv
+    // (PARAMS_REG) or are read from LDS at `lds` (PARAMS_LDS: gamma chunks then beta
     // chunks; with FL_GAMMA_REG gamma comes from gv and LDS holds only beta).
     //
     // LayerNorm statistics use the corrected two-pass form (Chan, Golub and LeVeque): a
     // rough mean a = sum(x) / n from a first pass (for fp16 / bf16 one v_dot2 per element
-    // pair, no widening), then one centered pass that accumulates c = sum(x - a) and
-    // q = sum((x - a)^2): mean = a + c / n and M2 = q - c^2 / n, exact for any a and
+    // pair, no widening; for fp32 a pass shifted by the wave's first element, so that a
+    // constant row gives a exactly), then one centered pass that accumulates c = sum(x - a)
+    // and q = sum((x - a)^2): mean = a + c / n and M2 = q - c^2 / n, exact for any a and
     // accurate when a is near the mean. Only the centered values x - a stay in registers.
-    // Across the waves of a row group the per-wave moments are made relative to a common
-    // point K = x[row, 0] and combined pairwise (Welford), as the walkthrough's section 6
-    // and the LLM-ops lesson's combine function describe.
+    // Across the waves of a row group the per-wave moments are combined pairwise (Welford),
+    // as the walkthrough's section 6 and the LLM-ops lesson's combine function describe.
+    //
+    // Softmax: per wave the maximum, then the sum of exp(x - max) with the exponentials kept
+    // in registers; the waves' (max, sum) pairs are combined with the rescaling of the online
+    // form; the output is exp(x - max_w) * (exp(max_w - max) / sum).
     template <int PSRC>
     __device__ static __forceinline__ void norm_row(const Params& p, int64_t row, int lane, int wr, int t, int Ci,
-                                                    const u32x4 (&xv)[V], const u32x4 (&rv)[NR], float K,
-                                                    u32x4 (&gv)[NG], u32x4 (&bv)[NB], const u32x4* lds,
-                                                    float (*part)[WS][3], int& buf) {
-        const float nf = static_cast<float>(p.N);
-        // Chunk i as the kernel sees it: the input, or for the fused op the rounded sum.
+                                                    const u32x4 (&xv)[V], const u32x4 (&rv)[NR], u32x4 (&gv)[NG],
+                                                    u32x4 (&bv)[NB], const u32x4* lds, WavePart (*part)[WS],
+                                                    int& buf) {
+        // Chunk i as the kernel sees it: the input, or for the fused ops the rounded sum.
         u32x4 src[V];
-        if constexpr (OP == OP_FUSED) {
+        if constexpr (OT::RES) {
             // ---- a2: t = round(x + residual), stored as residual_out; t is what gets normalized.
-            u32x4* ro = static_cast<u32x4*>(p.residual_out) + row * p.C;
+            u32x4* ro = static_cast<u32x4*>(p.residual_out) + row * p.cro;
 #pragma unroll
             for (int i = 0; i < V; ++i) {
                 float a[E], b[E];
@@ -356,14 +514,14 @@ struct VecRow {
 #pragma unroll
             for (int i = 0; i < V; ++i) src[i] = xv[i];
         }
-        if constexpr (!EXACT) {
+        if constexpr (!EXACT && !OT::SM) {
 #pragma unroll
             for (int i = 0; i < V; ++i)
                 if (!valid(i, t, Ci)) src[i] = u32x4{0u, 0u, 0u, 0u};  // idle lanes contribute zeros
         }
         float n_w;  // elements held by this wave
         if constexpr (W == 1) {
-            n_w = nf;
+            n_w = static_cast<float>(p.N);
         } else if constexpr (EXACT) {
             n_w = static_cast<float>(V * 64 * E);
         } else {
@@ -377,19 +535,17 @@ struct VecRow {
         }
 
         // NOFLOAT: the widened row is not kept; the epilogue widens the packed row again.
-        constexpr bool NOFLOAT = (FL & FL_NOFLOAT) != 0 && OP == OP_LN;
-        float v[NOFLOAT ? 1 : V][NOFLOAT ? 1 : E];  // LayerNorm: x - a; RMSNorm: x
-        float scale;    // rstd
+        constexpr bool NOFLOAT = (FL & FL_NOFLOAT) != 0 && OT::LN;
+        float v[NOFLOAT ? 1 : V][NOFLOAT ? 1 : E];  // LayerNorm: x - a; RMSNorm: x; softmax: exp
+        float scale;    // rstd, or 1 / sum for softmax
         float offset = 0.f;
         float a_keep = 0.f;  // LayerNorm: the rough mean a
-        if constexpr (OP == OP_LN) {
-            // ---- a3/a4, first pass: rough mean of this wave's part. The common reference
-            // K = x[row, 0] is needed by the cross-wave combine and, for fp32 rows, shifts
-            // this pass so that a constant row gives a == K exactly (for fp16 / bf16 rows
-            // the plain sums of a constant are exact already).
-            if constexpr (DT == DT_F32 && W == 1) K = uniform(IO::first(src[0]));  // lane 0 holds chunk 0
+        if constexpr (OT::LN) {
+            // ---- a3/a4, first pass: rough mean of this wave's part.
+            float K = 0.f;
             float s1 = 0.f;
             if constexpr (DT == DT_F32) {
+                K = uniform(IO::first(src[0]));  // lane 0 holds the wave's first chunk
 #pragma unroll
                 for (int i = 0; i < V; ++i) {
                     float f[E];
@@ -402,8 +558,7 @@ struct VecRow {
                 for (int i = 0; i < V; ++i) s1 = IO::sum(src[i], s1);
             }
             const float inv_w = W == 1 ? p.inv_n : (n_w > 0.f ? 1.0f / n_w : 0.f);  // constant when EXACT
-            const float mw = wave_sum(s1) * inv_w;
-            const float a = DT == DT_F32 ? K + mw : mw;
+            const float a = K + wave_sum(s1) * inv_w;
             // ---- centered pass.
             float c = 0.f, q = 0.f;
 #pragma unroll
@@ -421,62 +576,49 @@ struct VecRow {
             a_keep = a;
             const float Cw = wave_sum(c);
             const float Qw = wave_sum(q);
-            float rel;  // mean - a
-            float m2;   // sum of squared deviations
-            if constexpr (W == 1) {
-                rel = Cw * p.inv_n;
-                m2 = fmaxf(Qw - Cw * rel, 0.f);
-                if (t == 0 && p.mean) p.mean[row] = a + rel;
-            } else {
-                // ---- a5: per-wave (n, mean - K, M2), combined across the row group in LDS.
-                const float cw = Cw * inv_w;
-                Moments mo{n_w, (a - K) + cw, fmaxf(Qw - Cw * cw, 0.f)};
-                if (lane == 0) {
-                    part[buf][wr][0] = mo.n;
-                    part[buf][wr][1] = mo.m;
-                    part[buf][wr][2] = mo.m2;
-                }
-                __syncthreads();
-                Moments acc;
-                if constexpr (EXACT && (W & (W - 1)) == 0) {
-                    // equal parts: a fixed pairwise tree, (0,1) (2,3) ... then pairs of pairs
-                    Moments m[W];
-#pragma unroll
-                    for (int w = 0; w < W; ++w) m[w] = Moments{part[buf][w][0], part[buf][w][1], part[buf][w][2]};
-#pragma unroll
-                    for (int step = 1; step < W; step *= 2) {
-#pragma unroll
-                        for (int w = 0; w + step < W; w += 2 * step) m[w] = combine_equal(m[w], m[w + step]);
-                    }
-                    acc = m[0];
-                } else {
-                    acc = Moments{part[buf][0][0], part[buf][0][1], part[buf][0][2]};
-#pragma unroll
-                    for (int w = 1; w < W; ++w) acc = combine(acc, Moments{part[buf][w][0], part[buf][w][1], part[buf][w][2]});
-                }
-                buf ^= 1;
-                rel = acc.m - (a - K);  // row mean relative to this wave's a
-                m2 = acc.m2;
-                if (t == 0 && p.mean) p.mean[row] = K + acc.m;
-            }
+            const float cw = Cw * inv_w;
+            // ---- a5: per-wave (n, a, mean - a, M2), combined across the row group in LDS.
+            float rel, m2, mean;
+            group_moments<W, EXACT>(part, buf, lane, wr, n_w, a, cw, fmaxf(Qw - Cw * cw, 0.f), rel, m2, mean);
+            if (t == 0 && p.mean) p.mean[row] = mean;
             // ---- a6: finalize.
             scale = inv_sqrt(fmaf(m2, p.inv_n, p.eps));
             offset = -rel * scale;
             if (t == 0 && p.rstd) p.rstd[row] = scale;
+        } else if constexpr (OT::SM) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float f[E];
+                IO::unpack(src[i], f);
+#pragma unroll
+                for (int e = 0; e < E; ++e) mx = valid(i, t, Ci) ? fmaxf(mx, f[e]) : mx;
+            }
+            const float mw = wave_max(mx);
+            // exp(x - m_w): x - m_w is exact for the elements near the maximum.
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float f[E];
+                IO::unpack(src[i], f);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float ex = valid(i, t, Ci) ? exp_neg(f[e] - mw) : 0.f;
+                    v[i][e] = ex;
+                    s += ex;
+                }
+            }
+            float M, S;
+            group_softmax<W>(part, buf, lane, wr, mw, wave_sum(s), M, S);
+            scale = exp_neg(mw - M) / S;
+            if (t == 0 && p.mean) p.mean[row] = M;
+            if (t == 0 && p.rstd) p.rstd[row] = S;
         } else {
             // ---- RMSNorm statistics: sum of squares.
             float s = 0.f;
 #pragma unroll
             for (int i = 0; i < V; ++i) s = IO::sumsq(src[i], s);
-            float S = wave_sum(s);
-            if constexpr (W > 1) {
-                if (lane == 0) part[buf][wr][0] = S;
-                __syncthreads();
-                S = part[buf][0][0];
-#pragma unroll
-                for (int w = 1; w < W; ++w) S += part[buf][w][0];
-                buf ^= 1;
-            }
+            const float S = group_sum<W>(part, buf, lane, wr, wave_sum(s));
             scale = inv_sqrt(fmaf(S, p.inv_n, p.eps));
             if (t == 0 && p.rstd) p.rstd[row] = scale;
 #pragma unroll
@@ -489,8 +631,14 @@ struct VecRow {
             // rather than kept alive (as fp32 values) since the centered pass.
 #pragma unroll
             for (int i = 0; i < V; ++i) asm volatile("" : "+v"(src[i]));
+            // likewise the packed parameters: widen them here, not since their load
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                if constexpr (HG && PSRC == PARAMS_REG) asm volatile("" : "+v"(gv[i]));
+                if constexpr (HB && PSRC == PARAMS_REG) asm volatile("" : "+v"(bv[i]));
+            }
         }
-        u32x4* yr = static_cast<u32x4*>(p.y) + row * p.C;
+        u32x4* yr = static_cast<u32x4*>(p.y) + row * p.cy;
 #pragma unroll
         for (int i = 0; i < V; ++i) {
             float g[E], b[E], o[E];
@@ -520,7 +668,7 @@ struct VecRow {
                 if constexpr (NOFLOAT) {
                     z = fmaf(w[e], scale, offset);
                 } else {
-                    z = OP == OP_LN ? fmaf(v[i][e], scale, offset) : v[i][e] * scale;
+                    z = OT::LN ? fmaf(v[i][e], scale, offset) : v[i][e] * scale;
                 }
                 if constexpr (HG && HB) {
                     z = fmaf(z, g[e], b[e]);
@@ -551,7 +699,7 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_vec_kernel(Params p) {
     const int wr = wave - rg * W;  // wave index inside the row group
     const int t = wr * 64 + lane;  // lane index inside the row group
     const int Ci = static_cast<int>(p.C);  // chunks per row fit in 32 bits here (C <= 64 * W * V)
-    __shared__ float part[RPB][2][R::WS][3];
+    __shared__ WavePart part[RPB][2][R::WS];
     extern __shared__ u32x4 prm[];  // PLDS: gamma chunks [C], then beta chunks [C]
     constexpr bool GREG = PLDS && (FL & FL_GAMMA_REG) != 0 && R::HG && R::HB;
     u32x4 gkeep[GREG ? V : 1];  // GREG: this lane's gamma chunks, for all rows
@@ -581,16 +729,159 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_vec_kernel(Params p) {
             buf ^= 1;
             continue;
         }
+        // Per-lane addresses are recomputed for every row (a few VALU operations) rather than
+        // hoisted out of the loop, where they would hold two VGPRs each for the whole kernel.
+        int tl = t;
+        asm volatile("" : "+v"(tl));
         u32x4 xv[V], rv[R::NR], gv[R::NG], bv[R::NB];
-        float K = 0.f;
-        R::load_row(p, row, t, Ci, xv, rv, K);
-        if constexpr (PSRC == R::PARAMS_REG) R::load_params(p, t, Ci, gv, bv);
+        R::load_row(p, row, tl, Ci, xv, rv);
+        if constexpr (PSRC == R::PARAMS_REG) R::load_params(p, tl, Ci, gv, bv);
         if constexpr (GREG) {
 #pragma unroll
             for (int i = 0; i < V; ++i) gv[i] = gkeep[i];
         }
         __builtin_amdgcn_sched_barrier(0);  // every load of the row is issued before any use
-        R::template norm_row<PSRC>(p, row, lane, wr, t, Ci, xv, rv, K, gv, bv, prm, part[rg], buf);
+        R::template norm_row<PSRC>(p, row, lane, wr, tl, Ci, xv, rv, gv, bv, prm, part[rg], buf);
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Element kernel: rows that are not whole 16-byte chunks, or tensors that are only
+// element-aligned. The same register-resident structure with one element per slot: lane t
+// of a row group of W waves holds elements t, t + 64W, ... (V of them), loaded with
+// element-sized coalesced accesses, so the row is still read from HBM once.
+// ---------------------------------------------------------------------------------------
+
+template <int DT, int OP, int W, int V, int RPB, int AFF>
+__global__ __launch_bounds__(64 * W * RPB) void rownorm_elem_kernel(Params p) {
+    using IO = Io<DT>;
+    using OT = OpTraits<OP>;
+    constexpr int LANES = 64 * W;
+    constexpr int S = DT == DT_F32 ? 4 : 2;  // bytes per element
+    constexpr bool HG = !OT::SM && (AFF & AFF_G) != 0;
+    constexpr bool HB = OT::LN && (AFF & AFF_B) != 0;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int rg = wave / W;
+    const int wr = wave - rg * W;
+    const unsigned t = static_cast<unsigned>(wr * 64 + lane);
+    const unsigned N = static_cast<unsigned>(p.N);  // N <= 64 * W * V fits in 32 bits
+    __shared__ WavePart part_all[RPB][2][W > 1 ? W : 1];
+    WavePart(*part)[W > 1 ? W : 1] = part_all[rg];
+    // elements of this wave: slot i holds column i * LANES + wr * 64 + lane
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int k = static_cast<int>(N) - (i * LANES + wr * 64);
+        cnt += k <= 0 ? 0 : (k >= 64 ? 64 : k);
+    }
+    const float n_w = static_cast<float>(cnt);
+    int buf = 0;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * RPB; base < p.rows;
+         base += static_cast<int64_t>(gridDim.x) * RPB) {
+        const int64_t row = base + rg;
+        if (row >= p.rows) {
+            if constexpr (W == 1) break;
+            __syncthreads();
+            buf ^= 1;
+            continue;
+        }
+        // Row bases are wave-uniform; element offsets are 32-bit.
+        const char* xr = static_cast<const char*>(p.x) + row * p.ldx * S;
+        const char* rr = OT::RES ? static_cast<const char*>(p.residual) + row * p.ldr * S : nullptr;
+        float f[V];
+        // a1 (+ a2): load the row; the fused ops form, store and keep t = round(x + r)
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            const unsigned j = static_cast<unsigned>(i * LANES) + t;
+            f[i] = 0.f;
+            if (j < N) {
+                f[i] = IO::load1(xr, j);
+                if constexpr (OT::RES) f[i] += IO::load1(rr, j);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (OT::RES) {
+            char* orow = static_cast<char*>(p.residual_out) + row * p.ldro * S;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                const unsigned j = static_cast<unsigned>(i * LANES) + t;
+                f[i] = IO::round(f[i]);
+                if (j < N) IO::store1(orow, j, f[i]);
+            }
+        }
+        float scale, offset = 0.f;
+        if constexpr (OT::LN) {
+            const float K = uniform(f[0]);  // the wave's first element (0 if it holds none)
+            float s1 = 0.f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) s1 += static_cast<unsigned>(i * LANES) + t < N ? f[i] - K : 0.f;
+            const float inv_w = n_w > 0.f ? 1.0f / n_w : 0.f;
+            const float a = K + wave_sum(s1) * inv_w;
+            float c = 0.f, q = 0.f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                f[i] = static_cast<unsigned>(i * LANES) + t < N ? f[i] - a : 0.f;
+                c += f[i];
+                q = fmaf(f[i], f[i], q);
+            }
+            const float Cw = wave_sum(c);
+            const float Qw = wave_sum(q);
+            const float cw = Cw * inv_w;
+            float rel, m2, mean;
+            group_moments<W, false>(part, buf, lane, wr, n_w, a, cw, fmaxf(Qw - Cw * cw, 0.f), rel, m2, mean);
+            if (t == 0 && p.mean) p.mean[row] = mean;
+            scale = inv_sqrt(fmaf(m2, p.inv_n, p.eps));
+            offset = -rel * scale;
+            if (t == 0 && p.rstd) p.rstd[row] = scale;
+        } else if constexpr (OT::SM) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < V; ++i) mx = static_cast<unsigned>(i * LANES) + t < N ? fmaxf(mx, f[i]) : mx;
+            const float mw = wave_max(mx);
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                f[i] = static_cast<unsigned>(i * LANES) + t < N ? exp_neg(f[i] - mw) : 0.f;
+                s += f[i];
+            }
+            float M, Ssum;
+            group_softmax<W>(part, buf, lane, wr, mw, wave_sum(s), M, Ssum);
+            scale = exp_neg(mw - M) / Ssum;
+            if (t == 0 && p.mean) p.mean[row] = M;
+            if (t == 0 && p.rstd) p.rstd[row] = Ssum;
+        } else {
+            float s = 0.f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) s = fmaf(f[i], f[i], s);
+            const float Ssq = group_sum<W>(part, buf, lane, wr, wave_sum(s));
+            scale = inv_sqrt(fmaf(Ssq, p.inv_n, p.eps));
+            if (t == 0 && p.rstd) p.rstd[row] = scale;
+        }
+        // a7: the parameters are loaded here, after the row's addresses are dead (they are
+        // small and cache-resident), then normalize and store.
+        float g[HG ? V : 1], b[HB ? V : 1];
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            const unsigned j = static_cast<unsigned>(i * LANES) + t;
+            const unsigned jc = j < N ? j : N - 1;
+            if constexpr (HG) g[i] = IO::load1(p.gamma, jc);
+            if constexpr (HB) b[i] = IO::load1(p.beta, jc);
+        }
+        char* yrow = static_cast<char*>(p.y) + row * p.ldy * S;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            const unsigned j = static_cast<unsigned>(i * LANES) + t;
+            float z = OT::LN ? fmaf(f[i], scale, offset) : f[i] * scale;
+            if constexpr (HG && HB) {
+                z = fmaf(z, g[i], b[i]);
+            } else if constexpr (HG) {
+                z = z * g[i];
+            } else if constexpr (HB) {
+                z = z + b[i];
+            }
+            if (j < N) IO::store1(yrow, j, z);
+        }
     }
 }
 
@@ -609,25 +900,77 @@ __device__ __forceinline__ float block_sum(float v, float* slots) {
     return s;
 }
 
+template <int NWAVES>
+__device__ __forceinline__ float block_max(float v, float* slots) {
+    const float w = wave_max(v);
+    if ((threadIdx.x & 63) == 0) slots[threadIdx.x >> 6] = w;
+    __syncthreads();
+    float s = slots[0];
+#pragma unroll
+    for (int i = 1; i < NWAVES; ++i) s = fmaxf(s, slots[i]);
+    return s;
+}
+
 template <int DT, int OP>
 __global__ __launch_bounds__(kGeneralThreads) void rownorm_general_kernel(Params p) {
     using IO = Io<DT>;
+    using OT = OpTraits<OP>;
     constexpr int NW = kGeneralThreads / 64;
-    __shared__ float slots[2][NW];
+    __shared__ float slots[3][NW];
     const int tid = threadIdx.x;
     const int64_t N = p.N;
     const float nf = static_cast<float>(N);
     for (int64_t row = blockIdx.x; row < p.rows; row += gridDim.x) {
-        const int64_t off = row * N;
-        float center = 0.f, scale, K = 0.f;
-        if constexpr (OP == OP_LN) {
-            K = IO::load1(p.x, off);
+        const int64_t xo = row * p.ldx, ro = row * p.ldr, yo = row * p.ldy, oo = row * p.ldro;
+        // The row's source values: x, or for the fused ops residual_out (written by the
+        // same lane in the first sweep, so re-reading it is safe under exact aliasing).
+        float center = 0.f, scale = 1.f, K = 0.f;
+        if constexpr (OT::RES) {
+            if constexpr (OT::LN) K = IO::round(IO::load1(p.x, xo) + IO::load1(p.residual, ro));
+            __syncthreads();  // K is read before any lane overwrites x / residual in place
+            float s = 0.f;
+            for (int64_t j = tid; j < N; j += kGeneralThreads) {
+                const float v = IO::round(IO::load1(p.x, xo + j) + IO::load1(p.residual, ro + j));
+                IO::store1(p.residual_out, oo + j, v);
+                s += OT::LN ? v - K : v * v;
+            }
+            if constexpr (OT::LN) {
+                center = block_sum<NW>(s, slots[0]) / nf;
+            } else {
+                scale = inv_sqrt(block_sum<NW>(s, slots[0]) / nf + p.eps);
+            }
+        } else if constexpr (OT::LN) {
+            K = IO::load1(p.x, xo);
             float s1 = 0.f;
-            for (int64_t j = tid; j < N; j += kGeneralThreads) s1 += IO::load1(p.x, off + j) - K;
+            for (int64_t j = tid; j < N; j += kGeneralThreads) s1 += IO::load1(p.x, xo + j) - K;
             center = block_sum<NW>(s1, slots[0]) / nf;
+        } else if constexpr (OT::SM) {
+            float m = -INFINITY;
+            for (int64_t j = tid; j < N; j += kGeneralThreads) m = fmaxf(m, IO::load1(p.x, xo + j));
+            K = block_max<NW>(m, slots[0]);
+            float s = 0.f;
+            for (int64_t j = tid; j < N; j += kGeneralThreads)
+                s += exp_neg(IO::load1(p.x, xo + j) - K);
+            const float S = block_sum<NW>(s, slots[1]);
+            scale = 1.0f / S;
+            if (tid == 0) {
+                if (p.mean) p.mean[row] = K;
+                if (p.rstd) p.rstd[row] = S;
+            }
+        } else {
+            float s = 0.f;
+            for (int64_t j = tid; j < N; j += kGeneralThreads) {
+                const float v = IO::load1(p.x, xo + j);
+                s += v * v;
+            }
+            scale = inv_sqrt(block_sum<NW>(s, slots[0]) / nf + p.eps);
+        }
+        const void* src = OT::RES ? static_cast<const void*>(p.residual_out) : p.x;
+        const int64_t so = OT::RES ? oo : xo;
+        if constexpr (OT::LN) {
             float s2 = 0.f;
             for (int64_t j = tid; j < N; j += kGeneralThreads) {
-                const float d = (IO::load1(p.x, off + j) - K) - center;
+                const float d = (IO::load1(src, so + j) - K) - center;
                 s2 += d * d;
             }
             scale = inv_sqrt(block_sum<NW>(s2, slots[1]) / nf + p.eps);
@@ -635,34 +978,23 @@ __global__ __launch_bounds__(kGeneralThreads) void rownorm_general_kernel(Params
                 if (p.mean) p.mean[row] = K + center;
                 if (p.rstd) p.rstd[row] = scale;
             }
-        } else {
-            float s = 0.f;
-            for (int64_t j = tid; j < N; j += kGeneralThreads) {
-                float v;
-                if constexpr (OP == OP_FUSED) {
-                    v = IO::round(IO::load1(p.x, off + j) + IO::load1(p.residual, off + j));
-                    IO::store1(p.residual_out, off + j, v);
-                } else {
-                    v = IO::load1(p.x, off + j);
-                }
-                s += v * v;
-            }
-            scale = inv_sqrt(block_sum<NW>(s, slots[0]) / nf + p.eps);
+        } else if constexpr (!OT::SM) {
             if (tid == 0 && p.rstd) p.rstd[row] = scale;
         }
         for (int64_t j = tid; j < N; j += kGeneralThreads) {
-            const float g = p.gamma ? IO::load1(p.gamma, j) : 1.f;
+            const float v = IO::load1(src, so + j);
             float o;
-            if constexpr (OP == OP_LN) {
+            if constexpr (OT::LN) {
+                const float g = p.gamma ? IO::load1(p.gamma, j) : 1.f;
                 const float b = p.beta ? IO::load1(p.beta, j) : 0.f;
-                o = ((IO::load1(p.x, off + j) - K) - center) * scale * g + b;
-            } else if constexpr (OP == OP_FUSED) {
-                // this lane's own residual_out element, written above
-                o = IO::load1(p.residual_out, off + j) * scale * g;
+                o = ((v - K) - center) * scale * g + b;
+            } else if constexpr (OT::SM) {
+                o = exp_neg(v - K) * scale;
             } else {
-                o = IO::load1(p.x, off + j) * scale * g;
+                const float g = p.gamma ? IO::load1(p.gamma, j) : 1.f;
+                o = v * scale * g;
             }
-            IO::store1(p.y, off + j, o);
+            IO::store1(p.y, yo + j, o);
         }
         __syncthreads();  // slots are reused by the next row
     }
@@ -670,8 +1002,8 @@ __global__ __launch_bounds__(kGeneralThreads) void rownorm_general_kernel(Params
 
 // ---------------------------------------------------------------------------------------
 // Dispatch from a runtime plan to a template instance. Instantiated per dtype and mode in
-// rownorm_kernels_<dtype>.hip (grid-per-row launches and the general kernel) and
-// rownorm_kernels_<dtype>_persistent.hip (persistent launches).
+// rownorm_kernels_<dtype>.hip (grid-per-row launches, the element and the general kernel)
+// and rownorm_kernels_<dtype>_persistent.hip (persistent launches).
 // ---------------------------------------------------------------------------------------
 
 // Row groups per workgroup for a row-group width: 256-lane workgroups up to W = 4.
@@ -683,8 +1015,8 @@ constexpr int rows_per_block_for(int W) { return W <= 4 ? 4 / W : 1; }
 template <int OP, int AFF>
 constexpr int persistent_flags() {
     int fl = FL_NT_LOAD | FL_NT_STORE | FL_PARAMS_LDS;
-    if (OP == OP_LN) fl |= FL_NOFLOAT;
-    if (OP == OP_LN && AFF == (AFF_G | AFF_B)) fl |= FL_GAMMA_REG;
+    if (OpTraits<OP>::LN) fl |= FL_NOFLOAT;
+    if (OpTraits<OP>::LN && AFF == (AFF_G | AFF_B)) fl |= FL_GAMMA_REG;
     return fl;
 }
 
@@ -733,7 +1065,8 @@ inline hipError_t go_persistent(K kernel, const Plan& plan, const Params& p, hip
 template <int DT, int OP, int W, bool EXACT, int AFF, bool PERS>
 inline hipError_t launch_v(const Plan& plan, const Params& p, hipStream_t s) {
     constexpr int RPB = rows_per_block_for(W);
-    constexpr int FL = PERS ? persistent_flags<OP, AFF>() : 0;
+    // 1024-lane workgroups have 128 VGPRs per lane: LayerNorm rows there keep no fp32 copy.
+    constexpr int FL = PERS ? persistent_flags<OP, AFF>() : (W >= 16 && OpTraits<OP>::LN ? FL_NOFLOAT : 0);
     if (plan.rows_per_block != RPB) return hipErrorInvalidValue;
 #define RN_GO(VV) \
     (PERS ? go_persistent(rownorm_vec_kernel<DT, OP, W, VV, RPB, EXACT, AFF, FL>, plan, p, s) \
@@ -780,24 +1113,71 @@ inline hipError_t launch_e(const Plan& plan, const Params& p, hipStream_t s) {
     }
 }
 
+// Element kernel instances: W = 1 with 1-8 elements per lane; W = 2, 4, 8 with 8; W = 16
+// with 8 or 16 (rows of up to 16384 elements). Parameter presence is a runtime check here.
+template <int DT, int OP>
+inline hipError_t launch_elem(const Plan& plan, const Params& p, hipStream_t s) {
+    const int W = plan.waves_per_row, V = plan.chunks_per_lane;
+    const int aff = (p.gamma ? AFF_G : 0) | (OpTraits<OP>::LN && p.beta ? AFF_B : 0);
+    if (plan.rows_per_block != rows_per_block_for(W)) return hipErrorInvalidValue;
+#define RN_EL(WW, VV, A) go(rownorm_elem_kernel<DT, OP, WW, VV, rows_per_block_for(WW), A>, plan, p, s)
+#define RN_EL_AFF(WW, VV)                                                     \
+    do {                                                                      \
+        if constexpr (OpTraits<OP>::SM) return RN_EL(WW, VV, 0);              \
+        if (aff == 0) return RN_EL(WW, VV, 0);                                \
+        if (aff == AFF_G) return RN_EL(WW, VV, AFF_G);                        \
+        if constexpr (OpTraits<OP>::LN) {                                     \
+            if (aff == AFF_B) return RN_EL(WW, VV, AFF_B);                    \
+            return RN_EL(WW, VV, AFF_G | AFF_B);                              \
+        }                                                                     \
+        return hipErrorInvalidValue;                                          \
+    } while (0)
+    if (W == 1) {
+        switch (V) {
+        case 1: RN_EL_AFF(1, 1);
+        case 2: RN_EL_AFF(1, 2);
+        case 4: RN_EL_AFF(1, 4);
+        case 8: RN_EL_AFF(1, 8);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (W == 2 && V == 8) RN_EL_AFF(2, 8);
+    if (W == 4 && V == 8) RN_EL_AFF(4, 8);
+    if (W == 8 && V == 8) RN_EL_AFF(8, 8);
+    if (W == 16 && V == 8) RN_EL_AFF(16, 8);
+    if (W == 16 && V == 16) RN_EL_AFF(16, 16);
+#undef RN_EL_AFF
+#undef RN_EL
+    return hipErrorInvalidValue;
+}
+
 template <int DT, int OP, bool PERS>
 inline hipError_t launch_op(const Plan& plan, const Params& p, hipStream_t s) {
-    if (plan.variant == V_GENERAL) {
-        if constexpr (PERS) return hipErrorInvalidValue;
-        return go(rownorm_general_kernel<DT, OP>, plan, p, s);
+    if (plan.variant == V_GENERAL || plan.variant == V_ELEMENT) {
+        if constexpr (PERS) {
+            return hipErrorInvalidValue;
+        } else {
+            if (plan.variant == V_ELEMENT) return launch_elem<DT, OP>(plan, p, s);
+            return go(rownorm_general_kernel<DT, OP>, plan, p, s);
+        }
     }
     if (plan.variant != V_WAVE && plan.variant != V_WORKGROUP) return hipErrorInvalidValue;
-    const int aff = (p.gamma ? AFF_G : 0) | (OP == OP_LN && p.beta ? AFF_B : 0);
-    switch (aff) {
-    case 0: return launch_e<DT, OP, 0, PERS>(plan, p, s);
-    case AFF_G: return launch_e<DT, OP, AFF_G, PERS>(plan, p, s);
-    default: break;
+    if constexpr (OpTraits<OP>::SM) {
+        if constexpr (PERS) return hipErrorInvalidValue;
+        return launch_e<DT, OP, 0, false>(plan, p, s);
+    } else {
+        const int aff = (p.gamma ? AFF_G : 0) | (OpTraits<OP>::LN && p.beta ? AFF_B : 0);
+        switch (aff) {
+        case 0: return launch_e<DT, OP, 0, PERS>(plan, p, s);
+        case AFF_G: return launch_e<DT, OP, AFF_G, PERS>(plan, p, s);
+        default: break;
+        }
+        if constexpr (OpTraits<OP>::LN) {
+            if (aff == AFF_B) return launch_e<DT, OP, AFF_B, PERS>(plan, p, s);
+            return launch_e<DT, OP, AFF_G | AFF_B, PERS>(plan, p, s);
+        }
+        return hipErrorInvalidValue;
     }
-    if constexpr (OP == OP_LN) {
-        if (aff == AFF_B) return launch_e<DT, OP, AFF_B, PERS>(plan, p, s);
-        return launch_e<DT, OP, AFF_G | AFF_B, PERS>(plan, p, s);
-    }
-    return hipErrorInvalidValue;
 }
 
 template <int DT, bool PERS>
@@ -806,6 +1186,8 @@ inline hipError_t launch_dtype(int op, const Plan& plan, const Params& p, hipStr
     case OP_LN: return launch_op<DT, OP_LN, PERS>(plan, p, s);
     case OP_RMS: return launch_op<DT, OP_RMS, PERS>(plan, p, s);
     case OP_FUSED: return launch_op<DT, OP_FUSED, PERS>(plan, p, s);
+    case OP_FUSED_LN: return launch_op<DT, OP_FUSED_LN, PERS>(plan, p, s);
+    case OP_SOFTMAX: return launch_op<DT, OP_SOFTMAX, PERS>(plan, p, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -12,6 +12,16 @@
 * mean: |mean_gpu - mean_ref| <= 1e-5 * max(|mean_ref|, sigma_ref), sigma_ref = sqrt(var);
   rstd: |rstd_gpu / rstd_ref - 1| <= 1e-5.
 * residual_out: bit-exact.
+* softmax y: fp32 |y_gpu - y_ref| <= 1e-5 * y_ref + 2^-126; fp16 / bf16 as above (2 ulps).
+  Derivation for fp32: each output is exp(x - m_w) * exp(m_w - m) / S. x - m_w is exact
+  near the maximum; the kernel evaluates exp with a split argument (u * log2 e formed
+  exactly as hi + lo, 2^n applied by ldexp, v_exp_f32 only on [-0.5, 0.5]), so each
+  exponential is within a few ulps relative for every argument (a plain v_exp_f32 of
+  u * log2 e loses about |u| * 2^-23 relative: 1e-5 at u = -55). The rescaling and the
+  division add a few ulps, and S (per-lane sums of <= 16 terms, a 6-level lane tree, at
+  most 16 wave parts) at most (16 + 6 + 16) * 2^-24 = 2.3e-6 relative. The total stays
+  below 1e-5; the absolute floor covers results in the subnormal range.
+  row_max: bit-exact (a maximum of the inputs); row_sum: relative <= 1e-5.
 """
 
 from __future__ import annotations
@@ -79,3 +89,32 @@ def check_bits_equal(a: torch.Tensor, ref_bits: np.ndarray, what: str):
     bits = bits.reshape(ref_bits.shape)
     diff = bits != ref_bits
     assert not diff.any(), f"{what}: {int(diff.sum())} elements differ from the correctly rounded sum"
+
+
+SOFTMAX_REL_TOL = 1e-5
+SOFTMAX_ABS_FLOOR = 2.0 ** -126
+
+
+def check_softmax_y(y_gpu: torch.Tensor, y_ref: np.ndarray) -> float:
+    dt = dtype_name(y_gpu)
+    if dt != "fp32":
+        return check_y(y_gpu, y_ref, "softmax y")
+    got = y_gpu.detach().cpu().double().numpy().reshape(y_ref.shape)
+    assert np.all(np.isfinite(got)), "softmax y: non-finite outputs"
+    err = np.abs(got - y_ref)
+    bad = err > SOFTMAX_REL_TOL * np.abs(y_ref) + SOFTMAX_ABS_FLOOR
+    assert not bad.any(), f"softmax y: {int(bad.sum())} elements off, worst relative {float((err / np.maximum(y_ref, 1e-300)).max()):.3g}"
+    return float((err / np.maximum(y_ref, 1e-300)).max()) if err.size else 0.0
+
+
+def check_rel(got_t: torch.Tensor, ref: np.ndarray, tol: float, what: str):
+    got = got_t.detach().cpu().double().numpy().reshape(-1)
+    rel = np.abs(got / ref - 1.0)
+    worst = float(rel.max()) if rel.size else 0.0
+    assert worst <= tol, f"{what}: worst relative error {worst:.3g}"
+
+
+def check_equal_values(got_t: torch.Tensor, ref: np.ndarray, what: str):
+    got = got_t.detach().cpu().double().numpy().reshape(-1)
+    diff = got != ref.reshape(-1)
+    assert not diff.any(), f"{what}: {int(diff.sum())} values differ"

@@ -31,7 +31,8 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(rn.LIB_PATH)
     names = _declared_functions()
-    for n in ("ln_forward", "rms_norm", "fused_add_rms_norm", "rn_plan", "rn_status_string"):
+    for n in ("ln_forward", "rms_norm", "fused_add_rms_norm", "fused_add_layer_norm", "softmax_forward",
+              "rn_forward_ex", "rn_plan", "rn_status_string"):
         assert n in names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -41,7 +42,7 @@ def test_status_strings_and_version():
     for code, name in rn.STATUS.items():
         assert rn._lib.rn_status_string(code).decode() == name
     assert rn._lib.rn_status_string(99).decode() == "unknown status"
-    assert rn.version() == 10000
+    assert rn.version() == 10100
 
 
 @pytest.mark.parametrize("op,dtype,rows,N,variant,W,V,persistent", [
@@ -56,8 +57,15 @@ def test_status_strings_and_version():
     ("rms", torch.bfloat16, 16, 32768, "workgroup", 16, 4, False),
     ("ln", torch.float32, 16, 16388, "general", 0, 0, False),          # beyond a workgroup's registers
     ("ln", torch.float32, 16, 1000, "wave", 1, 4, False),              # ragged: 250 chunks
-    ("ln", torch.float16, 16, 1001, "general", 0, 0, False),           # not a whole number of 16-byte chunks
-    ("rms", torch.float32, 3, 1, "general", 0, 0, False),
+    ("ln", torch.float16, 16, 1001, "element", 2, 8, False),           # not a whole number of 16-byte chunks
+    ("rms", torch.float32, 3, 1, "element", 1, 1, False),
+    ("rms", torch.bfloat16, 8, 16383, "element", 16, 16, False),
+    ("ln", torch.bfloat16, 8, 16385, "general", 0, 0, False),          # odd and beyond the element kernel
+    ("fused_add_ln", torch.bfloat16, 8192, 4096, "workgroup", 2, 4, True),
+    ("fused_add_ln", torch.float32, 256, 4096, "workgroup", 4, 4, False),
+    ("softmax", torch.float32, 128, 4096, "workgroup", 4, 4, False),
+    ("softmax", torch.float32, 8192, 4096, "workgroup", 4, 4, False),  # no parameters: never persistent
+    ("softmax", torch.float16, 64, 333, "element", 1, 8, False),
 ])
 def test_plan_variant_choice(op, dtype, rows, N, variant, W, V, persistent):
     ptrs = {"gamma": 1 << 44, "beta": (1 << 44) + (1 << 30)}
@@ -68,6 +76,10 @@ def test_plan_variant_choice(op, dtype, rows, N, variant, W, V, persistent):
     assert info["persistent"] == persistent
     if variant == "general":
         assert info["grid_blocks"] == rows and info["block_threads"] == 256
+        return
+    if variant == "element":
+        assert info["waves_per_row"] == W and not info["exact"] and not info["persistent"]
+        assert 64 * W * V >= N and (V == 1 or 64 * W * V // 2 < N or W > 1)
         return
     assert info["waves_per_row"] == W
     rpb = 4 // W if W <= 4 else 1
@@ -94,11 +106,36 @@ def test_plan_grid_is_capped():
     assert st == OK and info["grid_blocks"] == 1 << 20
 
 
-def test_plan_misaligned_pointer_takes_general_path():
+def test_plan_misaligned_pointer_takes_element_path():
     st, info = rn.plan("ln", 8, 1024, torch.float32, ptrs={"x": (1 << 40) + 4})
-    assert st == OK and info["variant"] == "general"
+    assert st == OK and info["variant"] == "element" and info["waves_per_row"] == 2
     st, _ = rn.plan("ln", 8, 1024, torch.float32, ptrs={"x": (1 << 40) + 4}, variant="wave")
     assert st == UNSUP
+    st, info = rn.plan("ln", 8, 32768, torch.float16, ptrs={"x": (1 << 40) + 2})
+    assert st == OK and info["variant"] == "general"
+
+
+def test_plan_row_strides():
+    f16 = torch.float16
+    # padded rows whose stride is a whole number of 16-byte chunks keep the vectorized path
+    st, info = rn.plan("ln", 64, 4096, f16, strides={"x": 4096 + 64, "y": 4096})
+    assert st == OK and info["variant"] == "workgroup"
+    # a stride that is not a whole chunk takes the element kernel
+    st, info = rn.plan("ln", 64, 4096, f16, strides={"x": 4097})
+    assert st == OK and info["variant"] == "element"
+    st, _ = rn.plan("ln", 64, 4096, f16, strides={"x": 4097}, variant="workgroup")
+    assert st == UNSUP
+    # stride below N, or absurdly large
+    assert rn.plan("ln", 64, 4096, f16, strides={"y": 4095})[0] == SHAPE
+    assert rn.plan("ln", 4, 64, f16, strides={"x": 1 << 41})[0] == SHAPE
+    # unused entries are ignored (no residual in LayerNorm)
+    assert rn.plan("ln", 4, 64, f16, strides={"residual": 1})[0] == OK
+    # in place needs the same stride
+    base = 1 << 40
+    assert rn.plan("rms", 4, 64, f16, ptrs={"x": base, "y": base}, strides={"x": 128, "y": 128})[0] == OK
+    assert rn.plan("rms", 4, 64, f16, ptrs={"x": base, "y": base}, strides={"x": 128})[0] == ALIAS
+    # two column slices of one buffer interleave: refused (address ranges overlap)
+    assert rn.plan("rms", 4, 64, f16, ptrs={"x": base, "y": base + 128}, strides={"x": 128, "y": 128})[0] == ALIAS
 
 
 def test_plan_forced_variants():
@@ -109,6 +146,8 @@ def test_plan_forced_variants():
     assert rn.plan("ln", 4, 8192, torch.float32, variant="wave")[0] == UNSUP
     assert rn.plan("ln", 4, 32768, torch.float32, variant="workgroup")[0] == UNSUP
     assert rn.plan("ln", 4, 64, torch.float32, variant="general")[1]["variant"] == "general"
+    assert rn.plan("ln", 4, 4096, torch.float32, variant="element")[1]["variant"] == "element"
+    assert rn.plan("ln", 4, 16385, torch.float32, variant="element")[0] == UNSUP
     assert rn.plan("ln", 4, 64, torch.float32, variant=7)[0] == UNSUP
 
 
@@ -173,6 +212,12 @@ def test_entry_points_reject_before_launch():
     assert lib.fused_add_rms_norm(0x1000, None, None, 0x100000, 0x200000, None, 4, 64, 1e-6, 1, None) == NULL
     assert lib.ln_forward_variant(0x1000, None, None, 0x100000, None, None, 4, 8192, 1e-5, 0, None, 1) == UNSUP
     assert lib.ln_forward(None, None, None, None, None, None, 0, 64, 1e-5, 0, None) == OK
+    assert lib.softmax_forward(None, 0x100000, None, None, 4, 64, 0, None) == NULL
+    assert lib.softmax_forward(0x1000, 0x1000 + 64, None, None, 4, 64, 0, None) == ALIAS
+    assert lib.fused_add_layer_norm(0x1000, 0x200000, None, None, 0x300000, None, None, None, 4, 64, 1e-5, 2,
+                                    None) == NULL
+    assert lib.rn_forward_ex(9, 0x1000, None, None, None, 0x100000, None, None, None, 4, 64, 1e-5, 0, None, 0,
+                             None) == SHAPE
 
 
 def test_python_binding_rejects_cpu_tensors():

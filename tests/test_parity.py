@@ -14,7 +14,8 @@ import torch
 import oracle
 import row_wise_normalization_fp32_amd as rn
 import workloads
-from _compare import check_bits_equal, check_mean, check_rstd, check_y, dtype_name
+from _compare import (STAT_REL_TOL, check_bits_equal, check_equal_values, check_mean, check_rel, check_rstd,
+                      check_softmax_y, check_y, dtype_name)
 
 pytestmark = pytest.mark.gpu
 
@@ -28,16 +29,26 @@ def _gpu(inp):
 
 
 def run_gpu(w: workloads.Workload, inp, variant="auto", stats=True):
+    """Returns (y, second, third, fourth): LayerNorm (y, mean, rstd, None); RMSNorm (y, None,
+    rstd, None); fused add + RMSNorm (y, residual_out, rstd, None); fused add + LayerNorm
+    (y, residual_out, rstd, mean); softmax (y, None, row_sum, row_max)."""
     g = _gpu(inp)
     if w.op == "ln":
         out = rn.ln_forward(g["x"], g.get("gamma"), g.get("beta"), w.eps, return_stats=stats, variant=variant)
-        return (out if stats else (out, None, None))
+        return (out + (None,)) if stats else (out, None, None, None)
     if w.op == "rms":
         y, rstd = rn.rms_norm(g["x"], g.get("weight"), w.eps, return_rstd=True, variant=variant)
-        return y, None, rstd
+        return y, None, rstd, None
+    if w.op == "fused_add_ln":
+        y, ro, mean, rstd = rn.fused_add_layer_norm(g["x"], g["residual"], g.get("gamma"), g.get("beta"), w.eps,
+                                                    return_stats=True, variant=variant)
+        return y, ro, rstd, mean
+    if w.op == "softmax":
+        y, mx, sm = rn.softmax_forward(g["x"], return_stats=True, variant=variant)
+        return y, None, sm, mx
     y, ro, rstd = rn.fused_add_rms_norm(g["x"], g["residual"], g.get("weight"), w.eps, return_rstd=True,
                                         variant=variant)
-    return y, ro, rstd
+    return y, ro, rstd, None
 
 
 def run_oracle(w: workloads.Workload, inp):
@@ -45,24 +56,42 @@ def run_oracle(w: workloads.Workload, inp):
         return oracle.layer_norm(inp["x"], inp.get("gamma"), inp.get("beta"), w.eps, threads=THREADS)
     if w.op == "rms":
         return oracle.rms_norm(inp["x"], inp.get("weight"), w.eps, threads=THREADS)
+    if w.op == "fused_add_ln":
+        return oracle.fused_add_layer_norm(inp["x"], inp["residual"], inp.get("gamma"), inp.get("beta"), w.eps,
+                                           threads=THREADS)
+    if w.op == "softmax":
+        return oracle.softmax(inp["x"], threads=THREADS)
     return oracle.fused_add_rms_norm(inp["x"], inp["residual"], inp.get("weight"), w.eps, threads=THREADS)
 
 
-def check_case(w: workloads.Workload, variant="auto", inp=None):
-    inp = workloads.make_inputs(w) if inp is None else inp
-    ref = run_oracle(w, inp)
-    a, b, c = run_gpu(w, inp, variant)
-    torch.cuda.synchronize()
+def check_outputs(w: workloads.Workload, ref, a, b, c, d):
+    if w.op == "softmax":
+        err = check_softmax_y(a, ref["y"])
+        check_equal_values(d, ref["max"], "row_max")
+        check_rel(c, ref["sum"], STAT_REL_TOL, "row_sum")
+        return err
     err = check_y(a, ref["y"])
     if w.op == "ln":
         check_mean(b, ref["mean"], ref["rstd"], w.eps)
         check_rstd(c, ref["rstd"])
     elif w.op == "rms":
         check_rstd(c, ref["rstd"])
+    elif w.op == "fused_add_ln":
+        check_bits_equal(b, ref["residual_out"], "residual_out")
+        check_mean(d, ref["mean"], ref["rstd"], w.eps)
+        check_rstd(c, ref["rstd"])
     else:
         check_bits_equal(b, ref["residual_out"], "residual_out")
         check_rstd(c, ref["rstd"])
     return err
+
+
+def check_case(w: workloads.Workload, variant="auto", inp=None):
+    inp = workloads.make_inputs(w) if inp is None else inp
+    ref = run_oracle(w, inp)
+    a, b, c, d = run_gpu(w, inp, variant)
+    torch.cuda.synchronize()
+    return check_outputs(w, ref, a, b, c, d)
 
 
 # ---------------------------------------------------------------------------------------
@@ -79,6 +108,12 @@ def test_fused_large_shape():
     check_case(workloads.FUSED_8192)
 
 
+@pytest.mark.parametrize("w", [workloads.FUSED_LN, workloads.FUSED_LN_8192, workloads.SOFTMAX,
+                               workloads.SOFTMAX_8192], ids=lambda w: w.name)
+def test_new_ops_full_size(w):
+    check_case(w)
+
+
 # ---------------------------------------------------------------------------------------
 # Every kernel variant on shapes spanning several tiles and a ragged tail.
 # ---------------------------------------------------------------------------------------
@@ -86,11 +121,15 @@ def test_fused_large_shape():
 SHAPES = [(37, 1000), (5, 4096), (9, 2056), (3, 8)]
 
 
-@pytest.mark.parametrize("variant", ["wave", "workgroup", "general"])
-@pytest.mark.parametrize("op", ["ln", "rms", "fused_add_rms"])
+BASES = {"ln": workloads.C1, "rms": workloads.C3, "fused_add_rms": workloads.C4_FP16,
+         "fused_add_ln": workloads.FUSED_LN, "softmax": workloads.SOFTMAX}
+
+
+@pytest.mark.parametrize("variant", ["wave", "workgroup", "element", "general"])
+@pytest.mark.parametrize("op", ["ln", "rms", "fused_add_rms", "fused_add_ln", "softmax"])
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
 def test_variants_agree_with_oracle(variant, op, dtype):
-    base = {"ln": workloads.C1, "rms": workloads.C3, "fused_add_rms": workloads.C4_FP16}[op]
+    base = BASES[op]
     for rows, N in SHAPES:
         w = base.scaled(rows=rows, N=N, seed=500 + rows, dtype=dtype)
         check_case(w, variant)
@@ -117,10 +156,19 @@ def test_offset_rows_on_every_variant():
 # Edge cases.
 # ---------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("N", [1, 2, 3, 7, 64, 255, 1023, 4097, 8191, 20000])
+@pytest.mark.parametrize("N", [1, 2, 3, 7, 64, 255, 1023, 4097, 8191, 16383, 16385, 20000])
 def test_odd_widths(N):
-    for op, base in (("ln", workloads.C1), ("rms", workloads.C3), ("fused_add_rms", workloads.C4_BF16)):
+    for op, base in (("ln", workloads.C1), ("rms", workloads.C3), ("fused_add_rms", workloads.C4_BF16),
+                     ("fused_add_ln", workloads.FUSED_LN), ("softmax", workloads.SOFTMAX.scaled(dtype="fp16"))):
         check_case(base.scaled(rows=3, N=N, seed=700 + N))
+
+
+@pytest.mark.parametrize("op", ["ln", "rms", "fused_add_rms", "fused_add_ln", "softmax"])
+def test_element_kernel_every_width(op):
+    # the element kernel's (W, V) instances: W = 1 with V = 1..8, W = 2..16 with V = 8, W = 16 with V = 16
+    for rows, N in [(5, 33), (4, 100), (3, 300), (6, 511), (5, 1000), (3, 2047), (2, 4093), (2, 8191),
+                    (2, 12289), (2, 16384)]:
+        check_case(BASES[op].scaled(rows=rows, N=N, seed=710 + N, dtype="bf16"), "element")
 
 
 def test_zero_rows_is_a_noop():
@@ -156,7 +204,7 @@ def test_constant_rows_map_to_beta():
             assert torch.equal(mean, g["x"][:, 0].float())
 
 
-def test_misaligned_pointers_use_general_path():
+def test_misaligned_pointers_use_element_path():
     w = workloads.C1.scaled(rows=5, N=1024, seed=820)
     inp = workloads.make_inputs(w)
     ref = run_oracle(w, inp)
@@ -164,14 +212,14 @@ def test_misaligned_pointers_use_general_path():
     x = buf[1:].view(5, 1024)
     x.copy_(inp["x"].to(DEV))
     st, info = rn.plan("ln", 5, 1024, torch.float32, ptrs={"x": x.data_ptr()})
-    assert info["variant"] == "general"
+    assert info["variant"] == "element"
     y, mean, rstd = rn.ln_forward(x, inp["gamma"].to(DEV), inp["beta"].to(DEV), w.eps, return_stats=True)
     torch.cuda.synchronize()
     check_y(y, ref["y"])
     check_rstd(rstd, ref["rstd"])
 
 
-@pytest.mark.parametrize("variant", ["wave", "workgroup", "general"])
+@pytest.mark.parametrize("variant", ["wave", "workgroup", "element", "general"])
 def test_in_place(variant):
     w = workloads.C1.scaled(rows=11, N=2048, seed=830, dtype="bf16")
     inp = workloads.make_inputs(w)
@@ -198,6 +246,77 @@ def test_in_place(variant):
     torch.cuda.synchronize()
     check_y(r, ref["y"])
     check_bits_equal(x, ref["residual_out"], "residual_out over x")
+    # fused LayerNorm: every pairing of the outputs with the inputs
+    w = workloads.FUSED_LN.scaled(rows=11, N=2048, seed=832)
+    inp = workloads.make_inputs(w)
+    ref = run_oracle(w, inp)
+    g = _gpu(inp)
+    for y_on, ro_on in (("x", "residual"), ("residual", "x")):
+        t = {"x": g["x"].clone(), "residual": g["residual"].clone()}
+        rn.fused_add_layer_norm(t["x"], t["residual"], g["gamma"], g["beta"], w.eps, out=t[y_on],
+                                residual_out=t[ro_on], variant=variant)
+        torch.cuda.synchronize()
+        check_y(t[y_on], ref["y"])
+        check_bits_equal(t[ro_on], ref["residual_out"], f"fused LN residual_out over {ro_on}")
+    # softmax in place
+    w = workloads.SOFTMAX.scaled(rows=11, N=2048, seed=833, dtype="bf16")
+    inp = workloads.make_inputs(w)
+    ref = run_oracle(w, inp)
+    x = inp["x"].to(DEV)
+    rn.softmax_forward(x, out=x, variant=variant)
+    torch.cuda.synchronize()
+    check_softmax_y(x, ref["y"])
+
+
+@pytest.mark.parametrize("op", ["ln", "rms", "fused_add_rms", "fused_add_ln", "softmax"])
+@pytest.mark.parametrize("pad", [64, 8, 1])
+def test_padded_rows(op, pad):
+    # x, residual, y and residual_out are column slices of wider buffers (row stride N + pad
+    # elements); with bf16, pads 64 and 8 keep rows on 16-byte boundaries (vectorized
+    # kernels), pad 1 does not (element kernel). Columns beyond N must not be touched.
+    rows, N = 33, 4096
+    w = BASES[op].scaled(rows=rows, N=N, seed=860 + pad, dtype="bf16")
+    inp = workloads.make_inputs(w)
+    ref = run_oracle(w, inp)
+    g = _gpu(inp)
+    ld = N + pad
+
+    def slab(src=None):
+        buf = torch.full((rows, ld), float("nan"), dtype=torch.bfloat16, device=DEV)
+        if src is not None:
+            buf[:, :N].copy_(src)
+        return buf, buf[:, :N]
+
+    xb, x = slab(g["x"])
+    yb, y = slab()
+    assert x.stride(0) == ld
+    if op in ("fused_add_rms", "fused_add_ln"):
+        rb, r = slab(g["residual"])
+        ob, ro = slab()
+    st, info = rn.plan(op, rows, N, torch.bfloat16, strides={"x": ld, "y": ld, "residual": ld, "residual_out": ld},
+                       ptrs={"gamma": 1 << 44, "beta": (1 << 44) + (1 << 30)})
+    assert st == 0 and info["variant"] == ("workgroup" if pad % 8 == 0 else "element"), info
+    if op == "ln":
+        out = rn.ln_forward(x, g["gamma"], g["beta"], w.eps, out=y, return_stats=True) + (None,)
+    elif op == "rms":
+        yy, rstd = rn.rms_norm(x, g["weight"], w.eps, out=y, return_rstd=True)
+        out = (yy, None, rstd, None)
+    elif op == "fused_add_rms":
+        yy, roo, rstd = rn.fused_add_rms_norm(x, r, g["weight"], w.eps, out=y, residual_out=ro, return_rstd=True)
+        out = (yy, roo, rstd, None)
+    elif op == "fused_add_ln":
+        yy, roo, mean, rstd = rn.fused_add_layer_norm(x, r, g["gamma"], g["beta"], w.eps, out=y, residual_out=ro,
+                                                      return_stats=True)
+        out = (yy, roo, rstd, mean)
+    else:
+        yy, mx, sm = rn.softmax_forward(x, out=y, return_stats=True)
+        out = (yy, None, sm, mx)
+    torch.cuda.synchronize()
+    assert out[0].data_ptr() == y.data_ptr()
+    check_outputs(w, ref, *out)
+    assert torch.isnan(yb[:, N:]).all(), "y padding written"
+    if op in ("fused_add_rms", "fused_add_ln"):
+        assert torch.isnan(ob[:, N:]).all(), "residual_out padding written"
 
 
 def test_three_dimensional_input():
@@ -278,6 +397,9 @@ PERSISTENT_CASES = [
     ("rms", "bf16", 4096, 8192, True, True),
     ("fused_add_rms", "bf16", 4096, 4096, True, True),
     ("fused_add_rms", "fp32", 8192, 2048, True, True),
+    ("fused_add_ln", "bf16", 8192, 4096, True, True),
+    ("fused_add_ln", "fp16", 2048, 16384, True, False),
+    ("fused_add_ln", "fp32", 2048, 16384, False, True),
 ]
 
 
@@ -285,7 +407,8 @@ PERSISTENT_CASES = [
                                                         for c in PERSISTENT_CASES])
 def test_persistent_launches(case):
     op, dtype, rows, N, wg, wb = case
-    base = {"ln": workloads.C5, "rms": workloads.C3, "fused_add_rms": workloads.C4_BF16}[op]
+    base = {"ln": workloads.C5, "rms": workloads.C3, "fused_add_rms": workloads.C4_BF16,
+            "fused_add_ln": workloads.FUSED_LN}[op]
     w = base.scaled(rows=rows, N=N, seed=900 + N, dtype=dtype, with_gamma=wg, with_beta=wb)
     inp = workloads.make_inputs(w)
     st, info = rn.plan(op, rows, N, TD[dtype], ptrs={"gamma": 1 << 44, "beta": (1 << 44) + (1 << 30)}
@@ -323,3 +446,26 @@ def test_persistent_in_place():
     torch.cuda.synchronize()
     check_y(x, ref["y"])
     check_bits_equal(r, ref["residual_out"], "residual_out in place (persistent)")
+    # fused LayerNorm in place over a persistent launch with 2 waves per row
+    w = workloads.FUSED_LN.scaled(rows=8192, seed=922)
+    inp = workloads.make_inputs(w)
+    ref = run_oracle(w, inp)
+    g = _gpu(inp)
+    x, r = g["x"].clone(), g["residual"].clone()
+    rn.fused_add_layer_norm(x, r, g["gamma"], g["beta"], w.eps, out=x, residual_out=r)
+    torch.cuda.synchronize()
+    check_y(x, ref["y"])
+    check_bits_equal(r, ref["residual_out"], "fused LN residual_out in place (persistent)")
+
+
+def test_softmax_large_logits_and_constant_rows():
+    # logits spread over +-80 (exp ratios near the fp32 range), rows with one dominant
+    # element, and constant rows (exactly 1/N)
+    for dtype in ("fp32", "bf16"):
+        w = workloads.SOFTMAX.scaled(rows=64, N=4096, seed=940, dtype=dtype, x_scale=40.0)
+        check_case(w)
+        w = workloads.SOFTMAX.scaled(rows=16, N=4096, seed=941, dtype=dtype, x_dist="constant", row_offset=50.0)
+        inp = workloads.make_inputs(w)
+        y = rn.softmax_forward(inp["x"].to(DEV))
+        torch.cuda.synchronize()
+        assert torch.equal(y, torch.full_like(y, 1.0 / 4096)), dtype
