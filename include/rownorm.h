@@ -23,6 +23,8 @@
  *                         lesson, section 1 "Softmax"; the per-part (max, sum) pairs are
  *                         merged with the rescaling of its "Online Softmax" sections).
  *
+ * and the backward passes of LayerNorm and RMSNorm (ln_backward, rms_norm_backward).
+ *
  * Conventions shared by every entry point:
  *   - Pointers are DEVICE pointers (HIP device memory of the current device). x, residual,
  *     gamma / beta / weight, y and residual_out hold `dtype` elements; mean and rstd (softmax:
@@ -58,6 +60,7 @@
 #ifndef ROWNORM_H
 #define ROWNORM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include <hip/hip_runtime_api.h>
@@ -78,7 +81,9 @@ typedef enum rn_status {
     RN_ERR_ALIAS = 4,         /* an output overlaps another buffer other than by exact aliasing */
     RN_ERR_UNSUPPORTED = 5,   /* a forced kernel variant cannot run this shape / alignment */
     RN_ERR_HIP = 6,           /* the HIP runtime reported an error at launch */
-    RN_ERR_ALIGN = 7          /* a pointer is not aligned to its element size */
+    RN_ERR_ALIGN = 7,         /* a pointer is not aligned to its element size */
+    RN_ERR_WORKSPACE = 8      /* the backward workspace is missing or smaller than
+                                 rn_backward_workspace_bytes() */
 } rn_status;
 
 /* Kernel variants (for rn_*_variant entry points and rn_plan). */
@@ -184,6 +189,37 @@ int fused_add_rms_norm_variant(const void* x, const void* residual, const void* 
                                void* residual_out, float* rstd, int64_t rows, int64_t N, float eps, int dtype,
                                hipStream_t stream, int variant);
 
+/*
+ * Backward passes. With xhat_j = (x_j - mean) * rstd (RMSNorm: x_j * rstd) and g_j = dy_j *
+ * gamma_j, for each row
+ *   dx_j = rstd * (g_j - (1/N) sum_k g_k - xhat_j * (1/N) sum_k g_k xhat_k)
+ * (RMSNorm: without the (1/N) sum_k g_k term), and over all rows dgamma_j = sum_r dy_rj *
+ * xhat_rj, dbeta_j = sum_r dy_rj: the normalization gradient of "BatchNorm CUDA
+ * implementation" (jianying88.com/news/30214), section 3.1, with the reduction along the
+ * row (gamma varies along the row, so it sits inside the row sums).
+ *   dy, x        [rows, N] dtype (dense), required when rows > 0.
+ *   gamma        [N] dtype, nullable (1).
+ *   mean, rstd   [rows] fp32: the forward's statistics (ln_forward / rms_norm outputs), used
+ *                as given; required when rows > 0 (RMSNorm: rstd only).
+ *   dx           [rows, N] dtype, nullable (then only parameter gradients are computed); may
+ *                be dy or x itself.
+ *   dgamma, dbeta (RMSNorm: dweight)  [N] dtype, nullable; rows == 0 writes zeros.
+ *   workspace    device memory of at least rn_backward_workspace_bytes(op, rows, N) bytes,
+ *                4-byte aligned, owned by the caller; required only when a parameter gradient
+ *                is requested (RN_ERR_WORKSPACE otherwise). Its contents on entry do not
+ *                matter; on return they are unspecified. Calls that share a workspace must
+ *                be ordered (same stream).
+ * Rows up to 16384 elements (longer rows: RN_ERR_UNSUPPORTED). Column sums are formed in
+ * fp32 in a fixed order (no atomics): results are bitwise reproducible on a given device.
+ */
+size_t rn_backward_workspace_bytes(int op, int64_t rows, int64_t N);
+int ln_backward(const void* dy, const void* x, const void* gamma, const float* mean, const float* rstd, void* dx,
+                void* dgamma, void* dbeta, int64_t rows, int64_t N, int dtype, void* workspace,
+                size_t workspace_bytes, hipStream_t stream);
+int rms_norm_backward(const void* dy, const void* x, const void* weight, const float* rstd, void* dx,
+                      void* dweight, int64_t rows, int64_t N, int dtype, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
 /* Launch plan chosen for a call, computed on the host only (no HIP call is made), with the
  * same validation as the entry points. Pointers are only inspected for NULL, alignment and
  * overlap, never dereferenced. */
@@ -197,14 +233,21 @@ typedef struct rn_plan_info {
     int64_t grid_blocks;   /* workgroups launched (persistent launches: an upper bound; the launch
                               caps it at what the current device keeps resident) */
     int exact;             /* 1 if a row is exactly chunks_per_lane passes of its row group */
-    int persistent;        /* 1 if parameters are staged on chip once per workgroup and the
-                              workgroups loop over many rows */
+    int persistent;        /* 1 if the grid is sized to what the device keeps resident and the
+                              workgroups loop over many rows, with the parameters loaded on chip
+                              once per workgroup */
     int lds_bytes;         /* dynamic LDS per workgroup of a persistent launch */
 } rn_plan_info;
 
 int rn_plan(int op, const void* x, const void* residual, const void* gamma, const void* beta, const void* y,
             const void* residual_out, const void* mean, const void* rstd, int64_t rows, int64_t N, float eps,
             int dtype, int variant, const rn_row_strides* strides, rn_plan_info* out);
+
+/* The same for a backward call (op: RN_OP_LAYER_NORM or RN_OP_RMS_NORM); grid_blocks is the
+ * row kernel's workgroup count before the device cap of two per compute unit. */
+int rn_plan_backward(int op, const void* dy, const void* x, const void* gamma, const float* mean, const float* rstd,
+                     const void* dx, const void* dgamma, const void* dbeta, int64_t rows, int64_t N, int dtype,
+                     const void* workspace, size_t workspace_bytes, rn_plan_info* out);
 
 /* Static string naming a status code ("RN_OK", ...); "unknown status" otherwise. */
 const char* rn_status_string(int status);

@@ -24,7 +24,8 @@ from typing import Optional, Tuple, Union
 import torch
 
 __all__ = [
-    "ln_forward", "rms_norm", "fused_add_rms_norm", "fused_add_layer_norm", "softmax_forward", "plan",
+    "ln_forward", "rms_norm", "fused_add_rms_norm", "fused_add_layer_norm", "softmax_forward", "ln_backward",
+    "rms_norm_backward", "backward_workspace_bytes", "plan", "plan_backward",
     "RowNormError", "LIB_PATH", "VARIANTS", "STATUS", "version",
 ]
 
@@ -75,13 +76,22 @@ _lib.rn_version.restype = _ci
 _lib.rn_plan.argtypes = [_ci, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci, _ci,
                          ctypes.POINTER(RowStrides), ctypes.POINTER(PlanInfo)]
 _lib.rn_plan.restype = _ci
+_lib.rn_backward_workspace_bytes.argtypes = [_ci, _i64, _i64]
+_lib.rn_backward_workspace_bytes.restype = ctypes.c_size_t
+_lib.ln_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _ci, _vp, ctypes.c_size_t, _vp]
+_lib.ln_backward.restype = _ci
+_lib.rms_norm_backward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _ci, _vp, ctypes.c_size_t, _vp]
+_lib.rms_norm_backward.restype = _ci
+_lib.rn_plan_backward.argtypes = [_ci, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _ci, _vp, ctypes.c_size_t,
+                                  ctypes.POINTER(PlanInfo)]
+_lib.rn_plan_backward.restype = _ci
 
 DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 VARIANTS = {"auto": 0, "wave": 1, "workgroup": 2, "general": 3, "element": 4}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 OPS = {"ln": 0, "rms": 1, "fused_add_rms": 2, "fused_add_ln": 3, "softmax": 4}
 STATUS = {0: "RN_OK", 1: "RN_ERR_NULL", 2: "RN_ERR_SHAPE", 3: "RN_ERR_DTYPE", 4: "RN_ERR_ALIAS",
-          5: "RN_ERR_UNSUPPORTED", 6: "RN_ERR_HIP", 7: "RN_ERR_ALIGN"}
+          5: "RN_ERR_UNSUPPORTED", 6: "RN_ERR_HIP", 7: "RN_ERR_ALIGN", 8: "RN_ERR_WORKSPACE"}
 
 
 class RowNormError(RuntimeError):
@@ -283,6 +293,110 @@ def softmax_forward(x: torch.Tensor, *, out: Optional[torch.Tensor] = None, row_
     _call("softmax", "softmax_forward", x, None, None, None, y, None, row_max, row_sum, rows, N, 0.0,
           (ldx, 0, ldy, 0), variant, stream)
     return (y, row_max, row_sum) if want else y
+
+
+def backward_workspace_bytes(op: str, rows: int, N: int) -> int:
+    """Workspace bytes a backward call with parameter gradients needs (op "ln" or "rms")."""
+    return int(_lib.rn_backward_workspace_bytes(OPS[op], rows, N))
+
+
+def _bwd_prep(dy, x):
+    rows, N, ld = _prep(x)
+    if ld != 0:
+        raise ValueError("x must be contiguous for the backward pass")
+    _check_matrix("dy", dy, x)
+    if not dy.is_contiguous():
+        raise ValueError("dy must be contiguous")
+    return rows, N
+
+
+def _workspace(x, op, rows, N, workspace):
+    need = backward_workspace_bytes(op, rows, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 4), dtype=torch.uint8, device=x.device)
+    if workspace.device != x.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the device of x")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def ln_backward(dy: torch.Tensor, x: torch.Tensor, mean: torch.Tensor, rstd: torch.Tensor,
+                gamma: Optional[torch.Tensor] = None, *, dx: Optional[torch.Tensor] = None, want_dx: bool = True,
+                want_dgamma: bool = True, want_dbeta: bool = True, workspace: Optional[torch.Tensor] = None,
+                stream=None):
+    """LayerNorm backward from the forward's fp32 mean / rstd. Returns (dx, dgamma, dbeta);
+    entries not wanted are None. ``dx`` may be ``dy`` or ``x`` (in place). The workspace is
+    allocated with torch when not given."""
+    rows, N = _bwd_prep(dy, x)
+    _check_vector("gamma", gamma, x)
+    _check_vector("mean", mean, x, torch.float32, rows)
+    _check_vector("rstd", rstd, x, torch.float32, rows)
+    if want_dx:
+        dx = _new_like(x) if dx is None else dx
+        _check_matrix("dx", dx, x)
+        if not dx.is_contiguous():
+            raise ValueError("dx must be contiguous")
+    else:
+        dx = None
+    dg = torch.empty(N, dtype=x.dtype, device=x.device) if want_dgamma else None
+    db = torch.empty(N, dtype=x.dtype, device=x.device) if want_dbeta else None
+    ws, ws_bytes = (None, 0)
+    if want_dgamma or want_dbeta:
+        ws, ws_bytes = _workspace(x, "ln", rows, N, workspace)
+    with torch.cuda.device(x.device):
+        st = _lib.ln_backward(_ptr(dy), _ptr(x), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(dg), _ptr(db),
+                              rows, N, DTYPE_CODE[x.dtype], _ptr(ws), ws_bytes, _stream(x, stream))
+    if st != 0:
+        raise RowNormError(st, "ln_backward")
+    return dx, dg, db
+
+
+def rms_norm_backward(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor, weight: Optional[torch.Tensor] = None,
+                      *, dx: Optional[torch.Tensor] = None, want_dx: bool = True, want_dweight: bool = True,
+                      workspace: Optional[torch.Tensor] = None, stream=None):
+    """RMSNorm backward from the forward's fp32 rstd. Returns (dx, dweight)."""
+    rows, N = _bwd_prep(dy, x)
+    _check_vector("weight", weight, x)
+    _check_vector("rstd", rstd, x, torch.float32, rows)
+    if want_dx:
+        dx = _new_like(x) if dx is None else dx
+        _check_matrix("dx", dx, x)
+        if not dx.is_contiguous():
+            raise ValueError("dx must be contiguous")
+    else:
+        dx = None
+    dw = torch.empty(N, dtype=x.dtype, device=x.device) if want_dweight else None
+    ws, ws_bytes = (None, 0)
+    if want_dweight:
+        ws, ws_bytes = _workspace(x, "rms", rows, N, workspace)
+    with torch.cuda.device(x.device):
+        st = _lib.rms_norm_backward(_ptr(dy), _ptr(x), _ptr(weight), _ptr(rstd), _ptr(dx), _ptr(dw), rows, N,
+                                    DTYPE_CODE[x.dtype], _ptr(ws), ws_bytes, _stream(x, stream))
+    if st != 0:
+        raise RowNormError(st, "rms_norm_backward")
+    return dx, dw
+
+
+def plan_backward(op: str, rows: int, N: int, dtype: torch.dtype, *, ptrs: Optional[dict] = None,
+                  workspace_bytes: Optional[int] = None) -> Tuple[int, dict]:
+    """Host-only backward plan. ``ptrs`` maps dy, x, gamma, mean, rstd, dx, dgamma, dbeta,
+    workspace to addresses (defaults: non-overlapping, aligned; dgamma / dbeta / workspace
+    absent unless given)."""
+    s = torch.tensor([], dtype=dtype).element_size() if isinstance(dtype, torch.dtype) else 4
+    step = ((max(1, rows * N * s) + 4095) // 4096 + 1) * 4096
+    base = 1 << 40
+    p = {"dy": base, "x": base + step, "dx": base + 2 * step, "mean": base + 3 * step,
+         "rstd": base + 3 * step + ((rows * 4 + 4095) // 4096 + 1) * 4096}
+    if ptrs:
+        p.update(ptrs)
+    wsb = backward_workspace_bytes(op, rows, N) if workspace_bytes is None else workspace_bytes
+    info = PlanInfo()
+    st = _lib.rn_plan_backward(OPS[op], p.get("dy"), p.get("x"), p.get("gamma"), p.get("mean"), p.get("rstd"),
+                               p.get("dx"), p.get("dgamma"), p.get("dbeta"), rows, N, DTYPE_CODE.get(dtype, 99),
+                               p.get("workspace"), wsb, ctypes.byref(info))
+    return st, {"variant": VARIANT_NAMES.get(info.variant, info.variant), "waves_per_row": info.waves_per_row,
+                "rows_per_block": info.rows_per_block, "block_threads": info.block_threads,
+                "chunks_per_lane": info.chunks_per_lane, "grid_blocks": info.grid_blocks,
+                "exact": bool(info.exact), "lds_bytes": info.lds_bytes}
 
 
 def plan(op: str, rows: int, N: int, dtype: torch.dtype, *, ptrs: Optional[dict] = None, eps: float = 1e-5,

@@ -1,0 +1,382 @@
+// Backward passes of row-wise LayerNorm and RMSNorm for gfx950 (MI355X).
+//
+// For one row, with xhat_j = (x_j - mean) * rstd (RMSNorm: x_j * rstd) and g_j = dy_j *
+// gamma_j, the chain rule through the normalization gives
+//     dx_j = rstd * (g_j - (1/N) sum_k g_k - xhat_j * (1/N) sum_k g_k xhat_k)
+// (RMSNorm: without the (1/N) sum_k g_k term), and over all rows
+//     dgamma_j = sum_r dy_rj * xhat_rj,    dbeta_j = sum_r dy_rj.
+// This is the BatchNorm gradient of "BatchNorm CUDA implementation" (jianying88.com/news/
+// 30214), section 3.1, turned by 90 degrees: the statistics run along a row, so gamma sits
+// inside the row sums, and the parameter gradients become column sums over the rows. The
+// same article's section 3.2 weighs organizations of the kernel; the one here reads x and
+// dy once and writes dx once:
+//
+//   1. rownorm_bwd_vec_kernel (or rownorm_bwd_elem_kernel for rows that are not whole
+//      16-byte chunks): a grid of P workgroups loops over the rows. A row group of W waves
+//      holds a row of x and dy in VGPRs, reduces sum g and sum g * xhat across the row (DPP,
+//      then LDS across waves), and writes dx. Each lane owns the same columns for every row,
+//      so it also accumulates its columns' dgamma / dbeta terms in fp32 registers across
+//      all the rows it visits. At the end the row groups of a workgroup add their column
+//      sums in a fixed order through LDS, and the workgroup writes one fp32 partial row per
+//      parameter to the workspace: [2][P][N].
+//   2. rownorm_bwd_cols_kernel sums the P partial rows of each column in a fixed order and
+//      rounds to the I/O dtype.
+// No atomics: results are bitwise reproducible for a given P (P depends on the device's CU
+// count only).
+#pragma once
+
+#include "rownorm_kernels.hpp"
+
+namespace rn {
+
+// Sum of two per-wave values across the row group's waves (one barrier).
+template <int W>
+__device__ __forceinline__ void group_sum2(WavePart (*part)[W > 1 ? W : 1], int& buf, int lane, int wr, float& a,
+                                           float& b) {
+    if constexpr (W > 1) {
+        if (lane == 0) {
+            part[buf][wr].v[0] = a;
+            part[buf][wr].v[1] = b;
+        }
+        __syncthreads();
+        a = part[buf][0].v[0];
+        b = part[buf][0].v[1];
+#pragma unroll
+        for (int w = 1; w < W; ++w) {
+            a += part[buf][w].v[0];
+            b += part[buf][w].v[1];
+        }
+        buf ^= 1;
+    }
+}
+
+// Row groups of a workgroup add their per-lane column sums in order 0, 1, ..., RPB - 1
+// through LDS (red: n floats), and the last writes the workgroup's partial row to `out`.
+// `cols(i, e)` is the column of register slot (i, e); `ok(i, e)` whether it is in the row.
+template <int RPB, int NS, typename ColF, typename OkF>
+__device__ __forceinline__ void flush_columns(const float (&acc)[NS], float* red, int rg, float* out, ColF cols,
+                                              OkF ok) {
+    if constexpr (RPB == 1) {
+#pragma unroll
+        for (int k = 0; k < NS; ++k)
+            if (ok(k)) out[cols(k)] = acc[k];
+    } else {
+        for (int r = 0; r < RPB; ++r) {
+            if (rg == r) {
+#pragma unroll
+                for (int k = 0; k < NS; ++k) {
+                    if (!ok(k)) continue;
+                    const float v = r == 0 ? acc[k] : red[cols(k)] + acc[k];
+                    if (r == RPB - 1)
+                        out[cols(k)] = v;
+                    else
+                        red[cols(k)] = v;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+template <int DT, int OP, int W, int V, int RPB, bool EXACT, bool HG>
+__global__ __launch_bounds__(64 * W * RPB) void rownorm_bwd_vec_kernel(BwdParams p) {
+    using IO = Io<DT>;
+    constexpr int E = IO::E;
+    constexpr int LANES = 64 * W;
+    constexpr bool LN = OP == OP_LN;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int rg = wave / W;
+    const int wr = wave - rg * W;
+    const int t = wr * 64 + lane;
+    const int Ci = static_cast<int>(p.C);
+    __shared__ WavePart part_all[RPB][2][W > 1 ? W : 1];
+    extern __shared__ float red[];  // RPB > 1: N floats
+    WavePart(*part)[W > 1 ? W : 1] = part_all[rg];
+    auto chunk = [&](int i) {
+        const int c = i * LANES + t;
+        return EXACT ? c : (c < Ci ? c : Ci - 1);
+    };
+    auto valid = [&](int i) { return EXACT || i * LANES + t < Ci; };
+    const bool want_cols = p.ws != nullptr;
+
+    u32x4 gk[HG ? V : 1];
+    if constexpr (HG) {
+#pragma unroll
+        for (int i = 0; i < V; ++i) gk[i] = static_cast<const u32x4*>(p.gamma)[chunk(i)];
+    }
+    float adg[V * E], adb[LN ? V * E : 1];
+#pragma unroll
+    for (int k = 0; k < V * E; ++k) {
+        adg[k] = 0.f;
+        if constexpr (LN) adb[k] = 0.f;
+    }
+    int buf = 0;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * RPB; base < p.rows;
+         base += static_cast<int64_t>(gridDim.x) * RPB) {
+        const int64_t row = base + rg;
+        if (row >= p.rows) {
+            if constexpr (W > 1) {
+                __syncthreads();
+                buf ^= 1;
+            }
+            continue;
+        }
+        int tl = t;
+        asm volatile("" : "+v"(tl));
+        const u32x4* xr = static_cast<const u32x4*>(p.x) + row * p.C;
+        const u32x4* dr = static_cast<const u32x4*>(p.dy) + row * p.C;
+        u32x4 xv[V], dv[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            const int c = EXACT ? i * LANES + tl : (i * LANES + tl < Ci ? i * LANES + tl : Ci - 1);
+            xv[i] = __builtin_nontemporal_load(xr + c);
+            dv[i] = __builtin_nontemporal_load(dr + c);
+        }
+        const float mean = LN ? p.mean[row] : 0.f;
+        const float rstd = p.rstd[row];
+        __builtin_amdgcn_sched_barrier(0);
+        // gamma stays packed; it is widened where used (not hoisted out of the row loop as
+        // fp32 values, which would cost 4 VGPRs per chunk for the whole kernel)
+        u32x4 gl[HG ? V : 1];
+#pragma unroll
+        for (int i = 0; i < (HG ? V : 0); ++i) {
+            gl[i] = gk[i];
+            asm volatile("" : "+v"(gl[i]));
+        }
+        float sg = 0.f, sgx = 0.f;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            float xf[E], df[E], gf[E];
+            IO::unpack(xv[i], xf);
+            IO::unpack(dv[i], df);
+            if constexpr (HG) IO::unpack(gl[i], gf);
+            const bool ok = valid(i);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float xh = LN ? (xf[e] - mean) * rstd : xf[e] * rstd;
+                const float d = ok ? df[e] : 0.f;
+                const float g = HG ? d * gf[e] : d;
+                sg += g;
+                sgx = fmaf(g, xh, sgx);
+                adg[i * E + e] = fmaf(d, xh, adg[i * E + e]);
+                if constexpr (LN) adb[i * E + e] += d;
+            }
+        }
+        float Sg = wave_sum(sg), Sgx = wave_sum(sgx);
+        group_sum2<W>(part, buf, lane, wr, Sg, Sgx);
+        const float c1 = LN ? Sg * p.inv_n : 0.f;
+        const float c2 = Sgx * p.inv_n;
+        if (p.dx) {
+            u32x4* o = static_cast<u32x4*>(p.dx) + row * p.C;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float xf[E], df[E], gf[E], r[E];
+                IO::unpack(xv[i], xf);
+                IO::unpack(dv[i], df);
+                if constexpr (HG) IO::unpack(gl[i], gf);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float xh = LN ? (xf[e] - mean) * rstd : xf[e] * rstd;
+                    const float g = HG ? df[e] * gf[e] : df[e];
+                    r[e] = rstd * ((g - c1) - xh * c2);
+                }
+                if (valid(i)) __builtin_nontemporal_store(IO::pack(r), o + i * LANES + tl);
+            }
+        }
+    }
+    if (!want_cols) return;  // uniform over the grid
+    float* dg_out = p.ws + static_cast<int64_t>(blockIdx.x) * p.N;
+    float* db_out = p.ws + (static_cast<int64_t>(p.parts) + blockIdx.x) * p.N;
+    auto col = [&](int k) { return (k / E * LANES + t) * E + k % E; };
+    auto okc = [&](int k) { return EXACT || (k / E) * LANES + t < Ci; };
+    flush_columns<RPB>(adg, red, rg, dg_out, col, okc);
+    if constexpr (LN) flush_columns<RPB>(adb, red, rg, db_out, col, okc);
+}
+
+// Rows that are not whole 16-byte chunks: one element per register slot (rows up to
+// 16384 elements), the same computation.
+template <int DT, int OP, int W, int V, int RPB, bool HG>
+__global__ __launch_bounds__(64 * W * RPB) void rownorm_bwd_elem_kernel(BwdParams p) {
+    using IO = Io<DT>;
+    constexpr int LANES = 64 * W;
+    constexpr int S = DT == DT_F32 ? 4 : 2;
+    constexpr bool LN = OP == OP_LN;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int rg = wave / W;
+    const int wr = wave - rg * W;
+    const unsigned t = static_cast<unsigned>(wr * 64 + lane);
+    const unsigned N = static_cast<unsigned>(p.N);
+    __shared__ WavePart part_all[RPB][2][W > 1 ? W : 1];
+    extern __shared__ float red[];
+    WavePart(*part)[W > 1 ? W : 1] = part_all[rg];
+    float gv[HG ? V : 1];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const unsigned j = static_cast<unsigned>(i * LANES) + t;
+        if constexpr (HG) gv[i] = IO::load1(p.gamma, j < N ? j : N - 1);
+    }
+    float adg[V], adb[LN ? V : 1];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        adg[i] = 0.f;
+        if constexpr (LN) adb[i] = 0.f;
+    }
+    int buf = 0;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * RPB; base < p.rows;
+         base += static_cast<int64_t>(gridDim.x) * RPB) {
+        const int64_t row = base + rg;
+        if (row >= p.rows) {
+            if constexpr (W > 1) {
+                __syncthreads();
+                buf ^= 1;
+            }
+            continue;
+        }
+        const char* xr = static_cast<const char*>(p.x) + row * p.N * S;
+        const char* dr = static_cast<const char*>(p.dy) + row * p.N * S;
+        float xf[V], df[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            const unsigned j = static_cast<unsigned>(i * LANES) + t;
+            xf[i] = j < N ? IO::load1(xr, j) : 0.f;
+            df[i] = j < N ? IO::load1(dr, j) : 0.f;
+        }
+        const float mean = LN ? p.mean[row] : 0.f;
+        const float rstd = p.rstd[row];
+        __builtin_amdgcn_sched_barrier(0);
+        float sg = 0.f, sgx = 0.f;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            xf[i] = LN ? (xf[i] - mean) * rstd : xf[i] * rstd;  // xhat (0 where df is 0)
+            const float g = HG ? df[i] * gv[i] : df[i];
+            sg += g;
+            sgx = fmaf(g, xf[i], sgx);
+            adg[i] = fmaf(df[i], xf[i], adg[i]);
+            if constexpr (LN) adb[i] += df[i];
+        }
+        float Sg = wave_sum(sg), Sgx = wave_sum(sgx);
+        group_sum2<W>(part, buf, lane, wr, Sg, Sgx);
+        const float c1 = LN ? Sg * p.inv_n : 0.f;
+        const float c2 = Sgx * p.inv_n;
+        if (p.dx) {
+            char* o = static_cast<char*>(p.dx) + row * p.N * S;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                const unsigned j = static_cast<unsigned>(i * LANES) + t;
+                const float g = HG ? df[i] * gv[i] : df[i];
+                if (j < N) IO::store1(o, j, rstd * ((g - c1) - xf[i] * c2));
+            }
+        }
+    }
+    if (p.ws == nullptr) return;
+    float* dg_out = p.ws + static_cast<int64_t>(blockIdx.x) * p.N;
+    float* db_out = p.ws + (static_cast<int64_t>(p.parts) + blockIdx.x) * p.N;
+    auto col = [&](int k) { return static_cast<int>(k * LANES + t); };
+    auto okc = [&](int k) { return static_cast<unsigned>(k * LANES) + t < N; };
+    flush_columns<RPB>(adg, red, rg, dg_out, col, okc);
+    if constexpr (LN) flush_columns<RPB>(adb, red, rg, db_out, col, okc);
+}
+
+// dgamma_j = sum over the P partial rows, in order b = 0, 1, ..., P - 1 within each of 16
+// interleaved lanes, then the 16 lane sums in order; rounded once to the I/O dtype. A
+// workgroup covers 16 columns with 16 lanes each.
+template <int DT>
+__global__ __launch_bounds__(256) void rownorm_bwd_cols_kernel(BwdColParams p) {
+    using IO = Io<DT>;
+    __shared__ float sums[2][16][17];
+    const int q = threadIdx.x & 15;   // column within the tile
+    const int s = threadIdx.x >> 4;   // partial-row lane: rows b = s, s + 16, ...
+    const int64_t j = static_cast<int64_t>(blockIdx.x) * 16 + q;
+    for (int k = 0; k < 2; ++k) {
+        void* out = k == 0 ? p.dgamma : p.dbeta;
+        if (out == nullptr) continue;  // uniform
+        const float* src = p.ws + static_cast<int64_t>(k) * p.parts * p.N;
+        float a = 0.f;
+        if (j < p.N)
+            for (int b = s; b < p.parts; b += 16) a += src[static_cast<int64_t>(b) * p.N + j];
+        sums[k][s][q] = a;
+        __syncthreads();
+        if (s == 0 && j < p.N) {
+            float r = sums[k][0][q];
+#pragma unroll
+            for (int u = 1; u < 16; ++u) r += sums[k][u][q];
+            IO::store1(out, j, r);
+        }
+    }
+}
+
+constexpr int rows_per_block_bwd(int W) { return W >= 16 ? 1 : 16 / W; }  // 16-wave workgroups
+
+template <typename K>
+inline hipError_t go_bwd(K kernel, int parts, int threads, int lds, const BwdParams& p, hipStream_t s) {
+    BwdParams args = p;
+    void* argv[] = {&args};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<unsigned>(parts)),
+                           dim3(static_cast<unsigned>(threads)), argv, static_cast<size_t>(lds), s);
+}
+
+// Backward plan: variant (V_WORKGROUP for the vectorized kernel, V_ELEMENT), W, V, exact.
+template <int DT, int OP>
+inline hipError_t launch_bwd(const Plan& plan, const BwdParams& p, hipStream_t s) {
+    const int W = plan.waves_per_row, V = plan.chunks_per_lane;
+    const int threads = plan.block_threads;
+    const int parts = p.parts;
+    const int lds = plan.lds_bytes;
+    const bool hg = p.gamma != nullptr;
+    if (plan.rows_per_block != rows_per_block_bwd(W)) return hipErrorInvalidValue;
+#define RN_BV(WW, VV, EX)                                                                                        \
+    (hg ? go_bwd(rownorm_bwd_vec_kernel<DT, OP, WW, VV, rows_per_block_bwd(WW), EX, true>, parts, threads, lds, p, s) \
+        : go_bwd(rownorm_bwd_vec_kernel<DT, OP, WW, VV, rows_per_block_bwd(WW), EX, false>, parts, threads, lds, p, s))
+#define RN_BV_E(WW, VV) (plan.exact ? RN_BV(WW, VV, true) : RN_BV(WW, VV, false))
+#define RN_BE(WW, VV)                                                                                            \
+    (hg ? go_bwd(rownorm_bwd_elem_kernel<DT, OP, WW, VV, rows_per_block_bwd(WW), true>, parts, threads, lds, p, s) \
+        : go_bwd(rownorm_bwd_elem_kernel<DT, OP, WW, VV, rows_per_block_bwd(WW), false>, parts, threads, lds, p, s))
+    if (plan.variant == V_WORKGROUP || plan.variant == V_WAVE) {
+        switch (W * 100 + V) {
+        case 101: return RN_BV_E(1, 1);
+        case 102: return RN_BV_E(1, 2);
+        case 202: return RN_BV_E(2, 2);
+        case 402: return RN_BV_E(4, 2);
+        case 802: return RN_BV_E(8, 2);
+        case 1602: return RN_BV_E(16, 2);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (plan.variant == V_ELEMENT) {
+        switch (W * 100 + V) {
+        case 101: return RN_BE(1, 1);
+        case 102: return RN_BE(1, 2);
+        case 104: return RN_BE(1, 4);
+        case 108: return RN_BE(1, 8);
+        case 208: return RN_BE(2, 8);
+        case 408: return RN_BE(4, 8);
+        case 808: return RN_BE(8, 8);
+        case 1608: return RN_BE(16, 8);
+        case 1616: return RN_BE(16, 16);
+        default: return hipErrorInvalidValue;
+        }
+    }
+#undef RN_BE
+#undef RN_BV_E
+#undef RN_BV
+    return hipErrorInvalidValue;
+}
+
+template <int DT>
+inline hipError_t launch_bwd_dtype(int op, const Plan& plan, const BwdParams& p, const BwdColParams& cp,
+                                   hipStream_t s) {
+    hipError_t e = hipSuccess;
+    if (p.rows > 0 && (p.dx != nullptr || p.ws != nullptr))
+        e = op == OP_LN ? launch_bwd<DT, OP_LN>(plan, p, s) : launch_bwd<DT, OP_RMS>(plan, p, s);
+    if (e != hipSuccess) return e;
+    if (cp.dgamma == nullptr && cp.dbeta == nullptr) return hipSuccess;
+    BwdColParams args = cp;
+    void* argv[] = {&args};
+    const unsigned blocks = static_cast<unsigned>((cp.N + 15) / 16);
+    return hipLaunchKernel(reinterpret_cast<const void*>(rownorm_bwd_cols_kernel<DT>), dim3(blocks), dim3(256), argv,
+                           0, s);
+}
+
+}  // namespace rn

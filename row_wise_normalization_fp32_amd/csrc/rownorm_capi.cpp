@@ -8,6 +8,7 @@
 // launch's own HIP error.
 
 #include <math.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "../../include/rownorm.h"
@@ -210,9 +211,10 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     // workgroups up). Parameters go to LDS once per workgroup; the LayerNorm ops with both
     // keep gamma in VGPRs and stage only beta, so the LDS need is at most one row (64 KiB).
     const bool has_params = a.gamma != nullptr || (ln && a.beta != nullptr);
-    plan->persistent = vec && plan->exact && has_params && blocks >= rn::kPersistentBlocks;
+    plan->persistent = blocks >= rn::kPersistentBlocks &&
+                       ((vec && plan->exact && has_params) || plan->variant == rn::V_ELEMENT);
     plan->lds_bytes = 0;
-    if (plan->persistent) plan->lds_bytes = static_cast<int>(C * 16);  // one parameter vector in LDS
+    if (plan->persistent && vec) plan->lds_bytes = static_cast<int>(C * 16);  // one parameter vector in LDS
     *chunks = C;
     return RN_OK;
 }
@@ -245,14 +247,17 @@ int run(Args a, const rn_row_strides* strides, hipStream_t stream) {
     p.cro = a.ldro * s / 16;
     p.eps = a.eps;
     p.inv_n = static_cast<float>(1.0 / static_cast<double>(a.N));
+    // Persistent vectorized launches have instances of their own (parameters staged on
+    // chip); the element kernel is the same instance in both launch modes.
+    const bool pers_vec = plan.persistent && plan.variant != rn::V_ELEMENT;
     hipError_t e = hipErrorInvalidValue;
     switch (a.dtype) {
-    case RN_F32: e = plan.persistent ? rn::launch_f32_persistent(a.op, plan, p, stream)
-                                     : rn::launch_f32(a.op, plan, p, stream); break;
-    case RN_F16: e = plan.persistent ? rn::launch_f16_persistent(a.op, plan, p, stream)
-                                     : rn::launch_f16(a.op, plan, p, stream); break;
-    case RN_BF16: e = plan.persistent ? rn::launch_bf16_persistent(a.op, plan, p, stream)
-                                      : rn::launch_bf16(a.op, plan, p, stream); break;
+    case RN_F32: e = pers_vec ? rn::launch_f32_persistent(a.op, plan, p, stream)
+                              : rn::launch_f32(a.op, plan, p, stream); break;
+    case RN_F16: e = pers_vec ? rn::launch_f16_persistent(a.op, plan, p, stream)
+                              : rn::launch_f16(a.op, plan, p, stream); break;
+    case RN_BF16: e = pers_vec ? rn::launch_bf16_persistent(a.op, plan, p, stream)
+                               : rn::launch_bf16(a.op, plan, p, stream); break;
     default: break;
     }
     return e == hipSuccess ? RN_OK : RN_ERR_HIP;
@@ -278,6 +283,165 @@ Args make_args(int op, const void* x, const void* residual, const void* gamma, c
     a.variant = variant;
     a.ldx = a.ldr = a.ldy = a.ldro = N;
     return a;
+}
+
+// ---------------------------------------------------------------------------------------
+// Backward.
+// ---------------------------------------------------------------------------------------
+
+int64_t bwd_parts_cap(int64_t rows) { return rows < rn::kBwdMaxParts ? rows : rn::kBwdMaxParts; }
+
+size_t bwd_workspace_bytes(int op, int64_t rows, int64_t N) {
+    if (rows <= 0 || N <= 0) return 0;
+    const int64_t sets = op == RN_OP_LAYER_NORM ? 2 : 1;
+    return static_cast<size_t>(sets * bwd_parts_cap(rows) * N * 4);
+}
+
+struct BwdArgs {
+    int op;
+    const void *dy, *x, *gamma;
+    const float *mean, *rstd;
+    void *dx, *dgamma, *dbeta;
+    int64_t rows, N;
+    int dtype;
+    void* ws;
+    size_t ws_bytes;
+};
+
+// Validates a backward call and plans its row kernel. plan->grid is the number of row-kernel
+// workgroups before the device cap (the launch uses min(grid, 2 * CUs)).
+int validate_and_plan_bwd(BwdArgs& a, Plan* plan, int64_t* chunks) {
+    if (a.dtype != RN_F32 && a.dtype != RN_F16 && a.dtype != RN_BF16) return RN_ERR_DTYPE;
+    if (a.op != RN_OP_LAYER_NORM && a.op != RN_OP_RMS_NORM) return RN_ERR_SHAPE;
+    const int64_t s = a.dtype == RN_F32 ? 4 : 2;
+    const int64_t rows = a.rows, N = a.N;
+    if (rows < 0 || N <= 0 || N > (int64_t(1) << 40)) return RN_ERR_SHAPE;
+    if (rows > 0 && N > INT64_MAX / s / rows) return RN_ERR_SHAPE;
+    const bool ln = a.op == RN_OP_LAYER_NORM;
+    if (!ln) {
+        a.dbeta = nullptr;
+        a.mean = nullptr;
+    }
+    *plan = Plan{};
+    *chunks = 0;
+    const bool want_cols = a.dgamma != nullptr || a.dbeta != nullptr;
+    if (want_cols && rows > 0) {
+        if (!a.ws) return RN_ERR_WORKSPACE;
+        if (a.ws_bytes < bwd_workspace_bytes(a.op, rows, N)) return RN_ERR_WORKSPACE;
+    }
+    if (rows > 0) {
+        if (!a.dy || !a.x || !a.rstd || (ln && !a.mean)) return RN_ERR_NULL;
+    }
+    const int64_t mat = rows * N * s;
+    const Buf bufs[] = {
+        {a.dy, mat, 0, false, R_RES}, {a.x, mat, 0, false, R_X},       {a.gamma, N * s, 0, false, R_G},
+        {a.mean, rows * 4, 0, false, R_MEAN}, {a.rstd, rows * 4, 0, false, R_RSTD}, {a.dx, mat, 0, true, R_Y},
+        {a.dgamma, N * s, 0, true, R_B}, {a.dbeta, N * s, 0, true, R_B},
+        {want_cols ? a.ws : nullptr, static_cast<int64_t>(bwd_workspace_bytes(a.op, rows, N)), 0, true, R_RO},
+    };
+    const int nb = sizeof(bufs) / sizeof(bufs[0]);
+    for (int i = 0; i < nb; ++i) {
+        if (!bufs[i].p || bufs[i].bytes == 0) continue;
+        const uintptr_t ad = reinterpret_cast<uintptr_t>(bufs[i].p);
+        const int64_t need = (bufs[i].role == R_MEAN || bufs[i].role == R_RSTD || bufs[i].role == R_RO) ? 4 : s;
+        if (ad % static_cast<uintptr_t>(need) != 0) return RN_ERR_ALIGN;
+    }
+    for (int i = 0; i < nb; ++i) {
+        if (!bufs[i].p || !bufs[i].out || bufs[i].bytes == 0) continue;
+        for (int j = 0; j < nb; ++j) {
+            if (j == i || !bufs[j].p || bufs[j].bytes == 0) continue;
+            // dx may be dy or x itself: each element is read before the same lane writes it
+            const bool exact_ok = bufs[i].role == R_Y && bufs[i].p == bufs[j].p && bufs[i].bytes == bufs[j].bytes &&
+                                  (bufs[j].role == R_X || bufs[j].role == R_RES);
+            if (overlaps(bufs[i], bufs[j]) && !exact_ok) return RN_ERR_ALIAS;
+        }
+    }
+    if (rows == 0) return RN_OK;
+    bool vec_ok = (N * s) % 16 == 0;
+    for (const void* q : {a.dy, a.x, a.gamma, static_cast<const void*>(a.dx)})
+        if (q && reinterpret_cast<uintptr_t>(q) % 16 != 0) vec_ok = false;
+    const int64_t C = vec_ok ? N * s / 16 : 0;
+    const int64_t vec_cap = int64_t(64) * rn::kMaxGroupWaves * rn::kBwdTargetChunks;  // 2048 chunks
+    const int64_t elem_cap = int64_t(64) * rn::kMaxGroupWaves * rn::kElemMaxPerLane;   // 16384 elements
+    if (vec_ok && C <= vec_cap) {
+        int W = next_pow2((C + 64 * rn::kBwdTargetChunks - 1) / (64 * rn::kBwdTargetChunks));
+        if (W > rn::kMaxGroupWaves) W = rn::kMaxGroupWaves;
+        plan->variant = rn::V_WORKGROUP;
+        plan->waves_per_row = W;
+        plan->chunks_per_lane = next_pow2((C + 64 * W - 1) / (64 * W));
+        plan->exact = C == int64_t(64) * W * plan->chunks_per_lane;
+    } else if (N <= elem_cap) {
+        int W = next_pow2((N + 64 * rn::kElemTarget - 1) / (64 * rn::kElemTarget));
+        if (W > rn::kMaxGroupWaves) W = rn::kMaxGroupWaves;
+        plan->variant = rn::V_ELEMENT;
+        plan->waves_per_row = W;
+        plan->chunks_per_lane = next_pow2((N + 64 * W - 1) / (64 * W));
+    } else {
+        return RN_ERR_UNSUPPORTED;
+    }
+    const int W = plan->waves_per_row;
+    plan->rows_per_block = W >= 16 ? 1 : 16 / W;
+    plan->block_threads = 64 * W * plan->rows_per_block;  // 16-wave workgroups
+    const int64_t blocks = (rows + plan->rows_per_block - 1) / plan->rows_per_block;
+    plan->grid = blocks < rn::kBwdMaxParts ? blocks : rn::kBwdMaxParts;
+    plan->persistent = true;
+    plan->lds_bytes = plan->rows_per_block > 1 && want_cols ? static_cast<int>(N * 4) : 0;
+    *chunks = C;
+    return RN_OK;
+}
+
+int device_cus() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    int v = dev < 64 ? __atomic_load_n(&cache[dev], __ATOMIC_RELAXED) : 0;
+    if (v > 0) return v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (dev < 64) __atomic_store_n(&cache[dev], v, __ATOMIC_RELAXED);
+    return v;
+}
+
+int run_bwd(BwdArgs a, hipStream_t stream) {
+    Plan plan;
+    int64_t C = 0;
+    const int st = validate_and_plan_bwd(a, &plan, &C);
+    if (st != RN_OK) return st;
+    const bool want_cols = a.dgamma != nullptr || a.dbeta != nullptr;
+    if (a.rows == 0 && !want_cols) return RN_OK;
+    int64_t parts = 0;
+    if (a.rows > 0) {
+        const int cus = device_cus();
+        if (cus <= 0) return RN_ERR_HIP;
+        parts = plan.grid < 2 * int64_t(cus) ? plan.grid : 2 * int64_t(cus);  // two 16-wave workgroups per CU
+    }
+    rn::BwdParams p;
+    p.dy = a.dy;
+    p.x = a.x;
+    p.gamma = a.gamma;
+    p.mean = a.mean;
+    p.rstd = a.rstd;
+    p.dx = a.dx;
+    p.ws = want_cols ? static_cast<float*>(a.ws) : nullptr;
+    p.rows = a.rows;
+    p.N = a.N;
+    p.C = C;
+    p.inv_n = static_cast<float>(1.0 / static_cast<double>(a.N));
+    p.parts = static_cast<int>(parts);
+    rn::BwdColParams cp;
+    cp.ws = p.ws;
+    cp.dgamma = a.dgamma;
+    cp.dbeta = a.dbeta;
+    cp.N = a.N;
+    cp.parts = static_cast<int>(parts);
+    const int op = a.op == RN_OP_LAYER_NORM ? rn::OP_LN : rn::OP_RMS;
+    hipError_t e = hipErrorInvalidValue;
+    switch (a.dtype) {
+    case RN_F32: e = rn::launch_bwd_f32(op, plan, p, cp, stream); break;
+    case RN_F16: e = rn::launch_bwd_f16(op, plan, p, cp, stream); break;
+    case RN_BF16: e = rn::launch_bwd_bf16(op, plan, p, cp, stream); break;
+    default: break;
+    }
+    return e == hipSuccess ? RN_OK : RN_ERR_HIP;
 }
 
 }  // namespace
@@ -341,6 +505,49 @@ int fused_add_rms_norm_variant(const void* x, const void* residual, const void* 
                          N, eps, dtype, variant), nullptr, stream);
 }
 
+size_t rn_backward_workspace_bytes(int op, int64_t rows, int64_t N) {
+    if (op != RN_OP_LAYER_NORM && op != RN_OP_RMS_NORM) return 0;
+    return bwd_workspace_bytes(op, rows, N);
+}
+
+int ln_backward(const void* dy, const void* x, const void* gamma, const float* mean, const float* rstd, void* dx,
+                void* dgamma, void* dbeta, int64_t rows, int64_t N, int dtype, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+    BwdArgs a{RN_OP_LAYER_NORM, dy, x, gamma, mean, rstd, dx, dgamma, dbeta, rows, N, dtype, workspace,
+              workspace_bytes};
+    return run_bwd(a, stream);
+}
+
+int rms_norm_backward(const void* dy, const void* x, const void* weight, const float* rstd, void* dx,
+                      void* dweight, int64_t rows, int64_t N, int dtype, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+    BwdArgs a{RN_OP_RMS_NORM, dy, x, weight, nullptr, rstd, dx, dweight, nullptr, rows, N, dtype, workspace,
+              workspace_bytes};
+    return run_bwd(a, stream);
+}
+
+int rn_plan_backward(int op, const void* dy, const void* x, const void* gamma, const float* mean, const float* rstd,
+                     const void* dx, const void* dgamma, const void* dbeta, int64_t rows, int64_t N, int dtype,
+                     const void* workspace, size_t workspace_bytes, rn_plan_info* out) {
+    BwdArgs a{op, dy, x, gamma, mean, rstd, const_cast<void*>(dx), const_cast<void*>(dgamma),
+              const_cast<void*>(dbeta), rows, N, dtype, const_cast<void*>(workspace), workspace_bytes};
+    Plan plan;
+    int64_t C = 0;
+    const int st = validate_and_plan_bwd(a, &plan, &C);
+    if (out) {
+        out->variant = plan.variant;
+        out->waves_per_row = plan.waves_per_row;
+        out->rows_per_block = plan.rows_per_block;
+        out->block_threads = plan.block_threads;
+        out->chunks_per_lane = plan.chunks_per_lane;
+        out->grid_blocks = plan.grid;
+        out->exact = plan.exact ? 1 : 0;
+        out->persistent = plan.persistent ? 1 : 0;
+        out->lds_bytes = plan.lds_bytes;
+    }
+    return st;
+}
+
 int rn_plan(int op, const void* x, const void* residual, const void* gamma, const void* beta, const void* y,
             const void* residual_out, const void* mean, const void* rstd, int64_t rows, int64_t N, float eps,
             int dtype, int variant, const rn_row_strides* strides, rn_plan_info* out) {
@@ -372,6 +579,7 @@ const char* rn_status_string(int status) {
     case RN_ERR_UNSUPPORTED: return "RN_ERR_UNSUPPORTED";
     case RN_ERR_HIP: return "RN_ERR_HIP";
     case RN_ERR_ALIGN: return "RN_ERR_ALIGN";
+    case RN_ERR_WORKSPACE: return "RN_ERR_WORKSPACE";
     default: return "unknown status";
     }
 }

@@ -34,6 +34,31 @@ struct Params {
     float inv_n;  // 1 / N rounded to fp32
 };
 
+// Backward row kernel arguments (rownorm_backward.hpp).
+struct BwdParams {
+    const void* dy;
+    const void* x;
+    const void* gamma;  // gamma / weight, nullable (1)
+    const float* mean;  // LayerNorm only
+    const float* rstd;
+    void* dx;           // nullable: parameter gradients only
+    float* ws;          // [2][P][N] fp32 column partials; nullable when no parameter gradient is wanted
+    int64_t rows;
+    int64_t N;
+    int64_t C;          // 16-byte chunks per row (vectorized kernel)
+    float inv_n;
+    int parts;          // P = gridDim.x of the row kernel
+};
+
+// Backward column-sum kernel arguments.
+struct BwdColParams {
+    const float* ws;    // [2][P][N]
+    void* dgamma;       // nullable
+    void* dbeta;        // nullable
+    int64_t N;
+    int parts;
+};
+
 // Launch geometry chosen on the host.
 struct Plan {
     int variant;          // V_WAVE, V_WORKGROUP, V_ELEMENT or V_GENERAL
@@ -58,6 +83,8 @@ constexpr int kElemTarget = 8;         // element variant: about 8 elements per 
 constexpr int kElemMaxPerLane = 16;    // ... at most 16 (with 16 waves: rows up to 16384)
 constexpr int64_t kMaxGrid = 1 << 20;  // grid cap; kernels loop over the remaining rows
 constexpr int64_t kPersistentBlocks = 2048;  // at least this many workgroups: persistent launch
+constexpr int kBwdMaxParts = 1024;     // backward: at most this many partial column rows (workspace bound)
+constexpr int kBwdTargetChunks = 2;    // backward: about 2 chunks of x and of dy per lane
 
 // Enqueue the planned kernel for one I/O dtype (one translation unit per dtype and mode).
 hipError_t launch_f32(int op, const Plan& plan, const Params& p, hipStream_t stream);
@@ -66,5 +93,8 @@ hipError_t launch_bf16(int op, const Plan& plan, const Params& p, hipStream_t st
 hipError_t launch_f32_persistent(int op, const Plan& plan, const Params& p, hipStream_t stream);
 hipError_t launch_f16_persistent(int op, const Plan& plan, const Params& p, hipStream_t stream);
 hipError_t launch_bf16_persistent(int op, const Plan& plan, const Params& p, hipStream_t stream);
+hipError_t launch_bwd_f32(int op, const Plan& plan, const BwdParams& p, const BwdColParams& cp, hipStream_t stream);
+hipError_t launch_bwd_f16(int op, const Plan& plan, const BwdParams& p, const BwdColParams& cp, hipStream_t stream);
+hipError_t launch_bwd_bf16(int op, const Plan& plan, const BwdParams& p, const BwdColParams& cp, hipStream_t stream);
 
 }  // namespace rn

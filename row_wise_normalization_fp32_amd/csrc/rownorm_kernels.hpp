@@ -776,6 +776,15 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_elem_kernel(Params p) {
         cnt += k <= 0 ? 0 : (k >= 64 ? 64 : k);
     }
     const float n_w = static_cast<float>(cnt);
+    // The lane's columns are the same for every row: its parameters are loaded once.
+    float g[HG ? V : 1], b[HB ? V : 1];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const unsigned j = static_cast<unsigned>(i * LANES) + t;
+        const unsigned jc = j < N ? j : N - 1;
+        if constexpr (HG) g[i] = IO::load1(p.gamma, jc);
+        if constexpr (HB) b[i] = IO::load1(p.beta, jc);
+    }
     int buf = 0;
     for (int64_t base = static_cast<int64_t>(blockIdx.x) * RPB; base < p.rows;
          base += static_cast<int64_t>(gridDim.x) * RPB) {
@@ -858,16 +867,7 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_elem_kernel(Params p) {
             scale = inv_sqrt(fmaf(Ssq, p.inv_n, p.eps));
             if (t == 0 && p.rstd) p.rstd[row] = scale;
         }
-        // a7: the parameters are loaded here, after the row's addresses are dead (they are
-        // small and cache-resident), then normalize and store.
-        float g[HG ? V : 1], b[HB ? V : 1];
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-            const unsigned j = static_cast<unsigned>(i * LANES) + t;
-            const unsigned jc = j < N ? j : N - 1;
-            if constexpr (HG) g[i] = IO::load1(p.gamma, jc);
-            if constexpr (HB) b[i] = IO::load1(p.beta, jc);
-        }
+        // a7: normalize, apply the parameters, store.
         char* yrow = static_cast<char*>(p.y) + row * p.ldy * S;
 #pragma unroll
         for (int i = 0; i < V; ++i) {
@@ -1114,13 +1114,16 @@ inline hipError_t launch_e(const Plan& plan, const Params& p, hipStream_t s) {
 }
 
 // Element kernel instances: W = 1 with 1-8 elements per lane; W = 2, 4, 8 with 8; W = 16
-// with 8 or 16 (rows of up to 16384 elements). Parameter presence is a runtime check here.
+// with 8 or 16 (rows of up to 16384 elements). Many rows: a persistent grid (the kernel
+// loops over rows either way; its parameters stay in registers across rows).
 template <int DT, int OP>
 inline hipError_t launch_elem(const Plan& plan, const Params& p, hipStream_t s) {
     const int W = plan.waves_per_row, V = plan.chunks_per_lane;
     const int aff = (p.gamma ? AFF_G : 0) | (OpTraits<OP>::LN && p.beta ? AFF_B : 0);
     if (plan.rows_per_block != rows_per_block_for(W)) return hipErrorInvalidValue;
-#define RN_EL(WW, VV, A) go(rownorm_elem_kernel<DT, OP, WW, VV, rows_per_block_for(WW), A>, plan, p, s)
+#define RN_EL(WW, VV, A)                                                                      \
+    (plan.persistent ? go_persistent(rownorm_elem_kernel<DT, OP, WW, VV, rows_per_block_for(WW), A>, plan, p, s) \
+                     : go(rownorm_elem_kernel<DT, OP, WW, VV, rows_per_block_for(WW), A>, plan, p, s))
 #define RN_EL_AFF(WW, VV)                                                     \
     do {                                                                      \
         if constexpr (OpTraits<OP>::SM) return RN_EL(WW, VV, 0);              \

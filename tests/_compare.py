@@ -118,3 +118,42 @@ def check_equal_values(got_t: torch.Tensor, ref: np.ndarray, what: str):
     got = got_t.detach().cpu().double().numpy().reshape(-1)
     diff = got != ref.reshape(-1)
     assert not diff.any(), f"{what}: {int(diff.sum())} values differ"
+
+
+U32 = 2.0 ** -24
+
+
+def check_dx(dx_gpu: torch.Tensor, dx_ref: np.ndarray, row_scale: np.ndarray, what: str = "dx"):
+    """Backward dx. row_scale S_r = rstd_r * max_j |g_j| * max(1, max_j |xhat_j|)^2 bounds
+    the magnitude of every term of dx_j = rstd * (g_j - mean(g) - xhat_j * mean(g xhat)).
+    An fp32 evaluation (row sums of at most 16 terms per lane, a 6-level lane tree and 16
+    waves, then three roundings per element) errs by at most about 64 * 2^-24 * S_r; the
+    16-bit outputs add their own rounding (1 ulp of the result)."""
+    dt = dtype_name(dx_gpu)
+    got = dx_gpu.detach().cpu().double().numpy().reshape(dx_ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
+    tol = 64 * U32 * row_scale[:, None]
+    if dt != "fp32":
+        mag = np.maximum(np.abs(dx_ref), 2.0 ** -24)
+        tol = tol + np.exp2(np.floor(np.log2(mag)) - MANT_BITS[dt])
+    err = np.abs(got - dx_ref)
+    bad = err > tol
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements off, worst err/tol {float((err / tol).max()):.3g}"
+    return float((err / tol).max())
+
+
+def check_colsum(got_t: torch.Tensor, ref: np.ndarray, abs_sum: np.ndarray, depth: float, what: str):
+    """Column sums over rows (dgamma, dbeta): a sum of terms t_r whose fp32 evaluation
+    passes through at most `depth` sequential additions errs by at most about
+    (depth + 3) * 2^-24 * sum_r |t_r| (abs_sum); 16-bit outputs add 1 ulp of the result."""
+    dt = dtype_name(got_t)
+    got = got_t.detach().cpu().double().numpy().reshape(-1)
+    tol = (depth + 3) * U32 * abs_sum
+    if dt != "fp32":
+        mag = np.maximum(np.abs(ref), 2.0 ** -24)
+        tol = tol + np.exp2(np.floor(np.log2(mag)) - MANT_BITS[dt])
+    tol = np.maximum(tol, 1e-30)
+    err = np.abs(got - ref)
+    bad = err > tol
+    assert not bad.any(), f"{what}: {int(bad.sum())} columns off, worst err/tol {float((err / tol).max()):.3g}"
+    return float((err / tol).max())

@@ -1,0 +1,167 @@
+"""GPU parity of the backward passes (LayerNorm, RMSNorm) against the fp64 oracle.
+
+The forward statistics fed to both sides are the oracle's fp64 mean / rstd rounded to fp32
+(the dtype the forward stores), so both evaluate the same formula at the same point. Tolerances
+are derived in tests/_compare.py (check_dx, check_colsum); the column-sum depth comes from the
+launch plan: rows per lane, the row groups of a workgroup, and the P partial rows.
+"""
+
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import row_wise_normalization_fp32_amd as rn
+import workloads
+from _compare import check_colsum, check_dx
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TD = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _stats(w, inp):
+    if w.op == "ln_bwd":
+        f = oracle.layer_norm(inp["x"], None, None, w.eps, threads=min(16, os.cpu_count() or 1), want_y=False)
+        return f["mean"].astype(np.float32), f["rstd"].astype(np.float32)
+    f = oracle.rms_norm(inp["x"], None, w.eps, threads=min(16, os.cpu_count() or 1), want_y=False)
+    return None, f["rstd"].astype(np.float32)
+
+
+def _scales(w, inp, mean, rstd, gamma):
+    """Row scales for dx and absolute column sums for dgamma / dbeta (tolerance scales,
+    from the inputs)."""
+    x = inp["x"].double().numpy()
+    dy = inp["dy"].double().numpy()
+    r = rstd.astype(np.float64)[:, None]
+    xh = (x - mean.astype(np.float64)[:, None]) * r if mean is not None else x * r
+    g = dy * (gamma.double().numpy()[None, :] if gamma is not None else 1.0)
+    row = r[:, 0] * np.abs(g).max(axis=1) * np.maximum(1.0, np.abs(xh).max(axis=1)) ** 2
+    return row, np.abs(dy * xh).sum(axis=0), np.abs(dy).sum(axis=0)
+
+
+def _depth(op, rows, N, dtype):
+    st, info = rn.plan_backward(op, rows, N, TD[dtype])
+    assert st == 0, st
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    parts = min(info["grid_blocks"], 2 * cus)
+    rpb = info["rows_per_block"]
+    per_lane = -(-rows // (parts * rpb))
+    return per_lane + rpb + parts / 16 + 16
+
+
+def run_case(w, with_gamma=True, in_place=False):
+    inp = workloads.make_inputs(w)
+    gamma = inp.get("gamma" if w.op == "ln_bwd" else "weight") if with_gamma else None
+    mean, rstd = _stats(w, inp)
+    dev = {k: v.to(DEV) for k, v in inp.items()}
+    g_dev = gamma.to(DEV) if gamma is not None else None
+    rstd_d = torch.from_numpy(rstd).to(DEV)
+    if w.op == "ln_bwd":
+        ref = oracle.layer_norm_backward(inp["dy"], inp["x"], gamma, mean=mean, rstd=rstd, eps=w.eps)
+        mean_d = torch.from_numpy(mean).to(DEV)
+        dyv = dev["dy"].clone()
+        dx, dg, db = rn.ln_backward(dyv, dev["x"], mean_d, rstd_d, g_dev, dx=dyv if in_place else None)
+    else:
+        ref = oracle.rms_norm_backward(inp["dy"], inp["x"], gamma, rstd=rstd, eps=w.eps)
+        dyv = dev["dy"].clone()
+        dx, dg = rn.rms_norm_backward(dyv, dev["x"], rstd_d, g_dev, dx=dyv if in_place else None)
+        db = None
+    torch.cuda.synchronize()
+    row, a_g, a_b = _scales(w, inp, mean, rstd, gamma)
+    check_dx(dx, ref["dx"], row)
+    depth = _depth("ln" if w.op == "ln_bwd" else "rms", w.rows, w.N, w.dtype)
+    check_colsum(dg, ref["dgamma" if w.op == "ln_bwd" else "dweight"], a_g, depth, "dgamma")
+    if db is not None:
+        check_colsum(db, ref["dbeta"], a_b, depth, "dbeta")
+
+
+@pytest.mark.parametrize("w", [workloads.LN_BWD, workloads.RMS_BWD], ids=lambda w: w.name)
+def test_backward_full_size(w):
+    run_case(w)
+
+
+SHAPES = [(37, 1000), (5, 4096), (9, 2056), (3, 8), (64, 1024), (33, 333), (6, 16384), (4, 12289), (300, 64)]
+
+
+@pytest.mark.parametrize("op", ["ln_bwd", "rms_bwd"])
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+def test_backward_shapes(op, dtype):
+    base = workloads.LN_BWD if op == "ln_bwd" else workloads.RMS_BWD
+    for rows, N in SHAPES:
+        run_case(base.scaled(rows=rows, N=N, seed=1200 + N, dtype=dtype))
+
+
+@pytest.mark.parametrize("op", ["ln_bwd", "rms_bwd"])
+def test_backward_without_gamma_and_in_place(op):
+    base = workloads.LN_BWD if op == "ln_bwd" else workloads.RMS_BWD
+    run_case(base.scaled(rows=64, N=4096, seed=1210), with_gamma=False)
+    run_case(base.scaled(rows=64, N=4096, seed=1211), in_place=True)
+    run_case(base.scaled(rows=64, N=1001, seed=1212), in_place=True)  # element kernel
+
+
+def test_backward_offset_rows_and_many_rows():
+    # rows far from zero (the cancellation case of the forward) and more rows than the
+    # partial-row cap (several rows per lane)
+    run_case(workloads.LN_BWD.scaled(rows=256, N=4096, seed=1220, dtype="fp32", x_dist="row_offset",
+                                     row_offset=1000.0))
+    run_case(workloads.LN_BWD.scaled(rows=16384, N=1024, seed=1221, dtype="bf16"))
+    run_case(workloads.RMS_BWD.scaled(rows=16384, N=512, seed=1222, dtype="fp16"))
+
+
+def test_backward_partial_outputs_and_zero_rows():
+    w = workloads.LN_BWD.scaled(rows=32, N=2048, seed=1230)
+    inp = workloads.make_inputs(w)
+    mean, rstd = _stats(w, inp)
+    ref = oracle.layer_norm_backward(inp["dy"], inp["x"], inp["gamma"], mean=mean, rstd=rstd, eps=w.eps)
+    dev = {k: v.to(DEV) for k, v in inp.items()}
+    m, r = torch.from_numpy(mean).to(DEV), torch.from_numpy(rstd).to(DEV)
+    dx, dg, db = rn.ln_backward(dev["dy"], dev["x"], m, r, dev["gamma"], want_dgamma=False, want_dbeta=False)
+    assert dg is None and db is None
+    row, a_g, a_b = _scales(w, inp, mean, rstd, inp["gamma"])
+    torch.cuda.synchronize()
+    check_dx(dx, ref["dx"], row)
+    dx, dg, db = rn.ln_backward(dev["dy"], dev["x"], m, r, dev["gamma"], want_dx=False)
+    torch.cuda.synchronize()
+    assert dx is None
+    depth = _depth("ln", 32, 2048, "bf16")
+    check_colsum(dg, ref["dgamma"], a_g, depth, "dgamma")
+    check_colsum(db, ref["dbeta"], a_b, depth, "dbeta")
+    # rows == 0: the parameter gradients are sums over no rows
+    e = torch.empty(0, 64, device=DEV, dtype=torch.bfloat16)
+    z = torch.empty(0, device=DEV)
+    dx, dg, db = rn.ln_backward(e, e, z, z, torch.ones(64, device=DEV, dtype=torch.bfloat16))
+    torch.cuda.synchronize()
+    assert dx.shape == (0, 64) and torch.equal(dg, torch.zeros_like(dg)) and torch.equal(db, torch.zeros_like(db))
+
+
+def test_backward_is_deterministic():
+    w = workloads.LN_BWD.scaled(rows=2048, N=4096, seed=1240)
+    inp = workloads.make_inputs(w)
+    mean, rstd = _stats(w, inp)
+    dev = {k: v.to(DEV) for k, v in inp.items()}
+    m, r = torch.from_numpy(mean).to(DEV), torch.from_numpy(rstd).to(DEV)
+    first = None
+    for _ in range(10):
+        outs = rn.ln_backward(dev["dy"], dev["x"], m, r, dev["gamma"])
+        torch.cuda.synchronize()
+        outs = [o.clone() for o in outs]
+        if first is None:
+            first = outs
+        else:
+            for a, b in zip(first, outs):
+                assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_backward_argument_errors():
+    x = torch.zeros(4, 64, device=DEV)
+    s = torch.ones(4, device=DEV)
+    with pytest.raises(rn.RowNormError) as e:
+        rn.ln_backward(x, x, s, s, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    assert e.value.status == 8
+    with pytest.raises(rn.RowNormError) as e:
+        rn.ln_backward(torch.zeros(4, 32768, device=DEV), torch.zeros(4, 32768, device=DEV), s, s)
+    assert e.value.status == 5

@@ -17,13 +17,13 @@ import row_wise_normalization_fp32_amd as rn
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rownorm.h")
 
-OK, NULL, SHAPE, DTYPE, ALIAS, UNSUP, HIP, ALIGN = range(8)
+OK, NULL, SHAPE, DTYPE, ALIAS, UNSUP, HIP, ALIGN, WORKSPACE = range(9)
 
 
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^(?:int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+    names = re.findall(r"^(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
     assert names, "no declarations parsed"
     return names
 
@@ -32,7 +32,8 @@ def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(rn.LIB_PATH)
     names = _declared_functions()
     for n in ("ln_forward", "rms_norm", "fused_add_rms_norm", "fused_add_layer_norm", "softmax_forward",
-              "rn_forward_ex", "rn_plan", "rn_status_string"):
+              "rn_forward_ex", "ln_backward", "rms_norm_backward", "rn_backward_workspace_bytes",
+              "rn_plan_backward", "rn_plan", "rn_status_string"):
         assert n in names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
@@ -66,6 +67,7 @@ def test_status_strings_and_version():
     ("softmax", torch.float32, 128, 4096, "workgroup", 4, 4, False),
     ("softmax", torch.float32, 8192, 4096, "workgroup", 4, 4, False),  # no parameters: never persistent
     ("softmax", torch.float16, 64, 333, "element", 1, 8, False),
+    ("ln", torch.bfloat16, 16384, 4095, "element", 8, 8, True),        # many ragged rows: persistent
 ])
 def test_plan_variant_choice(op, dtype, rows, N, variant, W, V, persistent):
     ptrs = {"gamma": 1 << 44, "beta": (1 << 44) + (1 << 30)}
@@ -78,7 +80,8 @@ def test_plan_variant_choice(op, dtype, rows, N, variant, W, V, persistent):
         assert info["grid_blocks"] == rows and info["block_threads"] == 256
         return
     if variant == "element":
-        assert info["waves_per_row"] == W and not info["exact"] and not info["persistent"]
+        assert info["waves_per_row"] == W and not info["exact"] and info["lds_bytes"] == 0
+        assert info["persistent"] == persistent
         assert 64 * W * V >= N and (V == 1 or 64 * W * V // 2 < N or W > 1)
         return
     assert info["waves_per_row"] == W
@@ -225,3 +228,47 @@ def test_python_binding_rejects_cpu_tensors():
         rn.ln_forward(torch.zeros(2, 8))
     with pytest.raises(ValueError):
         rn.rms_norm(torch.zeros(2, 8))
+
+
+def test_backward_plan_and_validation():
+    bf16, f32 = torch.bfloat16, torch.float32
+    ws = {"dgamma": 1 << 45, "dbeta": (1 << 45) + (1 << 20), "workspace": 1 << 46}
+    st, info = rn.plan_backward("ln", 4096, 16384, bf16, ptrs=ws)
+    assert st == OK and info["variant"] == "workgroup" and info["waves_per_row"] == 16
+    assert info["chunks_per_lane"] == 2 and info["block_threads"] == 1024 and info["grid_blocks"] == 1024
+    st, info = rn.plan_backward("rms", 2048, 4096, torch.float16, ptrs=ws)
+    assert st == OK and info["waves_per_row"] == 4 and info["rows_per_block"] == 4 and info["lds_bytes"] == 4096 * 4
+    # rows that are not whole chunks: element kernel; beyond 16384 elements: unsupported
+    assert rn.plan_backward("ln", 8, 1001, bf16, ptrs=ws)[1]["variant"] == "element"
+    assert rn.plan_backward("ln", 8, 16384, f32, ptrs=ws)[1]["variant"] == "element"
+    assert rn.plan_backward("ln", 8, 32768, bf16, ptrs=ws)[0] == UNSUP
+    # workspace: required for parameter gradients, at least rn_backward_workspace_bytes
+    assert rn.backward_workspace_bytes("ln", 4096, 16384) == 2 * 1024 * 16384 * 4
+    assert rn.backward_workspace_bytes("rms", 100, 64) == 100 * 64 * 4
+    assert rn.plan_backward("ln", 64, 256, bf16, ptrs={"dgamma": 1 << 45})[0] == 8
+    assert rn.plan_backward("ln", 64, 256, bf16, ptrs=ws, workspace_bytes=100)[0] == 8
+    assert rn.plan_backward("ln", 64, 256, bf16)[0] == OK  # dx only: no workspace needed
+    assert rn.plan_backward("ln", 0, 256, bf16, ptrs={"dgamma": 1 << 45, "dy": None, "x": None})[0] == OK
+    # required inputs
+    assert rn.plan_backward("ln", 4, 256, bf16, ptrs={"mean": None})[0] == NULL
+    assert rn.plan_backward("rms", 4, 256, bf16, ptrs={"mean": None})[0] == OK
+    assert rn.plan_backward("ln", 4, 256, bf16, ptrs={"rstd": None})[0] == NULL
+    # aliasing: dx may be dy or x; the workspace and the parameter gradients overlap nothing
+    base = 1 << 40
+    assert rn.plan_backward("ln", 4, 256, bf16, ptrs={"dy": base, "dx": base})[0] == OK
+    assert rn.plan_backward("ln", 4, 256, bf16, ptrs={"x": base, "dx": base, "dy": base + (1 << 30)})[0] == OK
+    assert rn.plan_backward("ln", 4, 256, bf16, ptrs={"dy": base, "dx": base + 64})[0] == ALIAS
+    assert rn.plan_backward("ln", 4, 256, bf16, ptrs={**ws, "dbeta": (1 << 45) + 16})[0] == ALIAS
+    assert rn.plan_backward("ln", 4, 256, bf16, ptrs={**ws, "workspace": (1 << 45) + 64})[0] == ALIAS
+    assert rn.plan_backward("ln", 4, 256, bf16, ptrs={**ws, "workspace": (1 << 46) + 2})[0] == ALIGN
+    assert rn.plan_backward("softmax", 4, 256, bf16)[0] == SHAPE
+    assert rn.plan_backward("ln", 4, 256, 9)[0] == DTYPE
+
+
+def test_backward_entry_points_reject_before_launch():
+    lib = rn._lib
+    assert lib.ln_backward(None, None, None, None, None, None, None, None, 4, 64, 0, None, 0, None) == NULL
+    assert lib.ln_backward(0x1000, 0x2000, None, 0x3000, 0x4000, None, 0x5000, None, 4, 64, 0, None, 0,
+                           None) == 8
+    assert lib.rms_norm_backward(0x1000, 0x2000, None, 0x4000, 0x1000 + 64, None, 4, 64, 0, None, 0, None) == ALIAS
+    assert lib.rms_norm_backward(0x1000, 0x200000, None, 0x400000, None, None, 4, 65536, 0, None, 0, None) == UNSUP

@@ -163,6 +163,16 @@ def test_odd_widths(N):
         check_case(base.scaled(rows=3, N=N, seed=700 + N))
 
 
+@pytest.mark.parametrize("case", [("ln", "bf16", 16384, 4095), ("fused_add_ln", "fp16", 8192, 1001),
+                                  ("rms", "fp32", 16384, 101), ("fused_add_rms", "bf16", 2048, 16383),
+                                  ("softmax", "fp32", 16384, 333)], ids=lambda c: f"{c[0]}-{c[1]}-{c[2]}x{c[3]}")
+def test_element_kernel_persistent(case):
+    op, dtype, rows, N = case
+    st, info = rn.plan(op, rows, N, TD[dtype])
+    assert st == 0 and info["variant"] == "element" and info["persistent"], info
+    check_case(BASES[op].scaled(rows=rows, N=N, seed=720 + N, dtype=dtype))
+
+
 @pytest.mark.parametrize("op", ["ln", "rms", "fused_add_rms", "fused_add_ln", "softmax"])
 def test_element_kernel_every_width(op):
     # the element kernel's (W, V) instances: W = 1 with V = 1..8, W = 2..16 with V = 8, W = 16 with V = 16
