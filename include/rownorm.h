@@ -244,7 +244,7 @@ int rn_plan(int op, const void* x, const void* residual, const void* gamma, cons
             int dtype, int variant, const rn_row_strides* strides, rn_plan_info* out);
 
 /* The same for a backward call (op: RN_OP_LAYER_NORM or RN_OP_RMS_NORM); grid_blocks is the
- * row kernel's workgroup count before the device cap of two per compute unit. */
+ * row kernel's workgroup count before the launch caps it at what the device keeps resident. */
 int rn_plan_backward(int op, const void* dy, const void* x, const void* gamma, const float* mean, const float* rstd,
                      const void* dx, const void* dgamma, const void* dbeta, int64_t rows, int64_t N, int dtype,
                      const void* workspace, size_t workspace_bytes, rn_plan_info* out);

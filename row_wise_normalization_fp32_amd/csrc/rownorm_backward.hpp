@@ -309,31 +309,21 @@ __global__ __launch_bounds__(256) void rownorm_bwd_cols_kernel(BwdColParams p) {
 
 constexpr int rows_per_block_bwd(int W) { return W >= 16 ? 1 : 16 / W; }  // 16-wave workgroups
 
-template <typename K>
-inline hipError_t go_bwd(K kernel, int parts, int threads, int lds, const BwdParams& p, hipStream_t s) {
-    BwdParams args = p;
-    void* argv[] = {&args};
-    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), dim3(static_cast<unsigned>(parts)),
-                           dim3(static_cast<unsigned>(threads)), argv, static_cast<size_t>(lds), s);
-}
+using BwdKernel = void (*)(BwdParams);
 
-// Backward plan: variant (V_WORKGROUP for the vectorized kernel, V_ELEMENT), W, V, exact.
+// The row-kernel instance for a backward plan: V_WORKGROUP (vectorized) or V_ELEMENT.
 template <int DT, int OP>
-inline hipError_t launch_bwd(const Plan& plan, const BwdParams& p, hipStream_t s) {
+inline BwdKernel select_bwd(const Plan& plan, bool hg) {
     const int W = plan.waves_per_row, V = plan.chunks_per_lane;
-    const int threads = plan.block_threads;
-    const int parts = p.parts;
-    const int lds = plan.lds_bytes;
-    const bool hg = p.gamma != nullptr;
-    if (plan.rows_per_block != rows_per_block_bwd(W)) return hipErrorInvalidValue;
-#define RN_BV(WW, VV, EX)                                                                                        \
-    (hg ? go_bwd(rownorm_bwd_vec_kernel<DT, OP, WW, VV, rows_per_block_bwd(WW), EX, true>, parts, threads, lds, p, s) \
-        : go_bwd(rownorm_bwd_vec_kernel<DT, OP, WW, VV, rows_per_block_bwd(WW), EX, false>, parts, threads, lds, p, s))
+    if (plan.rows_per_block != rows_per_block_bwd(W)) return nullptr;
+#define RN_BV(WW, VV, EX)                                                                        \
+    (hg ? static_cast<BwdKernel>(rownorm_bwd_vec_kernel<DT, OP, WW, VV, rows_per_block_bwd(WW), EX, true>) \
+        : static_cast<BwdKernel>(rownorm_bwd_vec_kernel<DT, OP, WW, VV, rows_per_block_bwd(WW), EX, false>))
 #define RN_BV_E(WW, VV) (plan.exact ? RN_BV(WW, VV, true) : RN_BV(WW, VV, false))
-#define RN_BE(WW, VV)                                                                                            \
-    (hg ? go_bwd(rownorm_bwd_elem_kernel<DT, OP, WW, VV, rows_per_block_bwd(WW), true>, parts, threads, lds, p, s) \
-        : go_bwd(rownorm_bwd_elem_kernel<DT, OP, WW, VV, rows_per_block_bwd(WW), false>, parts, threads, lds, p, s))
-    if (plan.variant == V_WORKGROUP || plan.variant == V_WAVE) {
+#define RN_BE(WW, VV)                                                                             \
+    (hg ? static_cast<BwdKernel>(rownorm_bwd_elem_kernel<DT, OP, WW, VV, rows_per_block_bwd(WW), true>) \
+        : static_cast<BwdKernel>(rownorm_bwd_elem_kernel<DT, OP, WW, VV, rows_per_block_bwd(WW), false>))
+    if (plan.variant == V_WORKGROUP) {
         switch (W * 100 + V) {
         case 101: return RN_BV_E(1, 1);
         case 102: return RN_BV_E(1, 2);
@@ -341,7 +331,7 @@ inline hipError_t launch_bwd(const Plan& plan, const BwdParams& p, hipStream_t s
         case 402: return RN_BV_E(4, 2);
         case 802: return RN_BV_E(8, 2);
         case 1602: return RN_BV_E(16, 2);
-        default: return hipErrorInvalidValue;
+        default: return nullptr;
         }
     }
     if (plan.variant == V_ELEMENT) {
@@ -355,25 +345,50 @@ inline hipError_t launch_bwd(const Plan& plan, const BwdParams& p, hipStream_t s
         case 808: return RN_BE(8, 8);
         case 1608: return RN_BE(16, 8);
         case 1616: return RN_BE(16, 16);
-        default: return hipErrorInvalidValue;
+        default: return nullptr;
         }
     }
 #undef RN_BE
 #undef RN_BV_E
 #undef RN_BV
-    return hipErrorInvalidValue;
+    return nullptr;
 }
 
+// Row kernel, then column kernel. The row kernel's grid P is what the device keeps resident
+// (compute units x workgroups per unit for this instance, queried once per instance and
+// device), capped by the plan: more workgroups would only add partial rows to sum.
 template <int DT>
-inline hipError_t launch_bwd_dtype(int op, const Plan& plan, const BwdParams& p, const BwdColParams& cp,
+inline hipError_t launch_bwd_dtype(int op, const Plan& plan, const BwdParams& p0, const BwdColParams& cp0,
                                    hipStream_t s) {
-    hipError_t e = hipSuccess;
-    if (p.rows > 0 && (p.dx != nullptr || p.ws != nullptr))
-        e = op == OP_LN ? launch_bwd<DT, OP_LN>(plan, p, s) : launch_bwd<DT, OP_RMS>(plan, p, s);
-    if (e != hipSuccess) return e;
+    BwdParams p = p0;
+    BwdColParams cp = cp0;
+    if (p.rows > 0 && (p.dx != nullptr || p.ws != nullptr)) {
+        const bool hg = p.gamma != nullptr;
+        BwdKernel k = op == OP_LN ? select_bwd<DT, OP_LN>(plan, hg) : select_bwd<DT, OP_RMS>(plan, hg);
+        if (k == nullptr) return hipErrorInvalidValue;
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        int per_cu = 0, cus = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k),
+                                                         plan.block_threads, static_cast<size_t>(plan.lds_bytes));
+        if (e != hipSuccess) return e;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        int64_t parts = static_cast<int64_t>(cus) * (per_cu < 1 ? 1 : per_cu);
+        if (parts > plan.grid) parts = plan.grid;
+        p.parts = static_cast<int>(parts);
+        cp.parts = p.parts;
+        void* argv[] = {&p};
+        e = hipLaunchKernel(reinterpret_cast<const void*>(k), dim3(static_cast<unsigned>(parts)),
+                            dim3(static_cast<unsigned>(plan.block_threads)), argv,
+                            static_cast<size_t>(plan.lds_bytes), s);
+        if (e != hipSuccess) return e;
+    } else {
+        cp.parts = 0;
+    }
     if (cp.dgamma == nullptr && cp.dbeta == nullptr) return hipSuccess;
-    BwdColParams args = cp;
-    void* argv[] = {&args};
+    void* argv[] = {&cp};
     const unsigned blocks = static_cast<unsigned>((cp.N + 15) / 16);
     return hipLaunchKernel(reinterpret_cast<const void*>(rownorm_bwd_cols_kernel<DT>), dim3(blocks), dim3(256), argv,
                            0, s);

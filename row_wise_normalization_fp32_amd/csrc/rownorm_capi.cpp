@@ -390,17 +390,6 @@ int validate_and_plan_bwd(BwdArgs& a, Plan* plan, int64_t* chunks) {
     return RN_OK;
 }
 
-int device_cus() {
-    static int cache[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    int v = dev < 64 ? __atomic_load_n(&cache[dev], __ATOMIC_RELAXED) : 0;
-    if (v > 0) return v;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (dev < 64) __atomic_store_n(&cache[dev], v, __ATOMIC_RELAXED);
-    return v;
-}
-
 int run_bwd(BwdArgs a, hipStream_t stream) {
     Plan plan;
     int64_t C = 0;
@@ -408,12 +397,6 @@ int run_bwd(BwdArgs a, hipStream_t stream) {
     if (st != RN_OK) return st;
     const bool want_cols = a.dgamma != nullptr || a.dbeta != nullptr;
     if (a.rows == 0 && !want_cols) return RN_OK;
-    int64_t parts = 0;
-    if (a.rows > 0) {
-        const int cus = device_cus();
-        if (cus <= 0) return RN_ERR_HIP;
-        parts = plan.grid < 2 * int64_t(cus) ? plan.grid : 2 * int64_t(cus);  // two 16-wave workgroups per CU
-    }
     rn::BwdParams p;
     p.dy = a.dy;
     p.x = a.x;
@@ -426,13 +409,13 @@ int run_bwd(BwdArgs a, hipStream_t stream) {
     p.N = a.N;
     p.C = C;
     p.inv_n = static_cast<float>(1.0 / static_cast<double>(a.N));
-    p.parts = static_cast<int>(parts);
+    p.parts = 0;  // set at launch from the device's resident capacity
     rn::BwdColParams cp;
     cp.ws = p.ws;
     cp.dgamma = a.dgamma;
     cp.dbeta = a.dbeta;
     cp.N = a.N;
-    cp.parts = static_cast<int>(parts);
+    cp.parts = 0;
     const int op = a.op == RN_OP_LAYER_NORM ? rn::OP_LN : rn::OP_RMS;
     hipError_t e = hipErrorInvalidValue;
     switch (a.dtype) {

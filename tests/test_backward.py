@@ -46,11 +46,13 @@ def _scales(w, inp, mean, rstd, gamma):
 def _depth(op, rows, N, dtype):
     st, info = rn.plan_backward(op, rows, N, TD[dtype])
     assert st == 0, st
+    # the launch uses P = min(grid, CUs x resident workgroups per CU) partial rows: at least
+    # one workgroup per CU (rows per lane), at most the plan's grid (partial rows per lane
+    # of the column kernel)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    parts = min(info["grid_blocks"], 2 * cus)
     rpb = info["rows_per_block"]
-    per_lane = -(-rows // (parts * rpb))
-    return per_lane + rpb + parts / 16 + 16
+    per_lane = -(-rows // (min(info["grid_blocks"], cus) * rpb))
+    return per_lane + rpb + info["grid_blocks"] / 16 + 16
 
 
 def run_case(w, with_gamma=True, in_place=False):
