@@ -4,7 +4,10 @@
 One step = one LayerNorm forward (y, mean, rstd) over the 4096 x 16384 bf16 workload, the
 largest configuration and the one the bandwidth target applies to (rows * N = 64M >= 8M).
 The same measurement is also taken for fused residual-add + RMSNorm at 8192 x 4096 fp16
-(32M elements) and reported in the same JSON line under "fused_add_rms_norm".
+(32M elements) and reported in the same JSON line under "fused_add_rms_norm", and, under
+"more", for fused residual-add + LayerNorm (8192 x 4096 bf16), softmax (8192 x 4096 fp32),
+the LayerNorm backward (4096 x 16384 bf16: dx, dgamma, dbeta) and the RMSNorm backward
+(8192 x 4096 fp16: dx, dweight).
 
 Cold cache: inputs and outputs rotate through enough buffer sets that each launch touches
 memory the previous launches have pushed out of L2 (8 x 4 MiB) and the 256 MiB
@@ -17,7 +20,10 @@ current stream, which the binding passes to the C ABI), giving the per-kernel av
 duration used for the roofline.
 
 value = algorithmic bytes per step / ms_per_step (GB/s, 1 GB = 1e9 B). Algorithmic bytes:
-LayerNorm 2*rows*N*s + 2*N*s + 8*rows; fused 4*rows*N*s + N*s + 4*rows (with rstd).
+LayerNorm 2*rows*N*s + 2*N*s + 8*rows; fused 4*rows*N*s + N*s + 4*rows (with rstd); fused
+LayerNorm 4*rows*N*s + 2*N*s + 8*rows; softmax 2*rows*N*s; LayerNorm backward
+3*rows*N*s + 3*N*s + 8*rows; RMSNorm backward 3*rows*N*s + 2*N*s + 4*rows. (The backward's
+fp32 partial column rows are not algorithmic bytes: they count against it.)
 
 The CPU baseline times the fp64 oracle (oracle/) on the same workload on the host cores.
 
@@ -79,6 +85,7 @@ def counter_traffic(workload_key: str):
 def make_sets(w, nsets, dev):
     import torch
 
+    import row_wise_normalization_fp32_amd as rn
     import workloads
 
     base = workloads.make_inputs(w)
@@ -91,12 +98,21 @@ def make_sets(w, nsets, dev):
             else:
                 # distinct buffers with the workload's values (a rolled copy per set)
                 s[k] = torch.roll(v, shifts=i, dims=0).to(dev) if i else v.to(dev)
-        s["y"] = torch.empty_like(s["x"])
-        if w.op == "fused_add_rms":
-            s["residual_out"] = torch.empty_like(s["x"])
         s["rstd"] = torch.empty(w.rows, dtype=torch.float32, device=dev)
-        if w.op == "ln":
-            s["mean"] = torch.empty(w.rows, dtype=torch.float32, device=dev)
+        s["mean"] = torch.empty(w.rows, dtype=torch.float32, device=dev)
+        if w.op in ("ln_bwd", "rms_bwd"):
+            # the forward statistics the backward consumes (computed once, outside timing)
+            if w.op == "ln_bwd":
+                rn.ln_forward(s["x"], None, None, w.eps, mean=s["mean"], rstd=s["rstd"])
+            else:
+                rn.rms_norm(s["x"], None, w.eps, rstd=s["rstd"])
+            s["dx"] = torch.empty_like(s["x"])
+            s["ws"] = torch.empty(rn.backward_workspace_bytes("ln" if w.op == "ln_bwd" else "rms", w.rows, w.N),
+                                  dtype=torch.uint8, device=dev)
+        else:
+            s["y"] = torch.empty_like(s["x"])
+        if w.op in ("fused_add_rms", "fused_add_ln"):
+            s["residual_out"] = torch.empty_like(s["x"])
         sets.append(s)
     return sets
 
@@ -104,11 +120,16 @@ def make_sets(w, nsets, dev):
 def kernel_name(w, plan):
     """The kernel instance a workload's launch runs, as rocprofv3 lists it (template arguments:
     dtype, op, waves per row, chunks per lane, row groups per workgroup, exact, affine, flags)."""
+    if w.op in ("ln_bwd", "rms_bwd"):
+        k = "rownorm_bwd_vec_kernel" if plan["variant"] == "workgroup" else "rownorm_bwd_elem_kernel"
+        return (f"rn::{k} ({w.dtype}, {w.op}, W={plan['waves_per_row']} waves per row, V={plan['chunks_per_lane']}, "
+                f"{plan['rows_per_block']} row group(s) per workgroup) + rn::rownorm_bwd_cols_kernel")
     if plan["variant"] == "general":
         return f"rn::rownorm_general_kernel ({w.dtype}, {w.op})"
     mode = "persistent" if plan["persistent"] else "grid per row"
-    return (f"rn::rownorm_vec_kernel ({w.dtype}, {w.op}, W={plan['waves_per_row']} waves per row, "
-            f"V={plan['chunks_per_lane']} chunks per lane, {plan['rows_per_block']} row group(s) per workgroup, {mode})")
+    k = "rownorm_elem_kernel" if plan["variant"] == "element" else "rownorm_vec_kernel"
+    return (f"rn::{k} ({w.dtype}, {w.op}, W={plan['waves_per_row']} waves per row, "
+            f"V={plan['chunks_per_lane']} per lane, {plan['rows_per_block']} row group(s) per workgroup, {mode})")
 
 
 def launch(rn, w, s):
@@ -116,9 +137,23 @@ def launch(rn, w, s):
         rn.ln_forward(s["x"], s.get("gamma"), s.get("beta"), w.eps, out=s["y"], mean=s["mean"], rstd=s["rstd"])
     elif w.op == "rms":
         rn.rms_norm(s["x"], s.get("weight"), w.eps, out=s["y"], rstd=s["rstd"])
-    else:
+    elif w.op == "fused_add_rms":
         rn.fused_add_rms_norm(s["x"], s["residual"], s.get("weight"), w.eps, out=s["y"],
                               residual_out=s["residual_out"], rstd=s["rstd"])
+    elif w.op == "fused_add_ln":
+        rn.fused_add_layer_norm(s["x"], s["residual"], s.get("gamma"), s.get("beta"), w.eps, out=s["y"],
+                                residual_out=s["residual_out"], mean=s["mean"], rstd=s["rstd"])
+    elif w.op == "softmax":
+        rn.softmax_forward(s["x"], out=s["y"])
+    elif w.op == "ln_bwd":
+        rn.ln_backward(s["dy"], s["x"], s["mean"], s["rstd"], s.get("gamma"), dx=s["dx"], workspace=s["ws"])
+    elif w.op == "rms_bwd":
+        rn.rms_norm_backward(s["dy"], s["x"], s["rstd"], s.get("weight"), dx=s["dx"], workspace=s["ws"])
+    else:
+        raise ValueError(w.op)
+
+
+SET_TENSORS = {"ln": 2, "rms": 2, "softmax": 2, "fused_add_rms": 4, "fused_add_ln": 4, "ln_bwd": 3, "rms_bwd": 3}
 
 
 def measure(w, steps, warmup, cache, dev):
@@ -128,7 +163,7 @@ def measure(w, steps, warmup, cache, dev):
     import workloads
 
     nbytes = workloads.algorithmic_bytes(w.op, w.rows, w.N, w.elem_bytes, with_stats=True)
-    set_bytes = (4 if w.op == "fused_add_rms" else 2) * w.rows * w.N * w.elem_bytes
+    set_bytes = SET_TENSORS[w.op] * w.rows * w.N * w.elem_bytes
     nsets = 1 if cache == "hot" else max(2, min(64, math.ceil(COLD_FOOTPRINT / set_bytes)))
     log(f"[bench] {w.name}: {nsets} buffer set(s), {nbytes} algorithmic bytes per launch")
     sets = make_sets(w, nsets, dev)
@@ -155,11 +190,19 @@ def measure(w, steps, warmup, cache, dev):
     durs = [a.elapsed_time(b) for a, b in zip(starts, ends)]  # ms
     kernel_ms = sum(durs) / len(durs)
     s0 = sets[0]
-    ptrs = {k: s0[k].data_ptr() for k in ("x", "residual", "gamma", "beta", "weight", "y", "residual_out", "mean", "rstd")
-            if k in s0}
-    if "weight" in ptrs:
-        ptrs["gamma"] = ptrs.pop("weight")
-    st, info = rn.plan(w.op, w.rows, w.N, workloads.TORCH_DTYPES[w.dtype], ptrs=ptrs, eps=w.eps)
+    td = workloads.TORCH_DTYPES[w.dtype]
+    if w.op in ("ln_bwd", "rms_bwd"):
+        st, info = rn.plan_backward("ln" if w.op == "ln_bwd" else "rms", w.rows, w.N, td)
+        info["persistent"] = True
+    else:
+        ptrs = {k: s0[k].data_ptr() for k in ("x", "residual", "gamma", "beta", "weight", "y", "residual_out", "mean",
+                                              "rstd") if k in s0}
+        if "weight" in ptrs:
+            ptrs["gamma"] = ptrs.pop("weight")
+        if w.op == "softmax":
+            ptrs.pop("mean", None)
+            ptrs.pop("rstd", None)
+        st, info = rn.plan(w.op, w.rows, w.N, td, ptrs=ptrs, eps=w.eps)
     del sets
     torch.cuda.empty_cache()
     return {
@@ -234,6 +277,20 @@ def copy_calibration(dev):
     log(f"[bench] copy calibration: 10 copies of {n} bytes")
 
 
+def _more():
+    import workloads
+
+    return [
+        ("fused_add_layer_norm", workloads.FUSED_LN_8192,
+         "fused residual-add + LayerNorm, bf16 I/O, 8192 x 4096, eps 1e-5, y + residual_out + mean + rstd"),
+        ("softmax", workloads.SOFTMAX_8192, "row-wise softmax, fp32 I/O, 8192 x 4096"),
+        ("ln_backward", workloads.LN_BWD,
+         "LayerNorm backward, bf16 I/O, 4096 x 16384: dx, dgamma, dbeta from fp32 mean / rstd"),
+        ("rms_norm_backward", workloads.RMS_BWD.scaled(rows=8192, name="rms_bwd_fp16_8192x4096"),
+         "RMSNorm backward, fp16 I/O, 8192 x 4096: dx, dweight from fp32 rstd"),
+    ]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +300,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
+    ap.add_argument("--no-more", action="store_true", help="skip the fused LayerNorm, softmax and backward lines")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -257,6 +315,8 @@ def main():
 
     import workloads
 
+    global MORE
+    MORE = _more()
     dev = "cuda:0"
     if args.copy_calibration:
         copy_calibration(dev)
@@ -324,6 +384,23 @@ def main():
             "frac_kernel": round(fa / PEAK_HBM_GBS, 4), "bytes_per_launch": rf["bytes"],
             "kernel": kernel_name(f, rf["plan"]), "traffic": counter_traffic("fused_fp16_8192x4096"),
         }
+    if not args.no_more:
+        more = {}
+        extra_steps = min(args.steps, 100)
+        for key, x, what in MORE:
+            log(f"[bench] timing {x.name} ({args.cache} cache) ...")
+            rx = measure(x, extra_steps, min(args.warmup, 10), args.cache, dev)
+            xv = rx["bytes"] / (rx["ms_per_step"] * 1e-3) / 1e9
+            xa = rx["bytes"] / (rx["kernel_ms"] * 1e-3) / 1e9
+            more[key] = {
+                "workload": what, "value": round(xv, 2), "unit": "GB/s",
+                "pct_of_peak": round(100.0 * xv / PEAK_HBM_GBS, 2), "ms_per_step": round(rx["ms_per_step"], 5),
+                "steps": extra_steps, "kernel_avg_ms": round(rx["kernel_ms"], 5),
+                "achieved_kernel_GBs": round(xa, 2), "frac_kernel": round(xa / PEAK_HBM_GBS, 4),
+                "bytes_per_launch": rx["bytes"], "rows_per_s": round(x.rows / (rx["ms_per_step"] * 1e-3), 1),
+                "kernel": kernel_name(x, rx["plan"]),
+            }
+        out["more"] = more
     print(json.dumps(out), flush=True)
 
 

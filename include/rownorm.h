@@ -205,8 +205,9 @@ int fused_add_rms_norm_variant(const void* x, const void* residual, const void* 
  *                be dy or x itself.
  *   dgamma, dbeta (RMSNorm: dweight)  [N] dtype, nullable; rows == 0 writes zeros.
  *   workspace    device memory of at least rn_backward_workspace_bytes(op, rows, N) bytes,
- *                4-byte aligned, owned by the caller; required only when a parameter gradient
- *                is requested (RN_ERR_WORKSPACE otherwise). Its contents on entry do not
+ *                4-byte aligned (16-byte alignment is faster), owned by the caller;
+ *                required only when a parameter gradient is requested (RN_ERR_WORKSPACE
+ *                otherwise). Its contents on entry do not
  *                matter; on return they are unspecified. Calls that share a workspace must
  *                be ordered (same stream).
  * Rows up to 16384 elements (longer rows: RN_ERR_UNSUPPORTED). Column sums are formed in

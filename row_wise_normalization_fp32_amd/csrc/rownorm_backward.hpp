@@ -279,31 +279,47 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_bwd_elem_kernel(BwdParam
     if constexpr (LN) flush_columns<RPB>(adb, red, rg, db_out, col, okc);
 }
 
-// dgamma_j = sum over the P partial rows, in order b = 0, 1, ..., P - 1 within each of 16
-// interleaved lanes, then the 16 lane sums in order; rounded once to the I/O dtype. A
-// workgroup covers 16 columns with 16 lanes each.
+// dgamma_j = sum over the P partial rows: lane s of 16 sums rows b = s, s + 16, ... in
+// order, then the 16 lane sums are added in order; rounded once to the I/O dtype. A
+// workgroup covers 64 columns: 16 column quads x 16 lanes, so one wavefront load reads four
+// 256-byte runs of a partial row (16-byte loads when N is a multiple of 4 and the workspace
+// is 16-byte aligned; element loads otherwise).
 template <int DT>
 __global__ __launch_bounds__(256) void rownorm_bwd_cols_kernel(BwdColParams p) {
     using IO = Io<DT>;
-    __shared__ float sums[2][16][17];
-    const int q = threadIdx.x & 15;   // column within the tile
-    const int s = threadIdx.x >> 4;   // partial-row lane: rows b = s, s + 16, ...
-    const int64_t j = static_cast<int64_t>(blockIdx.x) * 16 + q;
+    typedef float f32x4 __attribute__((ext_vector_type(4)));
+    __shared__ f32x4 sums[16][17];
+    const int q = threadIdx.x & 15;  // column quad within the tile
+    const int s = threadIdx.x >> 4;  // partial-row lane
+    const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 64 + 4 * q;
+    const bool vec = (p.N & 3) == 0 && (reinterpret_cast<uintptr_t>(p.ws) & 15) == 0;
     for (int k = 0; k < 2; ++k) {
         void* out = k == 0 ? p.dgamma : p.dbeta;
         if (out == nullptr) continue;  // uniform
         const float* src = p.ws + static_cast<int64_t>(k) * p.parts * p.N;
-        float a = 0.f;
-        if (j < p.N)
-            for (int b = s; b < p.parts; b += 16) a += src[static_cast<int64_t>(b) * p.N + j];
-        sums[k][s][q] = a;
-        __syncthreads();
-        if (s == 0 && j < p.N) {
-            float r = sums[k][0][q];
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+        if (vec) {
+            if (j0 < p.N)
+                for (int b = s; b < p.parts; b += 16)
+                    a += *reinterpret_cast<const f32x4*>(src + static_cast<int64_t>(b) * p.N + j0);
+        } else {
+            for (int b = s; b < p.parts; b += 16) {
 #pragma unroll
-            for (int u = 1; u < 16; ++u) r += sums[k][u][q];
-            IO::store1(out, j, r);
+                for (int e = 0; e < 4; ++e)
+                    if (j0 + e < p.N) a[e] += src[static_cast<int64_t>(b) * p.N + j0 + e];
+            }
         }
+        sums[s][q] = a;
+        __syncthreads();
+        if (s == 0) {
+            f32x4 r = sums[0][q];
+#pragma unroll
+            for (int u = 1; u < 16; ++u) r += sums[u][q];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (j0 + e < p.N) IO::store1(out, j0 + e, r[e]);
+        }
+        __syncthreads();  // sums is rewritten for the next parameter
     }
 }
 
@@ -389,7 +405,7 @@ inline hipError_t launch_bwd_dtype(int op, const Plan& plan, const BwdParams& p0
     }
     if (cp.dgamma == nullptr && cp.dbeta == nullptr) return hipSuccess;
     void* argv[] = {&cp};
-    const unsigned blocks = static_cast<unsigned>((cp.N + 15) / 16);
+    const unsigned blocks = static_cast<unsigned>((cp.N + 63) / 64);
     return hipLaunchKernel(reinterpret_cast<const void*>(rownorm_bwd_cols_kernel<DT>), dim3(blocks), dim3(256), argv,
                            0, s);
 }
