@@ -47,7 +47,7 @@ METRIC = "achieved HBM GB/s (% of MI355X peak) + rows/s, LayerNorm & fused add+R
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published peak
 COLD_FOOTPRINT = 768 << 20  # bytes each buffer set cycle must exceed (L2 + 256 MiB MALL, with margin)
 KERNEL_SRCS = [os.path.join(ROOT, "row_wise_normalization_fp32_amd", "csrc", f)
-               for f in ("rownorm_kernels.hpp", "rownorm_capi.cpp")]  # the kernels and the launch plan
+               for f in ("rownorm_kernels.hpp", "rownorm_backward.hpp", "rownorm_capi.cpp")]  # kernels + launch plan
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.txt")
 
 
@@ -283,7 +283,8 @@ def _more():
     return [
         ("fused_add_layer_norm", workloads.FUSED_LN_8192,
          "fused residual-add + LayerNorm, bf16 I/O, 8192 x 4096, eps 1e-5, y + residual_out + mean + rstd"),
-        ("softmax", workloads.SOFTMAX_8192, "row-wise softmax, fp32 I/O, 8192 x 4096"),
+        ("softmax", workloads.SOFTMAX_8192.scaled(name="softmax_fp32_8192x4096"),
+         "row-wise softmax, fp32 I/O, 8192 x 4096"),
         ("ln_backward", workloads.LN_BWD,
          "LayerNorm backward, bf16 I/O, 4096 x 16384: dx, dgamma, dbeta from fp32 mean / rstd"),
         ("rms_norm_backward", workloads.RMS_BWD.scaled(rows=8192, name="rms_bwd_fp16_8192x4096"),
@@ -399,6 +400,8 @@ def main():
                 "achieved_kernel_GBs": round(xa, 2), "frac_kernel": round(xa / PEAK_HBM_GBS, 4),
                 "bytes_per_launch": rx["bytes"], "rows_per_s": round(x.rows / (rx["ms_per_step"] * 1e-3), 1),
                 "kernel": kernel_name(x, rx["plan"]),
+                # HBM bytes per call from the counter record (backward: row + column kernels)
+                "traffic": counter_traffic(x.name),
             }
         out["more"] = more
     print(json.dumps(out), flush=True)
