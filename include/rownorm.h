@@ -52,8 +52,9 @@
  *     by one 64-lane wavefront (rows of up to 4 KiB, or 16 KiB when forced) or by a group of
  *     up to 16 wavefronts (rows of up to 64 KiB: 16384 fp32 or 32768 fp16 / bf16 elements).
  *     Otherwise rows of up to 16384 elements are held in registers one element per slot
- *     (the element kernel, still one read of x), and longer rows take a general kernel
- *     that reads the row up to three times.
+ *     (the element kernel, still one read of x). Longer rows of whole chunks take the
+ *     split-row kernels when rn_forward_ex is given a workspace; all others take a general
+ *     kernel that reads the row up to three times.
  *   - Launches use the current HIP device (the device of the buffers and of `stream`). The
  *     first call of a kernel configuration on a device queries its occupancy once.
  */
@@ -92,8 +93,11 @@ typedef enum rn_variant {
     RN_VARIANT_WAVE = 1,      /* one 64-lane wavefront per row, row held in VGPRs (rows up to 16 KiB) */
     RN_VARIANT_WORKGROUP = 2, /* 2-16 wavefronts per row, partial moments combined in LDS (rows up to 64 KiB) */
     RN_VARIANT_GENERAL = 3,   /* any N, any element-aligned pointers; re-reads the row */
-    RN_VARIANT_ELEMENT = 4    /* rows up to 16384 elements held in VGPRs one element per slot;
+    RN_VARIANT_ELEMENT = 4,   /* rows up to 16384 elements held in VGPRs one element per slot;
                                  any element-aligned pointers and strides */
+    RN_VARIANT_WIDE = 5       /* rows longer than RN_VARIANT_WORKGROUP holds (whole 16-byte
+                                 chunks): split into 32 KiB segments, one workgroup each, in two
+                                 launches; needs a workspace (rn_forward_ex) */
 } rn_variant;
 
 /* Operation codes (for rn_forward_ex and rn_plan). */
@@ -165,17 +169,34 @@ int softmax_forward(const void* x, void* y, float* row_max, float* row_sum, int6
                     hipStream_t stream);
 
 /*
- * Any forward operation with explicit row strides and kernel variant.
- *   op       an rn_op; arguments the operation does not use are ignored (softmax: gamma,
- *            beta, residual, residual_out, eps; mean / rstd are row_max / row_sum).
- *   strides  nullable (all rows dense); see rn_row_strides.
- *   variant  an rn_variant; RN_VARIANT_AUTO chooses as the plain entry points do. A forced
- *            variant that cannot run the shape / alignment returns RN_ERR_UNSUPPORTED.
+ * Any forward operation with explicit row strides, kernel variant and workspace.
+ *   op         an rn_op; arguments the operation does not use are ignored (softmax: gamma,
+ *              beta, residual, residual_out, eps; mean / rstd are row_max / row_sum).
+ *   strides    nullable (all rows dense); see rn_row_strides.
+ *   variant    an rn_variant; RN_VARIANT_AUTO chooses as the plain entry points do, except
+ *              that rows too long for one workgroup's registers take RN_VARIANT_WIDE when a
+ *              large enough workspace is given. A forced variant that cannot run the shape /
+ *              alignment returns RN_ERR_UNSUPPORTED (RN_VARIANT_WIDE without a workspace:
+ *              RN_ERR_WORKSPACE).
+ *   workspace  nullable device memory of workspace_bytes, 16-byte aligned, owned by the
+ *              caller, overlapping no other argument: per-segment statistics of the split-row
+ *              path (rn_forward_workspace_bytes). Contents on entry do not matter; calls that
+ *              share it must be ordered (same stream).
  * Unknown op codes return RN_ERR_SHAPE.
+ *
+ * The split-row path (walkthrough section 1.1: a row that outgrows one block) reads x (for
+ * the fused ops: residual_out) a second time; the second read is served from the memory-side
+ * cache when the tensor fits in it. Without a workspace such rows take the general kernel.
  */
 int rn_forward_ex(int op, const void* x, const void* residual, const void* gamma, const void* beta, void* y,
                   void* residual_out, float* mean, float* rstd, int64_t rows, int64_t N, float eps, int dtype,
-                  const rn_row_strides* strides, int variant, hipStream_t stream);
+                  const rn_row_strides* strides, int variant, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream);
+
+/* Workspace bytes rn_forward_ex needs for the split-row path of this shape: rows *
+ * ceil(N * sizeof(dtype) / 32768) * 16 when rows are whole 16-byte chunks longer than a
+ * workgroup holds (more than 16384 fp32 or 32768 fp16 / bf16 elements), else 0. */
+size_t rn_forward_workspace_bytes(int op, int64_t rows, int64_t N, int dtype);
 
 /* Same as the first three entry points above, with the kernel variant forced (RN_VARIANT_AUTO
  * behaves exactly like the plain entry point). A forced variant that cannot run the given
@@ -226,7 +247,7 @@ int rms_norm_backward(const void* dy, const void* x, const void* weight, const f
  * overlap, never dereferenced. */
 typedef struct rn_plan_info {
     int variant;           /* rn_variant actually used */
-    int waves_per_row;     /* wavefronts cooperating on one row */
+    int waves_per_row;     /* wavefronts cooperating on one row (split-row variant: on one segment) */
     int rows_per_block;    /* rows one workgroup processes per iteration */
     int block_threads;     /* workgroup size */
     int chunks_per_lane;   /* 16-byte chunks (vectorized variants) or elements (element variant)
@@ -242,7 +263,8 @@ typedef struct rn_plan_info {
 
 int rn_plan(int op, const void* x, const void* residual, const void* gamma, const void* beta, const void* y,
             const void* residual_out, const void* mean, const void* rstd, int64_t rows, int64_t N, float eps,
-            int dtype, int variant, const rn_row_strides* strides, rn_plan_info* out);
+            int dtype, int variant, const rn_row_strides* strides, const void* workspace, size_t workspace_bytes,
+            rn_plan_info* out);
 
 /* The same for a backward call (op: RN_OP_LAYER_NORM or RN_OP_RMS_NORM); grid_blocks is the
  * row kernel's workgroup count before the launch caps it at what the device keeps resident. */

@@ -25,7 +25,7 @@ import torch
 
 __all__ = [
     "ln_forward", "rms_norm", "fused_add_rms_norm", "fused_add_layer_norm", "softmax_forward", "ln_backward",
-    "rms_norm_backward", "backward_workspace_bytes", "plan", "plan_backward",
+    "rms_norm_backward", "backward_workspace_bytes", "forward_workspace_bytes", "plan", "plan_backward",
     "RowNormError", "LIB_PATH", "VARIANTS", "STATUS", "version",
 ]
 
@@ -51,7 +51,7 @@ class PlanInfo(ctypes.Structure):
 
 
 _lib.rn_forward_ex.argtypes = [_ci, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci,
-                               ctypes.POINTER(RowStrides), _ci, _vp]
+                               ctypes.POINTER(RowStrides), _ci, _vp, ctypes.c_size_t, _vp]
 _lib.rn_forward_ex.restype = _ci
 _lib.ln_forward.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci, _vp]
 _lib.ln_forward.restype = _ci
@@ -74,7 +74,9 @@ _lib.rn_status_string.restype = ctypes.c_char_p
 _lib.rn_version.argtypes = []
 _lib.rn_version.restype = _ci
 _lib.rn_plan.argtypes = [_ci, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci, _ci,
-                         ctypes.POINTER(RowStrides), ctypes.POINTER(PlanInfo)]
+                         ctypes.POINTER(RowStrides), _vp, ctypes.c_size_t, ctypes.POINTER(PlanInfo)]
+_lib.rn_forward_workspace_bytes.argtypes = [_ci, _i64, _i64, _ci]
+_lib.rn_forward_workspace_bytes.restype = ctypes.c_size_t
 _lib.rn_plan.restype = _ci
 _lib.rn_backward_workspace_bytes.argtypes = [_ci, _i64, _i64]
 _lib.rn_backward_workspace_bytes.restype = ctypes.c_size_t
@@ -87,7 +89,7 @@ _lib.rn_plan_backward.argtypes = [_ci, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _
 _lib.rn_plan_backward.restype = _ci
 
 DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
-VARIANTS = {"auto": 0, "wave": 1, "workgroup": 2, "general": 3, "element": 4}
+VARIANTS = {"auto": 0, "wave": 1, "workgroup": 2, "general": 3, "element": 4, "wide": 5}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 OPS = {"ln": 0, "rms": 1, "fused_add_rms": 2, "fused_add_ln": 3, "softmax": 4}
 STATUS = {0: "RN_OK", 1: "RN_ERR_NULL", 2: "RN_ERR_SHAPE", 3: "RN_ERR_DTYPE", 4: "RN_ERR_ALIAS",
@@ -178,12 +180,23 @@ def _stats(name, t, x, rows, want):
     return t
 
 
-def _call(op: str, what: str, x, residual, gamma, beta, y, ro, mean, rstd, rows, N, eps, strides, variant, stream):
+def forward_workspace_bytes(op: str, rows: int, N: int, dtype: torch.dtype) -> int:
+    """Workspace bytes the split-row path needs for this shape (0 when it does not apply)."""
+    return int(_lib.rn_forward_workspace_bytes(OPS[op], rows, N, DTYPE_CODE[dtype]))
+
+
+def _call(op: str, what: str, x, residual, gamma, beta, y, ro, mean, rstd, rows, N, eps, strides, variant, stream,
+          workspace=None):
     st_obj = RowStrides(*strides)
+    need = forward_workspace_bytes(op, rows, N, x.dtype)
+    if need and workspace is None and _variant(variant) in (VARIANTS["auto"], VARIANTS["wide"]):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     with torch.cuda.device(x.device):
         st = _lib.rn_forward_ex(OPS[op], _ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(ro),
                                 _ptr(mean), _ptr(rstd), rows, N, float(eps), DTYPE_CODE[x.dtype],
-                                ctypes.byref(st_obj), _variant(variant), _stream(x, stream))
+                                ctypes.byref(st_obj), _variant(variant), _ptr(workspace), ws_bytes,
+                                _stream(x, stream))
     if st != 0:
         raise RowNormError(st, what)
 
@@ -400,11 +413,13 @@ def plan_backward(op: str, rows: int, N: int, dtype: torch.dtype, *, ptrs: Optio
 
 
 def plan(op: str, rows: int, N: int, dtype: torch.dtype, *, ptrs: Optional[dict] = None, eps: float = 1e-5,
-         variant: Union[str, int] = "auto", strides: Optional[dict] = None) -> Tuple[int, dict]:
+         variant: Union[str, int] = "auto", strides: Optional[dict] = None,
+         workspace_bytes: int = 0) -> Tuple[int, dict]:
     """Host-only launch plan (no GPU needed). ``ptrs`` maps buffer names (x, residual,
     gamma, beta, y, residual_out, mean, rstd) to integer addresses; missing required
     buffers default to 256-byte-aligned placeholders that never overlap. ``strides`` maps
-    x / residual / y / residual_out to row strides in elements. Returns ``(status, info)``."""
+    x / residual / y / residual_out to row strides in elements; ``workspace_bytes`` > 0
+    stands for a workspace of that size (the split-row path). Returns ``(status, info)``."""
     s = torch.tensor([], dtype=dtype).element_size()
     ld = max([N] + list((strides or {}).values()))
     span = max(1, rows * ld * s)
@@ -421,7 +436,9 @@ def plan(op: str, rows: int, N: int, dtype: torch.dtype, *, ptrs: Optional[dict]
     info = PlanInfo()
     st = _lib.rn_plan(OPS[op], p.get("x"), p.get("residual"), p.get("gamma"), p.get("beta"), p.get("y"),
                       p.get("residual_out"), p.get("mean"), p.get("rstd"), rows, N, float(eps),
-                      DTYPE_CODE.get(dtype, 99), _variant(variant), ctypes.byref(st_obj), ctypes.byref(info))
+                      DTYPE_CODE.get(dtype, 99), _variant(variant), ctypes.byref(st_obj),
+                      p.get("workspace", (1 << 47) if workspace_bytes else None), workspace_bytes,
+                      ctypes.byref(info))
     return st, {"variant": VARIANT_NAMES.get(info.variant, info.variant), "waves_per_row": info.waves_per_row,
                 "rows_per_block": info.rows_per_block, "block_threads": info.block_threads,
                 "chunks_per_lane": info.chunks_per_lane, "grid_blocks": info.grid_blocks,

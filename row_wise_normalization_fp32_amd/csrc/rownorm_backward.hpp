@@ -237,15 +237,23 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_bwd_elem_kernel(BwdParam
         const char* xr = static_cast<const char*>(p.x) + row * p.N * S;
         const char* dr = static_cast<const char*>(p.dy) + row * p.N * S;
         float xf[V], df[V];
+        // unconditional loads (clamped index), zeroed after: see rownorm_elem_kernel
 #pragma unroll
         for (int i = 0; i < V; ++i) {
             const unsigned j = static_cast<unsigned>(i * LANES) + t;
-            xf[i] = j < N ? IO::load1(xr, j) : 0.f;
-            df[i] = j < N ? IO::load1(dr, j) : 0.f;
+            const unsigned jc = j < N ? j : N - 1;
+            xf[i] = IO::load1(xr, jc);
+            df[i] = IO::load1(dr, jc);
         }
         const float mean = LN ? p.mean[row] : 0.f;
         const float rstd = p.rstd[row];
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            const unsigned j = static_cast<unsigned>(i * LANES) + t;
+            xf[i] = j < N ? xf[i] : 0.f;
+            df[i] = j < N ? df[i] : 0.f;
+        }
         float sg = 0.f, sgx = 0.f;
 #pragma unroll
         for (int i = 0; i < V; ++i) {

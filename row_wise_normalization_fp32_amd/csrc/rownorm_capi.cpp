@@ -62,14 +62,25 @@ struct Args {
     int dtype;
     int variant;
     int64_t ldx, ldr, ldy, ldro;  // resolved row strides (elements)
+    void* ws;                     // split-row workspace, nullable
+    size_t ws_bytes;
 };
+
+// Split-row path: rows of whole 16-byte chunks that are longer than a workgroup's registers.
+int64_t wide_segments(int64_t C) { return (C + rn::kWideSegChunks - 1) / rn::kWideSegChunks; }
+
+size_t wide_workspace_bytes(int64_t rows, int64_t N, int64_t s) {
+    const int64_t group_cap = int64_t(64) * rn::kMaxGroupWaves * rn::kMaxGroupChunks;
+    if (rows <= 0 || N <= 0 || (N * s) % 16 != 0 || N * s / 16 <= group_cap) return 0;
+    return static_cast<size_t>(rows * wide_segments(N * s / 16) * 16);
+}
 
 // Validates the arguments (dropping pointers the operation does not use) and chooses the
 // kernel. On success *C is the number of 16-byte chunks per row (vectorized variants).
 int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_t* chunks) {
     if (a.dtype != RN_F32 && a.dtype != RN_F16 && a.dtype != RN_BF16) return RN_ERR_DTYPE;
     if (a.op < RN_OP_LAYER_NORM || a.op > RN_OP_SOFTMAX) return RN_ERR_SHAPE;
-    if (a.variant < RN_VARIANT_AUTO || a.variant > RN_VARIANT_ELEMENT) return RN_ERR_UNSUPPORTED;
+    if (a.variant < RN_VARIANT_AUTO || a.variant > RN_VARIANT_WIDE) return RN_ERR_UNSUPPORTED;
     const int64_t s = a.dtype == RN_F32 ? 4 : 2;
     const int64_t rows = a.rows, N = a.N;
     if (rows < 0 || N <= 0) return RN_ERR_SHAPE;
@@ -141,6 +152,16 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
         }
     }
 
+    // The split-row workspace (only looked at when it is needed: see below).
+    const size_t ws_need = wide_workspace_bytes(rows, N, s);
+    const bool ws_given = a.ws != nullptr && ws_need > 0 && a.ws_bytes >= ws_need;
+    if (ws_given) {
+        if (reinterpret_cast<uintptr_t>(a.ws) % 16 != 0) return RN_ERR_ALIGN;
+        const Buf wsb{a.ws, static_cast<int64_t>(ws_need), 0, true, R_MEAN};
+        for (int j = 0; j < nb; ++j)
+            if (bufs[j].p && overlaps(wsb, bufs[j])) return RN_ERR_ALIAS;
+    }
+
     // Vectorized variants need whole 16-byte chunks per row, 16-byte aligned tensors and
     // row strides that are whole chunks.
     bool vec_ok = (N * s) % 16 == 0;
@@ -163,10 +184,26 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     if (v == RN_VARIANT_AUTO) {
         if (vec_ok && C <= group_cap)
             v = w_auto == 1 ? RN_VARIANT_WAVE : RN_VARIANT_WORKGROUP;
+        else if (vec_ok && ws_given)
+            v = RN_VARIANT_WIDE;
         else if (N <= elem_cap)
             v = RN_VARIANT_ELEMENT;
         else
             v = RN_VARIANT_GENERAL;
+    }
+    if (v == RN_VARIANT_WIDE) {
+        if (!vec_ok || C <= group_cap) return RN_ERR_UNSUPPORTED;
+        if (!ws_given) return RN_ERR_WORKSPACE;
+        const int64_t S = wide_segments(C);
+        plan->variant = rn::V_WIDE;
+        plan->waves_per_row = 8;  // per segment
+        plan->rows_per_block = 1;
+        plan->chunks_per_lane = 4;
+        plan->block_threads = 512;
+        plan->grid = rows * S < rn::kMaxGrid ? rows * S : rn::kMaxGrid;
+        plan->exact = C % rn::kWideSegChunks == 0;
+        *chunks = C;
+        return RN_OK;
     }
     int W = 0;
     if (v == RN_VARIANT_WAVE) {
@@ -250,6 +287,17 @@ int run(Args a, const rn_row_strides* strides, hipStream_t stream) {
     // Persistent vectorized launches have instances of their own (parameters staged on
     // chip); the element kernel is the same instance in both launch modes.
     const bool pers_vec = plan.persistent && plan.variant != rn::V_ELEMENT;
+    if (plan.variant == rn::V_WIDE) {
+        rn::WideArgs wa{a.ws, static_cast<int>(wide_segments(C))};
+        hipError_t e = hipErrorInvalidValue;
+        switch (a.dtype) {
+        case RN_F32: e = rn::launch_wide_f32(a.op, plan, p, wa, stream); break;
+        case RN_F16: e = rn::launch_wide_f16(a.op, plan, p, wa, stream); break;
+        case RN_BF16: e = rn::launch_wide_bf16(a.op, plan, p, wa, stream); break;
+        default: break;
+        }
+        return e == hipSuccess ? RN_OK : RN_ERR_HIP;
+    }
     hipError_t e = hipErrorInvalidValue;
     switch (a.dtype) {
     case RN_F32: e = pers_vec ? rn::launch_f32_persistent(a.op, plan, p, stream)
@@ -282,6 +330,8 @@ Args make_args(int op, const void* x, const void* residual, const void* gamma, c
     a.dtype = dtype;
     a.variant = variant;
     a.ldx = a.ldr = a.ldy = a.ldro = N;
+    a.ws = nullptr;
+    a.ws_bytes = 0;
     return a;
 }
 
@@ -464,9 +514,18 @@ int softmax_forward(const void* x, void* y, float* row_max, float* row_sum, int6
 
 int rn_forward_ex(int op, const void* x, const void* residual, const void* gamma, const void* beta, void* y,
                   void* residual_out, float* mean, float* rstd, int64_t rows, int64_t N, float eps, int dtype,
-                  const rn_row_strides* strides, int variant, hipStream_t stream) {
-    return run(make_args(op, x, residual, gamma, beta, y, residual_out, mean, rstd, rows, N, eps, dtype, variant),
-               strides, stream);
+                  const rn_row_strides* strides, int variant, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+    Args a = make_args(op, x, residual, gamma, beta, y, residual_out, mean, rstd, rows, N, eps, dtype, variant);
+    a.ws = workspace;
+    a.ws_bytes = workspace_bytes;
+    return run(a, strides, stream);
+}
+
+size_t rn_forward_workspace_bytes(int op, int64_t rows, int64_t N, int dtype) {
+    if (op < RN_OP_LAYER_NORM || op > RN_OP_SOFTMAX) return 0;
+    if (dtype != RN_F32 && dtype != RN_F16 && dtype != RN_BF16) return 0;
+    return wide_workspace_bytes(rows, N, dtype == RN_F32 ? 4 : 2);
 }
 
 int ln_forward_variant(const void* x, const void* gamma, const void* beta, void* y, float* mean, float* rstd,
@@ -533,10 +592,13 @@ int rn_plan_backward(int op, const void* dy, const void* x, const void* gamma, c
 
 int rn_plan(int op, const void* x, const void* residual, const void* gamma, const void* beta, const void* y,
             const void* residual_out, const void* mean, const void* rstd, int64_t rows, int64_t N, float eps,
-            int dtype, int variant, const rn_row_strides* strides, rn_plan_info* out) {
+            int dtype, int variant, const rn_row_strides* strides, const void* workspace, size_t workspace_bytes,
+            rn_plan_info* out) {
     Plan plan;
     int64_t C = 0;
     Args a = make_args(op, x, residual, gamma, beta, y, residual_out, mean, rstd, rows, N, eps, dtype, variant);
+    a.ws = const_cast<void*>(workspace);
+    a.ws_bytes = workspace_bytes;
     const int st = validate_and_plan(a, strides, &plan, &C);
     if (out) {
         out->variant = plan.variant;

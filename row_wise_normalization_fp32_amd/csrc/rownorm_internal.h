@@ -12,7 +12,7 @@ namespace rn {
 
 enum Op { OP_LN = 0, OP_RMS = 1, OP_FUSED = 2, OP_FUSED_LN = 3, OP_SOFTMAX = 4 };
 enum Dt { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
-enum Variant { V_AUTO = 0, V_WAVE = 1, V_WORKGROUP = 2, V_GENERAL = 3, V_ELEMENT = 4 };
+enum Variant { V_AUTO = 0, V_WAVE = 1, V_WORKGROUP = 2, V_GENERAL = 3, V_ELEMENT = 4, V_WIDE = 5 };
 
 // Kernel arguments, passed by value. Pointers are device pointers; nullable ones are
 // documented in include/rownorm.h.
@@ -32,6 +32,12 @@ struct Params {
     int64_t cx, cr, cy, cro;      // the same in 16-byte chunks (vectorized variants)
     float eps;
     float inv_n;  // 1 / N rounded to fp32
+};
+
+// Split-row (wide) launches: the caller's workspace of [rows][S] float4 segment records.
+struct WideArgs {
+    void* ws;
+    int S;  // segments per row
 };
 
 // Backward row kernel arguments (rownorm_backward.hpp).
@@ -83,6 +89,7 @@ constexpr int kElemTarget = 8;         // element variant: about 8 elements per 
 constexpr int kElemMaxPerLane = 16;    // ... at most 16 (with 16 waves: rows up to 16384)
 constexpr int64_t kMaxGrid = 1 << 20;  // grid cap; kernels loop over the remaining rows
 constexpr int64_t kPersistentBlocks = 2048;  // at least this many workgroups: persistent launch
+constexpr int kWideSegChunks = 2048;   // split-row variant: 16-byte chunks per segment (one workgroup)
 constexpr int kBwdMaxParts = 1024;     // backward: at most this many partial column rows (workspace bound)
 constexpr int kBwdTargetChunks = 2;    // backward: about 2 chunks of x and of dy per lane
 
@@ -93,6 +100,9 @@ hipError_t launch_bf16(int op, const Plan& plan, const Params& p, hipStream_t st
 hipError_t launch_f32_persistent(int op, const Plan& plan, const Params& p, hipStream_t stream);
 hipError_t launch_f16_persistent(int op, const Plan& plan, const Params& p, hipStream_t stream);
 hipError_t launch_bf16_persistent(int op, const Plan& plan, const Params& p, hipStream_t stream);
+hipError_t launch_wide_f32(int op, const Plan& plan, const Params& p, const WideArgs& wa, hipStream_t stream);
+hipError_t launch_wide_f16(int op, const Plan& plan, const Params& p, const WideArgs& wa, hipStream_t stream);
+hipError_t launch_wide_bf16(int op, const Plan& plan, const Params& p, const WideArgs& wa, hipStream_t stream);
 hipError_t launch_bwd_f32(int op, const Plan& plan, const BwdParams& p, const BwdColParams& cp, hipStream_t stream);
 hipError_t launch_bwd_f16(int op, const Plan& plan, const BwdParams& p, const BwdColParams& cp, hipStream_t stream);
 hipError_t launch_bwd_bf16(int op, const Plan& plan, const BwdParams& p, const BwdColParams& cp, hipStream_t stream);

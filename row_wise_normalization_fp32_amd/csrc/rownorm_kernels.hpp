@@ -180,10 +180,12 @@ struct Io<DT_BF16> {
     __device__ static __forceinline__ float load1(const void* p, int64_t i) {
         return lo(static_cast<const unsigned short*>(p)[i]);
     }
+    // Scalar conversions go through the packed hardware conversion (v_cvt_pk_bf16_f32,
+    // round to nearest even) instead of a scalar software rounding sequence.
     __device__ static __forceinline__ void store1(void* p, int64_t i, float v) {
-        static_cast<__bf16*>(p)[i] = static_cast<__bf16>(v);
+        static_cast<unsigned short*>(p)[i] = static_cast<unsigned short>(narrow2(v, v));
     }
-    __device__ static __forceinline__ float round(float v) { return static_cast<float>(static_cast<__bf16>(v)); }
+    __device__ static __forceinline__ float round(float v) { return lo(narrow2(v, v)); }
 };
 
 // ---------------------------------------------------------------------------------------
@@ -798,18 +800,25 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_elem_kernel(Params p) {
         // Row bases are wave-uniform; element offsets are 32-bit.
         const char* xr = static_cast<const char*>(p.x) + row * p.ldx * S;
         const char* rr = OT::RES ? static_cast<const char*>(p.residual) + row * p.ldr * S : nullptr;
-        float f[V];
-        // a1 (+ a2): load the row; the fused ops form, store and keep t = round(x + r)
+        float f[V], r[OT::RES ? V : 1];
+        // a1 (+ a2): load the row; the fused ops form, store and keep t = round(x + r).
+        // Every load is unconditional (idle slots read the row's last element and are
+        // zeroed after): a load under a branch would be followed by a wait for its data
+        // before the next one is issued.
 #pragma unroll
         for (int i = 0; i < V; ++i) {
             const unsigned j = static_cast<unsigned>(i * LANES) + t;
-            f[i] = 0.f;
-            if (j < N) {
-                f[i] = IO::load1(xr, j);
-                if constexpr (OT::RES) f[i] += IO::load1(rr, j);
-            }
+            const unsigned jc = j < N ? j : N - 1;
+            f[i] = IO::load1(xr, jc);
+            if constexpr (OT::RES) r[i] = IO::load1(rr, jc);
         }
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            const unsigned j = static_cast<unsigned>(i * LANES) + t;
+            if constexpr (OT::RES) f[i] += r[i];
+            f[i] = j < N ? f[i] : 0.f;
+        }
         if constexpr (OT::RES) {
             char* orow = static_cast<char*>(p.residual_out) + row * p.ldro * S;
 #pragma unroll
@@ -881,6 +890,239 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_elem_kernel(Params p) {
                 z = z + b[i];
             }
             if (j < N) IO::store1(yrow, j, z);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Split-row kernels: rows too long for one workgroup's registers (the walkthrough's
+// section 1.1 case of a row that outgrows one block), with 16-byte chunks. A row is cut into
+// S segments of kWideChunks chunks, one workgroup (kWideW waves, kWideV chunks per lane) per
+// segment, in two launches:
+//   1. rownorm_wide_stats_kernel: the segment's statistics (LayerNorm: count, a reference
+//      point R_s and the mean relative to it, M2; RMSNorm: sum of squares; softmax: max and
+//      sum of exp(x - max)) into the workspace, one float4 per segment. The fused ops also
+//      write residual_out here.
+//   2. rownorm_wide_norm_kernel: every workgroup of the row combines the S records in the
+//      same fixed order (so all get the same bits), re-reads its segment (x, or residual_out
+//      for the fused ops) and writes y.
+// x is read twice; when the tensor fits the 256 MiB memory-side cache the second read is
+// served from it.
+// ---------------------------------------------------------------------------------------
+
+constexpr int kWideW = 8;
+constexpr int kWideV = 4;
+constexpr int kWideLanes = 64 * kWideW;
+constexpr int kWideChunks = kWideLanes * kWideV;  // 2048 chunks = 32 KiB per segment
+static_assert(kWideChunks == kWideSegChunks, "segment size shared with the planner");
+
+template <int DT, int OP, bool EXACT>
+__global__ __launch_bounds__(kWideLanes) void rownorm_wide_stats_kernel(Params p, WideArgs wa) {
+    using IO = Io<DT>;
+    using OT = OpTraits<OP>;
+    constexpr int E = IO::E;
+    constexpr int V = kWideV;
+    const int lane = threadIdx.x & 63;
+    const int wr = threadIdx.x >> 6;
+    const int t = threadIdx.x;
+    __shared__ WavePart part[2][kWideW];
+    int buf = 0;
+    const int64_t total = p.rows * wa.S;
+    for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+        const int64_t row = b / wa.S;
+        const int seg = static_cast<int>(b - row * wa.S);
+        const int64_t c0 = static_cast<int64_t>(seg) * kWideChunks;
+        const int Cs = static_cast<int>(p.C - c0 < kWideChunks ? p.C - c0 : kWideChunks);  // chunks here
+        auto valid = [&](int i) { return EXACT || i * kWideLanes + t < Cs; };
+        auto chunk = [&](int i) {
+            const int c = i * kWideLanes + t;
+            return c0 + (EXACT ? c : (c < Cs ? c : Cs - 1));
+        };
+        u32x4 src[V];
+        const u32x4* xr = static_cast<const u32x4*>(p.x) + row * p.cx;
+#pragma unroll
+        for (int i = 0; i < V; ++i) src[i] = __builtin_nontemporal_load(xr + chunk(i));
+        if constexpr (OT::RES) {
+            const u32x4* rr = static_cast<const u32x4*>(p.residual) + row * p.cr;
+            u32x4 rv[V];
+#pragma unroll
+            for (int i = 0; i < V; ++i) rv[i] = __builtin_nontemporal_load(rr + chunk(i));
+            u32x4* ro = static_cast<u32x4*>(p.residual_out) + row * p.cro;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float a[E], c[E];
+                IO::unpack(src[i], a);
+                IO::unpack(rv[i], c);
+#pragma unroll
+                for (int e = 0; e < E; ++e) a[e] += c[e];
+                src[i] = IO::pack(a);
+                if (valid(i)) ro[chunk(i)] = src[i];
+            }
+        }
+        int cnt = 0;  // chunks of this wave
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            const int k = Cs - (i * kWideLanes + wr * 64);
+            cnt += k <= 0 ? 0 : (k >= 64 ? 64 : k);
+        }
+        const float n_w = static_cast<float>(cnt * E);
+        float4 rec;
+        if constexpr (OT::LN) {
+            const float K = uniform(IO::first(src[0]));
+            float s1 = 0.f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float f[E];
+                IO::unpack(src[i], f);
+#pragma unroll
+                for (int e = 0; e < E; ++e) s1 += valid(i) ? f[e] - K : 0.f;
+            }
+            const float inv_w = n_w > 0.f ? 1.0f / n_w : 0.f;
+            const float a = K + wave_sum(s1) * inv_w;
+            float c = 0.f, q = 0.f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float f[E];
+                IO::unpack(src[i], f);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float d = valid(i) ? f[e] - a : 0.f;
+                    c += d;
+                    q = fmaf(d, d, q);
+                }
+            }
+            const float Cw = wave_sum(c), Qw = wave_sum(q);
+            const float cw = Cw * inv_w;
+            float rel, m2, mean;
+            group_moments<kWideW, false>(part, buf, lane, wr, n_w, a, cw, fmaxf(Qw - Cw * cw, 0.f), rel, m2, mean);
+            // relative to wave 0's rough mean R: rel is the mean minus this wave's a, so
+            // mean - R = rel + (a - R); wave 0 (a == R) writes the record
+            rec = make_float4(static_cast<float>(Cs * E), a, rel, m2);
+        } else if constexpr (OT::SM) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float f[E];
+                IO::unpack(src[i], f);
+#pragma unroll
+                for (int e = 0; e < E; ++e) mx = valid(i) ? fmaxf(mx, f[e]) : mx;
+            }
+            const float mw = wave_max(mx);
+            float sm = 0.f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float f[E];
+                IO::unpack(src[i], f);
+#pragma unroll
+                for (int e = 0; e < E; ++e) sm += valid(i) ? exp_neg(f[e] - mw) : 0.f;
+            }
+            float M, Ssum;
+            group_softmax<kWideW>(part, buf, lane, wr, mw, wave_sum(sm), M, Ssum);
+            rec = make_float4(M, Ssum, 0.f, 0.f);
+        } else {
+            float sq = 0.f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                float f[E];
+                IO::unpack(src[i], f);
+#pragma unroll
+                for (int e = 0; e < E; ++e) sq = valid(i) ? fmaf(f[e], f[e], sq) : sq;
+            }
+            rec = make_float4(group_sum<kWideW>(part, buf, lane, wr, wave_sum(sq)), 0.f, 0.f, 0.f);
+        }
+        if (t == 0) static_cast<float4*>(wa.ws)[row * wa.S + seg] = rec;
+    }
+}
+
+template <int DT, int OP, bool EXACT, int AFF>
+__global__ __launch_bounds__(kWideLanes) void rownorm_wide_norm_kernel(Params p, WideArgs wa) {
+    using IO = Io<DT>;
+    using OT = OpTraits<OP>;
+    constexpr int E = IO::E;
+    constexpr int V = kWideV;
+    constexpr bool HG = !OT::SM && (AFF & AFF_G) != 0;
+    constexpr bool HB = OT::LN && (AFF & AFF_B) != 0;
+    const int t = threadIdx.x;
+    const int64_t total = p.rows * wa.S;
+    for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+        const int64_t row = b / wa.S;
+        const int seg = static_cast<int>(b - row * wa.S);
+        const int64_t c0 = static_cast<int64_t>(seg) * kWideChunks;
+        const int Cs = static_cast<int>(p.C - c0 < kWideChunks ? p.C - c0 : kWideChunks);
+        auto valid = [&](int i) { return EXACT || i * kWideLanes + t < Cs; };
+        auto chunk = [&](int i) {
+            const int c = i * kWideLanes + t;
+            return c0 + (EXACT ? c : (c < Cs ? c : Cs - 1));
+        };
+        // the segment's data (x, or residual_out for the fused ops) and parameters
+        const u32x4* sr = OT::RES ? static_cast<const u32x4*>(p.residual_out) + row * p.cro
+                                  : static_cast<const u32x4*>(p.x) + row * p.cx;
+        u32x4 src[V], gv[HG ? V : 1], bv[HB ? V : 1];
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            src[i] = __builtin_nontemporal_load(sr + chunk(i));
+            if constexpr (HG) gv[i] = static_cast<const u32x4*>(p.gamma)[chunk(i)];
+            if constexpr (HB) bv[i] = static_cast<const u32x4*>(p.beta)[chunk(i)];
+        }
+        // combine the row's segment records in order 0, 1, ..., S - 1 (same bits everywhere)
+        const float4* rec = static_cast<const float4*>(wa.ws) + row * wa.S;
+        float scale, offset = 0.f, R0 = 0.f;
+        if constexpr (OT::LN) {
+            const float4 r0 = rec[0];
+            R0 = r0.y;
+            Moments acc{r0.x, r0.z, r0.w};  // mean relative to R0
+            for (int k = 1; k < wa.S; ++k) {
+                const float4 r = rec[k];
+                acc = combine(acc, Moments{r.x, (r.y - R0) + r.z, r.w});
+            }
+            scale = inv_sqrt(fmaf(acc.m2, p.inv_n, p.eps));
+            offset = -acc.m * scale;
+            if (seg == 0 && t == 0) {
+                if (p.mean) p.mean[row] = R0 + acc.m;
+                if (p.rstd) p.rstd[row] = scale;
+            }
+        } else if constexpr (OT::SM) {
+            float M = rec[0].x, Ssum = rec[0].y;
+            for (int k = 1; k < wa.S; ++k) softmax_combine(M, Ssum, rec[k].x, rec[k].y);
+            R0 = M;
+            scale = 1.0f / Ssum;
+            if (seg == 0 && t == 0) {
+                if (p.mean) p.mean[row] = M;
+                if (p.rstd) p.rstd[row] = Ssum;
+            }
+        } else {
+            float sq = rec[0].x;
+            for (int k = 1; k < wa.S; ++k) sq += rec[k].x;
+            scale = inv_sqrt(fmaf(sq, p.inv_n, p.eps));
+            if (seg == 0 && t == 0 && p.rstd) p.rstd[row] = scale;
+        }
+        u32x4* yr = static_cast<u32x4*>(p.y) + row * p.cy;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            float f[E], g[E], bb[E], o[E];
+            IO::unpack(src[i], f);
+            if constexpr (HG) IO::unpack(gv[i], g);
+            if constexpr (HB) IO::unpack(bv[i], bb);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                float z;
+                if constexpr (OT::LN) {
+                    z = fmaf(f[e] - R0, scale, offset);
+                } else if constexpr (OT::SM) {
+                    z = exp_neg(f[e] - R0) * scale;
+                } else {
+                    z = f[e] * scale;
+                }
+                if constexpr (HG && HB) {
+                    z = fmaf(z, g[e], bb[e]);
+                } else if constexpr (HG) {
+                    z = z * g[e];
+                } else if constexpr (HB) {
+                    z = z + bb[e];
+                }
+                o[e] = z;
+            }
+            if (valid(i)) __builtin_nontemporal_store(IO::pack(o), yr + chunk(i));
         }
     }
 }
@@ -1180,6 +1422,50 @@ inline hipError_t launch_op(const Plan& plan, const Params& p, hipStream_t s) {
             return launch_e<DT, OP, AFF_G | AFF_B, PERS>(plan, p, s);
         }
         return hipErrorInvalidValue;
+    }
+}
+
+// Split-row launches: statistics, then normalization, on the same stream.
+template <int DT, int OP>
+inline hipError_t launch_wide_op(const Plan& plan, const Params& p, const WideArgs& wa, hipStream_t s) {
+    Params pa = p;
+    WideArgs wb = wa;
+    void* argv[] = {&pa, &wb};
+    const dim3 grid(static_cast<unsigned>(plan.grid)), block(kWideLanes);
+    hipError_t e = plan.exact
+        ? hipLaunchKernel(reinterpret_cast<const void*>(rownorm_wide_stats_kernel<DT, OP, true>), grid, block, argv, 0, s)
+        : hipLaunchKernel(reinterpret_cast<const void*>(rownorm_wide_stats_kernel<DT, OP, false>), grid, block, argv, 0, s);
+    if (e != hipSuccess) return e;
+    const int aff = (OpTraits<OP>::SM ? 0 : (p.gamma ? AFF_G : 0)) | (OpTraits<OP>::LN && p.beta ? AFF_B : 0);
+#define RN_WN(A)                                                                                                      \
+    (plan.exact ? hipLaunchKernel(reinterpret_cast<const void*>(rownorm_wide_norm_kernel<DT, OP, true, A>), grid, block, \
+                                  argv, 0, s)                                                                         \
+                : hipLaunchKernel(reinterpret_cast<const void*>(rownorm_wide_norm_kernel<DT, OP, false, A>), grid, block, \
+                                  argv, 0, s))
+    if constexpr (OpTraits<OP>::SM) {
+        return RN_WN(0);
+    } else {
+        if (aff == 0) return RN_WN(0);
+        if (aff == AFF_G) return RN_WN(AFF_G);
+        if constexpr (OpTraits<OP>::LN) {
+            if (aff == AFF_B) return RN_WN(AFF_B);
+            return RN_WN(AFF_G | AFF_B);
+        }
+        return hipErrorInvalidValue;
+    }
+#undef RN_WN
+}
+
+template <int DT>
+inline hipError_t launch_wide(int op, const Plan& plan, const Params& p, const WideArgs& wa, hipStream_t s) {
+    if (plan.variant != V_WIDE || wa.ws == nullptr || wa.S < 1) return hipErrorInvalidValue;
+    switch (op) {
+    case OP_LN: return launch_wide_op<DT, OP_LN>(plan, p, wa, s);
+    case OP_RMS: return launch_wide_op<DT, OP_RMS>(plan, p, wa, s);
+    case OP_FUSED: return launch_wide_op<DT, OP_FUSED>(plan, p, wa, s);
+    case OP_FUSED_LN: return launch_wide_op<DT, OP_FUSED_LN>(plan, p, wa, s);
+    case OP_SOFTMAX: return launch_wide_op<DT, OP_SOFTMAX>(plan, p, wa, s);
+    default: return hipErrorInvalidValue;
     }
 }
 

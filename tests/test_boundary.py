@@ -32,7 +32,7 @@ def test_library_exports_every_declared_function():
     lib = ctypes.CDLL(rn.LIB_PATH)
     names = _declared_functions()
     for n in ("ln_forward", "rms_norm", "fused_add_rms_norm", "fused_add_layer_norm", "softmax_forward",
-              "rn_forward_ex", "ln_backward", "rms_norm_backward", "rn_backward_workspace_bytes",
+              "rn_forward_ex", "rn_forward_workspace_bytes", "ln_backward", "rms_norm_backward", "rn_backward_workspace_bytes",
               "rn_plan_backward", "rn_plan", "rn_status_string"):
         assert n in names
     for n in names:
@@ -62,6 +62,7 @@ def test_status_strings_and_version():
     ("rms", torch.float32, 3, 1, "element", 1, 1, False),
     ("rms", torch.bfloat16, 8, 16383, "element", 16, 16, False),
     ("ln", torch.bfloat16, 8, 16385, "general", 0, 0, False),          # odd and beyond the element kernel
+    ("ln", torch.float32, 8, 65536, "general", 0, 0, False),           # long rows without a workspace
     ("fused_add_ln", torch.bfloat16, 8192, 4096, "workgroup", 2, 4, True),
     ("fused_add_ln", torch.float32, 256, 4096, "workgroup", 4, 4, False),
     ("softmax", torch.float32, 128, 4096, "workgroup", 4, 4, False),
@@ -220,7 +221,7 @@ def test_entry_points_reject_before_launch():
     assert lib.fused_add_layer_norm(0x1000, 0x200000, None, None, 0x300000, None, None, None, 4, 64, 1e-5, 2,
                                     None) == NULL
     assert lib.rn_forward_ex(9, 0x1000, None, None, None, 0x100000, None, None, None, 4, 64, 1e-5, 0, None, 0,
-                             None) == SHAPE
+                             None, 0, None) == SHAPE
 
 
 def test_python_binding_rejects_cpu_tensors():
@@ -272,3 +273,25 @@ def test_backward_entry_points_reject_before_launch():
                            None) == 8
     assert lib.rms_norm_backward(0x1000, 0x2000, None, 0x4000, 0x1000 + 64, None, 4, 64, 0, None, 0, None) == ALIAS
     assert lib.rms_norm_backward(0x1000, 0x200000, None, 0x400000, None, None, 4, 65536, 0, None, 0, None) == UNSUP
+
+
+def test_plan_split_rows():
+    f32, bf16 = torch.float32, torch.bfloat16
+    need = rn.forward_workspace_bytes("ln", 64, 65536, f32)
+    assert need == 64 * 8 * 16  # 16384 chunks = 8 segments of 2048, one float4 each
+    assert rn.forward_workspace_bytes("ln", 64, 16384, f32) == 0  # fits one workgroup
+    assert rn.forward_workspace_bytes("ln", 64, 32768, bf16) == 0
+    assert rn.forward_workspace_bytes("ln", 64, 32776, bf16) == 64 * 3 * 16
+    assert rn.forward_workspace_bytes("ln", 64, 65537, bf16) == 0  # not whole chunks
+    st, info = rn.plan("ln", 64, 65536, f32, workspace_bytes=need)
+    assert st == OK and info["variant"] == "wide" and info["grid_blocks"] == 64 * 8 and info["exact"]
+    st, info = rn.plan("softmax", 8, 32776, bf16, workspace_bytes=8 * 3 * 16)
+    assert st == OK and info["variant"] == "wide" and not info["exact"]
+    # too small a workspace: the general kernel (auto) or an error (forced)
+    assert rn.plan("ln", 64, 65536, f32, workspace_bytes=need - 16)[1]["variant"] == "general"
+    assert rn.plan("ln", 64, 65536, f32, variant="wide")[0] == WORKSPACE
+    assert rn.plan("ln", 64, 4096, f32, variant="wide", workspace_bytes=1 << 20)[0] == UNSUP
+    assert rn.plan("ln", 64, 65537, f32, variant="wide", workspace_bytes=1 << 20)[0] == UNSUP
+    # workspace alignment and overlap
+    assert rn.plan("ln", 64, 65536, f32, workspace_bytes=need, ptrs={"workspace": (1 << 47) + 4})[0] == ALIGN
+    assert rn.plan("ln", 64, 65536, f32, workspace_bytes=need, ptrs={"workspace": 1 << 40})[0] == ALIAS

@@ -145,6 +145,48 @@ def test_workgroup_path_32k_bf16_rows():
     check_case(workloads.C5.scaled(rows=5, N=32768, seed=601))
 
 
+WIDE_SHAPES = {"fp32": [(3, 16388), (4, 24576), (3, 65536)], "bf16": [(3, 32776), (2, 65536), (2, 131080)],
+               "fp16": [(3, 40960)]}
+
+
+@pytest.mark.parametrize("op", ["ln", "rms", "fused_add_rms", "fused_add_ln", "softmax"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
+def test_split_rows(op, dtype):
+    # rows longer than a workgroup's registers: statistics per 32 KiB segment, then a
+    # fixed-order combine in every segment's workgroup (the binding passes a workspace)
+    for rows, N in WIDE_SHAPES[dtype]:
+        st, info = rn.plan(op, rows, N, TD[dtype], workspace_bytes=rn.forward_workspace_bytes(op, rows, N, TD[dtype]))
+        assert st == 0 and info["variant"] == "wide", info
+        check_case(BASES[op].scaled(rows=rows, N=N, seed=620 + N, dtype=dtype))
+
+
+def test_split_rows_offset_constant_and_in_place():
+    # cancellation stress and constant rows on the split-row path
+    check_case(workloads.C2.scaled(rows=4, N=65536, seed=630))
+    w = workloads.C2.scaled(rows=3, N=65536, seed=631, x_dist="constant")
+    g = _gpu(workloads.make_inputs(w))
+    y = rn.ln_forward(g["x"], g["gamma"], g["beta"], w.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(y, g["beta"].expand_as(y))
+    # in place: y over x; fused: residual_out over residual and y over x
+    w = workloads.C5.scaled(rows=3, N=65536, seed=632)
+    inp = workloads.make_inputs(w)
+    ref = run_oracle(w, inp)
+    x = inp["x"].to(DEV)
+    rn.ln_forward(x, inp["gamma"].to(DEV), inp["beta"].to(DEV), w.eps, out=x)
+    torch.cuda.synchronize()
+    check_y(x, ref["y"])
+    w = workloads.FUSED_LN.scaled(rows=3, N=65536, seed=633)
+    inp = workloads.make_inputs(w)
+    ref = run_oracle(w, inp)
+    g = _gpu(inp)
+    rn.fused_add_layer_norm(g["x"], g["residual"], g["gamma"], g["beta"], w.eps, out=g["x"],
+                            residual_out=g["residual"])
+    torch.cuda.synchronize()
+    check_y(g["x"], ref["y"])
+    check_bits_equal(g["residual"], ref["residual_out"], "split-row residual_out in place")
+
+
 def test_offset_rows_on_every_variant():
     # The cancellation stress (row offsets up to +-1000) on each kernel.
     for variant in ("wave", "workgroup", "general"):
