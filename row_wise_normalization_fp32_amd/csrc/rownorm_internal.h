@@ -91,7 +91,7 @@ constexpr int64_t kMaxGrid = 1 << 20;  // grid cap; kernels loop over the remain
 constexpr int64_t kPersistentBlocks = 2048;  // at least this many workgroups: persistent launch
 constexpr int kWideSegChunks = 2048;   // split-row variant: 16-byte chunks per segment (one workgroup)
 constexpr int kBwdMaxParts = 1024;     // backward: at most this many partial column rows (workspace bound)
-constexpr int kBwdTargetChunks = 2;    // backward: about 2 chunks of x and of dy per lane
+constexpr int kBwdTargetChunks = 2;    // backward: about 2 chunks of x and of dy per lane (1 measured slower)
 
 // Enqueue the planned kernel for one I/O dtype (one translation unit per dtype and mode).
 hipError_t launch_f32(int op, const Plan& plan, const Params& p, hipStream_t stream);

@@ -938,10 +938,12 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_stats_kernel(Params p
             const int c = i * kWideLanes + t;
             return c0 + (EXACT ? c : (c < Cs ? c : Cs - 1));
         };
+        // Ordinary (temporal) loads and stores here: the second launch reads the same bytes
+        // again, from the memory-side cache when they are still there.
         u32x4 src[V];
         const u32x4* xr = static_cast<const u32x4*>(p.x) + row * p.cx;
 #pragma unroll
-        for (int i = 0; i < V; ++i) src[i] = __builtin_nontemporal_load(xr + chunk(i));
+        for (int i = 0; i < V; ++i) src[i] = xr[chunk(i)];
         if constexpr (OT::RES) {
             const u32x4* rr = static_cast<const u32x4*>(p.residual) + row * p.cr;
             u32x4 rv[V];
