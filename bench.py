@@ -7,7 +7,11 @@ The same measurement is also taken for fused residual-add + RMSNorm at 8192 x 40
 (32M elements) and reported in the same JSON line under "fused_add_rms_norm", and, under
 "more", for fused residual-add + LayerNorm (8192 x 4096 bf16), softmax (8192 x 4096 fp32),
 the LayerNorm backward (4096 x 16384 bf16: dx, dgamma, dbeta) and the RMSNorm backward
-(8192 x 4096 fp16: dx, dweight).
+(8192 x 4096 fp16: dx, dweight); under "scale_up_sweep", fused add + RMSNorm at
+N = 4096 over 2048 / 8192 / 32768 rows (fp16 and bf16), LayerNorm bf16 2048 x 4096, and the
+headline workload with a hot cache. Small launches (tens of microseconds) are shorter than
+the Python binding's per-call host time, so the sweep also replays its launches from a HIP
+graph ("graph_ms": device time per launch without host gaps).
 
 Cold cache: inputs and outputs rotate through enough buffer sets that each launch touches
 memory the previous launches have pushed out of L2 (8 x 4 MiB) and the 256 MiB
@@ -156,7 +160,33 @@ def launch(rn, w, s):
 SET_TENSORS = {"ln": 2, "rms": 2, "softmax": 2, "fused_add_rms": 4, "fused_add_ln": 4, "ln_bwd": 3, "rms_bwd": 3}
 
 
-def measure(w, steps, warmup, cache, dev):
+def graph_time(rn, w, sets, steps):
+    """Per-launch device time with the host taken out: `steps` launches (rotating over the
+    buffer sets) captured into one HIP graph, replayed once to warm up, then one timed
+    replay between two events. None if the capture fails."""
+    import torch
+
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                launch(rn, w, sets[i % len(sets)])
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        del g
+        return ms
+    except Exception as e:  # capture not possible here: report without it
+        log(f"[bench] graph timing unavailable: {e}")
+        return None
+
+
+def measure(w, steps, warmup, cache, dev, graph=False):
     import torch
 
     import row_wise_normalization_fp32_amd as rn
@@ -189,6 +219,7 @@ def measure(w, steps, warmup, cache, dev):
     torch.cuda.synchronize()
     durs = [a.elapsed_time(b) for a, b in zip(starts, ends)]  # ms
     kernel_ms = sum(durs) / len(durs)
+    graph_ms = graph_time(rn, w, sets, steps) if graph else None
     s0 = sets[0]
     td = workloads.TORCH_DTYPES[w.dtype]
     if w.op in ("ln_bwd", "rms_bwd"):
@@ -206,7 +237,7 @@ def measure(w, steps, warmup, cache, dev):
     del sets
     torch.cuda.empty_cache()
     return {
-        "bytes": nbytes, "ms_per_step": ms_per_step, "kernel_ms": kernel_ms,
+        "bytes": nbytes, "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, "graph_ms": graph_ms,
         "kernel_ms_median": sorted(durs)[len(durs) // 2], "nsets": nsets, "plan": info,
     }
 
@@ -302,6 +333,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--no-more", action="store_true", help="skip the fused LayerNorm, softmax and backward lines")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the scale-up sweep and the hot-cache line")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -404,6 +436,28 @@ def main():
                 "traffic": counter_traffic(x.name),
             }
         out["more"] = more
+    if not args.no_sweep:
+        # The scale-up sweep of the 8M-element target clause (fused add + RMSNorm at N = 4096,
+        # fp16 and bf16, 2048 / 8192 / 32768 rows; LayerNorm bf16 2048 x 4096), cold cache,
+        # and the headline workload hot (one buffer set, re-launched back to back).
+        sweep = {}
+        cases = [(workloads.C4_FP16.scaled(rows=r, name=f"fused_fp16_{r}x4096"), "cold") for r in (2048, 8192, 32768)]
+        cases += [(workloads.C4_BF16.scaled(rows=r, name=f"fused_bf16_{r}x4096"), "cold") for r in (2048, 8192, 32768)]
+        cases += [(workloads.C5.scaled(rows=2048, N=4096, name="ln_bf16_2048x4096"), "cold"),
+                  (workloads.C5.scaled(name="ln_bf16_4096x16384_hot"), "hot")]
+        for x, cache in cases:
+            log(f"[bench] sweep {x.name} ({cache}) ...")
+            rx = measure(x, min(args.steps, 100), min(args.warmup, 10), cache, dev, graph=True)
+            xa = rx["bytes"] / (rx["kernel_ms"] * 1e-3) / 1e9
+            xv = rx["bytes"] / (rx["ms_per_step"] * 1e-3) / 1e9
+            gm = rx["graph_ms"]
+            sweep[x.name] = {"elements": x.rows * x.N, "cache": cache, "kernel_avg_ms": round(rx["kernel_ms"], 5),
+                             "frac_kernel": round(xa / PEAK_HBM_GBS, 4), "value": round(xv, 2),
+                             "pct_of_peak": round(100.0 * xv / PEAK_HBM_GBS, 2),
+                             # device time per launch from a replayed HIP graph (no host gaps)
+                             "graph_ms": None if gm is None else round(gm, 5),
+                             "frac_graph": None if gm is None else round(rx["bytes"] / (gm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        out["scale_up_sweep"] = sweep
     print(json.dumps(out), flush=True)
 
 
