@@ -25,6 +25,10 @@
 // count only).
 #pragma once
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "rownorm_kernels.hpp"
 
 namespace rn {
@@ -378,6 +382,42 @@ inline BwdKernel select_bwd(const Plan& plan, bool hg) {
     return nullptr;
 }
 
+// Resident workgroups per CU of a backward row-kernel instance and the CU count, queried
+// once per (instance, LDS size, device) and cached (the host may call from several threads).
+inline hipError_t bwd_resident(BwdKernel k, int dev, const Plan& plan, int* per_cu, int* cus) {
+    struct Key {
+        BwdKernel k;
+        int dev, lds;
+        bool operator<(const Key& o) const {
+            if (k != o.k) return reinterpret_cast<uintptr_t>(k) < reinterpret_cast<uintptr_t>(o.k);
+            if (dev != o.dev) return dev < o.dev;
+            return lds < o.lds;
+        }
+    };
+    static std::mutex mu;
+    static std::map<Key, std::pair<int, int>> cache;
+    const Key key{k, dev, plan.lds_bytes};
+    {
+        std::lock_guard<std::mutex> g(mu);
+        auto it = cache.find(key);
+        if (it != cache.end()) {
+            *per_cu = it->second.first;
+            *cus = it->second.second;
+            return hipSuccess;
+        }
+    }
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(per_cu, reinterpret_cast<const void*>(k),
+                                                                plan.block_threads,
+                                                                static_cast<size_t>(plan.lds_bytes));
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (*per_cu < 1) *per_cu = 1;
+    std::lock_guard<std::mutex> g(mu);
+    cache[key] = {*per_cu, *cus};
+    return hipSuccess;
+}
+
 // Row kernel, then column kernel. The row kernel's grid P is what the device keeps resident
 // (compute units x workgroups per unit for this instance, queried once per instance and
 // device), capped by the plan: more workgroups would only add partial rows to sum.
@@ -394,12 +434,9 @@ inline hipError_t launch_bwd_dtype(int op, const Plan& plan, const BwdParams& p0
         hipError_t e = hipGetDevice(&dev);
         if (e != hipSuccess) return e;
         int per_cu = 0, cus = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k),
-                                                         plan.block_threads, static_cast<size_t>(plan.lds_bytes));
+        e = bwd_resident(k, dev, plan, &per_cu, &cus);
         if (e != hipSuccess) return e;
-        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
-        int64_t parts = static_cast<int64_t>(cus) * (per_cu < 1 ? 1 : per_cu);
+        int64_t parts = static_cast<int64_t>(cus) * per_cu;
         if (parts > plan.grid) parts = plan.grid;
         p.parts = static_cast<int>(parts);
         cp.parts = p.parts;
