@@ -9,7 +9,8 @@ The same measurement is also taken for fused residual-add + RMSNorm at 8192 x 40
 the LayerNorm backward (4096 x 16384 bf16: dx, dgamma, dbeta) and the RMSNorm backward
 (8192 x 4096 fp16: dx, dweight); under "scale_up_sweep", fused add + RMSNorm at
 N = 4096 over 2048 / 8192 / 32768 rows (fp16 and bf16), LayerNorm bf16 2048 x 4096, and the
-headline workload with a hot cache. Small launches (tens of microseconds) are shorter than
+headline workload with a hot cache; under "configs", every listed configuration (cold and
+hot, events and graph replay, next to the oracle's host throughput). Small launches (tens of microseconds) are shorter than
 the Python binding's per-call host time, so the sweep also replays its launches from a HIP
 graph ("graph_ms": device time per launch without host gaps).
 
@@ -243,6 +244,7 @@ def measure(w, steps, warmup, cache, dev, graph=False):
 
 
 def cpu_baseline(w, seconds):
+    """The oracle on `w` over about `seconds` of host time (median pass)."""
     import oracle
     import workloads
 
@@ -334,6 +336,7 @@ def main():
     ap.add_argument("--no-fused", action="store_true")
     ap.add_argument("--no-more", action="store_true", help="skip the fused LayerNorm, softmax and backward lines")
     ap.add_argument("--no-sweep", action="store_true", help="skip the scale-up sweep and the hot-cache line")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration throughput block")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
 
@@ -436,6 +439,31 @@ def main():
                 "traffic": counter_traffic(x.name),
             }
         out["more"] = more
+    if not args.no_configs:
+        # Every configuration the target lists (C1-C5, C4 in fp16 and bf16): rows/s and
+        # GB/s with % of peak, cold (rotating buffers) and hot (one buffer set), from HIP
+        # events per launch and from a replayed HIP graph (device time without host gaps),
+        # next to the oracle on the host cores (a baseline, not the target).
+        confs = {}
+        for c in workloads.CONFIGS:
+            entry = {"rows": c.rows, "N": c.N, "dtype": c.dtype, "op": c.op}
+            for cache in ("cold", "hot"):
+                rc = measure(c, min(args.steps, 100), min(args.warmup, 10), cache, dev, graph=True)
+                gm = rc["graph_ms"]
+                entry[cache] = {
+                    "kernel_avg_ms": round(rc["kernel_ms"], 5),
+                    "graph_ms": None if gm is None else round(gm, 5),
+                    "GBs_graph": None if gm is None else round(rc["bytes"] / (gm * 1e-3) / 1e9, 2),
+                    "pct_of_peak_graph": None if gm is None else round(100 * rc["bytes"] / (gm * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+                    "rows_per_s_graph": None if gm is None else round(c.rows / (gm * 1e-3), 1),
+                    "GBs_events": round(rc["bytes"] / (rc["kernel_ms"] * 1e-3) / 1e9, 2),
+                }
+            entry["bytes_per_call"] = rc["bytes"]
+            if not args.no_cpu_baseline:
+                cb = cpu_baseline(c, min(args.cpu_seconds, 1.0))
+                entry["cpu_oracle"] = {"rows_per_s": cb["rows_per_s"], "GBs": cb["value"], "cores": cb["cores"]}
+            confs[c.name] = entry
+        out["configs"] = confs
     if not args.no_sweep:
         # The scale-up sweep of the 8M-element target clause (fused add + RMSNorm at N = 4096,
         # fp16 and bf16, 2048 / 8192 / 32768 rows; LayerNorm bf16 2048 x 4096), cold cache,
