@@ -311,9 +311,20 @@ __global__ __launch_bounds__(256) void rownorm_bwd_cols_kernel(BwdColParams p) {
         const float* src = p.ws + static_cast<int64_t>(k) * p.parts * p.N;
         f32x4 a = {0.f, 0.f, 0.f, 0.f};
         if (vec) {
-            if (j0 < p.N)
-                for (int b = s; b < p.parts; b += 16)
-                    a += *reinterpret_cast<const f32x4*>(src + static_cast<int64_t>(b) * p.N + j0);
+            if (j0 < p.N) {
+                // batches of 8 loads in flight, then added in order b = s, s + 16, ...
+                constexpr int B = 8;
+                int b = s;
+                for (; b + 16 * (B - 1) < p.parts; b += 16 * B) {
+                    f32x4 v[B];
+#pragma unroll
+                    for (int u = 0; u < B; ++u)
+                        v[u] = *reinterpret_cast<const f32x4*>(src + static_cast<int64_t>(b + 16 * u) * p.N + j0);
+#pragma unroll
+                    for (int u = 0; u < B; ++u) a += v[u];
+                }
+                for (; b < p.parts; b += 16) a += *reinterpret_cast<const f32x4*>(src + static_cast<int64_t>(b) * p.N + j0);
+            }
         } else {
             for (int b = s; b < p.parts; b += 16) {
 #pragma unroll
