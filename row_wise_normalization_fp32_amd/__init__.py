@@ -166,9 +166,15 @@ def _prep(x: torch.Tensor):
     return rows, N, ld
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(x: torch.Tensor, stream) -> int:
-    s = torch.cuda.current_stream(x.device) if stream is None else stream
-    return s.cuda_stream
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:  # the current stream's handle without building a Stream object
+        return _raw_stream(x.get_device())
+    return torch.cuda.current_stream(x.device).cuda_stream
 
 
 def _stats(name, t, x, rows, want):
@@ -185,18 +191,30 @@ def forward_workspace_bytes(op: str, rows: int, N: int, dtype: torch.dtype) -> i
     return int(_lib.rn_forward_workspace_bytes(OPS[op], rows, N, DTYPE_CODE[dtype]))
 
 
+_ELEM_BYTES = {torch.float32: 4, torch.float16: 2, torch.bfloat16: 2}
+_NO_STRIDES = RowStrides(0, 0, 0, 0)
+
+
 def _call(op: str, what: str, x, residual, gamma, beta, y, ro, mean, rstd, rows, N, eps, strides, variant, stream,
           workspace=None):
-    st_obj = RowStrides(*strides)
-    need = forward_workspace_bytes(op, rows, N, x.dtype)
-    if need and workspace is None and _variant(variant) in (VARIANTS["auto"], VARIANTS["wide"]):
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    with torch.cuda.device(x.device):
-        st = _lib.rn_forward_ex(OPS[op], _ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(ro),
-                                _ptr(mean), _ptr(rstd), rows, N, float(eps), DTYPE_CODE[x.dtype],
-                                ctypes.byref(st_obj), _variant(variant), _ptr(workspace), ws_bytes,
-                                _stream(x, stream))
+    # Host time per call matters for small launches: the common case (dense rows, current
+    # device, no workspace) takes no context manager and builds no ctypes structure.
+    st_obj = _NO_STRIDES if not any(strides) else RowStrides(*strides)
+    v = _variant(variant)
+    ws_bytes = 0
+    if N * _ELEM_BYTES[x.dtype] > 65536:  # only rows beyond a workgroup's registers use a workspace
+        need = forward_workspace_bytes(op, rows, N, x.dtype)
+        if need and workspace is None and v in (VARIANTS["auto"], VARIANTS["wide"]):
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace is not None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    args = (OPS[op], _ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(ro), _ptr(mean), _ptr(rstd),
+            rows, N, float(eps), DTYPE_CODE[x.dtype], ctypes.byref(st_obj), v, _ptr(workspace), ws_bytes)
+    if x.get_device() == torch.cuda.current_device():
+        st = _lib.rn_forward_ex(*args, _stream(x, stream))
+    else:
+        with torch.cuda.device(x.device):
+            st = _lib.rn_forward_ex(*args, _stream(x, stream))
     if st != 0:
         raise RowNormError(st, what)
 
