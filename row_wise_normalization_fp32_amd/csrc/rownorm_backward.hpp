@@ -207,7 +207,7 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_bwd_elem_kernel(BwdParam
     constexpr int S = DT == DT_F32 ? 4 : 2;
     constexpr bool LN = OP == OP_LN;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: row bases stay in SGPRs
     const int rg = wave / W;
     const int wr = wave - rg * W;
     const unsigned t = static_cast<unsigned>(wr * 64 + lane);
@@ -215,11 +215,16 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_bwd_elem_kernel(BwdParam
     __shared__ WavePart part_all[RPB][2][W > 1 ? W : 1];
     extern __shared__ float red[];
     WavePart(*part)[W > 1 ? W : 1] = part_all[rg];
+    const uint32_t row_bytes = N * S;  // N <= 64 * W * V: 32-bit offsets
+    // gamma lives in VGPRs across rows unless that would push the widest instance (16
+    // slots per lane, 1024 threads, 128 VGPRs) into spills; then it is re-read per row
+    // (an L1/L2 hit: every row reads the same N values).
+    constexpr bool GREG = HG && V < 16;
+    const Rsrc gr = make_rsrc(p.gamma, HG ? row_bytes : 0);
     float gv[HG ? V : 1];
+    if constexpr (GREG) {
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-        const unsigned j = static_cast<unsigned>(i * LANES) + t;
-        if constexpr (HG) gv[i] = IO::load1(p.gamma, j < N ? j : N - 1);
+        for (int i = 0; i < V; ++i) gv[i] = IO::bload(gr, static_cast<unsigned>(i * LANES) + t);
     }
     float adg[V], adb[LN ? V : 1];
 #pragma unroll
@@ -238,48 +243,40 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_bwd_elem_kernel(BwdParam
             }
             continue;
         }
-        const char* xr = static_cast<const char*>(p.x) + row * p.N * S;
-        const char* dr = static_cast<const char*>(p.dy) + row * p.N * S;
+        // buffer resources bounded by the row: slots beyond N read 0 (so they add nothing
+        // to the sums or the column partials) and their dx stores are dropped
+        const Rsrc xr = make_rsrc(static_cast<const char*>(p.x) + row * p.N * S, row_bytes);
+        const Rsrc dr = make_rsrc(static_cast<const char*>(p.dy) + row * p.N * S, row_bytes);
         float xf[V], df[V];
-        // unconditional loads (clamped index), zeroed after: see rownorm_elem_kernel
 #pragma unroll
         for (int i = 0; i < V; ++i) {
             const unsigned j = static_cast<unsigned>(i * LANES) + t;
-            const unsigned jc = j < N ? j : N - 1;
-            xf[i] = IO::load1(xr, jc);
-            df[i] = IO::load1(dr, jc);
+            xf[i] = IO::bload(xr, j);
+            df[i] = IO::bload(dr, j);
+            if constexpr (HG && !GREG) gv[i] = IO::bload(gr, j);
         }
         const float mean = LN ? p.mean[row] : 0.f;
         const float rstd = p.rstd[row];
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-            const unsigned j = static_cast<unsigned>(i * LANES) + t;
-            xf[i] = j < N ? xf[i] : 0.f;
-            df[i] = j < N ? df[i] : 0.f;
-        }
         float sg = 0.f, sgx = 0.f;
 #pragma unroll
         for (int i = 0; i < V; ++i) {
             xf[i] = LN ? (xf[i] - mean) * rstd : xf[i] * rstd;  // xhat (0 where df is 0)
-            const float g = HG ? df[i] * gv[i] : df[i];
-            sg += g;
-            sgx = fmaf(g, xf[i], sgx);
             adg[i] = fmaf(df[i], xf[i], adg[i]);
             if constexpr (LN) adb[i] += df[i];
+            if constexpr (HG) df[i] *= gv[i];  // from here on df holds g = dy * gamma
+            sg += df[i];
+            sgx = fmaf(df[i], xf[i], sgx);
         }
         float Sg = wave_sum(sg), Sgx = wave_sum(sgx);
         group_sum2<W>(part, buf, lane, wr, Sg, Sgx);
         const float c1 = LN ? Sg * p.inv_n : 0.f;
         const float c2 = Sgx * p.inv_n;
         if (p.dx) {
-            char* o = static_cast<char*>(p.dx) + row * p.N * S;
+            const Rsrc o = make_rsrc(static_cast<char*>(p.dx) + row * p.N * S, row_bytes);
 #pragma unroll
-            for (int i = 0; i < V; ++i) {
-                const unsigned j = static_cast<unsigned>(i * LANES) + t;
-                const float g = HG ? df[i] * gv[i] : df[i];
-                if (j < N) IO::store1(o, j, rstd * ((g - c1) - xf[i] * c2));
-            }
+            for (int i = 0; i < V; ++i)
+                IO::bstore(o, static_cast<unsigned>(i * LANES) + t, rstd * ((df[i] - c1) - xf[i] * c2));
         }
     }
     if (p.ws == nullptr) return;
@@ -326,10 +323,28 @@ __global__ __launch_bounds__(256) void rownorm_bwd_cols_kernel(BwdColParams p) {
                 for (; b < p.parts; b += 16) a += *reinterpret_cast<const f32x4*>(src + static_cast<int64_t>(b) * p.N + j0);
             }
         } else {
-            for (int b = s; b < p.parts; b += 16) {
+            // element loads at clamped columns (values of columns past N are never
+            // stored), in the same batches and order as above
+            int64_t jc[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (j0 + e < p.N) a[e] += src[static_cast<int64_t>(b) * p.N + j0 + e];
+            for (int e = 0; e < 4; ++e) jc[e] = j0 + e < p.N ? j0 + e : p.N - 1;
+            constexpr int B = 8;
+            int b = s;
+            for (; b + 16 * (B - 1) < p.parts; b += 16 * B) {
+                f32x4 v[B];
+#pragma unroll
+                for (int u = 0; u < B; ++u) {
+                    const float* r = src + static_cast<int64_t>(b + 16 * u) * p.N;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[u][e] = r[jc[e]];
+                }
+#pragma unroll
+                for (int u = 0; u < B; ++u) a += v[u];
+            }
+            for (; b < p.parts; b += 16) {
+                const float* r = src + static_cast<int64_t>(b) * p.N;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[e] += r[jc[e]];
             }
         }
         sums[s][q] = a;

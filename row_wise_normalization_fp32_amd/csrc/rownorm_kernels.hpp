@@ -68,6 +68,18 @@ __device__ __forceinline__ To bit_cast(From v) {
     return __builtin_bit_cast(To, v);
 }
 
+// Buffer resources for element-granular rows: a descriptor in SGPRs (base, byte size) and
+// 32-bit byte offsets in VGPRs. Loads beyond the size return 0 and stores beyond it are
+// dropped by the hardware (raw buffer addressing), so a row needs neither clamped indices
+// nor branches around its accesses, and no 64-bit address per element.
+using Rsrc = __amdgpu_buffer_rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // 32-bit data format, no swizzle (untyped accesses)
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                             kRsrcWord3);
+}
+
 // ---------------------------------------------------------------------------------------
 // I/O element types: widen 16-byte chunks to fp32 and narrow fp32 back (round to nearest
 // even; the hardware conversions v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32 do this).
@@ -105,6 +117,12 @@ struct Io<DT_F32> {
     }
     __device__ static __forceinline__ void store1(void* p, int64_t i, float v) { static_cast<float*>(p)[i] = v; }
     __device__ static __forceinline__ float round(float v) { return v; }
+    __device__ static __forceinline__ float bload(Rsrc r, uint32_t j) {
+        return bit_cast<float>(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(j * 4), 0, 0));
+    }
+    __device__ static __forceinline__ void bstore(Rsrc r, uint32_t j, float v) {
+        __builtin_amdgcn_raw_buffer_store_b32(bit_cast<unsigned>(v), r, static_cast<int>(j * 4), 0, 0);
+    }
 };
 
 template <>
@@ -146,6 +164,14 @@ struct Io<DT_F16> {
         static_cast<_Float16*>(p)[i] = static_cast<_Float16>(v);
     }
     __device__ static __forceinline__ float round(float v) { return static_cast<float>(static_cast<_Float16>(v)); }
+    __device__ static __forceinline__ float bload(Rsrc r, uint32_t j) {
+        return static_cast<float>(
+            bit_cast<_Float16>(__builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(j * 2), 0, 0)));
+    }
+    __device__ static __forceinline__ void bstore(Rsrc r, uint32_t j, float v) {
+        __builtin_amdgcn_raw_buffer_store_b16(bit_cast<unsigned short>(static_cast<_Float16>(v)), r,
+                                              static_cast<int>(j * 2), 0, 0);
+    }
 };
 
 template <>
@@ -186,6 +212,13 @@ struct Io<DT_BF16> {
         static_cast<unsigned short*>(p)[i] = static_cast<unsigned short>(narrow2(v, v));
     }
     __device__ static __forceinline__ float round(float v) { return lo(narrow2(v, v)); }
+    __device__ static __forceinline__ float bload(Rsrc r, uint32_t j) {
+        return lo(__builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(j * 2), 0, 0));
+    }
+    __device__ static __forceinline__ void bstore(Rsrc r, uint32_t j, float v) {
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(narrow2(v, v)), r, static_cast<int>(j * 2),
+                                              0, 0);
+    }
 };
 
 // ---------------------------------------------------------------------------------------
@@ -233,13 +266,15 @@ struct Moments {
     float n, m, m2;
 };
 
-// Pairwise Welford combine; an empty side returns the other side unchanged.
+// Pairwise Welford combine; an empty side returns the other side unchanged. The weight
+// nb / n uses the hardware reciprocal (about 1 ulp; a correctly rounded division costs about
+// ten instructions, per part and row). Equal means (d == 0) combine exactly either way.
 __device__ __forceinline__ Moments combine(const Moments& a, const Moments& b) {
     if (b.n == 0.f) return a;
     if (a.n == 0.f) return b;
     const float n = a.n + b.n;
     const float d = b.m - a.m;
-    const float f = b.n / n;
+    const float f = b.n * __builtin_amdgcn_rcpf(n);
     return Moments{n, a.m + d * f, a.m2 + b.m2 + d * d * a.n * f};
 }
 
@@ -696,7 +731,7 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_vec_kernel(Params p) {
     constexpr bool PLDS = (FL & FL_PARAMS_LDS) != 0 && (R::HG || R::HB);
     constexpr int PSRC = PLDS ? R::PARAMS_LDS : R::PARAMS_REG;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
     const int rg = wave / W;       // row slot of this wave in the workgroup
     const int wr = wave - rg * W;  // wave index inside the row group
     const int t = wr * 64 + lane;  // lane index inside the row group
@@ -763,11 +798,12 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_elem_kernel(Params p) {
     constexpr bool HG = !OT::SM && (AFF & AFF_G) != 0;
     constexpr bool HB = OT::LN && (AFF & AFF_B) != 0;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
     const int rg = wave / W;
     const int wr = wave - rg * W;
     const unsigned t = static_cast<unsigned>(wr * 64 + lane);
     const unsigned N = static_cast<unsigned>(p.N);  // N <= 64 * W * V fits in 32 bits
+    const uint32_t row_bytes = N * S;
     __shared__ WavePart part_all[RPB][2][W > 1 ? W : 1];
     WavePart(*part)[W > 1 ? W : 1] = part_all[rg];
     // elements of this wave: slot i holds column i * LANES + wr * 64 + lane
@@ -778,14 +814,19 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_elem_kernel(Params p) {
         cnt += k <= 0 ? 0 : (k >= 64 ? 64 : k);
     }
     const float n_w = static_cast<float>(cnt);
-    // The lane's columns are the same for every row: its parameters are loaded once.
+    const float inv_w = n_w > 0.f ? 1.0f / n_w : 0.f;
+    // The lane's columns are the same for every row: its parameters are loaded once
+    // (columns beyond N read as 0).
     float g[HG ? V : 1], b[HB ? V : 1];
+    {
+        const Rsrc gr = make_rsrc(p.gamma, HG ? row_bytes : 0);
+        const Rsrc br = make_rsrc(p.beta, HB ? row_bytes : 0);
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-        const unsigned j = static_cast<unsigned>(i * LANES) + t;
-        const unsigned jc = j < N ? j : N - 1;
-        if constexpr (HG) g[i] = IO::load1(p.gamma, jc);
-        if constexpr (HB) b[i] = IO::load1(p.beta, jc);
+        for (int i = 0; i < V; ++i) {
+            const unsigned j = static_cast<unsigned>(i * LANES) + t;
+            if constexpr (HG) g[i] = IO::bload(gr, j);
+            if constexpr (HB) b[i] = IO::bload(br, j);
+        }
     }
     int buf = 0;
     for (int64_t base = static_cast<int64_t>(blockIdx.x) * RPB; base < p.rows;
@@ -797,35 +838,25 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_elem_kernel(Params p) {
             buf ^= 1;
             continue;
         }
-        // Row bases are wave-uniform; element offsets are 32-bit.
-        const char* xr = static_cast<const char*>(p.x) + row * p.ldx * S;
-        const char* rr = OT::RES ? static_cast<const char*>(p.residual) + row * p.ldr * S : nullptr;
+        // One buffer resource per row and tensor (row bases are wave-uniform): loads beyond
+        // the row read 0, so idle slots need no masking; stores beyond it are dropped.
+        const Rsrc xr = make_rsrc(static_cast<const char*>(p.x) + row * p.ldx * S, row_bytes);
         float f[V], r[OT::RES ? V : 1];
-        // a1 (+ a2): load the row; the fused ops form, store and keep t = round(x + r).
-        // Every load is unconditional (idle slots read the row's last element and are
-        // zeroed after): a load under a branch would be followed by a wait for its data
-        // before the next one is issued.
+        // a1 (+ a2): load the row; the fused ops form, store and keep t = round(x + r)
 #pragma unroll
-        for (int i = 0; i < V; ++i) {
-            const unsigned j = static_cast<unsigned>(i * LANES) + t;
-            const unsigned jc = j < N ? j : N - 1;
-            f[i] = IO::load1(xr, jc);
-            if constexpr (OT::RES) r[i] = IO::load1(rr, jc);
+        for (int i = 0; i < V; ++i) f[i] = IO::bload(xr, static_cast<unsigned>(i * LANES) + t);
+        if constexpr (OT::RES) {
+            const Rsrc rr = make_rsrc(static_cast<const char*>(p.residual) + row * p.ldr * S, row_bytes);
+#pragma unroll
+            for (int i = 0; i < V; ++i) r[i] = IO::bload(rr, static_cast<unsigned>(i * LANES) + t);
         }
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-            const unsigned j = static_cast<unsigned>(i * LANES) + t;
-            if constexpr (OT::RES) f[i] += r[i];
-            f[i] = j < N ? f[i] : 0.f;
-        }
         if constexpr (OT::RES) {
-            char* orow = static_cast<char*>(p.residual_out) + row * p.ldro * S;
+            const Rsrc orr = make_rsrc(static_cast<char*>(p.residual_out) + row * p.ldro * S, row_bytes);
 #pragma unroll
             for (int i = 0; i < V; ++i) {
-                const unsigned j = static_cast<unsigned>(i * LANES) + t;
-                f[i] = IO::round(f[i]);
-                if (j < N) IO::store1(orow, j, f[i]);
+                f[i] = IO::round(f[i] + r[i]);  // 0 + 0 = 0 in idle slots
+                IO::bstore(orr, static_cast<unsigned>(i * LANES) + t, f[i]);
             }
         }
         float scale, offset = 0.f;
@@ -834,7 +865,6 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_elem_kernel(Params p) {
             float s1 = 0.f;
 #pragma unroll
             for (int i = 0; i < V; ++i) s1 += static_cast<unsigned>(i * LANES) + t < N ? f[i] - K : 0.f;
-            const float inv_w = n_w > 0.f ? 1.0f / n_w : 0.f;
             const float a = K + wave_sum(s1) * inv_w;
             float c = 0.f, q = 0.f;
 #pragma unroll
@@ -857,30 +887,29 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_elem_kernel(Params p) {
 #pragma unroll
             for (int i = 0; i < V; ++i) mx = static_cast<unsigned>(i * LANES) + t < N ? fmaxf(mx, f[i]) : mx;
             const float mw = wave_max(mx);
-            float s = 0.f;
+            float sm = 0.f;
 #pragma unroll
             for (int i = 0; i < V; ++i) {
                 f[i] = static_cast<unsigned>(i * LANES) + t < N ? exp_neg(f[i] - mw) : 0.f;
-                s += f[i];
+                sm += f[i];
             }
             float M, Ssum;
-            group_softmax<W>(part, buf, lane, wr, mw, wave_sum(s), M, Ssum);
+            group_softmax<W>(part, buf, lane, wr, mw, wave_sum(sm), M, Ssum);
             scale = exp_neg(mw - M) / Ssum;
             if (t == 0 && p.mean) p.mean[row] = M;
             if (t == 0 && p.rstd) p.rstd[row] = Ssum;
         } else {
-            float s = 0.f;
+            float sq = 0.f;
 #pragma unroll
-            for (int i = 0; i < V; ++i) s = fmaf(f[i], f[i], s);
-            const float Ssq = group_sum<W>(part, buf, lane, wr, wave_sum(s));
+            for (int i = 0; i < V; ++i) sq = fmaf(f[i], f[i], sq);  // idle slots hold 0
+            const float Ssq = group_sum<W>(part, buf, lane, wr, wave_sum(sq));
             scale = inv_sqrt(fmaf(Ssq, p.inv_n, p.eps));
             if (t == 0 && p.rstd) p.rstd[row] = scale;
         }
-        // a7: normalize, apply the parameters, store.
-        char* yrow = static_cast<char*>(p.y) + row * p.ldy * S;
+        // a7: normalize, apply the parameters, store (stores beyond the row are dropped).
+        const Rsrc yr = make_rsrc(static_cast<char*>(p.y) + row * p.ldy * S, row_bytes);
 #pragma unroll
         for (int i = 0; i < V; ++i) {
-            const unsigned j = static_cast<unsigned>(i * LANES) + t;
             float z = OT::LN ? fmaf(f[i], scale, offset) : f[i] * scale;
             if constexpr (HG && HB) {
                 z = fmaf(z, g[i], b[i]);
@@ -889,7 +918,7 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_elem_kernel(Params p) {
             } else if constexpr (HB) {
                 z = z + b[i];
             }
-            if (j < N) IO::store1(yrow, j, z);
+            IO::bstore(yr, static_cast<unsigned>(i * LANES) + t, z);
         }
     }
 }
@@ -923,7 +952,7 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_stats_kernel(Params p
     constexpr int E = IO::E;
     constexpr int V = kWideV;
     const int lane = threadIdx.x & 63;
-    const int wr = threadIdx.x >> 6;
+    const int wr = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
     const int t = threadIdx.x;
     __shared__ WavePart part[2][kWideW];
     int buf = 0;
