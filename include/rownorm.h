@@ -259,6 +259,9 @@ typedef struct rn_plan_info {
                               workgroups loop over many rows, with the parameters loaded on chip
                               once per workgroup */
     int lds_bytes;         /* dynamic LDS per workgroup of a persistent launch */
+    int pairs;             /* element variant: 1 if each lane slot holds two adjacent 16-bit
+                              elements moved as one 4-byte word (chunks_per_lane then counts
+                              such slots) */
 } rn_plan_info;
 
 int rn_plan(int op, const void* x, const void* residual, const void* gamma, const void* beta, const void* y,

@@ -47,7 +47,7 @@ class RowStrides(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [("variant", _ci), ("waves_per_row", _ci), ("rows_per_block", _ci), ("block_threads", _ci),
                 ("chunks_per_lane", _ci), ("grid_blocks", _i64), ("exact", _ci), ("persistent", _ci),
-                ("lds_bytes", _ci)]
+                ("lds_bytes", _ci), ("pairs", _ci)]
 
 
 _lib.rn_forward_ex.argtypes = [_ci, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci,
@@ -427,7 +427,8 @@ def plan_backward(op: str, rows: int, N: int, dtype: torch.dtype, *, ptrs: Optio
     return st, {"variant": VARIANT_NAMES.get(info.variant, info.variant), "waves_per_row": info.waves_per_row,
                 "rows_per_block": info.rows_per_block, "block_threads": info.block_threads,
                 "chunks_per_lane": info.chunks_per_lane, "grid_blocks": info.grid_blocks,
-                "exact": bool(info.exact), "lds_bytes": info.lds_bytes}
+                "exact": bool(info.exact), "lds_bytes": info.lds_bytes,
+                "pairs": bool(info.pairs)}
 
 
 def plan(op: str, rows: int, N: int, dtype: torch.dtype, *, ptrs: Optional[dict] = None, eps: float = 1e-5,
@@ -460,4 +461,5 @@ def plan(op: str, rows: int, N: int, dtype: torch.dtype, *, ptrs: Optional[dict]
     return st, {"variant": VARIANT_NAMES.get(info.variant, info.variant), "waves_per_row": info.waves_per_row,
                 "rows_per_block": info.rows_per_block, "block_threads": info.block_threads,
                 "chunks_per_lane": info.chunks_per_lane, "grid_blocks": info.grid_blocks,
-                "exact": bool(info.exact), "persistent": bool(info.persistent), "lds_bytes": info.lds_bytes}
+                "exact": bool(info.exact), "persistent": bool(info.persistent), "lds_bytes": info.lds_bytes,
+                "pairs": bool(info.pairs)}

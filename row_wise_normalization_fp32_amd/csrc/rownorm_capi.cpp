@@ -113,6 +113,7 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     plan->exact = false;
     plan->persistent = false;
     plan->lds_bytes = 0;
+    plan->pairs = false;
     *chunks = 0;
     if (rows == 0) return RN_OK;
 
@@ -226,12 +227,34 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
         plan->chunks_per_lane = 0;
         plan->block_threads = rn::kGeneralThreads;
     } else if (plan->variant == rn::V_ELEMENT) {
-        // about kElemTarget elements per lane: W = 1 up to 512 elements, then 2, 4, 8, 16
-        int We = next_pow2((N + 64 * rn::kElemTarget - 1) / (64 * rn::kElemTarget));
-        if (We > rn::kMaxGroupWaves) We = rn::kMaxGroupWaves;
+        // 16-bit rows move as 4-byte element pairs when every row tensor has the same
+        // position in its 4-byte word on every row (same address bit 1 on the base
+        // pointers and the same stride parity). A row starting in the upper half of a word
+        // (head 1: x's address bit 1 on row 0, or an odd stride on the rows after it)
+        // covers (N + 2) / 2 words, otherwise (N + 1) / 2.
+        const uintptr_t h0 = (reinterpret_cast<uintptr_t>(a.x) >> 1) & 1;
+        const int64_t hmax = (h0 != 0 || (rows > 1 && (a.ldx & 1) != 0)) ? 1 : 0;
+        const int64_t words = (N + hmax + 1) / 2;
+        bool pairs = s == 2 && words <= int64_t(64) * rn::kMaxGroupWaves * rn::kPairMaxPerLane;
+        for (int i = 0; i < nb && pairs; ++i) {
+            const Buf& bf = bufs[i];
+            if (!bf.p || !(bf.role == R_RES || bf.role == R_Y || bf.role == R_RO)) continue;
+            if (((reinterpret_cast<uintptr_t>(bf.p) >> 1) & 1) != h0) pairs = false;
+            if (rows > 1 && ((bf.stride ^ a.ldx) & 1) != 0) pairs = false;
+        }
+        plan->pairs = pairs;
+        int We;
+        if (pairs) {  // about kPairTarget words per lane
+            We = next_pow2((words + 64 * rn::kPairTarget - 1) / (64 * rn::kPairTarget));
+            if (We > rn::kMaxGroupWaves) We = rn::kMaxGroupWaves;
+            plan->chunks_per_lane = next_pow2((words + 64 * We - 1) / (64 * We));
+        } else {  // about kElemTarget elements per lane: W = 1 up to 512 elements, then 2, 4, 8, 16
+            We = next_pow2((N + 64 * rn::kElemTarget - 1) / (64 * rn::kElemTarget));
+            if (We > rn::kMaxGroupWaves) We = rn::kMaxGroupWaves;
+            plan->chunks_per_lane = next_pow2((N + 64 * We - 1) / (64 * We));
+        }
         plan->waves_per_row = We;
         plan->rows_per_block = We <= 4 ? 4 / We : 1;
-        plan->chunks_per_lane = next_pow2((N + 64 * We - 1) / (64 * We));
         plan->block_threads = 64 * We * plan->rows_per_block;
     } else {
         plan->waves_per_row = W;
@@ -441,7 +464,7 @@ int validate_and_plan_bwd(BwdArgs& a, Plan* plan, int64_t* chunks) {
 }
 
 int run_bwd(BwdArgs a, hipStream_t stream) {
-    Plan plan;
+    Plan plan{};
     int64_t C = 0;
     const int st = validate_and_plan_bwd(a, &plan, &C);
     if (st != RN_OK) return st;
@@ -573,7 +596,7 @@ int rn_plan_backward(int op, const void* dy, const void* x, const void* gamma, c
                      const void* workspace, size_t workspace_bytes, rn_plan_info* out) {
     BwdArgs a{op, dy, x, gamma, mean, rstd, const_cast<void*>(dx), const_cast<void*>(dgamma),
               const_cast<void*>(dbeta), rows, N, dtype, const_cast<void*>(workspace), workspace_bytes};
-    Plan plan;
+    Plan plan{};
     int64_t C = 0;
     const int st = validate_and_plan_bwd(a, &plan, &C);
     if (out) {
@@ -586,6 +609,7 @@ int rn_plan_backward(int op, const void* dy, const void* x, const void* gamma, c
         out->exact = plan.exact ? 1 : 0;
         out->persistent = plan.persistent ? 1 : 0;
         out->lds_bytes = plan.lds_bytes;
+        out->pairs = plan.pairs ? 1 : 0;
     }
     return st;
 }
@@ -594,7 +618,7 @@ int rn_plan(int op, const void* x, const void* residual, const void* gamma, cons
             const void* residual_out, const void* mean, const void* rstd, int64_t rows, int64_t N, float eps,
             int dtype, int variant, const rn_row_strides* strides, const void* workspace, size_t workspace_bytes,
             rn_plan_info* out) {
-    Plan plan;
+    Plan plan{};
     int64_t C = 0;
     Args a = make_args(op, x, residual, gamma, beta, y, residual_out, mean, rstd, rows, N, eps, dtype, variant);
     a.ws = const_cast<void*>(workspace);
@@ -610,6 +634,7 @@ int rn_plan(int op, const void* x, const void* residual, const void* gamma, cons
         out->exact = plan.exact ? 1 : 0;
         out->persistent = plan.persistent ? 1 : 0;
         out->lds_bytes = plan.lds_bytes;
+        out->pairs = plan.pairs ? 1 : 0;
     }
     return st;
 }

@@ -77,6 +77,7 @@ struct Plan {
     bool exact;           // C == 64 * W * V: no tail handling needed
     bool persistent;      // parameters staged on chip once, grid sized to resident capacity
     int lds_bytes;        // dynamic LDS of a persistent launch
+    bool pairs;           // element variant, 16-bit: slots of two adjacent elements (pair kernel)
 };
 
 // Shapes the vectorized kernels are built for.
@@ -87,6 +88,9 @@ constexpr int kTargetChunks = 4;       // automatic choice: about 4 chunks per l
 constexpr int kGeneralThreads = 256;   // general variant: 256 lanes per row
 constexpr int kElemTarget = 8;         // element variant: about 8 elements per lane ...
 constexpr int kElemMaxPerLane = 16;    // ... at most 16 (with 16 waves: rows up to 16384)
+constexpr int kPairTarget = 8;         // pair kernel: about 8 two-element slots per lane ...
+constexpr int kPairMaxPerLane = 8;     // ... at most 8 (with 16 waves: rows up to 16384)
+constexpr int kElemCuRowBytes = 32768; // element kernels, persistent: row bytes held per CU
 constexpr int64_t kMaxGrid = 1 << 20;  // grid cap; kernels loop over the remaining rows
 constexpr int64_t kPersistentBlocks = 2048;  // at least this many workgroups: persistent launch
 constexpr int kWideSegChunks = 2048;   // split-row variant: 16-byte chunks per segment (one workgroup)

@@ -172,6 +172,8 @@ struct Io<DT_F16> {
         __builtin_amdgcn_raw_buffer_store_b16(bit_cast<unsigned short>(static_cast<_Float16>(v)), r,
                                               static_cast<int>(j * 2), 0, 0);
     }
+    // two adjacent elements held in one 32-bit word, the lower-addressed one in the low half
+    __device__ static __forceinline__ f32x2 widen_pair(unsigned u) { return widen2(u); }
 };
 
 template <>
@@ -219,7 +221,20 @@ struct Io<DT_BF16> {
         __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(narrow2(v, v)), r, static_cast<int>(j * 2),
                                               0, 0);
     }
+    __device__ static __forceinline__ f32x2 widen_pair(unsigned u) { return f32x2{lo(u), hi(u)}; }
 };
+
+// 32-bit and 16-bit buffer accesses at a byte offset (out of range: loads read 0, stores
+// are dropped).
+__device__ __forceinline__ unsigned bload32(Rsrc r, uint32_t off) {
+    return static_cast<unsigned>(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0));
+}
+__device__ __forceinline__ void bstore32(Rsrc r, uint32_t off, unsigned v) {
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, static_cast<int>(off), 0, 0);
+}
+__device__ __forceinline__ void bstore16(Rsrc r, uint32_t off, unsigned v) {
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(v), r, static_cast<int>(off), 0, 0);
+}
 
 // ---------------------------------------------------------------------------------------
 // Wavefront reductions. Must be called with all 64 lanes active.
@@ -924,6 +939,198 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_elem_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Pair kernel: 16-bit rows that are not whole 16-byte chunks (ragged N, padded or unaligned
+// rows). A lane slot holds two adjacent elements and moves them with one 4-byte access:
+// half the memory instructions of the element kernel, each moving twice the bytes. Slots
+// sit on 4-byte boundaries, so a row that starts in the upper half of a word has head
+// h = 1 and slot position q holds element q - h. The at most two positions outside the row
+// (one before it, one after it, each in a word that also holds row data, so never on
+// another page) are read but masked out of the statistics, and never written: a wave's slot
+// that does not lie wholly inside the row is written with 2-byte stores. Every row tensor
+// of the call has the same head on a given row (checked by the planner).
+// ---------------------------------------------------------------------------------------
+template <int DT, int OP, int W, int VP, int RPB, int AFF>
+__global__ __launch_bounds__(64 * W * RPB) void rownorm_pair_kernel(Params p) {
+    using IO = Io<DT>;
+    using OT = OpTraits<OP>;
+    constexpr int LANES = 64 * W;
+    constexpr int NE = 2 * VP;  // elements per lane
+    constexpr bool HG = !OT::SM && (AFF & AFF_G) != 0;
+    constexpr bool HB = OT::LN && (AFF & AFF_B) != 0;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rg = wave / W;
+    const int wr = wave - rg * W;
+    const int t = wr * 64 + lane;
+    const int N = static_cast<int>(p.N);  // 2 * 64 * W * VP > N: 32-bit offsets
+    __shared__ WavePart part_all[RPB][2][W > 1 ? W : 1];
+    WavePart(*part)[W > 1 ? W : 1] = part_all[rg];
+    float g[HG ? NE : 1], b[HB ? NE : 1];
+    int hp = -1;  // the head that the parameters and n_w were set up for
+    float n_w = 0.f, inv_w = 0.f;
+    int buf = 0;
+    for (int64_t base = static_cast<int64_t>(blockIdx.x) * RPB; base < p.rows;
+         base += static_cast<int64_t>(gridDim.x) * RPB) {
+        const int64_t row = base + rg;
+        if (row >= p.rows) {
+            if constexpr (W == 1) break;
+            __syncthreads();
+            buf ^= 1;
+            continue;
+        }
+        const char* xrow = static_cast<const char*>(p.x) + row * p.ldx * 2;
+        const int h = static_cast<int>((reinterpret_cast<uintptr_t>(xrow) >> 1) & 1);
+        // a0 + 2 * i * LANES (+ 1) is the element in slot i's low (high) half
+        const int a0 = 2 * t - h;
+        if (h != hp) {  // wave-uniform; once per row group when its rows share a head
+            hp = h;
+            int cnt = 0;
+#pragma unroll
+            for (int i = 0; i < VP; ++i) {
+                const int s0 = 2 * (i * LANES + wr * 64);  // the wave's first position in slot i
+                const int k = N + h - s0;
+                cnt += (k <= 0 ? 0 : (k >= 128 ? 128 : k)) - (s0 == 0 ? h : 0);
+            }
+            n_w = static_cast<float>(cnt);
+            inv_w = cnt > 0 ? 1.0f / n_w : 0.f;
+            const Rsrc gr = make_rsrc(p.gamma, HG ? static_cast<uint32_t>(2 * N) : 0);
+            const Rsrc br = make_rsrc(p.beta, HB ? static_cast<uint32_t>(2 * N) : 0);
+#pragma unroll
+            for (int e = 0; e < NE; ++e) {
+                const int j = a0 + 2 * (e >> 1) * LANES + (e & 1);
+                const uint32_t jj = j >= 0 ? static_cast<uint32_t>(j) : static_cast<uint32_t>(N);  // N: reads 0
+                if constexpr (HG) g[e] = IO::bload(gr, jj);
+                if constexpr (HB) b[e] = IO::bload(br, jj);
+            }
+        }
+        // Element e of the lane (slot e / 2, half e % 2) is in the row iff
+        // 0 <= a0 + 2 * (e / 2) * LANES + e % 2 < N; only e = 0 can fall below 0. The test
+        // is one compare against a constant; `av` is made opaque before each use so that
+        // the compiler recomputes the tests instead of holding 2 * VP masks in SGPRs.
+        int av = a0;
+        auto ok = [&](int e) {
+            return e == 0 ? static_cast<unsigned>(av) < static_cast<unsigned>(N)
+                          : av < N - 2 * (e >> 1) * LANES - (e & 1);
+        };
+        const uint32_t wbytes = static_cast<uint32_t>(((N + h + 1) >> 1) * 4);  // words holding row data
+        // stores of slot i's word: whole when the wave's 64 words lie in the row, else halves
+        auto store_slot = [&](char* rowp, int i, unsigned w) {
+            const int s0 = 2 * (i * LANES + wr * 64);
+            if (s0 >= h && s0 + 128 <= N + h) {
+                bstore32(make_rsrc(rowp - 2 * h, wbytes), static_cast<uint32_t>(4 * (i * LANES + t)), w);
+            } else {
+                const Rsrc r16 = make_rsrc(rowp, static_cast<uint32_t>(2 * N));
+                const int e0 = a0 + 2 * i * LANES;
+                bstore16(r16, static_cast<uint32_t>(ok(2 * i) ? 2 * e0 : 2 * N), w & 0xffffu);
+                bstore16(r16, static_cast<uint32_t>(ok(2 * i + 1) ? 2 * e0 + 2 : 2 * N), w >> 16);
+            }
+        };
+        unsigned u[VP], ur[OT::RES ? VP : 1];
+        {
+            const Rsrc xr = make_rsrc(xrow - 2 * h, wbytes);
+#pragma unroll
+            for (int i = 0; i < VP; ++i) u[i] = bload32(xr, static_cast<uint32_t>(4 * (i * LANES + t)));
+        }
+        if constexpr (OT::RES) {
+            const char* rrow = static_cast<const char*>(p.residual) + row * p.ldr * 2;
+            const Rsrc rr = make_rsrc(rrow - 2 * h, wbytes);
+#pragma unroll
+            for (int i = 0; i < VP; ++i) ur[i] = bload32(rr, static_cast<uint32_t>(4 * (i * LANES + t)));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        float f[NE];
+#pragma unroll
+        for (int i = 0; i < VP; ++i) {
+            const f32x2 v = IO::widen_pair(u[i]);
+            f[2 * i] = v.x;
+            f[2 * i + 1] = v.y;
+        }
+        if constexpr (OT::RES) {
+            char* orow = static_cast<char*>(p.residual_out) + row * p.ldro * 2;
+#pragma unroll
+            for (int i = 0; i < VP; ++i) {
+                const f32x2 r = IO::widen_pair(ur[i]);
+                const unsigned w = IO::narrow2(f[2 * i] + r.x, f[2 * i + 1] + r.y);  // t = round(x + r)
+                store_slot(orow, i, w);
+                const f32x2 v = IO::widen_pair(w);
+                f[2 * i] = v.x;
+                f[2 * i + 1] = v.y;
+            }
+        }
+        float scale, offset = 0.f;
+        if constexpr (OT::LN) {
+            const float K = uniform(ok(1) ? f[1] : 0.f);  // a shift near the wave's data
+            float s1 = 0.f;
+            asm volatile("" : "+v"(av));
+#pragma unroll
+            for (int e = 0; e < NE; ++e) s1 += ok(e) ? f[e] - K : 0.f;
+            const float a = K + wave_sum(s1) * inv_w;
+            float c = 0.f, q = 0.f;
+            asm volatile("" : "+v"(av));
+#pragma unroll
+            for (int e = 0; e < NE; ++e) {
+                f[e] = ok(e) ? f[e] - a : 0.f;
+                c += f[e];
+                q = fmaf(f[e], f[e], q);
+            }
+            const float Cw = wave_sum(c);
+            const float Qw = wave_sum(q);
+            const float cw = Cw * inv_w;
+            float rel, m2, mean;
+            group_moments<W, false>(part, buf, lane, wr, n_w, a, cw, fmaxf(Qw - Cw * cw, 0.f), rel, m2, mean);
+            if (t == 0 && p.mean) p.mean[row] = mean;
+            scale = inv_sqrt(fmaf(m2, p.inv_n, p.eps));
+            offset = -rel * scale;
+            if (t == 0 && p.rstd) p.rstd[row] = scale;
+        } else if constexpr (OT::SM) {
+            float mx = -INFINITY;
+            asm volatile("" : "+v"(av));
+#pragma unroll
+            for (int e = 0; e < NE; ++e) mx = ok(e) ? fmaxf(mx, f[e]) : mx;
+            const float mw = wave_max(mx);
+            float sm = 0.f;
+            asm volatile("" : "+v"(av));
+#pragma unroll
+            for (int e = 0; e < NE; ++e) {
+                f[e] = ok(e) ? exp_neg(f[e] - mw) : 0.f;
+                sm += f[e];
+            }
+            float M, Ssum;
+            group_softmax<W>(part, buf, lane, wr, mw, wave_sum(sm), M, Ssum);
+            scale = exp_neg(mw - M) / Ssum;
+            if (t == 0 && p.mean) p.mean[row] = M;
+            if (t == 0 && p.rstd) p.rstd[row] = Ssum;
+        } else {
+            float sq = 0.f;
+#pragma unroll
+            for (int e = 0; e < NE; ++e) sq = ok(e) ? fmaf(f[e], f[e], sq) : sq;
+            const float Ssq = group_sum<W>(part, buf, lane, wr, wave_sum(sq));
+            scale = inv_sqrt(fmaf(Ssq, p.inv_n, p.eps));
+            if (t == 0 && p.rstd) p.rstd[row] = scale;
+        }
+        char* yrow = static_cast<char*>(p.y) + row * p.ldy * 2;
+        asm volatile("" : "+v"(av));
+#pragma unroll
+        for (int i = 0; i < VP; ++i) {
+            float z[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int e = 2 * i + k;
+                z[k] = OT::LN ? fmaf(f[e], scale, offset) : f[e] * scale;
+                if constexpr (HG && HB) {
+                    z[k] = fmaf(z[k], g[e], b[e]);
+                } else if constexpr (HG) {
+                    z[k] = z[k] * g[e];
+                } else if constexpr (HB) {
+                    z[k] = z[k] + b[e];
+                }
+            }
+            store_slot(yrow, i, IO::narrow2(z[0], z[1]));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
 // Split-row kernels: rows too long for one workgroup's registers (the walkthrough's
 // section 1.1 case of a row that outgrows one block), with 16-byte chunks. A row is cut into
 // S segments of kWideChunks chunks, one workgroup (kWideW waves, kWideV chunks per lane) per
@@ -1307,7 +1514,7 @@ constexpr int kMaxDevices = 64;
 // per kernel instance and device: the kernel is a template argument, so each instance has
 // its own cache), capped as below, at most one per row group of work.
 template <auto KERNEL>
-inline hipError_t go_persistent(const Plan& plan, const Params& p, hipStream_t stream) {
+inline hipError_t go_persistent(const Plan& plan, const Params& p, hipStream_t stream, int row_bytes_per_wave = 0) {
     static int per_cu_cache[kMaxDevices];  // 0: not yet known; a benign race writes the same value
     static int cus_cache[kMaxDevices];
     int dev = 0;
@@ -1327,10 +1534,21 @@ inline hipError_t go_persistent(const Plan& plan, const Params& p, hipStream_t s
             __atomic_store_n(&cus_cache[dev], cus, __ATOMIC_RELAXED);
         }
     }
-    // Workgroups holding 4 chunks per lane: at most two per CU (more rows per workgroup,
-    // measured better for fused add + LayerNorm 8192 x 4096: 68.3% -> 70.0%, neutral for the
-    // others); smaller rows keep the full resident count for bytes in flight.
-    const int cap = plan.chunks_per_lane >= 4 && per_cu > 2 ? 2 : per_cu;
+    // Vectorized workgroups holding 4 chunks per lane: at most two per CU (more rows per
+    // workgroup, measured better for fused add + LayerNorm 8192 x 4096: 68.3% -> 70.0%,
+    // neutral for the others); smaller rows keep the full resident count for bytes in flight.
+    // The element kernels (row_bytes_per_wave > 0: the row bytes one wave holds) keep about
+    // kElemCuRowBytes of row data per CU (measured on MI355X, persistent grids of 1 to 6
+    // workgroups per CU: 16 waves of 2 KiB or 32 of 1 KiB are the best or within noise of
+    // it; fp32 LayerNorm 8192 x 4095: 60% resident-limited -> 68%).
+    int cap = per_cu;
+    if (row_bytes_per_wave > 0) {
+        const int waves = kElemCuRowBytes / row_bytes_per_wave;
+        const int wg = waves / (plan.block_threads / 64);
+        cap = wg < 1 ? 1 : (wg < per_cu ? wg : per_cu);
+    } else if (plan.chunks_per_lane >= 4 && per_cu > 2) {
+        cap = 2;
+    }
     int64_t grid = static_cast<int64_t>(cus) * cap;
     if (grid > plan.grid) grid = plan.grid;
     Params args = p;
@@ -1395,12 +1613,60 @@ inline hipError_t launch_e(const Plan& plan, const Params& p, hipStream_t s) {
 // with 8 or 16 (rows of up to 16384 elements). Many rows: a persistent grid (the kernel
 // loops over rows either way; its parameters stay in registers across rows).
 template <int DT, int OP>
-inline hipError_t launch_elem(const Plan& plan, const Params& p, hipStream_t s) {
+inline hipError_t launch_pair(const Plan& plan, const Params& p, hipStream_t s) {
     const int W = plan.waves_per_row, V = plan.chunks_per_lane;
     const int aff = (p.gamma ? AFF_G : 0) | (OpTraits<OP>::LN && p.beta ? AFF_B : 0);
     if (plan.rows_per_block != rows_per_block_for(W)) return hipErrorInvalidValue;
+#define RN_PR(WW, VV, A)                                                                      \
+    (plan.persistent ? go_persistent<rownorm_pair_kernel<DT, OP, WW, VV, rows_per_block_for(WW), A>>(plan, p, s, 256 * VV) \
+                     : go(rownorm_pair_kernel<DT, OP, WW, VV, rows_per_block_for(WW), A>, plan, p, s))
+#define RN_PR_AFF(WW, VV)                                                     \
+    do {                                                                      \
+        if constexpr (OpTraits<OP>::SM) return RN_PR(WW, VV, 0);              \
+        if (aff == 0) return RN_PR(WW, VV, 0);                                \
+        if (aff == AFF_G) return RN_PR(WW, VV, AFF_G);                        \
+        if constexpr (OpTraits<OP>::LN) {                                     \
+            if (aff == AFF_B) return RN_PR(WW, VV, AFF_B);                    \
+            return RN_PR(WW, VV, AFF_G | AFF_B);                              \
+        }                                                                     \
+        return hipErrorInvalidValue;                                          \
+    } while (0)
+    // the shapes the planner produces: W = 1 with 1..8 words per lane, else 8 words per lane
+    if (W == 1) {
+        switch (V) {
+        case 1: RN_PR_AFF(1, 1);
+        case 2: RN_PR_AFF(1, 2);
+        case 4: RN_PR_AFF(1, 4);
+        case 8: RN_PR_AFF(1, 8);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    if (V != 8) return hipErrorInvalidValue;
+    switch (W) {
+    case 2: RN_PR_AFF(2, 8);
+    case 4: RN_PR_AFF(4, 8);
+    case 8: RN_PR_AFF(8, 8);
+    case 16: RN_PR_AFF(16, 8);
+    default: return hipErrorInvalidValue;
+    }
+#undef RN_PR_AFF
+#undef RN_PR
+}
+
+template <int DT, int OP>
+inline hipError_t launch_elem(const Plan& plan, const Params& p, hipStream_t s) {
+    const int W = plan.waves_per_row, V = plan.chunks_per_lane;
+    const int aff = (p.gamma ? AFF_G : 0) | (OpTraits<OP>::LN && p.beta ? AFF_B : 0);
+    if (plan.pairs) {
+        if constexpr (DT == DT_F32) {
+            return hipErrorInvalidValue;
+        } else {
+            return launch_pair<DT, OP>(plan, p, s);
+        }
+    }
+    if (plan.rows_per_block != rows_per_block_for(W)) return hipErrorInvalidValue;
 #define RN_EL(WW, VV, A)                                                                      \
-    (plan.persistent ? go_persistent<rownorm_elem_kernel<DT, OP, WW, VV, rows_per_block_for(WW), A>>(plan, p, s) \
+    (plan.persistent ? go_persistent<rownorm_elem_kernel<DT, OP, WW, VV, rows_per_block_for(WW), A>>(plan, p, s, 64 * VV * (DT == DT_F32 ? 4 : 2)) \
                      : go(rownorm_elem_kernel<DT, OP, WW, VV, rows_per_block_for(WW), A>, plan, p, s))
 #define RN_EL_AFF(WW, VV)                                                     \
     do {                                                                      \

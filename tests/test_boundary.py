@@ -58,17 +58,20 @@ def test_status_strings_and_version():
     ("rms", torch.bfloat16, 16, 32768, "workgroup", 16, 4, False),
     ("ln", torch.float32, 16, 16388, "general", 0, 0, False),          # beyond a workgroup's registers
     ("ln", torch.float32, 16, 1000, "wave", 1, 4, False),              # ragged: 250 chunks
-    ("ln", torch.float16, 16, 1001, "element", 2, 8, False),           # not a whole number of 16-byte chunks
+    ("ln", torch.float16, 16, 1001, "element", 1, 8, False),           # not whole 16-byte chunks: 501 pairs
     ("rms", torch.float32, 3, 1, "element", 1, 1, False),
-    ("rms", torch.bfloat16, 8, 16383, "element", 16, 16, False),
+    ("rms", torch.bfloat16, 8, 16383, "element", 16, 8, False),        # 8192 pairs
+    ("rms", torch.float32, 8, 16383, "element", 16, 16, False),
     ("ln", torch.bfloat16, 8, 16385, "general", 0, 0, False),          # odd and beyond the element kernel
     ("ln", torch.float32, 8, 65536, "general", 0, 0, False),           # long rows without a workspace
     ("fused_add_ln", torch.bfloat16, 8192, 4096, "workgroup", 2, 4, True),
     ("fused_add_ln", torch.float32, 256, 4096, "workgroup", 4, 4, False),
     ("softmax", torch.float32, 128, 4096, "workgroup", 4, 4, False),
     ("softmax", torch.float32, 8192, 4096, "workgroup", 4, 4, False),  # no parameters: never persistent
-    ("softmax", torch.float16, 64, 333, "element", 1, 8, False),
-    ("ln", torch.bfloat16, 16384, 4095, "element", 8, 8, True),        # many ragged rows: persistent
+    ("softmax", torch.float16, 64, 333, "element", 1, 4, False),
+    ("softmax", torch.float32, 64, 333, "element", 1, 8, False),
+    ("ln", torch.bfloat16, 16384, 4095, "element", 4, 8, True),        # many ragged rows: persistent
+    ("ln", torch.float32, 16384, 4095, "element", 8, 8, True),
 ])
 def test_plan_variant_choice(op, dtype, rows, N, variant, W, V, persistent):
     ptrs = {"gamma": 1 << 44, "beta": (1 << 44) + (1 << 30)}
@@ -83,7 +86,12 @@ def test_plan_variant_choice(op, dtype, rows, N, variant, W, V, persistent):
     if variant == "element":
         assert info["waves_per_row"] == W and not info["exact"] and info["lds_bytes"] == 0
         assert info["persistent"] == persistent
-        assert 64 * W * V >= N and (V == 1 or 64 * W * V // 2 < N or W > 1)
+        # 16-bit rows of contiguous tensors move as element pairs: up to N + 1 positions
+        # (a row may start in the upper half of a 4-byte word)
+        pairs = dtype != torch.float32
+        assert info["pairs"] == pairs
+        n = (N + 2) // 2 if pairs else N
+        assert 64 * W * V >= n and (V == 1 or 64 * W * V // 2 < n or W > 1)
         return
     assert info["waves_per_row"] == W
     rpb = 4 // W if W <= 4 else 1
@@ -117,6 +125,46 @@ def test_plan_misaligned_pointer_takes_element_path():
     assert st == UNSUP
     st, info = rn.plan("ln", 8, 32768, torch.float16, ptrs={"x": (1 << 40) + 2})
     assert st == OK and info["variant"] == "general"
+
+
+def test_plan_element_pairs():
+    # 16-bit element rows move as 4-byte pairs when every row tensor has the same position
+    # in its 4-byte word on every row: same address bit 1 and same stride parity.
+    bf, base = torch.bfloat16, 1 << 40
+    far = 1 << 42
+
+    def pairs(op="ln", rows=8, N=4095, **kw):
+        st, info = rn.plan(op, rows, N, bf, **kw)
+        assert st == OK and info["variant"] == "element", info
+        return info["pairs"]
+
+    assert pairs()
+    assert pairs(ptrs={"x": base + 2, "y": far + 2})       # both start in an upper half
+    assert not pairs(ptrs={"x": base + 2, "y": far})       # x does, y does not
+    assert not pairs(ptrs={"x": base, "y": far + 6})
+    assert pairs(ptrs={"x": base + 4, "y": far})           # 4-byte offsets keep the halves
+    assert pairs(strides={"x": 4097, "y": 4099})           # both odd
+    assert not pairs(strides={"x": 4097, "y": 4096})       # parities differ ...
+    assert pairs(rows=1, strides={"x": 4097, "y": 4096})   # ... which one row never sees
+    # fused ops: residual and residual_out count too
+    assert pairs("fused_add_rms", ptrs={"residual": far + (1 << 30)})
+    assert not pairs("fused_add_rms", ptrs={"residual": far + (1 << 30) + 2})
+    assert not pairs("fused_add_ln", strides={"residual_out": 4096})
+    # 16 waves x 8 slots hold 8192 words: rows of up to 16384 elements when no row starts in
+    # an upper half, else up to 16383; fp32 never pairs
+    st, info = rn.plan("ln", 8, 16383, bf, variant="element")
+    assert info["pairs"] and info["waves_per_row"] == 16 and info["chunks_per_lane"] == 8
+    st, info = rn.plan("ln", 8, 16384, bf, variant="element")
+    assert info["pairs"] and info["waves_per_row"] == 16 and info["chunks_per_lane"] == 8
+    st, info = rn.plan("ln", 8, 16384, bf, variant="element", ptrs={"x": base + 2, "y": far + 2})
+    assert st == OK and not info["pairs"] and info["chunks_per_lane"] == 16
+    # even rows that all start on a word need N / 2 words: 2048 for 4096 elements (4 waves)
+    st, info = rn.plan("ln", 8, 4096, bf, variant="element")
+    assert info["pairs"] and info["waves_per_row"] == 4 and info["chunks_per_lane"] == 8
+    st, info = rn.plan("ln", 8, 4096, bf, variant="element", ptrs={"x": base + 2, "y": far + 2})
+    assert info["pairs"] and info["waves_per_row"] == 8 and info["chunks_per_lane"] == 8
+    assert not rn.plan("ln", 8, 4095, torch.float32)[1]["pairs"]
+    assert not rn.plan("ln", 8, 4096, bf)[1]["pairs"]  # vectorized
 
 
 def test_plan_row_strides():

@@ -215,12 +215,117 @@ def test_element_kernel_persistent(case):
     check_case(BASES[op].scaled(rows=rows, N=N, seed=720 + N, dtype=dtype))
 
 
+ROW_TENSORS = ("x", "residual", "y", "residual_out")
+
+
+def run_placed(w: workloads.Workload, inp, offset=None, ld=None, variant="auto", expect_pairs=None):
+    """Runs the op with each row tensor placed in its own NaN-filled buffer, at an element
+    offset (``offset[name]``) and row stride (``ld[name]``, default N), with 64 guard
+    elements on both sides. Checks that nothing outside the outputs' rows is written and,
+    if ``expect_pairs`` is given, that the plan for these very pointers agrees. Returns the
+    outputs in run_gpu's order."""
+    offset, ld = offset or {}, ld or {}
+    g = _gpu(inp)
+    rows, N = inp["x"].shape
+    T = inp["x"].dtype
+    fused = w.op in ("fused_add_rms", "fused_add_ln")
+    names = ROW_TENSORS if fused else ("x", "y")
+    bufs, views = {}, {}
+    for n in names:
+        o, l = offset.get(n, 0), ld.get(n, N)
+        buf = torch.full((64 + o + (rows - 1) * l + N + 64,), float("nan"), dtype=T, device=DEV)
+        views[n] = buf.as_strided((rows, N), (l, 1), 64 + o)
+        bufs[n] = buf
+        if n in ("x", "residual"):
+            views[n].copy_(g[n])
+    ptrs = {n: views[n].data_ptr() for n in names}
+    strides = {n: ld.get(n, N) for n in names}
+    if "gamma" in g:
+        ptrs["gamma"] = g["gamma"].data_ptr()
+    st, info = rn.plan(w.op, rows, N, T, ptrs=ptrs, strides=strides, variant=variant)
+    assert st == 0, st
+    if expect_pairs is not None:
+        assert info["variant"] == "element" and info["pairs"] == expect_pairs, info
+    x, y = views["x"], views["y"]
+    if w.op == "ln":
+        out = rn.ln_forward(x, g.get("gamma"), g.get("beta"), w.eps, out=y, return_stats=True,
+                            variant=variant) + (None,)
+    elif w.op == "rms":
+        yy, rstd = rn.rms_norm(x, g.get("weight"), w.eps, out=y, return_rstd=True, variant=variant)
+        out = (yy, None, rstd, None)
+    elif w.op == "fused_add_rms":
+        yy, ro, rstd = rn.fused_add_rms_norm(x, views["residual"], g.get("weight"), w.eps, out=y,
+                                             residual_out=views["residual_out"], return_rstd=True, variant=variant)
+        out = (yy, ro, rstd, None)
+    elif w.op == "fused_add_ln":
+        yy, ro, mean, rstd = rn.fused_add_layer_norm(x, views["residual"], g.get("gamma"), g.get("beta"), w.eps,
+                                                     out=y, residual_out=views["residual_out"], return_stats=True,
+                                                     variant=variant)
+        out = (yy, ro, rstd, mean)
+    else:
+        yy, mx, sm = rn.softmax_forward(x, out=y, return_stats=True, variant=variant)
+        out = (yy, None, sm, mx)
+    torch.cuda.synchronize()
+    for n in ("y", "residual_out"):
+        if n not in views:
+            continue
+        inside = torch.zeros(bufs[n].shape, dtype=torch.bool, device=DEV)
+        inside.as_strided((rows, N), (strides[n], 1), 64 + offset.get(n, 0)).fill_(True)
+        assert torch.isnan(bufs[n][~inside]).all(), f"{n}: written outside its rows"
+    return out
+
+
 @pytest.mark.parametrize("op", ["ln", "rms", "fused_add_rms", "fused_add_ln", "softmax"])
 def test_element_kernel_every_width(op):
-    # the element kernel's (W, V) instances: W = 1 with V = 1..8, W = 2..16 with V = 8, W = 16 with V = 16
+    # the element kernel's (W, V) instances: W = 1 with V = 1..8, W = 2..16 with V = 8, W = 16 with V = 16;
+    # 16-bit rows take it when their tensors sit at different positions in 4-byte words
+    # (here: x one element off), else they move as element pairs
     for rows, N in [(5, 33), (4, 100), (3, 300), (6, 511), (5, 1000), (3, 2047), (2, 4093), (2, 8191),
                     (2, 12289), (2, 16384)]:
-        check_case(BASES[op].scaled(rows=rows, N=N, seed=710 + N, dtype="bf16"), "element")
+        check_case(BASES[op].scaled(rows=rows, N=N, seed=710 + N, dtype="fp32"), "element")
+        w = BASES[op].scaled(rows=rows, N=N, seed=710 + N, dtype="bf16")
+        inp = workloads.make_inputs(w)
+        out = run_placed(w, inp, offset={"x": 1}, variant="element", expect_pairs=False)
+        check_outputs(w, run_oracle(w, inp), *out)
+
+
+@pytest.mark.parametrize("op", ["ln", "rms", "fused_add_rms", "fused_add_ln", "softmax"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_pair_kernel_every_width(op, dtype):
+    # the pair kernel's (W, V) instances: W = 1 with V = 1, 2, 4, 8; W = 2, 4, 8, 16 with V = 8.
+    # Odd N: every other row starts in the upper half of a 4-byte word.
+    for rows, N in [(5, 33), (4, 201), (3, 301), (6, 1001), (3, 1002), (5, 2045), (3, 4093), (3, 4094),
+                    (2, 8191), (2, 12289), (2, 16383)]:
+        w = BASES[op].scaled(rows=rows, N=N, seed=740 + N, dtype=dtype)
+        assert rn.plan(op, rows, N, TD[dtype])[1]["pairs"]
+        check_case(w)
+    # 16384 elements whose rows all start on a word: exactly the 8192 words of W = 16, V = 8
+    w = BASES[op].scaled(rows=3, N=16384, seed=741, dtype=dtype)
+    assert rn.plan(op, 3, 16384, TD[dtype], variant="element")[1]["pairs"]
+    check_case(w, "element")
+
+
+@pytest.mark.parametrize("op", ["ln", "rms", "fused_add_rms", "fused_add_ln", "softmax"])
+def test_pair_kernel_offsets_strides_and_guards(op):
+    # rows starting in the upper half of a word from row 0 on, odd and even strides; nothing
+    # outside the output rows written (NaN guards); mismatched tensors fall back to single
+    # elements
+    for N in (33, 1000, 4095):
+        w = BASES[op].scaled(rows=7, N=N, seed=750 + N, dtype="bf16")
+        inp = workloads.make_inputs(w)
+        ref = run_oracle(w, inp)
+        all_one = {n: 1 for n in ROW_TENSORS}
+        cases = [
+            (all_one, None, True),
+            ({"x": 3, "y": 1, "residual": 5, "residual_out": 7}, None, True),
+            (None, {n: N + 1 for n in ROW_TENSORS}, True),
+            (all_one, {"x": N + 3, "y": N + 1, "residual": N + 5, "residual_out": N + 1}, True),
+            ({"y": 1}, None, False),
+            (None, {"x": N + 1, "y": N + 2}, False),
+        ]
+        for off, ld, pairs in cases:
+            out = run_placed(w, inp, offset=off, ld=ld, expect_pairs=pairs)
+            check_outputs(w, ref, *out)
 
 
 def test_zero_rows_is_a_noop():
