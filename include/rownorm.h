@@ -52,9 +52,11 @@
  *     by one 64-lane wavefront (rows of up to 4 KiB, or 16 KiB when forced) or by a group of
  *     up to 16 wavefronts (rows of up to 64 KiB: 16384 fp32 or 32768 fp16 / bf16 elements).
  *     Otherwise rows of up to 16384 elements are held in registers one element per slot
- *     (the element kernel, still one read of x). Longer rows of whole chunks take the
- *     split-row kernels when rn_forward_ex is given a workspace; all others take a general
- *     kernel that reads the row up to three times.
+ *     (the element kernel, still one read of x; 16-bit rows whose tensors share their
+ *     position within 4-byte words move as element pairs). Longer rows take the split-row
+ *     kernels (whole-chunk rows: 16-byte chunks; other rows: elements) when rn_forward_ex is
+ *     given a workspace; without one they take a general kernel that reads the row up to
+ *     three times.
  *   - Launches use the current HIP device (the device of the buffers and of `stream`). The
  *     first call of a kernel configuration on a device queries its occupancy once.
  */
@@ -83,8 +85,8 @@ typedef enum rn_status {
     RN_ERR_UNSUPPORTED = 5,   /* a forced kernel variant cannot run this shape / alignment */
     RN_ERR_HIP = 6,           /* the HIP runtime reported an error at launch */
     RN_ERR_ALIGN = 7,         /* a pointer is not aligned to its element size */
-    RN_ERR_WORKSPACE = 8      /* the backward workspace is missing or smaller than
-                                 rn_backward_workspace_bytes() */
+    RN_ERR_WORKSPACE = 8      /* a required workspace is missing or smaller than
+                                 rn_backward_workspace_bytes() / rn_forward_workspace_bytes() */
 } rn_status;
 
 /* Kernel variants (for rn_*_variant entry points and rn_plan). */
@@ -95,9 +97,13 @@ typedef enum rn_variant {
     RN_VARIANT_GENERAL = 3,   /* any N, any element-aligned pointers; re-reads the row */
     RN_VARIANT_ELEMENT = 4,   /* rows up to 16384 elements held in VGPRs one element per slot;
                                  any element-aligned pointers and strides */
-    RN_VARIANT_WIDE = 5       /* rows longer than RN_VARIANT_WORKGROUP holds (whole 16-byte
+    RN_VARIANT_WIDE = 5,      /* rows longer than RN_VARIANT_WORKGROUP holds (whole 16-byte
                                  chunks): split into 32 KiB segments, one workgroup each, in two
                                  launches; needs a workspace (rn_forward_ex) */
+    RN_VARIANT_WIDE_ELEMENT = 6 /* rows of more than 16384 elements with any element-aligned
+                                 pointers and strides: split into segments of 8192 elements (one
+                                 per register slot), one workgroup each, in two launches; needs a
+                                 workspace (rn_forward_ex) */
 } rn_variant;
 
 /* Operation codes (for rn_forward_ex and rn_plan). */
@@ -174,10 +180,11 @@ int softmax_forward(const void* x, void* y, float* row_max, float* row_sum, int6
  *              beta, residual, residual_out, eps; mean / rstd are row_max / row_sum).
  *   strides    nullable (all rows dense); see rn_row_strides.
  *   variant    an rn_variant; RN_VARIANT_AUTO chooses as the plain entry points do, except
- *              that rows too long for one workgroup's registers take RN_VARIANT_WIDE when a
- *              large enough workspace is given. A forced variant that cannot run the shape /
- *              alignment returns RN_ERR_UNSUPPORTED (RN_VARIANT_WIDE without a workspace:
- *              RN_ERR_WORKSPACE).
+ *              that rows too long for one workgroup's registers take RN_VARIANT_WIDE (whole
+ *              16-byte chunks) or RN_VARIANT_WIDE_ELEMENT (any other rows of more than 16384
+ *              elements) when a large enough workspace is given. A forced variant that cannot
+ *              run the shape / alignment returns RN_ERR_UNSUPPORTED (the split-row variants
+ *              without a large enough workspace: RN_ERR_WORKSPACE).
  *   workspace  nullable device memory of workspace_bytes, 16-byte aligned, owned by the
  *              caller, overlapping no other argument: per-segment statistics of the split-row
  *              path (rn_forward_workspace_bytes). Contents on entry do not matter; calls that
@@ -193,9 +200,9 @@ int rn_forward_ex(int op, const void* x, const void* residual, const void* gamma
                   const rn_row_strides* strides, int variant, void* workspace, size_t workspace_bytes,
                   hipStream_t stream);
 
-/* Workspace bytes rn_forward_ex needs for the split-row path of this shape: rows *
- * ceil(N * sizeof(dtype) / 32768) * 16 when rows are whole 16-byte chunks longer than a
- * workgroup holds (more than 16384 fp32 or 32768 fp16 / bf16 elements), else 0. */
+/* Workspace bytes rn_forward_ex needs for the split-row paths of this shape: rows *
+ * ceil(N / 8192) * 16 when N > 16384 (enough for either split-row variant, whatever the
+ * alignment), else 0 (such rows are never split). */
 size_t rn_forward_workspace_bytes(int op, int64_t rows, int64_t N, int dtype);
 
 /* Same as the first three entry points above, with the kernel variant forced (RN_VARIANT_AUTO

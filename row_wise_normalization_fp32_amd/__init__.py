@@ -89,7 +89,7 @@ _lib.rn_plan_backward.argtypes = [_ci, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _
 _lib.rn_plan_backward.restype = _ci
 
 DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
-VARIANTS = {"auto": 0, "wave": 1, "workgroup": 2, "general": 3, "element": 4, "wide": 5}
+VARIANTS = {"auto": 0, "wave": 1, "workgroup": 2, "general": 3, "element": 4, "wide": 5, "wide_element": 6}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 OPS = {"ln": 0, "rms": 1, "fused_add_rms": 2, "fused_add_ln": 3, "softmax": 4}
 STATUS = {0: "RN_OK", 1: "RN_ERR_NULL", 2: "RN_ERR_SHAPE", 3: "RN_ERR_DTYPE", 4: "RN_ERR_ALIAS",
@@ -202,9 +202,12 @@ def _call(op: str, what: str, x, residual, gamma, beta, y, ro, mean, rstd, rows,
     st_obj = _NO_STRIDES if not any(strides) else RowStrides(*strides)
     v = _variant(variant)
     ws_bytes = 0
-    if N * _ELEM_BYTES[x.dtype] > 65536:  # only rows beyond a workgroup's registers use a workspace
+    nb = N * _ELEM_BYTES[x.dtype]
+    # only rows beyond a workgroup's registers use a workspace (rows of whole 16-byte chunks
+    # up to 64 KiB, and any rows up to 16384 elements, never do)
+    if N > 16384 and (nb > 65536 or nb % 16 != 0):
         need = forward_workspace_bytes(op, rows, N, x.dtype)
-        if need and workspace is None and v in (VARIANTS["auto"], VARIANTS["wide"]):
+        if need and workspace is None and v in (VARIANTS["auto"], VARIANTS["wide"], VARIANTS["wide_element"]):
             workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     if workspace is not None:
         ws_bytes = workspace.numel() * workspace.element_size()

@@ -66,13 +66,17 @@ struct Args {
     size_t ws_bytes;
 };
 
-// Split-row path: rows of whole 16-byte chunks that are longer than a workgroup's registers.
+// Split-row paths: rows longer than a workgroup's registers hold. Segments of 2048 16-byte
+// chunks (whole-chunk rows) or of 8192 elements (any rows); one 16-byte record per segment.
 int64_t wide_segments(int64_t C) { return (C + rn::kWideSegChunks - 1) / rn::kWideSegChunks; }
+int64_t wide_elem_segments(int64_t N) { return (N + rn::kWideElemSeg - 1) / rn::kWideElemSeg; }
 
-size_t wide_workspace_bytes(int64_t rows, int64_t N, int64_t s) {
-    const int64_t group_cap = int64_t(64) * rn::kMaxGroupWaves * rn::kMaxGroupChunks;
-    if (rows <= 0 || N <= 0 || (N * s) % 16 != 0 || N * s / 16 <= group_cap) return 0;
-    return static_cast<size_t>(rows * wide_segments(N * s / 16) * 16);
+// Workspace for either split-row path (the element segmentation has at least as many
+// segments); 0 for rows of up to 16384 elements, which the automatic choice never splits.
+size_t wide_workspace_bytes(int64_t rows, int64_t N) {
+    const int64_t elem_cap = int64_t(64) * rn::kMaxGroupWaves * rn::kElemMaxPerLane;
+    if (rows <= 0 || N <= elem_cap) return 0;
+    return static_cast<size_t>(rows * wide_elem_segments(N) * 16);
 }
 
 // Validates the arguments (dropping pointers the operation does not use) and chooses the
@@ -80,7 +84,7 @@ size_t wide_workspace_bytes(int64_t rows, int64_t N, int64_t s) {
 int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_t* chunks) {
     if (a.dtype != RN_F32 && a.dtype != RN_F16 && a.dtype != RN_BF16) return RN_ERR_DTYPE;
     if (a.op < RN_OP_LAYER_NORM || a.op > RN_OP_SOFTMAX) return RN_ERR_SHAPE;
-    if (a.variant < RN_VARIANT_AUTO || a.variant > RN_VARIANT_WIDE) return RN_ERR_UNSUPPORTED;
+    if (a.variant < RN_VARIANT_AUTO || a.variant > RN_VARIANT_WIDE_ELEMENT) return RN_ERR_UNSUPPORTED;
     const int64_t s = a.dtype == RN_F32 ? 4 : 2;
     const int64_t rows = a.rows, N = a.N;
     if (rows < 0 || N <= 0) return RN_ERR_SHAPE;
@@ -154,7 +158,7 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     }
 
     // The split-row workspace (only looked at when it is needed: see below).
-    const size_t ws_need = wide_workspace_bytes(rows, N, s);
+    const size_t ws_need = wide_workspace_bytes(rows, N);
     const bool ws_given = a.ws != nullptr && ws_need > 0 && a.ws_bytes >= ws_need;
     if (ws_given) {
         if (reinterpret_cast<uintptr_t>(a.ws) % 16 != 0) return RN_ERR_ALIGN;
@@ -189,8 +193,25 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
             v = RN_VARIANT_WIDE;
         else if (N <= elem_cap)
             v = RN_VARIANT_ELEMENT;
+        else if (ws_given)
+            v = RN_VARIANT_WIDE_ELEMENT;
         else
             v = RN_VARIANT_GENERAL;
+    }
+    if (v == RN_VARIANT_WIDE_ELEMENT) {
+        if (N <= elem_cap) return RN_ERR_UNSUPPORTED;
+        if (!ws_given) return RN_ERR_WORKSPACE;
+        const int64_t S = wide_elem_segments(N);
+        if (S > INT32_MAX) return RN_ERR_UNSUPPORTED;
+        plan->variant = rn::V_WIDE_ELEM;
+        plan->waves_per_row = 8;  // per segment
+        plan->rows_per_block = 1;
+        plan->chunks_per_lane = rn::kWideElemSeg / 512;  // elements per lane
+        plan->block_threads = 512;
+        plan->grid = rows * S < rn::kMaxGrid ? rows * S : rn::kMaxGrid;
+        plan->exact = N % rn::kWideElemSeg == 0;
+        *chunks = C;
+        return RN_OK;
     }
     if (v == RN_VARIANT_WIDE) {
         if (!vec_ok || C <= group_cap) return RN_ERR_UNSUPPORTED;
@@ -310,8 +331,8 @@ int run(Args a, const rn_row_strides* strides, hipStream_t stream) {
     // Persistent vectorized launches have instances of their own (parameters staged on
     // chip); the element kernel is the same instance in both launch modes.
     const bool pers_vec = plan.persistent && plan.variant != rn::V_ELEMENT;
-    if (plan.variant == rn::V_WIDE) {
-        rn::WideArgs wa{a.ws, static_cast<int>(wide_segments(C))};
+    if (plan.variant == rn::V_WIDE || plan.variant == rn::V_WIDE_ELEM) {
+        rn::WideArgs wa{a.ws, static_cast<int>(plan.variant == rn::V_WIDE ? wide_segments(C) : wide_elem_segments(a.N))};
         hipError_t e = hipErrorInvalidValue;
         switch (a.dtype) {
         case RN_F32: e = rn::launch_wide_f32(a.op, plan, p, wa, stream); break;
@@ -548,7 +569,7 @@ int rn_forward_ex(int op, const void* x, const void* residual, const void* gamma
 size_t rn_forward_workspace_bytes(int op, int64_t rows, int64_t N, int dtype) {
     if (op < RN_OP_LAYER_NORM || op > RN_OP_SOFTMAX) return 0;
     if (dtype != RN_F32 && dtype != RN_F16 && dtype != RN_BF16) return 0;
-    return wide_workspace_bytes(rows, N, dtype == RN_F32 ? 4 : 2);
+    return wide_workspace_bytes(rows, N);
 }
 
 int ln_forward_variant(const void* x, const void* gamma, const void* beta, void* y, float* mean, float* rstd,

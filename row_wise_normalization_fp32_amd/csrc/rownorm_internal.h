@@ -12,7 +12,7 @@ namespace rn {
 
 enum Op { OP_LN = 0, OP_RMS = 1, OP_FUSED = 2, OP_FUSED_LN = 3, OP_SOFTMAX = 4 };
 enum Dt { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
-enum Variant { V_AUTO = 0, V_WAVE = 1, V_WORKGROUP = 2, V_GENERAL = 3, V_ELEMENT = 4, V_WIDE = 5 };
+enum Variant { V_AUTO = 0, V_WAVE = 1, V_WORKGROUP = 2, V_GENERAL = 3, V_ELEMENT = 4, V_WIDE = 5, V_WIDE_ELEM = 6 };
 
 // Kernel arguments, passed by value. Pointers are device pointers; nullable ones are
 // documented in include/rownorm.h.
@@ -67,7 +67,7 @@ struct BwdColParams {
 
 // Launch geometry chosen on the host.
 struct Plan {
-    int variant;          // V_WAVE, V_WORKGROUP, V_ELEMENT or V_GENERAL
+    int variant;          // a Variant other than V_AUTO
     int waves_per_row;    // W: wavefronts that share one row
     int rows_per_block;   // RPB: row groups per workgroup
     int chunks_per_lane;  // V: 16-byte chunks (vectorized variants) or elements (element
@@ -94,6 +94,7 @@ constexpr int kElemCuRowBytes = 32768; // element kernels, persistent: row bytes
 constexpr int64_t kMaxGrid = 1 << 20;  // grid cap; kernels loop over the remaining rows
 constexpr int64_t kPersistentBlocks = 2048;  // at least this many workgroups: persistent launch
 constexpr int kWideSegChunks = 2048;   // split-row variant: 16-byte chunks per segment (one workgroup)
+constexpr int kWideElemSeg = 8192;     // split-row element variant: elements per segment (one workgroup)
 constexpr int kBwdMaxParts = 1024;     // backward: at most this many partial column rows (workspace bound)
 constexpr int kBwdTargetChunks = 2;    // backward: about 2 chunks of x and of dy per lane (1 measured slower)
 

@@ -117,11 +117,13 @@ struct Io<DT_F32> {
     }
     __device__ static __forceinline__ void store1(void* p, int64_t i, float v) { static_cast<float*>(p)[i] = v; }
     __device__ static __forceinline__ float round(float v) { return v; }
+    template <int CP = 0>
     __device__ static __forceinline__ float bload(Rsrc r, uint32_t j) {
-        return bit_cast<float>(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(j * 4), 0, 0));
+        return bit_cast<float>(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(j * 4), 0, CP));
     }
+    template <int CP = 0>
     __device__ static __forceinline__ void bstore(Rsrc r, uint32_t j, float v) {
-        __builtin_amdgcn_raw_buffer_store_b32(bit_cast<unsigned>(v), r, static_cast<int>(j * 4), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(bit_cast<unsigned>(v), r, static_cast<int>(j * 4), 0, CP);
     }
 };
 
@@ -164,13 +166,15 @@ struct Io<DT_F16> {
         static_cast<_Float16*>(p)[i] = static_cast<_Float16>(v);
     }
     __device__ static __forceinline__ float round(float v) { return static_cast<float>(static_cast<_Float16>(v)); }
+    template <int CP = 0>
     __device__ static __forceinline__ float bload(Rsrc r, uint32_t j) {
         return static_cast<float>(
-            bit_cast<_Float16>(__builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(j * 2), 0, 0)));
+            bit_cast<_Float16>(__builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(j * 2), 0, CP)));
     }
+    template <int CP = 0>
     __device__ static __forceinline__ void bstore(Rsrc r, uint32_t j, float v) {
         __builtin_amdgcn_raw_buffer_store_b16(bit_cast<unsigned short>(static_cast<_Float16>(v)), r,
-                                              static_cast<int>(j * 2), 0, 0);
+                                              static_cast<int>(j * 2), 0, CP);
     }
     // two adjacent elements held in one 32-bit word, the lower-addressed one in the low half
     __device__ static __forceinline__ f32x2 widen_pair(unsigned u) { return widen2(u); }
@@ -214,26 +218,31 @@ struct Io<DT_BF16> {
         static_cast<unsigned short*>(p)[i] = static_cast<unsigned short>(narrow2(v, v));
     }
     __device__ static __forceinline__ float round(float v) { return lo(narrow2(v, v)); }
+    template <int CP = 0>
     __device__ static __forceinline__ float bload(Rsrc r, uint32_t j) {
-        return lo(__builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(j * 2), 0, 0));
+        return lo(__builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(j * 2), 0, CP));
     }
+    template <int CP = 0>
     __device__ static __forceinline__ void bstore(Rsrc r, uint32_t j, float v) {
         __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(narrow2(v, v)), r, static_cast<int>(j * 2),
-                                              0, 0);
+                                              0, CP);
     }
     __device__ static __forceinline__ f32x2 widen_pair(unsigned u) { return f32x2{lo(u), hi(u)}; }
 };
 
 // 32-bit and 16-bit buffer accesses at a byte offset (out of range: loads read 0, stores
-// are dropped).
+// are dropped). CP is the instruction's cache-policy field (2: non-temporal).
+template <int CP = 0>
 __device__ __forceinline__ unsigned bload32(Rsrc r, uint32_t off) {
-    return static_cast<unsigned>(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0));
+    return static_cast<unsigned>(__builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, CP));
 }
+template <int CP = 0>
 __device__ __forceinline__ void bstore32(Rsrc r, uint32_t off, unsigned v) {
-    __builtin_amdgcn_raw_buffer_store_b32(v, r, static_cast<int>(off), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, static_cast<int>(off), 0, CP);
 }
+template <int CP = 0>
 __device__ __forceinline__ void bstore16(Rsrc r, uint32_t off, unsigned v) {
-    __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(v), r, static_cast<int>(off), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(v), r, static_cast<int>(off), 0, CP);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1130,6 +1139,50 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_pair_kernel(Params p) {
     }
 }
 
+// The S segment records of a split row, combined by one wave: lane k takes records k, k + 64,
+// ... in that order, then the 64 lane results meet in a butterfly whose every step combines
+// (lower lane, upper lane) in that order. All lanes, waves and workgroups of the row so get
+// the same bits, and the records are read in parallel (one load per lane for S <= 64)
+// instead of one after another.
+//   LayerNorm records (n, R, mean - R, M2): returns (R0, mean - R0, M2, n) with R0 = record 0's R.
+//   Softmax records (max, sum): returns (max, sum).  RMSNorm records (sum of squares): (sum).
+template <int OP>
+__device__ __forceinline__ float4 combine_records(const float4* rec, int S, int lane) {
+    using OT = OpTraits<OP>;
+    if constexpr (OT::LN) {
+        const float R0 = rec[0].y;
+        Moments acc{0.f, 0.f, 0.f};
+        for (int k = lane; k < S; k += 64) {
+            const float4 r = rec[k];
+            acc = combine(acc, Moments{r.x, (r.y - R0) + r.z, r.w});
+        }
+#pragma unroll
+        for (int step = 1; step < 64; step <<= 1) {
+            const Moments o{__shfl_xor(acc.n, step), __shfl_xor(acc.m, step), __shfl_xor(acc.m2, step)};
+            acc = (lane & step) ? combine(o, acc) : combine(acc, o);
+        }
+        return make_float4(R0, acc.m, acc.m2, acc.n);
+    } else if constexpr (OT::SM) {
+        float m = -INFINITY, s = 0.f;
+        for (int k = lane; k < S; k += 64) {
+            const float4 r = rec[k];
+            softmax_combine(m, s, r.x, r.y);
+        }
+#pragma unroll
+        for (int step = 1; step < 64; step <<= 1) {
+            const float mo = __shfl_xor(m, step), so = __shfl_xor(s, step);
+            softmax_combine(m, s, mo, so);  // symmetric in its two sides, bit for bit
+        }
+        return make_float4(m, s, 0.f, 0.f);
+    } else {
+        float q = 0.f;
+        for (int k = lane; k < S; k += 64) q += rec[k].x;
+#pragma unroll
+        for (int step = 1; step < 64; step <<= 1) q += __shfl_xor(q, step);  // a + b == b + a
+        return make_float4(q, 0.f, 0.f, 0.f);
+    }
+}
+
 // ---------------------------------------------------------------------------------------
 // Split-row kernels: rows too long for one workgroup's registers (the walkthrough's
 // section 1.1 case of a row that outgrows one block), with 16-byte chunks. A row is cut into
@@ -1302,36 +1355,26 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_norm_kernel(Params p,
             if constexpr (HG) gv[i] = static_cast<const u32x4*>(p.gamma)[chunk(i)];
             if constexpr (HB) bv[i] = static_cast<const u32x4*>(p.beta)[chunk(i)];
         }
-        // combine the row's segment records in order 0, 1, ..., S - 1 (same bits everywhere)
-        const float4* rec = static_cast<const float4*>(wa.ws) + row * wa.S;
+        // combine the row's segment records (same bits in every workgroup of the row)
+        const float4 tot = combine_records<OP>(static_cast<const float4*>(wa.ws) + row * wa.S, wa.S, t & 63);
         float scale, offset = 0.f, R0 = 0.f;
         if constexpr (OT::LN) {
-            const float4 r0 = rec[0];
-            R0 = r0.y;
-            Moments acc{r0.x, r0.z, r0.w};  // mean relative to R0
-            for (int k = 1; k < wa.S; ++k) {
-                const float4 r = rec[k];
-                acc = combine(acc, Moments{r.x, (r.y - R0) + r.z, r.w});
-            }
-            scale = inv_sqrt(fmaf(acc.m2, p.inv_n, p.eps));
-            offset = -acc.m * scale;
+            R0 = tot.x;
+            scale = inv_sqrt(fmaf(tot.z, p.inv_n, p.eps));
+            offset = -tot.y * scale;
             if (seg == 0 && t == 0) {
-                if (p.mean) p.mean[row] = R0 + acc.m;
+                if (p.mean) p.mean[row] = R0 + tot.y;
                 if (p.rstd) p.rstd[row] = scale;
             }
         } else if constexpr (OT::SM) {
-            float M = rec[0].x, Ssum = rec[0].y;
-            for (int k = 1; k < wa.S; ++k) softmax_combine(M, Ssum, rec[k].x, rec[k].y);
-            R0 = M;
-            scale = 1.0f / Ssum;
+            R0 = tot.x;
+            scale = 1.0f / tot.y;
             if (seg == 0 && t == 0) {
-                if (p.mean) p.mean[row] = M;
-                if (p.rstd) p.rstd[row] = Ssum;
+                if (p.mean) p.mean[row] = tot.x;
+                if (p.rstd) p.rstd[row] = tot.y;
             }
         } else {
-            float sq = rec[0].x;
-            for (int k = 1; k < wa.S; ++k) sq += rec[k].x;
-            scale = inv_sqrt(fmaf(sq, p.inv_n, p.eps));
+            scale = inv_sqrt(fmaf(tot.x, p.inv_n, p.eps));
             if (seg == 0 && t == 0 && p.rstd) p.rstd[row] = scale;
         }
         u32x4* yr = static_cast<u32x4*>(p.y) + row * p.cy;
@@ -1361,6 +1404,175 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_norm_kernel(Params p,
                 o[e] = z;
             }
             if (valid(i)) __builtin_nontemporal_store(IO::pack(o), yr + chunk(i));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Split-row element kernels: the same two launches for long rows that are not whole 16-byte
+// chunks (ragged N, unaligned tensors, strides that are not whole chunks). A segment is
+// kWideElemSeg elements, one per register slot (kWideEV slots per lane, element i * 512 + t
+// of the segment); every tensor of the segment is read and written through a buffer
+// resource bounded by the segment, so slots past the row's end read 0 and write nothing.
+// ---------------------------------------------------------------------------------------
+
+constexpr int kWideEV = kWideElemSeg / kWideLanes;  // 16 elements per lane
+static_assert(kWideEV * kWideLanes == kWideElemSeg, "element segment = 512 lanes x kWideEV");
+
+template <int DT, int OP>
+__global__ __launch_bounds__(kWideLanes) void rownorm_wide_elem_stats_kernel(Params p, WideArgs wa) {
+    using IO = Io<DT>;
+    using OT = OpTraits<OP>;
+    constexpr int V = kWideEV;
+    constexpr int S = DT == DT_F32 ? 4 : 2;
+    const int lane = threadIdx.x & 63;
+    const int wr = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int t = threadIdx.x;
+    __shared__ WavePart part[2][kWideW];
+    int buf = 0;
+    const int64_t total = p.rows * wa.S;
+    for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+        const int64_t row = b / wa.S;
+        const int seg = static_cast<int>(b - row * wa.S);
+        const int64_t e0 = static_cast<int64_t>(seg) * kWideElemSeg;
+        const int Ns = static_cast<int>(p.N - e0 < kWideElemSeg ? p.N - e0 : kWideElemSeg);  // elements here
+        const uint32_t nb = static_cast<uint32_t>(Ns * S);
+        auto valid = [&](int i) { return i * kWideLanes + t < Ns; };
+        // temporal loads and stores: the second launch reads the same bytes again
+        const Rsrc xr = make_rsrc(static_cast<const char*>(p.x) + (row * p.ldx + e0) * S, nb);
+        float f[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) f[i] = IO::bload(xr, static_cast<uint32_t>(i * kWideLanes + t));
+        if constexpr (OT::RES) {
+            const Rsrc rr = make_rsrc(static_cast<const char*>(p.residual) + (row * p.ldr + e0) * S, nb);
+            float r[V];
+#pragma unroll
+            for (int i = 0; i < V; ++i) r[i] = IO::bload(rr, static_cast<uint32_t>(i * kWideLanes + t));
+            const Rsrc orr = make_rsrc(static_cast<char*>(p.residual_out) + (row * p.ldro + e0) * S, nb);
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                f[i] = IO::round(f[i] + r[i]);
+                IO::bstore(orr, static_cast<uint32_t>(i * kWideLanes + t), f[i]);
+            }
+        }
+        int cnt = 0;  // elements of this wave
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            const int k = Ns - (i * kWideLanes + wr * 64);
+            cnt += k <= 0 ? 0 : (k >= 64 ? 64 : k);
+        }
+        const float n_w = static_cast<float>(cnt);
+        float4 rec;
+        if constexpr (OT::LN) {
+            const float K = uniform(f[0]);  // 0 when the wave holds no element
+            float s1 = 0.f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) s1 += valid(i) ? f[i] - K : 0.f;
+            const float inv_w = n_w > 0.f ? 1.0f / n_w : 0.f;
+            const float a = K + wave_sum(s1) * inv_w;
+            float c = 0.f, q = 0.f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                const float d = valid(i) ? f[i] - a : 0.f;
+                c += d;
+                q = fmaf(d, d, q);
+            }
+            const float Cw = wave_sum(c), Qw = wave_sum(q);
+            const float cw = Cw * inv_w;
+            float rel, m2, mean;
+            group_moments<kWideW, false>(part, buf, lane, wr, n_w, a, cw, fmaxf(Qw - Cw * cw, 0.f), rel, m2, mean);
+            rec = make_float4(static_cast<float>(Ns), a, rel, m2);  // wave 0 (a == R) writes it
+        } else if constexpr (OT::SM) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < V; ++i) mx = valid(i) ? fmaxf(mx, f[i]) : mx;
+            const float mw = wave_max(mx);
+            float sm = 0.f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) sm += valid(i) ? exp_neg(f[i] - mw) : 0.f;
+            float M, Ssum;
+            group_softmax<kWideW>(part, buf, lane, wr, mw, wave_sum(sm), M, Ssum);
+            rec = make_float4(M, Ssum, 0.f, 0.f);
+        } else {
+            float sq = 0.f;
+#pragma unroll
+            for (int i = 0; i < V; ++i) sq = fmaf(f[i], f[i], sq);  // slots past the row hold 0
+            rec = make_float4(group_sum<kWideW>(part, buf, lane, wr, wave_sum(sq)), 0.f, 0.f, 0.f);
+        }
+        if (t == 0) static_cast<float4*>(wa.ws)[row * wa.S + seg] = rec;
+    }
+}
+
+template <int DT, int OP, int AFF>
+__global__ __launch_bounds__(kWideLanes) void rownorm_wide_elem_norm_kernel(Params p, WideArgs wa) {
+    using IO = Io<DT>;
+    using OT = OpTraits<OP>;
+    constexpr int V = kWideEV;
+    constexpr int S = DT == DT_F32 ? 4 : 2;
+    constexpr bool HG = !OT::SM && (AFF & AFF_G) != 0;
+    constexpr bool HB = OT::LN && (AFF & AFF_B) != 0;
+    const int t = threadIdx.x;
+    const int64_t total = p.rows * wa.S;
+    for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+        const int64_t row = b / wa.S;
+        const int seg = static_cast<int>(b - row * wa.S);
+        const int64_t e0 = static_cast<int64_t>(seg) * kWideElemSeg;
+        const int Ns = static_cast<int>(p.N - e0 < kWideElemSeg ? p.N - e0 : kWideElemSeg);
+        const uint32_t nb = static_cast<uint32_t>(Ns * S);
+        // the segment's data (x, or residual_out for the fused ops) and parameters
+        const Rsrc sr = OT::RES ? make_rsrc(static_cast<const char*>(p.residual_out) + (row * p.ldro + e0) * S, nb)
+                                : make_rsrc(static_cast<const char*>(p.x) + (row * p.ldx + e0) * S, nb);
+        const Rsrc gr = make_rsrc(HG ? static_cast<const char*>(p.gamma) + e0 * S : nullptr, HG ? nb : 0);
+        const Rsrc br = make_rsrc(HB ? static_cast<const char*>(p.beta) + e0 * S : nullptr, HB ? nb : 0);
+        float f[V], g[HG ? V : 1], bb[HB ? V : 1];
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            const uint32_t j = static_cast<uint32_t>(i * kWideLanes + t);
+            f[i] = IO::bload(sr, j);
+            if constexpr (HG) g[i] = IO::bload(gr, j);
+            if constexpr (HB) bb[i] = IO::bload(br, j);
+        }
+        // combine the row's segment records (same bits in every workgroup of the row)
+        const float4 tot = combine_records<OP>(static_cast<const float4*>(wa.ws) + row * wa.S, wa.S, t & 63);
+        float scale, offset = 0.f, R0 = 0.f;
+        if constexpr (OT::LN) {
+            R0 = tot.x;
+            scale = inv_sqrt(fmaf(tot.z, p.inv_n, p.eps));
+            offset = -tot.y * scale;
+            if (seg == 0 && t == 0) {
+                if (p.mean) p.mean[row] = R0 + tot.y;
+                if (p.rstd) p.rstd[row] = scale;
+            }
+        } else if constexpr (OT::SM) {
+            R0 = tot.x;
+            scale = 1.0f / tot.y;
+            if (seg == 0 && t == 0) {
+                if (p.mean) p.mean[row] = tot.x;
+                if (p.rstd) p.rstd[row] = tot.y;
+            }
+        } else {
+            scale = inv_sqrt(fmaf(tot.x, p.inv_n, p.eps));
+            if (seg == 0 && t == 0 && p.rstd) p.rstd[row] = scale;
+        }
+        const Rsrc yr = make_rsrc(static_cast<char*>(p.y) + (row * p.ldy + e0) * S, nb);
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            float z;
+            if constexpr (OT::LN) {
+                z = fmaf(f[i] - R0, scale, offset);
+            } else if constexpr (OT::SM) {
+                z = exp_neg(f[i] - R0) * scale;
+            } else {
+                z = f[i] * scale;
+            }
+            if constexpr (HG && HB) {
+                z = fmaf(z, g[i], bb[i]);
+            } else if constexpr (HG) {
+                z = z * g[i];
+            } else if constexpr (HB) {
+                z = z + bb[i];
+            }
+            IO::bstore(yr, static_cast<uint32_t>(i * kWideLanes + t), z);
         }
     }
 }
@@ -1513,9 +1725,12 @@ constexpr int kMaxDevices = 64;
 // Persistent launch: as many workgroups as the current device keeps resident (queried once
 // per kernel instance and device: the kernel is a template argument, so each instance has
 // its own cache), capped as below, at most one per row group of work.
+// Resident capacity of a kernel instance: CUs and workgroups per CU at this block size and
+// dynamic LDS, queried once per device (per instance: each template instance has its own
+// cache; a benign race writes the same values).
 template <auto KERNEL>
-inline hipError_t go_persistent(const Plan& plan, const Params& p, hipStream_t stream, int row_bytes_per_wave = 0) {
-    static int per_cu_cache[kMaxDevices];  // 0: not yet known; a benign race writes the same value
+inline hipError_t resident(int block_threads, int lds_bytes, int* cus_out, int* per_cu_out) {
+    static int per_cu_cache[kMaxDevices];  // 0: not yet known
     static int cus_cache[kMaxDevices];
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -1523,8 +1738,8 @@ inline hipError_t go_persistent(const Plan& plan, const Params& p, hipStream_t s
     int per_cu = dev < kMaxDevices ? __atomic_load_n(&per_cu_cache[dev], __ATOMIC_RELAXED) : 0;
     int cus = dev < kMaxDevices ? __atomic_load_n(&cus_cache[dev], __ATOMIC_RELAXED) : 0;
     if (per_cu <= 0 || cus <= 0) {
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(KERNEL),
-                                                         plan.block_threads, static_cast<size_t>(plan.lds_bytes));
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(KERNEL), block_threads,
+                                                         static_cast<size_t>(lds_bytes));
         if (e != hipSuccess) return e;
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
@@ -1534,6 +1749,16 @@ inline hipError_t go_persistent(const Plan& plan, const Params& p, hipStream_t s
             __atomic_store_n(&cus_cache[dev], cus, __ATOMIC_RELAXED);
         }
     }
+    *cus_out = cus;
+    *per_cu_out = per_cu;
+    return hipSuccess;
+}
+
+template <auto KERNEL>
+inline hipError_t go_persistent(const Plan& plan, const Params& p, hipStream_t stream, int row_bytes_per_wave = 0) {
+    int cus = 0, per_cu = 0;
+    hipError_t e = resident<KERNEL>(plan.block_threads, plan.lds_bytes, &cus, &per_cu);
+    if (e != hipSuccess) return e;
     // Vectorized workgroups holding 4 chunks per lane: at most two per CU (more rows per
     // workgroup, measured better for fused add + LayerNorm 8192 x 4096: 68.3% -> 70.0%,
     // neutral for the others); smaller rows keep the full resident count for bytes in flight.
@@ -1728,22 +1953,49 @@ inline hipError_t launch_op(const Plan& plan, const Params& p, hipStream_t s) {
 }
 
 // Split-row launches: statistics, then normalization, on the same stream.
-template <int DT, int OP>
-inline hipError_t launch_wide_op(const Plan& plan, const Params& p, const WideArgs& wa, hipStream_t s) {
+// A split-row launch: one workgroup per (row, segment) work item up to the grid cap (a grid
+// of only what the device keeps resident, looping over the work items, measured 5-10%
+// slower on MI355X).
+template <auto KERNEL>
+inline hipError_t go_wide(const Plan& plan, const Params& p, const WideArgs& wa, hipStream_t s) {
+    const int64_t grid = plan.grid;
     Params pa = p;
     WideArgs wb = wa;
     void* argv[] = {&pa, &wb};
-    const dim3 grid(static_cast<unsigned>(plan.grid)), block(kWideLanes);
-    hipError_t e = plan.exact
-        ? hipLaunchKernel(reinterpret_cast<const void*>(rownorm_wide_stats_kernel<DT, OP, true>), grid, block, argv, 0, s)
-        : hipLaunchKernel(reinterpret_cast<const void*>(rownorm_wide_stats_kernel<DT, OP, false>), grid, block, argv, 0, s);
+    return hipLaunchKernel(reinterpret_cast<const void*>(KERNEL), dim3(static_cast<unsigned>(grid)), dim3(kWideLanes),
+                           argv, 0, s);
+}
+
+template <int DT, int OP>
+inline hipError_t launch_wide_elem_op(const Plan& plan, const Params& p, const WideArgs& wa, hipStream_t s) {
+    hipError_t e = go_wide<rownorm_wide_elem_stats_kernel<DT, OP>>(plan, p, wa, s);
     if (e != hipSuccess) return e;
     const int aff = (OpTraits<OP>::SM ? 0 : (p.gamma ? AFF_G : 0)) | (OpTraits<OP>::LN && p.beta ? AFF_B : 0);
-#define RN_WN(A)                                                                                                      \
-    (plan.exact ? hipLaunchKernel(reinterpret_cast<const void*>(rownorm_wide_norm_kernel<DT, OP, true, A>), grid, block, \
-                                  argv, 0, s)                                                                         \
-                : hipLaunchKernel(reinterpret_cast<const void*>(rownorm_wide_norm_kernel<DT, OP, false, A>), grid, block, \
-                                  argv, 0, s))
+#define RN_WEN(A) go_wide<rownorm_wide_elem_norm_kernel<DT, OP, A>>(plan, p, wa, s)
+    if constexpr (OpTraits<OP>::SM) {
+        return RN_WEN(0);
+    } else {
+        if (aff == 0) return RN_WEN(0);
+        if (aff == AFF_G) return RN_WEN(AFF_G);
+        if constexpr (OpTraits<OP>::LN) {
+            if (aff == AFF_B) return RN_WEN(AFF_B);
+            return RN_WEN(AFF_G | AFF_B);
+        }
+        return hipErrorInvalidValue;
+    }
+#undef RN_WEN
+}
+
+template <int DT, int OP>
+inline hipError_t launch_wide_op(const Plan& plan, const Params& p, const WideArgs& wa, hipStream_t s) {
+    if (plan.variant == V_WIDE_ELEM) return launch_wide_elem_op<DT, OP>(plan, p, wa, s);
+    hipError_t e = plan.exact ? go_wide<rownorm_wide_stats_kernel<DT, OP, true>>(plan, p, wa, s)
+                              : go_wide<rownorm_wide_stats_kernel<DT, OP, false>>(plan, p, wa, s);
+    if (e != hipSuccess) return e;
+    const int aff = (OpTraits<OP>::SM ? 0 : (p.gamma ? AFF_G : 0)) | (OpTraits<OP>::LN && p.beta ? AFF_B : 0);
+#define RN_WN(A)                                                                    \
+    (plan.exact ? go_wide<rownorm_wide_norm_kernel<DT, OP, true, A>>(plan, p, wa, s) \
+                : go_wide<rownorm_wide_norm_kernel<DT, OP, false, A>>(plan, p, wa, s))
     if constexpr (OpTraits<OP>::SM) {
         return RN_WN(0);
     } else {
@@ -1760,7 +2012,8 @@ inline hipError_t launch_wide_op(const Plan& plan, const Params& p, const WideAr
 
 template <int DT>
 inline hipError_t launch_wide(int op, const Plan& plan, const Params& p, const WideArgs& wa, hipStream_t s) {
-    if (plan.variant != V_WIDE || wa.ws == nullptr || wa.S < 1) return hipErrorInvalidValue;
+    if ((plan.variant != V_WIDE && plan.variant != V_WIDE_ELEM) || wa.ws == nullptr || wa.S < 1)
+        return hipErrorInvalidValue;
     switch (op) {
     case OP_LN: return launch_wide_op<DT, OP_LN>(plan, p, wa, s);
     case OP_RMS: return launch_wide_op<DT, OP_RMS>(plan, p, wa, s);

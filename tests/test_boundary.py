@@ -325,21 +325,38 @@ def test_backward_entry_points_reject_before_launch():
 
 def test_plan_split_rows():
     f32, bf16 = torch.float32, torch.bfloat16
+    # one 16-byte record per 8192-element segment (enough for both split-row variants)
     need = rn.forward_workspace_bytes("ln", 64, 65536, f32)
-    assert need == 64 * 8 * 16  # 16384 chunks = 8 segments of 2048, one float4 each
+    assert need == 64 * 8 * 16
     assert rn.forward_workspace_bytes("ln", 64, 16384, f32) == 0  # fits one workgroup
-    assert rn.forward_workspace_bytes("ln", 64, 32768, bf16) == 0
-    assert rn.forward_workspace_bytes("ln", 64, 32776, bf16) == 64 * 3 * 16
-    assert rn.forward_workspace_bytes("ln", 64, 65537, bf16) == 0  # not whole chunks
+    assert rn.forward_workspace_bytes("ln", 64, 16385, bf16) == 64 * 3 * 16
+    assert rn.forward_workspace_bytes("ln", 64, 65537, bf16) == 64 * 9 * 16
+    assert rn.forward_workspace_bytes("ln", 0, 65536, f32) == 0
+    # whole 16-byte chunks: segments of 2048 chunks
     st, info = rn.plan("ln", 64, 65536, f32, workspace_bytes=need)
     assert st == OK and info["variant"] == "wide" and info["grid_blocks"] == 64 * 8 and info["exact"]
-    st, info = rn.plan("softmax", 8, 32776, bf16, workspace_bytes=8 * 3 * 16)
-    assert st == OK and info["variant"] == "wide" and not info["exact"]
+    st, info = rn.plan("softmax", 8, 32776, bf16, workspace_bytes=8 * 5 * 16)
+    assert st == OK and info["variant"] == "wide" and not info["exact"] and info["grid_blocks"] == 8 * 3
+    # bf16 rows of whole chunks up to 32768 elements stay in one workgroup, workspace or not
+    assert rn.plan("ln", 8, 32768, bf16, workspace_bytes=8 * 8 * 16)[1]["variant"] == "workgroup"
+    # other rows longer than 16384 elements: segments of 8192 elements
+    for N, dt, ptrs, strides in [(65537, f32, None, None), (50257, bf16, None, None),
+                                 (65536, f32, {"x": (1 << 40) + 4}, None), (20000, bf16, None, {"x": 20001})]:
+        ws = rn.forward_workspace_bytes("ln", 8, N, dt)
+        st, info = rn.plan("ln", 8, N, dt, workspace_bytes=ws, ptrs=ptrs, strides=strides)
+        S = (N + 8191) // 8192
+        assert st == OK and info["variant"] == "wide_element", (N, info)
+        assert info["grid_blocks"] == 8 * S and info["block_threads"] == 512 and info["chunks_per_lane"] == 16
+        assert info["exact"] == (N % 8192 == 0)
+        assert rn.plan("ln", 8, N, dt, workspace_bytes=ws - 16, ptrs=ptrs, strides=strides)[1]["variant"] == "general"
     # too small a workspace: the general kernel (auto) or an error (forced)
     assert rn.plan("ln", 64, 65536, f32, workspace_bytes=need - 16)[1]["variant"] == "general"
     assert rn.plan("ln", 64, 65536, f32, variant="wide")[0] == WORKSPACE
+    assert rn.plan("ln", 64, 65537, f32, variant="wide_element")[0] == WORKSPACE
     assert rn.plan("ln", 64, 4096, f32, variant="wide", workspace_bytes=1 << 20)[0] == UNSUP
     assert rn.plan("ln", 64, 65537, f32, variant="wide", workspace_bytes=1 << 20)[0] == UNSUP
+    assert rn.plan("ln", 64, 16384, f32, variant="wide_element", workspace_bytes=1 << 20)[0] == UNSUP
+    assert rn.plan("ln", 64, 65536, f32, variant="wide_element", workspace_bytes=need)[1]["variant"] == "wide_element"
     # workspace alignment and overlap
     assert rn.plan("ln", 64, 65536, f32, workspace_bytes=need, ptrs={"workspace": (1 << 47) + 4})[0] == ALIGN
     assert rn.plan("ln", 64, 65536, f32, workspace_bytes=need, ptrs={"workspace": 1 << 40})[0] == ALIAS

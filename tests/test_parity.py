@@ -160,6 +160,56 @@ def test_split_rows(op, dtype):
         check_case(BASES[op].scaled(rows=rows, N=N, seed=620 + N, dtype=dtype))
 
 
+ELEM_WIDE_SHAPES = {"fp32": [(3, 16385), (2, 50257), (3, 65537)], "bf16": [(3, 20001), (2, 50257), (2, 131073)],
+                    "fp16": [(3, 32769)]}
+
+
+@pytest.mark.parametrize("op", ["ln", "rms", "fused_add_rms", "fused_add_ln", "softmax"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
+def test_split_rows_element(op, dtype):
+    # rows of more than 16384 elements that are not whole 16-byte chunks (a vocabulary-sized
+    # softmax, 50257): statistics per 8192-element segment, then the same fixed-order combine
+    for rows, N in ELEM_WIDE_SHAPES[dtype]:
+        st, info = rn.plan(op, rows, N, TD[dtype], workspace_bytes=rn.forward_workspace_bytes(op, rows, N, TD[dtype]))
+        assert st == 0 and info["variant"] == "wide_element", info
+        check_case(BASES[op].scaled(rows=rows, N=N, seed=660 + N, dtype=dtype))
+    # forced on rows of whole chunks (segments end exactly on the row's end)
+    check_case(BASES[op].scaled(rows=2, N=65536, seed=661, dtype=dtype), "wide_element")
+
+
+def test_split_rows_element_offsets_strides_constant_and_in_place():
+    # cancellation stress, constant rows, unaligned and padded rows, NaN guards, in place
+    check_case(workloads.C2.scaled(rows=4, N=65537, seed=670))
+    w = workloads.C2.scaled(rows=3, N=50257, seed=671, x_dist="constant")
+    g = _gpu(workloads.make_inputs(w))
+    y = rn.ln_forward(g["x"], g["gamma"], g["beta"], w.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(y, g["beta"].expand_as(y))
+    for op in ("ln", "rms", "fused_add_rms", "fused_add_ln", "softmax"):
+        w = BASES[op].scaled(rows=3, N=20001, seed=672, dtype="bf16")
+        inp = workloads.make_inputs(w)
+        ref = run_oracle(w, inp)
+        for off, ld in [({n: 1 for n in ROW_TENSORS}, None), ({"x": 3, "y": 0}, {n: 20003 for n in ROW_TENSORS})]:
+            out = run_placed(w, inp, offset=off, ld=ld, expect_variant="wide_element")
+            check_outputs(w, ref, *out)
+    w = workloads.C5.scaled(rows=3, N=50257, seed=673)
+    inp = workloads.make_inputs(w)
+    ref = run_oracle(w, inp)
+    x = inp["x"].to(DEV)
+    rn.ln_forward(x, inp["gamma"].to(DEV), inp["beta"].to(DEV), w.eps, out=x)
+    torch.cuda.synchronize()
+    check_y(x, ref["y"])
+    w = workloads.FUSED_LN.scaled(rows=3, N=50257, seed=674)
+    inp = workloads.make_inputs(w)
+    ref = run_oracle(w, inp)
+    g = _gpu(inp)
+    rn.fused_add_layer_norm(g["x"], g["residual"], g["gamma"], g["beta"], w.eps, out=g["x"],
+                            residual_out=g["residual"])
+    torch.cuda.synchronize()
+    check_y(g["x"], ref["y"])
+    check_bits_equal(g["residual"], ref["residual_out"], "split-row element residual_out in place")
+
+
 def test_split_rows_offset_constant_and_in_place():
     # cancellation stress and constant rows on the split-row path
     check_case(workloads.C2.scaled(rows=4, N=65536, seed=630))
@@ -218,12 +268,14 @@ def test_element_kernel_persistent(case):
 ROW_TENSORS = ("x", "residual", "y", "residual_out")
 
 
-def run_placed(w: workloads.Workload, inp, offset=None, ld=None, variant="auto", expect_pairs=None):
+def run_placed(w: workloads.Workload, inp, offset=None, ld=None, variant="auto", expect_pairs=None,
+               expect_variant=None):
     """Runs the op with each row tensor placed in its own NaN-filled buffer, at an element
     offset (``offset[name]``) and row stride (``ld[name]``, default N), with 64 guard
     elements on both sides. Checks that nothing outside the outputs' rows is written and,
     if ``expect_pairs`` is given, that the plan for these very pointers agrees. Returns the
-    outputs in run_gpu's order."""
+    outputs in run_gpu's order (the binding supplies a split-row workspace when one is
+    needed)."""
     offset, ld = offset or {}, ld or {}
     g = _gpu(inp)
     rows, N = inp["x"].shape
@@ -242,8 +294,11 @@ def run_placed(w: workloads.Workload, inp, offset=None, ld=None, variant="auto",
     strides = {n: ld.get(n, N) for n in names}
     if "gamma" in g:
         ptrs["gamma"] = g["gamma"].data_ptr()
-    st, info = rn.plan(w.op, rows, N, T, ptrs=ptrs, strides=strides, variant=variant)
+    st, info = rn.plan(w.op, rows, N, T, ptrs=ptrs, strides=strides, variant=variant,
+                       workspace_bytes=rn.forward_workspace_bytes(w.op, rows, N, T))
     assert st == 0, st
+    if expect_variant is not None:
+        assert info["variant"] == expect_variant, info
     if expect_pairs is not None:
         assert info["variant"] == "element" and info["pairs"] == expect_pairs, info
     x, y = views["x"], views["y"]
