@@ -6,8 +6,9 @@ largest configuration and the one the bandwidth target applies to (rows * N = 64
 The same measurement is also taken for fused residual-add + RMSNorm at 8192 x 4096 fp16
 (32M elements) and reported in the same JSON line under "fused_add_rms_norm", and, under
 "more", for fused residual-add + LayerNorm (8192 x 4096 bf16), softmax (8192 x 4096 fp32),
-the LayerNorm backward (4096 x 16384 bf16: dx, dgamma, dbeta) and the RMSNorm backward
-(8192 x 4096 fp16: dx, dweight); under "scale_up_sweep", fused add + RMSNorm at
+the LayerNorm backward (4096 x 16384 bf16: dx, dgamma, dbeta), the RMSNorm backward
+(8192 x 4096 fp16: dx, dweight), ragged LayerNorm rows (16384 x 4095 bf16), split rows
+(LayerNorm 1024 x 65536 fp32) and a vocabulary-sized softmax (1024 x 50257 fp32); under "scale_up_sweep", fused add + RMSNorm at
 N = 4096 over 2048 / 8192 / 32768 rows (fp16 and bf16), LayerNorm bf16 2048 x 4096, and the
 headline workload with a hot cache; under "configs", every listed configuration (cold and
 hot, events and graph replay, next to the oracle's host throughput). Small launches (tens of microseconds) are shorter than
@@ -131,8 +132,15 @@ def kernel_name(w, plan):
                 f"{plan['rows_per_block']} row group(s) per workgroup) + rn::rownorm_bwd_cols_kernel")
     if plan["variant"] == "general":
         return f"rn::rownorm_general_kernel ({w.dtype}, {w.op})"
+    if plan["variant"] in ("wide", "wide_element"):
+        k = "rownorm_wide_elem" if plan["variant"] == "wide_element" else "rownorm_wide"
+        return (f"rn::{k}_stats_kernel + rn::{k}_norm_kernel ({w.dtype}, {w.op}, one 512-lane workgroup per "
+                f"row segment, {plan['grid_blocks']} segments)")
     mode = "persistent" if plan["persistent"] else "grid per row"
-    k = "rownorm_elem_kernel" if plan["variant"] == "element" else "rownorm_vec_kernel"
+    if plan["variant"] == "element":
+        k = "rownorm_pair_kernel" if plan.get("pairs") else "rownorm_elem_kernel"
+    else:
+        k = "rownorm_vec_kernel"
     return (f"rn::{k} ({w.dtype}, {w.op}, W={plan['waves_per_row']} waves per row, "
             f"V={plan['chunks_per_lane']} per lane, {plan['rows_per_block']} row group(s) per workgroup, {mode})")
 
@@ -234,7 +242,8 @@ def measure(w, steps, warmup, cache, dev, graph=False):
         if w.op == "softmax":
             ptrs.pop("mean", None)
             ptrs.pop("rstd", None)
-        st, info = rn.plan(w.op, w.rows, w.N, td, ptrs=ptrs, eps=w.eps)
+        st, info = rn.plan(w.op, w.rows, w.N, td, ptrs=ptrs, eps=w.eps,
+                           workspace_bytes=rn.forward_workspace_bytes(w.op, w.rows, w.N, td))
     del sets
     torch.cuda.empty_cache()
     return {
@@ -322,6 +331,13 @@ def _more():
          "LayerNorm backward, bf16 I/O, 4096 x 16384: dx, dgamma, dbeta from fp32 mean / rstd"),
         ("rms_norm_backward", workloads.RMS_BWD.scaled(rows=8192, name="rms_bwd_fp16_8192x4096"),
          "RMSNorm backward, fp16 I/O, 8192 x 4096: dx, dweight from fp32 rstd"),
+        ("layer_norm_ragged", workloads.C5.scaled(rows=16384, N=4095, name="ln_bf16_16384x4095"),
+         "LayerNorm, bf16 I/O, 16384 x 4095 (rows not whole 16-byte chunks: element-pair kernel), y + mean + rstd"),
+        ("layer_norm_split_rows", workloads.C2.scaled(rows=1024, N=65536, name="ln_fp32_1024x65536"),
+         "LayerNorm, fp32 I/O, 1024 x 65536 (rows beyond a workgroup's registers: split-row kernels)"),
+        ("softmax_vocab", workloads.SOFTMAX.scaled(rows=1024, N=50257, name="softmax_fp32_1024x50257"),
+         "row-wise softmax, fp32 I/O, 1024 x 50257 (vocabulary-sized rows, not whole chunks: split-row "
+         "element kernels)"),
     ]
 
 
