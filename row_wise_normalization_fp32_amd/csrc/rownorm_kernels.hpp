@@ -1805,6 +1805,11 @@ inline hipError_t launch_v(const Plan& plan, const Params& p, hipStream_t s) {
         default: break;
         }
     }
+    // softmax and RMSNorm rows of up to 128 KiB, one workgroup each (measured against the
+    // split-row path; the LayerNorm ops are faster split)
+    if constexpr (W == 16 && !PERS && (OP == OP_SOFTMAX || OP == OP_RMS)) {
+        if (plan.chunks_per_lane == 8) return RN_GO(8);
+    }
 #undef RN_GO
     return hipErrorInvalidValue;
 }

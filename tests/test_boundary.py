@@ -56,7 +56,11 @@ def test_status_strings_and_version():
     ("fused_add_rms", torch.float16, 8192, 4096, "workgroup", 2, 4, True),
     ("ln", torch.float32, 16, 16384, "workgroup", 16, 4, False),
     ("rms", torch.bfloat16, 16, 32768, "workgroup", 16, 4, False),
-    ("ln", torch.float32, 16, 16388, "general", 0, 0, False),          # beyond a workgroup's registers
+    ("rms", torch.float32, 16, 16388, "workgroup", 16, 8, False),      # 4097 chunks: 16 waves x 8 chunks
+    ("ln", torch.float32, 16, 16388, "general", 0, 0, False),          # LayerNorm rows that long are split
+    ("softmax", torch.float32, 16, 32768, "workgroup", 16, 8, False),  # 128 KiB rows, one workgroup each
+    ("fused_add_ln", torch.bfloat16, 8, 32776, "general", 0, 0, False),  # no room for 8 chunks: split (no workspace)
+    ("ln", torch.float32, 16, 32772, "general", 0, 0, False),          # beyond a workgroup's registers
     ("ln", torch.float32, 16, 1000, "wave", 1, 4, False),              # ragged: 250 chunks
     ("ln", torch.float16, 16, 1001, "element", 1, 8, False),           # not whole 16-byte chunks: 501 pairs
     ("rms", torch.float32, 3, 1, "element", 1, 1, False),
@@ -196,6 +200,8 @@ def test_plan_forced_variants():
     assert rn.plan("ln", 4, 4096, torch.float32, variant="wave")[1]["chunks_per_lane"] == 16
     assert rn.plan("ln", 4, 8192, torch.float16, variant="wave")[1]["chunks_per_lane"] == 16
     assert rn.plan("ln", 4, 8192, torch.float32, variant="wave")[0] == UNSUP
+    assert rn.plan("softmax", 4, 32768, torch.float32, variant="workgroup")[1]["chunks_per_lane"] == 8
+    assert rn.plan("softmax", 4, 32772, torch.float32, variant="workgroup")[0] == UNSUP
     assert rn.plan("ln", 4, 32768, torch.float32, variant="workgroup")[0] == UNSUP
     assert rn.plan("ln", 4, 64, torch.float32, variant="general")[1]["variant"] == "general"
     assert rn.plan("ln", 4, 4096, torch.float32, variant="element")[1]["variant"] == "element"
@@ -335,8 +341,14 @@ def test_plan_split_rows():
     # whole 16-byte chunks: segments of 2048 chunks
     st, info = rn.plan("ln", 64, 65536, f32, workspace_bytes=need)
     assert st == OK and info["variant"] == "wide" and info["grid_blocks"] == 64 * 8 and info["exact"]
-    st, info = rn.plan("softmax", 8, 32776, bf16, workspace_bytes=8 * 5 * 16)
-    assert st == OK and info["variant"] == "wide" and not info["exact"] and info["grid_blocks"] == 8 * 3
+    st, info = rn.plan("softmax", 8, 65544, bf16, workspace_bytes=8 * 9 * 16)
+    assert st == OK and info["variant"] == "wide" and not info["exact"] and info["grid_blocks"] == 8 * 5
+    # softmax and RMSNorm rows up to 128 KiB stay in one workgroup (16 waves x 8 chunks)
+    ws = rn.forward_workspace_bytes("ln", 8, 32776, bf16)
+    assert rn.plan("softmax", 8, 32776, bf16, workspace_bytes=ws)[1]["variant"] == "workgroup"
+    assert rn.plan("rms", 8, 32776, bf16, workspace_bytes=ws)[1]["variant"] == "workgroup"
+    for op in ("ln", "fused_add_rms", "fused_add_ln"):
+        assert rn.plan(op, 8, 32776, bf16, workspace_bytes=ws)[1]["variant"] == "wide"
     # bf16 rows of whole chunks up to 32768 elements stay in one workgroup, workspace or not
     assert rn.plan("ln", 8, 32768, bf16, workspace_bytes=8 * 8 * 16)[1]["variant"] == "workgroup"
     # other rows longer than 16384 elements: segments of 8192 elements

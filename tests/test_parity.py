@@ -145,8 +145,24 @@ def test_workgroup_path_32k_bf16_rows():
     check_case(workloads.C5.scaled(rows=5, N=32768, seed=601))
 
 
-WIDE_SHAPES = {"fp32": [(3, 16388), (4, 24576), (3, 65536)], "bf16": [(3, 32776), (2, 65536), (2, 131080)],
-               "fp16": [(3, 40960)]}
+WIDE_SHAPES = {"fp32": [(3, 32772), (2, 40960), (3, 65536)], "bf16": [(3, 65544), (2, 131080)],
+               "fp16": [(3, 81920)]}
+BIG_SHAPES = {"fp32": [(3, 16388), (4, 24576), (2, 32768)], "bf16": [(3, 32776), (2, 65536)], "fp16": [(3, 40960)]}
+
+
+@pytest.mark.parametrize("op", ["ln", "rms", "fused_add_rms", "fused_add_ln", "softmax"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
+def test_workgroup_path_128k_rows(op, dtype):
+    # rows of 64-128 KiB: softmax and RMSNorm in one 16-wave workgroup holding 8 chunks per
+    # lane (x read once); the other ops take the split-row path there
+    for rows, N in BIG_SHAPES[dtype]:
+        td = TD[dtype]
+        st, info = rn.plan(op, rows, N, td, workspace_bytes=rn.forward_workspace_bytes(op, rows, N, td))
+        if op in ("softmax", "rms"):
+            assert st == 0 and info["variant"] == "workgroup" and info["chunks_per_lane"] == 8, info
+        else:
+            assert st == 0 and info["variant"] == "wide", info
+        check_case(BASES[op].scaled(rows=rows, N=N, seed=680 + N, dtype=dtype))
 
 
 @pytest.mark.parametrize("op", ["ln", "rms", "fused_add_rms", "fused_add_ln", "softmax"])
@@ -219,7 +235,7 @@ def test_split_rows_offset_constant_and_in_place():
     torch.cuda.synchronize()
     assert torch.equal(y, g["beta"].expand_as(y))
     # in place: y over x; fused: residual_out over residual and y over x
-    w = workloads.C5.scaled(rows=3, N=65536, seed=632)
+    w = workloads.C5.scaled(rows=3, N=131072, seed=632)
     inp = workloads.make_inputs(w)
     ref = run_oracle(w, inp)
     x = inp["x"].to(DEV)
