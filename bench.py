@@ -19,11 +19,13 @@ Cold cache: inputs and outputs rotate through enough buffer sets that each launc
 memory the previous launches have pushed out of L2 (8 x 4 MiB) and the 256 MiB
 memory-side cache. Inputs are resident in HBM before the timed region starts.
 
-Timed region: W warmup steps untimed, then exactly K steps bracketed by
-torch.cuda.synchronize(); ms_per_step is the wall time over K. Then the same K launches
-are repeated, each bracketed by HIP events on the stream the kernel runs on (torch's
-current stream, which the binding passes to the C ABI), giving the per-kernel average
-duration used for the roofline.
+Timed region: about 50 ms of plain device copies (the GPU's clocks rise over the first ~10 ms
+of work after the idle host-side set-up), W warmup steps untimed, then exactly K steps
+bracketed by torch.cuda.synchronize(); ms_per_step is the wall time over K. Two HIP events recorded on
+the stream the kernels run on (torch's current stream, which the binding passes to the C
+ABI) bracket the same K launches: their elapsed time over K is the per-launch kernel
+duration used for the roofline (back-to-back launches; it includes the few-hundred-ns
+dispatch gaps between them).
 
 value = algorithmic bytes per step / ms_per_step (GB/s, 1 GB = 1e9 B). Algorithmic bytes:
 LayerNorm 2*rows*N*s + 2*N*s + 8*rows; fused 4*rows*N*s + N*s + 4*rows (with rstd); fused
@@ -195,7 +197,36 @@ def graph_time(rn, w, sets, steps):
         return None
 
 
-def measure(w, steps, warmup, cache, dev, graph=False):
+def kernel_time(r):
+    """Per-launch device time for the roofline: from the replay of a HIP graph holding the
+    K timed launches (HIP events around the replay, on the launch stream), which leaves out
+    the dispatch gaps of eager back-to-back launches (≈2 µs each here, which rocprofv3's
+    kernel durations also leave out); the eager stream events when no graph could be
+    captured."""
+    if r.get("graph_ms"):
+        return r["graph_ms"], "HIP events around one replay of a HIP graph of the K timed launches"
+    return r["kernel_ms"], "HIP events around the K eager launches (no graph capture)"
+
+
+def prime_gpu(dev, ms=50.0):
+    """Keeps the GPU busy with plain copies for about `ms` before a measurement. After the
+    host-side set-up of a workload the GPU has been idle, and the first ~10 ms of work after
+    idle run up to 8% slower (measured: C5 LayerNorm launches at 47-51 us, then a steady
+    46.3 us); without this the timed region would straddle that ramp. The copies touch
+    none of the workload's buffers."""
+    import torch
+
+    src = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+    del src, dst
+
+
+def measure(w, steps, warmup, cache, dev, graph=True):
     import torch
 
     import row_wise_normalization_fp32_amd as rn
@@ -207,27 +238,24 @@ def measure(w, steps, warmup, cache, dev, graph=False):
     log(f"[bench] {w.name}: {nsets} buffer set(s), {nbytes} algorithmic bytes per launch")
     sets = make_sets(w, nsets, dev)
     torch.cuda.synchronize()
+    prime_gpu(dev)
     for i in range(warmup):
         launch(rn, w, sets[i % nsets])
-    # Timed region: exactly `steps` steps, nothing else enqueued between them.
+    # Timed region: exactly `steps` steps, nothing else enqueued between them, bracketed by
+    # torch.cuda.synchronize() (wall clock) and by two HIP events on the stream the kernels
+    # run on (torch's current stream, which the binding passes to the C ABI): the device
+    # time per step, the kernel duration used for the roofline.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record()
     for i in range(steps):
         launch(rn, w, sets[(warmup + i) % nsets])
+    ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / steps
-    # Per-kernel durations: the same launches again, each bracketed by HIP events on the
-    # stream the kernel runs on (torch's current stream, passed to the C ABI).
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    for i in range(steps):
-        starts[i].record()
-        launch(rn, w, sets[(warmup + i) % nsets])
-        ends[i].record()
-    torch.cuda.synchronize()
-    durs = [a.elapsed_time(b) for a, b in zip(starts, ends)]  # ms
-    kernel_ms = sum(durs) / len(durs)
+    kernel_ms = ev0.elapsed_time(ev1) / steps
     graph_ms = graph_time(rn, w, sets, steps) if graph else None
     s0 = sets[0]
     td = workloads.TORCH_DTYPES[w.dtype]
@@ -248,7 +276,7 @@ def measure(w, steps, warmup, cache, dev, graph=False):
     torch.cuda.empty_cache()
     return {
         "bytes": nbytes, "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, "graph_ms": graph_ms,
-        "kernel_ms_median": sorted(durs)[len(durs) // 2], "nsets": nsets, "plan": info,
+        "nsets": nsets, "plan": info,
     }
 
 
@@ -384,7 +412,8 @@ def main():
     log(f"[bench] timing {w.name} ({args.cache} cache) ...")
     r = measure(w, args.steps, args.warmup, args.cache, dev)
     value = r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
-    achieved = r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+    kms, timing = kernel_time(r)
+    achieved = r["bytes"] / (kms * 1e-3) / 1e9
     traffic = counter_traffic("ln_bf16_4096x16384")
     out = {
         "metric": METRIC,
@@ -411,7 +440,8 @@ def main():
             "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
             "kernel": kernel_name(w, r["plan"]),
-            "kernel_avg_ms": round(r["kernel_ms"], 5), "kernel_median_ms": round(r["kernel_ms_median"], 5),
+            "kernel_avg_ms": round(kms, 5), "kernel_timing": timing,
+            "stream_ms_per_launch": round(r["kernel_ms"], 5),
             "bytes_per_launch": r["bytes"],
         },
         "cpu_baseline": cpu,
@@ -427,12 +457,14 @@ def main():
         log(f"[bench] timing {f.name} ({args.cache} cache) ...")
         rf = measure(f, args.steps, args.warmup, args.cache, dev)
         fv = rf["bytes"] / (rf["ms_per_step"] * 1e-3) / 1e9
-        fa = rf["bytes"] / (rf["kernel_ms"] * 1e-3) / 1e9
+        fkms, _ = kernel_time(rf)
+        fa = rf["bytes"] / (fkms * 1e-3) / 1e9
         out["fused_add_rms_norm"] = {
             "workload": "fused residual-add + RMSNorm, fp16 I/O, 8192 x 4096, eps 1e-6, y + residual_out + rstd",
             "value": round(fv, 2), "unit": "GB/s", "pct_of_peak": round(100.0 * fv / PEAK_HBM_GBS, 2),
             "rows_per_s": round(f.rows / (rf["ms_per_step"] * 1e-3), 1), "ms_per_step": round(rf["ms_per_step"], 5),
-            "kernel_avg_ms": round(rf["kernel_ms"], 5), "achieved_kernel_GBs": round(fa, 2),
+            "kernel_avg_ms": round(fkms, 5), "stream_ms_per_launch": round(rf["kernel_ms"], 5),
+            "achieved_kernel_GBs": round(fa, 2),
             "frac_kernel": round(fa / PEAK_HBM_GBS, 4), "bytes_per_launch": rf["bytes"],
             "kernel": kernel_name(f, rf["plan"]), "traffic": counter_traffic("fused_fp16_8192x4096"),
         }
@@ -443,11 +475,13 @@ def main():
             log(f"[bench] timing {x.name} ({args.cache} cache) ...")
             rx = measure(x, extra_steps, min(args.warmup, 10), args.cache, dev)
             xv = rx["bytes"] / (rx["ms_per_step"] * 1e-3) / 1e9
-            xa = rx["bytes"] / (rx["kernel_ms"] * 1e-3) / 1e9
+            xkms, _ = kernel_time(rx)
+            xa = rx["bytes"] / (xkms * 1e-3) / 1e9
             more[key] = {
                 "workload": what, "value": round(xv, 2), "unit": "GB/s",
                 "pct_of_peak": round(100.0 * xv / PEAK_HBM_GBS, 2), "ms_per_step": round(rx["ms_per_step"], 5),
-                "steps": extra_steps, "kernel_avg_ms": round(rx["kernel_ms"], 5),
+                "steps": extra_steps, "kernel_avg_ms": round(xkms, 5),
+                "stream_ms_per_launch": round(rx["kernel_ms"], 5),
                 "achieved_kernel_GBs": round(xa, 2), "frac_kernel": round(xa / PEAK_HBM_GBS, 4),
                 "bytes_per_launch": rx["bytes"], "rows_per_s": round(x.rows / (rx["ms_per_step"] * 1e-3), 1),
                 "kernel": kernel_name(x, rx["plan"]),
@@ -495,8 +529,10 @@ def main():
             xa = rx["bytes"] / (rx["kernel_ms"] * 1e-3) / 1e9
             xv = rx["bytes"] / (rx["ms_per_step"] * 1e-3) / 1e9
             gm = rx["graph_ms"]
-            sweep[x.name] = {"elements": x.rows * x.N, "cache": cache, "kernel_avg_ms": round(rx["kernel_ms"], 5),
-                             "frac_kernel": round(xa / PEAK_HBM_GBS, 4), "value": round(xv, 2),
+            sweep[x.name] = {"elements": x.rows * x.N, "cache": cache,
+                             # eager launches: HIP events around the K timed launches
+                             "stream_ms_per_launch": round(rx["kernel_ms"], 5),
+                             "frac_stream": round(xa / PEAK_HBM_GBS, 4), "value": round(xv, 2),
                              "pct_of_peak": round(100.0 * xv / PEAK_HBM_GBS, 2),
                              # device time per launch from a replayed HIP graph (no host gaps)
                              "graph_ms": None if gm is None else round(gm, 5),
