@@ -359,11 +359,11 @@ def _more():
          "LayerNorm backward, bf16 I/O, 4096 x 16384: dx, dgamma, dbeta from fp32 mean / rstd"),
         ("rms_norm_backward", workloads.RMS_BWD.scaled(rows=8192, name="rms_bwd_fp16_8192x4096"),
          "RMSNorm backward, fp16 I/O, 8192 x 4096: dx, dweight from fp32 rstd"),
-        ("layer_norm_ragged", workloads.C5.scaled(rows=16384, N=4095, name="ln_bf16_16384x4095"),
+        ("layer_norm_ragged", workloads.LN_RAGGED,
          "LayerNorm, bf16 I/O, 16384 x 4095 (rows not whole 16-byte chunks: element-pair kernel), y + mean + rstd"),
-        ("layer_norm_split_rows", workloads.C2.scaled(rows=1024, N=65536, name="ln_fp32_1024x65536"),
+        ("layer_norm_split_rows", workloads.LN_SPLIT,
          "LayerNorm, fp32 I/O, 1024 x 65536 (rows beyond a workgroup's registers: split-row kernels)"),
-        ("softmax_vocab", workloads.SOFTMAX.scaled(rows=1024, N=50257, name="softmax_fp32_1024x50257"),
+        ("softmax_vocab", workloads.SOFTMAX_VOCAB,
          "row-wise softmax, fp32 I/O, 1024 x 50257 (vocabulary-sized rows, not whole chunks: split-row "
          "element kernels)"),
     ]

@@ -114,6 +114,17 @@ def test_new_ops_full_size(w):
     check_case(w)
 
 
+@pytest.mark.parametrize("w,variant", [(workloads.LN_RAGGED, "element"), (workloads.LN_SPLIT, "wide"),
+                                       (workloads.SOFTMAX_VOCAB, "wide_element")], ids=lambda v: getattr(v, "name", v))
+def test_general_shapes_full_size(w, variant):
+    # the benchmark's general-shape workloads at full size, in the launch configuration it
+    # times (automatic choice; the binding supplies the split-row workspace)
+    td = TD[w.dtype]
+    st, info = rn.plan(w.op, w.rows, w.N, td, workspace_bytes=rn.forward_workspace_bytes(w.op, w.rows, w.N, td))
+    assert st == 0 and info["variant"] == variant, info
+    check_case(w)
+
+
 # ---------------------------------------------------------------------------------------
 # Every kernel variant on shapes spanning several tiles and a ragged tail.
 # ---------------------------------------------------------------------------------------

@@ -202,3 +202,11 @@ def algorithmic_bytes(op: str, rows: int, N: int, elem_bytes: int, with_params: 
     if op == "rms_bwd":
         return 3 * elems + (2 if with_params else 1) * N * elem_bytes + 4 * rows
     raise ValueError(op)
+
+# General shapes with the input distributions of the configs above: rows that are not whole
+# 16-byte chunks (the 16384-wide config's distributions at N = 4095), rows beyond a
+# workgroup's registers (the offset-row config at N = 65536, fp32), and a vocabulary-sized
+# softmax (N = 50257 logits, fp32, not whole chunks).
+LN_RAGGED = C5.scaled(rows=16384, N=4095, seed=1205, name="ln_bf16_16384x4095")
+LN_SPLIT = C2.scaled(rows=1024, N=65536, seed=1202, name="ln_fp32_1024x65536")
+SOFTMAX_VOCAB = SOFTMAX.scaled(rows=1024, N=50257, seed=1231, name="softmax_fp32_1024x50257")
