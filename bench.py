@@ -280,7 +280,7 @@ def measure(w, steps, warmup, cache, dev, graph=True):
     }
 
 
-def cpu_baseline(w, seconds):
+def cpu_baseline(w, seconds, single_thread=False):
     """The oracle on `w` over about `seconds` of host time (median pass)."""
     import oracle
     import workloads
@@ -306,11 +306,33 @@ def cpu_baseline(w, seconds):
         if time.perf_counter() - t_start >= seconds or len(times) >= 2000:
             break
     med = sorted(times)[len(times) // 2]
-    return {
+    out = {
         "value": round(nbytes / med / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
         "rows_per_s": round(w.rows / med, 1),
         "sample": f"full {w.rows}x{w.N} {w.dtype} workload, {len(times)} passes over {sum(times):.1f} s, median pass",
     }
+    if single_thread and threads > 1:
+        # the same oracle on one host thread, over the first rows of the workload (about a
+        # quarter of the multi-threaded budget), scaled to the whole workload's rows/s
+        sub = {k: (v[: max(1, w.rows // 8)] if v.dim() == 2 else v) for k, v in inp.items()}
+        rows1 = sub["x"].shape[0]
+        t1 = []
+        t_start = time.perf_counter()
+        while time.perf_counter() - t_start < seconds / 4 and len(t1) < 200:
+            t0 = time.perf_counter()
+            if w.op == "ln":
+                oracle.layer_norm(sub["x"], sub.get("gamma"), sub.get("beta"), w.eps, threads=1)
+            elif w.op == "rms":
+                oracle.rms_norm(sub["x"], sub.get("weight"), w.eps, threads=1)
+            else:
+                oracle.fused_add_rms_norm(sub["x"], sub["residual"], sub.get("weight"), w.eps, threads=1)
+            t1.append(time.perf_counter() - t0)
+        m1 = sorted(t1)[len(t1) // 2]
+        b1 = workloads.algorithmic_bytes(w.op, rows1, w.N, w.elem_bytes, with_stats=True)
+        out["single_thread"] = {"value": round(b1 / m1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                                "rows_per_s": round(rows1 / m1, 1),
+                                "sample": f"first {rows1} rows, {len(t1)} passes, median pass"}
+    return out
 
 
 def copy_reference(nbytes_each, steps, dev):
@@ -405,7 +427,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle) ...")
-        cpu = cpu_baseline(workloads.C5, args.cpu_seconds)
+        cpu = cpu_baseline(workloads.C5, args.cpu_seconds, single_thread=True)
         log(f"[bench] cpu baseline: {cpu}")
 
     w = workloads.C5
