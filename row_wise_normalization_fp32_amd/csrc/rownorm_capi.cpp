@@ -294,15 +294,16 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     plan->grid = blocks < rn::kMaxGrid ? blocks : rn::kMaxGrid;
     const bool vec = plan->variant == rn::V_WAVE || plan->variant == rn::V_WORKGROUP;
     plan->exact = vec && C == int64_t(64) * W * plan->chunks_per_lane;
-    // Persistent launch: for exact shapes with parameters and enough rows that workgroups
-    // would otherwise be launched many times over (measured: it pays from about 2048
-    // workgroups up). Parameters go to LDS once per workgroup; the LayerNorm ops with both
-    // keep gamma in VGPRs and stage only beta, so the LDS need is at most one row (64 KiB).
+    // Persistent launch: for exact shapes with enough rows that workgroups would otherwise
+    // be launched many times over (measured: it pays from about 2048 workgroups up; softmax,
+    // which has no parameters, gains from the streaming loads and stores and the resident
+    // grid alone). Parameters go to LDS once per workgroup; the LayerNorm ops with both keep
+    // gamma in VGPRs and stage only beta, so the LDS need is at most one row (64 KiB).
     const bool has_params = a.gamma != nullptr || (ln && a.beta != nullptr);
     plan->persistent = blocks >= rn::kPersistentBlocks &&
-                       ((vec && plan->exact && has_params && C <= group_cap) || plan->variant == rn::V_ELEMENT);
+                       ((vec && plan->exact && C <= group_cap) || plan->variant == rn::V_ELEMENT);
     plan->lds_bytes = 0;
-    if (plan->persistent && vec) plan->lds_bytes = static_cast<int>(C * 16);  // one parameter vector in LDS
+    if (plan->persistent && vec && has_params) plan->lds_bytes = static_cast<int>(C * 16);  // one parameter vector in LDS
     *chunks = C;
     return RN_OK;
 }

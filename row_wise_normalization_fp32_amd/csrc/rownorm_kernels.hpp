@@ -1759,9 +1759,11 @@ inline hipError_t go_persistent(const Plan& plan, const Params& p, hipStream_t s
     int cus = 0, per_cu = 0;
     hipError_t e = resident<KERNEL>(plan.block_threads, plan.lds_bytes, &cus, &per_cu);
     if (e != hipSuccess) return e;
-    // Vectorized workgroups holding 4 chunks per lane: at most two per CU (more rows per
-    // workgroup, measured better for fused add + LayerNorm 8192 x 4096: 68.3% -> 70.0%,
-    // neutral for the others); smaller rows keep the full resident count for bytes in flight.
+    // Vectorized workgroups that stage parameters and hold 4 chunks per lane: at most two
+    // per CU (more rows per workgroup, measured better for fused add + LayerNorm 8192 x 4096:
+    // 68.3% -> 70.0%, neutral for the others); smaller rows, and launches without parameters
+    // (softmax: 54-64% -> 63-69% for 16-bit rows of 4096-16384 uncapped), keep the full
+    // resident count for bytes in flight.
     // The element kernels (row_bytes_per_wave > 0: the row bytes one wave holds) keep about
     // kElemCuRowBytes of row data per CU (measured on MI355X, persistent grids of 1 to 6
     // workgroups per CU: 16 waves of 2 KiB or 32 of 1 KiB are the best or within noise of
@@ -1771,7 +1773,7 @@ inline hipError_t go_persistent(const Plan& plan, const Params& p, hipStream_t s
         const int waves = kElemCuRowBytes / row_bytes_per_wave;
         const int wg = waves / (plan.block_threads / 64);
         cap = wg < 1 ? 1 : (wg < per_cu ? wg : per_cu);
-    } else if (plan.chunks_per_lane >= 4 && per_cu > 2) {
+    } else if (plan.chunks_per_lane >= 4 && per_cu > 2 && plan.lds_bytes > 0) {
         cap = 2;
     }
     int64_t grid = static_cast<int64_t>(cus) * cap;
@@ -1829,10 +1831,9 @@ inline hipError_t launch_w(const Plan& plan, const Params& p, hipStream_t s) {
 template <int DT, int OP, int AFF, bool PERS>
 inline hipError_t launch_e(const Plan& plan, const Params& p, hipStream_t s) {
     if constexpr (PERS) {
-        // persistent launches are planned only for exact shapes with parameters
-        if (!plan.exact || AFF == 0) return hipErrorInvalidValue;
-        if constexpr (AFF != 0) return launch_w<DT, OP, true, AFF, true>(plan, p, s);
-        return hipErrorInvalidValue;
+        // persistent launches are planned only for exact shapes
+        if (!plan.exact) return hipErrorInvalidValue;
+        return launch_w<DT, OP, true, AFF, true>(plan, p, s);
     } else {
         return plan.exact ? launch_w<DT, OP, true, AFF, false>(plan, p, s)
                           : launch_w<DT, OP, false, AFF, false>(plan, p, s);
@@ -1940,8 +1941,7 @@ inline hipError_t launch_op(const Plan& plan, const Params& p, hipStream_t s) {
     }
     if (plan.variant != V_WAVE && plan.variant != V_WORKGROUP) return hipErrorInvalidValue;
     if constexpr (OpTraits<OP>::SM) {
-        if constexpr (PERS) return hipErrorInvalidValue;
-        return launch_e<DT, OP, 0, false>(plan, p, s);
+        return launch_e<DT, OP, 0, PERS>(plan, p, s);
     } else {
         const int aff = (p.gamma ? AFF_G : 0) | (OpTraits<OP>::LN && p.beta ? AFF_B : 0);
         switch (aff) {

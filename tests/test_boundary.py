@@ -71,7 +71,7 @@ def test_status_strings_and_version():
     ("fused_add_ln", torch.bfloat16, 8192, 4096, "workgroup", 2, 4, True),
     ("fused_add_ln", torch.float32, 256, 4096, "workgroup", 4, 4, False),
     ("softmax", torch.float32, 128, 4096, "workgroup", 4, 4, False),
-    ("softmax", torch.float32, 8192, 4096, "workgroup", 4, 4, False),  # no parameters: never persistent
+    ("softmax", torch.float32, 8192, 4096, "workgroup", 4, 4, True),   # persistent without parameters
     ("softmax", torch.float16, 64, 333, "element", 1, 4, False),
     ("softmax", torch.float32, 64, 333, "element", 1, 8, False),
     ("ln", torch.bfloat16, 16384, 4095, "element", 4, 8, True),        # many ragged rows: persistent
@@ -105,14 +105,22 @@ def test_plan_variant_choice(op, dtype, rows, N, variant, W, V, persistent):
     s = torch.tensor([], dtype=dtype).element_size()
     assert info["exact"] == (N * s // 16 == 64 * W * V)
     if persistent:
-        assert info["lds_bytes"] == N * s  # one parameter vector staged in LDS
+        # one parameter vector staged in LDS (softmax has none)
+        assert info["lds_bytes"] == (0 if op == "softmax" else N * s)
 
 
-def test_plan_persistent_needs_parameters():
-    # without gamma / beta there is nothing to stage: grid-per-row launch
+def test_plan_persistent_launches():
+    # without gamma / beta nothing is staged: persistent, but no LDS
     st, info = rn.plan("ln", 4096, 16384, torch.bfloat16)
-    assert st == OK and not info["persistent"] and info["lds_bytes"] == 0
-    # ragged rows are never persistent
+    assert st == OK and info["persistent"] and info["lds_bytes"] == 0
+    st, info = rn.plan("softmax", 8192, 4096, torch.bfloat16)
+    assert st == OK and info["persistent"] and info["lds_bytes"] == 0
+    # with parameters: one parameter vector in LDS
+    st, info = rn.plan("rms", 8192, 4096, torch.bfloat16, ptrs={"gamma": 1 << 44})
+    assert st == OK and info["persistent"] and info["lds_bytes"] == 4096 * 2
+    # too few workgroups: grid per row
+    assert not rn.plan("softmax", 2048, 4096, torch.bfloat16)[1]["persistent"]
+    # ragged rows of the vectorized kernels are never persistent
     st, info = rn.plan("rms", 1 << 15, 1000, torch.float32, ptrs={"gamma": 1 << 44})
     assert st == OK and not info["exact"] and not info["persistent"]
 

@@ -639,6 +639,11 @@ PERSISTENT_CASES = [
     ("fused_add_ln", "bf16", 8192, 4096, True, True),
     ("fused_add_ln", "fp16", 2048, 16384, True, False),
     ("fused_add_ln", "fp32", 2048, 16384, False, True),
+    ("ln", "bf16", 4096, 16384, False, False),  # no parameters: nothing staged
+    ("rms", "fp16", 8192, 4096, False, False),
+    ("softmax", "fp32", 8192, 4096, False, False),
+    ("softmax", "bf16", 8192, 1024, False, False),  # one wave per row
+    ("softmax", "fp16", 4096, 16384, False, False),
 ]
 
 
@@ -647,11 +652,15 @@ PERSISTENT_CASES = [
 def test_persistent_launches(case):
     op, dtype, rows, N, wg, wb = case
     base = {"ln": workloads.C5, "rms": workloads.C3, "fused_add_rms": workloads.C4_BF16,
-            "fused_add_ln": workloads.FUSED_LN}[op]
+            "fused_add_ln": workloads.FUSED_LN, "softmax": workloads.SOFTMAX}[op]
     w = base.scaled(rows=rows, N=N, seed=900 + N, dtype=dtype, with_gamma=wg, with_beta=wb)
     inp = workloads.make_inputs(w)
-    st, info = rn.plan(op, rows, N, TD[dtype], ptrs={"gamma": 1 << 44, "beta": (1 << 44) + (1 << 30)}
-                       if (wg and wb) else ({"gamma": 1 << 44} if wg else {"beta": (1 << 44) + (1 << 30)}))
+    ptrs = {}
+    if wg:
+        ptrs["gamma"] = 1 << 44
+    if wb:
+        ptrs["beta"] = (1 << 44) + (1 << 30)
+    st, info = rn.plan(op, rows, N, TD[dtype], ptrs=ptrs)
     assert st == 0 and info["persistent"], info
     check_case(w, inp=inp)
 
