@@ -50,7 +50,8 @@
  *     sizeof(dtype) and every row stride in bytes are multiples of 16 and every [rows, N] /
  *     [N] pointer is 16-byte aligned, the vectorized kernels run: a row is held in registers
  *     by one 64-lane wavefront (rows of up to 4 KiB, or 16 KiB when forced) or by a group of
- *     up to 16 wavefronts (rows of up to 64 KiB: 16384 fp32 or 32768 fp16 / bf16 elements).
+ *     up to 16 wavefronts (rows of up to 64 KiB: 16384 fp32 or 32768 fp16 / bf16 elements;
+ *     softmax and RMSNorm rows of up to 128 KiB).
  *     Otherwise rows of up to 16384 elements are held in registers one element per slot
  *     (the element kernel, still one read of x; 16-bit rows whose tensors share their
  *     position within 4-byte words move as element pairs). Longer rows take the split-row
@@ -93,7 +94,8 @@ typedef enum rn_status {
 typedef enum rn_variant {
     RN_VARIANT_AUTO = 0,      /* choose from N, dtype, alignment and rows (what the plain entry points do) */
     RN_VARIANT_WAVE = 1,      /* one 64-lane wavefront per row, row held in VGPRs (rows up to 16 KiB) */
-    RN_VARIANT_WORKGROUP = 2, /* 2-16 wavefronts per row, partial moments combined in LDS (rows up to 64 KiB) */
+    RN_VARIANT_WORKGROUP = 2, /* 2-16 wavefronts per row, partial moments combined in LDS (rows up to 64 KiB;
+                                 softmax and RMSNorm up to 128 KiB) */
     RN_VARIANT_GENERAL = 3,   /* any N, any element-aligned pointers; re-reads the row */
     RN_VARIANT_ELEMENT = 4,   /* rows up to 16384 elements held in VGPRs one element per slot;
                                  any element-aligned pointers and strides */
