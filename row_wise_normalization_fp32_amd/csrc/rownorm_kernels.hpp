@@ -1,6 +1,7 @@
-// Row-wise LayerNorm / RMSNorm / fused residual-add + RMSNorm kernels for gfx950 (MI355X).
+// Row-wise LayerNorm / RMSNorm / fused residual-add + RMSNorm / fused residual-add +
+// LayerNorm / softmax kernels for gfx950 (MI355X).
 //
-// The operations are defined in include/rownorm.h. All three are bandwidth-bound: a few
+// The operations are defined in include/rownorm.h. All of them are bandwidth-bound: a few
 // fp32 operations per element against 2-4 bytes moved per element (the LayerNorm CUDA
 // walkthrough, lpnh.cn/news/2756757, section 1, counts about 5 FLOP per 4-byte element;
 // "CUDA fused RMSNorm kernel", diycv.top, section 1, calls RMSNorm memory-bound). The
@@ -44,9 +45,20 @@
 //     LDS for LayerNorm, the weight in LDS otherwise), rows stream with non-temporal
 //     accesses, and LayerNorm keeps only the loaded row between statistics and output.
 //
-// General kernel (rownorm_general_kernel): any N and any element-aligned pointers. One
-// 256-lane workgroup per row; it reads the row up to three times (statistics, centered
-// squares, normalization), element by element. Correct everywhere, not tuned.
+// Element kernel (rownorm_elem_kernel) and pair kernel (rownorm_pair_kernel): rows that are
+// not whole 16-byte chunks or tensors that are only element-aligned, rows of up to 16384
+// elements. The same register-resident structure at element granularity, through buffer
+// resources bounded by the row; 16-bit rows move as 4-byte element pairs when all row
+// tensors sit at the same position within 4-byte words.
+//
+// Split-row kernels (rownorm_wide_* and rownorm_wide_elem_*): rows longer than a workgroup's
+// registers, cut into segments; a statistics launch writes one record per segment to a
+// caller workspace, a second launch combines the row's records and normalizes.
+//
+// General kernel (rownorm_general_kernel): any N and any element-aligned pointers, for long
+// rows without a workspace. One 256-lane workgroup per row; it reads the row up to three
+// times (statistics, centered squares, normalization), element by element. Correct
+// everywhere, not tuned.
 #pragma once
 
 #include <hip/hip_runtime.h>
