@@ -8,7 +8,8 @@ The same measurement is also taken for fused residual-add + RMSNorm at 8192 x 40
 "more", for fused residual-add + LayerNorm (8192 x 4096 bf16), softmax (8192 x 4096 fp32),
 the LayerNorm backward (4096 x 16384 bf16: dx, dgamma, dbeta), the RMSNorm backward
 (8192 x 4096 fp16: dx, dweight), ragged LayerNorm rows (16384 x 4095 bf16), split rows
-(LayerNorm 1024 x 65536 fp32) and a vocabulary-sized softmax (1024 x 50257 fp32); under "scale_up_sweep", fused add + RMSNorm at
+(LayerNorm 1024 x 65536 fp32) and a vocabulary-sized softmax (1024 x 50257 fp32, element
+kernel); under "scale_up_sweep", fused add + RMSNorm at
 N = 4096 over 2048 / 8192 / 32768 rows (fp16 and bf16), LayerNorm bf16 2048 x 4096, and the
 headline workload with a hot cache; under "configs", every listed configuration (cold and
 hot, events and graph replay, next to the oracle's host throughput). Small launches (tens of microseconds) are shorter than
@@ -386,8 +387,8 @@ def _more():
         ("layer_norm_split_rows", workloads.LN_SPLIT,
          "LayerNorm, fp32 I/O, 1024 x 65536 (rows beyond a workgroup's registers: split-row kernels)"),
         ("softmax_vocab", workloads.SOFTMAX_VOCAB,
-         "row-wise softmax, fp32 I/O, 1024 x 50257 (vocabulary-sized rows, not whole chunks: split-row "
-         "element kernels)"),
+         "row-wise softmax, fp32 I/O, 1024 x 50257 (vocabulary-sized rows, not whole chunks: element kernel, "
+         "one 16-wave workgroup per row)"),
     ]
 
 

@@ -179,6 +179,9 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     const int64_t wave_cap = int64_t(64) * rn::kMaxWaveChunks;                         // 1024 chunks
     const int64_t group_cap = int64_t(64) * rn::kMaxGroupWaves * rn::kMaxGroupChunks;  // 4096 chunks
     const int64_t elem_cap = int64_t(64) * rn::kMaxGroupWaves * rn::kElemMaxPerLane;   // 16384 elements
+    // Softmax keeps no parameters in registers: its element / pair kernels hold rows of up to
+    // 65536 elements in one 16-wave workgroup (x read once) instead of splitting them.
+    const int64_t elem_cap_op = sm ? int64_t(64) * rn::kMaxGroupWaves * rn::kSoftmaxElemMaxPerLane : elem_cap;
     // Softmax and RMSNorm: 16 waves x 8 chunks hold rows up to 8192 chunks in one workgroup
     // (grid per row). Measured on MI355X against the split-row path: softmax 51-54% -> 55-61%,
     // RMSNorm 59% -> 61%; the LayerNorm ops (42-50% vs 51-57%) and fused add + RMSNorm (66%
@@ -198,7 +201,7 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
             v = w_auto == 1 ? RN_VARIANT_WAVE : RN_VARIANT_WORKGROUP;
         else if (vec_ok && ws_given)
             v = RN_VARIANT_WIDE;
-        else if (N <= elem_cap)
+        else if (N <= elem_cap_op)
             v = RN_VARIANT_ELEMENT;
         else if (ws_given)
             v = RN_VARIANT_WIDE_ELEMENT;
@@ -244,7 +247,7 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
         W = w_auto < 2 ? 2 : w_auto;
         plan->variant = rn::V_WORKGROUP;
     } else if (v == RN_VARIANT_ELEMENT) {
-        if (N > elem_cap) return RN_ERR_UNSUPPORTED;
+        if (N > elem_cap_op) return RN_ERR_UNSUPPORTED;
         plan->variant = rn::V_ELEMENT;
     } else {
         plan->variant = rn::V_GENERAL;
@@ -263,7 +266,8 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
         const uintptr_t h0 = (reinterpret_cast<uintptr_t>(a.x) >> 1) & 1;
         const int64_t hmax = (h0 != 0 || (rows > 1 && (a.ldx & 1) != 0)) ? 1 : 0;
         const int64_t words = (N + hmax + 1) / 2;
-        bool pairs = s == 2 && words <= int64_t(64) * rn::kMaxGroupWaves * rn::kPairMaxPerLane;
+        const int64_t pair_cap = int64_t(64) * rn::kMaxGroupWaves * (sm ? rn::kSoftmaxPairMaxPerLane : rn::kPairMaxPerLane);
+        bool pairs = s == 2 && words <= pair_cap;
         for (int i = 0; i < nb && pairs; ++i) {
             const Buf& bf = bufs[i];
             if (!bf.p || !(bf.role == R_RES || bf.role == R_Y || bf.role == R_RO)) continue;

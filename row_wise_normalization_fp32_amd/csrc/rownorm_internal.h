@@ -91,6 +91,8 @@ constexpr int kElemTarget = 8;         // element variant: about 8 elements per 
 constexpr int kElemMaxPerLane = 16;    // ... at most 16 (with 16 waves: rows up to 16384)
 constexpr int kPairTarget = 8;         // pair kernel: about 8 two-element slots per lane ...
 constexpr int kPairMaxPerLane = 8;     // ... at most 8 (with 16 waves: rows up to 16384)
+constexpr int kSoftmaxElemMaxPerLane = 64;  // softmax rows (no parameters in registers): up to 64
+constexpr int kSoftmaxPairMaxPerLane = 32;  // elements / 32 pairs per lane, rows up to 65536
 constexpr int kElemCuRowBytes = 32768; // element kernels, persistent: row bytes held per CU
 constexpr int64_t kMaxGrid = 1 << 20;  // grid cap; kernels loop over the remaining rows
 constexpr int64_t kPersistentBlocks = 2048;  // at least this many workgroups: persistent launch

@@ -1865,14 +1865,17 @@ inline hipError_t launch_pair(const Plan& plan, const Params& p, hipStream_t s) 
                      : go(rownorm_pair_kernel<DT, OP, WW, VV, rows_per_block_for(WW), A>, plan, p, s))
 #define RN_PR_AFF(WW, VV)                                                     \
     do {                                                                      \
-        if constexpr (OpTraits<OP>::SM) return RN_PR(WW, VV, 0);              \
-        if (aff == 0) return RN_PR(WW, VV, 0);                                \
-        if (aff == AFF_G) return RN_PR(WW, VV, AFF_G);                        \
-        if constexpr (OpTraits<OP>::LN) {                                     \
-            if (aff == AFF_B) return RN_PR(WW, VV, AFF_B);                    \
-            return RN_PR(WW, VV, AFF_G | AFF_B);                              \
+        if constexpr (OpTraits<OP>::SM) {                                     \
+            return RN_PR(WW, VV, 0);                                          \
+        } else {                                                              \
+            if (aff == 0) return RN_PR(WW, VV, 0);                            \
+            if (aff == AFF_G) return RN_PR(WW, VV, AFF_G);                    \
+            if constexpr (OpTraits<OP>::LN) {                                 \
+                if (aff == AFF_B) return RN_PR(WW, VV, AFF_B);                \
+                return RN_PR(WW, VV, AFF_G | AFF_B);                          \
+            }                                                                 \
+            return hipErrorInvalidValue;                                      \
         }                                                                     \
-        return hipErrorInvalidValue;                                          \
     } while (0)
     // the shapes the planner produces: W = 1 with 1..8 words per lane, else 8 words per lane
     if (W == 1) {
@@ -1883,6 +1886,10 @@ inline hipError_t launch_pair(const Plan& plan, const Params& p, hipStream_t s) 
         case 8: RN_PR_AFF(1, 8);
         default: return hipErrorInvalidValue;
         }
+    }
+    if constexpr (OpTraits<OP>::SM) {  // rows of up to 65536 elements
+        if (W == 16 && V == 16) RN_PR_AFF(16, 16);
+        if (W == 16 && V == 32) RN_PR_AFF(16, 32);
     }
     if (V != 8) return hipErrorInvalidValue;
     switch (W) {
@@ -1913,14 +1920,17 @@ inline hipError_t launch_elem(const Plan& plan, const Params& p, hipStream_t s) 
                      : go(rownorm_elem_kernel<DT, OP, WW, VV, rows_per_block_for(WW), A>, plan, p, s))
 #define RN_EL_AFF(WW, VV)                                                     \
     do {                                                                      \
-        if constexpr (OpTraits<OP>::SM) return RN_EL(WW, VV, 0);              \
-        if (aff == 0) return RN_EL(WW, VV, 0);                                \
-        if (aff == AFF_G) return RN_EL(WW, VV, AFF_G);                        \
-        if constexpr (OpTraits<OP>::LN) {                                     \
-            if (aff == AFF_B) return RN_EL(WW, VV, AFF_B);                    \
-            return RN_EL(WW, VV, AFF_G | AFF_B);                              \
+        if constexpr (OpTraits<OP>::SM) {                                     \
+            return RN_EL(WW, VV, 0);                                          \
+        } else {                                                              \
+            if (aff == 0) return RN_EL(WW, VV, 0);                            \
+            if (aff == AFF_G) return RN_EL(WW, VV, AFF_G);                    \
+            if constexpr (OpTraits<OP>::LN) {                                 \
+                if (aff == AFF_B) return RN_EL(WW, VV, AFF_B);                \
+                return RN_EL(WW, VV, AFF_G | AFF_B);                          \
+            }                                                                 \
+            return hipErrorInvalidValue;                                      \
         }                                                                     \
-        return hipErrorInvalidValue;                                          \
     } while (0)
     if (W == 1) {
         switch (V) {
@@ -1936,6 +1946,10 @@ inline hipError_t launch_elem(const Plan& plan, const Params& p, hipStream_t s) 
     if (W == 8 && V == 8) RN_EL_AFF(8, 8);
     if (W == 16 && V == 8) RN_EL_AFF(16, 8);
     if (W == 16 && V == 16) RN_EL_AFF(16, 16);
+    if constexpr (OpTraits<OP>::SM) {  // rows of up to 65536 elements
+        if (W == 16 && V == 32) RN_EL_AFF(16, 32);
+        if (W == 16 && V == 64) RN_EL_AFF(16, 64);
+    }
 #undef RN_EL_AFF
 #undef RN_EL
     return hipErrorInvalidValue;

@@ -179,6 +179,21 @@ def test_plan_element_pairs():
     assert not rn.plan("ln", 8, 4096, bf)[1]["pairs"]  # vectorized
 
 
+def test_plan_long_softmax_rows_stay_in_one_workgroup():
+    f32, bf = torch.float32, torch.bfloat16
+    ws = 1 << 24
+    st, info = rn.plan("softmax", 8, 50257, f32, workspace_bytes=ws)
+    assert st == OK and info["variant"] == "element" and info["waves_per_row"] == 16 and info["chunks_per_lane"] == 64
+    st, info = rn.plan("softmax", 8, 50257, bf, workspace_bytes=ws)
+    assert st == OK and info["variant"] == "element" and info["pairs"] and info["chunks_per_lane"] == 32
+    # up to 65536 elements; the other ops split such rows
+    assert rn.plan("softmax", 8, 65536, f32, ptrs={"x": (1 << 40) + 4}, workspace_bytes=ws)[1]["variant"] == "element"
+    assert rn.plan("softmax", 8, 65537, f32, workspace_bytes=ws)[1]["variant"] == "wide_element"
+    assert rn.plan("rms", 8, 50257, f32, workspace_bytes=ws)[1]["variant"] == "wide_element"
+    assert rn.plan("softmax", 8, 65537, f32, variant="element")[0] == UNSUP
+    assert rn.plan("ln", 8, 16385, f32, variant="element")[0] == UNSUP
+
+
 def test_plan_row_strides():
     f16 = torch.float16
     # padded rows whose stride is a whole number of 16-byte chunks keep the vectorized path

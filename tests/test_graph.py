@@ -25,7 +25,7 @@ def test_graph_replays_match_eager():
     fl = {k: v.to(DEV) for k, v in workloads.make_inputs(workloads.FUSED_LN.scaled(rows=512)).items()}
     sm = {k: v.to(DEV) for k, v in workloads.make_inputs(workloads.SOFTMAX).items()}
     wide = {k: v.to(DEV) for k, v in workloads.make_inputs(workloads.C5.scaled(rows=4, N=131072)).items()}
-    wel = {k: v.to(DEV) for k, v in workloads.make_inputs(workloads.SOFTMAX.scaled(rows=4, N=50257)).items()}
+    wel = {k: v.to(DEV) for k, v in workloads.make_inputs(workloads.C2.scaled(rows=4, N=50257)).items()}
     bw = {k: v.to(DEV) for k, v in workloads.make_inputs(workloads.LN_BWD.scaled(rows=256, N=4096)).items()}
 
     def run():
@@ -34,7 +34,7 @@ def test_graph_replays_match_eager():
         y3, ro3 = rn.fused_add_layer_norm(fl["x"], fl["residual"], fl["gamma"], fl["beta"], 1e-5)
         y4 = rn.softmax_forward(sm["x"])
         y5 = rn.ln_forward(wide["x"], wide["gamma"], wide["beta"], 1e-5)  # split rows: two launches
-        y7 = rn.softmax_forward(wel["x"])  # split rows at element granularity
+        y7 = rn.ln_forward(wel["x"], wel["gamma"], wel["beta"], 1e-5)  # split rows at element granularity
         _, m6, r6 = rn.ln_forward(bw["x"], None, None, 1e-5, return_stats=True)
         dx, dg, db = rn.ln_backward(bw["dy"], bw["x"], m6, r6, bw["gamma"])  # row + column kernels
         return [y1, m1, r1, y2, ro2, y3, ro3, y4, y5, y7, dx, dg, db]

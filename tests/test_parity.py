@@ -115,7 +115,7 @@ def test_new_ops_full_size(w):
 
 
 @pytest.mark.parametrize("w,variant", [(workloads.LN_RAGGED, "element"), (workloads.LN_SPLIT, "wide"),
-                                       (workloads.SOFTMAX_VOCAB, "wide_element")], ids=lambda v: getattr(v, "name", v))
+                                       (workloads.SOFTMAX_VOCAB, "element")], ids=lambda v: getattr(v, "name", v))
 def test_general_shapes_full_size(w, variant):
     # the benchmark's general-shape workloads at full size, in the launch configuration it
     # times (automatic choice; the binding supplies the split-row workspace)
@@ -196,12 +196,28 @@ ELEM_WIDE_SHAPES = {"fp32": [(3, 16385), (2, 50257), (3, 65537)], "bf16": [(3, 2
 def test_split_rows_element(op, dtype):
     # rows of more than 16384 elements that are not whole 16-byte chunks (a vocabulary-sized
     # softmax, 50257): statistics per 8192-element segment, then the same fixed-order combine
+    # (softmax rows of up to 65536 elements stay in one workgroup: the element / pair kernels)
     for rows, N in ELEM_WIDE_SHAPES[dtype]:
         st, info = rn.plan(op, rows, N, TD[dtype], workspace_bytes=rn.forward_workspace_bytes(op, rows, N, TD[dtype]))
-        assert st == 0 and info["variant"] == "wide_element", info
+        expect = "element" if op == "softmax" and N <= 65536 else "wide_element"
+        assert st == 0 and info["variant"] == expect, info
         check_case(BASES[op].scaled(rows=rows, N=N, seed=660 + N, dtype=dtype))
     # forced on rows of whole chunks (segments end exactly on the row's end)
     check_case(BASES[op].scaled(rows=2, N=65536, seed=661, dtype=dtype), "wide_element")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
+def test_softmax_long_rows_one_workgroup(dtype):
+    # softmax rows of 16385-65536 elements that are not whole chunks (or unaligned): one
+    # 16-wave workgroup per row holding up to 64 elements (32 pairs) per lane
+    for rows, N, v in [(3, 16385, 32), (2, 32768 + 7, 64), (2, 50257, 64), (2, 65535, 64)]:
+        td = TD[dtype]
+        st, info = rn.plan("softmax", rows, N, td, workspace_bytes=rn.forward_workspace_bytes("softmax", rows, N, td))
+        assert st == 0 and info["variant"] == "element" and info["waves_per_row"] == 16, info
+        assert info["chunks_per_lane"] == (v if dtype == "fp32" else v // 2) and info["pairs"] == (dtype != "fp32")
+        check_case(workloads.SOFTMAX.scaled(rows=rows, N=N, seed=690 + N, dtype=dtype))
+    # large logits (spread +-160) on the longest rows
+    check_case(workloads.SOFTMAX.scaled(rows=2, N=65535, seed=699, dtype="fp32", x_scale=80.0))
 
 
 def test_split_rows_element_offsets_strides_constant_and_in_place():
@@ -217,7 +233,7 @@ def test_split_rows_element_offsets_strides_constant_and_in_place():
         inp = workloads.make_inputs(w)
         ref = run_oracle(w, inp)
         for off, ld in [({n: 1 for n in ROW_TENSORS}, None), ({"x": 3, "y": 0}, {n: 20003 for n in ROW_TENSORS})]:
-            out = run_placed(w, inp, offset=off, ld=ld, expect_variant="wide_element")
+            out = run_placed(w, inp, offset=off, ld=ld, expect_variant="element" if op == "softmax" else "wide_element")
             check_outputs(w, ref, *out)
     w = workloads.C5.scaled(rows=3, N=50257, seed=673)
     inp = workloads.make_inputs(w)
