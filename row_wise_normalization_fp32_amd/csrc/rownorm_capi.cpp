@@ -186,9 +186,12 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     // (grid per row). Measured on MI355X against the split-row path: softmax 51-54% -> 55-61%,
     // RMSNorm 59% -> 61%; the LayerNorm ops (42-50% vs 51-57%) and fused add + RMSNorm (66%
     // vs 67%) stay split.
-    const int64_t big_cap = (a.op == RN_OP_SOFTMAX || a.op == RN_OP_RMS_NORM)
-                                ? int64_t(64) * rn::kMaxGroupWaves * rn::kMaxBigChunks
-                                : group_cap;
+    // fp32 softmax, which holds nothing else in registers, takes 16 chunks per lane: rows of
+    // 65536 elements (256 KiB); 16-bit softmax rows of that length fit 8 chunks per lane.
+    const int64_t big_cap = a.op == RN_OP_SOFTMAX
+                                ? int64_t(64) * rn::kMaxGroupWaves * (s == 4 ? rn::kMaxSoftmaxChunks : rn::kMaxBigChunks)
+                            : a.op == RN_OP_RMS_NORM ? int64_t(64) * rn::kMaxGroupWaves * rn::kMaxBigChunks
+                                                     : group_cap;
 
     // Automatic row-group width: enough waves that each lane holds about kTargetChunks
     // chunks (measured on MI355X: 4 chunks per lane balances bytes in flight against VGPRs).

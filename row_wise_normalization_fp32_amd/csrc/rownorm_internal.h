@@ -84,7 +84,8 @@ struct Plan {
 constexpr int kMaxWaveChunks = 16;     // wave variant: up to 16 chunks per lane (1024 per row)
 constexpr int kMaxGroupWaves = 16;     // workgroup variant: up to 16 waves per row ...
 constexpr int kMaxGroupChunks = 4;     // ... holding up to 4 chunks per lane (4096 per row)
-constexpr int kMaxBigChunks = 8;       // softmax / RMSNorm: 16 waves x 8 chunks per lane (rows up to 128 KiB)
+constexpr int kMaxBigChunks = 8;       // RMSNorm: 16 waves x 8 chunks per lane (rows up to 128 KiB)
+constexpr int kMaxSoftmaxChunks = 16;  // fp32 softmax: 16 waves x 16 chunks per lane (rows up to 256 KiB)
 constexpr int kTargetChunks = 4;       // automatic choice: about 4 chunks per lane
 constexpr int kGeneralThreads = 256;   // general variant: 256 lanes per row
 constexpr int kElemTarget = 8;         // element variant: about 8 elements per lane ...

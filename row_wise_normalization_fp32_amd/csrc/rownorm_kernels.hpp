@@ -1824,6 +1824,9 @@ inline hipError_t launch_v(const Plan& plan, const Params& p, hipStream_t s) {
     if constexpr (W == 16 && !PERS && (OP == OP_SOFTMAX || OP == OP_RMS)) {
         if (plan.chunks_per_lane == 8) return RN_GO(8);
     }
+    if constexpr (W == 16 && !PERS && OP == OP_SOFTMAX && DT == DT_F32) {  // fp32 softmax rows up to 256 KiB
+        if (plan.chunks_per_lane == 16) return RN_GO(16);
+    }
 #undef RN_GO
     return hipErrorInvalidValue;
 }

@@ -224,7 +224,9 @@ def test_plan_forced_variants():
     assert rn.plan("ln", 4, 8192, torch.float16, variant="wave")[1]["chunks_per_lane"] == 16
     assert rn.plan("ln", 4, 8192, torch.float32, variant="wave")[0] == UNSUP
     assert rn.plan("softmax", 4, 32768, torch.float32, variant="workgroup")[1]["chunks_per_lane"] == 8
-    assert rn.plan("softmax", 4, 32772, torch.float32, variant="workgroup")[0] == UNSUP
+    assert rn.plan("softmax", 4, 65536, torch.float32, variant="workgroup")[1]["chunks_per_lane"] == 16
+    assert rn.plan("softmax", 4, 65540, torch.float32, variant="workgroup")[0] == UNSUP
+    assert rn.plan("softmax", 4, 65544, torch.bfloat16, variant="workgroup")[0] == UNSUP
     assert rn.plan("ln", 4, 32768, torch.float32, variant="workgroup")[0] == UNSUP
     assert rn.plan("ln", 4, 64, torch.float32, variant="general")[1]["variant"] == "general"
     assert rn.plan("ln", 4, 4096, torch.float32, variant="element")[1]["variant"] == "element"

@@ -183,7 +183,9 @@ def test_split_rows(op, dtype):
     # fixed-order combine in every segment's workgroup (the binding passes a workspace)
     for rows, N in WIDE_SHAPES[dtype]:
         st, info = rn.plan(op, rows, N, TD[dtype], workspace_bytes=rn.forward_workspace_bytes(op, rows, N, TD[dtype]))
-        assert st == 0 and info["variant"] == "wide", info
+        # (fp32 softmax rows of up to 65536 elements stay in one workgroup, 16 chunks per lane)
+        expect = "workgroup" if op == "softmax" and dtype == "fp32" and N <= 65536 else "wide"
+        assert st == 0 and info["variant"] == expect, info
         check_case(BASES[op].scaled(rows=rows, N=N, seed=620 + N, dtype=dtype))
 
 
@@ -218,6 +220,12 @@ def test_softmax_long_rows_one_workgroup(dtype):
         check_case(workloads.SOFTMAX.scaled(rows=rows, N=N, seed=690 + N, dtype=dtype))
     # large logits (spread +-160) on the longest rows
     check_case(workloads.SOFTMAX.scaled(rows=2, N=65535, seed=699, dtype="fp32", x_scale=80.0))
+    if dtype == "fp32":
+        # whole-chunk fp32 rows of up to 65536 elements: 16 chunks per lane
+        for rows, N in [(3, 40960), (2, 50304), (2, 65536)]:
+            st, info = rn.plan("softmax", rows, N, torch.float32)
+            assert st == 0 and info["variant"] == "workgroup" and info["chunks_per_lane"] == 16, info
+            check_case(workloads.SOFTMAX.scaled(rows=rows, N=N, seed=695 + N))
 
 
 def test_split_rows_element_offsets_strides_constant_and_in_place():
