@@ -288,76 +288,75 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_bwd_elem_kernel(BwdParam
     if constexpr (LN) flush_columns<RPB>(adb, red, rg, db_out, col, okc);
 }
 
-// dgamma_j = sum over the P partial rows: lane s of 16 sums rows b = s, s + 16, ... in
-// order, then the 16 lane sums are added in order; rounded once to the I/O dtype. A
-// workgroup covers 64 columns: 16 column quads x 16 lanes, so one wavefront load reads four
-// 256-byte runs of a partial row (16-byte loads when N is a multiple of 4 and the workspace
-// is 16-byte aligned; element loads otherwise).
+// dgamma_j (dbeta_j) = the sum of the P partial rows of column j: lane s of 16 sums rows
+// b = s, s + 16, ... in order, then the 16 lane sums are added in order; rounded once to the
+// I/O dtype. A workgroup covers 64 columns of one parameter (blockIdx.y: 0 dgamma, 1 dbeta):
+// 16 column quads x 16 lanes, so one wavefront load reads four 256-byte runs of partial rows
+// (16-byte loads when N is a multiple of 4 and the workspace is 16-byte aligned; element
+// loads otherwise). The two parameters run in parallel workgroups. Runs of 256 bytes or more
+// matter: 64-byte runs (16 columns per workgroup) took twice as long.
 template <int DT>
 __global__ __launch_bounds__(256) void rownorm_bwd_cols_kernel(BwdColParams p) {
     using IO = Io<DT>;
     typedef float f32x4 __attribute__((ext_vector_type(4)));
-    __shared__ f32x4 sums[16][17];
-    const int q = threadIdx.x & 15;  // column quad within the tile
-    const int s = threadIdx.x >> 4;  // partial-row lane
-    const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 64 + 4 * q;
+    constexpr int L = 16;       // partial-row lanes
+    constexpr int Q = 256 / L;  // column quads per workgroup
+    constexpr int B = 8;        // loads in flight per lane
+    __shared__ f32x4 sums[L][Q + 1];
+    void* out = blockIdx.y == 0 ? p.dgamma : p.dbeta;
+    if (out == nullptr) return;  // uniform over the workgroup
+    const int q = threadIdx.x % Q;   // column quad within the tile
+    const int s = threadIdx.x / Q;  // partial-row lane
+    const int64_t j0 = static_cast<int64_t>(blockIdx.x) * (4 * Q) + 4 * q;
     const bool vec = (p.N & 3) == 0 && (reinterpret_cast<uintptr_t>(p.ws) & 15) == 0;
-    for (int k = 0; k < 2; ++k) {
-        void* out = k == 0 ? p.dgamma : p.dbeta;
-        if (out == nullptr) continue;  // uniform
-        const float* src = p.ws + static_cast<int64_t>(k) * p.parts * p.N;
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
-        if (vec) {
-            if (j0 < p.N) {
-                // batches of 8 loads in flight, then added in order b = s, s + 16, ...
-                constexpr int B = 8;
-                int b = s;
-                for (; b + 16 * (B - 1) < p.parts; b += 16 * B) {
-                    f32x4 v[B];
-#pragma unroll
-                    for (int u = 0; u < B; ++u)
-                        v[u] = *reinterpret_cast<const f32x4*>(src + static_cast<int64_t>(b + 16 * u) * p.N + j0);
-#pragma unroll
-                    for (int u = 0; u < B; ++u) a += v[u];
-                }
-                for (; b < p.parts; b += 16) a += *reinterpret_cast<const f32x4*>(src + static_cast<int64_t>(b) * p.N + j0);
-            }
-        } else {
-            // element loads at clamped columns (values of columns past N are never
-            // stored), in the same batches and order as above
-            int64_t jc[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) jc[e] = j0 + e < p.N ? j0 + e : p.N - 1;
-            constexpr int B = 8;
+    const float* src = p.ws + static_cast<int64_t>(blockIdx.y) * p.parts * p.N;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    if (vec) {
+        if (j0 < p.N) {  // then j0 + 3 < N as well
             int b = s;
-            for (; b + 16 * (B - 1) < p.parts; b += 16 * B) {
+            for (; b + L * (B - 1) < p.parts; b += L * B) {
                 f32x4 v[B];
 #pragma unroll
-                for (int u = 0; u < B; ++u) {
-                    const float* r = src + static_cast<int64_t>(b + 16 * u) * p.N;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[u][e] = r[jc[e]];
-                }
+                for (int u = 0; u < B; ++u)
+                    v[u] = *reinterpret_cast<const f32x4*>(src + static_cast<int64_t>(b + L * u) * p.N + j0);
 #pragma unroll
                 for (int u = 0; u < B; ++u) a += v[u];
             }
-            for (; b < p.parts; b += 16) {
-                const float* r = src + static_cast<int64_t>(b) * p.N;
+            for (; b < p.parts; b += L) a += *reinterpret_cast<const f32x4*>(src + static_cast<int64_t>(b) * p.N + j0);
+        }
+    } else {
+        // element loads at clamped columns (values of columns past N are never stored), in
+        // the same batches and order as above
+        int64_t jc[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) a[e] += r[jc[e]];
+        for (int e = 0; e < 4; ++e) jc[e] = j0 + e < p.N ? j0 + e : p.N - 1;
+        int b = s;
+        for (; b + L * (B - 1) < p.parts; b += L * B) {
+            f32x4 v[B];
+#pragma unroll
+            for (int u = 0; u < B; ++u) {
+                const float* r = src + static_cast<int64_t>(b + L * u) * p.N;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[u][e] = r[jc[e]];
             }
-        }
-        sums[s][q] = a;
-        __syncthreads();
-        if (s == 0) {
-            f32x4 r = sums[0][q];
 #pragma unroll
-            for (int u = 1; u < 16; ++u) r += sums[u][q];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (j0 + e < p.N) IO::store1(out, j0 + e, r[e]);
+            for (int u = 0; u < B; ++u) a += v[u];
         }
-        __syncthreads();  // sums is rewritten for the next parameter
+        for (; b < p.parts; b += L) {
+            const float* r = src + static_cast<int64_t>(b) * p.N;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[e] += r[jc[e]];
+        }
+    }
+    sums[s][q] = a;
+    __syncthreads();
+    if (s == 0) {
+        f32x4 r = sums[0][q];
+#pragma unroll
+        for (int u = 1; u < L; ++u) r += sums[u][q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (j0 + e < p.N) IO::store1(out, j0 + e, r[e]);
     }
 }
 
@@ -477,8 +476,8 @@ inline hipError_t launch_bwd_dtype(int op, const Plan& plan, const BwdParams& p0
     if (cp.dgamma == nullptr && cp.dbeta == nullptr) return hipSuccess;
     void* argv[] = {&cp};
     const unsigned blocks = static_cast<unsigned>((cp.N + 63) / 64);
-    return hipLaunchKernel(reinterpret_cast<const void*>(rownorm_bwd_cols_kernel<DT>), dim3(blocks), dim3(256), argv,
-                           0, s);
+    return hipLaunchKernel(reinterpret_cast<const void*>(rownorm_bwd_cols_kernel<DT>),
+                           dim3(blocks, cp.dbeta != nullptr ? 2u : 1u), dim3(256), argv, 0, s);
 }
 
 }  // namespace rn

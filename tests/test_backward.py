@@ -132,6 +132,15 @@ def test_backward_partial_outputs_and_zero_rows():
     depth = _depth("ln", 32, 2048, "bf16")
     check_colsum(dg, ref["dgamma"], a_g, depth, "dgamma")
     check_colsum(db, ref["dbeta"], a_b, depth, "dbeta")
+    # one parameter gradient alone (the column pass runs one workgroup column per parameter)
+    _, dg, db = rn.ln_backward(dev["dy"], dev["x"], m, r, dev["gamma"], want_dx=False, want_dgamma=False)
+    torch.cuda.synchronize()
+    assert dg is None
+    check_colsum(db, ref["dbeta"], a_b, depth, "dbeta")
+    _, dg, db = rn.ln_backward(dev["dy"], dev["x"], m, r, dev["gamma"], want_dx=False, want_dbeta=False)
+    torch.cuda.synchronize()
+    assert db is None
+    check_colsum(dg, ref["dgamma"], a_g, depth, "dgamma")
     # rows == 0: the parameter gradients are sums over no rows
     e = torch.empty(0, 64, device=DEV, dtype=torch.bfloat16)
     z = torch.empty(0, device=DEV)
