@@ -73,6 +73,10 @@
 extern "C" {
 #endif
 
+/* The library is built with hidden symbol visibility; the entry points declared here are
+ * the only symbols it exports. */
+#pragma GCC visibility push(default)
+
 /* I/O element type. */
 typedef enum rn_dtype { RN_F32 = 0, RN_F16 = 1, RN_BF16 = 2 } rn_dtype;
 
@@ -289,6 +293,8 @@ const char* rn_status_string(int status);
 
 /* Library version as major * 10000 + minor * 100 + patch. */
 int rn_version(void);
+
+#pragma GCC visibility pop
 
 #ifdef __cplusplus
 }
