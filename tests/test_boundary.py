@@ -8,6 +8,8 @@
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 import torch
@@ -37,6 +39,17 @@ def test_library_exports_every_declared_function():
         assert n in names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_library_exports_nothing_else():
+    # the ELF dynamic symbol table holds only the declared C entry points among the
+    # library's own defined functions (internal C++ helpers are hidden)
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", rn.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    funcs = {l.split()[-1] for l in out.splitlines() if len(l.split()) == 3 and l.split()[1] == "T"}
+    assert funcs == set(_declared_functions()), sorted(funcs ^ set(_declared_functions()))
 
 
 def test_status_strings_and_version():
