@@ -22,11 +22,15 @@ memory-side cache. Inputs are resident in HBM before the timed region starts.
 
 Timed region: about 50 ms of plain device copies (the GPU's clocks rise over the first ~10 ms
 of work after the idle host-side set-up), W warmup steps untimed, then exactly K steps
-bracketed by torch.cuda.synchronize(); ms_per_step is the wall time over K. Two HIP events recorded on
-the stream the kernels run on (torch's current stream, which the binding passes to the C
-ABI) bracket the same K launches: their elapsed time over K is the per-launch kernel
-duration used for the roofline (back-to-back launches; it includes the few-hundred-ns
-dispatch gaps between them).
+launched eagerly from Python, bracketed by torch.cuda.synchronize() ("eager": wall time over
+K), then the same K steps captured into one HIP graph, replayed once untimed and once
+between torch.cuda.synchronize() calls: ms_per_step is that replay's wall time over K (the
+eager time when no graph can be captured; "timing" says which). A graph is how a serving or
+training loop runs a fixed sequence of launches: each step still launches its kernel on its
+own rotating buffers; only the per-call Python and dispatch overhead between steps (about
+2 us per launch here) is gone. Two HIP events recorded on the launch stream (torch's current
+stream, which the binding passes to the C ABI) around the timed replay give the per-launch
+kernel duration used for the roofline; rocprofv3's kernel durations agree with it.
 
 value = algorithmic bytes per step / ms_per_step (GB/s, 1 GB = 1e9 B). Algorithmic bytes:
 LayerNorm 2*rows*N*s + 2*N*s + 8*rows; fused 4*rows*N*s + N*s + 4*rows (with rstd); fused
@@ -173,9 +177,10 @@ SET_TENSORS = {"ln": 2, "rms": 2, "softmax": 2, "fused_add_rms": 4, "fused_add_l
 
 
 def graph_time(rn, w, sets, steps):
-    """Per-launch device time with the host taken out: `steps` launches (rotating over the
-    buffer sets) captured into one HIP graph, replayed once to warm up, then one timed
-    replay between two events. None if the capture fails."""
+    """`steps` launches (rotating over the buffer sets) captured into one HIP graph, replayed
+    once to warm up, then one timed replay bracketed by torch.cuda.synchronize() (wall clock)
+    and by two HIP events on the launch stream. Returns {"wall_ms", "event_ms"} per step, or
+    None if the capture fails."""
     import torch
 
     try:
@@ -186,16 +191,33 @@ def graph_time(rn, w, sets, steps):
         g.replay()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
         a.record()
         g.replay()
         b.record()
         torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / steps
+        wall = time.perf_counter() - t0
+        out = {"wall_ms": wall * 1e3 / steps, "event_ms": a.elapsed_time(b) / steps}
         del g
-        return ms
+        return out
     except Exception as e:  # capture not possible here: report without it
         log(f"[bench] graph timing unavailable: {e}")
         return None
+
+
+TIMING = {
+    "graph": "K steps captured in one HIP graph, one replay timed by wall clock between "
+             "torch.cuda.synchronize() calls (after an untimed eager pass and an untimed replay)",
+    "eager": "K eager launches timed by wall clock between torch.cuda.synchronize() calls",
+}
+
+
+def eager_fields(r):
+    """The same K steps launched eagerly from Python (one binding call each)."""
+    v = r["bytes"] / (r["eager_ms_per_step"] * 1e-3) / 1e9
+    return {"ms_per_step": round(r["eager_ms_per_step"], 5), "value": round(v, 2),
+            "pct_of_peak": round(100.0 * v / PEAK_HBM_GBS, 2)}
 
 
 def kernel_time(r):
@@ -255,9 +277,12 @@ def measure(w, steps, warmup, cache, dev, graph=True):
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / steps
+    eager_ms = wall * 1e3 / steps
     kernel_ms = ev0.elapsed_time(ev1) / steps
-    graph_ms = graph_time(rn, w, sets, steps) if graph else None
+    gt = graph_time(rn, w, sets, steps) if graph else None
+    graph_ms = gt["event_ms"] if gt else None
+    # the steps as one replayed HIP graph when it can be captured, else the eager launches
+    ms_per_step = gt["wall_ms"] if gt else eager_ms
     s0 = sets[0]
     td = workloads.TORCH_DTYPES[w.dtype]
     if w.op in ("ln_bwd", "rms_bwd"):
@@ -276,7 +301,8 @@ def measure(w, steps, warmup, cache, dev, graph=True):
     del sets
     torch.cuda.empty_cache()
     return {
-        "bytes": nbytes, "ms_per_step": ms_per_step, "kernel_ms": kernel_ms, "graph_ms": graph_ms,
+        "bytes": nbytes, "ms_per_step": ms_per_step, "timing": "graph" if gt else "eager",
+        "eager_ms_per_step": eager_ms, "kernel_ms": kernel_ms, "graph_ms": graph_ms,
         "nsets": nsets, "plan": info,
     }
 
@@ -339,7 +365,9 @@ def cpu_baseline(w, seconds, single_thread=False):
 def copy_reference(nbytes_each, steps, dev):
     """GB/s of a plain device copy (torch -> the HIP runtime's copy kernel) moving the same
     bytes as a LayerNorm launch (read nbytes_each, write nbytes_each), with the same buffer
-    rotation: the practical read+write ceiling on this GPU, for context."""
+    rotation and the same timing as the steps (one replay of a HIP graph of K copies, wall
+    clock between synchronizations; eager copies if no graph can be captured): the practical
+    read+write ceiling on this GPU, for context."""
     import torch
 
     nsets = max(2, math.ceil(COLD_FOOTPRINT / (2 * nbytes_each)))
@@ -348,12 +376,22 @@ def copy_reference(nbytes_each, steps, dev):
     for i in range(5):
         dst[i % nsets].copy_(src[i % nsets])
     torch.cuda.synchronize()
+    run = lambda: [dst[i % nsets].copy_(src[i % nsets]) for i in range(steps)]  # noqa: E731
+    g = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run()
+        g.replay()
+        run = g.replay
+    except Exception as e:  # capture not possible here: eager copies
+        log(f"[bench] copy reference without a graph: {e}")
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        dst[i % nsets].copy_(src[i % nsets])
+    run()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
-    del src, dst
+    del g, src, dst
     torch.cuda.empty_cache()
     return 2 * nbytes_each / (ms * 1e-3) / 1e9
 
@@ -459,6 +497,8 @@ def main():
         },
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "rows_per_s": round(w.rows / (r["ms_per_step"] * 1e-3), 1),
+        "timing": TIMING[r["timing"]],
+        "eager": eager_fields(r),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
@@ -490,6 +530,7 @@ def main():
             "achieved_kernel_GBs": round(fa, 2),
             "frac_kernel": round(fa / PEAK_HBM_GBS, 4), "bytes_per_launch": rf["bytes"],
             "kernel": kernel_name(f, rf["plan"]), "traffic": counter_traffic("fused_fp16_8192x4096"),
+            "timing": rf["timing"], "eager": eager_fields(rf),
         }
     if not args.no_more:
         more = {}
@@ -510,6 +551,7 @@ def main():
                 "kernel": kernel_name(x, rx["plan"]),
                 # HBM bytes per call from the counter record (backward: row + column kernels)
                 "traffic": counter_traffic(x.name),
+                "timing": rx["timing"], "eager": eager_fields(rx),
             }
         out["more"] = more
     if not args.no_configs:
@@ -550,13 +592,14 @@ def main():
             log(f"[bench] sweep {x.name} ({cache}) ...")
             rx = measure(x, min(args.steps, 100), min(args.warmup, 10), cache, dev, graph=True)
             xa = rx["bytes"] / (rx["kernel_ms"] * 1e-3) / 1e9
-            xv = rx["bytes"] / (rx["ms_per_step"] * 1e-3) / 1e9
+            xv = rx["bytes"] / (rx["eager_ms_per_step"] * 1e-3) / 1e9
             gm = rx["graph_ms"]
             sweep[x.name] = {"elements": x.rows * x.N, "cache": cache,
                              # eager launches: HIP events around the K timed launches
                              "stream_ms_per_launch": round(rx["kernel_ms"], 5),
-                             "frac_stream": round(xa / PEAK_HBM_GBS, 4), "value": round(xv, 2),
-                             "pct_of_peak": round(100.0 * xv / PEAK_HBM_GBS, 2),
+                             "frac_stream": round(xa / PEAK_HBM_GBS, 4),
+                             # wall clock over the eager launches
+                             "value": round(xv, 2), "pct_of_peak": round(100.0 * xv / PEAK_HBM_GBS, 2),
                              # device time per launch from a replayed HIP graph (no host gaps)
                              "graph_ms": None if gm is None else round(gm, 5),
                              "frac_graph": None if gm is None else round(rx["bytes"] / (gm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
