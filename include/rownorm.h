@@ -240,12 +240,16 @@ int fused_add_rms_norm_variant(const void* x, const void* residual, const void* 
  *   dgamma, dbeta (RMSNorm: dweight)  [N] dtype, nullable; rows == 0 writes zeros.
  *   workspace    device memory of at least rn_backward_workspace_bytes(op, rows, N) bytes,
  *                4-byte aligned (16-byte alignment is faster), owned by the caller;
- *                required only when a parameter gradient is requested (RN_ERR_WORKSPACE
- *                otherwise). Its contents on entry do not
- *                matter; on return they are unspecified. Calls that share a workspace must
- *                be ordered (same stream).
- * Rows up to 16384 elements (longer rows: RN_ERR_UNSUPPORTED). Column sums are formed in
- * fp32 in a fixed order (no atomics): results are bitwise reproducible on a given device.
+ *                required when a parameter gradient is requested or when rows are longer
+ *                than 16384 elements (RN_ERR_WORKSPACE otherwise). Its contents on entry
+ *                do not matter; on return they are unspecified. Calls that share a
+ *                workspace must be ordered (same stream).
+ * Rows of up to 16384 elements are held by one row group. Longer rows (any N) are split
+ * into 8192-element segments over three launches: per-segment sums of g and g * xhat into
+ * the workspace, then dx from the row's combined sums with the parameter-gradient columns
+ * accumulated per segment, then the column sums (x and dy are read twice; plan variant
+ * RN_VARIANT_WIDE). Row and column sums are formed in fp32 in a fixed order (no atomics):
+ * results are bitwise reproducible on a given device.
  */
 size_t rn_backward_workspace_bytes(int op, int64_t rows, int64_t N);
 int ln_backward(const void* dy, const void* x, const void* gamma, const float* mean, const float* rstd, void* dx,
@@ -283,7 +287,9 @@ int rn_plan(int op, const void* x, const void* residual, const void* gamma, cons
             rn_plan_info* out);
 
 /* The same for a backward call (op: RN_OP_LAYER_NORM or RN_OP_RMS_NORM); grid_blocks is the
- * row kernel's workgroup count before the launch caps it at what the device keeps resident. */
+ * row kernel's workgroup count before the launch caps it at what the device keeps resident
+ * (split rows, RN_VARIANT_WIDE: the workgroups per segment at most; exact: 1 when rows move
+ * in 16-byte groups). */
 int rn_plan_backward(int op, const void* dy, const void* x, const void* gamma, const float* mean, const float* rstd,
                      const void* dx, const void* dgamma, const void* dbeta, int64_t rows, int64_t N, int dtype,
                      const void* workspace, size_t workspace_bytes, rn_plan_info* out);

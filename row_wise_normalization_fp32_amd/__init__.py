@@ -329,8 +329,14 @@ def softmax_forward(x: torch.Tensor, *, out: Optional[torch.Tensor] = None, row_
     return (y, row_max, row_sum) if want else y
 
 
+# Backward rows longer than this many elements are split across workgroups, which keep
+# per-segment records in the workspace: such calls need it even without parameter gradients.
+BWD_ROW_CAP = 16384
+
+
 def backward_workspace_bytes(op: str, rows: int, N: int) -> int:
-    """Workspace bytes a backward call with parameter gradients needs (op "ln" or "rms")."""
+    """Workspace bytes a backward call with parameter gradients (or with rows longer than
+    BWD_ROW_CAP elements) needs (op "ln" or "rms")."""
     return int(_lib.rn_backward_workspace_bytes(OPS[op], rows, N))
 
 
@@ -374,7 +380,7 @@ def ln_backward(dy: torch.Tensor, x: torch.Tensor, mean: torch.Tensor, rstd: tor
     dg = torch.empty(N, dtype=x.dtype, device=x.device) if want_dgamma else None
     db = torch.empty(N, dtype=x.dtype, device=x.device) if want_dbeta else None
     ws, ws_bytes = (None, 0)
-    if want_dgamma or want_dbeta:
+    if want_dgamma or want_dbeta or N > BWD_ROW_CAP:
         ws, ws_bytes = _workspace(x, "ln", rows, N, workspace)
     with torch.cuda.device(x.device):
         st = _lib.ln_backward(_ptr(dy), _ptr(x), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(dg), _ptr(db),
@@ -400,7 +406,7 @@ def rms_norm_backward(dy: torch.Tensor, x: torch.Tensor, rstd: torch.Tensor, wei
         dx = None
     dw = torch.empty(N, dtype=x.dtype, device=x.device) if want_dweight else None
     ws, ws_bytes = (None, 0)
-    if want_dweight:
+    if want_dweight or N > BWD_ROW_CAP:
         ws, ws_bytes = _workspace(x, "rms", rows, N, workspace)
     with torch.cuda.device(x.device):
         st = _lib.rms_norm_backward(_ptr(dy), _ptr(x), _ptr(weight), _ptr(rstd), _ptr(dx), _ptr(dw), rows, N,

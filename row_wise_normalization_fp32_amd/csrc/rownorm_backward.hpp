@@ -360,6 +360,172 @@ __global__ __launch_bounds__(256) void rownorm_bwd_cols_kernel(BwdColParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Split-row backward: rows longer than one workgroup holds (more than 16384 elements). A row
+// is cut into S segments of kBwdSeg elements (512 lanes x 16), and the work takes three
+// launches:
+//   1. rownorm_bwd_wide_stats_kernel: per (row, segment) the segment's sum of g = dy * gamma
+//      and of g * xhat, one record of two floats per segment in the workspace;
+//   2. rownorm_bwd_wide_dx_kernel: workgroup (q, s) owns segment s of rows q, q + Q, ...: it
+//      adds the row's S records in a fixed order (so every workgroup of the row gets the
+//      same bits), writes dx for its segment, and accumulates its columns' dgamma / dbeta
+//      terms in fp32 registers across its rows; at the end it writes its columns of partial
+//      row q to the workspace ([2][Q][N], the layout the column kernel reads);
+//   3. rownorm_bwd_cols_kernel sums the Q partial rows.
+// x and dy are read twice. Rows, tensors and segments that are whole 16-byte groups move
+// in 16-byte accesses (lane t holds groups i * 512 + t of the segment); otherwise element by
+// element (lane t holds elements k * 512 + t). Elements past the row read as 0, which adds
+// nothing to any sum (dy = 0), and are never written.
+// ---------------------------------------------------------------------------------------
+
+template <int DT>
+struct BwdSeg {
+    using IO = Io<DT>;
+    static constexpr int SB = DT == DT_F32 ? 4 : 2;  // bytes per element
+    static constexpr int G = 16 / SB;                // elements per 16-byte group
+    static constexpr int V = kBwdSegPerLane;
+
+    __device__ static __forceinline__ void load(const void* base, uint32_t nbytes, bool vec, int t, float (&f)[V]) {
+        const Rsrc r = make_rsrc(base, nbytes);
+        if (vec) {
+#pragma unroll
+            for (int i = 0; i < V / G; ++i) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (i * kBwdSegLanes + t) * 16, 0, 0);
+                IO::unpack(v, &f[i * G]);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < V; ++k) f[k] = IO::bload(r, static_cast<uint32_t>(k * kBwdSegLanes + t));
+        }
+    }
+
+    __device__ static __forceinline__ void store(void* base, uint32_t nbytes, bool vec, int t, const float (&f)[V]) {
+        const Rsrc r = make_rsrc(base, nbytes);
+        if (vec) {
+#pragma unroll
+            for (int i = 0; i < V / G; ++i)
+                __builtin_amdgcn_raw_buffer_store_b128(IO::pack(&f[i * G]), r, (i * kBwdSegLanes + t) * 16, 0, 0);
+        } else {
+#pragma unroll
+            for (int k = 0; k < V; ++k) IO::bstore(r, static_cast<uint32_t>(k * kBwdSegLanes + t), f[k]);
+        }
+    }
+
+    // fp32 values at the segment's element positions (the partial column rows)
+    __device__ static __forceinline__ void store_f32(float* base, uint32_t n, bool vec, int t, const float (&f)[V]) {
+        const Rsrc r = make_rsrc(base, n * 4);
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const uint32_t j = vec ? static_cast<uint32_t>((k / G * kBwdSegLanes + t) * G + k % G)
+                                   : static_cast<uint32_t>(k * kBwdSegLanes + t);
+            Io<DT_F32>::bstore(r, j, f[k]);
+        }
+    }
+};
+
+template <int DT, int OP, bool HG>
+__global__ __launch_bounds__(kBwdSegLanes) void rownorm_bwd_wide_stats_kernel(BwdParams p) {
+    using SG = BwdSeg<DT>;
+    constexpr int V = SG::V;
+    constexpr bool LN = OP == OP_LN;
+    const int lane = threadIdx.x & 63;
+    const int wr = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int t = threadIdx.x;
+    __shared__ WavePart part[2][kBwdSegLanes / 64];
+    int buf = 0;
+    const bool vec = p.vec != 0;
+    const int64_t total = p.rows * p.S;
+    for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+        const int64_t row = b / p.S;
+        const int seg = static_cast<int>(b - row * p.S);
+        const int64_t e0 = static_cast<int64_t>(seg) * kBwdSeg;
+        const uint32_t nb = static_cast<uint32_t>((p.N - e0 < kBwdSeg ? p.N - e0 : kBwdSeg) * SG::SB);
+        const int64_t off = (row * p.N + e0) * SG::SB;
+        float xf[V], df[V], gf[HG ? V : 1];
+        SG::load(static_cast<const char*>(p.x) + off, nb, vec, t, xf);
+        SG::load(static_cast<const char*>(p.dy) + off, nb, vec, t, df);
+        if constexpr (HG) SG::load(static_cast<const char*>(p.gamma) + e0 * SG::SB, nb, vec, t, gf);
+        const float mean = LN ? p.mean[row] : 0.f;
+        const float rstd = p.rstd[row];
+        float sg = 0.f, sgx = 0.f;
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const float xh = LN ? (xf[k] - mean) * rstd : xf[k] * rstd;
+            const float g = HG ? df[k] * gf[k] : df[k];
+            sg += g;
+            sgx = fmaf(g, xh, sgx);
+        }
+        float Sg = wave_sum(sg), Sgx = wave_sum(sgx);
+        group_sum2<kBwdSegLanes / 64>(part, buf, lane, wr, Sg, Sgx);
+        if (t == 0) {
+            p.rec[2 * (row * p.S + seg)] = Sg;
+            p.rec[2 * (row * p.S + seg) + 1] = Sgx;
+        }
+    }
+}
+
+template <int DT, int OP, bool HG>
+__global__ __launch_bounds__(kBwdSegLanes) void rownorm_bwd_wide_dx_kernel(BwdParams p) {
+    using SG = BwdSeg<DT>;
+    constexpr int V = SG::V;
+    constexpr bool LN = OP == OP_LN;
+    const int lane = threadIdx.x & 63;
+    const int t = threadIdx.x;
+    const bool vec = p.vec != 0;
+    const int S = p.S;
+    const int seg = static_cast<int>(blockIdx.x % static_cast<unsigned>(S));
+    const int q = static_cast<int>(blockIdx.x / static_cast<unsigned>(S));
+    const int Q = static_cast<int>(gridDim.x / static_cast<unsigned>(S));
+    const int64_t e0 = static_cast<int64_t>(seg) * kBwdSeg;
+    const int Ns = static_cast<int>(p.N - e0 < kBwdSeg ? p.N - e0 : kBwdSeg);
+    const uint32_t nb = static_cast<uint32_t>(Ns * SG::SB);
+    float gf[HG ? V : 1];
+    if constexpr (HG) SG::load(static_cast<const char*>(p.gamma) + e0 * SG::SB, nb, vec, t, gf);
+    float adg[V], adb[LN ? V : 1];
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        adg[k] = 0.f;
+        if constexpr (LN) adb[k] = 0.f;
+    }
+    for (int64_t row = q; row < p.rows; row += Q) {
+        const int64_t off = (row * p.N + e0) * SG::SB;
+        float xf[V], df[V];
+        SG::load(static_cast<const char*>(p.x) + off, nb, vec, t, xf);
+        SG::load(static_cast<const char*>(p.dy) + off, nb, vec, t, df);
+        // the row's sums: lane k adds records k, k + 64, ... in order, then a butterfly
+        // whose every step adds two equal operand pairs (a + b == b + a): same bits in every
+        // lane and every workgroup of the row
+        const float* rec = p.rec + 2 * row * S;
+        float Sg = 0.f, Sgx = 0.f;
+        for (int k = lane; k < S; k += 64) {
+            Sg += rec[2 * k];
+            Sgx += rec[2 * k + 1];
+        }
+#pragma unroll
+        for (int step = 1; step < 64; step <<= 1) {
+            Sg += __shfl_xor(Sg, step);
+            Sgx += __shfl_xor(Sgx, step);
+        }
+        const float mean = LN ? p.mean[row] : 0.f;
+        const float rstd = p.rstd[row];
+        const float c1 = LN ? Sg * p.inv_n : 0.f;
+        const float c2 = Sgx * p.inv_n;
+        float r[V];
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            const float xh = LN ? (xf[k] - mean) * rstd : xf[k] * rstd;
+            const float g = HG ? df[k] * gf[k] : df[k];
+            r[k] = rstd * ((g - c1) - xh * c2);
+            adg[k] = fmaf(df[k], xh, adg[k]);
+            if constexpr (LN) adb[k] += df[k];
+        }
+        if (p.dx) SG::store(static_cast<char*>(p.dx) + off, nb, vec, t, r);
+    }
+    if (p.ws == nullptr) return;  // uniform over the grid
+    SG::store_f32(p.ws + static_cast<int64_t>(q) * p.N + e0, static_cast<uint32_t>(Ns), vec, t, adg);
+    if constexpr (LN) SG::store_f32(p.ws + (static_cast<int64_t>(Q) + q) * p.N + e0, static_cast<uint32_t>(Ns), vec, t, adb);
+}
+
 constexpr int rows_per_block_bwd(int W) { return W >= 16 ? 1 : 16 / W; }  // 16-wave workgroups
 
 using BwdKernel = void (*)(BwdParams);
@@ -446,9 +612,51 @@ inline hipError_t bwd_resident(BwdKernel k, int dev, const Plan& plan, int* per_
 // Row kernel, then column kernel. The row kernel's grid P is what the device keeps resident
 // (compute units x workgroups per unit for this instance, queried once per instance and
 // device), capped by the plan: more workgroups would only add partial rows to sum.
+// Split rows: statistics launch, dx launch (Q workgroups per segment: what the device keeps
+// resident, capped by the plan's workspace bound), column launch.
+template <int DT>
+inline hipError_t launch_bwd_wide(int op, const Plan& plan, const BwdParams& p0, const BwdColParams& cp0,
+                                  hipStream_t s) {
+    BwdParams p = p0;
+    BwdColParams cp = cp0;
+    const bool hg = p.gamma != nullptr;
+    const bool ln = op == OP_LN;
+#define RN_BW(KER) \
+    (ln ? (hg ? KER<DT, OP_LN, true> : KER<DT, OP_LN, false>) : (hg ? KER<DT, OP_RMS, true> : KER<DT, OP_RMS, false>))
+    const BwdKernel ks = RN_BW(rownorm_bwd_wide_stats_kernel);
+    const BwdKernel kd = RN_BW(rownorm_bwd_wide_dx_kernel);
+#undef RN_BW
+    if (p.S < 1 || p.rec == nullptr) return hipErrorInvalidValue;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    int per_cu = 0, cus = 0;
+    e = bwd_resident(kd, dev, plan, &per_cu, &cus);
+    if (e != hipSuccess) return e;
+    int64_t Q = static_cast<int64_t>(cus) * per_cu / p.S;
+    if (Q < 1) Q = 1;
+    if (Q > plan.grid) Q = plan.grid;
+    const int64_t total = p.rows * p.S;
+    const unsigned g1 = static_cast<unsigned>(total < kMaxGrid ? total : kMaxGrid);
+    void* argv[] = {&p};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(ks), dim3(g1), dim3(kBwdSegLanes), argv, 0, s);
+    if (e != hipSuccess) return e;
+    p.parts = static_cast<int>(Q);
+    e = hipLaunchKernel(reinterpret_cast<const void*>(kd), dim3(static_cast<unsigned>(Q * p.S)), dim3(kBwdSegLanes),
+                        argv, 0, s);
+    if (e != hipSuccess) return e;
+    if (cp.dgamma == nullptr && cp.dbeta == nullptr) return hipSuccess;
+    cp.parts = p.parts;
+    void* cargv[] = {&cp};
+    const unsigned blocks = static_cast<unsigned>((cp.N + 63) / 64);
+    return hipLaunchKernel(reinterpret_cast<const void*>(rownorm_bwd_cols_kernel<DT>),
+                           dim3(blocks, cp.dbeta != nullptr ? 2u : 1u), dim3(256), cargv, 0, s);
+}
+
 template <int DT>
 inline hipError_t launch_bwd_dtype(int op, const Plan& plan, const BwdParams& p0, const BwdColParams& cp0,
                                    hipStream_t s) {
+    if (plan.variant == V_WIDE && p0.rows > 0) return launch_bwd_wide<DT>(op, plan, p0, cp0, s);
     BwdParams p = p0;
     BwdColParams cp = cp0;
     if (p.rows > 0 && (p.dx != nullptr || p.ws != nullptr)) {

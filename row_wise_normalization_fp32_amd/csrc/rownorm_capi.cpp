@@ -400,10 +400,32 @@ Args make_args(int op, const void* x, const void* residual, const void* gamma, c
 
 int64_t bwd_parts_cap(int64_t rows) { return rows < rn::kBwdMaxParts ? rows : rn::kBwdMaxParts; }
 
+// Rows longer than the row kernels hold (16384 elements, whatever the alignment) take the
+// split-row backward.
+constexpr int64_t kBwdRowCap = int64_t(64) * rn::kMaxGroupWaves * rn::kElemMaxPerLane;
+bool bwd_wide(int64_t N) { return N > kBwdRowCap; }
+int64_t bwd_wide_segments(int64_t N) { return (N + rn::kBwdSeg - 1) / rn::kBwdSeg; }
+// Split rows: workgroups per segment (partial rows) at most.
+int64_t bwd_wide_q_cap(int64_t rows, int64_t N) {
+    int64_t q = rn::kBwdWideMaxGroups / bwd_wide_segments(N);
+    if (q < 1) q = 1;
+    return q < rows ? q : rows;
+}
+// Split rows: the workspace holds the partial rows, then (from a 256-byte boundary) the
+// segment records.
+size_t bwd_partial_bytes(int op, int64_t rows, int64_t N) {
+    const int64_t sets = op == RN_OP_LAYER_NORM ? 2 : 1;
+    const int64_t parts = bwd_wide(N) ? bwd_wide_q_cap(rows, N) : bwd_parts_cap(rows);
+    return static_cast<size_t>(sets * parts * N * 4);
+}
+size_t bwd_records_offset(int op, int64_t rows, int64_t N) {
+    return (bwd_partial_bytes(op, rows, N) + 255) / 256 * 256;
+}
+
 size_t bwd_workspace_bytes(int op, int64_t rows, int64_t N) {
     if (rows <= 0 || N <= 0) return 0;
-    const int64_t sets = op == RN_OP_LAYER_NORM ? 2 : 1;
-    return static_cast<size_t>(sets * bwd_parts_cap(rows) * N * 4);
+    if (!bwd_wide(N)) return bwd_partial_bytes(op, rows, N);
+    return bwd_records_offset(op, rows, N) + static_cast<size_t>(rows * bwd_wide_segments(N) * 8);
 }
 
 struct BwdArgs {
@@ -434,7 +456,8 @@ int validate_and_plan_bwd(BwdArgs& a, Plan* plan, int64_t* chunks) {
     *plan = Plan{};
     *chunks = 0;
     const bool want_cols = a.dgamma != nullptr || a.dbeta != nullptr;
-    if (want_cols && rows > 0) {
+    const bool need_ws = want_cols || bwd_wide(N);  // split rows keep their records there
+    if (need_ws && rows > 0) {
         if (!a.ws) return RN_ERR_WORKSPACE;
         if (a.ws_bytes < bwd_workspace_bytes(a.op, rows, N)) return RN_ERR_WORKSPACE;
     }
@@ -446,7 +469,7 @@ int validate_and_plan_bwd(BwdArgs& a, Plan* plan, int64_t* chunks) {
         {a.dy, mat, 0, false, R_RES}, {a.x, mat, 0, false, R_X},       {a.gamma, N * s, 0, false, R_G},
         {a.mean, rows * 4, 0, false, R_MEAN}, {a.rstd, rows * 4, 0, false, R_RSTD}, {a.dx, mat, 0, true, R_Y},
         {a.dgamma, N * s, 0, true, R_B}, {a.dbeta, N * s, 0, true, R_B},
-        {want_cols ? a.ws : nullptr, static_cast<int64_t>(bwd_workspace_bytes(a.op, rows, N)), 0, true, R_RO},
+        {need_ws ? a.ws : nullptr, static_cast<int64_t>(bwd_workspace_bytes(a.op, rows, N)), 0, true, R_RO},
     };
     const int nb = sizeof(bufs) / sizeof(bufs[0]);
     for (int i = 0; i < nb; ++i) {
@@ -486,7 +509,19 @@ int validate_and_plan_bwd(BwdArgs& a, Plan* plan, int64_t* chunks) {
         plan->waves_per_row = W;
         plan->chunks_per_lane = next_pow2((N + 64 * W - 1) / (64 * W));
     } else {
-        return RN_ERR_UNSUPPORTED;
+        // split rows: 8192-element segments of 512 lanes x 16 elements; 16-byte groups when
+        // rows and tensors are whole 16-byte groups. grid = workgroups per segment at most.
+        plan->variant = rn::V_WIDE;
+        plan->waves_per_row = rn::kBwdSegLanes / 64;
+        plan->chunks_per_lane = rn::kBwdSegPerLane;
+        plan->rows_per_block = 1;
+        plan->block_threads = rn::kBwdSegLanes;
+        plan->grid = bwd_wide_q_cap(rows, N);
+        plan->persistent = true;
+        plan->exact = (N * s) % 16 == 0 && vec_ok;
+        plan->lds_bytes = 0;
+        *chunks = 0;
+        return RN_OK;
     }
     const int W = plan->waves_per_row;
     plan->rows_per_block = W >= 16 ? 1 : 16 / W;
@@ -519,6 +554,14 @@ int run_bwd(BwdArgs a, hipStream_t stream) {
     p.C = C;
     p.inv_n = static_cast<float>(1.0 / static_cast<double>(a.N));
     p.parts = 0;  // set at launch from the device's resident capacity
+    p.rec = nullptr;
+    p.S = 0;
+    p.vec = 0;
+    if (plan.variant == rn::V_WIDE) {
+        p.rec = reinterpret_cast<float*>(static_cast<char*>(a.ws) + bwd_records_offset(a.op, a.rows, a.N));
+        p.S = static_cast<int>(bwd_wide_segments(a.N));
+        p.vec = plan.exact ? 1 : 0;
+    }
     rn::BwdColParams cp;
     cp.ws = p.ws;
     cp.dgamma = a.dgamma;

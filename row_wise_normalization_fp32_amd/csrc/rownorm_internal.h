@@ -54,6 +54,10 @@ struct BwdParams {
     int64_t C;          // 16-byte chunks per row (vectorized kernel)
     float inv_n;
     int parts;          // P = gridDim.x of the row kernel
+    // split rows (rows longer than one workgroup holds)
+    float* rec;         // [rows][S] records of two floats: the segment's sum g and sum g * xhat
+    int S;              // segments per row
+    int vec;            // rows, tensors and segments are whole 16-byte groups
 };
 
 // Backward column-sum kernel arguments.
@@ -100,6 +104,10 @@ constexpr int64_t kPersistentBlocks = 2048;  // at least this many workgroups: p
 constexpr int kWideSegChunks = 2048;   // split-row variant: 16-byte chunks per segment (one workgroup)
 constexpr int kWideElemSeg = 8192;     // split-row element variant: elements per segment (one workgroup)
 constexpr int kBwdMaxParts = 1024;     // backward: at most this many partial column rows (workspace bound)
+constexpr int kBwdSegLanes = 512;      // backward split rows: 512 lanes ...
+constexpr int kBwdSegPerLane = 16;     // ... of 16 elements: 8192-element segments
+constexpr int kBwdSeg = kBwdSegLanes * kBwdSegPerLane;
+constexpr int kBwdWideMaxGroups = 2048;  // backward split rows: at most this many segment workgroups
 constexpr int kBwdTargetChunks = 2;    // backward: about 2 chunks of x and of dy per lane (1 measured slower)
 
 // Enqueue the planned kernel for one I/O dtype (one translation unit per dtype and mode).

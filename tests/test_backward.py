@@ -44,18 +44,23 @@ def _scales(w, inp, mean, rstd, gamma):
 
 
 def _depth(op, rows, N, dtype):
-    st, info = rn.plan_backward(op, rows, N, TD[dtype])
+    st, info = rn.plan_backward(op, rows, N, TD[dtype], ptrs={"workspace": 1 << 46})
     assert st == 0, st
     # the launch uses P = min(grid, CUs x resident workgroups per CU) partial rows: at least
     # one workgroup per CU (rows per lane), at most the plan's grid (partial rows per lane
-    # of the column kernel)
+    # of the column kernel). Split rows: P = min(grid, resident workgroups / S) per segment,
+    # at least one.
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     rpb = info["rows_per_block"]
-    per_lane = -(-rows // (min(info["grid_blocks"], cus) * rpb))
+    if info["variant"] == "wide":
+        S = -(-N // 8192)
+        per_lane = -(-rows // max(1, min(info["grid_blocks"], cus // S)))
+    else:
+        per_lane = -(-rows // (min(info["grid_blocks"], cus) * rpb))
     return per_lane + rpb + info["grid_blocks"] / 16 + 16
 
 
-def run_case(w, with_gamma=True, in_place=False):
+def run_case(w, with_gamma=True, in_place=False, params=True):
     inp = workloads.make_inputs(w)
     gamma = inp.get("gamma" if w.op == "ln_bwd" else "weight") if with_gamma else None
     mean, rstd = _stats(w, inp)
@@ -66,15 +71,20 @@ def run_case(w, with_gamma=True, in_place=False):
         ref = oracle.layer_norm_backward(inp["dy"], inp["x"], gamma, mean=mean, rstd=rstd, eps=w.eps)
         mean_d = torch.from_numpy(mean).to(DEV)
         dyv = dev["dy"].clone()
-        dx, dg, db = rn.ln_backward(dyv, dev["x"], mean_d, rstd_d, g_dev, dx=dyv if in_place else None)
+        dx, dg, db = rn.ln_backward(dyv, dev["x"], mean_d, rstd_d, g_dev, dx=dyv if in_place else None,
+                                    want_dgamma=params, want_dbeta=params)
     else:
         ref = oracle.rms_norm_backward(inp["dy"], inp["x"], gamma, rstd=rstd, eps=w.eps)
         dyv = dev["dy"].clone()
-        dx, dg = rn.rms_norm_backward(dyv, dev["x"], rstd_d, g_dev, dx=dyv if in_place else None)
+        dx, dg = rn.rms_norm_backward(dyv, dev["x"], rstd_d, g_dev, dx=dyv if in_place else None,
+                                      want_dweight=params)
         db = None
     torch.cuda.synchronize()
     row, a_g, a_b = _scales(w, inp, mean, rstd, gamma)
     check_dx(dx, ref["dx"], row)
+    if not params:
+        assert dg is None and db is None
+        return
     depth = _depth("ln" if w.op == "ln_bwd" else "rms", w.rows, w.N, w.dtype)
     check_colsum(dg, ref["dgamma" if w.op == "ln_bwd" else "dweight"], a_g, depth, "dgamma")
     if db is not None:
@@ -95,6 +105,51 @@ def test_backward_shapes(op, dtype):
     base = workloads.LN_BWD if op == "ln_bwd" else workloads.RMS_BWD
     for rows, N in SHAPES:
         run_case(base.scaled(rows=rows, N=N, seed=1200 + N, dtype=dtype))
+
+
+# Rows longer than 16384 elements: split into 8192-element segments (16-byte groups when
+# N * s is a multiple of 16, else element by element), ragged last segments included.
+LONG = [("ln_bwd", "bf16", 24, 32768), ("ln_bwd", "fp32", 12, 50001), ("ln_bwd", "fp16", 40, 16392),
+        ("rms_bwd", "fp16", 16, 65536), ("rms_bwd", "bf16", 8, 20001), ("rms_bwd", "fp32", 10, 24580)]
+
+
+@pytest.mark.parametrize("op,dtype,rows,N", LONG, ids=lambda v: str(v))
+def test_backward_split_rows(op, dtype, rows, N):
+    base = workloads.LN_BWD if op == "ln_bwd" else workloads.RMS_BWD
+    w = base.scaled(rows=rows, N=N, seed=1300 + N, dtype=dtype)
+    assert rn.plan_backward("ln" if op == "ln_bwd" else "rms", rows, N, TD[dtype],
+                            ptrs={"workspace": 1 << 46})[1]["variant"] == "wide"
+    run_case(w)
+
+
+@pytest.mark.parametrize("op", ["ln_bwd", "rms_bwd"])
+def test_backward_split_rows_variants(op):
+    base = workloads.LN_BWD if op == "ln_bwd" else workloads.RMS_BWD
+    run_case(base.scaled(rows=6, N=40960, seed=1320, dtype="bf16"), with_gamma=False)
+    run_case(base.scaled(rows=6, N=40960, seed=1321, dtype="bf16"), in_place=True)
+    run_case(base.scaled(rows=5, N=33333, seed=1322, dtype="fp32"), in_place=True, params=False)  # dx only
+    run_case(base.scaled(rows=7, N=32768, seed=1323, dtype="fp16"), params=False)
+    # more rows than workgroups per segment: each workgroup loops over rows
+    run_case(base.scaled(rows=600, N=16392, seed=1324, dtype="bf16"))
+
+
+def test_backward_split_rows_deterministic_and_param_only():
+    w = workloads.LN_BWD.scaled(rows=64, N=24576, seed=1330, dtype="bf16")
+    inp = workloads.make_inputs(w)
+    mean, rstd = _stats(w, inp)
+    dev = {k: v.to(DEV) for k, v in inp.items()}
+    m, r = torch.from_numpy(mean).to(DEV), torch.from_numpy(rstd).to(DEV)
+    first = [o.clone() for o in rn.ln_backward(dev["dy"], dev["x"], m, r, dev["gamma"])]
+    for _ in range(3):
+        outs = rn.ln_backward(dev["dy"], dev["x"], m, r, dev["gamma"])
+        torch.cuda.synchronize()
+        for a, b in zip(first, outs):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    # parameter gradients alone give the same bits
+    _, dg, db = rn.ln_backward(dev["dy"], dev["x"], m, r, dev["gamma"], want_dx=False)
+    torch.cuda.synchronize()
+    assert torch.equal(dg.view(torch.uint8), first[1].view(torch.uint8))
+    assert torch.equal(db.view(torch.uint8), first[2].view(torch.uint8))
 
 
 @pytest.mark.parametrize("op", ["ln_bwd", "rms_bwd"])
@@ -173,6 +228,9 @@ def test_backward_argument_errors():
     with pytest.raises(rn.RowNormError) as e:
         rn.ln_backward(x, x, s, s, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
     assert e.value.status == 8
+    # rows split across workgroups keep their segment records in the workspace: needed (and
+    # checked) even when only dx is wanted
     with pytest.raises(rn.RowNormError) as e:
-        rn.ln_backward(torch.zeros(4, 32768, device=DEV), torch.zeros(4, 32768, device=DEV), s, s)
-    assert e.value.status == 5
+        rn.ln_backward(torch.zeros(4, 32768, device=DEV), torch.zeros(4, 32768, device=DEV), s, s,
+                       want_dgamma=False, want_dbeta=False, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    assert e.value.status == 8

@@ -331,10 +331,25 @@ def test_backward_plan_and_validation():
     assert info["chunks_per_lane"] == 2 and info["block_threads"] == 1024 and info["grid_blocks"] == 1024
     st, info = rn.plan_backward("rms", 2048, 4096, torch.float16, ptrs=ws)
     assert st == OK and info["waves_per_row"] == 4 and info["rows_per_block"] == 4 and info["lds_bytes"] == 4096 * 4
-    # rows that are not whole chunks: element kernel; beyond 16384 elements: unsupported
+    # rows that are not whole chunks: element kernel; beyond 16384 elements: split rows
     assert rn.plan_backward("ln", 8, 1001, bf16, ptrs=ws)[1]["variant"] == "element"
     assert rn.plan_backward("ln", 8, 16384, f32, ptrs=ws)[1]["variant"] == "element"
-    assert rn.plan_backward("ln", 8, 32768, bf16, ptrs=ws)[0] == UNSUP
+    st, info = rn.plan_backward("ln", 8, 32768, bf16, ptrs=ws)
+    assert st == OK and info["variant"] == "wide" and info["block_threads"] == 512 and info["exact"]
+    assert info["chunks_per_lane"] == 16 and info["grid_blocks"] == 8  # min(rows, 2048 / 4 segments)
+    st, info = rn.plan_backward("rms", 4096, 40001, f32, ptrs=ws)  # element-aligned rows: 5 segments
+    assert st == OK and info["variant"] == "wide" and not info["exact"] and info["grid_blocks"] == 2048 // 5
+    st, info = rn.plan_backward("ln", 8, 32768, bf16, ptrs={**ws, "x": (1 << 40) + 2})  # x not 16-byte aligned
+    assert st == OK and info["variant"] == "wide" and not info["exact"]
+    # split rows keep their segment records in the workspace: needed even for dx alone
+    assert rn.plan_backward("ln", 8, 32768, bf16)[0] == 8
+    assert rn.plan_backward("ln", 8, 32768, bf16, ptrs={"workspace": 1 << 46})[0] == OK
+    assert rn.plan_backward("ln", 8, 16384, bf16)[0] == OK
+    # split-row workspace: partial rows (sets x min(rows, 2048 / S) x N x 4), then from a
+    # 256-byte boundary the records (rows x S x 8)
+    assert rn.backward_workspace_bytes("ln", 100, 32768) == 2 * 100 * 32768 * 4 + 100 * 4 * 8
+    assert rn.backward_workspace_bytes("rms", 4096, 40001) == \
+        -(-(409 * 40001 * 4) // 256) * 256 + 4096 * 5 * 8
     # workspace: required for parameter gradients, at least rn_backward_workspace_bytes
     assert rn.backward_workspace_bytes("ln", 4096, 16384) == 2 * 1024 * 16384 * 4
     assert rn.backward_workspace_bytes("rms", 100, 64) == 100 * 64 * 4
@@ -364,7 +379,8 @@ def test_backward_entry_points_reject_before_launch():
     assert lib.ln_backward(0x1000, 0x2000, None, 0x3000, 0x4000, None, 0x5000, None, 4, 64, 0, None, 0,
                            None) == 8
     assert lib.rms_norm_backward(0x1000, 0x2000, None, 0x4000, 0x1000 + 64, None, 4, 64, 0, None, 0, None) == ALIAS
-    assert lib.rms_norm_backward(0x1000, 0x200000, None, 0x400000, None, None, 4, 65536, 0, None, 0, None) == UNSUP
+    # 65536-element rows are split across workgroups: the workspace for their records is missing
+    assert lib.rms_norm_backward(0x1000, 0x200000, None, 0x400000, None, None, 4, 65536, 0, None, 0, None) == 8
 
 
 def test_plan_split_rows():
