@@ -8,8 +8,8 @@ The same measurement is also taken for fused residual-add + RMSNorm at 8192 x 40
 "more", for fused residual-add + LayerNorm (8192 x 4096 bf16), softmax (8192 x 4096 fp32),
 the LayerNorm backward (4096 x 16384 bf16: dx, dgamma, dbeta), the RMSNorm backward
 (8192 x 4096 fp16: dx, dweight), ragged LayerNorm rows (16384 x 4095 bf16), split rows
-(LayerNorm 1024 x 65536 fp32) and a vocabulary-sized softmax (1024 x 50257 fp32, element
-kernel); under "scale_up_sweep", fused add + RMSNorm at
+(LayerNorm 1024 x 65536 fp32), a vocabulary-sized softmax (1024 x 50257 fp32, element
+kernel) and the split-row LayerNorm backward (1024 x 65536 bf16); under "scale_up_sweep", fused add + RMSNorm at
 N = 4096 over 2048 / 8192 / 32768 rows (fp16 and bf16), LayerNorm bf16 2048 x 4096, and the
 headline workload with a hot cache; under "configs", every listed configuration (cold and
 hot, events and graph replay, next to the oracle's host throughput). Small launches (tens of microseconds) are shorter than
@@ -134,6 +134,10 @@ def kernel_name(w, plan):
     """The kernel instance a workload's launch runs, as rocprofv3 lists it (template arguments:
     dtype, op, waves per row, chunks per lane, row groups per workgroup, exact, affine, flags)."""
     if w.op in ("ln_bwd", "rms_bwd"):
+        if plan["variant"] == "wide":
+            return (f"rn::rownorm_bwd_wide_stats_kernel + rn::rownorm_bwd_wide_dx_kernel ({w.dtype}, {w.op}, "
+                    f"8192-element segments, 512 lanes each, at most {plan['grid_blocks']} workgroups per segment) "
+                    f"+ rn::rownorm_bwd_cols_kernel")
         k = "rownorm_bwd_vec_kernel" if plan["variant"] == "workgroup" else "rownorm_bwd_elem_kernel"
         return (f"rn::{k} ({w.dtype}, {w.op}, W={plan['waves_per_row']} waves per row, V={plan['chunks_per_lane']}, "
                 f"{plan['rows_per_block']} row group(s) per workgroup) + rn::rownorm_bwd_cols_kernel")
@@ -286,7 +290,9 @@ def measure(w, steps, warmup, cache, dev, graph=True):
     s0 = sets[0]
     td = workloads.TORCH_DTYPES[w.dtype]
     if w.op in ("ln_bwd", "rms_bwd"):
-        st, info = rn.plan_backward("ln" if w.op == "ln_bwd" else "rms", w.rows, w.N, td)
+        # the plan of the timed call (host only): it passes a workspace, which split rows need
+        st, info = rn.plan_backward("ln" if w.op == "ln_bwd" else "rms", w.rows, w.N, td,
+                                    ptrs={"workspace": s0["ws"].data_ptr()})
         info["persistent"] = True
     else:
         ptrs = {k: s0[k].data_ptr() for k in ("x", "residual", "gamma", "beta", "weight", "y", "residual_out", "mean",
@@ -427,6 +433,9 @@ def _more():
         ("softmax_vocab", workloads.SOFTMAX_VOCAB,
          "row-wise softmax, fp32 I/O, 1024 x 50257 (vocabulary-sized rows, not whole chunks: element kernel, "
          "one 16-wave workgroup per row)"),
+        ("ln_backward_split_rows", workloads.LN_BWD.scaled(rows=1024, N=65536, name="ln_bwd_bf16_1024x65536"),
+         "LayerNorm backward, bf16 I/O, 1024 x 65536 (rows beyond one workgroup: segment sums, then dx with "
+         "per-segment column partials, then column sums; x and dy read twice)"),
     ]
 
 

@@ -487,7 +487,11 @@ __global__ __launch_bounds__(kBwdSegLanes) void rownorm_bwd_wide_dx_kernel(BwdPa
         adg[k] = 0.f;
         if constexpr (LN) adb[k] = 0.f;
     }
-    for (int64_t row = q; row < p.rows; row += Q) {
+    for (int64_t rr = q; rr < p.rows; rr += Q) {
+        // last rows first: the statistics launch read them last, so they may still be in
+        // the memory-side cache (LayerNorm fp32 1024 x 65537: 34.0% -> 35.1% of HBM peak,
+        // RMSNorm bf16 512 x 131072: 36.0% -> 37.1%)
+        const int64_t row = p.rows - 1 - rr;
         const int64_t off = (row * p.N + e0) * SG::SB;
         float xf[V], df[V];
         SG::load(static_cast<const char*>(p.x) + off, nb, vec, t, xf);

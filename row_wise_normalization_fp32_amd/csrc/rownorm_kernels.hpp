@@ -1525,7 +1525,11 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_elem_norm_kernel(Para
     constexpr bool HB = OT::LN && (AFF & AFF_B) != 0;
     const int t = threadIdx.x;
     const int64_t total = p.rows * wa.S;
-    for (int64_t b = blockIdx.x; b < total; b += gridDim.x) {
+    for (int64_t it = blockIdx.x; it < total; it += gridDim.x) {
+        // last rows first: the statistics launch read them last, so they may still be in
+        // the memory-side cache (fp32 LayerNorm 1024 x 65537: 37.6% -> 42.1% of HBM peak;
+        // the whole-chunk split rows measured no better this way)
+        const int64_t b = total - 1 - it;
         const int64_t row = b / wa.S;
         const int seg = static_cast<int>(b - row * wa.S);
         const int64_t e0 = static_cast<int64_t>(seg) * kWideElemSeg;
