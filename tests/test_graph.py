@@ -27,6 +27,7 @@ def test_graph_replays_match_eager():
     wide = {k: v.to(DEV) for k, v in workloads.make_inputs(workloads.C5.scaled(rows=4, N=131072)).items()}
     wel = {k: v.to(DEV) for k, v in workloads.make_inputs(workloads.C2.scaled(rows=4, N=50257)).items()}
     bw = {k: v.to(DEV) for k, v in workloads.make_inputs(workloads.LN_BWD.scaled(rows=256, N=4096)).items()}
+    bl = {k: v.to(DEV) for k, v in workloads.make_inputs(workloads.RMS_BWD.scaled(rows=8, N=40000)).items()}
 
     def run():
         y1, m1, r1 = rn.ln_forward(ln["x"], ln["gamma"], ln["beta"], 1e-5, return_stats=True)
@@ -37,7 +38,9 @@ def test_graph_replays_match_eager():
         y7 = rn.ln_forward(wel["x"], wel["gamma"], wel["beta"], 1e-5)  # split rows at element granularity
         _, m6, r6 = rn.ln_forward(bw["x"], None, None, 1e-5, return_stats=True)
         dx, dg, db = rn.ln_backward(bw["dy"], bw["x"], m6, r6, bw["gamma"])  # row + column kernels
-        return [y1, m1, r1, y2, ro2, y3, ro3, y4, y5, y7, dx, dg, db]
+        _, r8 = rn.rms_norm(bl["x"], None, 1e-6, return_rstd=True)
+        dx8, dw8 = rn.rms_norm_backward(bl["dy"], bl["x"], r8, bl["weight"])  # split rows: three launches
+        return [y1, m1, r1, y2, ro2, y3, ro3, y4, y5, y7, dx, dg, db, dx8, dw8]
 
     eager = [_bits(t) for t in run()]
     torch.cuda.synchronize()
