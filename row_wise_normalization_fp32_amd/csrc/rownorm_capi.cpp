@@ -188,10 +188,16 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     // vs 67%) stay split.
     // fp32 softmax, which holds nothing else in registers, takes 16 chunks per lane: rows of
     // 65536 elements (256 KiB); 16-bit softmax rows of that length fit 8 chunks per lane.
+    // Without a workspace (no split rows possible) LayerNorm and fused add + RMSNorm rows of
+    // up to 8192 chunks also take one 16-wave workgroup instead of the general kernel (which
+    // reads the row up to three times, element by element).
+    const bool big_instead_of_general =
+        !ws_given && (a.op == RN_OP_LAYER_NORM || a.op == RN_OP_FUSED_ADD_RMS_NORM);
     const int64_t big_cap = a.op == RN_OP_SOFTMAX
                                 ? int64_t(64) * rn::kMaxGroupWaves * (s == 4 ? rn::kMaxSoftmaxChunks : rn::kMaxBigChunks)
-                            : a.op == RN_OP_RMS_NORM ? int64_t(64) * rn::kMaxGroupWaves * rn::kMaxBigChunks
-                                                     : group_cap;
+                            : (a.op == RN_OP_RMS_NORM || big_instead_of_general)
+                                ? int64_t(64) * rn::kMaxGroupWaves * rn::kMaxBigChunks
+                                : group_cap;
 
     // Automatic row-group width: enough waves that each lane holds about kTargetChunks
     // chunks (measured on MI355X: 4 chunks per lane balances bytes in flight against VGPRs).

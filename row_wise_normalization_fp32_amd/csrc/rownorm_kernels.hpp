@@ -1824,8 +1824,9 @@ inline hipError_t launch_v(const Plan& plan, const Params& p, hipStream_t s) {
         }
     }
     // softmax and RMSNorm rows of up to 128 KiB, one workgroup each (measured against the
-    // split-row path; the LayerNorm ops are faster split)
-    if constexpr (W == 16 && !PERS && (OP == OP_SOFTMAX || OP == OP_RMS)) {
+    // split-row path); LayerNorm and fused add + RMSNorm rows too when no workspace allows
+    // split rows (the fused add + LayerNorm instance would spill)
+    if constexpr (W == 16 && !PERS && (OP == OP_SOFTMAX || OP == OP_RMS || OP == OP_LN || OP == OP_FUSED)) {
         if (plan.chunks_per_lane == 8) return RN_GO(8);
     }
     if constexpr (W == 16 && !PERS && OP == OP_SOFTMAX && DT == DT_F32) {  // fp32 softmax rows up to 256 KiB

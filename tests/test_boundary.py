@@ -70,7 +70,8 @@ def test_status_strings_and_version():
     ("ln", torch.float32, 16, 16384, "workgroup", 16, 4, False),
     ("rms", torch.bfloat16, 16, 32768, "workgroup", 16, 4, False),
     ("rms", torch.float32, 16, 16388, "workgroup", 16, 8, False),      # 4097 chunks: 16 waves x 8 chunks
-    ("ln", torch.float32, 16, 16388, "general", 0, 0, False),          # LayerNorm rows that long are split
+    ("ln", torch.float32, 16, 16388, "workgroup", 16, 8, False),      # no workspace for split rows: one workgroup
+    ("fused_add_rms", torch.float16, 16, 65536, "workgroup", 16, 8, False),  # likewise, 8192 chunks
     ("softmax", torch.float32, 16, 32768, "workgroup", 16, 8, False),  # 128 KiB rows, one workgroup each
     ("fused_add_ln", torch.bfloat16, 8, 32776, "general", 0, 0, False),  # no room for 8 chunks: split (no workspace)
     ("ln", torch.float32, 16, 32772, "general", 0, 0, False),          # beyond a workgroup's registers
@@ -240,7 +241,12 @@ def test_plan_forced_variants():
     assert rn.plan("softmax", 4, 65536, torch.float32, variant="workgroup")[1]["chunks_per_lane"] == 16
     assert rn.plan("softmax", 4, 65540, torch.float32, variant="workgroup")[0] == UNSUP
     assert rn.plan("softmax", 4, 65544, torch.bfloat16, variant="workgroup")[0] == UNSUP
-    assert rn.plan("ln", 4, 32768, torch.float32, variant="workgroup")[0] == UNSUP
+    # LayerNorm rows of 8192 chunks: one workgroup without a workspace, split rows with one
+    assert rn.plan("ln", 4, 32768, torch.float32, variant="workgroup")[1]["chunks_per_lane"] == 8
+    need = rn.forward_workspace_bytes("ln", 4, 32768, torch.float32)
+    assert rn.plan("ln", 4, 32768, torch.float32, workspace_bytes=need)[1]["variant"] == "wide"
+    assert rn.plan("ln", 4, 32768, torch.float32, variant="workgroup", workspace_bytes=need)[0] == UNSUP
+    assert rn.plan("ln", 4, 32772, torch.float32, variant="workgroup")[0] == UNSUP  # 8193 chunks
     assert rn.plan("ln", 4, 64, torch.float32, variant="general")[1]["variant"] == "general"
     assert rn.plan("ln", 4, 4096, torch.float32, variant="element")[1]["variant"] == "element"
     assert rn.plan("ln", 4, 16385, torch.float32, variant="element")[0] == UNSUP

@@ -176,6 +176,18 @@ def test_workgroup_path_128k_rows(op, dtype):
         check_case(BASES[op].scaled(rows=rows, N=N, seed=680 + N, dtype=dtype))
 
 
+@pytest.mark.parametrize("op", ["ln", "fused_add_rms"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
+def test_workgroup_path_128k_rows_without_workspace(op, dtype):
+    # without a workspace (C callers that pass none; here a forced variant, for which the
+    # binding allocates none) LayerNorm and fused add + RMSNorm rows of 64-128 KiB take one
+    # 16-wave workgroup with 8 chunks per lane instead of the general kernel
+    for rows, N in BIG_SHAPES[dtype]:
+        st, info = rn.plan(op, rows, N, TD[dtype], variant="workgroup")
+        assert st == 0 and info["chunks_per_lane"] == 8 and info["waves_per_row"] == 16, info
+        check_case(BASES[op].scaled(rows=rows, N=N, seed=690 + N, dtype=dtype), variant="workgroup")
+
+
 @pytest.mark.parametrize("op", ["ln", "rms", "fused_add_rms", "fused_add_ln", "softmax"])
 @pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
 def test_split_rows(op, dtype):
