@@ -51,13 +51,14 @@
  *     [N] pointer is 16-byte aligned, the vectorized kernels run: a row is held in registers
  *     by one 64-lane wavefront (rows of up to 4 KiB, or 16 KiB when forced) or by a group of
  *     up to 16 wavefronts (rows of up to 64 KiB: 16384 fp32 or 32768 fp16 / bf16 elements;
- *     softmax and RMSNorm rows of up to 128 KiB).
+ *     softmax and RMSNorm rows of up to 128 KiB, and LayerNorm and fused add + RMSNorm rows
+ *     of up to 128 KiB when no workspace is given).
  *     Otherwise rows of up to 16384 elements are held in registers one element per slot
  *     (the element kernel, still one read of x; 16-bit rows whose tensors share their
  *     position within 4-byte words move as element pairs). Longer rows take the split-row
  *     kernels (whole-chunk rows: 16-byte chunks; other rows: elements) when rn_forward_ex is
- *     given a workspace; without one they take a general kernel that reads the row up to
- *     three times.
+ *     given a workspace; without one (and beyond the 128 KiB rows above) they take a general
+ *     kernel that reads the row up to three times.
  *   - Launches use the current HIP device (the device of the buffers and of `stream`). The
  *     first call of a kernel configuration on a device queries its occupancy once.
  */
@@ -99,7 +100,8 @@ typedef enum rn_variant {
     RN_VARIANT_AUTO = 0,      /* choose from N, dtype, alignment and rows (what the plain entry points do) */
     RN_VARIANT_WAVE = 1,      /* one 64-lane wavefront per row, row held in VGPRs (rows up to 16 KiB) */
     RN_VARIANT_WORKGROUP = 2, /* 2-16 wavefronts per row, partial moments combined in LDS (rows up to 64 KiB;
-                                 softmax and RMSNorm up to 128 KiB) */
+                                 softmax and RMSNorm up to 128 KiB, LayerNorm and fused add + RMSNorm
+                                 too when no workspace is given) */
     RN_VARIANT_GENERAL = 3,   /* any N, any element-aligned pointers; re-reads the row */
     RN_VARIANT_ELEMENT = 4,   /* rows up to 16384 elements held in VGPRs one element per slot;
                                  any element-aligned pointers and strides */
@@ -199,7 +201,9 @@ int softmax_forward(const void* x, void* y, float* row_max, float* row_sum, int6
  *
  * The split-row path (walkthrough section 1.1: a row that outgrows one block) reads x (for
  * the fused ops: residual_out) a second time; the second read is served from the memory-side
- * cache when the tensor fits in it. Without a workspace such rows take the general kernel.
+ * cache when the tensor fits in it. Without a workspace, LayerNorm and fused add + RMSNorm
+ * rows of whole chunks up to 128 KiB take one 16-wave workgroup; other such rows take the
+ * general kernel.
  */
 int rn_forward_ex(int op, const void* x, const void* residual, const void* gamma, const void* beta, void* y,
                   void* residual_out, float* mean, float* rstd, int64_t rows, int64_t N, float eps, int dtype,
