@@ -253,20 +253,25 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_bwd_elem_kernel(BwdParam
             const unsigned j = static_cast<unsigned>(i * LANES) + t;
             xf[i] = IO::bload(xr, j);
             df[i] = IO::bload(dr, j);
-            if constexpr (HG && !GREG) gv[i] = IO::bload(gr, j);
         }
         const float mean = LN ? p.mean[row] : 0.f;
         const float rstd = p.rstd[row];
         __builtin_amdgcn_sched_barrier(0);
+        // gamma of slot i: held (GREG) or read where it is used, in this loop and again in
+        // the dx loop, so that only dy stays in registers across the row's reduction
+        auto gam = [&](int i) {
+            if constexpr (GREG) return gv[i];
+            return IO::bload(gr, static_cast<unsigned>(i * LANES) + t);
+        };
         float sg = 0.f, sgx = 0.f;
 #pragma unroll
         for (int i = 0; i < V; ++i) {
             xf[i] = LN ? (xf[i] - mean) * rstd : xf[i] * rstd;  // xhat (0 where df is 0)
             adg[i] = fmaf(df[i], xf[i], adg[i]);
             if constexpr (LN) adb[i] += df[i];
-            if constexpr (HG) df[i] *= gv[i];  // from here on df holds g = dy * gamma
-            sg += df[i];
-            sgx = fmaf(df[i], xf[i], sgx);
+            const float g = HG ? df[i] * gam(i) : df[i];
+            sg += g;
+            sgx = fmaf(g, xf[i], sgx);
         }
         float Sg = wave_sum(sg), Sgx = wave_sum(sgx);
         group_sum2<W>(part, buf, lane, wr, Sg, Sgx);
@@ -275,8 +280,10 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_bwd_elem_kernel(BwdParam
         if (p.dx) {
             const Rsrc o = make_rsrc(static_cast<char*>(p.dx) + row * p.N * S, row_bytes);
 #pragma unroll
-            for (int i = 0; i < V; ++i)
-                IO::bstore(o, static_cast<unsigned>(i * LANES) + t, rstd * ((df[i] - c1) - xf[i] * c2));
+            for (int i = 0; i < V; ++i) {
+                const float g = HG ? df[i] * gam(i) : df[i];
+                IO::bstore(o, static_cast<unsigned>(i * LANES) + t, rstd * ((g - c1) - xf[i] * c2));
+            }
         }
     }
     if (p.ws == nullptr) return;
