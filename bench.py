@@ -30,7 +30,9 @@ training loop runs a fixed sequence of launches: each step still launches its ke
 own rotating buffers; only the per-call Python and dispatch overhead between steps (about
 2 us per launch here) is gone. Two HIP events recorded on the launch stream (torch's current
 stream, which the binding passes to the C ABI) around the timed replay give the per-launch
-kernel duration used for the roofline; rocprofv3's kernel durations agree with it.
+kernel duration used for the roofline; rocprofv3's kernel durations agree with it. Five
+further replays, each between two events, give the spread ("replays": median and quartiles
+of the per-step device time).
 
 value = algorithmic bytes per step / ms_per_step (GB/s, 1 GB = 1e9 B). Algorithmic bytes:
 LayerNorm 2*rows*N*s + 2*N*s + 8*rows; fused 4*rows*N*s + N*s + 4*rows (with rstd); fused
@@ -180,6 +182,19 @@ def launch(rn, w, s):
 SET_TENSORS = {"ln": 2, "rms": 2, "softmax": 2, "fused_add_rms": 4, "fused_add_ln": 4, "ln_bwd": 3, "rms_bwd": 3}
 
 
+REPEATS = 5
+
+
+def spread(r):
+    """Median and interquartile range of the per-step device time over the repeated replays."""
+    reps = sorted(r.get("repeats_ms") or [])
+    if not reps:
+        return None
+    q = lambda f: reps[min(len(reps) - 1, int(round(f * (len(reps) - 1))))]  # noqa: E731
+    return {"n": len(reps), "median_ms": round(q(0.5), 5), "q1_ms": round(q(0.25), 5), "q3_ms": round(q(0.75), 5),
+            "what": f"{len(reps)} further replays of the same HIP graph of K steps, HIP events around each"}
+
+
 def graph_time(rn, w, sets, steps):
     """`steps` launches (rotating over the buffer sets) captured into one HIP graph, replayed
     once to warm up, then one timed replay bracketed by torch.cuda.synchronize() (wall clock)
@@ -203,6 +218,16 @@ def graph_time(rn, w, sets, steps):
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         out = {"wall_ms": wall * 1e3 / steps, "event_ms": a.elapsed_time(b) / steps}
+        # spread: REPEATS further replays, each between two events (median and quartiles
+        # of the per-step device time)
+        reps = []
+        for _ in range(REPEATS):
+            a.record()
+            g.replay()
+            b.record()
+            torch.cuda.synchronize()
+            reps.append(a.elapsed_time(b) / steps)
+        out["repeats_ms"] = reps
         del g
         return out
     except Exception as e:  # capture not possible here: report without it
@@ -309,6 +334,7 @@ def measure(w, steps, warmup, cache, dev, graph=True):
     return {
         "bytes": nbytes, "ms_per_step": ms_per_step, "timing": "graph" if gt else "eager",
         "eager_ms_per_step": eager_ms, "kernel_ms": kernel_ms, "graph_ms": graph_ms,
+        "repeats_ms": gt["repeats_ms"] if gt else None,
         "nsets": nsets, "plan": info,
     }
 
@@ -508,6 +534,7 @@ def main():
         "rows_per_s": round(w.rows / (r["ms_per_step"] * 1e-3), 1),
         "timing": TIMING[r["timing"]],
         "eager": eager_fields(r),
+        "replays": spread(r),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
@@ -539,7 +566,7 @@ def main():
             "achieved_kernel_GBs": round(fa, 2),
             "frac_kernel": round(fa / PEAK_HBM_GBS, 4), "bytes_per_launch": rf["bytes"],
             "kernel": kernel_name(f, rf["plan"]), "traffic": counter_traffic("fused_fp16_8192x4096"),
-            "timing": rf["timing"], "eager": eager_fields(rf),
+            "timing": rf["timing"], "eager": eager_fields(rf), "replays": spread(rf),
         }
     if not args.no_more:
         more = {}
@@ -560,7 +587,7 @@ def main():
                 "kernel": kernel_name(x, rx["plan"]),
                 # HBM bytes per call from the counter record (backward: row + column kernels)
                 "traffic": counter_traffic(x.name),
-                "timing": rx["timing"], "eager": eager_fields(rx),
+                "timing": rx["timing"], "eager": eager_fields(rx), "replays": spread(rx),
             }
         out["more"] = more
     if not args.no_configs:

@@ -69,3 +69,9 @@ def test_eager_fields():
 @pytest.mark.parametrize("key", ["graph", "eager"])
 def test_timing_descriptions(key):
     assert "torch.cuda.synchronize()" in bench.TIMING[key]
+
+
+def test_replay_spread():
+    s = bench.spread({"repeats_ms": [0.047, 0.046, 0.0465, 0.0462, 0.048]})
+    assert s["n"] == 5 and s["median_ms"] == 0.0465 and s["q1_ms"] == 0.0462 and s["q3_ms"] == 0.047
+    assert bench.spread({"repeats_ms": None}) is None
