@@ -16,9 +16,9 @@ hot, events and graph replay, next to the oracle's host throughput). Small launc
 the Python binding's per-call host time, so the sweep also replays its launches from a HIP
 graph ("graph_ms": device time per launch without host gaps).
 
-Cold cache: inputs and outputs rotate through enough buffer sets that each launch touches
-memory the previous launches have pushed out of L2 (8 x 4 MiB) and the 256 MiB
-memory-side cache. Inputs are resident in HBM before the timed region starts.
+Cold cache: inputs and outputs rotate through enough buffer sets (at least four, at least
+1 GiB per cycle) that each launch touches memory the previous launches have pushed out of
+L2 (8 x 4 MiB) and the 256 MiB memory-side cache. Inputs are resident in HBM before the timed region starts.
 
 Timed region: about 50 ms of plain device copies (the GPU's clocks rise over the first ~10 ms
 of work after the idle host-side set-up), W warmup steps untimed, then exactly K steps
@@ -60,7 +60,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "achieved HBM GB/s (% of MI355X peak) + rows/s, LayerNorm & fused add+RMSNorm"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published peak
-COLD_FOOTPRINT = 768 << 20  # bytes each buffer set cycle must exceed (L2 + 256 MiB MALL, with margin)
+COLD_FOOTPRINT = 1 << 30  # bytes each buffer set cycle must exceed (L2 + 256 MiB MALL, with margin)
+MIN_COLD_SETS = 4  # buffer sets a cold-cache line rotates through at least
 KERNEL_SRCS = [os.path.join(ROOT, "row_wise_normalization_fp32_amd", "csrc", f)
                for f in ("rownorm_kernels.hpp", "rownorm_backward.hpp", "rownorm_capi.cpp")]  # kernels + launch plan
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_counters.txt")
@@ -286,7 +287,7 @@ def measure(w, steps, warmup, cache, dev, graph=True):
 
     nbytes = workloads.algorithmic_bytes(w.op, w.rows, w.N, w.elem_bytes, with_stats=True)
     set_bytes = SET_TENSORS[w.op] * w.rows * w.N * w.elem_bytes
-    nsets = 1 if cache == "hot" else max(2, min(64, math.ceil(COLD_FOOTPRINT / set_bytes)))
+    nsets = 1 if cache == "hot" else max(MIN_COLD_SETS, min(64, math.ceil(COLD_FOOTPRINT / set_bytes)))
     log(f"[bench] {w.name}: {nsets} buffer set(s), {nbytes} algorithmic bytes per launch")
     sets = make_sets(w, nsets, dev)
     torch.cuda.synchronize()
@@ -402,7 +403,7 @@ def copy_reference(nbytes_each, steps, dev):
     read+write ceiling on this GPU, for context."""
     import torch
 
-    nsets = max(2, math.ceil(COLD_FOOTPRINT / (2 * nbytes_each)))
+    nsets = max(MIN_COLD_SETS, math.ceil(COLD_FOOTPRINT / (2 * nbytes_each)))
     src = [torch.ones(nbytes_each // 2, dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
     dst = [torch.empty_like(a) for a in src]
     for i in range(5):
