@@ -36,6 +36,10 @@ ULP_TOL = 2.0
 STAT_REL_TOL = 1e-5
 MANT_BITS = {"fp16": 10, "bf16": 7}
 MAG_FLOOR = {"fp16": 2.0 ** -10, "bf16": 2.0 ** -14}
+# For one output ulp of a backward result: below its smallest normal (2^-14) fp16's grid
+# keeps the subnormal spacing 2^-24, so the magnitude is floored there; bf16's subnormals
+# (below 2^-126) are out of reach, 2^-24 only keeps the logarithm finite.
+GRID_FLOOR = {"fp16": 2.0 ** -14, "bf16": 2.0 ** -24}
 _NAME = {torch.float32: "fp32", torch.float16: "fp16", torch.bfloat16: "bf16"}
 
 
@@ -134,7 +138,7 @@ def check_dx(dx_gpu: torch.Tensor, dx_ref: np.ndarray, row_scale: np.ndarray, wh
     assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
     tol = 64 * U32 * row_scale[:, None]
     if dt != "fp32":
-        mag = np.maximum(np.abs(dx_ref), 2.0 ** -24)
+        mag = np.maximum(np.abs(dx_ref), GRID_FLOOR[dt])
         tol = tol + np.exp2(np.floor(np.log2(mag)) - MANT_BITS[dt])
     err = np.abs(got - dx_ref)
     bad = err > tol
@@ -150,7 +154,7 @@ def check_colsum(got_t: torch.Tensor, ref: np.ndarray, abs_sum: np.ndarray, dept
     got = got_t.detach().cpu().double().numpy().reshape(-1)
     tol = (depth + 3) * U32 * abs_sum
     if dt != "fp32":
-        mag = np.maximum(np.abs(ref), 2.0 ** -24)
+        mag = np.maximum(np.abs(ref), GRID_FLOOR[dt])
         tol = tol + np.exp2(np.floor(np.log2(mag)) - MANT_BITS[dt])
     tol = np.maximum(tol, 1e-30)
     err = np.abs(got - ref)

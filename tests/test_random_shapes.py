@@ -51,3 +51,30 @@ def test_random_shape(case):
     ref = run_oracle(w, inp)
     out = run_placed(w, inp, offset=off, ld=ld)
     check_outputs(w, ref, *out)
+
+
+def _bwd_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        op, dtype = ["ln_bwd", "rms_bwd"][rng.integers(2)], DTYPES[rng.integers(len(DTYPES))]
+        band = rng.integers(4)
+        lo, hi = [(1, 64), (65, 4096), (4097, 16384), (16385, 70000)][band]
+        N = int(rng.integers(lo, hi + 1))
+        if rng.random() < 0.4:
+            e = 4 if dtype == "fp32" else 8
+            N = max(e, N // e * e)
+        rows = int(rng.choice([1, 2, 3, 7, 40, 300] if band < 2 else [1, 2, 5, 24]))
+        out.append((i, op, dtype, rows, N, bool(rng.random() < 0.8), bool(rng.random() < 0.3),
+                    bool(rng.random() < 0.85)))
+    return out
+
+
+@pytest.mark.parametrize("case", _bwd_cases(160, 2025), ids=lambda c: f"{c[0]}-{c[1]}-{c[2]}-{c[3]}x{c[4]}")
+def test_random_backward(case):
+    from test_backward import run_case
+
+    i, op, dtype, rows, N, with_gamma, in_place, params = case
+    base = workloads.LN_BWD if op == "ln_bwd" else workloads.RMS_BWD
+    run_case(base.scaled(rows=rows, N=N, seed=6000 + i, dtype=dtype), with_gamma=with_gamma, in_place=in_place,
+             params=params)
