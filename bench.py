@@ -23,16 +23,16 @@ L2 (8 x 4 MiB) and the 256 MiB memory-side cache. Inputs are resident in HBM bef
 Timed region: about 50 ms of plain device copies (the GPU's clocks rise over the first ~10 ms
 of work after the idle host-side set-up), W warmup steps untimed, then exactly K steps
 launched eagerly from Python, bracketed by torch.cuda.synchronize() ("eager": wall time over
-K), then the same K steps captured into one HIP graph, replayed once untimed and once
-between torch.cuda.synchronize() calls: ms_per_step is that replay's wall time over K (the
-eager time when no graph can be captured; "timing" says which). A graph is how a serving or
+K), then the same K steps captured into one HIP graph, replayed once untimed and then five
+times, each replay between torch.cuda.synchronize() calls: ms_per_step is the median of the
+five replays' wall time over K (the eager time when no graph can be captured; "timing" says
+which). A graph is how a serving or
 training loop runs a fixed sequence of launches: each step still launches its kernel on its
 own rotating buffers; only the per-call Python and dispatch overhead between steps (about
 2 us per launch here) is gone. Two HIP events recorded on the launch stream (torch's current
-stream, which the binding passes to the C ABI) around the timed replay give the per-launch
-kernel duration used for the roofline; rocprofv3's kernel durations agree with it. Five
-further replays, each between two events, give the spread ("replays": median and quartiles
-of the per-step device time).
+stream, which the binding passes to the C ABI) around each timed replay give the per-launch
+kernel duration used for the roofline (their median); rocprofv3's kernel durations agree
+with it. "replays" gives their spread (median and quartiles of the per-step device time).
 
 value = algorithmic bytes per step / ms_per_step (GB/s, 1 GB = 1e9 B). Algorithmic bytes:
 LayerNorm 2*rows*N*s + 2*N*s + 8*rows; fused 4*rows*N*s + N*s + 4*rows (with rstd); fused
@@ -187,20 +187,21 @@ REPEATS = 5
 
 
 def spread(r):
-    """Median and interquartile range of the per-step device time over the repeated replays."""
+    """Median and quartiles of the per-step device time over the timed replays."""
     reps = sorted(r.get("repeats_ms") or [])
     if not reps:
         return None
     q = lambda f: reps[min(len(reps) - 1, int(round(f * (len(reps) - 1))))]  # noqa: E731
     return {"n": len(reps), "median_ms": round(q(0.5), 5), "q1_ms": round(q(0.25), 5), "q3_ms": round(q(0.75), 5),
-            "what": f"{len(reps)} further replays of the same HIP graph of K steps, HIP events around each"}
+            "what": f"{len(reps)} timed replays of one HIP graph of the K steps, HIP events around each"}
 
 
 def graph_time(rn, w, sets, steps):
     """`steps` launches (rotating over the buffer sets) captured into one HIP graph, replayed
-    once to warm up, then one timed replay bracketed by torch.cuda.synchronize() (wall clock)
-    and by two HIP events on the launch stream. Returns {"wall_ms", "event_ms"} per step, or
-    None if the capture fails."""
+    once to warm up, then REPEATS timed replays, each bracketed by torch.cuda.synchronize()
+    (wall clock) and by two HIP events on the launch stream. Returns the medians per step
+    ({"wall_ms", "event_ms"}) and every replay's per-step event time ("repeats_ms"), or None
+    if the capture fails."""
     import torch
 
     try:
@@ -211,33 +212,26 @@ def graph_time(rn, w, sets, steps):
         g.replay()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        a.record()
-        g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        out = {"wall_ms": wall * 1e3 / steps, "event_ms": a.elapsed_time(b) / steps}
-        # spread: REPEATS further replays, each between two events (median and quartiles
-        # of the per-step device time)
-        reps = []
+        walls, events = [], []
         for _ in range(REPEATS):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
             a.record()
             g.replay()
             b.record()
             torch.cuda.synchronize()
-            reps.append(a.elapsed_time(b) / steps)
-        out["repeats_ms"] = reps
+            walls.append((time.perf_counter() - t0) * 1e3 / steps)
+            events.append(a.elapsed_time(b) / steps)
         del g
-        return out
+        med = lambda v: sorted(v)[len(v) // 2]  # noqa: E731
+        return {"wall_ms": med(walls), "event_ms": med(events), "repeats_ms": events, "walls_ms": walls}
     except Exception as e:  # capture not possible here: report without it
         log(f"[bench] graph timing unavailable: {e}")
         return None
 
 
 TIMING = {
-    "graph": "K steps captured in one HIP graph, one replay timed by wall clock between "
+    "graph": "K steps captured in one HIP graph; median over 5 replays, each timed by wall clock between "
              "torch.cuda.synchronize() calls (after an untimed eager pass and an untimed replay)",
     "eager": "K eager launches timed by wall clock between torch.cuda.synchronize() calls",
 }
@@ -251,13 +245,14 @@ def eager_fields(r):
 
 
 def kernel_time(r):
-    """Per-launch device time for the roofline: from the replay of a HIP graph holding the
-    K timed launches (HIP events around the replay, on the launch stream), which leaves out
-    the dispatch gaps of eager back-to-back launches (≈2 µs each here, which rocprofv3's
-    kernel durations also leave out); the eager stream events when no graph could be
-    captured."""
+    """Per-launch device time for the roofline: from the replays of a HIP graph holding the
+    K timed launches (median of the HIP events around each replay, on the launch stream),
+    which leave out the dispatch gaps of eager back-to-back launches (≈2 µs each here, which
+    rocprofv3's kernel durations also leave out); the eager stream events when no graph
+    could be captured."""
     if r.get("graph_ms"):
-        return r["graph_ms"], "HIP events around one replay of a HIP graph of the K timed launches"
+        return r["graph_ms"], (f"median over {REPEATS} replays of a HIP graph of the K timed launches, "
+                               "HIP events around each")
     return r["kernel_ms"], "HIP events around the K eager launches (no graph capture)"
 
 
