@@ -273,30 +273,41 @@ static void rms_row(const job_t* jb, const double* xr, const double* w, int64_t 
  * y_j = exp(x_j - m) / d. Independently, the single-pass online form of the same section
  * ("denominator correction"): a running maximum m_k and denominator d_k, where a new
  * element x_k gives m_k = max(m_{k-1}, x_k) and d_k = d_{k-1} * exp(m_{k-1} - m_k) +
- * exp(x_k - m_k). Both must give the same maximum and, up to fp64 rounding, the same
- * denominator, or the oracle refuses to answer. Rows are expected to hold finite values. */
+ * exp(x_k - m_k), starting from m = -inf, d = 0. Both must give the same maximum and, up
+ * to fp64 rounding, the same denominator, or the oracle refuses to answer.
+ * Entries of -inf (masked logits) have exp(x_j - m) = 0 and take no part; the online form
+ * skips them (its rescaling is undefined while both maxima are -inf). A row with no entry
+ * above -inf has no softmax: its maximum is -inf, its sum 0 and its outputs NaN. Other
+ * entries are expected to be finite. */
 static int softmax_row(const job_t* jb, const double* xr, int64_t r) {
     const int64_t N = jb->N;
-    double m = xr[0];
-    for (int64_t j = 1; j < N; ++j)
+    double m = -INFINITY;
+    for (int64_t j = 0; j < N; ++j)
         if (xr[j] > m) m = xr[j];
+    double* yr = jb->y ? jb->y + r * N : NULL;
+    if (m == -INFINITY) {
+        if (jb->mean) jb->mean[r] = m;
+        if (jb->rstd) jb->rstd[r] = 0.0;
+        if (yr)
+            for (int64_t j = 0; j < N; ++j) yr[j] = NAN;
+        return ORC_OK;
+    }
     double d = 0.0;
     for (int64_t j = 0; j < N; ++j) d += exp(xr[j] - m);
 
-    double mo = xr[0], dn = 1.0; /* online: after the first element */
-    for (int64_t k = 1; k < N; ++k) {
+    double mo = -INFINITY, dn = 0.0; /* online */
+    for (int64_t k = 0; k < N; ++k) {
+        if (xr[k] == -INFINITY) continue;
         const double mk = xr[k] > mo ? xr[k] : mo;
-        dn = dn * exp(mo - mk) + exp(xr[k] - mk);
+        dn = (mo == -INFINITY ? 0.0 : dn * exp(mo - mk)) + exp(xr[k] - mk);
         mo = mk;
     }
     if (mo != m || !(fabs(dn - d) <= 1e-12 * d)) return ORC_EONLINE;
 
     if (jb->mean) jb->mean[r] = m;
     if (jb->rstd) jb->rstd[r] = d;
-    if (jb->y) {
-        double* yr = jb->y + r * N;
+    if (yr)
         for (int64_t j = 0; j < N; ++j) yr[j] = exp(xr[j] - m) / d;
-    }
     return ORC_OK;
 }
 

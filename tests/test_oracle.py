@@ -495,6 +495,36 @@ def test_softmax_matches_scipy_float64(dtype, rows, N):
     assert np.allclose(out["y"].sum(axis=1), 1.0, rtol=0, atol=1e-14)
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+def test_softmax_masked_entries(dtype):
+    # entries of -inf (masked logits) take no part: the softmax of a masked row is scipy's
+    # float64 softmax of its other entries, with exact zeros where masked; leading runs of
+    # -inf (where the online form's rescaling is undefined) included
+    from scipy.special import softmax as sp_softmax
+
+    inp = workloads.make_inputs(workloads.SOFTMAX.scaled(rows=6, N=300, dtype=dtype, seed=11))
+    x = inp["x"].clone()
+    rng = np.random.default_rng(12)
+    mask = rng.random(x.shape) < 0.4
+    mask[1, :37] = True  # a leading run
+    mask[2, 150:] = True  # a trailing run
+    mask[3, :] = False
+    mask[3, 299] = True
+    x[torch.from_numpy(mask)] = float("-inf")
+    out = oracle.softmax(x)
+    for r in range(x.shape[0]):
+        keep = ~mask[r]
+        ref = np.zeros(x.shape[1])
+        ref[keep] = sp_softmax(x[r].double().numpy()[keep])
+        assert np.allclose(out["y"][r], ref, rtol=1e-13, atol=0)
+        assert np.all(out["y"][r][mask[r]] == 0.0)
+        assert out["max"][r] == x[r].double().numpy()[keep].max()
+    # no entry above -inf: no softmax (NaN outputs), maximum -inf, sum 0
+    z = torch.full((2, 9), float("-inf"), dtype=x.dtype)
+    o = oracle.softmax(z)
+    assert np.all(np.isnan(o["y"])) and np.all(o["max"] == -np.inf) and np.all(o["sum"] == 0.0)
+
+
 def test_softmax_closed_forms_and_invariants():
     # two elements: the logistic function of the difference
     x = torch.tensor([[2.0, -1.0], [0.0, 0.0], [-5.0, 5.0]], dtype=torch.float32)
