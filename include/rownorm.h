@@ -22,6 +22,8 @@
  *   softmax_forward       y_j = exp(x_j - m) / sum_k exp(x_k - m), m = max_k x_k ("05 LLM Ops"
  *                         lesson, section 1 "Softmax"; the per-part (max, sum) pairs are
  *                         merged with the rescaling of its "Online Softmax" sections).
+ *                         Entries of -inf (masked logits) give exactly 0; a row with no
+ *                         entry above -inf gives NaN outputs, row max -inf and row sum 0.
  *
  * and the backward passes of LayerNorm and RMSNorm (ln_backward, rms_norm_backward).
  *

@@ -753,3 +753,42 @@ def test_softmax_large_logits_and_constant_rows():
         y = rn.softmax_forward(inp["x"].to(DEV))
         torch.cuda.synchronize()
         assert torch.equal(y, torch.full_like(y, 1.0 / 4096)), dtype
+
+
+# Masked logits (-inf entries) through every softmax path: random masks, leading and trailing
+# runs, a row with one entry left, and a row with none (NaN outputs, max -inf, sum 0).
+MASKED = [("fp32", 64, 4096, None), ("bf16", 64, 4096, None), ("fp32", 4096, 4096, None),  # vec, persistent
+          ("fp32", 33, 4095, None), ("bf16", 33, 4095, None), ("fp16", 33, 4095, {"x": 1, "y": 1}),  # element / pairs
+          ("bf16", 33, 4096, {"x": 1}),  # single elements
+          ("fp32", 16, 32768, None), ("fp32", 16, 65536, None), ("bf16", 8, 65536, None),  # one workgroup, 128-256 KiB
+          ("fp32", 4, 50257, None), ("bf16", 4, 50257, None),  # element / pair kernel, 16 waves
+          ("fp32", 5, 131072, None), ("bf16", 5, 131073, None)]  # split rows (rows 0-4 carry the patterns)
+
+
+@pytest.mark.parametrize("dtype,rows,N,off", MASKED, ids=lambda v: str(v))
+def test_softmax_masked_rows(dtype, rows, N, off):
+    w = workloads.SOFTMAX.scaled(rows=rows, N=N, seed=910 + N % 97, dtype=dtype)
+    inp = workloads.make_inputs(w)
+    rng = np.random.default_rng(N + rows)
+    mask = rng.random((rows, N)) < 0.3
+    mask[0, :] = False
+    mask[1, : N // 2] = True
+    mask[2, N // 3:] = True
+    mask[3, :] = True  # nothing left: no softmax
+    mask[4 % rows, :] = True
+    mask[4 % rows, N - 1] = False  # one entry left (y = 1 there)
+    x = inp["x"].clone()
+    x[torch.from_numpy(mask)] = float("-inf")
+    inp = dict(inp, x=x)
+    ref = run_oracle(w, inp)
+    y, _, ssum, smax = run_placed(w, inp, offset=off) if off else run_gpu(w, inp)
+    torch.cuda.synchronize()
+    dead = mask.all(axis=1)
+    live = torch.from_numpy(~dead)
+    yg = y.detach().cpu()
+    assert torch.isnan(yg[torch.from_numpy(dead)].float()).all(), "rows without a finite entry must be NaN"
+    assert (yg[live][torch.from_numpy(mask[~dead])] == 0).all(), "masked entries must be exactly 0"
+    check_softmax_y(yg[live], ref["y"][~dead])
+    check_equal_values(smax.cpu(), ref["max"], "row_max")  # -inf where nothing is left
+    check_rel(ssum.cpu()[live], ref["sum"][~dead], STAT_REL_TOL, "row_sum")
+    assert (ssum.cpu()[torch.from_numpy(dead)] == 0).all()
