@@ -279,17 +279,23 @@ __device__ __forceinline__ float wave_sum(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
-// Maximum over the 64 lanes, by the same exchange pattern.
+// Maximum of two values that is NaN if either is (v_maximum3_f32), unlike fmaxf, which
+// returns the other operand. Softmax takes its maxima this way so that a NaN logit makes its
+// row NaN (0 / 0 in the final scale) instead of silently dropping out of the row; -inf
+// (masked) entries still drop out, as max(-inf, x) = x.
+__device__ __forceinline__ float max_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
+// Maximum over the 64 lanes, by the same exchange pattern (NaN if any lane holds NaN).
 __device__ __forceinline__ float wave_max(float v) {
-    v = fmaxf(v, dpp<0xB1>(v));
-    v = fmaxf(v, dpp<0x4E>(v));
-    v = fmaxf(v, dpp<0x141>(v));
-    v = fmaxf(v, dpp<0x140>(v));
+    v = max_nan(v, dpp<0xB1>(v));
+    v = max_nan(v, dpp<0x4E>(v));
+    v = max_nan(v, dpp<0x141>(v));
+    v = max_nan(v, dpp<0x140>(v));
     const float r0 = bit_cast<float>(__builtin_amdgcn_readlane(bit_cast<int>(v), 0));
     const float r1 = bit_cast<float>(__builtin_amdgcn_readlane(bit_cast<int>(v), 16));
     const float r2 = bit_cast<float>(__builtin_amdgcn_readlane(bit_cast<int>(v), 32));
     const float r3 = bit_cast<float>(__builtin_amdgcn_readlane(bit_cast<int>(v), 48));
-    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+    return max_nan(max_nan(r0, r1), max_nan(r2, r3));
 }
 
 __device__ __forceinline__ float uniform(float v) {
@@ -328,7 +334,9 @@ constexpr float kLog2eLo = 1.92596298909109e-8f;            // log2(e) - kLog2e
 // product is formed exactly as hi + lo (fma for the rounding error of hi, plus the part of
 // log2(e) that fp32 drops), its integer part n is split off exactly, 2^(fraction) comes
 // from v_exp_f32 on [-0.5, 0.5], and ldexp applies 2^n without rounding (down to the
-// subnormal range). Arguments below -200 (including -inf, an empty part's maximum) give 0.
+// subnormal range). Arguments below -200 (including -inf, an empty part's maximum) give 0,
+// and so does NaN (-inf - (-inf) for a part holding only masked entries); a NaN logit
+// reaches the result through the row's maximum instead (see max_nan).
 __device__ __forceinline__ float exp_neg(float u) {
     u = fmaxf(u, -200.f);
     const float hi = u * kLog2e;
@@ -351,7 +359,7 @@ __device__ __forceinline__ Moments combine_equal(const Moments& a, const Moments
 // smarter.xin, sections "Online Softmax denominator correction" and "merging (max, sum)
 // with decay").
 __device__ __forceinline__ void softmax_combine(float& m, float& s, float mb, float sb) {
-    const float M = fmaxf(m, mb);
+    const float M = max_nan(m, mb);
     s = s * exp_neg(m - M) + sb * exp_neg(mb - M);
     m = M;
 }
@@ -665,7 +673,7 @@ struct VecRow {
                 float f[E];
                 IO::unpack(src[i], f);
 #pragma unroll
-                for (int e = 0; e < E; ++e) mx = valid(i, t, Ci) ? fmaxf(mx, f[e]) : mx;
+                for (int e = 0; e < E; ++e) mx = valid(i, t, Ci) ? max_nan(mx, f[e]) : mx;
             }
             const float mw = wave_max(mx);
             // exp(x - m_w): x - m_w is exact for the elements near the maximum.
@@ -921,7 +929,7 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_elem_kernel(Params p) {
         } else if constexpr (OT::SM) {
             float mx = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < V; ++i) mx = static_cast<unsigned>(i * LANES) + t < N ? fmaxf(mx, f[i]) : mx;
+            for (int i = 0; i < V; ++i) mx = static_cast<unsigned>(i * LANES) + t < N ? max_nan(mx, f[i]) : mx;
             const float mw = wave_max(mx);
             float sm = 0.f;
 #pragma unroll
@@ -1107,7 +1115,7 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_pair_kernel(Params p) {
             float mx = -INFINITY;
             asm volatile("" : "+v"(av));
 #pragma unroll
-            for (int e = 0; e < NE; ++e) mx = ok(e) ? fmaxf(mx, f[e]) : mx;
+            for (int e = 0; e < NE; ++e) mx = ok(e) ? max_nan(mx, f[e]) : mx;
             const float mw = wave_max(mx);
             float sm = 0.f;
             asm volatile("" : "+v"(av));
@@ -1308,7 +1316,7 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_stats_kernel(Params p
                 float f[E];
                 IO::unpack(src[i], f);
 #pragma unroll
-                for (int e = 0; e < E; ++e) mx = valid(i) ? fmaxf(mx, f[e]) : mx;
+                for (int e = 0; e < E; ++e) mx = valid(i) ? max_nan(mx, f[e]) : mx;
             }
             const float mw = wave_max(mx);
             float sm = 0.f;
@@ -1497,7 +1505,7 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_elem_stats_kernel(Par
         } else if constexpr (OT::SM) {
             float mx = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < V; ++i) mx = valid(i) ? fmaxf(mx, f[i]) : mx;
+            for (int i = 0; i < V; ++i) mx = valid(i) ? max_nan(mx, f[i]) : mx;
             const float mw = wave_max(mx);
             float sm = 0.f;
 #pragma unroll
@@ -1615,7 +1623,7 @@ __device__ __forceinline__ float block_max(float v, float* slots) {
     __syncthreads();
     float s = slots[0];
 #pragma unroll
-    for (int i = 1; i < NWAVES; ++i) s = fmaxf(s, slots[i]);
+    for (int i = 1; i < NWAVES; ++i) s = max_nan(s, slots[i]);
     return s;
 }
 
@@ -1654,7 +1662,7 @@ __global__ __launch_bounds__(kGeneralThreads) void rownorm_general_kernel(Params
             center = block_sum<NW>(s1, slots[0]) / nf;
         } else if constexpr (OT::SM) {
             float m = -INFINITY;
-            for (int64_t j = tid; j < N; j += kGeneralThreads) m = fmaxf(m, IO::load1(p.x, xo + j));
+            for (int64_t j = tid; j < N; j += kGeneralThreads) m = max_nan(m, IO::load1(p.x, xo + j));
             K = block_max<NW>(m, slots[0]);
             float s = 0.f;
             for (int64_t j = tid; j < N; j += kGeneralThreads)

@@ -792,3 +792,31 @@ def test_softmax_masked_rows(dtype, rows, N, off):
     check_equal_values(smax.cpu(), ref["max"], "row_max")  # -inf where nothing is left
     check_rel(ssum.cpu()[live], ref["sum"][~dead], STAT_REL_TOL, "row_sum")
     assert (ssum.cpu()[torch.from_numpy(dead)] == 0).all()
+
+
+@pytest.mark.parametrize("op", ["ln", "rms", "fused_add_rms", "fused_add_ln", "softmax"])
+@pytest.mark.parametrize("rows,N", [(4096, 4096), (4096, 4095), (4, 65536)])
+def test_nonfinite_rows_stay_in_their_rows(op, rows, N):
+    # a NaN or +inf in a row makes that row's outputs non-finite and leaves every other row
+    # bit for bit as without it (persistent workgroups loop over many rows; split rows
+    # exchange records), whatever the path
+    w = BASES[op].scaled(rows=rows, N=N, seed=930, dtype="bf16")
+    inp = workloads.make_inputs(w)
+    clean = [o.clone() if o is not None else None for o in run_gpu(w, inp)]
+    bad_rows = [1, rows // 2, rows - 1]
+    x = inp["x"].clone()
+    x[bad_rows[0], N // 3] = float("nan")
+    x[bad_rows[1], 0] = float("inf")
+    x[bad_rows[2], N - 1] = float("nan")
+    dirty = run_gpu(w, dict(inp, x=x))
+    torch.cuda.synchronize()
+    keep = torch.ones(rows, dtype=torch.bool)
+    keep[bad_rows] = False
+    for c, d in zip(clean, dirty):
+        if c is None:
+            continue
+        assert torch.equal(c[keep].view(torch.uint8) if c.dim() > 1 else c[keep].view(torch.uint8),
+                           d[keep].view(torch.uint8) if d.dim() > 1 else d[keep].view(torch.uint8))
+    y = dirty[0]
+    for r in bad_rows:
+        assert not torch.isfinite(y[r].float()).all()
