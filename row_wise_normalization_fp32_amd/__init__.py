@@ -24,7 +24,7 @@ from typing import Optional, Tuple, Union
 import torch
 
 __all__ = [
-    "ln_forward", "rms_norm", "fused_add_rms_norm", "fused_add_layer_norm", "softmax_forward", "ln_backward",
+    "ln_forward", "layer_norm", "rms_norm", "fused_add_rms_norm", "fused_add_layer_norm", "softmax_forward", "ln_backward",
     "rms_norm_backward", "backward_workspace_bytes", "forward_workspace_bytes", "plan", "plan_backward",
     "RowNormError", "LIB_PATH", "VARIANTS", "STATUS", "version",
 ]
@@ -247,6 +247,10 @@ def ln_forward(x: torch.Tensor, gamma: Optional[torch.Tensor] = None, beta: Opti
     _call("ln", "ln_forward", x, None, gamma, beta, y, None, mean, rstd, rows, N, eps, (ldx, 0, ldy, 0), variant,
           stream)
     return (y, mean, rstd) if want else y
+
+
+# The same function under the name of the usual Python wrapper of a LayerNorm kernel.
+layer_norm = ln_forward
 
 
 def rms_norm(x: torch.Tensor, weight: Optional[torch.Tensor] = None, eps: float = 1e-6, *,

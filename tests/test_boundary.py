@@ -432,3 +432,11 @@ def test_plan_split_rows():
     # workspace alignment and overlap
     assert rn.plan("ln", 64, 65536, f32, workspace_bytes=need, ptrs={"workspace": (1 << 47) + 4})[0] == ALIGN
     assert rn.plan("ln", 64, 65536, f32, workspace_bytes=need, ptrs={"workspace": 1 << 40})[0] == ALIAS
+
+
+def test_python_wrapper_names():
+    # the C ABI names, plus layer_norm for the LayerNorm forward
+    assert rn.layer_norm is rn.ln_forward
+    for n in ("ln_forward", "layer_norm", "rms_norm", "fused_add_rms_norm", "fused_add_layer_norm",
+              "softmax_forward", "ln_backward", "rms_norm_backward"):
+        assert callable(getattr(rn, n)) and n in rn.__all__
