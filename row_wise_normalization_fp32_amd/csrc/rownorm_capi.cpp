@@ -308,13 +308,17 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     const bool vec = plan->variant == rn::V_WAVE || plan->variant == rn::V_WORKGROUP;
     plan->exact = vec && C == int64_t(64) * W * plan->chunks_per_lane;
     // Persistent launch: for exact shapes with enough rows that workgroups would otherwise
-    // be launched many times over (measured: it pays from about 2048 workgroups up; softmax,
+    // be launched many times over, and for the element / pair kernels with many rows.
+    // Measured on MI355X (cold cache): vectorized launches gain from 256 workgroups up
+    // (softmax fp32 1024x4096 48% -> 62%, LayerNorm bf16 512x16384 43% -> 54%, fused add +
+    // LayerNorm bf16 2048x4096 55% -> 60%, LayerNorm bf16 2048x4096 45% -> 47%; softmax,
     // which has no parameters, gains from the streaming loads and stores and the resident
-    // grid alone). Parameters go to LDS once per workgroup; the LayerNorm ops with both keep
-    // gamma in VGPRs and stage only beta, so the LDS need is at most one row (64 KiB).
+    // grid alone); the element / pair kernels from about 2048 (fp32 1024x4095: 42% -> 41%).
+    // Parameters go to LDS once per workgroup; the LayerNorm ops with both keep gamma in
+    // VGPRs and stage only beta, so the LDS need is at most one row (64 KiB).
     const bool has_params = a.gamma != nullptr || (ln && a.beta != nullptr);
-    plan->persistent = blocks >= rn::kPersistentBlocks &&
-                       ((vec && plan->exact && C <= group_cap) || plan->variant == rn::V_ELEMENT);
+    plan->persistent = (vec && plan->exact && C <= group_cap && blocks >= rn::kPersistentVecBlocks) ||
+                       (plan->variant == rn::V_ELEMENT && blocks >= rn::kPersistentBlocks);
     plan->lds_bytes = 0;
     if (plan->persistent && vec && has_params) plan->lds_bytes = static_cast<int>(C * 16);  // one parameter vector in LDS
     *chunks = C;

@@ -100,7 +100,8 @@ constexpr int kSoftmaxElemMaxPerLane = 64;  // softmax rows (no parameters in re
 constexpr int kSoftmaxPairMaxPerLane = 32;  // elements / 32 pairs per lane, rows up to 65536
 constexpr int kElemCuRowBytes = 32768; // element kernels, persistent: row bytes held per CU
 constexpr int64_t kMaxGrid = 1 << 20;  // grid cap; kernels loop over the remaining rows
-constexpr int64_t kPersistentBlocks = 2048;  // at least this many workgroups: persistent launch
+constexpr int64_t kPersistentBlocks = 2048;  // element / pair kernels: persistent launch from this many workgroups
+constexpr int64_t kPersistentVecBlocks = 256;  // vectorized kernels: persistent launch from this many workgroups
 constexpr int kWideSegChunks = 2048;   // split-row variant: 16-byte chunks per segment (one workgroup)
 constexpr int kWideElemSeg = 8192;     // split-row element variant: elements per segment (one workgroup)
 constexpr int kBwdMaxParts = 1024;     // backward: at most this many partial column rows (workspace bound)

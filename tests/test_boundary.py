@@ -62,7 +62,7 @@ def test_status_strings_and_version():
 @pytest.mark.parametrize("op,dtype,rows,N,variant,W,V,persistent", [
     ("ln", torch.float32, 64, 1024, "wave", 1, 4, False),              # C1: 256 chunks
     ("ln", torch.float32, 128, 4096, "workgroup", 4, 4, False),        # C2: 1024 chunks
-    ("rms", torch.float16, 2048, 4096, "workgroup", 2, 4, False),      # C3: 512 chunks, 1024 groups
+    ("rms", torch.float16, 2048, 4096, "workgroup", 2, 4, True),       # C3: 512 chunks, 1024 workgroups of 2 rows
     ("fused_add_rms", torch.float16, 256, 4096, "workgroup", 2, 4, False),   # C4
     ("fused_add_rms", torch.bfloat16, 256, 4096, "workgroup", 2, 4, False),  # C4
     ("ln", torch.bfloat16, 4096, 16384, "workgroup", 8, 4, True),      # C5: 2048 chunks, 4096 groups
@@ -83,7 +83,8 @@ def test_status_strings_and_version():
     ("ln", torch.bfloat16, 8, 16385, "general", 0, 0, False),          # odd and beyond the element kernel
     ("ln", torch.float32, 8, 65536, "general", 0, 0, False),           # long rows without a workspace
     ("fused_add_ln", torch.bfloat16, 8192, 4096, "workgroup", 2, 4, True),
-    ("fused_add_ln", torch.float32, 256, 4096, "workgroup", 4, 4, False),
+    ("fused_add_ln", torch.float32, 256, 4096, "workgroup", 4, 4, True),   # 256 workgroups: persistent from there
+    ("fused_add_ln", torch.float32, 255, 4096, "workgroup", 4, 4, False),
     ("softmax", torch.float32, 128, 4096, "workgroup", 4, 4, False),
     ("softmax", torch.float32, 8192, 4096, "workgroup", 4, 4, True),   # persistent without parameters
     ("softmax", torch.float16, 64, 333, "element", 1, 4, False),
@@ -132,8 +133,12 @@ def test_plan_persistent_launches():
     # with parameters: one parameter vector in LDS
     st, info = rn.plan("rms", 8192, 4096, torch.bfloat16, ptrs={"gamma": 1 << 44})
     assert st == OK and info["persistent"] and info["lds_bytes"] == 4096 * 2
-    # too few workgroups: grid per row
-    assert not rn.plan("softmax", 2048, 4096, torch.bfloat16)[1]["persistent"]
+    # vectorized launches are persistent from 256 workgroups, the element / pair kernels from 2048
+    assert rn.plan("softmax", 2048, 4096, torch.bfloat16)[1]["persistent"]  # 1024 workgroups
+    assert not rn.plan("softmax", 510, 4096, torch.bfloat16)[1]["persistent"]  # 255 workgroups of 2 rows
+    assert rn.plan("softmax", 512, 4096, torch.bfloat16)[1]["persistent"]
+    assert not rn.plan("ln", 2047, 4095, torch.float32)[1]["persistent"]  # element kernel, 2047 workgroups
+    assert rn.plan("ln", 2048, 4095, torch.float32)[1]["persistent"]
     # ragged rows of the vectorized kernels are never persistent
     st, info = rn.plan("rms", 1 << 15, 1000, torch.float32, ptrs={"gamma": 1 << 44})
     assert st == OK and not info["exact"] and not info["persistent"]
