@@ -63,8 +63,12 @@ def test_status_strings_and_version():
     ("ln", torch.float32, 64, 1024, "wave", 1, 4, False),              # C1: 256 chunks
     ("ln", torch.float32, 128, 4096, "workgroup", 4, 4, False),        # C2: 1024 chunks
     ("rms", torch.float16, 2048, 4096, "workgroup", 2, 4, True),       # C3: 512 chunks, 1024 workgroups of 2 rows
-    ("fused_add_rms", torch.float16, 256, 4096, "workgroup", 2, 4, False),   # C4
-    ("fused_add_rms", torch.bfloat16, 256, 4096, "workgroup", 2, 4, False),  # C4
+    # C4: 2 rows per workgroup would make 128 workgroups; one row per 4-wave workgroup instead
+    ("fused_add_rms", torch.float16, 256, 4096, "workgroup", 4, 2, True),
+    ("fused_add_rms", torch.bfloat16, 256, 4096, "workgroup", 4, 2, True),
+    ("fused_add_rms", torch.bfloat16, 64, 4096, "workgroup", 4, 2, False),
+    ("ln", torch.bfloat16, 511, 4096, "workgroup", 2, 4, True),       # 256 workgroups of 2 rows
+    ("rms", torch.float16, 255, 3072, "workgroup", 4, 2, False),      # 384 chunks, not exact
     ("ln", torch.bfloat16, 4096, 16384, "workgroup", 8, 4, True),      # C5: 2048 chunks, 4096 groups
     ("fused_add_rms", torch.float16, 8192, 4096, "workgroup", 2, 4, True),
     ("ln", torch.float32, 16, 16384, "workgroup", 16, 4, False),
@@ -135,8 +139,12 @@ def test_plan_persistent_launches():
     assert st == OK and info["persistent"] and info["lds_bytes"] == 4096 * 2
     # vectorized launches are persistent from 256 workgroups, the element / pair kernels from 2048
     assert rn.plan("softmax", 2048, 4096, torch.bfloat16)[1]["persistent"]  # 1024 workgroups
-    assert not rn.plan("softmax", 510, 4096, torch.bfloat16)[1]["persistent"]  # 255 workgroups of 2 rows
-    assert rn.plan("softmax", 512, 4096, torch.bfloat16)[1]["persistent"]
+    # 510 rows would be 255 workgroups of 2 rows: one row per workgroup instead, 510 workgroups
+    st, info = rn.plan("softmax", 510, 4096, torch.bfloat16)
+    assert info["persistent"] and info["rows_per_block"] == 1 and info["waves_per_row"] == 4
+    st, info = rn.plan("softmax", 512, 4096, torch.bfloat16)
+    assert info["persistent"] and info["rows_per_block"] == 2 and info["waves_per_row"] == 2
+    assert not rn.plan("softmax", 255, 4096, torch.bfloat16)[1]["persistent"]  # 255 workgroups of 1 row
     assert not rn.plan("ln", 2047, 4095, torch.float32)[1]["persistent"]  # element kernel, 2047 workgroups
     assert rn.plan("ln", 2048, 4095, torch.float32)[1]["persistent"]
     # ragged rows of the vectorized kernels are never persistent
