@@ -138,8 +138,8 @@ def kernel_name(w, plan):
     dtype, op, waves per row, chunks per lane, row groups per workgroup, exact, affine, flags)."""
     if w.op in ("ln_bwd", "rms_bwd"):
         if plan["variant"] == "wide":
-            return (f"rn::rownorm_bwd_wide_stats_kernel + rn::rownorm_bwd_wide_dx_kernel ({w.dtype}, {w.op}, "
-                    f"8192-element segments, 512 lanes each, at most {plan['grid_blocks']} workgroups per segment) "
+            return (f"rn::rownorm_bwd_wide_clear_kernel + rn::rownorm_bwd_wide_onepass_kernel ({w.dtype}, {w.op}, "
+                    f"8192-element segments, 512 lanes each, at most {plan['grid_blocks']} row blocks) "
                     f"+ rn::rownorm_bwd_cols_kernel")
         k = "rownorm_bwd_vec_kernel" if plan["variant"] == "workgroup" else "rownorm_bwd_elem_kernel"
         return (f"rn::{k} ({w.dtype}, {w.op}, W={plan['waves_per_row']} waves per row, V={plan['chunks_per_lane']}, "
@@ -456,8 +456,8 @@ def _more():
          "row-wise softmax, fp32 I/O, 1024 x 50257 (vocabulary-sized rows, not whole chunks: element kernel, "
          "one 16-wave workgroup per row)"),
         ("ln_backward_split_rows", workloads.LN_BWD.scaled(rows=1024, N=65536, name="ln_bwd_bf16_1024x65536"),
-         "LayerNorm backward, bf16 I/O, 1024 x 65536 (rows beyond one workgroup: segment sums, then dx with "
-         "per-segment column partials, then column sums; x and dy read twice)"),
+         "LayerNorm backward, bf16 I/O, 1024 x 65536 (rows beyond one workgroup: one launch in which the "
+         "segments of a row exchange their sums through the workspace, x and dy read once; then column sums)"),
     ]
 
 

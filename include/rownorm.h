@@ -251,10 +251,18 @@ int fused_add_rms_norm_variant(const void* x, const void* residual, const void* 
  *                do not matter; on return they are unspecified. Calls that share a
  *                workspace must be ordered (same stream).
  * Rows of up to 16384 elements are held by one row group. Longer rows (any N) are split
- * into 8192-element segments over three launches: per-segment sums of g and g * xhat into
- * the workspace, then dx from the row's combined sums with the parameter-gradient columns
- * accumulated per segment, then the column sums (x and dy are read twice; plan variant
- * RN_VARIANT_WIDE). Row and column sums are formed in fp32 in a fixed order (no atomics):
+ * into 8192-element segments (plan variant RN_VARIANT_WIDE). With a 16-byte aligned
+ * workspace and up to (workgroups the device keeps resident) / 2 segments per row, x and dy
+ * are read once: a small launch clears a ticket counter and the segment records in the
+ * workspace, then workgroups take (row block, segment) tickets in order, publish each
+ * row's per-segment sums of g and g * xhat in the workspace, wait for the row's other
+ * segments (only ever for tickets taken before or with their own, so the wait cannot
+ * depend on a workgroup that is not running) and write dx; the column sums follow. A wait
+ * is bounded (about a second): should other work keep the device's compute units away for
+ * that long, the affected rows' dx and the parameter gradients of their columns come out
+ * NaN rather than the call hanging. Otherwise three launches: per-segment sums into the
+ * workspace, dx with the parameter-gradient columns, column sums (x and dy read twice).
+ * Row and column sums are formed in fp32 in a fixed order (no floating-point atomics):
  * results are bitwise reproducible on a given device.
  */
 size_t rn_backward_workspace_bytes(int op, int64_t rows, int64_t N);

@@ -369,8 +369,10 @@ __global__ __launch_bounds__(256) void rownorm_bwd_cols_kernel(BwdColParams p) {
 
 // ---------------------------------------------------------------------------------------
 // Split-row backward: rows longer than one workgroup holds (more than 16384 elements). A row
-// is cut into S segments of kBwdSeg elements (512 lanes x 16), and the work takes three
-// launches:
+// is cut into S segments of kBwdSeg elements (512 lanes x 16). The one-pass kernel below
+// (rownorm_bwd_wide_onepass_kernel) is the usual path; rows of more segments than half the
+// workgroups the device keeps resident, and workspaces that are not 16-byte aligned, take
+// three launches instead:
 //   1. rownorm_bwd_wide_stats_kernel: per (row, segment) the segment's sum of g = dy * gamma
 //      and of g * xhat, one record of two floats per segment in the workspace;
 //   2. rownorm_bwd_wide_dx_kernel: workgroup (q, s) owns segment s of rows q, q + Q, ...: it
@@ -537,6 +539,217 @@ __global__ __launch_bounds__(kBwdSegLanes) void rownorm_bwd_wide_dx_kernel(BwdPa
     if constexpr (LN) SG::store_f32(p.ws + (static_cast<int64_t>(Q) + q) * p.N + e0, static_cast<uint32_t>(Ns), vec, t, adb);
 }
 
+// ---------------------------------------------------------------------------------------
+// One-pass split rows: x and dy are read once. The rows are cut into P blocks of R rows; a
+// ticket is one (block, segment) pair, ticket = block * S + segment. Workgroups take
+// tickets from a counter in the workspace in increasing order. For each row of its block,
+// the workgroup holding a ticket:
+//   - reduces its segment's sum g and sum g * xhat and publishes them as two 64-bit words
+//     (tag 1 in the upper half, the float's bits in the lower half; single-copy atomic, so a
+//     reader sees either the cleared word or the whole value);
+//   - issues the loads of its next row;
+//   - waits (wave 0, one lane per record) until all S records of the row carry the tag,
+//     adds them in a fixed order (the same bits in every workgroup of the row), and writes
+//     dx for its segment, accumulating its columns' dgamma / dbeta terms in registers;
+// then writes its columns of partial row `block` ([2][P][N], as the column kernel reads).
+// Progress does not depend on which workgroups are resident: a workgroup waits only for
+// the S - 1 other tickets of its block, which were or will be taken before any later
+// ticket. If the lowest unfinished block still has tickets nobody holds, fewer than S
+// workgroups hold tickets of it and no workgroup holds a later one, so with a grid of at
+// least S workgroups (the host's condition) some workgroup is free to take the next
+// ticket. The wait is bounded all the same (kBwdSpinLimit polls, about a second): past it
+// the workgroup sets the time-out flag and makes its rows' dx and parameter partials NaN.
+// The counter, flag and records are zeroed by rownorm_bwd_wide_clear_kernel before each
+// launch (a kernel, not a memset, so that the call can be captured in a graph).
+// ---------------------------------------------------------------------------------------
+
+template <int DT>  // one instance per dtype's translation unit
+__global__ __launch_bounds__(256) void rownorm_bwd_wide_clear_kernel(u32x4* p, int64_t n16) {
+    const u32x4 z{0u, 0u, 0u, 0u};
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n16;
+         i += static_cast<int64_t>(gridDim.x) * 256)
+        p[i] = z;
+}
+
+// One row's segment as loaded: 16-byte groups kept packed (VEC), or single elements.
+template <int DT, bool VEC>
+struct SegRaw {
+    using IO = Io<DT>;
+    static constexpr int V = kBwdSegPerLane;
+    static constexpr int G = IO::E;  // elements per 16-byte group
+    u32x4 v[VEC ? V / G : 1];
+    float f[VEC ? 1 : V];
+
+    __device__ __forceinline__ void load(const void* base, uint32_t nbytes, int t) {
+        const Rsrc r = make_rsrc(base, nbytes);
+        if constexpr (VEC) {
+#pragma unroll
+            for (int i = 0; i < V / G; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (i * kBwdSegLanes + t) * 16, 0, 0);
+        } else {
+#pragma unroll
+            for (int k = 0; k < V; ++k) f[k] = IO::bload(r, static_cast<uint32_t>(k * kBwdSegLanes + t));
+        }
+    }
+    // element k of the lane: the same positions as BwdSeg's load / store / store_f32
+    __device__ __forceinline__ float operator[](int k) const {
+        if constexpr (VEC)
+            return IO::elem(v[k / G], k % G);
+        else
+            return f[k];
+    }
+};
+
+template <int DT, int OP, bool HG, bool VEC>
+__global__ __launch_bounds__(kBwdSegLanes) void rownorm_bwd_wide_onepass_kernel(BwdParams p) {
+    using SG = BwdSeg<DT>;
+    using RW = SegRaw<DT, VEC>;
+    constexpr int V = SG::V;
+    constexpr bool LN = OP == OP_LN;
+    const int lane = threadIdx.x & 63;
+    const int wr = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int t = threadIdx.x;
+    __shared__ WavePart part[2][kBwdSegLanes / 64];
+    __shared__ float rowsum[2];
+    __shared__ int row_bad;
+    __shared__ unsigned s_ticket;
+    // the columns' dgamma (and dbeta) terms, slot k of lane t at [k][t]: each lane owns its
+    // slots, so they need no barrier; in LDS, not VGPRs, so that two workgroups fit a CU
+    __shared__ float acc_s[LN ? 2 : 1][V][kBwdSegLanes];
+    int buf = 0;
+    const int S = p.S;
+    const unsigned total = static_cast<unsigned>(p.parts) * static_cast<unsigned>(S);
+    const int64_t rowbytes = p.N * SG::SB;
+    for (;;) {
+        if (t == 0) s_ticket = __hip_atomic_fetch_add(p.sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const unsigned ticket = s_ticket;  // read before the first barrier of the block's rows
+        if (ticket >= total) break;        // uniform over the workgroup
+        const int64_t blk = ticket / static_cast<unsigned>(S);
+        const int seg = static_cast<int>(ticket % static_cast<unsigned>(S));
+        const int64_t e0 = static_cast<int64_t>(seg) * kBwdSeg;
+        const int Ns = static_cast<int>(p.N - e0 < kBwdSeg ? p.N - e0 : kBwdSeg);
+        const uint32_t nb = static_cast<uint32_t>(Ns * SG::SB);
+        const char* xb = static_cast<const char*>(p.x) + e0 * SG::SB;
+        const char* db = static_cast<const char*>(p.dy) + e0 * SG::SB;
+        RW gr;
+        if constexpr (HG) gr.load(static_cast<const char*>(p.gamma) + e0 * SG::SB, nb, t);
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            acc_s[0][k][t] = 0.f;
+            if constexpr (LN) acc_s[LN ? 1 : 0][k][t] = 0.f;
+        }
+        // the segment's sums of one row, published as the row's record `seg`
+        auto post = [&](int64_t row, const RW& x, const RW& d) {
+            const float mean = LN ? p.mean[row] : 0.f;
+            const float rstd = p.rstd[row];
+            float sg = 0.f, sgx = 0.f;
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const float xh = LN ? (x[k] - mean) * rstd : x[k] * rstd;
+                const float g = HG ? d[k] * gr[k] : d[k];
+                sg += g;
+                sgx = fmaf(g, xh, sgx);
+            }
+            float Sg = wave_sum(sg), Sgx = wave_sum(sgx);
+            group_sum2<kBwdSegLanes / 64>(part, buf, lane, wr, Sg, Sgx);
+            if (t == 0) {
+                unsigned long long* rec = p.rec64 + 2 * (row * S + seg);
+                const unsigned long long tag = 1ull << 32;
+                __hip_atomic_store(rec, tag | bit_cast<unsigned>(Sg), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(rec + 1, tag | bit_cast<unsigned>(Sgx), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        };
+        const int64_t r0 = blk * p.R;
+        const int64_t r1 = r0 + p.R < p.rows ? r0 + p.R : p.rows;
+        // three rows in flight: row (sums posted, waiting), row + 1 (sums posted before the
+        // wait for row), row + 2 (loads issued before that wait)
+        RW cx, cd, nx, nd;
+        cx.load(xb + r0 * rowbytes, nb, t);
+        cd.load(db + r0 * rowbytes, nb, t);
+        if (r0 + 1 < r1) {
+            nx.load(xb + (r0 + 1) * rowbytes, nb, t);
+            nd.load(db + (r0 + 1) * rowbytes, nb, t);
+        }
+        post(r0, cx, cd);
+        bool timed_out = false;
+        for (int64_t row = r0; row < r1; ++row) {
+            RW mx, md;
+            if (row + 2 < r1) {
+                mx.load(xb + (row + 2) * rowbytes, nb, t);
+                md.load(db + (row + 2) * rowbytes, nb, t);
+            }
+            if (row + 1 < r1) post(row + 1, nx, nd);
+            if (wr == 0) {
+                // lane k adds records k, k + 64, ... in order, then a butterfly whose every
+                // step adds two equal operand pairs: the same bits in every workgroup
+                const unsigned long long* rec = p.rec64 + 2 * row * S;
+                float a = 0.f, b = 0.f;
+                bool bad = false;
+                for (int k = lane; k < S; k += 64) {
+                    unsigned long long w0 = 0, w1 = 0;
+                    for (int n = 0;; ++n) {
+                        w0 = __hip_atomic_load(rec + 2 * k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        w1 = __hip_atomic_load(rec + 2 * k + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if ((w0 >> 32) != 0 && (w1 >> 32) != 0) break;
+                        if (n >= kBwdSpinLimit) {
+                            bad = true;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(8);
+                    }
+                    a += bit_cast<float>(static_cast<unsigned>(w0));
+                    b += bit_cast<float>(static_cast<unsigned>(w1));
+                }
+#pragma unroll
+                for (int step = 1; step < 64; step <<= 1) {
+                    a += __shfl_xor(a, step);
+                    b += __shfl_xor(b, step);
+                }
+                const bool any_bad = __any(bad);  // all 64 lanes active here
+                if (any_bad) {
+                    a = b = __builtin_nanf("");
+                    if (lane == 0) __hip_atomic_store(p.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+                if (lane == 0) {
+                    rowsum[0] = a;
+                    rowsum[1] = b;
+                    row_bad = any_bad ? 1 : 0;
+                }
+            }
+            __syncthreads();
+            const float c1 = LN ? rowsum[0] * p.inv_n : 0.f;
+            const float c2 = rowsum[1] * p.inv_n;
+            timed_out = timed_out || row_bad != 0;
+            const float mean = LN ? p.mean[row] : 0.f;
+            const float rstd = p.rstd[row];
+            float r[V];
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const float xh = LN ? (cx[k] - mean) * rstd : cx[k] * rstd;
+                const float g = HG ? cd[k] * gr[k] : cd[k];
+                r[k] = rstd * ((g - c1) - xh * c2);
+                acc_s[0][k][t] = fmaf(cd[k], xh, acc_s[0][k][t]);
+                if constexpr (LN) acc_s[LN ? 1 : 0][k][t] += cd[k];
+            }
+            if (p.dx) SG::store(static_cast<char*>(p.dx) + (row * p.N + e0) * SG::SB, nb, VEC, t, r);
+            cx = nx;
+            cd = nd;
+            nx = mx;
+            nd = md;
+        }
+        if (p.ws == nullptr) continue;  // uniform over the grid
+        float adg[V], adb[LN ? V : 1];
+#pragma unroll
+        for (int k = 0; k < V; ++k) {
+            adg[k] = timed_out ? __builtin_nanf("") : acc_s[0][k][t];
+            if constexpr (LN) adb[k] = timed_out ? __builtin_nanf("") : acc_s[LN ? 1 : 0][k][t];
+        }
+        SG::store_f32(p.ws + blk * p.N + e0, static_cast<uint32_t>(Ns), VEC, t, adg);
+        if constexpr (LN)
+            SG::store_f32(p.ws + (static_cast<int64_t>(p.parts) + blk) * p.N + e0, static_cast<uint32_t>(Ns), VEC, t, adb);
+    }
+}
+
 constexpr int rows_per_block_bwd(int W) { return W >= 16 ? 1 : 16 / W; }  // 16-wave workgroups
 
 using BwdKernel = void (*)(BwdParams);
@@ -623,8 +836,11 @@ inline hipError_t bwd_resident(BwdKernel k, int dev, const Plan& plan, int* per_
 // Row kernel, then column kernel. The row kernel's grid P is what the device keeps resident
 // (compute units x workgroups per unit for this instance, queried once per instance and
 // device), capped by the plan: more workgroups would only add partial rows to sum.
-// Split rows: statistics launch, dx launch (Q workgroups per segment: what the device keeps
-// resident, capped by the plan's workspace bound), column launch.
+// Split rows, when the device keeps at least 2 S one-pass workgroups resident: clear launch,
+// one-pass launch (P row blocks, P = what the device keeps resident / S, capped by the
+// plan's workspace bound; grid = min(resident, P S) workgroups), column launch. Otherwise:
+// statistics launch, dx launch (Q workgroups per segment, bounded the same way), column
+// launch.
 template <int DT>
 inline hipError_t launch_bwd_wide(int op, const Plan& plan, const BwdParams& p0, const BwdColParams& cp0,
                                   hipStream_t s) {
@@ -637,25 +853,56 @@ inline hipError_t launch_bwd_wide(int op, const Plan& plan, const BwdParams& p0,
     const BwdKernel ks = RN_BW(rownorm_bwd_wide_stats_kernel);
     const BwdKernel kd = RN_BW(rownorm_bwd_wide_dx_kernel);
 #undef RN_BW
+#define RN_B1(VV)                                                                                                  \
+    (ln ? (hg ? rownorm_bwd_wide_onepass_kernel<DT, OP_LN, true, VV> : rownorm_bwd_wide_onepass_kernel<DT, OP_LN, false, VV>) \
+        : (hg ? rownorm_bwd_wide_onepass_kernel<DT, OP_RMS, true, VV> : rownorm_bwd_wide_onepass_kernel<DT, OP_RMS, false, VV>))
+    const BwdKernel k1 = p.vec ? RN_B1(true) : RN_B1(false);
+#undef RN_B1
     if (p.S < 1 || p.rec == nullptr) return hipErrorInvalidValue;
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     int per_cu = 0, cus = 0;
-    e = bwd_resident(kd, dev, plan, &per_cu, &cus);
-    if (e != hipSuccess) return e;
-    int64_t Q = static_cast<int64_t>(cus) * per_cu / p.S;
-    if (Q < 1) Q = 1;
-    if (Q > plan.grid) Q = plan.grid;
-    const int64_t total = p.rows * p.S;
-    const unsigned g1 = static_cast<unsigned>(total < kMaxGrid ? total : kMaxGrid);
     void* argv[] = {&p};
-    e = hipLaunchKernel(reinterpret_cast<const void*>(ks), dim3(g1), dim3(kBwdSegLanes), argv, 0, s);
+    e = bwd_resident(k1, dev, plan, &per_cu, &cus);
     if (e != hipSuccess) return e;
-    p.parts = static_cast<int>(Q);
-    e = hipLaunchKernel(reinterpret_cast<const void*>(kd), dim3(static_cast<unsigned>(Q * p.S)), dim3(kBwdSegLanes),
-                        argv, 0, s);
-    if (e != hipSuccess) return e;
+    const int64_t resident = static_cast<int64_t>(cus) * per_cu;
+    if (p.sync != nullptr && p.rec64 != nullptr && resident >= 2 * static_cast<int64_t>(p.S)) {
+        int64_t P = resident / p.S;
+        if (P > plan.grid) P = plan.grid;
+        const int64_t R = (p.rows + P - 1) / P;
+        P = (p.rows + R - 1) / R;
+        const int64_t tickets = P * p.S;
+        // counter, flag and records: 256 + rows * S * 16 bytes from p.sync
+        const int64_t n16 = (256 + p.rows * p.S * 16) / 16;
+        int64_t gc = (n16 + 255) / 256;
+        if (gc > 1024) gc = 1024;
+        u32x4* clr = reinterpret_cast<u32x4*>(p.sync);
+        void* zargv[] = {&clr, const_cast<int64_t*>(&n16)};
+        e = hipLaunchKernel(reinterpret_cast<const void*>(rownorm_bwd_wide_clear_kernel<DT>), dim3(static_cast<unsigned>(gc)),
+                            dim3(256), zargv, 0, s);
+        if (e != hipSuccess) return e;
+        p.parts = static_cast<int>(P);
+        p.R = static_cast<int>(R);
+        const int64_t g = resident < tickets ? resident : tickets;
+        e = hipLaunchKernel(reinterpret_cast<const void*>(k1), dim3(static_cast<unsigned>(g)), dim3(kBwdSegLanes), argv,
+                            0, s);
+        if (e != hipSuccess) return e;
+    } else {
+        e = bwd_resident(kd, dev, plan, &per_cu, &cus);
+        if (e != hipSuccess) return e;
+        int64_t Q = static_cast<int64_t>(cus) * per_cu / p.S;
+        if (Q < 1) Q = 1;
+        if (Q > plan.grid) Q = plan.grid;
+        const int64_t total = p.rows * p.S;
+        const unsigned g1 = static_cast<unsigned>(total < kMaxGrid ? total : kMaxGrid);
+        e = hipLaunchKernel(reinterpret_cast<const void*>(ks), dim3(g1), dim3(kBwdSegLanes), argv, 0, s);
+        if (e != hipSuccess) return e;
+        p.parts = static_cast<int>(Q);
+        e = hipLaunchKernel(reinterpret_cast<const void*>(kd), dim3(static_cast<unsigned>(Q * p.S)),
+                            dim3(kBwdSegLanes), argv, 0, s);
+        if (e != hipSuccess) return e;
+    }
     if (cp.dgamma == nullptr && cp.dbeta == nullptr) return hipSuccess;
     cp.parts = p.parts;
     void* cargv[] = {&cp};

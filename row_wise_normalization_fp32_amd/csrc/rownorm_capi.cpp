@@ -443,10 +443,13 @@ size_t bwd_records_offset(int op, int64_t rows, int64_t N) {
     return (bwd_partial_bytes(op, rows, N) + 255) / 256 * 256;
 }
 
+// Split rows, from the records offset: a 256-byte header (ticket counter, time-out flag),
+// then 16 bytes per (row, segment) record (two 64-bit words; the two-pass kernels use the
+// first 8 bytes per record of the same space).
 size_t bwd_workspace_bytes(int op, int64_t rows, int64_t N) {
     if (rows <= 0 || N <= 0) return 0;
     if (!bwd_wide(N)) return bwd_partial_bytes(op, rows, N);
-    return bwd_records_offset(op, rows, N) + static_cast<size_t>(rows * bwd_wide_segments(N) * 8);
+    return bwd_records_offset(op, rows, N) + 256 + static_cast<size_t>(rows * bwd_wide_segments(N) * 16);
 }
 
 struct BwdArgs {
@@ -578,10 +581,19 @@ int run_bwd(BwdArgs a, hipStream_t stream) {
     p.rec = nullptr;
     p.S = 0;
     p.vec = 0;
+    p.sync = nullptr;
+    p.rec64 = nullptr;
+    p.R = 0;
     if (plan.variant == rn::V_WIDE) {
-        p.rec = reinterpret_cast<float*>(static_cast<char*>(a.ws) + bwd_records_offset(a.op, a.rows, a.N));
+        char* recs = static_cast<char*>(a.ws) + bwd_records_offset(a.op, a.rows, a.N);
+        p.rec = reinterpret_cast<float*>(recs);
         p.S = static_cast<int>(bwd_wide_segments(a.N));
         p.vec = plan.exact ? 1 : 0;
+        // the one-pass kernel's 64-bit atomics and 16-byte clears need 16-byte alignment
+        if (reinterpret_cast<uintptr_t>(recs) % 16 == 0) {
+            p.sync = reinterpret_cast<unsigned*>(recs);
+            p.rec64 = reinterpret_cast<unsigned long long*>(recs + 256);
+        }
     }
     rn::BwdColParams cp;
     cp.ws = p.ws;

@@ -133,6 +133,42 @@ def test_backward_split_rows_variants(op):
     run_case(base.scaled(rows=600, N=16392, seed=1324, dtype="bf16"))
 
 
+# Rows of more than 64 segments: each lane of the waiting wave adds several records of the
+# row. Rows of so many segments that the device keeps fewer than 2 S one-pass workgroups
+# resident (S > 128 for the one-workgroup-per-CU instances: fp32, and rows that are not whole
+# 16-byte groups) take the statistics + dx launches instead.
+MANY_SEGMENTS = [("ln_bwd", "bf16", 3, 1100000), ("rms_bwd", "fp32", 2, 1100000), ("ln_bwd", "fp16", 2, 2200005)]
+
+
+@pytest.mark.parametrize("op,dtype,rows,N", MANY_SEGMENTS, ids=lambda v: str(v))
+def test_backward_split_rows_many_segments(op, dtype, rows, N):
+    base = workloads.LN_BWD if op == "ln_bwd" else workloads.RMS_BWD
+    run_case(base.scaled(rows=rows, N=N, seed=1350 + rows, dtype=dtype))
+
+
+def test_backward_split_rows_workspace_contents_do_not_matter():
+    # the one-pass launch takes tickets from a counter and polls records in the workspace;
+    # both are cleared by the call itself: a workspace full of ones (every record "ready")
+    # gives the same bits as a fresh one, and the wait time-out flag (the second 32-bit word
+    # of the 256-byte header in front of the rows x S 16-byte records) stays clear
+    rows, N = 256, 65536
+    w = workloads.LN_BWD.scaled(rows=rows, N=N, seed=1341, dtype="bf16")
+    inp = workloads.make_inputs(w)
+    mean, rstd = _stats(w, inp)
+    dev = {k: v.to(DEV) for k, v in inp.items()}
+    m, r = torch.from_numpy(mean).to(DEV), torch.from_numpy(rstd).to(DEV)
+    need = rn.backward_workspace_bytes("ln", rows, N)
+    header = need - (256 + rows * (N // 8192) * 16)
+    ref = [o.clone() for o in rn.ln_backward(dev["dy"], dev["x"], m, r, dev["gamma"])]
+    for fill in (0xFF, 0x00):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device=DEV)
+        outs = rn.ln_backward(dev["dy"], dev["x"], m, r, dev["gamma"], workspace=ws)
+        torch.cuda.synchronize()
+        for a, b in zip(ref, outs):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+        assert int(ws[header + 4:header + 8].view(torch.int32).item()) == 0
+
+
 def test_backward_split_rows_deterministic_and_param_only():
     w = workloads.LN_BWD.scaled(rows=64, N=24576, seed=1330, dtype="bf16")
     inp = workloads.make_inputs(w)

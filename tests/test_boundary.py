@@ -365,10 +365,11 @@ def test_backward_plan_and_validation():
     assert rn.plan_backward("ln", 8, 32768, bf16, ptrs={"workspace": 1 << 46})[0] == OK
     assert rn.plan_backward("ln", 8, 16384, bf16)[0] == OK
     # split-row workspace: partial rows (sets x min(rows, 2048 / S) x N x 4), then from a
-    # 256-byte boundary the records (rows x S x 8)
-    assert rn.backward_workspace_bytes("ln", 100, 32768) == 2 * 100 * 32768 * 4 + 100 * 4 * 8
+    # 256-byte boundary a 256-byte header (ticket counter, time-out flag) and the records
+    # (rows x S x 16)
+    assert rn.backward_workspace_bytes("ln", 100, 32768) == 2 * 100 * 32768 * 4 + 256 + 100 * 4 * 16
     assert rn.backward_workspace_bytes("rms", 4096, 40001) == \
-        -(-(409 * 40001 * 4) // 256) * 256 + 4096 * 5 * 8
+        -(-(409 * 40001 * 4) // 256) * 256 + 256 + 4096 * 5 * 16
     # workspace: required for parameter gradients, at least rn_backward_workspace_bytes
     assert rn.backward_workspace_bytes("ln", 4096, 16384) == 2 * 1024 * 16384 * 4
     assert rn.backward_workspace_bytes("rms", 100, 64) == 100 * 64 * 4
