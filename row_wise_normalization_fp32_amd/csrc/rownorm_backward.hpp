@@ -33,6 +33,11 @@
 
 namespace rn {
 
+// Cache-policy operand of the buffer builtins: the non-temporal bit (gfx940 and later), for
+// x, dy and dx, which each call touches once (LayerNorm bf16 1024 x 65536 split rows: 120.5
+// -> 116.0 us; fp32 512 x 65536: 103 -> 94.7 us).
+constexpr int kNonTemporal = 2;
+
 // Sum of two per-wave values across the row group's waves (one barrier).
 template <int W>
 __device__ __forceinline__ void group_sum2(WavePart (*part)[W > 1 ? W : 1], int& buf, int lane, int wr, float& a,
@@ -251,8 +256,8 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_bwd_elem_kernel(BwdParam
 #pragma unroll
         for (int i = 0; i < V; ++i) {
             const unsigned j = static_cast<unsigned>(i * LANES) + t;
-            xf[i] = IO::bload(xr, j);
-            df[i] = IO::bload(dr, j);
+            xf[i] = IO::template bload<kNonTemporal>(xr, j);
+            df[i] = IO::template bload<kNonTemporal>(dr, j);
         }
         const float mean = LN ? p.mean[row] : 0.f;
         const float rstd = p.rstd[row];
@@ -282,7 +287,7 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_bwd_elem_kernel(BwdParam
 #pragma unroll
             for (int i = 0; i < V; ++i) {
                 const float g = HG ? df[i] * gam(i) : df[i];
-                IO::bstore(o, static_cast<unsigned>(i * LANES) + t, rstd * ((g - c1) - xf[i] * c2));
+                IO::template bstore<kNonTemporal>(o, static_cast<unsigned>(i * LANES) + t, rstd * ((g - c1) - xf[i] * c2));
             }
         }
     }
@@ -371,8 +376,8 @@ __global__ __launch_bounds__(256) void rownorm_bwd_cols_kernel(BwdColParams p) {
 // Split-row backward: rows longer than one workgroup holds (more than 16384 elements). A row
 // is cut into S segments of kBwdSeg elements (512 lanes x 16). The one-pass kernel below
 // (rownorm_bwd_wide_onepass_kernel) is the usual path; rows of more segments than half the
-// workgroups the device keeps resident, and workspaces that are not 16-byte aligned, take
-// three launches instead:
+// workgroups the device keeps resident, 16-bit rows that are not whole 16-byte groups, and
+// workspaces that are not 16-byte aligned take three launches instead:
 //   1. rownorm_bwd_wide_stats_kernel: per (row, segment) the segment's sum of g = dy * gamma
 //      and of g * xhat, one record of two floats per segment in the workspace;
 //   2. rownorm_bwd_wide_dx_kernel: workgroup (q, s) owns segment s of rows q, q + Q, ...: it
@@ -408,15 +413,17 @@ struct BwdSeg {
         }
     }
 
+    // AUX: cache policy of the 16-byte stores (kNonTemporal for data not read again soon)
+    template <int AUX = 0>
     __device__ static __forceinline__ void store(void* base, uint32_t nbytes, bool vec, int t, const float (&f)[V]) {
         const Rsrc r = make_rsrc(base, nbytes);
         if (vec) {
 #pragma unroll
             for (int i = 0; i < V / G; ++i)
-                __builtin_amdgcn_raw_buffer_store_b128(IO::pack(&f[i * G]), r, (i * kBwdSegLanes + t) * 16, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(IO::pack(&f[i * G]), r, (i * kBwdSegLanes + t) * 16, 0, AUX);
         } else {
 #pragma unroll
-            for (int k = 0; k < V; ++k) IO::bstore(r, static_cast<uint32_t>(k * kBwdSegLanes + t), f[k]);
+            for (int k = 0; k < V; ++k) IO::template bstore<AUX>(r, static_cast<uint32_t>(k * kBwdSegLanes + t), f[k]);
         }
     }
 
@@ -548,7 +555,7 @@ __global__ __launch_bounds__(kBwdSegLanes) void rownorm_bwd_wide_dx_kernel(BwdPa
 //     (tag 1 in the upper half, the float's bits in the lower half; single-copy atomic, so a
 //     reader sees either the cleared word or the whole value);
 //   - issues the loads of its next row;
-//   - waits (wave 0, one lane per record) until all S records of the row carry the tag,
+//   - waits (one wave, one lane per record) until all S records of the row carry the tag,
 //     adds them in a fixed order (the same bits in every workgroup of the row), and writes
 //     dx for its segment, accumulating its columns' dgamma / dbeta terms in registers;
 // then writes its columns of partial row `block` ([2][P][N], as the column kernel reads).
@@ -580,14 +587,15 @@ struct SegRaw {
     u32x4 v[VEC ? V / G : 1];
     float f[VEC ? 1 : V];
 
+    template <int AUX = 0>
     __device__ __forceinline__ void load(const void* base, uint32_t nbytes, int t) {
         const Rsrc r = make_rsrc(base, nbytes);
         if constexpr (VEC) {
 #pragma unroll
-            for (int i = 0; i < V / G; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (i * kBwdSegLanes + t) * 16, 0, 0);
+            for (int i = 0; i < V / G; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, (i * kBwdSegLanes + t) * 16, 0, AUX);
         } else {
 #pragma unroll
-            for (int k = 0; k < V; ++k) f[k] = IO::bload(r, static_cast<uint32_t>(k * kBwdSegLanes + t));
+            for (int k = 0; k < V; ++k) f[k] = IO::template bload<AUX>(r, static_cast<uint32_t>(k * kBwdSegLanes + t));
         }
     }
     // element k of the lane: the same positions as BwdSeg's load / store / store_f32
@@ -664,22 +672,25 @@ __global__ __launch_bounds__(kBwdSegLanes) void rownorm_bwd_wide_onepass_kernel(
         // three rows in flight: row (sums posted, waiting), row + 1 (sums posted before the
         // wait for row), row + 2 (loads issued before that wait)
         RW cx, cd, nx, nd;
-        cx.load(xb + r0 * rowbytes, nb, t);
-        cd.load(db + r0 * rowbytes, nb, t);
+        cx.template load<kNonTemporal>(xb + r0 * rowbytes, nb, t);
+        cd.template load<kNonTemporal>(db + r0 * rowbytes, nb, t);
         if (r0 + 1 < r1) {
-            nx.load(xb + (r0 + 1) * rowbytes, nb, t);
-            nd.load(db + (r0 + 1) * rowbytes, nb, t);
+            nx.template load<kNonTemporal>(xb + (r0 + 1) * rowbytes, nb, t);
+            nd.template load<kNonTemporal>(db + (r0 + 1) * rowbytes, nb, t);
         }
         post(r0, cx, cd);
         bool timed_out = false;
         for (int64_t row = r0; row < r1; ++row) {
             RW mx, md;
             if (row + 2 < r1) {
-                mx.load(xb + (row + 2) * rowbytes, nb, t);
-                md.load(db + (row + 2) * rowbytes, nb, t);
+                mx.template load<kNonTemporal>(xb + (row + 2) * rowbytes, nb, t);
+                md.template load<kNonTemporal>(db + (row + 2) * rowbytes, nb, t);
             }
             if (row + 1 < r1) post(row + 1, nx, nd);
-            if (wr == 0) {
+            // the last wave polls: not wave 0, whose lane 0 has just stored the record (vector
+            // memory counts retire in order, so its poll would also wait for those stores;
+            // LayerNorm bf16 1024 x 65536: 123.9 -> 120.5 us)
+            if (wr == kBwdSegLanes / 64 - 1) {
                 // lane k adds records k, k + 64, ... in order, then a butterfly whose every
                 // step adds two equal operand pairs: the same bits in every workgroup
                 const unsigned long long* rec = p.rec64 + 2 * row * S;
@@ -731,7 +742,7 @@ __global__ __launch_bounds__(kBwdSegLanes) void rownorm_bwd_wide_onepass_kernel(
                 acc_s[0][k][t] = fmaf(cd[k], xh, acc_s[0][k][t]);
                 if constexpr (LN) acc_s[LN ? 1 : 0][k][t] += cd[k];
             }
-            if (p.dx) SG::store(static_cast<char*>(p.dx) + (row * p.N + e0) * SG::SB, nb, VEC, t, r);
+            if (p.dx) SG::template store<kNonTemporal>(static_cast<char*>(p.dx) + (row * p.N + e0) * SG::SB, nb, VEC, t, r);
             cx = nx;
             cd = nd;
             nx = mx;
@@ -836,7 +847,8 @@ inline hipError_t bwd_resident(BwdKernel k, int dev, const Plan& plan, int* per_
 // Row kernel, then column kernel. The row kernel's grid P is what the device keeps resident
 // (compute units x workgroups per unit for this instance, queried once per instance and
 // device), capped by the plan: more workgroups would only add partial rows to sum.
-// Split rows, when the device keeps at least 2 S one-pass workgroups resident: clear launch,
+// Split rows, when the device keeps at least 2 S one-pass workgroups resident (and the rows
+// are fp32 or whole 16-byte groups, with a 16-byte aligned workspace): clear launch,
 // one-pass launch (P row blocks, P = what the device keeps resident / S, capped by the
 // plan's workspace bound; grid = min(resident, P S) workgroups), column launch. Otherwise:
 // statistics launch, dx launch (Q workgroups per segment, bounded the same way), column
@@ -867,7 +879,11 @@ inline hipError_t launch_bwd_wide(int op, const Plan& plan, const BwdParams& p0,
     e = bwd_resident(k1, dev, plan, &per_cu, &cus);
     if (e != hipSuccess) return e;
     const int64_t resident = static_cast<int64_t>(cus) * per_cu;
-    if (p.sync != nullptr && p.rec64 != nullptr && resident >= 2 * static_cast<int64_t>(p.S)) {
+    // 16-bit rows that are not whole 16-byte groups (two-byte loads, one workgroup per CU)
+    // measured faster in three launches (bf16 1024 x 65537: 154 us against 192 us one-pass;
+    // fp32 1024 x 65537: 274 against 240, bf16 1024 x 65536 in 16-byte groups: 143 against 116)
+    const bool onepass_rows = p.vec != 0 || DT == DT_F32;
+    if (onepass_rows && p.sync != nullptr && p.rec64 != nullptr && resident >= 2 * static_cast<int64_t>(p.S)) {
         int64_t P = resident / p.S;
         if (P > plan.grid) P = plan.grid;
         const int64_t R = (p.rows + P - 1) / P;
