@@ -22,6 +22,8 @@ def _calls():
     wd = {k: v.to(DEV) for k, v in workloads.make_inputs(workloads.LN_SPLIT.scaled(rows=64)).items()}
     bw = {k: v.to(DEV) for k, v in workloads.make_inputs(workloads.LN_BWD.scaled(rows=512, N=4096)).items()}
     _, m, r = rn.ln_forward(bw["x"], None, None, 1e-5, return_stats=True)
+    sb = {k: v.to(DEV) for k, v in workloads.make_inputs(workloads.LN_BWD.scaled(rows=256, N=65536)).items()}
+    _, m2, r2 = rn.ln_forward(sb["x"], None, None, 1e-5, return_stats=True)
     torch.cuda.synchronize()
     return [
         lambda: [rn.ln_forward(ln["x"], ln["gamma"], ln["beta"], 1e-5)],  # persistent vectorized
@@ -29,6 +31,9 @@ def _calls():
         lambda: [rn.ln_forward(rg["x"], rg["gamma"], rg["beta"], 1e-5)],  # persistent pairs
         lambda: [rn.ln_forward(wd["x"], wd["gamma"], wd["beta"], 1e-5)],  # split rows + workspace
         lambda: list(rn.ln_backward(bw["dy"], bw["x"], m, r, bw["gamma"])),  # row + column kernels
+        # split rows in one pass: tickets and records in each call's own workspace, calls
+        # on other streams competing for the compute units meanwhile
+        lambda: list(rn.ln_backward(sb["dy"], sb["x"], m2, r2, sb["gamma"])),
     ]
 
 

@@ -28,6 +28,8 @@ def test_graph_replays_match_eager():
     wel = {k: v.to(DEV) for k, v in workloads.make_inputs(workloads.C2.scaled(rows=4, N=50257)).items()}
     bw = {k: v.to(DEV) for k, v in workloads.make_inputs(workloads.LN_BWD.scaled(rows=256, N=4096)).items()}
     bl = {k: v.to(DEV) for k, v in workloads.make_inputs(workloads.RMS_BWD.scaled(rows=8, N=40000)).items()}
+    be = {k: v.to(DEV) for k, v in workloads.make_inputs(
+        workloads.LN_BWD.scaled(rows=6, N=40001, dtype="bf16")).items()}
 
     def run():
         y1, m1, r1 = rn.ln_forward(ln["x"], ln["gamma"], ln["beta"], 1e-5, return_stats=True)
@@ -39,8 +41,13 @@ def test_graph_replays_match_eager():
         _, m6, r6 = rn.ln_forward(bw["x"], None, None, 1e-5, return_stats=True)
         dx, dg, db = rn.ln_backward(bw["dy"], bw["x"], m6, r6, bw["gamma"])  # row + column kernels
         _, r8 = rn.rms_norm(bl["x"], None, 1e-6, return_rstd=True)
-        dx8, dw8 = rn.rms_norm_backward(bl["dy"], bl["x"], r8, bl["weight"])  # split rows: three launches
-        return [y1, m1, r1, y2, ro2, y3, ro3, y4, y5, y7, dx, dg, db, dx8, dw8]
+        # split rows in one pass (clear, one-pass and column launches; the clear kernel resets
+        # the ticket counter on every replay)
+        dx8, dw8 = rn.rms_norm_backward(bl["dy"], bl["x"], r8, bl["weight"])
+        _, m9, r9 = rn.ln_forward(be["x"], None, None, 1e-5, return_stats=True)
+        # 16-bit split rows that are not whole 16-byte groups: statistics, dx, column launches
+        dx9, dg9, db9 = rn.ln_backward(be["dy"], be["x"], m9, r9, be["gamma"])
+        return [y1, m1, r1, y2, ro2, y3, ro3, y4, y5, y7, dx, dg, db, dx8, dw8, dx9, dg9, db9]
 
     eager = [_bits(t) for t in run()]
     torch.cuda.synchronize()
