@@ -254,8 +254,8 @@ int fused_add_rms_norm_variant(const void* x, const void* residual, const void* 
  * into 8192-element segments (plan variant RN_VARIANT_WIDE). For fp32 rows and rows of
  * whole 16-byte groups, with a 16-byte aligned workspace and up to (workgroups the device
  * keeps resident) / 2 segments per row, x and dy are read once: a small launch clears a
- * ticket counter and the segment records in the
- * workspace, then workgroups take (row block, segment) tickets in order, publish each
+ * ticket counter and the segment records in the workspace, then workgroups take (row
+ * block, segment) tickets in order, publish each
  * row's per-segment sums of g and g * xhat in the workspace, wait for the row's other
  * segments (only ever for tickets taken before or with their own, so the wait cannot
  * depend on a workgroup that is not running) and write dx; the column sums follow. A wait
