@@ -2,17 +2,24 @@
 
 * fp32 outputs: max |y_gpu - y_ref| <= 1e-4 (absolute), y_ref in fp64.
 * fp16 / bf16 outputs: at most 2 output ulps from round(y_ref), the oracle's single
-  round-to-nearest-even of the fp64 result. The ulp is taken at max(|y_ref|, floor_T),
-  floor_bf16 = 2^-14 (spacing 2^-21) and floor_fp16 = 2^-10 (spacing 2^-20). Where a
-  LayerNorm output crosses zero (z * gamma close to -beta) an fp32-accumulating kernel
-  carries an absolute error of a few fp32 ulps of |beta| (about 3e-7 for |beta| near 0.4),
-  finer than the 2-ulp band of either format at its smallest normal magnitudes; the floors
-  put that band at 9.5e-7 (bf16) and 1.9e-6 (fp16). Above the floor the native 2-ulp bar
-  applies unchanged. RMSNorm has no additive term, so its outputs never cancel.
+  round-to-nearest-even of the fp64 result, with the ulp measured on the format's own grid:
+  the spacing at |y_ref|, and below the smallest normal (fp16 2^-14, bf16 2^-126) the
+  subnormal spacing (fp16 2^-24, bf16 2^-133). This native bar applies to RMSNorm, fused
+  add + RMSNorm and softmax: their outputs are products and quotients (x * rstd * w,
+  exp(x - m) / S) whose fp32 evaluation errs by a few fp32 ulps relative to the result,
+  far below one 16-bit ulp at any magnitude, so one rounding leaves at most 1 ulp.
+  LayerNorm and fused add + LayerNorm alone add beta: where an output crosses zero
+  (z * gamma close to -beta) the fp32 sum carries an absolute error of a few fp32 ulps of
+  |beta| (about 3e-7 for |beta| near 0.4), which no fp32-accumulating kernel avoids and
+  which exceeds the native 2-ulp band at the smallest magnitudes. For these two ops only,
+  the ulp is taken at max(|y_ref|, floor_T): floor_bf16 = 2^-14 (spacing 2^-21),
+  floor_fp16 = 2^-10 (spacing 2^-20), which puts the band at 9.5e-7 (bf16) and 1.9e-6
+  (fp16). Above the floor the native 2-ulp bar applies unchanged.
 * mean: |mean_gpu - mean_ref| <= 1e-5 * max(|mean_ref|, sigma_ref), sigma_ref = sqrt(var);
   rstd: |rstd_gpu / rstd_ref - 1| <= 1e-5.
 * residual_out: bit-exact.
-* softmax y: fp32 |y_gpu - y_ref| <= 1e-5 * y_ref + 2^-126; fp16 / bf16 as above (2 ulps).
+* softmax y: fp32 |y_gpu - y_ref| <= 1e-5 * y_ref + 2^-126; fp16 / bf16 as above (2 native
+  ulps).
   Derivation for fp32: each output is exp(x - m_w) * exp(m_w - m) / S. x - m_w is exact
   near the maximum; the kernel evaluates exp with a split argument (u * log2 e formed
   exactly as hi + lo, 2^n applied by ldexp, v_exp_f32 only on [-0.5, 0.5]), so each
@@ -35,7 +42,11 @@ FP32_ABS_TOL = 1e-4
 ULP_TOL = 2.0
 STAT_REL_TOL = 1e-5
 MANT_BITS = {"fp16": 10, "bf16": 7}
-MAG_FLOOR = {"fp16": 2.0 ** -10, "bf16": 2.0 ** -14}
+# Magnitude floor of the ulp for the ops whose outputs can cancel against beta.
+CANCEL_FLOOR = {"fp16": 2.0 ** -10, "bf16": 2.0 ** -14}
+# The format's own grid: below the smallest normal the spacing stays the subnormal one.
+NATIVE_FLOOR = {"fp16": 2.0 ** -14, "bf16": 2.0 ** -126}
+CANCELLING_OPS = ("ln", "fused_add_ln")
 # For one output ulp of a backward result: below its smallest normal (2^-14) fp16's grid
 # keeps the subnormal spacing 2^-24, so the magnitude is floored there; bf16's subnormals
 # (below 2^-126) are out of reach, 2^-24 only keeps the logarithm finite.
@@ -47,16 +58,20 @@ def dtype_name(t: torch.Tensor) -> str:
     return _NAME[t.dtype]
 
 
-def ulp_distance(got: np.ndarray, ref64: np.ndarray, dtype: str) -> np.ndarray:
-    """|got - round(ref)| in ulps of the I/O dtype at max(|ref|, floor of the dtype)."""
+def ulp_distance(got: np.ndarray, ref64: np.ndarray, dtype: str, op: str | None = None) -> np.ndarray:
+    """|got - round(ref)| in ulps of the I/O dtype at max(|ref|, floor): the cancellation
+    floor for LayerNorm ops, the format's own grid for every other op."""
     ref_r = oracle.round_to(ref64, dtype)
-    mag = np.maximum(np.abs(ref64), MAG_FLOOR[dtype])
+    floor = CANCEL_FLOOR[dtype] if op in CANCELLING_OPS else NATIVE_FLOOR[dtype]
+    mag = np.maximum(np.abs(ref64), floor)
     ulp = np.exp2(np.floor(np.log2(mag)) - MANT_BITS[dtype])
     return np.abs(got - ref_r) / ulp
 
 
-def check_y(y_gpu: torch.Tensor, y_ref: np.ndarray, what: str = "y") -> float:
-    """Assert the tolerance for y; return the worst error (abs for fp32, ulps otherwise)."""
+def check_y(y_gpu: torch.Tensor, y_ref: np.ndarray, what: str = "y", op: str | None = None) -> float:
+    """Assert the tolerance for y of operation `op` ("ln", "rms", "fused_add_rms",
+    "fused_add_ln", "softmax"); return the worst error (abs for fp32, ulps otherwise).
+    Without `op` the native 16-bit grid applies (the strictest bar)."""
     dt = dtype_name(y_gpu)
     got = y_gpu.detach().cpu().double().numpy().reshape(y_ref.shape)
     assert np.all(np.isfinite(got)), f"{what}: non-finite outputs"
@@ -64,7 +79,7 @@ def check_y(y_gpu: torch.Tensor, y_ref: np.ndarray, what: str = "y") -> float:
         err = float(np.abs(got - y_ref).max()) if got.size else 0.0
         assert err <= FP32_ABS_TOL, f"{what}: max abs error {err:.3g} > {FP32_ABS_TOL}"
         return err
-    d = ulp_distance(got, y_ref, dt)
+    d = ulp_distance(got, y_ref, dt, op)
     err = float(d.max()) if d.size else 0.0
     assert err <= ULP_TOL, f"{what}: max ulp distance {err} > {ULP_TOL} (count {(d > ULP_TOL).sum()})"
     return err
@@ -102,7 +117,7 @@ SOFTMAX_ABS_FLOOR = 2.0 ** -126
 def check_softmax_y(y_gpu: torch.Tensor, y_ref: np.ndarray) -> float:
     dt = dtype_name(y_gpu)
     if dt != "fp32":
-        return check_y(y_gpu, y_ref, "softmax y")
+        return check_y(y_gpu, y_ref, "softmax y", op="softmax")
     got = y_gpu.detach().cpu().double().numpy().reshape(y_ref.shape)
     assert np.all(np.isfinite(got)), "softmax y: non-finite outputs"
     err = np.abs(got - y_ref)

@@ -48,7 +48,7 @@ def _forward_case(rows, N, seed, expect):
     torch.cuda.synchronize()
     idx = torch.tensor(_rows_to_check(rows, N), device=DEV)
     ref = oracle.layer_norm(x[idx].cpu(), gamma.cpu(), beta.cpu(), EPS)
-    check_y(y[idx], ref["y"])
+    check_y(y[idx], ref["y"], op="ln")
     check_mean(mean[idx], ref["mean"], ref["rstd"], EPS)
     check_rstd(rstd[idx], ref["rstd"])
 
@@ -71,7 +71,7 @@ def test_split_rows_beyond_4gib():
     torch.cuda.synchronize()
     idx = torch.tensor(_rows_to_check(rows, N, 4), device=DEV)
     ref = oracle.layer_norm(x[idx].cpu(), gamma.cpu(), beta.cpu(), EPS)
-    check_y(y[idx], ref["y"])
+    check_y(y[idx], ref["y"], op="ln")
     check_mean(mean[idx], ref["mean"], ref["rstd"], EPS)
     check_rstd(rstd[idx], ref["rstd"])
 

@@ -70,7 +70,7 @@ def check_outputs(w: workloads.Workload, ref, a, b, c, d):
         check_equal_values(d, ref["max"], "row_max")
         check_rel(c, ref["sum"], STAT_REL_TOL, "row_sum")
         return err
-    err = check_y(a, ref["y"])
+    err = check_y(a, ref["y"], op=w.op)
     if w.op == "ln":
         check_mean(b, ref["mean"], ref["rstd"], w.eps)
         check_rstd(c, ref["rstd"])
@@ -261,7 +261,7 @@ def test_split_rows_element_offsets_strides_constant_and_in_place():
     x = inp["x"].to(DEV)
     rn.ln_forward(x, inp["gamma"].to(DEV), inp["beta"].to(DEV), w.eps, out=x)
     torch.cuda.synchronize()
-    check_y(x, ref["y"])
+    check_y(x, ref["y"], op="ln")
     w = workloads.FUSED_LN.scaled(rows=3, N=50257, seed=674)
     inp = workloads.make_inputs(w)
     ref = run_oracle(w, inp)
@@ -269,7 +269,7 @@ def test_split_rows_element_offsets_strides_constant_and_in_place():
     rn.fused_add_layer_norm(g["x"], g["residual"], g["gamma"], g["beta"], w.eps, out=g["x"],
                             residual_out=g["residual"])
     torch.cuda.synchronize()
-    check_y(g["x"], ref["y"])
+    check_y(g["x"], ref["y"], op="fused_add_ln")
     check_bits_equal(g["residual"], ref["residual_out"], "split-row element residual_out in place")
 
 
@@ -288,7 +288,7 @@ def test_split_rows_offset_constant_and_in_place():
     x = inp["x"].to(DEV)
     rn.ln_forward(x, inp["gamma"].to(DEV), inp["beta"].to(DEV), w.eps, out=x)
     torch.cuda.synchronize()
-    check_y(x, ref["y"])
+    check_y(x, ref["y"], op="ln")
     w = workloads.FUSED_LN.scaled(rows=3, N=65536, seed=633)
     inp = workloads.make_inputs(w)
     ref = run_oracle(w, inp)
@@ -296,7 +296,7 @@ def test_split_rows_offset_constant_and_in_place():
     rn.fused_add_layer_norm(g["x"], g["residual"], g["gamma"], g["beta"], w.eps, out=g["x"],
                             residual_out=g["residual"])
     torch.cuda.synchronize()
-    check_y(g["x"], ref["y"])
+    check_y(g["x"], ref["y"], op="fused_add_ln")
     check_bits_equal(g["residual"], ref["residual_out"], "split-row residual_out in place")
 
 
@@ -490,7 +490,7 @@ def test_misaligned_pointers_use_element_path():
     assert info["variant"] == "element"
     y, mean, rstd = rn.ln_forward(x, inp["gamma"].to(DEV), inp["beta"].to(DEV), w.eps, return_stats=True)
     torch.cuda.synchronize()
-    check_y(y, ref["y"])
+    check_y(y, ref["y"], op="ln")
     check_rstd(rstd, ref["rstd"])
 
 
@@ -504,7 +504,7 @@ def test_in_place(variant):
     y = rn.ln_forward(x, g["gamma"], g["beta"], w.eps, out=x, variant=variant)
     torch.cuda.synchronize()
     assert y.data_ptr() == x.data_ptr()
-    check_y(x, ref["y"])
+    check_y(x, ref["y"], op="ln")
     # fused: residual_out written over residual, y over x
     w = workloads.C4_BF16.scaled(rows=11, N=2048, seed=831)
     inp = workloads.make_inputs(w)
@@ -513,13 +513,13 @@ def test_in_place(variant):
     x, r = g["x"].clone(), g["residual"].clone()
     rn.fused_add_rms_norm(x, r, g["weight"], w.eps, out=x, residual_out=r, variant=variant)
     torch.cuda.synchronize()
-    check_y(x, ref["y"])
+    check_y(x, ref["y"], op="fused_add_rms")
     check_bits_equal(r, ref["residual_out"], "residual_out in place")
     # fused: residual_out written over x, y over residual
     x, r = g["x"].clone(), g["residual"].clone()
     rn.fused_add_rms_norm(x, r, g["weight"], w.eps, out=r, residual_out=x, variant=variant)
     torch.cuda.synchronize()
-    check_y(r, ref["y"])
+    check_y(r, ref["y"], op="fused_add_rms")
     check_bits_equal(x, ref["residual_out"], "residual_out over x")
     # fused LayerNorm: every pairing of the outputs with the inputs
     w = workloads.FUSED_LN.scaled(rows=11, N=2048, seed=832)
@@ -531,7 +531,7 @@ def test_in_place(variant):
         rn.fused_add_layer_norm(t["x"], t["residual"], g["gamma"], g["beta"], w.eps, out=t[y_on],
                                 residual_out=t[ro_on], variant=variant)
         torch.cuda.synchronize()
-        check_y(t[y_on], ref["y"])
+        check_y(t[y_on], ref["y"], op="fused_add_ln")
         check_bits_equal(t[ro_on], ref["residual_out"], f"fused LN residual_out over {ro_on}")
     # softmax in place
     w = workloads.SOFTMAX.scaled(rows=11, N=2048, seed=833, dtype="bf16")
@@ -602,7 +602,7 @@ def test_three_dimensional_input():
     y = rn.rms_norm(x3, inp["weight"].to(DEV), w.eps)
     torch.cuda.synchronize()
     assert y.shape == (4, 6, 4096)
-    check_y(y.view(24, 4096), ref["y"])
+    check_y(y.view(24, 4096), ref["y"], op="rms")
 
 
 def test_outputs_fully_written_and_nothing_outside():
@@ -720,7 +720,7 @@ def test_persistent_in_place():
     x = g["x"].clone()
     rn.ln_forward(x, g["gamma"], g["beta"], w.eps, out=x)
     torch.cuda.synchronize()
-    check_y(x, ref["y"])
+    check_y(x, ref["y"], op="ln")
     w = workloads.C4_FP16.scaled(rows=8192, seed=921)
     inp = workloads.make_inputs(w)
     ref = run_oracle(w, inp)
@@ -728,7 +728,7 @@ def test_persistent_in_place():
     x, r = g["x"].clone(), g["residual"].clone()
     rn.fused_add_rms_norm(x, r, g["weight"], w.eps, out=x, residual_out=r)
     torch.cuda.synchronize()
-    check_y(x, ref["y"])
+    check_y(x, ref["y"], op="fused_add_rms")
     check_bits_equal(r, ref["residual_out"], "residual_out in place (persistent)")
     # fused LayerNorm in place over a persistent launch with 2 waves per row
     w = workloads.FUSED_LN.scaled(rows=8192, seed=922)
@@ -738,7 +738,7 @@ def test_persistent_in_place():
     x, r = g["x"].clone(), g["residual"].clone()
     rn.fused_add_layer_norm(x, r, g["gamma"], g["beta"], w.eps, out=x, residual_out=r)
     torch.cuda.synchronize()
-    check_y(x, ref["y"])
+    check_y(x, ref["y"], op="fused_add_ln")
     check_bits_equal(r, ref["residual_out"], "fused LN residual_out in place (persistent)")
 
 
