@@ -11,9 +11,13 @@ Recipe (the same for every workload, so a reader can regenerate any input by han
 * draws in float64, in this order: the per-column parameters (gamma, then beta, or
   the RMSNorm weight), the per-row constants (offset, or mean then std), x, then the
   residual;
-* each array is rounded once to the I/O dtype by torch's CPU conversion
-  (float64 -> float32 -> dtype). The rounding of inputs is immaterial to parity: both
-  the oracle and the GPU receive the identical bits.
+* each array is rounded once, round-to-nearest-even, from float64 straight to the I/O
+  dtype (``round_once``: the value is scaled by a power of two so that the dtype's last
+  mantissa bit has weight 1, rounded to an integer by ``numpy.rint``, and scaled back;
+  every step but the ``rint`` is exact). A detour through float32 would round twice,
+  and for arbitrary float64 values that differs from one rounding at a few values per
+  million. The rounding of inputs is immaterial to parity: both the oracle and the GPU
+  receive the identical bits.
 
 The five headline workloads follow the shapes the pages measure: the LayerNorm
 walkthrough's "mean away from 0, variance away from 1" input advice at N=1024
@@ -123,8 +127,27 @@ RMS_BWD = Workload("rms_bwd_fp16_2048x4096", "rms_bwd", "fp16", 2048, 4096, 1e-6
 FUSED_8192 = C4_FP16.scaled(rows=8192, seed=1104, name="fused_fp16_8192x4096")
 
 
+# (explicit mantissa bits, exponent of the smallest normal) of each I/O dtype
+_FORMAT = {"fp32": (23, -126), "fp16": (10, -14), "bf16": (7, -126)}
+
+
+def round_once(a: np.ndarray, dtype: str) -> np.ndarray:
+    """float64 values rounded once (nearest, ties to even) to ``dtype``, still as float64.
+
+    With |v| = m * 2^k, 0.5 <= m < 1, the dtype's spacing at v is 2^(max(k - 1, emin) - mant);
+    v / spacing is exact, ``rint`` rounds it to the nearest integer (ties to even) and the
+    product with the spacing is exact again. Inputs here stay far inside every format's
+    range, so overflow is not handled."""
+    mant, emin = _FORMAT[dtype]
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    _, k = np.frexp(a)
+    e = np.maximum(k - 1, emin) - mant
+    return np.ldexp(np.rint(np.ldexp(a, -e)), e)
+
+
 def _to_dtype(a: np.ndarray, dtype: str) -> torch.Tensor:
-    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64)).to(torch.float32).to(TORCH_DTYPES[dtype])
+    # the rounded values are exact in float32 and in the dtype: the conversions are exact
+    return torch.from_numpy(round_once(a, dtype)).to(torch.float32).to(TORCH_DTYPES[dtype])
 
 
 def make_inputs(w: Workload) -> Dict[str, torch.Tensor]:
