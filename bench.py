@@ -20,19 +20,28 @@ Cold cache: inputs and outputs rotate through enough buffer sets (at least four,
 1 GiB per cycle) that each launch touches memory the previous launches have pushed out of
 L2 (8 x 4 MiB) and the 256 MiB memory-side cache. Inputs are resident in HBM before the timed region starts.
 
-Timed region: about 50 ms of plain device copies (the GPU's clocks rise over the first ~10 ms
-of work after the idle host-side set-up), W warmup steps untimed, then exactly K steps
-launched eagerly from Python, bracketed by torch.cuda.synchronize() ("eager": wall time over
-K), then the same K steps captured into one HIP graph, replayed once untimed and then five
-times, each replay between torch.cuda.synchronize() calls: ms_per_step is the median of the
-five replays' wall time over K (the eager time when no graph can be captured; "timing" says
-which). A graph is how a serving or
-training loop runs a fixed sequence of launches: each step still launches its kernel on its
-own rotating buffers; only the per-call Python and dispatch overhead between steps (about
-2 us per launch here) is gone. Two HIP events recorded on the launch stream (torch's current
-stream, which the binding passes to the C ABI) around each timed replay give the per-launch
-kernel duration used for the roofline (their median); rocprofv3's kernel durations agree
-with it. "replays" gives their spread (median and quartiles of the per-step device time).
+Timed region: the workload's own launches for about 300 ms first (the GPU has been idle
+during the host-side set-up, and its first milliseconds of work run slower), W warmup steps
+untimed, then exactly K steps launched eagerly from Python, bracketed by
+torch.cuda.synchronize() ("eager": wall time over K), then the same K steps captured into
+one HIP graph, replayed once untimed and then at least five times and for at least 200 ms
+of device time (--replay-ms), each replay between torch.cuda.synchronize() calls:
+ms_per_step is the median of the replays' wall time over K (the eager time when no graph
+can be captured; "timing" says which). A graph is how a serving or training loop runs a
+fixed sequence of launches: each step still launches its kernel on its own rotating
+buffers; only the per-call Python and dispatch overhead between steps (about 2 us per
+launch here) is gone. Two HIP events recorded on the launch stream (torch's current
+stream, which the binding passes to the C ABI) around each timed replay give the
+per-launch kernel duration used for the roofline (their median); rocprofv3's kernel
+durations agree with it. "replays" gives their spread (median and quartiles of the
+per-step device time).
+
+Ceiling: a hand-written streaming copy kernel (libstreamprobe.so, include/stream_probe.h)
+timed the same way at the traffic of LayerNorm bf16 at 8M elements, fused add + RMSNorm at
+8M elements and the 4096 x 16384 LayerNorm ("ceiling"); the roofline and the 8M-element
+sweep points also report their fraction of that measured ceiling. The CPU baseline runs
+last, after every GPU line, so that its seconds of host-only work do not precede a timed
+region.
 
 value = algorithmic bytes per step / ms_per_step (GB/s, 1 GB = 1e9 B). Algorithmic bytes:
 LayerNorm 2*rows*N*s + 2*N*s + 8*rows; fused 4*rows*N*s + N*s + 4*rows (with rstd); fused
@@ -42,7 +51,8 @@ fp32 partial column rows are not algorithmic bytes: they count against it.)
 
 The CPU baseline times the fp64 oracle (oracle/) on the same workload on the host cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--cache cold|hot]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--cache cold|hot] [--replay-ms MS]
+       python bench.py --ceiling-sweep      (every geometry of the copy kernel at the ceiling sizes)
        python bench.py --copy-calibration   (plain copy of known size, for counter scaling)
 """
 
@@ -183,7 +193,9 @@ def launch(rn, w, s):
 SET_TENSORS = {"ln": 2, "rms": 2, "softmax": 2, "fused_add_rms": 4, "fused_add_ln": 4, "ln_bwd": 3, "rms_bwd": 3}
 
 
-REPEATS = 5
+REPEATS = 5  # timed replays of a graph at least ...
+MIN_REPLAY_MS = 200.0  # ... and until they add up to this much device time (at most MAX_REPLAYS)
+MAX_REPLAYS = 400
 
 
 def spread(r):
@@ -196,24 +208,37 @@ def spread(r):
             "what": f"{len(reps)} timed replays of one HIP graph of the K steps, HIP events around each"}
 
 
-def graph_time(rn, w, sets, steps):
-    """`steps` launches (rotating over the buffer sets) captured into one HIP graph, replayed
-    once to warm up, then REPEATS timed replays, each bracketed by torch.cuda.synchronize()
-    (wall clock) and by two HIP events on the launch stream. Returns the medians per step
-    ({"wall_ms", "event_ms"}) and every replay's per-step event time ("repeats_ms"), or None
-    if the capture fails."""
+def replay_count(first_replay_ms: float) -> int:
+    """Timed replays: at least REPEATS, and enough to cover MIN_REPLAY_MS of device time (a
+    replay of a few short steps lasts about a millisecond, too short for a stable median),
+    at most MAX_REPLAYS."""
+    if first_replay_ms <= 0:
+        return REPEATS
+    return int(max(REPEATS, min(MAX_REPLAYS, math.ceil(MIN_REPLAY_MS / first_replay_ms))))
+
+
+def graph_time_fn(step, steps):
+    """`steps` calls of step(i) captured into one HIP graph, replayed once to warm up, then
+    timed replays (replay_count), each bracketed by torch.cuda.synchronize() (wall clock) and
+    by two HIP events on the launch stream. Returns the medians per step ({"wall_ms",
+    "event_ms"}) and every replay's per-step event time ("repeats_ms"), or None if the
+    capture fails."""
     import torch
 
     try:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(steps):
-                launch(rn, w, sets[i % len(sets)])
-        g.replay()
-        torch.cuda.synchronize()
+                step(i)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        n = replay_count(a.elapsed_time(b))
         walls, events = [], []
-        for _ in range(REPEATS):
+        for _ in range(n):
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             a.record()
@@ -230,9 +255,15 @@ def graph_time(rn, w, sets, steps):
         return None
 
 
+def graph_time(rn, w, sets, steps):
+    """The K steps of workload `w`, rotating over its buffer sets, as a replayed HIP graph."""
+    return graph_time_fn(lambda i: launch(rn, w, sets[i % len(sets)]), steps)
+
+
 TIMING = {
-    "graph": "K steps captured in one HIP graph; median over 5 replays, each timed by wall clock between "
-             "torch.cuda.synchronize() calls (after an untimed eager pass and an untimed replay)",
+    "graph": "K steps captured in one HIP graph; median over the timed replays (at least 5, and at least "
+             "200 ms of device time), each timed by wall clock between torch.cuda.synchronize() calls (after "
+             "the workload's own launches for about 300 ms, an untimed eager pass and an untimed replay)",
     "eager": "K eager launches timed by wall clock between torch.cuda.synchronize() calls",
 }
 
@@ -251,27 +282,28 @@ def kernel_time(r):
     rocprofv3's kernel durations also leave out); the eager stream events when no graph
     could be captured."""
     if r.get("graph_ms"):
-        return r["graph_ms"], (f"median over {REPEATS} replays of a HIP graph of the K timed launches, "
+        n = len(r.get("repeats_ms") or []) or REPEATS
+        return r["graph_ms"], (f"median over {n} replays of a HIP graph of the K timed launches, "
                                "HIP events around each")
     return r["kernel_ms"], "HIP events around the K eager launches (no graph capture)"
 
 
-def prime_gpu(dev, ms=50.0):
-    """Keeps the GPU busy with plain copies for about `ms` before a measurement. After the
-    host-side set-up of a workload the GPU has been idle, and the first ~10 ms of work after
-    idle run up to 8% slower (measured: C5 LayerNorm launches at 47-51 us, then a steady
-    46.3 us); without this the timed region would straddle that ramp. The copies touch
-    none of the workload's buffers."""
+def prime_gpu(step, ms=300.0):
+    """Runs the workload's own launches (step(i), eagerly) for about `ms` before a
+    measurement. After the host-side set-up of a workload (or the CPU baseline) the GPU
+    has been idle, and its first milliseconds of work run slower (measured: C5 LayerNorm
+    launches at 47-51 us, then a steady 46.3 us; a 50 ms prime of plain copies still left
+    the timed replays of a short run 4% slower than the same kernel later in the run). The
+    launches write only the workload's own output buffers."""
     import torch
 
-    src = torch.empty(64 << 20, dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
     t0 = time.perf_counter()
+    i = 0
     while (time.perf_counter() - t0) * 1e3 < ms:
-        for _ in range(10):
-            dst.copy_(src)
+        for _ in range(20):
+            step(i)
+            i += 1
         torch.cuda.synchronize()
-    del src, dst
 
 
 def measure(w, steps, warmup, cache, dev, graph=True):
@@ -286,7 +318,7 @@ def measure(w, steps, warmup, cache, dev, graph=True):
     log(f"[bench] {w.name}: {nsets} buffer set(s), {nbytes} algorithmic bytes per launch")
     sets = make_sets(w, nsets, dev)
     torch.cuda.synchronize()
-    prime_gpu(dev)
+    prime_gpu(lambda i: launch(rn, w, sets[i % nsets]))
     for i in range(warmup):
         launch(rn, w, sets[i % nsets])
     # Timed region: exactly `steps` steps, nothing else enqueued between them, bracketed by
@@ -390,38 +422,92 @@ def cpu_baseline(w, seconds, single_thread=False):
     return out
 
 
-def copy_reference(nbytes_each, steps, dev):
-    """GB/s of a plain device copy (torch -> the HIP runtime's copy kernel) moving the same
-    bytes as a LayerNorm launch (read nbytes_each, write nbytes_each), with the same buffer
-    rotation and the same timing as the steps (one replay of a HIP graph of K copies, wall
-    clock between synchronizations; eager copies if no graph can be captured): the practical
-    read+write ceiling on this GPU, for context."""
+PROBE_PATH = os.path.join(ROOT, "row_wise_normalization_fp32_amd", "libstreamprobe.so")
+# Geometry of the ceiling copy kernel (include/stream_probe.h) at each size (key: bytes read
+# per launch): 16-byte chunks per lane, lanes per workgroup, workgroups per CU (0: one
+# workgroup per tile; k > 0: k per CU, looping over the tiles), non-temporal accesses. Each
+# is the fastest of the 64 geometries `python bench.py --ceiling-sweep` times on MI355X
+# (profiles/stream_ceiling_sweep.md).
+CEILING_GEOM = {
+    16 << 20: {"chunks_per_lane": 4, "block_threads": 256, "per_cu": 0, "nontemporal": 1},
+    32 << 20: {"chunks_per_lane": 1, "block_threads": 256, "per_cu": 4, "nontemporal": 1},
+    128 << 20: {"chunks_per_lane": 2, "block_threads": 512, "per_cu": 0, "nontemporal": 1},
+}
+# Traffic sizes (bytes read = bytes written) of the ceiling: LayerNorm bf16 at 8M elements
+# (x 16 MiB), fused add + RMSNorm at 8M (x + residual 32 MiB), and the 4096 x 16384 bf16
+# LayerNorm (x 128 MiB).
+CEILING_READ_BYTES = tuple(sorted(CEILING_GEOM))
+
+
+def probe_lib():
+    import ctypes
+
+    if not os.path.exists(PROBE_PATH):
+        raise RuntimeError(f"{PROBE_PATH} is missing: build with `python row_wise_normalization_fp32_amd/build.py`")
+    lib = ctypes.CDLL(PROBE_PATH)
+    lib.rn_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    lib.rn_probe_copy.restype = ctypes.c_int
+    return lib
+
+
+def stream_ceiling(read_bytes, steps, dev, geom=None, prime_ms=100.0):
+    """Throughput of the hand-written streaming copy kernel (libstreamprobe.so) reading
+    `read_bytes` and writing as many, under the same protocol as the workloads: buffer sets
+    rotating over at least 1 GiB (cold L2 and memory-side cache), the kernel's own launches
+    for `prime_ms`, then K launches captured in a HIP graph and replayed; the per-launch
+    device time is the median of the HIP events around the replays. Checks that the copy
+    is exact. This is the practical read+write ceiling at that size."""
     import torch
 
-    nsets = max(MIN_COLD_SETS, math.ceil(COLD_FOOTPRINT / (2 * nbytes_each)))
-    src = [torch.ones(nbytes_each // 2, dtype=torch.bfloat16, device=dev) for _ in range(nsets)]
-    dst = [torch.empty_like(a) for a in src]
-    for i in range(5):
-        dst[i % nsets].copy_(src[i % nsets])
+    geom = dict(CEILING_GEOM[read_bytes] if geom is None else geom)
+    lib = probe_lib()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    grid = cus * geom["per_cu"] if geom["per_cu"] > 0 else 0
+    nsets = max(MIN_COLD_SETS, math.ceil(COLD_FOOTPRINT / (2 * read_bytes)))
+    src = [torch.randint(0, 1 << 15, (read_bytes // 2,), dtype=torch.int16, device=dev) for _ in range(nsets)]
+    dst = [torch.zeros_like(a) for a in src]
+
+    def step(i):
+        # torch's current stream at the call: inside a graph capture it is the capturing stream
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        st = lib.rn_probe_copy(src[i % nsets].data_ptr(), dst[i % nsets].data_ptr(), read_bytes,
+                               geom["chunks_per_lane"], geom["block_threads"], grid, geom["nontemporal"], stream)
+        if st != 0:
+            raise RuntimeError(f"rn_probe_copy failed with status {st}")
+
     torch.cuda.synchronize()
-    run = lambda: [dst[i % nsets].copy_(src[i % nsets]) for i in range(steps)]  # noqa: E731
-    g = None
-    try:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            run()
-        g.replay()
-        run = g.replay
-    except Exception as e:  # capture not possible here: eager copies
-        log(f"[bench] copy reference without a graph: {e}")
+    prime_gpu(step, prime_ms)
+    gt = graph_time_fn(step, steps)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    run()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
-    del g, src, dst
+    assert all(torch.equal(a, b) for a, b in zip(src, dst)), "stream probe: copy is not exact"
+    del src, dst
     torch.cuda.empty_cache()
-    return 2 * nbytes_each / (ms * 1e-3) / 1e9
+    if gt is None:
+        return None
+    ms = gt["event_ms"]
+    gbs = 2 * read_bytes / (ms * 1e-3) / 1e9
+    return {"read_bytes": read_bytes, "traffic_bytes": 2 * read_bytes, "kernel_ms": round(ms, 5),
+            "GBs": round(gbs, 2), "frac": round(gbs / PEAK_HBM_GBS, 4), "replays": spread(gt), "geometry": geom}
+
+
+def ceiling_sweep(steps, dev):
+    """Every geometry of the copy kernel at each ceiling size (cold protocol)."""
+    out = {}
+    for rb in CEILING_READ_BYTES:
+        rows = []
+        for v in (1, 2, 4, 8):
+            for b in (256, 512):
+                for nt in (0, 1):
+                    for per_cu in (0, 2, 4, 8):
+                        g = {"chunks_per_lane": v, "block_threads": b, "per_cu": per_cu, "nontemporal": nt}
+                        r = stream_ceiling(rb, steps, dev, g, prime_ms=20.0)
+                        rows.append({**g, "kernel_ms": r["kernel_ms"], "GBs": r["GBs"], "frac": r["frac"],
+                                     "q1_ms": r["replays"]["q1_ms"], "q3_ms": r["replays"]["q3_ms"]})
+                        log(f"[bench] ceiling {2 * rb} B traffic {g}: {r['kernel_ms'] * 1e3:.2f} us, {r['frac']:.3f}")
+        rows.sort(key=lambda x: x["kernel_ms"])
+        out[str(2 * rb)] = rows
+    return out
 
 
 def copy_calibration(dev):
@@ -462,6 +548,7 @@ def _more():
 
 
 def main():
+    global MORE, MIN_REPLAY_MS
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -474,6 +561,11 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the scale-up sweep and the hot-cache line")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-configuration throughput block")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--ceiling-sweep", action="store_true",
+                    help="time every geometry of the streaming copy kernel at the ceiling sizes, print JSON, exit")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-copy ceiling lines")
+    ap.add_argument("--replay-ms", type=float, default=MIN_REPLAY_MS,
+                    help="device time the timed graph replays of a line add up to (at least 5 replays)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -487,18 +579,15 @@ def main():
 
     import workloads
 
-    global MORE
     MORE = _more()
+    MIN_REPLAY_MS = args.replay_ms
     dev = "cuda:0"
     if args.copy_calibration:
         copy_calibration(dev)
         return
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle) ...")
-        cpu = cpu_baseline(workloads.C5, args.cpu_seconds, single_thread=True)
-        log(f"[bench] cpu baseline: {cpu}")
+    if args.ceiling_sweep:
+        print(json.dumps({"ceiling_sweep": ceiling_sweep(args.steps, dev)}), flush=True)
+        return
 
     w = workloads.C5
     log(f"[bench] timing {w.name} ({args.cache} cache) ...")
@@ -539,13 +628,7 @@ def main():
             "stream_ms_per_launch": round(r["kernel_ms"], 5),
             "bytes_per_launch": r["bytes"],
         },
-        "cpu_baseline": cpu,
-    }
-    cref = copy_reference(w.rows * w.N * w.elem_bytes, args.steps, dev)
-    out["copy_reference"] = {
-        "what": "plain device copy of the same bytes (x -> y) with the same buffer rotation",
-        "value": round(cref, 2), "unit": "GB/s", "frac_of_peak": round(cref / PEAK_HBM_GBS, 4),
-        "ln_value_over_copy": round(value / cref, 4),
+        "cpu_baseline": None,
     }
     if not args.no_fused:
         f = workloads.FUSED_8192
@@ -606,9 +689,6 @@ def main():
                     "GBs_events": round(rc["bytes"] / (rc["kernel_ms"] * 1e-3) / 1e9, 2),
                 }
             entry["bytes_per_call"] = rc["bytes"]
-            if not args.no_cpu_baseline:
-                cb = cpu_baseline(c, min(args.cpu_seconds, 1.0))
-                entry["cpu_oracle"] = {"rows_per_s": cb["rows_per_s"], "GBs": cb["value"], "cores": cb["cores"]}
             confs[c.name] = entry
         out["configs"] = confs
     if not args.no_sweep:
@@ -626,7 +706,7 @@ def main():
             xa = rx["bytes"] / (rx["kernel_ms"] * 1e-3) / 1e9
             xv = rx["bytes"] / (rx["eager_ms_per_step"] * 1e-3) / 1e9
             gm = rx["graph_ms"]
-            sweep[x.name] = {"elements": x.rows * x.N, "cache": cache,
+            sweep[x.name] = {"elements": x.rows * x.N, "cache": cache, "bytes": rx["bytes"],
                              # eager launches: HIP events around the K timed launches
                              "stream_ms_per_launch": round(rx["kernel_ms"], 5),
                              "frac_stream": round(xa / PEAK_HBM_GBS, 4),
@@ -636,6 +716,41 @@ def main():
                              "graph_ms": None if gm is None else round(gm, 5),
                              "frac_graph": None if gm is None else round(rx["bytes"] / (gm * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         out["scale_up_sweep"] = sweep
+    if not args.no_ceiling:
+        # The hand-written streaming copy kernel at the traffic of LayerNorm bf16 at 8M
+        # elements, fused add + RMSNorm at 8M elements and the 4096 x 16384 LayerNorm, under
+        # the same cold protocol: the practical read+write ceiling at each size.
+        ceil = {}
+        for rb in CEILING_READ_BYTES:
+            log(f"[bench] ceiling: streaming copy of {rb} bytes ...")
+            c = stream_ceiling(rb, min(args.steps, 100), dev)
+            if c is not None:
+                ceil[str(2 * rb)] = c
+        out["ceiling"] = {"what": "hand-written streaming copy kernel (libstreamprobe.so), same protocol as the "
+                                  "lines; key = bytes moved per launch (read + write)", "sizes": ceil}
+        by_traffic = {int(k): v for k, v in ceil.items()}
+
+        def vs_ceiling(nbytes, ms):
+            t = min(by_traffic, key=lambda k: abs(k - nbytes), default=None)
+            if t is None or abs(t - nbytes) > 0.02 * nbytes or not ms:
+                return None
+            return round((nbytes / ms) / (t / by_traffic[t]["kernel_ms"]), 4)
+
+        out["roofline"]["frac_of_ceiling"] = vs_ceiling(r["bytes"], kms)
+        for x in out.get("scale_up_sweep", {}).values():
+            bx = x.get("bytes")
+            if bx and x.get("graph_ms"):
+                x["graph_frac_of_ceiling"] = vs_ceiling(bx, x["graph_ms"])
+    # The CPU baseline last: the oracle on the host cores keeps the GPU idle for seconds,
+    # so it runs after every GPU line instead of before the headline.
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(workloads.C5, args.cpu_seconds, single_thread=True)
+        log(f"[bench] cpu baseline: {out['cpu_baseline']}")
+        for c in workloads.CONFIGS if "configs" in out else ():
+            cb = cpu_baseline(c, min(args.cpu_seconds, 1.0))
+            out["configs"][c.name]["cpu_oracle"] = {"rows_per_s": cb["rows_per_s"], "GBs": cb["value"],
+                                                    "cores": cb["cores"]}
     print(json.dumps(out), flush=True)
 
 
