@@ -288,7 +288,10 @@ def kernel_time(r):
     return r["kernel_ms"], "HIP events around the K eager launches (no graph capture)"
 
 
-def prime_gpu(step, ms=300.0):
+PRIME_MS = 300.0
+
+
+def prime_gpu(step, ms=None):
     """Runs the workload's own launches (step(i), eagerly) for about `ms` before a
     measurement. After the host-side set-up of a workload (or the CPU baseline) the GPU
     has been idle, and its first milliseconds of work run slower (measured: C5 LayerNorm
@@ -297,6 +300,7 @@ def prime_gpu(step, ms=300.0):
     launches write only the workload's own output buffers."""
     import torch
 
+    ms = PRIME_MS if ms is None else min(ms, PRIME_MS)
     t0 = time.perf_counter()
     i = 0
     while (time.perf_counter() - t0) * 1e3 < ms:
@@ -306,7 +310,31 @@ def prime_gpu(step, ms=300.0):
         torch.cuda.synchronize()
 
 
+class line_marker:
+    """A roctx range (torch.cuda.nvtx) around one bench line, named "bench:<line>", so that a
+    rocprofv3 --marker-trace run can attribute each kernel dispatch to its line."""
+
+    def __init__(self, name):
+        self.name = name
+
+    def __enter__(self):
+        import torch
+
+        torch.cuda.nvtx.range_push(f"bench:{self.name}")
+
+    def __exit__(self, *exc):
+        import torch
+
+        torch.cuda.synchronize()
+        torch.cuda.nvtx.range_pop()
+
+
 def measure(w, steps, warmup, cache, dev, graph=True):
+    with line_marker(f"{w.name}:{cache}"):
+        return _measure(w, steps, warmup, cache, dev, graph)
+
+
+def _measure(w, steps, warmup, cache, dev, graph=True):
     import torch
 
     import row_wise_normalization_fp32_amd as rn
@@ -452,6 +480,11 @@ def probe_lib():
 
 
 def stream_ceiling(read_bytes, steps, dev, geom=None, prime_ms=100.0):
+    with line_marker(f"ceiling_{2 * read_bytes}"):
+        return _stream_ceiling(read_bytes, steps, dev, geom, prime_ms)
+
+
+def _stream_ceiling(read_bytes, steps, dev, geom=None, prime_ms=100.0):
     """Throughput of the hand-written streaming copy kernel (libstreamprobe.so) reading
     `read_bytes` and writing as many, under the same protocol as the workloads: buffer sets
     rotating over at least 1 GiB (cold L2 and memory-side cache), the kernel's own launches
@@ -467,8 +500,10 @@ def stream_ceiling(read_bytes, steps, dev, geom=None, prime_ms=100.0):
     nsets = max(MIN_COLD_SETS, math.ceil(COLD_FOOTPRINT / (2 * read_bytes)))
     src = [torch.randint(0, 1 << 15, (read_bytes // 2,), dtype=torch.int16, device=dev) for _ in range(nsets)]
     dst = [torch.zeros_like(a) for a in src]
+    touched = set()
 
     def step(i):
+        touched.add(i % nsets)
         # torch's current stream at the call: inside a graph capture it is the capturing stream
         stream = torch.cuda.current_stream(dev).cuda_stream
         st = lib.rn_probe_copy(src[i % nsets].data_ptr(), dst[i % nsets].data_ptr(), read_bytes,
@@ -480,7 +515,7 @@ def stream_ceiling(read_bytes, steps, dev, geom=None, prime_ms=100.0):
     prime_gpu(step, prime_ms)
     gt = graph_time_fn(step, steps)
     torch.cuda.synchronize()
-    assert all(torch.equal(a, b) for a, b in zip(src, dst)), "stream probe: copy is not exact"
+    assert all(torch.equal(src[i], dst[i]) for i in touched), "stream probe: copy is not exact"
     del src, dst
     torch.cuda.empty_cache()
     if gt is None:
@@ -511,6 +546,8 @@ def ceiling_sweep(steps, dev):
 
 
 def copy_calibration(dev):
+    """Copies of known size for scaling the HBM counters: 10 copies of 256 MiB by torch (the
+    HIP runtime's copy kernel), then 10 by the streaming copy kernel of libstreamprobe.so."""
     import torch
 
     n = 256 << 20
@@ -519,7 +556,12 @@ def copy_calibration(dev):
     for _ in range(10):
         dst.copy_(src)
     torch.cuda.synchronize()
-    log(f"[bench] copy calibration: 10 copies of {n} bytes")
+    lib = probe_lib()
+    for _ in range(10):
+        st = lib.rn_probe_copy(src.data_ptr(), dst.data_ptr(), n, 2, 512, 0, 1, torch.cuda.current_stream().cuda_stream)
+        assert st == 0, st
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: 10 + 10 copies of {n} bytes")
 
 
 def _more():
@@ -548,7 +590,7 @@ def _more():
 
 
 def main():
-    global MORE, MIN_REPLAY_MS
+    global MORE, MIN_REPLAY_MS, PRIME_MS
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -564,6 +606,8 @@ def main():
     ap.add_argument("--ceiling-sweep", action="store_true",
                     help="time every geometry of the streaming copy kernel at the ceiling sizes, print JSON, exit")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-copy ceiling lines")
+    ap.add_argument("--prime-ms", type=float, default=PRIME_MS,
+                    help="the workload's own launches before each line (shorter for counter runs)")
     ap.add_argument("--replay-ms", type=float, default=MIN_REPLAY_MS,
                     help="device time the timed graph replays of a line add up to (at least 5 replays)")
     args = ap.parse_args()
@@ -581,6 +625,7 @@ def main():
 
     MORE = _more()
     MIN_REPLAY_MS = args.replay_ms
+    PRIME_MS = args.prime_ms
     dev = "cuda:0"
     if args.copy_calibration:
         copy_calibration(dev)
@@ -741,6 +786,9 @@ def main():
             bx = x.get("bytes")
             if bx and x.get("graph_ms"):
                 x["graph_frac_of_ceiling"] = vs_ceiling(bx, x["graph_ms"])
+        for x in out.get("configs", {}).values():
+            if x.get("cold", {}).get("graph_ms"):
+                x["cold"]["graph_frac_of_ceiling"] = vs_ceiling(x["bytes_per_call"], x["cold"]["graph_ms"])
     # The CPU baseline last: the oracle on the host cores keeps the GPU idle for seconds,
     # so it runs after every GPU line instead of before the headline.
     if not args.no_cpu_baseline:

@@ -376,6 +376,8 @@ enum {
     FL_PARAMS_LDS = 16,  // stage gamma / beta / weight in LDS once per workgroup, not VGPRs
     FL_GAMMA_REG = 32,   // with FL_PARAMS_LDS and both parameters: gamma stays in VGPRs (loaded
                          // once per workgroup), only beta is staged in LDS (half the LDS)
+    FL_PREFETCH = 64,    // grid-stride loop: the next row's loads are issued before the current
+                         // row's reductions and stores (two rows of registers per lane)
 };
 
 template <int FL>
@@ -769,11 +771,16 @@ struct VecRow {
 // FL_PARAMS_LDS the workgroup first stages gamma / beta / weight in LDS, once, and all its
 // row groups read them from there for every row; the grid is then sized to the device's
 // resident capacity so that each workgroup handles many rows.
+//
+// FL_PREFETCH keeps two rows per row group in flight: row r + stride is loaded into a second
+// register set before row r is reduced and stored, and the two sets alternate (the loop is
+// unrolled by two so that no registers are copied).
 template <int DT, int OP, int W, int V, int RPB, bool EXACT, int AFF, int FL>
 __global__ __launch_bounds__(64 * W * RPB) void rownorm_vec_kernel(Params p) {
     using R = VecRow<DT, OP, W, V, EXACT, AFF, FL>;
     constexpr bool PLDS = (FL & FL_PARAMS_LDS) != 0 && (R::HG || R::HB);
     constexpr int PSRC = PLDS ? R::PARAMS_LDS : R::PARAMS_REG;
+    constexpr bool PF = (FL & FL_PREFETCH) != 0;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
     const int rg = wave / W;       // row slot of this wave in the workgroup
@@ -784,6 +791,10 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_vec_kernel(Params p) {
     extern __shared__ u32x4 prm[];  // PLDS: gamma chunks [C], then beta chunks [C]
     constexpr bool GREG = PLDS && (FL & FL_GAMMA_REG) != 0 && R::HG && R::HB;
     u32x4 gkeep[GREG ? V : 1];  // GREG: this lane's gamma chunks, for all rows
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * RPB;
+    int64_t base = static_cast<int64_t>(blockIdx.x) * RPB;
+    // Row registers: xa / ra hold the row being processed; with FL_PREFETCH, xb / rb the next.
+    u32x4 xa[V], ra[R::NR], xb[PF ? V : 1], rb[PF ? R::NR : 1];
     if constexpr (PLDS) {
         for (int c = threadIdx.x; c < Ci; c += 64 * W * RPB) {
             if constexpr (GREG) {
@@ -800,29 +811,63 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_vec_kernel(Params p) {
         __syncthreads();
     }
     int buf = 0;
-    for (int64_t base = static_cast<int64_t>(blockIdx.x) * RPB; base < p.rows;
-         base += static_cast<int64_t>(gridDim.x) * RPB) {
-        const int64_t row = base + rg;
-        if (row >= p.rows) {
-            if constexpr (W == 1) break;  // wave-uniform; no barrier in this variant
-            // a row group without a row still takes part in the workgroup barrier
-            __syncthreads();
-            buf ^= 1;
-            continue;
-        }
-        // Per-lane addresses are recomputed for every row (a few VALU operations) rather than
-        // hoisted out of the loop, where they would hold two VGPRs each for the whole kernel.
-        int tl = t;
-        asm volatile("" : "+v"(tl));
-        u32x4 xv[V], rv[R::NR], gv[R::NG], bv[R::NB];
-        R::load_row(p, row, tl, Ci, xv, rv);
-        if constexpr (PSRC == R::PARAMS_REG) R::load_params(p, tl, Ci, gv, bv);
-        if constexpr (GREG) {
+    if constexpr (!PF) {
+        for (; base < p.rows; base += stride) {
+            const int64_t row = base + rg;
+            if (row >= p.rows) {
+                if constexpr (W == 1) break;  // wave-uniform; no barrier in this variant
+                // a row group without a row still takes part in the workgroup barrier
+                __syncthreads();
+                buf ^= 1;
+                continue;
+            }
+            // Per-lane addresses are recomputed for every row (a few VALU operations) rather than
+            // hoisted out of the loop, where they would hold two VGPRs each for the whole kernel.
+            int tl = t;
+            asm volatile("" : "+v"(tl));
+            u32x4 gv[R::NG], bv[R::NB];
+            R::load_row(p, row, tl, Ci, xa, ra);
+            if constexpr (PSRC == R::PARAMS_REG) R::load_params(p, tl, Ci, gv, bv);
+            if constexpr (GREG) {
 #pragma unroll
-            for (int i = 0; i < V; ++i) gv[i] = gkeep[i];
+                for (int i = 0; i < V; ++i) gv[i] = gkeep[i];
+            }
+            __builtin_amdgcn_sched_barrier(0);  // every load of the row is issued before any use
+            R::template norm_row<PSRC>(p, row, lane, wr, tl, Ci, xa, ra, gv, bv, prm, part[rg], buf);
         }
-        __builtin_amdgcn_sched_barrier(0);  // every load of the row is issued before any use
-        R::template norm_row<PSRC>(p, row, lane, wr, tl, Ci, xv, rv, gv, bv, prm, part[rg], buf);
+    } else {
+        static_assert(PSRC == R::PARAMS_LDS || !(R::HG || R::HB), "the prefetching loop stages the parameters");
+        {
+            int tl = t;
+            asm volatile("" : "+v"(tl));
+            if (base + rg < p.rows) R::load_row(p, base + rg, tl, Ci, xa, ra);
+        }
+        // One row: its registers (xc, rc) are already loaded; the row one stride further is
+        // loaded into (xn, rn) first.
+        auto one = [&](int64_t row, u32x4(&xc)[V], u32x4(&rc)[R::NR], u32x4(&xn)[V], u32x4(&rn)[R::NR]) {
+            int tl = t;
+            asm volatile("" : "+v"(tl));
+            if (row + stride < p.rows) R::load_row(p, row + stride, tl, Ci, xn, rn);
+            u32x4 gv[R::NG], bv[R::NB];
+            if constexpr (GREG) {
+#pragma unroll
+                for (int i = 0; i < V; ++i) gv[i] = gkeep[i];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (row < p.rows) {
+                R::template norm_row<PSRC>(p, row, lane, wr, tl, Ci, xc, rc, gv, bv, prm, part[rg], buf);
+            } else if constexpr (W > 1) {
+                __syncthreads();  // a row group without a row still takes part in the barrier
+                buf ^= 1;
+            }
+        };
+        while (base < p.rows) {
+            one(base + rg, xa, ra, xb, rb);
+            base += stride;
+            if (base >= p.rows) break;
+            one(base + rg, xb, rb, xa, ra);
+            base += stride;
+        }
     }
 }
 
@@ -1809,21 +1854,115 @@ inline hipError_t go_persistent(const Plan& plan, const Params& p, hipStream_t s
                            static_cast<size_t>(plan.lds_bytes), stream);
 }
 
+// Persistent vectorized launches: parameters staged on chip, streaming accesses, and a grid
+// set by R = blocks / (CUs x resident workgroups per CU of the prefetching instance), where a
+// block is the RPB rows one workgroup takes at a time:
+//   R <= A: one workgroup per block, so that every row of the launch is in flight at once
+//           (A = 3/4 for the fused ops, which read two row tensors; just under 1 for the
+//           others, and 1 for 16-bit LayerNorm);
+//   R <= 3: half as many workgroups, each loading its second block while it reduces and
+//           stores the first (FL_PREFETCH);
+//   R >  3: one workgroup per block again (the hardware starts a workgroup whenever one ends,
+//           which keeps rows in flight without holding a second row in registers), except
+//           for rows of 4 or more waves with parameters, whose staged parameters are as large
+//           as the block or larger: two workgroups per CU loop over the rows without
+//           prefetching, staging the parameters once.
+// The thresholds come from a sweep on MI355X (cold cache, device time per launch of replayed
+// HIP graphs) over LayerNorm, RMSNorm, fused add + RMSNorm / LayerNorm and softmax, 256 to
+// 65536 rows of 1024 to 16384 elements, at grids of 1 to 8 workgroups per CU, half and full:
+// the rule is within 0.5% of the fastest measured grid on average (at most 5% off), where
+// the earlier fixed grid of two looping workgroups per CU was 6% off on average and up to
+// 29%. Examples against that grid: LayerNorm bf16 2048 x 4096 8.82 -> 7.63 us, 4096 x 4096
+// 14.14 -> 11.97 us, 32768 x 4096 89.75 -> 86.81 us; fused add + RMSNorm fp16 2048 x 4096
+// 13.74 -> 11.64 us, 32768 x 4096 184.1 -> 174.2 us; RMSNorm fp16 2048 x 4096 8.01 -> 6.96
+// us; fused add + LayerNorm bf16 32768 x 4096 184.8 -> 171.8 us; softmax fp32 32768 x 4096
+// 182.1 -> 169.9 us; LayerNorm bf16 4096 x 16384 unchanged at 46.3 us.
+struct GridRule {
+    bool two_tensors;  // fused ops: x and the residual
+    bool ln16;         // LayerNorm of 16-bit rows
+    bool loop_wide;    // 4 or more waves per row, with parameters
+};
+
+template <auto PF_KERNEL>
+inline hipError_t persistent_grid(const Plan& plan, const GridRule& rule, int* grid_out, bool* loop_out) {
+    int cus = 0, per_cu = 0;
+    hipError_t e = resident<PF_KERNEL>(plan.block_threads, plan.lds_bytes, &cus, &per_cu);
+    if (e != hipSuccess) return e;
+    const int64_t blocks = plan.grid;
+    const int64_t res = static_cast<int64_t>(cus) * per_cu;  // resident workgroups
+    const bool one_round = rule.two_tensors ? 4 * blocks <= 3 * res : (rule.ln16 ? blocks <= res : blocks < res);
+    int64_t grid = blocks;
+    bool loop = false;
+    if (!one_round) {
+        if (blocks <= 3 * res) {
+            grid = (blocks + 1) / 2;
+        } else {
+            loop = rule.loop_wide;
+        }
+    }
+    if (grid > kMaxGrid) grid = kMaxGrid;
+    *grid_out = static_cast<int>(grid);
+    *loop_out = loop;
+    return hipSuccess;
+}
+
+template <auto KERNEL>
+inline hipError_t launch_grid(const Plan& plan, const Params& p, hipStream_t stream, int64_t grid) {
+    Params args = p;
+    void* argv[] = {&args};
+    return hipLaunchKernel(reinterpret_cast<const void*>(KERNEL), dim3(static_cast<unsigned>(grid)),
+                           dim3(static_cast<unsigned>(plan.block_threads)), argv,
+                           static_cast<size_t>(plan.lds_bytes), stream);
+}
+
+// One vectorized launch: persistent (the prefetching instance, or the looping one for wide
+// rows with parameters when R > 3) or grid per row.
+template <int DT, int OP, int W, int V, bool EXACT, int AFF, bool PERS>
+inline hipError_t go_v(const Plan& plan, const Params& p, hipStream_t s) {
+    constexpr int RPB = rows_per_block_for(W);
+    if constexpr (PERS) {
+        constexpr int FL = persistent_flags<OP, AFF>();
+        // 1024-lane workgroups have no registers for a second row, nor have one-wave rows of 8
+        // or more chunks per lane (reached only by forcing the wave variant): they loop
+        // without prefetching, as do wide rows with parameters when R > 2.
+        constexpr bool NOPF = W >= 16 || (W == 1 && V >= 8);
+        constexpr bool WIDE_PARAMS = W >= 4 && AFF != 0 && !OpTraits<OP>::SM;
+        if constexpr (NOPF) {
+            return go_persistent<rownorm_vec_kernel<DT, OP, W, V, RPB, EXACT, AFF, FL>>(plan, p, s);
+        } else {
+            constexpr auto PFK = rownorm_vec_kernel<DT, OP, W, V, RPB, EXACT, AFF, FL | FL_PREFETCH>;
+            constexpr GridRule rule{OpTraits<OP>::RES, OP == OP_LN && DT != DT_F32, WIDE_PARAMS};
+            int grid = 0;
+            bool loop = false;
+            hipError_t e = persistent_grid<PFK>(plan, rule, &grid, &loop);
+            if (e != hipSuccess) return e;
+            if constexpr (WIDE_PARAMS) {
+                if (loop) return go_persistent<rownorm_vec_kernel<DT, OP, W, V, RPB, EXACT, AFF, FL>>(plan, p, s);
+            }
+            return launch_grid<PFK>(plan, p, s, grid);
+        }
+    } else {
+        // 1024-lane workgroups have 128 VGPRs per lane: LayerNorm rows there keep no fp32 copy.
+        constexpr int FL = W >= 16 && OpTraits<OP>::LN ? FL_NOFLOAT : 0;
+        return go(rownorm_vec_kernel<DT, OP, W, V, RPB, EXACT, AFF, FL>, plan, p, s);
+    }
+}
+
 template <int DT, int OP, int W, bool EXACT, int AFF, bool PERS>
 inline hipError_t launch_v(const Plan& plan, const Params& p, hipStream_t s) {
     constexpr int RPB = rows_per_block_for(W);
-    // 1024-lane workgroups have 128 VGPRs per lane: LayerNorm rows there keep no fp32 copy.
-    constexpr int FL = PERS ? persistent_flags<OP, AFF>() : (W >= 16 && OpTraits<OP>::LN ? FL_NOFLOAT : 0);
     if (plan.rows_per_block != RPB) return hipErrorInvalidValue;
-#define RN_GO(VV) \
-    (PERS ? go_persistent<rownorm_vec_kernel<DT, OP, W, VV, RPB, EXACT, AFF, FL>>(plan, p, s) \
-          : go(rownorm_vec_kernel<DT, OP, W, VV, RPB, EXACT, AFF, FL>, plan, p, s))
-    switch (plan.chunks_per_lane) {
-    case 1: return RN_GO(1);
-    case 2: return RN_GO(2);
-    case 4: return RN_GO(4);
-    default: break;
+#define RN_GO(VV) go_v<DT, OP, W, VV, EXACT, AFF, PERS>(plan, p, s)
+    // The planner gives rows of 8 and 16 waves 4 chunks per lane (or 8 / 16 for the one-
+    // workgroup rows below); fewer chunks per lane occur only with 1, 2 and 4 waves.
+    if constexpr (W <= 4) {
+        switch (plan.chunks_per_lane) {
+        case 1: return RN_GO(1);
+        case 2: return RN_GO(2);
+        default: break;
+        }
     }
+    if (plan.chunks_per_lane == 4) return RN_GO(4);
     if constexpr (W == 1) {
         switch (plan.chunks_per_lane) {
         case 8: return RN_GO(8);
