@@ -253,18 +253,23 @@ int fused_add_rms_norm_variant(const void* x, const void* residual, const void* 
  * Rows of up to 16384 elements are held by one row group. Longer rows (any N) are split
  * into 8192-element segments (plan variant RN_VARIANT_WIDE). For fp32 rows and rows of
  * whole 16-byte groups, with a 16-byte aligned workspace and up to (workgroups the device
- * keeps resident) / 2 segments per row, x and dy are read once: a small launch clears a
- * ticket counter and the segment records in the workspace, then workgroups take (row
- * block, segment) tickets in order, publish each
- * row's per-segment sums of g and g * xhat in the workspace, wait for the row's other
- * segments (only ever for tickets taken before or with their own, so the wait cannot
- * depend on a workgroup that is not running) and write dx; the column sums follow. A wait
- * is bounded (about a second): should other work keep the device's compute units away for
- * that long, the affected rows' dx and the parameter gradients of their columns come out
- * NaN rather than the call hanging. Otherwise three launches: per-segment sums into the
- * workspace, dx with the parameter-gradient columns, column sums (x and dy read twice).
- * Row and column sums are formed in fp32 in a fixed order (no floating-point atomics):
- * results are bitwise reproducible on a given device.
+ * keeps resident) / 2 segments per row (at most 256), x and dy are read once: a small launch
+ * clears a ticket counter and the segment records in the workspace, then workgroups take
+ * (row block, segment) tickets in order (an integer atomic counter), publish each row's
+ * per-segment sums of g and g * xhat in the workspace (64-bit atomic stores of tagged
+ * words), wait for the row's other segments and write dx; the column sums follow. The wait
+ * never fails and never depends on other workgroups being scheduled: after a bounded number
+ * of polls (4096, about 5-10 ms; the environment variable RN_BWD_WAIT_POLLS, read at every
+ * call, overrides it) the waiting workgroup computes a missing segment's sums itself, from
+ * that segment's x, dy and gamma, with the same lanes and order as the segment's own
+ * workgroup, so the result has the same bits either way. The number of records computed
+ * that way is left in the workspace as a diagnostic: the 32-bit word at byte offset
+ * rn_backward_workspace_bytes(op, rows, N) - 16 * rows * S - 252, S = ceil(N / 8192)
+ * segments per row (zero when the segments of each row run side by side). Otherwise three
+ * launches: per-segment sums into the workspace, dx with the parameter-gradient columns,
+ * column sums (x and dy read twice).
+ * Row and column sums are formed in fp32 in a fixed order; no floating-point value is ever
+ * accumulated with an atomic, so results are bitwise reproducible on a given device.
  */
 size_t rn_backward_workspace_bytes(int op, int64_t rows, int64_t N);
 int ln_backward(const void* dy, const void* x, const void* gamma, const float* mean, const float* rstd, void* dx,

@@ -21,8 +21,11 @@
 //      parameter to the workspace: [2][P][N].
 //   2. rownorm_bwd_cols_kernel sums the P partial rows of each column in a fixed order and
 //      rounds to the I/O dtype.
-// No atomics: results are bitwise reproducible for a given P (P depends on the device's CU
-// count only).
+// Results are bitwise reproducible for a given P: every floating-point sum is formed in a
+// fixed order, and none is accumulated with an atomic. P depends on the device's CU count
+// and the kernels' occupancy (and, for split rows, on the segments per row). The one-pass
+// split-row kernel below uses integer atomics only to hand out work (a ticket counter) and
+// to publish its per-segment sums (tagged 64-bit words read in a fixed order).
 #pragma once
 
 #include <map>
@@ -559,15 +562,16 @@ __global__ __launch_bounds__(kBwdSegLanes) void rownorm_bwd_wide_dx_kernel(BwdPa
 //     adds them in a fixed order (the same bits in every workgroup of the row), and writes
 //     dx for its segment, accumulating its columns' dgamma / dbeta terms in registers;
 // then writes its columns of partial row `block` ([2][P][N], as the column kernel reads).
-// Progress does not depend on which workgroups are resident: a workgroup waits only for
-// the S - 1 other tickets of its block, which were or will be taken before any later
-// ticket. If the lowest unfinished block still has tickets nobody holds, fewer than S
-// workgroups hold tickets of it and no workgroup holds a later one, so with a grid of at
-// least S workgroups (the host's condition) some workgroup is free to take the next
-// ticket. The wait is bounded all the same (kBwdSpinLimit polls, about a second): past it
-// the workgroup sets the time-out flag and makes its rows' dx and parameter partials NaN.
-// The counter, flag and records are zeroed by rownorm_bwd_wide_clear_kernel before each
-// launch (a kernel, not a memset, so that the call can be captured in a graph).
+// Progress does not depend on which workgroups are resident or how many: the wait for a
+// record is bounded (p.wait_polls polls), and a record still missing after it is computed by
+// the waiting workgroup itself, from that segment's x, dy and gamma, with the same lanes,
+// element positions and reduction order as its owner uses, so the sums have the same bits
+// whichever workgroup computes them (it also publishes them, which is harmless: the owner
+// stores the same words). A workgroup therefore never waits on another to be scheduled,
+// and no result depends on timing. The count of records computed this way is added to
+// sync[1] (a diagnostic; it is zero when the segments of a row run side by side).
+// The counter, the count and the records are zeroed by rownorm_bwd_wide_clear_kernel before
+// each launch (a kernel, not a memset, so that the call can be captured in a graph).
 // ---------------------------------------------------------------------------------------
 
 template <int DT>  // one instance per dtype's translation unit
@@ -607,6 +611,18 @@ struct SegRaw {
     }
 };
 
+// One element's terms of a segment record: g = dy * gamma (or dy), g * xhat. The record's
+// owner and a workgroup that computes it in its place both go through this, in the same
+// element order, so the sums have the same bits.
+template <bool LN, bool HG>
+__device__ __forceinline__ void record_terms(float x, float d, float gm, float mean, float rstd, float& sg,
+                                             float& sgx) {
+    const float xh = LN ? (x - mean) * rstd : x * rstd;
+    const float g = HG ? d * gm : d;
+    sg += g;
+    sgx = fmaf(g, xh, sgx);
+}
+
 template <int DT, int OP, bool HG, bool VEC>
 __global__ __launch_bounds__(kBwdSegLanes) void rownorm_bwd_wide_onepass_kernel(BwdParams p) {
     using SG = BwdSeg<DT>;
@@ -617,12 +633,18 @@ __global__ __launch_bounds__(kBwdSegLanes) void rownorm_bwd_wide_onepass_kernel(
     const int wr = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int t = threadIdx.x;
     __shared__ WavePart part[2][kBwdSegLanes / 64];
-    __shared__ float rowsum[2];
-    __shared__ int row_bad;
+    // per row, double-buffered by row parity: one barrier separates a row's reads from the
+    // writes of the row after the next
+    __shared__ float rowsum[2][2];  // [parity][sum g, sum g * xhat] of the whole row
+    __shared__ int s_need[2];       // [parity] some record of the row is computed here
+    __shared__ unsigned char s_miss[kBwdOnePassMaxSeg];  // records to compute here
+    __shared__ float s_rec[2][kBwdOnePassMaxSeg];        // the row's records (sum g, sum g * xhat)
     __shared__ unsigned s_ticket;
     // the columns' dgamma (and dbeta) terms, slot k of lane t at [k][t]: each lane owns its
     // slots, so they need no barrier; in LDS, not VGPRs, so that two workgroups fit a CU
     __shared__ float acc_s[LN ? 2 : 1][V][kBwdSegLanes];
+    constexpr int POLLER = kBwdSegLanes / 64 - 1;  // the wave that waits for the records
+    constexpr int RPL = kBwdOnePassMaxSeg / 64;      // records per lane of that wave
     int buf = 0;
     const int S = p.S;
     const unsigned total = static_cast<unsigned>(p.parts) * static_cast<unsigned>(S);
@@ -646,26 +668,73 @@ __global__ __launch_bounds__(kBwdSegLanes) void rownorm_bwd_wide_onepass_kernel(
             acc_s[0][k][t] = 0.f;
             if constexpr (LN) acc_s[LN ? 1 : 0][k][t] = 0.f;
         }
-        // the segment's sums of one row, published as the row's record `seg`
-        auto post = [&](int64_t row, const RW& x, const RW& d) {
+        // the sums g and g * xhat of this workgroup's segment of one row, from registers;
+        // every wave takes part (one barrier)
+        auto seg_sums = [&](int64_t row, const RW& x, const RW& d, float& Sg, float& Sgx) {
             const float mean = LN ? p.mean[row] : 0.f;
             const float rstd = p.rstd[row];
             float sg = 0.f, sgx = 0.f;
 #pragma unroll
-            for (int k = 0; k < V; ++k) {
-                const float xh = LN ? (x[k] - mean) * rstd : x[k] * rstd;
-                const float g = HG ? d[k] * gr[k] : d[k];
-                sg += g;
-                sgx = fmaf(g, xh, sgx);
-            }
-            float Sg = wave_sum(sg), Sgx = wave_sum(sgx);
+            for (int k = 0; k < V; ++k) record_terms<LN, HG>(x[k], d[k], HG ? gr[k] : 1.f, mean, rstd, sg, sgx);
+            Sg = wave_sum(sg);
+            Sgx = wave_sum(sgx);
             group_sum2<kBwdSegLanes / 64>(part, buf, lane, wr, Sg, Sgx);
+        };
+        // the same sums for another segment s2 of the row, read from memory one 16-byte group
+        // (or element) per tensor at a time: the lanes and element order of seg_sums, and few
+        // registers, since the rows in flight stay live around it
+        auto other_seg_sums = [&](int64_t row, int s2, float& Sg, float& Sgx) {
+            const int64_t e2 = static_cast<int64_t>(s2) * kBwdSeg;
+            const uint32_t nb2 = static_cast<uint32_t>((p.N - e2 < kBwdSeg ? p.N - e2 : kBwdSeg) * SG::SB);
+            const Rsrc rx = make_rsrc(static_cast<const char*>(p.x) + (row * p.N + e2) * SG::SB, nb2);
+            const Rsrc rd = make_rsrc(static_cast<const char*>(p.dy) + (row * p.N + e2) * SG::SB, nb2);
+            const Rsrc rg = make_rsrc(HG ? static_cast<const char*>(p.gamma) + e2 * SG::SB : nullptr, HG ? nb2 : 0u);
+            const float mean = LN ? p.mean[row] : 0.f;
+            const float rstd = p.rstd[row];
+            float sg = 0.f, sgx = 0.f;
+            if constexpr (VEC) {
+                using IO = Io<DT>;
+#pragma unroll 1
+                for (int i = 0; i < V / RW::G; ++i) {
+                    const int off = (i * kBwdSegLanes + t) * 16;
+                    const u32x4 xv = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+                    const u32x4 dv = __builtin_amdgcn_raw_buffer_load_b128(rd, off, 0, 0);
+                    u32x4 gv = u32x4{0u, 0u, 0u, 0u};
+                    if constexpr (HG) gv = __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0);
+#pragma unroll
+                    for (int e = 0; e < RW::G; ++e)
+                        record_terms<LN, HG>(IO::elem(xv, e), IO::elem(dv, e), HG ? IO::elem(gv, e) : 1.f, mean, rstd,
+                                             sg, sgx);
+                    asm volatile("" ::: "memory");  // one group per tensor in flight
+                }
+            } else {
+                using IO = Io<DT>;
+#pragma unroll 1
+                for (int k = 0; k < V; ++k) {
+                    const uint32_t j = static_cast<uint32_t>(k * kBwdSegLanes + t);
+                    const float xk = IO::bload(rx, j), dk = IO::bload(rd, j);
+                    const float gk = HG ? IO::bload(rg, j) : 1.f;
+                    record_terms<LN, HG>(xk, dk, gk, mean, rstd, sg, sgx);
+                    asm volatile("" ::: "memory");
+                }
+            }
+            Sg = wave_sum(sg);
+            Sgx = wave_sum(sgx);
+            group_sum2<kBwdSegLanes / 64>(part, buf, lane, wr, Sg, Sgx);
+        };
+        auto publish = [&](int64_t row, int sgm, float Sg, float Sgx) {
             if (t == 0) {
-                unsigned long long* rec = p.rec64 + 2 * (row * S + seg);
+                unsigned long long* rec = p.rec64 + 2 * (row * S + sgm);
                 const unsigned long long tag = 1ull << 32;
                 __hip_atomic_store(rec, tag | bit_cast<unsigned>(Sg), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(rec + 1, tag | bit_cast<unsigned>(Sgx), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
+        };
+        // this workgroup's segment of one row, published as the row's record `seg`
+        auto post = [&](int64_t row, const RW& x, const RW& d) {
+            float Sg, Sgx;
+            seg_sums(row, x, d, Sg, Sgx);
+            publish(row, seg, Sg, Sgx);
         };
         const int64_t r0 = blk * p.R;
         const int64_t r1 = r0 + p.R < p.rows ? r0 + p.R : p.rows;
@@ -679,58 +748,93 @@ __global__ __launch_bounds__(kBwdSegLanes) void rownorm_bwd_wide_onepass_kernel(
             nd.template load<kNonTemporal>(db + (r0 + 1) * rowbytes, nb, t);
         }
         post(r0, cx, cd);
-        bool timed_out = false;
         for (int64_t row = r0; row < r1; ++row) {
+            const int par = static_cast<int>(row & 1);
             RW mx, md;
             if (row + 2 < r1) {
                 mx.template load<kNonTemporal>(xb + (row + 2) * rowbytes, nb, t);
                 md.template load<kNonTemporal>(db + (row + 2) * rowbytes, nb, t);
             }
             if (row + 1 < r1) post(row + 1, nx, nd);
-            // the last wave polls: not wave 0, whose lane 0 has just stored the record (vector
+            // The last wave polls: not wave 0, whose lane 0 has just stored the record (vector
             // memory counts retire in order, so its poll would also wait for those stores;
-            // LayerNorm bf16 1024 x 65536: 123.9 -> 120.5 us)
-            if (wr == kBwdSegLanes / 64 - 1) {
-                // lane k adds records k, k + 64, ... in order, then a butterfly whose every
-                // step adds two equal operand pairs: the same bits in every workgroup
-                const unsigned long long* rec = p.rec64 + 2 * row * S;
+            // LayerNorm bf16 1024 x 65536: 123.9 -> 120.5 us). Lane l holds records l, l + 64,
+            // ...; they are added in that order, then a butterfly whose every step adds two
+            // equal operand pairs: the same bits in every workgroup of the row.
+            // The records go to LDS (s_rec), whoever computed them; the poller adds them from
+            // there.
+            unsigned miss = 0;
+            auto finish = [&]() {
                 float a = 0.f, b = 0.f;
-                bool bad = false;
-                for (int k = lane; k < S; k += 64) {
-                    unsigned long long w0 = 0, w1 = 0;
-                    for (int n = 0;; ++n) {
-                        w0 = __hip_atomic_load(rec + 2 * k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        w1 = __hip_atomic_load(rec + 2 * k + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        if ((w0 >> 32) != 0 && (w1 >> 32) != 0) break;
-                        if (n >= kBwdSpinLimit) {
-                            bad = true;
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(8);
+#pragma unroll
+                for (int j = 0; j < RPL; ++j) {
+                    if (lane + 64 * j < S) {
+                        a += s_rec[0][lane + 64 * j];
+                        b += s_rec[1][lane + 64 * j];
                     }
-                    a += bit_cast<float>(static_cast<unsigned>(w0));
-                    b += bit_cast<float>(static_cast<unsigned>(w1));
                 }
 #pragma unroll
                 for (int step = 1; step < 64; step <<= 1) {
                     a += __shfl_xor(a, step);
                     b += __shfl_xor(b, step);
                 }
-                const bool any_bad = __any(bad);  // all 64 lanes active here
-                if (any_bad) {
-                    a = b = __builtin_nanf("");
-                    if (lane == 0) __hip_atomic_store(p.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
                 if (lane == 0) {
-                    rowsum[0] = a;
-                    rowsum[1] = b;
-                    row_bad = any_bad ? 1 : 0;
+                    rowsum[par][0] = a;
+                    rowsum[par][1] = b;
                 }
+            };
+            if (wr == POLLER) {
+                const unsigned long long* rec = p.rec64 + 2 * row * S;
+#pragma unroll
+                for (int j = 0; j < RPL; ++j) {
+                    const int k = lane + 64 * j;
+                    if (k < S) {
+                        bool got = false;
+                        for (int n = 0;; ++n) {
+                            const unsigned long long w0 = __hip_atomic_load(rec + 2 * k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            const unsigned long long w1 = __hip_atomic_load(rec + 2 * k + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            if ((w0 >> 32) != 0 && (w1 >> 32) != 0) {
+                                s_rec[0][k] = bit_cast<float>(static_cast<unsigned>(w0));
+                                s_rec[1][k] = bit_cast<float>(static_cast<unsigned>(w1));
+                                got = true;
+                                break;
+                            }
+                            if (n >= p.wait_polls) break;
+                            __builtin_amdgcn_s_sleep(8);
+                        }
+                        if (!got) miss |= 1u << j;
+                        s_miss[k] = got ? 0 : 1;
+                    }
+                }
+                const bool any = __any(miss != 0);  // all 64 lanes active here
+                if (!any) finish();
+                if (lane == 0) s_need[par] = any ? 1 : 0;
             }
             __syncthreads();
-            const float c1 = LN ? rowsum[0] * p.inv_n : 0.f;
-            const float c2 = rowsum[1] * p.inv_n;
-            timed_out = timed_out || row_bad != 0;
+            if (s_need[par] != 0) {  // uniform: compute the missing records here
+                int computed = 0;
+                for (int s2 = 0; s2 < S; ++s2) {
+                    if (s_miss[s2] == 0) continue;  // uniform
+                    float Sg, Sgx;
+                    other_seg_sums(row, s2, Sg, Sgx);
+                    publish(row, s2, Sg, Sgx);
+                    if (t == 0) {
+                        s_rec[0][s2] = Sg;
+                        s_rec[1][s2] = Sgx;
+                    }
+                    ++computed;
+                }
+                __syncthreads();
+                if (wr == POLLER) {
+                    finish();
+                    if (lane == 0)
+                        __hip_atomic_fetch_add(p.sync + 1, static_cast<unsigned>(computed), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+                }
+                __syncthreads();
+            }
+            const float c1 = LN ? rowsum[par][0] * p.inv_n : 0.f;
+            const float c2 = rowsum[par][1] * p.inv_n;
             const float mean = LN ? p.mean[row] : 0.f;
             const float rstd = p.rstd[row];
             float r[V];
@@ -752,8 +856,8 @@ __global__ __launch_bounds__(kBwdSegLanes) void rownorm_bwd_wide_onepass_kernel(
         float adg[V], adb[LN ? V : 1];
 #pragma unroll
         for (int k = 0; k < V; ++k) {
-            adg[k] = timed_out ? __builtin_nanf("") : acc_s[0][k][t];
-            if constexpr (LN) adb[k] = timed_out ? __builtin_nanf("") : acc_s[LN ? 1 : 0][k][t];
+            adg[k] = acc_s[0][k][t];
+            if constexpr (LN) adb[k] = acc_s[LN ? 1 : 0][k][t];
         }
         SG::store_f32(p.ws + blk * p.N + e0, static_cast<uint32_t>(Ns), VEC, t, adg);
         if constexpr (LN)
@@ -868,7 +972,14 @@ inline hipError_t launch_bwd_wide(int op, const Plan& plan, const BwdParams& p0,
 #define RN_B1(VV)                                                                                                  \
     (ln ? (hg ? rownorm_bwd_wide_onepass_kernel<DT, OP_LN, true, VV> : rownorm_bwd_wide_onepass_kernel<DT, OP_LN, false, VV>) \
         : (hg ? rownorm_bwd_wide_onepass_kernel<DT, OP_RMS, true, VV> : rownorm_bwd_wide_onepass_kernel<DT, OP_RMS, false, VV>))
-    const BwdKernel k1 = p.vec ? RN_B1(true) : RN_B1(false);
+    // 16-bit rows that are not whole 16-byte groups take three launches (below): their
+    // element-layout one-pass instances are not built
+    BwdKernel k1 = nullptr;
+    if constexpr (DT == DT_F32) {
+        k1 = p.vec ? RN_B1(true) : RN_B1(false);
+    } else {
+        k1 = p.vec ? RN_B1(true) : nullptr;
+    }
 #undef RN_B1
     if (p.S < 1 || p.rec == nullptr) return hipErrorInvalidValue;
     int dev = 0;
@@ -876,20 +987,25 @@ inline hipError_t launch_bwd_wide(int op, const Plan& plan, const BwdParams& p0,
     if (e != hipSuccess) return e;
     int per_cu = 0, cus = 0;
     void* argv[] = {&p};
-    e = bwd_resident(k1, dev, plan, &per_cu, &cus);
-    if (e != hipSuccess) return e;
-    const int64_t resident = static_cast<int64_t>(cus) * per_cu;
+    int64_t resident = 0;
+    if (k1 != nullptr) {
+        e = bwd_resident(k1, dev, plan, &per_cu, &cus);
+        if (e != hipSuccess) return e;
+        resident = static_cast<int64_t>(cus) * per_cu;
+    }
     // 16-bit rows that are not whole 16-byte groups (two-byte loads, one workgroup per CU)
     // measured faster in three launches (bf16 1024 x 65537: 154 us against 192 us one-pass;
     // fp32 1024 x 65537: 274 against 240, bf16 1024 x 65536 in 16-byte groups: 143 against 116)
     const bool onepass_rows = p.vec != 0 || DT == DT_F32;
-    if (onepass_rows && p.sync != nullptr && p.rec64 != nullptr && resident >= 2 * static_cast<int64_t>(p.S)) {
+    if (onepass_rows && k1 != nullptr && p.sync != nullptr && p.rec64 != nullptr &&
+        resident >= 2 * static_cast<int64_t>(p.S) && p.S <= kBwdOnePassMaxSeg) {
         int64_t P = resident / p.S;
         if (P > plan.grid) P = plan.grid;
         const int64_t R = (p.rows + P - 1) / P;
         P = (p.rows + R - 1) / R;
         const int64_t tickets = P * p.S;
-        // counter, flag and records: 256 + rows * S * 16 bytes from p.sync
+        // counter, count of locally computed records, and the records: 256 + rows * S * 16
+        // bytes from p.sync
         const int64_t n16 = (256 + p.rows * p.S * 16) / 16;
         int64_t gc = (n16 + 255) / 256;
         if (gc > 1024) gc = 1024;

@@ -10,6 +10,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "../../include/rownorm.h"
 #include "rownorm_internal.h"
@@ -425,6 +426,19 @@ int64_t bwd_parts_cap(int64_t rows) { return rows < rn::kBwdMaxParts ? rows : rn
 // split-row backward.
 constexpr int64_t kBwdRowCap = int64_t(64) * rn::kMaxGroupWaves * rn::kElemMaxPerLane;
 bool bwd_wide(int64_t N) { return N > kBwdRowCap; }
+
+// Polls of a missing segment record before the one-pass split-row backward computes it in the
+// waiting workgroup: rn::kBwdWaitPolls, or RN_BWD_WAIT_POLLS from the environment (a
+// non-negative integer; 0 computes every other segment's sums locally, which tests use to
+// check that both ways give the same bits). Read at every call.
+int bwd_wait_polls() {
+    const char* v = getenv("RN_BWD_WAIT_POLLS");
+    if (v == nullptr || *v == '\0') return rn::kBwdWaitPolls;
+    char* end = nullptr;
+    const long n = strtol(v, &end, 10);
+    if (end == v || *end != '\0' || n < 0 || n > (1L << 30)) return rn::kBwdWaitPolls;
+    return static_cast<int>(n);
+}
 int64_t bwd_wide_segments(int64_t N) { return (N + rn::kBwdSeg - 1) / rn::kBwdSeg; }
 // Split rows: workgroups per segment (partial rows) at most.
 int64_t bwd_wide_q_cap(int64_t rows, int64_t N) {
@@ -443,7 +457,8 @@ size_t bwd_records_offset(int op, int64_t rows, int64_t N) {
     return (bwd_partial_bytes(op, rows, N) + 255) / 256 * 256;
 }
 
-// Split rows, from the records offset: a 256-byte header (ticket counter, time-out flag),
+// Split rows, from the records offset: a 256-byte header (ticket counter, count of records
+// computed by a waiting workgroup),
 // then 16 bytes per (row, segment) record (two 64-bit words; the two-pass kernels use the
 // first 8 bytes per record of the same space).
 size_t bwd_workspace_bytes(int op, int64_t rows, int64_t N) {
@@ -584,6 +599,7 @@ int run_bwd(BwdArgs a, hipStream_t stream) {
     p.sync = nullptr;
     p.rec64 = nullptr;
     p.R = 0;
+    p.wait_polls = bwd_wait_polls();
     if (plan.variant == rn::V_WIDE) {
         char* recs = static_cast<char*>(a.ws) + bwd_records_offset(a.op, a.rows, a.N);
         p.rec = reinterpret_cast<float*>(recs);

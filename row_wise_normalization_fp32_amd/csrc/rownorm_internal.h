@@ -58,11 +58,13 @@ struct BwdParams {
     float* rec;         // [rows][S] records of two floats: the segment's sum g and sum g * xhat
     int S;              // segments per row
     int vec;            // rows, tensors and segments are whole 16-byte groups
-    // one-pass split rows: [0] ticket counter, [1] wait time-out flag (zeroed before launch);
-    // records of two 64-bit words (tag << 32 | fp32 bits) per (row, segment)
+    // one-pass split rows: [0] ticket counter, [1] count of records a waiting workgroup
+    // computed itself (zeroed before launch); records of two 64-bit words
+    // (tag << 32 | fp32 bits) per (row, segment)
     unsigned* sync;
     unsigned long long* rec64;
     int R;              // rows per row block (one ticket = one block of one segment)
+    int wait_polls;     // polls of a missing record before the waiting workgroup computes it
 };
 
 // Backward column-sum kernel arguments.
@@ -114,7 +116,9 @@ constexpr int kBwdSegLanes = 512;      // backward split rows: 512 lanes ...
 constexpr int kBwdSegPerLane = 16;     // ... of 16 elements: 8192-element segments
 constexpr int kBwdSeg = kBwdSegLanes * kBwdSegPerLane;
 constexpr int kBwdWideMaxGroups = 2048;  // backward split rows: at most this many segment workgroups
-constexpr int kBwdSpinLimit = 1 << 20;   // one-pass split rows: polls of a row's records before giving up
+constexpr int kBwdWaitPolls = 1 << 12;   // one-pass split rows: polls of a missing record (about 1-2 us
+                                         // each) before the waiting workgroup computes it itself
+constexpr int kBwdOnePassMaxSeg = 256;   // one-pass split rows: at most this many segments per row
 constexpr int kBwdTargetChunks = 2;    // backward: about 2 chunks of x and of dy per lane (1 measured slower)
 
 // Enqueue the planned kernel for one I/O dtype (one translation unit per dtype and mode).

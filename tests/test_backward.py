@@ -174,8 +174,9 @@ def test_backward_split_rows_one_and_two_pass_agree(dtype, N):
 def test_backward_split_rows_workspace_contents_do_not_matter():
     # the one-pass launch takes tickets from a counter and polls records in the workspace;
     # both are cleared by the call itself: a workspace full of ones (every record "ready")
-    # gives the same bits as a fresh one, and the wait time-out flag (the second 32-bit word
-    # of the 256-byte header in front of the rows x S 16-byte records) stays clear
+    # gives the same bits as a fresh one, and the count of records computed by waiting
+    # workgroups (the second 32-bit word of the 256-byte header in front of the rows x S
+    # 16-byte records) starts from zero
     rows, N = 256, 65536
     w = workloads.LN_BWD.scaled(rows=rows, N=N, seed=1341, dtype="bf16")
     inp = workloads.make_inputs(w)
@@ -191,7 +192,56 @@ def test_backward_split_rows_workspace_contents_do_not_matter():
         torch.cuda.synchronize()
         for a, b in zip(ref, outs):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
-        assert int(ws[header + 4:header + 8].view(torch.int32).item()) == 0
+        assert 0 <= int(ws[header + 4:header + 8].view(torch.int32).item()) <= rows * (N // 8192)
+
+
+@pytest.mark.parametrize("op,dtype,rows,N,gamma", [("ln", "bf16", 96, 65536, True), ("ln", "fp32", 40, 40001, True),
+                                                   ("rms", "fp16", 64, 32768, True), ("ln", "fp16", 48, 24576, False),
+                                                   ("rms", "bf16", 33, 16392, False)])
+def test_backward_split_rows_records_computed_by_the_waiting_workgroup(monkeypatch, op, dtype, rows, N, gamma):
+    # RN_BWD_WAIT_POLLS=0: a workgroup polls each record of a row once and computes every
+    # record not yet published itself, from that segment's x, dy and gamma. It uses the
+    # lanes and the order of the segment's own workgroup, so dx, dgamma and dbeta have the
+    # same bits as with the normal wait; the diagnostic count in the workspace header shows
+    # that records were computed that way. Every kernel still ends normally: nothing waits
+    # for a workgroup that is not running.
+    base = workloads.LN_BWD if op == "ln" else workloads.RMS_BWD
+    w = base.scaled(rows=rows, N=N, seed=1370 + rows, dtype=dtype, with_gamma=gamma)
+    inp = workloads.make_inputs(w)
+    mean, rstd = _stats(w, inp)
+    dev = {k: v.to(DEV) for k, v in inp.items()}
+    r = torch.from_numpy(rstd).to(DEV)
+    g = dev.get("gamma", dev.get("weight"))
+    need = rn.backward_workspace_bytes(op, rows, N)
+    S = -(-N // 8192)
+    header = need - (256 + rows * S * 16)
+
+    def call(ws):
+        if op == "ln":
+            out = rn.ln_backward(dev["dy"], dev["x"], torch.from_numpy(mean).to(DEV), r, g, workspace=ws)
+        else:
+            out = rn.rms_norm_backward(dev["dy"], dev["x"], r, g, workspace=ws)
+        torch.cuda.synchronize()
+        return [o.clone() for o in out if o is not None]
+
+    monkeypatch.delenv("RN_BWD_WAIT_POLLS", raising=False)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    normal = call(ws)
+    monkeypatch.setenv("RN_BWD_WAIT_POLLS", "0")
+    local = call(ws)
+    computed = int(ws[header + 4:header + 8].view(torch.int32).item())
+    monkeypatch.delenv("RN_BWD_WAIT_POLLS")
+    assert 0 < computed <= rows * S * (S - 1)  # each workgroup of a row may compute the others
+    for a, b in zip(normal, local):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    # and against the oracle
+    if op == "ln":
+        ref = oracle.layer_norm_backward(inp["dy"], inp["x"], inp.get("gamma"), mean=mean, rstd=rstd, eps=w.eps)
+    else:
+        ref = oracle.rms_norm_backward(inp["dy"], inp["x"], inp.get("weight"), rstd=rstd, eps=w.eps)
+    gam = inp.get("gamma", inp.get("weight"))
+    s_r, a_g, a_b = _scales(w, inp, mean, rstd, gam)
+    check_dx(local[0], ref["dx"], s_r)
 
 
 def test_backward_split_rows_deterministic_and_param_only():
