@@ -93,8 +93,10 @@ typedef enum rn_status {
     RN_ERR_UNSUPPORTED = 5,   /* a forced kernel variant cannot run this shape / alignment */
     RN_ERR_HIP = 6,           /* the HIP runtime reported an error at launch */
     RN_ERR_ALIGN = 7,         /* a pointer is not aligned to its element size */
-    RN_ERR_WORKSPACE = 8      /* a required workspace is missing or smaller than
+    RN_ERR_WORKSPACE = 8,     /* a required workspace is missing or smaller than
                                  rn_backward_workspace_bytes() / rn_forward_workspace_bytes() */
+    RN_ERR_SCRATCH = 9        /* rn_forward_noalloc: the shape needs more scratch than the
+                                 library's static array holds (RN_NOALLOC_SCRATCH_BYTES) */
 } rn_status;
 
 /* Kernel variants (for rn_*_variant entry points and rn_plan). */
@@ -211,6 +213,25 @@ int rn_forward_ex(int op, const void* x, const void* residual, const void* gamma
                   void* residual_out, float* mean, float* rstd, int64_t rows, int64_t N, float eps, int dtype,
                   const rn_row_strides* strides, int variant, void* workspace, size_t workspace_bytes,
                   hipStream_t stream);
+
+/*
+ * rn_forward_ex without a workspace argument and without any allocation, for callers that
+ * cannot allocate device memory (work being captured into a HIP graph, serving loops that
+ * must not call hipMalloc, harnesses that forbid it). Arguments, results and errors are
+ * those of rn_forward_ex with variant RN_VARIANT_AUTO; the split-row workspace, when the
+ * shape needs one (rn_forward_workspace_bytes > 0), is a static device array of the library,
+ * RN_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU, held from the library's first use on that GPU
+ * until the process ends. A shape that needs more returns RN_ERR_SCRATCH before anything is
+ * enqueued. The call itself allocates nothing and calls no allocating routine.
+ * Every call on one GPU shares that GPU's array: calls that may run at the same time on one
+ * GPU (different streams, or different host threads without ordering) race on it and must
+ * not both take the split-row path; calls ordered on one stream are safe. Nothing is left in
+ * the array that a later call depends on.
+ */
+#define RN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int rn_forward_noalloc(int op, const void* x, const void* residual, const void* gamma, const void* beta, void* y,
+                       void* residual_out, float* mean, float* rstd, int64_t rows, int64_t N, float eps, int dtype,
+                       const rn_row_strides* strides, hipStream_t stream);
 
 /* Workspace bytes rn_forward_ex needs for the split-row paths of this shape: rows *
  * ceil(N / 8192) * 16 when N > 16384 (enough for either split-row variant, whatever the

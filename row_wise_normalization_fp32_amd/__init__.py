@@ -75,6 +75,9 @@ _lib.rn_version.argtypes = []
 _lib.rn_version.restype = _ci
 _lib.rn_plan.argtypes = [_ci, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci, _ci,
                          ctypes.POINTER(RowStrides), _vp, ctypes.c_size_t, ctypes.POINTER(PlanInfo)]
+_lib.rn_forward_noalloc.argtypes = [_ci, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci,
+                                    ctypes.POINTER(RowStrides), _vp]
+_lib.rn_forward_noalloc.restype = _ci
 _lib.rn_forward_workspace_bytes.argtypes = [_ci, _i64, _i64, _ci]
 _lib.rn_forward_workspace_bytes.restype = ctypes.c_size_t
 _lib.rn_plan.restype = _ci
@@ -93,7 +96,7 @@ VARIANTS = {"auto": 0, "wave": 1, "workgroup": 2, "general": 3, "element": 4, "w
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 OPS = {"ln": 0, "rms": 1, "fused_add_rms": 2, "fused_add_ln": 3, "softmax": 4}
 STATUS = {0: "RN_OK", 1: "RN_ERR_NULL", 2: "RN_ERR_SHAPE", 3: "RN_ERR_DTYPE", 4: "RN_ERR_ALIAS",
-          5: "RN_ERR_UNSUPPORTED", 6: "RN_ERR_HIP", 7: "RN_ERR_ALIGN", 8: "RN_ERR_WORKSPACE"}
+          5: "RN_ERR_UNSUPPORTED", 6: "RN_ERR_HIP", 7: "RN_ERR_ALIGN", 8: "RN_ERR_WORKSPACE", 9: "RN_ERR_SCRATCH"}
 
 
 class RowNormError(RuntimeError):

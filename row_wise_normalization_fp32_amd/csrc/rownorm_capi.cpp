@@ -778,6 +778,7 @@ const char* rn_status_string(int status) {
     case RN_ERR_HIP: return "RN_ERR_HIP";
     case RN_ERR_ALIGN: return "RN_ERR_ALIGN";
     case RN_ERR_WORKSPACE: return "RN_ERR_WORKSPACE";
+    case RN_ERR_SCRATCH: return "RN_ERR_SCRATCH";
     default: return "unknown status";
     }
 }
