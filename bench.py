@@ -156,10 +156,14 @@ def kernel_name(w, plan):
                 f"{plan['rows_per_block']} row group(s) per workgroup) + rn::rownorm_bwd_cols_kernel")
     if plan["variant"] == "general":
         return f"rn::rownorm_general_kernel ({w.dtype}, {w.op})"
-    if plan["variant"] in ("wide", "wide_element"):
-        k = "rownorm_wide_elem" if plan["variant"] == "wide_element" else "rownorm_wide"
-        return (f"rn::{k}_stats_kernel + rn::{k}_norm_kernel ({w.dtype}, {w.op}, one 512-lane workgroup per "
-                f"row segment, {plan['grid_blocks']} segments)")
+    if plan["variant"] == "wide":
+        # the bench passes the full workspace and writes out of place: the one-pass form
+        return (f"rn::rownorm_wide_clear_kernel + rn::rownorm_wide_onepass_kernel ({w.dtype}, {w.op}, 32 KiB "
+                f"segments, one 512-lane workgroup per (row block, segment) ticket, {plan['grid_blocks']} row "
+                f"segments, x read once)")
+    if plan["variant"] == "wide_element":
+        return (f"rn::rownorm_wide_elem_stats_kernel + rn::rownorm_wide_elem_norm_kernel ({w.dtype}, {w.op}, one "
+                f"512-lane workgroup per row segment, {plan['grid_blocks']} segments)")
     mode = "persistent" if plan["persistent"] else "grid per row"
     if plan["variant"] == "element":
         k = "rownorm_pair_kernel" if plan.get("pairs") else "rownorm_elem_kernel"
@@ -579,7 +583,8 @@ def _more():
         ("layer_norm_ragged", workloads.LN_RAGGED,
          "LayerNorm, bf16 I/O, 16384 x 4095 (rows not whole 16-byte chunks: element-pair kernel), y + mean + rstd"),
         ("layer_norm_split_rows", workloads.LN_SPLIT,
-         "LayerNorm, fp32 I/O, 1024 x 65536 (rows beyond a workgroup's registers: split-row kernels)"),
+         "LayerNorm, fp32 I/O, 1024 x 65536 (rows beyond a workgroup's registers: one-pass split rows, the "
+         "segments of a row exchanging their statistics through the workspace, x read once)"),
         ("softmax_vocab", workloads.SOFTMAX_VOCAB,
          "row-wise softmax, fp32 I/O, 1024 x 50257 (vocabulary-sized rows, not whole chunks: element kernel, "
          "one 16-wave workgroup per row)"),

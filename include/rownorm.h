@@ -110,8 +110,10 @@ typedef enum rn_variant {
     RN_VARIANT_ELEMENT = 4,   /* rows up to 16384 elements held in VGPRs one element per slot;
                                  any element-aligned pointers and strides */
     RN_VARIANT_WIDE = 5,      /* rows longer than RN_VARIANT_WORKGROUP holds (whole 16-byte
-                                 chunks): split into 32 KiB segments, one workgroup each, in two
-                                 launches; needs a workspace (rn_forward_ex) */
+                                 chunks): split into 32 KiB segments, one workgroup each, that
+                                 exchange statistics through the workspace; x is read once
+                                 (two launches, x read twice, for in-place calls or a workspace
+                                 of only the two-launch size); needs a workspace (rn_forward_ex) */
     RN_VARIANT_WIDE_ELEMENT = 6 /* rows of more than 16384 elements with any element-aligned
                                  pointers and strides: split into segments of 8192 elements (one
                                  per register slot), one workgroup each, in two launches; needs a
@@ -203,11 +205,22 @@ int softmax_forward(const void* x, void* y, float* row_max, float* row_sum, int6
  *              share it must be ordered (same stream).
  * Unknown op codes return RN_ERR_SHAPE.
  *
- * The split-row path (walkthrough section 1.1: a row that outgrows one block) reads x (for
- * the fused ops: residual_out) a second time; the second read is served from the memory-side
- * cache when the tensor fits in it. Without a workspace, LayerNorm and fused add + RMSNorm
- * rows of whole chunks up to 128 KiB take one 16-wave workgroup; other such rows take the
- * general kernel.
+ * Split rows (walkthrough section 1.1: a row that outgrows one block). Rows of whole 16-byte
+ * chunks with up to 256 segments, called out of place with a workspace of
+ * rn_forward_workspace_bytes, take one pass that reads x (and the residual) once: a small
+ * kernel first clears a 256-byte header (a ticket counter; at byte offset 4 a 32-bit count of
+ * records computed by waiting workgroups, left there as a diagnostic) and the records; the
+ * workgroups then take (row block, segment) tickets in order, publish each segment's
+ * statistics record as tagged 64-bit words, wait a bounded time for the row's other records
+ * and compute any still missing themselves from the inputs, with the same bits, so the result
+ * never depends on which workgroups run at the same time. The environment variable
+ * RN_FWD_WAIT_POLLS (a non-negative integer, read at every call) sets the wait; 0 computes
+ * every other record locally. In-place calls (y == x, residual_out == residual, ...), rows
+ * of more than 256 segments, and a workspace of only the two-launch size (rows * ceil(N /
+ * 8192) * 16 bytes) take two launches: records, then normalization, which reads x (for the
+ * fused ops: residual_out) a second time. Both forms give the same bits. Without a
+ * workspace, LayerNorm and fused add + RMSNorm rows of whole chunks up to 128 KiB take one
+ * 16-wave workgroup; other such rows take the general kernel.
  */
 int rn_forward_ex(int op, const void* x, const void* residual, const void* gamma, const void* beta, void* y,
                   void* residual_out, float* mean, float* rstd, int64_t rows, int64_t N, float eps, int dtype,
@@ -233,9 +246,11 @@ int rn_forward_noalloc(int op, const void* x, const void* residual, const void* 
                        void* residual_out, float* mean, float* rstd, int64_t rows, int64_t N, float eps, int dtype,
                        const rn_row_strides* strides, hipStream_t stream);
 
-/* Workspace bytes rn_forward_ex needs for the split-row paths of this shape: rows *
- * ceil(N / 8192) * 16 when N > 16384 (enough for either split-row variant, whatever the
- * alignment), else 0 (such rows are never split). */
+/* Workspace bytes rn_forward_ex needs for the split-row paths of this shape, 0 when N <= 16384
+ * (such rows are never split). Otherwise the larger of the two-launch layout, rows *
+ * ceil(N / 8192) * 16 bytes (16-byte records), and the one-pass layout, 256 + rows *
+ * ceil(N * element_bytes / 32768) * 32 bytes (a header, then four 64-bit words per record):
+ * enough for either split-row variant, whatever the alignment. */
 size_t rn_forward_workspace_bytes(int op, int64_t rows, int64_t N, int dtype);
 
 /* Same as the first three entry points above, with the kernel variant forced (RN_VARIANT_AUTO

@@ -74,10 +74,44 @@ int64_t wide_elem_segments(int64_t N) { return (N + rn::kWideElemSeg - 1) / rn::
 
 // Workspace for either split-row path (the element segmentation has at least as many
 // segments); 0 for rows of up to 16384 elements, which the automatic choice never splits.
+// Split-row workspace. The two-launch form: one 16-byte record per (row, segment), at most
+// rows * ceil(N / 8192) of them (element segments are never longer than chunk segments).
 size_t wide_workspace_bytes(int64_t rows, int64_t N) {
     const int64_t elem_cap = int64_t(64) * rn::kMaxGroupWaves * rn::kElemMaxPerLane;
     if (rows <= 0 || N <= elem_cap) return 0;
     return static_cast<size_t>(rows * wide_elem_segments(N) * 16);
+}
+
+// The one-pass form (rows of whole chunks): a 256-byte header (ticket counter, count of
+// records computed by waiting workgroups), then four 64-bit words per (row, chunk segment).
+size_t wide_onepass_bytes(int64_t rows, int64_t C) { return 256 + static_cast<size_t>(rows * wide_segments(C) * 32); }
+
+// The one-pass layout's bytes for rows of N elements of s bytes (0 when N * s is not whole
+// chunks: such rows never take it).
+template <class A>
+size_t vec_layout_bytes(const A&, int64_t rows, int64_t N, int64_t s) {
+    return (N * s) % 16 == 0 ? wide_onepass_bytes(rows, N * s / 16) : 0;
+}
+
+// What rn_forward_workspace_bytes reports: room for either form.
+size_t wide_workspace_bytes_any(int64_t rows, int64_t N, int64_t s) {
+    const size_t two = wide_workspace_bytes(rows, N);
+    if (two == 0) return 0;
+    const size_t one = wide_onepass_bytes(rows, (N * s + 15) / 16);
+    return one > two ? one : two;
+}
+
+// Polls of a missing segment record before the one-pass split-row forward computes it in the
+// waiting workgroup: rn::kWideWaitPolls, or RN_FWD_WAIT_POLLS from the environment (a
+// non-negative integer; 0 computes every other segment's record locally, which tests use to
+// check that both ways give the same bits). Read at every call.
+int fwd_wait_polls() {
+    const char* v = getenv("RN_FWD_WAIT_POLLS");
+    if (v == nullptr || *v == '\0') return rn::kWideWaitPolls;
+    char* end = nullptr;
+    const long n = strtol(v, &end, 10);
+    if (end == v || *end != '\0' || n < 0 || n > (1L << 30)) return rn::kWideWaitPolls;
+    return static_cast<int>(n);
 }
 
 // Validates the arguments (dropping pointers the operation does not use) and chooses the
@@ -163,7 +197,10 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     const bool ws_given = a.ws != nullptr && ws_need > 0 && a.ws_bytes >= ws_need;
     if (ws_given) {
         if (reinterpret_cast<uintptr_t>(a.ws) % 16 != 0) return RN_ERR_ALIGN;
-        const Buf wsb{a.ws, static_cast<int64_t>(ws_need), 0, true, R_MEAN};
+        // the bytes a launch may touch: the one-pass layout when the workspace holds it
+        const size_t one = vec_layout_bytes(a, rows, N, s);
+        const size_t used = a.ws_bytes >= one && one > ws_need ? one : ws_need;
+        const Buf wsb{a.ws, static_cast<int64_t>(used), 0, true, R_MEAN};
         for (int j = 0; j < nb; ++j)
             if (bufs[j].p && overlaps(wsb, bufs[j])) return RN_ERR_ALIAS;
     }
@@ -369,7 +406,22 @@ int run(Args a, const rn_row_strides* strides, hipStream_t stream) {
     // chip); the element kernel is the same instance in both launch modes.
     const bool pers_vec = plan.persistent && plan.variant != rn::V_ELEMENT;
     if (plan.variant == rn::V_WIDE || plan.variant == rn::V_WIDE_ELEM) {
-        rn::WideArgs wa{a.ws, static_cast<int>(plan.variant == rn::V_WIDE ? wide_segments(C) : wide_elem_segments(a.N))};
+        rn::WideArgs wa{};
+        wa.ws = a.ws;
+        wa.S = static_cast<int>(plan.variant == rn::V_WIDE ? wide_segments(C) : wide_elem_segments(a.N));
+        wa.wait_polls = fwd_wait_polls();
+        // the one-pass layout, when the workspace holds it (its 64-bit atomics and 16-byte
+        // clears need 16-byte alignment, which every split-row workspace has). Not in place:
+        // a waiting workgroup may compute another segment's record from that segment's
+        // inputs, which in place its owner may already have overwritten; in-place calls take
+        // the two launches, whose first reads everything before the second writes.
+        const bool in_place = a.y == a.x || (a.residual_out != nullptr &&
+                                             (a.residual_out == a.residual || a.residual_out == a.x)) ||
+                              (a.residual != nullptr && a.y == a.residual);
+        if (plan.variant == rn::V_WIDE && !in_place && a.ws_bytes >= wide_onepass_bytes(a.rows, C)) {
+            wa.sync = static_cast<unsigned*>(a.ws);
+            wa.rec64 = reinterpret_cast<unsigned long long*>(static_cast<char*>(a.ws) + 256);
+        }
         hipError_t e = hipErrorInvalidValue;
         switch (a.dtype) {
         case RN_F32: e = rn::launch_wide_f32(a.op, plan, p, wa, stream); break;
@@ -605,8 +657,12 @@ int run_bwd(BwdArgs a, hipStream_t stream) {
         p.rec = reinterpret_cast<float*>(recs);
         p.S = static_cast<int>(bwd_wide_segments(a.N));
         p.vec = plan.exact ? 1 : 0;
-        // the one-pass kernel's 64-bit atomics and 16-byte clears need 16-byte alignment
-        if (reinterpret_cast<uintptr_t>(recs) % 16 == 0) {
+        // the one-pass kernel's 64-bit atomics and 16-byte clears need 16-byte alignment. Not
+        // in place: a waiting workgroup may compute another segment's sums from that
+        // segment's x and dy, which its owner may already have overwritten with dx; in-place
+        // calls take the two launches, whose first reads x and dy before the second writes.
+        const bool in_place = a.dx != nullptr && (a.dx == a.dy || a.dx == a.x);
+        if (reinterpret_cast<uintptr_t>(recs) % 16 == 0 && !in_place) {
             p.sync = reinterpret_cast<unsigned*>(recs);
             p.rec64 = reinterpret_cast<unsigned long long*>(recs + 256);
         }
@@ -676,7 +732,8 @@ int rn_forward_ex(int op, const void* x, const void* residual, const void* gamma
 size_t rn_forward_workspace_bytes(int op, int64_t rows, int64_t N, int dtype) {
     if (op < RN_OP_LAYER_NORM || op > RN_OP_SOFTMAX) return 0;
     if (dtype != RN_F32 && dtype != RN_F16 && dtype != RN_BF16) return 0;
-    return wide_workspace_bytes(rows, N);
+    if (rows <= 0 || N <= 0 || rows > (int64_t(1) << 40) || N > (int64_t(1) << 40)) return 0;
+    return wide_workspace_bytes_any(rows, N, dtype == RN_F32 ? 4 : 2);
 }
 
 int ln_forward_variant(const void* x, const void* gamma, const void* beta, void* y, float* mean, float* rstd,

@@ -38,6 +38,14 @@ struct Params {
 struct WideArgs {
     void* ws;
     int S;  // segments per row
+    // one-pass launches: [0] ticket counter, [1] count of records computed by waiting
+    // workgroups (zeroed before launch), then records of four 64-bit words
+    // (tag << 32 | fp32 bits) per (row, segment)
+    unsigned* sync;
+    unsigned long long* rec64;
+    int P;           // row blocks
+    int R;           // rows per block (one ticket = one block of one segment)
+    int wait_polls;  // polls of a missing record before the waiting workgroup computes it
 };
 
 // Backward row kernel arguments (rownorm_backward.hpp).
@@ -119,6 +127,9 @@ constexpr int kBwdWideMaxGroups = 2048;  // backward split rows: at most this ma
 constexpr int kBwdWaitPolls = 1 << 12;   // one-pass split rows: polls of a missing record (about 1-2 us
                                          // each) before the waiting workgroup computes it itself
 constexpr int kBwdOnePassMaxSeg = 256;   // one-pass split rows: at most this many segments per row
+constexpr int kWideOnePassMaxSeg = 256;  // forward one-pass split rows: at most this many segments per row
+constexpr int kWideWaitPolls = 1 << 12;  // forward one-pass split rows: polls of a missing record
+constexpr int kWideOnePassRows = 4;      // forward one-pass split rows: rows per ticket (row block)
 constexpr int kBwdTargetChunks = 2;    // backward: about 2 chunks of x and of dy per lane (1 measured slower)
 
 // Enqueue the planned kernel for one I/O dtype (one translation unit per dtype and mode).

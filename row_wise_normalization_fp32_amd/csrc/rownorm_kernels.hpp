@@ -338,6 +338,9 @@ constexpr float kLog2eLo = 1.92596298909109e-8f;            // log2(e) - kLog2e
 // and so does NaN (-inf - (-inf) for a part holding only masked entries); a NaN logit
 // reaches the result through the row's maximum instead (see max_nan).
 __device__ __forceinline__ float exp_neg(float u) {
+    // No contraction: every kernel that inlines this gets the same roundings (the segment
+    // records of a split row must have the same bits whichever kernel forms them).
+#pragma clang fp contract(off)
     u = fmaxf(u, -200.f);
     const float hi = u * kLog2e;
     const float lo = fmaf(u, kLog2e, -hi) + u * kLog2eLo;
@@ -359,6 +362,9 @@ __device__ __forceinline__ Moments combine_equal(const Moments& a, const Moments
 // smarter.xin, sections "Online Softmax denominator correction" and "merging (max, sum)
 // with decay").
 __device__ __forceinline__ void softmax_combine(float& m, float& s, float mb, float sb) {
+    // No contraction: both products are rounded, so combining (a, b) and (b, a) gives the same
+    // bits (the butterflies rely on it) in every kernel that inlines this.
+#pragma clang fp contract(off)
     const float M = max_nan(m, mb);
     s = s * exp_neg(m - M) + sb * exp_neg(mb - M);
     m = M;
@@ -1270,6 +1276,94 @@ constexpr int kWideLanes = 64 * kWideW;
 constexpr int kWideChunks = kWideLanes * kWideV;  // 2048 chunks = 32 KiB per segment
 static_assert(kWideChunks == kWideSegChunks, "segment size shared with the planner");
 
+// The statistics record of one segment (Cs chunks; lane t holds chunks t, t + 512, ... of it):
+// LayerNorm (count, this wave's rough mean a, the segment mean relative to a, M2), written by
+// wave 0 so relative to its a; softmax (max, sum of exp(x - max)); RMSNorm (sum of squares).
+// get(i) returns the lane's chunk i (x, or the rounded residual sum for the fused ops); it is
+// called once per pass (twice for LayerNorm and softmax), so it may read memory again. Every
+// wave takes part (one barrier). The two-launch statistics kernel, the one-pass kernel and a
+// workgroup that computes another segment's record in its place all go through this, so the
+// records have the same bits.
+template <int DT, int OP, bool EXACT, class Get>
+__device__ __forceinline__ float4 wide_record(Get get, int Cs, int t, int lane, int wr, WavePart (*part)[kWideW],
+                                              int& buf) {
+    using IO = Io<DT>;
+    using OT = OpTraits<OP>;
+    constexpr int E = IO::E;
+    constexpr int V = kWideV;
+    auto valid = [&](int i) { return EXACT || i * kWideLanes + t < Cs; };
+    int cnt = 0;  // chunks of this wave
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        const int k = Cs - (i * kWideLanes + wr * 64);
+        cnt += k <= 0 ? 0 : (k >= 64 ? 64 : k);
+    }
+    const float n_w = static_cast<float>(cnt * E);
+    if constexpr (OT::LN) {
+        const float K = uniform(IO::first(get(0)));
+        float s1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            float f[E];
+            IO::unpack(get(i), f);
+#pragma unroll
+            for (int e = 0; e < E; ++e) s1 += valid(i) ? f[e] - K : 0.f;
+        }
+        const float inv_w = n_w > 0.f ? 1.0f / n_w : 0.f;
+        const float a = K + wave_sum(s1) * inv_w;
+        float c = 0.f, q = 0.f;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            float f[E];
+            IO::unpack(get(i), f);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float d = valid(i) ? f[e] - a : 0.f;
+                c += d;
+                q = fmaf(d, d, q);
+            }
+        }
+        const float Cw = wave_sum(c), Qw = wave_sum(q);
+        const float cw = Cw * inv_w;
+        float rel, m2, mean;
+        group_moments<kWideW, false>(part, buf, lane, wr, n_w, a, cw, fmaxf(Qw - Cw * cw, 0.f), rel, m2, mean);
+        // relative to wave 0's rough mean R: rel is the mean minus this wave's a, so
+        // mean - R = rel + (a - R); wave 0 (a == R) writes the record
+        return make_float4(static_cast<float>(Cs * E), a, rel, m2);
+    } else if constexpr (OT::SM) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            float f[E];
+            IO::unpack(get(i), f);
+#pragma unroll
+            for (int e = 0; e < E; ++e) mx = valid(i) ? max_nan(mx, f[e]) : mx;
+        }
+        const float mw = wave_max(mx);
+        float sm = 0.f;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            float f[E];
+            IO::unpack(get(i), f);
+#pragma unroll
+            for (int e = 0; e < E; ++e) sm += valid(i) ? exp_neg(f[e] - mw) : 0.f;
+        }
+        float M, Ssum;
+        group_softmax<kWideW>(part, buf, lane, wr, mw, wave_sum(sm), M, Ssum);
+        return make_float4(M, Ssum, 0.f, 0.f);
+    } else {
+        float sq = 0.f;
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+            float f[E];
+            IO::unpack(get(i), f);
+#pragma unroll
+            for (int e = 0; e < E; ++e) sq = valid(i) ? fmaf(f[e], f[e], sq) : sq;
+        }
+        return make_float4(group_sum<kWideW>(part, buf, lane, wr, wave_sum(sq)), 0.f, 0.f, 0.f);
+    }
+}
+
 template <int DT, int OP, bool EXACT>
 __global__ __launch_bounds__(kWideLanes) void rownorm_wide_stats_kernel(Params p, WideArgs wa) {
     using IO = Io<DT>;
@@ -1315,86 +1409,85 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_stats_kernel(Params p
                 if (valid(i)) ro[chunk(i)] = src[i];
             }
         }
-        int cnt = 0;  // chunks of this wave
-#pragma unroll
-        for (int i = 0; i < V; ++i) {
-            const int k = Cs - (i * kWideLanes + wr * 64);
-            cnt += k <= 0 ? 0 : (k >= 64 ? 64 : k);
-        }
-        const float n_w = static_cast<float>(cnt * E);
-        float4 rec;
-        if constexpr (OT::LN) {
-            const float K = uniform(IO::first(src[0]));
-            float s1 = 0.f;
-#pragma unroll
-            for (int i = 0; i < V; ++i) {
-                float f[E];
-                IO::unpack(src[i], f);
-#pragma unroll
-                for (int e = 0; e < E; ++e) s1 += valid(i) ? f[e] - K : 0.f;
-            }
-            const float inv_w = n_w > 0.f ? 1.0f / n_w : 0.f;
-            const float a = K + wave_sum(s1) * inv_w;
-            float c = 0.f, q = 0.f;
-#pragma unroll
-            for (int i = 0; i < V; ++i) {
-                float f[E];
-                IO::unpack(src[i], f);
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float d = valid(i) ? f[e] - a : 0.f;
-                    c += d;
-                    q = fmaf(d, d, q);
-                }
-            }
-            const float Cw = wave_sum(c), Qw = wave_sum(q);
-            const float cw = Cw * inv_w;
-            float rel, m2, mean;
-            group_moments<kWideW, false>(part, buf, lane, wr, n_w, a, cw, fmaxf(Qw - Cw * cw, 0.f), rel, m2, mean);
-            // relative to wave 0's rough mean R: rel is the mean minus this wave's a, so
-            // mean - R = rel + (a - R); wave 0 (a == R) writes the record
-            rec = make_float4(static_cast<float>(Cs * E), a, rel, m2);
-        } else if constexpr (OT::SM) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < V; ++i) {
-                float f[E];
-                IO::unpack(src[i], f);
-#pragma unroll
-                for (int e = 0; e < E; ++e) mx = valid(i) ? max_nan(mx, f[e]) : mx;
-            }
-            const float mw = wave_max(mx);
-            float sm = 0.f;
-#pragma unroll
-            for (int i = 0; i < V; ++i) {
-                float f[E];
-                IO::unpack(src[i], f);
-#pragma unroll
-                for (int e = 0; e < E; ++e) sm += valid(i) ? exp_neg(f[e] - mw) : 0.f;
-            }
-            float M, Ssum;
-            group_softmax<kWideW>(part, buf, lane, wr, mw, wave_sum(sm), M, Ssum);
-            rec = make_float4(M, Ssum, 0.f, 0.f);
-        } else {
-            float sq = 0.f;
-#pragma unroll
-            for (int i = 0; i < V; ++i) {
-                float f[E];
-                IO::unpack(src[i], f);
-#pragma unroll
-                for (int e = 0; e < E; ++e) sq = valid(i) ? fmaf(f[e], f[e], sq) : sq;
-            }
-            rec = make_float4(group_sum<kWideW>(part, buf, lane, wr, wave_sum(sq)), 0.f, 0.f, 0.f);
-        }
+        const float4 rec = wide_record<DT, OP, EXACT>([&](int i) { return src[i]; }, Cs, t, lane, wr, part, buf);
         if (t == 0) static_cast<float4*>(wa.ws)[row * wa.S + seg] = rec;
     }
 }
 
-template <int DT, int OP, bool EXACT, int AFF>
-__global__ __launch_bounds__(kWideLanes) void rownorm_wide_norm_kernel(Params p, WideArgs wa) {
+// The row's normalization from its combined records (combine_records): LayerNorm subtracts
+// R0 and scales by rstd with the offset -(mean - R0) * rstd; softmax scales exp(x - max) by
+// 1 / sum; RMSNorm scales by rstd. Shared by the split-row normalize steps.
+struct WideScale {
+    float R0, scale, offset;
+};
+
+template <int OP>
+__device__ __forceinline__ WideScale wide_scale(const float4& tot, const Params& p) {
+    using OT = OpTraits<OP>;
+    WideScale w{0.f, 0.f, 0.f};
+    if constexpr (OT::LN) {
+        w.R0 = tot.x;
+        w.scale = inv_sqrt(fmaf(tot.z, p.inv_n, p.eps));
+        w.offset = -tot.y * w.scale;
+    } else if constexpr (OT::SM) {
+        w.R0 = tot.x;
+        w.scale = 1.0f / tot.y;
+    } else {
+        w.scale = inv_sqrt(fmaf(tot.x, p.inv_n, p.eps));
+    }
+    return w;
+}
+
+// The row statistics the caller asked for (the segment-0 workgroup stores them).
+template <int OP>
+__device__ __forceinline__ void wide_store_stats(const Params& p, int64_t row, const float4& tot, const WideScale& w) {
+    using OT = OpTraits<OP>;
+    if constexpr (OT::LN) {
+        if (p.mean) p.mean[row] = w.R0 + tot.y;
+        if (p.rstd) p.rstd[row] = w.scale;
+    } else if constexpr (OT::SM) {
+        if (p.mean) p.mean[row] = tot.x;
+        if (p.rstd) p.rstd[row] = tot.y;
+    } else {
+        if (p.rstd) p.rstd[row] = w.scale;
+    }
+}
+
+// One output chunk: the normalized source chunk with the affine parameters, rounded once.
+template <int DT, int OP, bool HG, bool HB>
+__device__ __forceinline__ u32x4 wide_out(const u32x4& src, const u32x4& gv, const u32x4& bv, const WideScale& w) {
     using IO = Io<DT>;
     using OT = OpTraits<OP>;
     constexpr int E = IO::E;
+    float f[E], g[E], bb[E], o[E];
+    IO::unpack(src, f);
+    if constexpr (HG) IO::unpack(gv, g);
+    if constexpr (HB) IO::unpack(bv, bb);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        float z;
+        if constexpr (OT::LN) {
+            z = fmaf(f[e] - w.R0, w.scale, w.offset);
+        } else if constexpr (OT::SM) {
+            z = exp_neg(f[e] - w.R0) * w.scale;
+        } else {
+            z = f[e] * w.scale;
+        }
+        if constexpr (HG && HB) {
+            z = fmaf(z, g[e], bb[e]);
+        } else if constexpr (HG) {
+            z = z * g[e];
+        } else if constexpr (HB) {
+            z = z + bb[e];
+        }
+        o[e] = z;
+    }
+    return IO::pack(o);
+}
+
+template <int DT, int OP, bool EXACT, int AFF>
+__global__ __launch_bounds__(kWideLanes) void rownorm_wide_norm_kernel(Params p, WideArgs wa) {
+    using OT = OpTraits<OP>;
     constexpr int V = kWideV;
     constexpr bool HG = !OT::SM && (AFF & AFF_G) != 0;
     constexpr bool HB = OT::LN && (AFF & AFF_B) != 0;
@@ -1422,53 +1515,238 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_norm_kernel(Params p,
         }
         // combine the row's segment records (same bits in every workgroup of the row)
         const float4 tot = combine_records<OP>(static_cast<const float4*>(wa.ws) + row * wa.S, wa.S, t & 63);
-        float scale, offset = 0.f, R0 = 0.f;
-        if constexpr (OT::LN) {
-            R0 = tot.x;
-            scale = inv_sqrt(fmaf(tot.z, p.inv_n, p.eps));
-            offset = -tot.y * scale;
-            if (seg == 0 && t == 0) {
-                if (p.mean) p.mean[row] = R0 + tot.y;
-                if (p.rstd) p.rstd[row] = scale;
-            }
-        } else if constexpr (OT::SM) {
-            R0 = tot.x;
-            scale = 1.0f / tot.y;
-            if (seg == 0 && t == 0) {
-                if (p.mean) p.mean[row] = tot.x;
-                if (p.rstd) p.rstd[row] = tot.y;
-            }
-        } else {
-            scale = inv_sqrt(fmaf(tot.x, p.inv_n, p.eps));
-            if (seg == 0 && t == 0 && p.rstd) p.rstd[row] = scale;
-        }
+        const WideScale w = wide_scale<OP>(tot, p);
+        if (seg == 0 && t == 0) wide_store_stats<OP>(p, row, tot, w);
         u32x4* yr = static_cast<u32x4*>(p.y) + row * p.cy;
 #pragma unroll
         for (int i = 0; i < V; ++i) {
-            float f[E], g[E], bb[E], o[E];
-            IO::unpack(src[i], f);
-            if constexpr (HG) IO::unpack(gv[i], g);
-            if constexpr (HB) IO::unpack(bv[i], bb);
+            const u32x4 o = wide_out<DT, OP, HG, HB>(src[i], gv[HG ? i : 0], bv[HB ? i : 0], w);
+            if (valid(i)) __builtin_nontemporal_store(o, yr + chunk(i));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// One-pass split rows (whole 16-byte chunks): x (for the fused ops, x and the residual) is
+// read once, the walkthrough's single-read layout (sections 3-4) carried over to a row that
+// outgrows one workgroup (section 1.1). The rows are cut into P blocks of R rows; a ticket is
+// one (block, segment) pair, ticket = block * S + segment, and workgroups take tickets from a
+// counter in the workspace in increasing order. For each row of its block the workgroup
+// holding a ticket keeps its segment in registers, forms the segment's statistics record
+// (wide_record, as the two-launch path does) and publishes it as four 64-bit words (tag 1 in
+// the upper half, the float's bits in the lower half; single-copy atomic, device scope), loads
+// the row after next, posts the next row, and then waits (one wave, one lane per record)
+// until all S records of the row carry the tag. The S records are combined in the same fixed
+// order in every workgroup of the row (combine_records, so all get the same bits, the same as
+// the two-launch path's), and the segment is normalized from its registers. A record still
+// missing after a bounded wait (wait_polls polls) is computed by the waiting workgroup itself
+// from that segment's data with wide_record, so nothing waits on a workgroup that is not
+// running and the result does not depend on timing. The segment's gamma / beta are staged in
+// LDS once per ticket. The counter, a count of records computed by waiting workgroups (a
+// diagnostic) and the records are zeroed by rownorm_wide_clear_kernel before each launch (a
+// kernel, not a memset, so that the call can be captured in a graph).
+// ---------------------------------------------------------------------------------------
+
+template <int DT>  // one instance per dtype's translation unit
+__global__ __launch_bounds__(256) void rownorm_wide_clear_kernel(u32x4* p, int64_t n16) {
+    const u32x4 z{0u, 0u, 0u, 0u};
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n16;
+         i += static_cast<int64_t>(gridDim.x) * 256)
+        p[i] = z;
+}
+
+template <int DT, int OP, bool EXACT, int AFF>
+__global__ __launch_bounds__(kWideLanes) void rownorm_wide_onepass_kernel(Params p, WideArgs wa) {
+    using IO = Io<DT>;
+    using OT = OpTraits<OP>;
+    constexpr int E = IO::E;
+    constexpr int V = kWideV;
+    constexpr bool HG = !OT::SM && (AFF & AFF_G) != 0;
+    constexpr bool HB = OT::LN && (AFF & AFF_B) != 0;
+    constexpr int NR = OT::RES ? V : 1;
+    constexpr int POLLER = kWideW - 1;             // the wave that waits for the records
+    constexpr int RPL = kWideOnePassMaxSeg / 64;   // records per lane of that wave
+    const int lane = threadIdx.x & 63;
+    const int wr = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform (SGPR)
+    const int t = threadIdx.x;
+    __shared__ WavePart part[2][kWideW];
+    __shared__ u32x4 prm[(HG ? kWideChunks : 0) + (HB ? kWideChunks : 0) + 1];  // gamma, then beta
+    // per row, double-buffered by row parity: one barrier separates a row's reads from the
+    // writes of the row after the next
+    __shared__ float4 s_rec[2][kWideOnePassMaxSeg];  // the row's records
+    __shared__ int s_need[2];                        // some record is computed here
+    __shared__ unsigned char s_miss[kWideOnePassMaxSeg];
+    __shared__ unsigned s_ticket;
+    int buf = 0;
+    const int S = wa.S;
+    const unsigned total = static_cast<unsigned>(wa.P) * static_cast<unsigned>(S);
+    for (;;) {
+        if (t == 0) s_ticket = __hip_atomic_fetch_add(wa.sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const unsigned ticket = s_ticket;  // read before the first barrier of the block's rows
+        if (ticket >= total) break;        // uniform over the workgroup
+        const int64_t blk = ticket / static_cast<unsigned>(S);
+        const int seg = static_cast<int>(ticket % static_cast<unsigned>(S));
+        const int64_t c0 = static_cast<int64_t>(seg) * kWideChunks;
+        const int Cs = static_cast<int>(p.C - c0 < kWideChunks ? p.C - c0 : kWideChunks);
+        auto valid = [&](int i) { return EXACT || i * kWideLanes + t < Cs; };
+        auto chunk = [&](int i) {
+            const int c = i * kWideLanes + t;
+            return c0 + (EXACT ? c : (c < Cs ? c : Cs - 1));
+        };
+        // the segment's parameters, for all the block's rows (read after the first row's
+        // wait, which is past at least one barrier)
+        for (int c = t; c < kWideChunks; c += kWideLanes) {
+            const int64_t cc = c0 + (c < Cs ? c : Cs - 1);
+            if constexpr (HG) prm[c] = static_cast<const u32x4*>(p.gamma)[cc];
+            if constexpr (HB) prm[(HG ? kWideChunks : 0) + c] = static_cast<const u32x4*>(p.beta)[cc];
+        }
+        auto load = [&](int64_t row, u32x4(&xv)[V], u32x4(&rv)[NR]) {
+            const u32x4* xr = static_cast<const u32x4*>(p.x) + row * p.cx;
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                float z;
-                if constexpr (OT::LN) {
-                    z = fmaf(f[e] - R0, scale, offset);
-                } else if constexpr (OT::SM) {
-                    z = exp_neg(f[e] - R0) * scale;
-                } else {
-                    z = f[e] * scale;
-                }
-                if constexpr (HG && HB) {
-                    z = fmaf(z, g[e], bb[e]);
-                } else if constexpr (HG) {
-                    z = z * g[e];
-                } else if constexpr (HB) {
-                    z = z + bb[e];
-                }
-                o[e] = z;
+            for (int i = 0; i < V; ++i) xv[i] = __builtin_nontemporal_load(xr + chunk(i));
+            if constexpr (OT::RES) {
+                const u32x4* rr = static_cast<const u32x4*>(p.residual) + row * p.cr;
+#pragma unroll
+                for (int i = 0; i < V; ++i) rv[i] = __builtin_nontemporal_load(rr + chunk(i));
             }
-            if (valid(i)) __builtin_nontemporal_store(IO::pack(o), yr + chunk(i));
+        };
+        auto publish = [&](int64_t row, int sgm, const float4& rec) {
+            if (t == 0) {
+                unsigned long long* w = wa.rec64 + 4 * (row * S + sgm);
+                const unsigned long long tag = 1ull << 32;
+                __hip_atomic_store(w, tag | bit_cast<unsigned>(rec.x), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(w + 1, tag | bit_cast<unsigned>(rec.y), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(w + 2, tag | bit_cast<unsigned>(rec.z), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(w + 3, tag | bit_cast<unsigned>(rec.w), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        };
+        // this workgroup's segment of one row: the fused ops form the rounded sum (kept in xv)
+        // and store residual_out; then the record, published as record `seg` of the row
+        auto post = [&](int64_t row, u32x4(&xv)[V], const u32x4(&rv)[NR]) {
+            if constexpr (OT::RES) {
+                u32x4* ro = static_cast<u32x4*>(p.residual_out) + row * p.cro;
+#pragma unroll
+                for (int i = 0; i < V; ++i) {
+                    float a[E], c[E];
+                    IO::unpack(xv[i], a);
+                    IO::unpack(rv[i], c);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) a[e] += c[e];
+                    xv[i] = IO::pack(a);
+                    if (valid(i)) __builtin_nontemporal_store(xv[i], ro + chunk(i));
+                }
+            }
+            const float4 rec = wide_record<DT, OP, EXACT>([&](int i) { return xv[i]; }, Cs, t, lane, wr, part, buf);
+            publish(row, seg, rec);
+        };
+        // segment s2's record of one row, computed here from memory, one chunk per tensor at a
+        // time (the rows in flight keep their registers)
+        auto other_record = [&](int64_t row, int s2) {
+            const int64_t c2 = static_cast<int64_t>(s2) * kWideChunks;
+            const int Cs2 = static_cast<int>(p.C - c2 < kWideChunks ? p.C - c2 : kWideChunks);
+            const u32x4* xr = static_cast<const u32x4*>(p.x) + row * p.cx + c2;
+            const u32x4* rr = OT::RES ? static_cast<const u32x4*>(p.residual) + row * p.cr + c2 : nullptr;
+            auto get = [&](int i) {
+                const int c = i * kWideLanes + t;
+                const int cc = EXACT ? c : (c < Cs2 ? c : Cs2 - 1);
+                u32x4 v = xr[cc];
+                if constexpr (OT::RES) {
+                    const u32x4 r = rr[cc];
+                    float a[E], b[E];
+                    IO::unpack(v, a);
+                    IO::unpack(r, b);
+#pragma unroll
+                    for (int e = 0; e < E; ++e) a[e] += b[e];
+                    v = IO::pack(a);
+                }
+                asm volatile("" ::: "memory");  // one chunk per tensor in flight
+                return v;
+            };
+            return wide_record<DT, OP, EXACT>(get, Cs2, t, lane, wr, part, buf);
+        };
+        const int64_t r0 = blk * wa.R;
+        const int64_t r1 = r0 + wa.R < p.rows ? r0 + wa.R : p.rows;
+        // three rows in flight: row (record posted, waiting), row + 1 (posted before the wait
+        // for row), row + 2 (loads issued before that wait)
+        u32x4 cx[V], cr[NR], nx[V], nr[NR];
+        load(r0, cx, cr);
+        if (r0 + 1 < r1) load(r0 + 1, nx, nr);
+        post(r0, cx, cr);
+        for (int64_t row = r0; row < r1; ++row) {
+            const int par = static_cast<int>(row & 1);
+            u32x4 mx[V], mr[NR];
+            if (row + 2 < r1) load(row + 2, mx, mr);
+            if (row + 1 < r1) post(row + 1, nx, nr);
+            if (wr == POLLER) {
+                const unsigned long long* w = wa.rec64 + 4 * row * S;
+                unsigned miss = 0;
+#pragma unroll
+                for (int j = 0; j < RPL; ++j) {
+                    const int k = lane + 64 * j;
+                    if (k < S) {
+                        bool got = false;
+                        for (int n = 0;; ++n) {
+                            const unsigned long long w0 = __hip_atomic_load(w + 4 * k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            const unsigned long long w1 = __hip_atomic_load(w + 4 * k + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            const unsigned long long w2 = __hip_atomic_load(w + 4 * k + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            const unsigned long long w3 = __hip_atomic_load(w + 4 * k + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            if (((w0 & w1 & w2 & w3) >> 32) != 0) {
+                                s_rec[par][k] = make_float4(bit_cast<float>(static_cast<unsigned>(w0)),
+                                                            bit_cast<float>(static_cast<unsigned>(w1)),
+                                                            bit_cast<float>(static_cast<unsigned>(w2)),
+                                                            bit_cast<float>(static_cast<unsigned>(w3)));
+                                got = true;
+                                break;
+                            }
+                            if (n >= wa.wait_polls) break;
+                            __builtin_amdgcn_s_sleep(8);
+                        }
+                        if (!got) miss |= 1u << j;
+                        s_miss[k] = got ? 0 : 1;
+                    }
+                }
+                const bool any = __any(miss != 0);  // all 64 lanes active here
+                if (lane == 0) s_need[par] = any ? 1 : 0;
+            }
+            __syncthreads();
+            if (s_need[par] != 0) {  // uniform: compute the missing records here
+                int computed = 0;
+                for (int s2 = 0; s2 < S; ++s2) {
+                    if (s_miss[s2] == 0) continue;  // uniform
+                    const float4 rec = other_record(row, s2);
+                    publish(row, s2, rec);
+                    if (t == 0) s_rec[par][s2] = rec;
+                    ++computed;
+                }
+                if (t == 0)
+                    __hip_atomic_fetch_add(wa.sync + 1, static_cast<unsigned>(computed), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                __syncthreads();
+            }
+            // combine the row's records (same bits in every workgroup of the row) and normalize
+            const float4 tot = combine_records<OP>(s_rec[par], S, lane);
+            const WideScale ws = wide_scale<OP>(tot, p);
+            if (seg == 0 && t == 0) wide_store_stats<OP>(p, row, tot, ws);
+            u32x4* yr = static_cast<u32x4*>(p.y) + row * p.cy;
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                const int c = i * kWideLanes + t;
+                const int cl = EXACT ? c : (c < Cs ? c : Cs - 1);
+                const u32x4 gv = HG ? prm[cl] : u32x4{0u, 0u, 0u, 0u};
+                const u32x4 bv = HB ? prm[(HG ? kWideChunks : 0) + cl] : u32x4{0u, 0u, 0u, 0u};
+                const u32x4 o = wide_out<DT, OP, HG, HB>(cx[i], gv, bv, ws);
+                if (valid(i)) __builtin_nontemporal_store(o, yr + chunk(i));
+            }
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                cx[i] = nx[i];
+                nx[i] = mx[i];
+                if constexpr (OT::RES) {
+                    cr[i] = nr[i];
+                    nr[i] = mr[i];
+                }
+            }
         }
     }
 }
@@ -2172,9 +2450,74 @@ inline hipError_t launch_wide_elem_op(const Plan& plan, const Params& p, const W
 #undef RN_WEN
 }
 
+// One-pass split rows (rows of whole chunks, a workspace that holds the one-pass layout):
+// the clear launch, then the one-pass kernel on min(resident, P * S) workgroups over P row
+// blocks (at most 256 segments and room for two workgroups per segment on the device;
+// otherwise, or for lack of the layout, the two launches). Returns hipErrorNotSupported when
+// the one pass does not apply.
+template <int DT, int OP, bool EXACT, int AFF>
+inline hipError_t go_wide_onepass(const Plan& plan, const Params& p, const WideArgs& wa0, hipStream_t s) {
+    constexpr auto K = rownorm_wide_onepass_kernel<DT, OP, EXACT, AFF>;
+    if (wa0.sync == nullptr || wa0.rec64 == nullptr || wa0.S > kWideOnePassMaxSeg) return hipErrorNotSupported;
+    int cus = 0, per_cu = 0;
+    hipError_t e = resident<K>(kWideLanes, 0, &cus, &per_cu);
+    if (e != hipSuccess) return e;
+    const int64_t res = static_cast<int64_t>(cus) * per_cu;
+    if (res < 2 * static_cast<int64_t>(wa0.S)) return hipErrorNotSupported;
+    // Blocks of about kWideOnePassRows rows (at least enough blocks to fill the resident
+    // grid): measured on MI355X, LayerNorm fp32 1024 x 65536: 16 rows per block 114.3 us, 8
+    // 109.0, 4 107.9; 512 rows: 8 rows 62.5 us, 4 63.3; 2048 rows: 32 rows 214.0 us, 8 201.6,
+    // 4 200.0.
+    WideArgs wa = wa0;
+    int64_t P = (p.rows + kWideOnePassRows - 1) / kWideOnePassRows;
+    if (P < res / wa.S) P = res / wa.S;
+    if (P > p.rows) P = p.rows;
+    const int64_t R = (p.rows + P - 1) / P;
+    P = (p.rows + R - 1) / R;
+    if (P * wa.S > INT32_MAX) return hipErrorNotSupported;  // tickets come from a 32-bit counter
+    wa.P = static_cast<int>(P);
+    wa.R = static_cast<int>(R);
+    // header (counter, count) and records: 256 + rows * S * 32 bytes
+    const int64_t n16 = (256 + p.rows * wa.S * 32) / 16;
+    int64_t gc = (n16 + 255) / 256;
+    if (gc > 1024) gc = 1024;
+    u32x4* clr = reinterpret_cast<u32x4*>(wa.sync);
+    void* zargv[] = {&clr, const_cast<int64_t*>(&n16)};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(rownorm_wide_clear_kernel<DT>), dim3(static_cast<unsigned>(gc)),
+                        dim3(256), zargv, 0, s);
+    if (e != hipSuccess) return e;
+    const int64_t tickets = P * wa.S;
+    const int64_t g = res < tickets ? res : tickets;
+    Params pa = p;
+    void* argv[] = {&pa, &wa};
+    return hipLaunchKernel(reinterpret_cast<const void*>(K), dim3(static_cast<unsigned>(g)), dim3(kWideLanes), argv, 0,
+                           s);
+}
+
+template <int DT, int OP, bool EXACT>
+inline hipError_t launch_wide_onepass(const Plan& plan, const Params& p, const WideArgs& wa, hipStream_t s) {
+    if constexpr (OpTraits<OP>::SM) {
+        return go_wide_onepass<DT, OP, EXACT, 0>(plan, p, wa, s);
+    } else {
+        const int aff = (p.gamma ? AFF_G : 0) | (OpTraits<OP>::LN && p.beta ? AFF_B : 0);
+        if (aff == 0) return go_wide_onepass<DT, OP, EXACT, 0>(plan, p, wa, s);
+        if (aff == AFF_G) return go_wide_onepass<DT, OP, EXACT, AFF_G>(plan, p, wa, s);
+        if constexpr (OpTraits<OP>::LN) {
+            if (aff == AFF_B) return go_wide_onepass<DT, OP, EXACT, AFF_B>(plan, p, wa, s);
+            return go_wide_onepass<DT, OP, EXACT, AFF_G | AFF_B>(plan, p, wa, s);
+        }
+        return hipErrorInvalidValue;
+    }
+}
+
 template <int DT, int OP>
 inline hipError_t launch_wide_op(const Plan& plan, const Params& p, const WideArgs& wa, hipStream_t s) {
     if (plan.variant == V_WIDE_ELEM) return launch_wide_elem_op<DT, OP>(plan, p, wa, s);
+    {
+        const hipError_t e1 = plan.exact ? launch_wide_onepass<DT, OP, true>(plan, p, wa, s)
+                                         : launch_wide_onepass<DT, OP, false>(plan, p, wa, s);
+        if (e1 != hipErrorNotSupported) return e1;
+    }
     hipError_t e = plan.exact ? go_wide<rownorm_wide_stats_kernel<DT, OP, true>>(plan, p, wa, s)
                               : go_wide<rownorm_wide_stats_kernel<DT, OP, false>>(plan, p, wa, s);
     if (e != hipSuccess) return e;

@@ -195,6 +195,27 @@ def test_backward_split_rows_workspace_contents_do_not_matter():
         assert 0 <= int(ws[header + 4:header + 8].view(torch.int32).item()) <= rows * (N // 8192)
 
 
+def test_backward_split_rows_in_place_take_two_launches(monkeypatch):
+    # dx over dy or over x: a waiting workgroup could compute another segment's sums from
+    # data its owner has already overwritten, so in-place split rows take the three
+    # launches; with every record forced to be computed locally the results keep their bits
+    monkeypatch.setenv("RN_BWD_WAIT_POLLS", "0")
+    w = workloads.LN_BWD.scaled(rows=48, N=65536, seed=1390, dtype="bf16")
+    inp = workloads.make_inputs(w)
+    mean, rstd = _stats(w, inp)
+    dev = {k: v.to(DEV) for k, v in inp.items()}
+    m, r = torch.from_numpy(mean).to(DEV), torch.from_numpy(rstd).to(DEV)
+    ref = [o.clone() for o in rn.ln_backward(dev["dy"], dev["x"], m, r, dev["gamma"])]
+    for over in ("dy", "x"):
+        t = {k: dev[k].clone() for k in ("dy", "x")}
+        out = rn.ln_backward(t["dy"], t["x"], m, r, dev["gamma"], dx=t[over])
+        torch.cuda.synchronize()
+        assert out[0].data_ptr() == t[over].data_ptr()
+        check_dx(out[0], oracle.layer_norm_backward(inp["dy"], inp["x"], inp["gamma"], mean=mean, rstd=rstd,
+                                                     eps=w.eps)["dx"], _scales(w, inp, mean, rstd, inp["gamma"])[0])
+        assert torch.equal(out[0].view(torch.uint8), ref[0].view(torch.uint8))
+
+
 @pytest.mark.parametrize("op,dtype,rows,N,gamma", [("ln", "bf16", 96, 65536, True), ("ln", "fp32", 40, 40001, True),
                                                    ("rms", "fp16", 64, 32768, True), ("ln", "fp16", 48, 24576, False),
                                                    ("rms", "bf16", 33, 16392, False)])

@@ -405,13 +405,19 @@ def test_backward_entry_points_reject_before_launch():
 
 def test_plan_split_rows():
     f32, bf16 = torch.float32, torch.bfloat16
-    # one 16-byte record per 8192-element segment (enough for both split-row variants)
+    # room for either split-row form: the two launches keep one 16-byte record per
+    # 8192-element segment; the one pass a 256-byte header and four 64-bit words per 32 KiB
+    # chunk segment (rows of whole chunks)
     need = rn.forward_workspace_bytes("ln", 64, 65536, f32)
-    assert need == 64 * 8 * 16
+    assert need == 256 + 64 * 8 * 32
     assert rn.forward_workspace_bytes("ln", 64, 16384, f32) == 0  # fits one workgroup
-    assert rn.forward_workspace_bytes("ln", 64, 16385, bf16) == 64 * 3 * 16
-    assert rn.forward_workspace_bytes("ln", 64, 65537, bf16) == 64 * 9 * 16
+    assert rn.forward_workspace_bytes("ln", 64, 16385, bf16) == max(64 * 3 * 16, 256 + 64 * 2 * 32)
+    assert rn.forward_workspace_bytes("ln", 64, 65537, bf16) == max(64 * 9 * 16, 256 + 64 * 5 * 32)
+    assert rn.forward_workspace_bytes("ln", 64, 131072, bf16) == 256 + 64 * 8 * 32
     assert rn.forward_workspace_bytes("ln", 0, 65536, f32) == 0
+    # the two-launch form needs only its records: a workspace of that size still splits rows
+    st, info = rn.plan("ln", 64, 65536, f32, workspace_bytes=64 * 8 * 16)
+    assert st == OK and info["variant"] == "wide"
     # whole 16-byte chunks: segments of 2048 chunks
     st, info = rn.plan("ln", 64, 65536, f32, workspace_bytes=need)
     assert st == OK and info["variant"] == "wide" and info["grid_blocks"] == 64 * 8 and info["exact"]
@@ -434,9 +440,11 @@ def test_plan_split_rows():
         assert st == OK and info["variant"] == "wide_element", (N, info)
         assert info["grid_blocks"] == 8 * S and info["block_threads"] == 512 and info["chunks_per_lane"] == 16
         assert info["exact"] == (N % 8192 == 0)
-        assert rn.plan("ln", 8, N, dt, workspace_bytes=ws - 16, ptrs=ptrs, strides=strides)[1]["variant"] == "general"
+        # below the two-launch form's records (one per 8192 elements): no split rows
+        assert rn.plan("ln", 8, N, dt, workspace_bytes=8 * S * 16 - 16, ptrs=ptrs,
+                       strides=strides)[1]["variant"] == "general"
     # too small a workspace: the general kernel (auto) or an error (forced)
-    assert rn.plan("ln", 64, 65536, f32, workspace_bytes=need - 16)[1]["variant"] == "general"
+    assert rn.plan("ln", 64, 65536, f32, workspace_bytes=64 * 8 * 16 - 16)[1]["variant"] == "general"
     assert rn.plan("ln", 64, 65536, f32, variant="wide")[0] == WORKSPACE
     assert rn.plan("ln", 64, 65537, f32, variant="wide_element")[0] == WORKSPACE
     assert rn.plan("ln", 64, 4096, f32, variant="wide", workspace_bytes=1 << 20)[0] == UNSUP

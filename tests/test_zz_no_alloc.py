@@ -102,7 +102,7 @@ def test_no_alloc_rejects_shapes_beyond_the_scratch_before_any_launch():
                                   None, 1 << 20, 1 << 17, ctypes.c_float(1e-5), 0, None, None) == SCRATCH
     # exactly at the limit the size check passes (the argument checks of rn_forward_ex follow:
     # a NULL x is reported as such, still before any launch)
-    rows = (16 << 20) // 16 // 8
+    rows = ((16 << 20) - 256) // (8 * 32)  # one-pass layout: 256-byte header, 32 bytes per segment record
     assert int(LIB.rn_forward_workspace_bytes(0, rows, 65536, 0)) == 16 << 20
     assert LIB.rn_forward_noalloc(0, None, None, None, None, ctypes.c_void_p(1 << 40), None, None, None, rows, 65536,
                                   ctypes.c_float(1e-5), 0, None, None) == 1
