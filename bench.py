@@ -54,6 +54,10 @@ The CPU baseline times the fp64 oracle (oracle/) on the same workload on the hos
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--cache cold|hot] [--replay-ms MS]
        python bench.py --ceiling-sweep      (every geometry of the copy kernel at the ceiling sizes)
        python bench.py --copy-calibration   (plain copy of known size, for counter scaling)
+       python bench.py --plan-sweep --steps 20 --replay-ms 40   (automatic launch plans against
+                                            every built alternative, JSON)
+       python bench.py --plan-sweep-report SWEEP.json [--trace DIR]   (its markdown tables)
+       python bench.py --trace-summary DIR  (kernels per roctx range of a rocprofv3 trace of this script)
 """
 
 import argparse
@@ -173,19 +177,21 @@ def kernel_name(w, plan):
             f"V={plan['chunks_per_lane']} per lane, {plan['rows_per_block']} row group(s) per workgroup, {mode})")
 
 
-def launch(rn, w, s):
+def launch(rn, w, s, tuning=None):
+    """One call of workload `w` on buffer set `s` (forward ops: with an optional tuning)."""
+    kw = {} if tuning is None else {"tuning": tuning}
     if w.op == "ln":
-        rn.ln_forward(s["x"], s.get("gamma"), s.get("beta"), w.eps, out=s["y"], mean=s["mean"], rstd=s["rstd"])
+        rn.ln_forward(s["x"], s.get("gamma"), s.get("beta"), w.eps, out=s["y"], mean=s["mean"], rstd=s["rstd"], **kw)
     elif w.op == "rms":
-        rn.rms_norm(s["x"], s.get("weight"), w.eps, out=s["y"], rstd=s["rstd"])
+        rn.rms_norm(s["x"], s.get("weight"), w.eps, out=s["y"], rstd=s["rstd"], **kw)
     elif w.op == "fused_add_rms":
         rn.fused_add_rms_norm(s["x"], s["residual"], s.get("weight"), w.eps, out=s["y"],
-                              residual_out=s["residual_out"], rstd=s["rstd"])
+                              residual_out=s["residual_out"], rstd=s["rstd"], **kw)
     elif w.op == "fused_add_ln":
         rn.fused_add_layer_norm(s["x"], s["residual"], s.get("gamma"), s.get("beta"), w.eps, out=s["y"],
-                                residual_out=s["residual_out"], mean=s["mean"], rstd=s["rstd"])
+                                residual_out=s["residual_out"], mean=s["mean"], rstd=s["rstd"], **kw)
     elif w.op == "softmax":
-        rn.softmax_forward(s["x"], out=s["y"])
+        rn.softmax_forward(s["x"], out=s["y"], **kw)
     elif w.op == "ln_bwd":
         rn.ln_backward(s["dy"], s["x"], s["mean"], s["rstd"], s.get("gamma"), dx=s["dx"], workspace=s["ws"])
     elif w.op == "rms_bwd":
@@ -568,6 +574,248 @@ def copy_calibration(dev):
     log(f"[bench] copy calibration: 10 + 10 copies of {n} bytes")
 
 
+# ---------------------------------------------------------------------------------------
+# Launch-plan sweep: for each shape, the automatic plan against every alternative the library
+# builds (rn_forward_tuned: waves per row, grid per row or persistent, the prefetching or the
+# looping instance, the persistent grid), each timed under the lines' cold protocol. Each
+# candidate runs inside a roctx range "bench:plan:<shape>:<candidate>", so that a rocprofv3
+# kernel trace of the same run shows the instance and grid each one launched
+# (--trace-summary).
+# ---------------------------------------------------------------------------------------
+
+PLAN_PRIME_MS = 30.0  # each candidate's own launches before its timed replays
+
+
+def plan_sweep_shapes():
+    import workloads
+
+    c5, fused, fln, sm = workloads.C5, workloads.C4_FP16, workloads.FUSED_LN, workloads.SOFTMAX
+    ln4k = lambda r: c5.scaled(rows=r, N=4096, name=f"ln_bf16_{r}x4096")  # noqa: E731
+    return [
+        (c5, "rows of 2048 chunks (8 waves x 4 chunks) with parameters, many rows: the looping instance on "
+             "two workgroups per CU"),
+        (c5.scaled(rows=16384, N=8192, name="ln_bf16_16384x8192"), "4-wave rows with parameters, many rows: "
+                                                                   "the looping instance"),
+        (ln4k(2048), "2-wave rows, few rows per resident workgroup: one workgroup per row block"),
+        (ln4k(16384), "2-wave rows, 1 to 3 row blocks per resident workgroup: half as many workgroups, "
+                      "prefetching"),
+        (ln4k(32768), "2-wave rows, more than 3 row blocks per resident workgroup: one workgroup per row "
+                      "block"),
+        (fused.scaled(rows=2048, name="fused_fp16_2048x4096"), "fused add + RMSNorm (two row tensors), few rows"),
+        (fused.scaled(rows=8192, name="fused_fp16_8192x4096"), "fused add + RMSNorm, more rows"),
+        (fused.scaled(rows=16384, N=8192, name="fused_fp16_16384x8192"), "fused add + RMSNorm, 4-wave rows "
+                                                                         "with a weight, many rows"),
+        (fln.scaled(rows=8192, name="fused_ln_bf16_8192x4096"), "fused add + LayerNorm, 2-wave rows"),
+        (fln.scaled(rows=16384, N=8192, name="fused_ln_bf16_16384x8192"), "fused add + LayerNorm, 4-wave rows "
+                                                                          "with parameters, many rows"),
+        (fln.scaled(rows=4096, N=16384, name="fused_ln_bf16_4096x16384"), "fused add + LayerNorm, 8-wave rows "
+                                                                          "with parameters"),
+        (sm.scaled(rows=8192, name="softmax_fp32_8192x4096"), "softmax (no parameters)"),
+        (workloads.C3, "RMSNorm fp16 2048 x 4096"),
+        (workloads.C1.scaled(rows=16384, name="ln_fp32_16384x1024"), "one-wave rows, four rows per "
+                                                                     "workgroup"),
+        (ln4k(128), "persistent threshold: 128 rows (widened to 4 waves: 128 row blocks)"),
+        (ln4k(256), "persistent threshold: 256 rows (widened to 4 waves: 256 row blocks)"),
+        (ln4k(384), "persistent threshold: 384 rows (widened to 4 waves: 384 row blocks)"),
+        (ln4k(1024), "persistent threshold: 1024 rows (2 waves: 512 row blocks)"),
+        (workloads.C4_FP16, "persistent threshold: fused add + RMSNorm fp16 256 rows"),
+        (fln.scaled(rows=384, name="fused_ln_bf16_384x4096"), "persistent threshold: fused add + LayerNorm "
+                                                              "384 rows"),
+        (sm.scaled(rows=256, name="softmax_fp32_256x4096"), "persistent threshold: softmax 256 rows"),
+        (c5.scaled(rows=256, name="ln_bf16_256x16384"), "persistent threshold: 8-wave rows, 256 rows"),
+        (c5.scaled(rows=512, name="ln_bf16_512x16384"), "persistent threshold: 8-wave rows, 512 rows"),
+    ]
+
+
+def _plan_ptrs(w, s0):
+    ptrs = {k: s0[k].data_ptr() for k in ("x", "residual", "gamma", "beta", "weight", "y", "residual_out", "mean",
+                                          "rstd") if k in s0}
+    if "weight" in ptrs:
+        ptrs["gamma"] = ptrs.pop("weight")
+    if w.op == "softmax":
+        ptrs.pop("mean", None)
+        ptrs.pop("rstd", None)
+    if w.op in ("rms", "fused_add_rms"):
+        ptrs.pop("mean", None)
+    return ptrs
+
+
+def plan_candidates(rn, w, s0, cus):
+    """(label, tuning, plan) for the automatic plan and each distinct built alternative."""
+    import workloads
+
+    td = workloads.TORCH_DTYPES[w.dtype]
+    ptrs = _plan_ptrs(w, s0)
+    st, auto = rn.plan(w.op, w.rows, w.N, td, ptrs=ptrs, eps=w.eps)
+    if st != 0:
+        raise RuntimeError(f"{w.name}: automatic plan failed ({rn.STATUS.get(st, st)})")
+    blocks = auto["grid_blocks"]
+    tries = [{"waves_per_row": W} for W in (1, 2, 4, 8, 16)]
+    tries += [{"waves_per_row": W, "persistent": 0} for W in (1, 2, 4, 8, 16)]
+    if auto["persistent"]:
+        grids = sorted({g for g in [k * cus for k in (1, 2, 3, 4, 6, 8)] + [(blocks + 1) // 2, blocks]
+                        if 0 < g <= blocks})
+        tries += [{"prefetch": pf, "grid_blocks": g} for pf in (1, 0) for g in grids]
+    else:
+        tries.append({"persistent": 1})
+    key = lambda i, t: (i["waves_per_row"], i["chunks_per_lane"], i["rows_per_block"], i["persistent"],  # noqa
+                        i["grid_blocks"], (t or {}).get("prefetch", -1))
+    out, seen = [("auto", None, auto)], {key(auto, None)}
+    for t in tries:
+        st, info = rn.plan(w.op, w.rows, w.N, td, ptrs=ptrs, eps=w.eps, tuning=t)
+        if st != 0 or key(info, t) in seen:
+            continue
+        seen.add(key(info, t))
+        label = f"W{info['waves_per_row']}xV{info['chunks_per_lane']}"
+        if not info["persistent"]:
+            label += " grid per row"
+        else:
+            label += " persistent"
+            if "prefetch" in t:
+                label += (" prefetching" if t["prefetch"] == 1 else " looping") + f" grid {info['grid_blocks']}"
+        out.append((label, t, info))
+    return out
+
+
+def plan_sweep(dev, steps):
+    import torch
+
+    import row_wise_normalization_fp32_amd as rn
+    import workloads
+
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    res = {}
+    for w, why in plan_sweep_shapes():
+        nbytes = workloads.algorithmic_bytes(w.op, w.rows, w.N, w.elem_bytes, with_stats=True)
+        set_bytes = SET_TENSORS[w.op] * w.rows * w.N * w.elem_bytes
+        nsets = max(MIN_COLD_SETS, min(64, math.ceil(COLD_FOOTPRINT / set_bytes)))
+        sets = make_sets(w, nsets, dev)
+        cands = plan_candidates(rn, w, sets[0], cus)
+        log(f"[bench] plan sweep {w.name}: {len(cands)} plans, {nsets} buffer sets")
+        rows = []
+        for label, tuning, info in cands:
+            step = lambda i: launch(rn, w, sets[i % nsets], tuning)  # noqa: E731
+            with line_marker(f"plan:{w.name}:{label}"):
+                prime_gpu(step, ms=PLAN_PRIME_MS)
+                gt = graph_time_fn(step, steps)
+            if gt is None:
+                continue
+            sp = spread({"repeats_ms": gt["repeats_ms"]})
+            us = gt["event_ms"] * 1e3
+            rows.append({"label": label, "tuning": tuning, "plan": info, "us": round(us, 3),
+                         "q1_us": round(sp["q1_ms"] * 1e3, 3), "q3_us": round(sp["q3_ms"] * 1e3, 3),
+                         "replays": sp["n"], "pct_of_peak": round(100.0 * nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2)})
+        best = min(r["us"] for r in rows)
+        for r in rows:
+            r["vs_best"] = round(r["us"] / best, 4)
+        auto = next(r for r in rows if r["label"] == "auto")
+        res[w.name] = {"op": w.op, "dtype": w.dtype, "rows": w.rows, "N": w.N, "bytes": nbytes, "why": why,
+                       "planner_vs_best": auto["vs_best"],
+                       "planner_rank": 1 + sum(r["us"] < auto["us"] for r in rows), "candidates": rows}
+        log(f"[bench] plan sweep {w.name}: planner {auto['us']:.2f} us, best {best:.2f} us "
+            f"({auto['vs_best']:.3f}x)")
+        del sets
+        torch.cuda.empty_cache()
+    return {"cus": cus, "steps": steps, "replay_ms": MIN_REPLAY_MS, "prime_ms": PLAN_PRIME_MS, "shapes": res}
+
+
+def trace_by_range(trace_dir):
+    """Kernel dispatches of a rocprofv3 --kernel-trace --marker-trace run, grouped by the
+    roctx range ("bench:...") whose host-time span contains each dispatch's start: per range,
+    per kernel, (dispatches, median duration in us of the last 100, workgroups). torch's own
+    helper kernels are left out."""
+    import bisect
+    import csv
+    import statistics
+
+    marks = [r for r in csv.DictReader(open(os.path.join(trace_dir, "trace_marker_api_trace.csv")))
+             if r["Function"].startswith("bench:")]
+    marks = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Function"][6:]) for r in marks)
+    starts = [m[0] for m in marks]
+    by = {m[2]: {} for m in marks}
+    kt = os.path.join(trace_dir, "trace_kernel_trace.csv")
+    if not os.path.exists(kt) and os.path.exists(kt + ".gz"):  # kept compressed
+        import gzip
+
+        kfile = gzip.open(kt + ".gz", "rt")
+    else:
+        kfile = open(kt)
+    for r in csv.DictReader(kfile):
+        t = int(r["Start_Timestamp"])
+        i = bisect.bisect_right(starts, t) - 1
+        if i < 0 or t > marks[i][1]:
+            continue
+        # the template name: no return type, no argument list
+        name = re.sub(r"\(.*$", "", r["Kernel_Name"].replace("void ", "").replace("(anonymous namespace)::", ""))
+        if name.startswith("at::") or name.startswith("__amd"):
+            continue
+        wg = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+        wg *= int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]) // max(1, int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"]))
+        by[marks[i][2]].setdefault((name, wg), []).append((t, int(r["End_Timestamp"]) - t))
+    out = {}
+    for rng, ks in by.items():
+        rowsk = []
+        for (name, wg), v in ks.items():
+            v.sort()
+            rowsk.append((v[0][0], name, len(v), statistics.median(d for _, d in v[-100:]) / 1e3, wg))
+        out[rng] = [(n, c, us, wg) for _, n, c, us, wg in sorted(rowsk)]
+    return out
+
+
+def trace_summary(trace_dir):
+    """Markdown table of trace_by_range: kernels launched at least 20 times in a range."""
+    lines = ["| range | kernel (template arguments) | workgroups | dispatches | median us (last 100) |",
+             "|---|---|---|---|---|"]
+    for rng, ks in trace_by_range(trace_dir).items():
+        for name, c, us, wg in ks:
+            if c >= 20:
+                lines.append(f"| {rng} | `{name}` | {wg} | {c} | {us:.2f} |")
+    return "\n".join(lines)
+
+
+def plan_sweep_report(sweep, trace_dir=None, top=0):
+    """Markdown tables of a --plan-sweep result (and, with its trace, the kernel instance and
+    grid each candidate launched with their traced durations); top > 0: per shape only the
+    `top` fastest plans, the planner's and the slowest."""
+    tr = trace_by_range(trace_dir) if trace_dir else {}
+    out = []
+    ratios = []
+    for name, r in sweep["shapes"].items():
+        out.append(f"### {name} ({r['op']}, {r['dtype']}, {r['rows']} x {r['N']}): {r['why']}")
+        out.append("")
+        out.append(f"Planner: {r['planner_vs_best']:.3f}x the fastest plan (rank {r['planner_rank']} of "
+                   f"{len(r['candidates'])}).")
+        out.append("")
+        hdr = "| plan | µs (events, median) | % of 8 TB/s | vs fastest |"
+        sep = "|---|---|---|---|"
+        if tr:
+            hdr += " kernel instance (trace) | workgroups | µs (trace) |"
+            sep += "---|---|---|"
+        out += [hdr, sep]
+        ratios.append(r["planner_vs_best"])
+        cands = sorted(r["candidates"], key=lambda c: c["us"])
+        if top > 0:
+            cands = [c for i, c in enumerate(cands) if i < top or i == len(cands) - 1 or c["label"] == "auto"]
+        for c in cands:
+            lab = "**planner** (" + _plan_label(c["plan"]) + ")" if c["label"] == "auto" else c["label"]
+            line = f"| {lab} | {c['us']:.2f} | {c['pct_of_peak']:.1f} | {c['vs_best']:.3f} |"
+            if tr:
+                ks = [k for k in tr.get(f"plan:{name}:{c['label']}", []) if k[1] >= 20]
+                line += (" " + " + ".join(f"`{k[0]}`" for k in ks) + " | " + " + ".join(str(k[3]) for k in ks) +
+                         " | " + f"{sum(k[2] for k in ks):.2f} |")
+            out.append(line)
+        out.append("")
+    gm = math.exp(sum(math.log(x) for x in ratios) / len(ratios)) if ratios else float("nan")
+    head = [f"Planner against the fastest built plan over {len(ratios)} shapes: geometric mean "
+            f"{gm:.3f}x, worst {max(ratios):.3f}x.", ""]
+    return "\n".join(head + out)
+
+
+def _plan_label(info):
+    s = f"W{info['waves_per_row']}xV{info['chunks_per_lane']}"
+    return s + (" persistent, grid rule" if info["persistent"] else " grid per row")
+
+
 def _more():
     import workloads
 
@@ -611,6 +859,16 @@ def main():
     ap.add_argument("--ceiling-sweep", action="store_true",
                     help="time every geometry of the streaming copy kernel at the ceiling sizes, print JSON, exit")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-copy ceiling lines")
+    ap.add_argument("--plan-sweep", action="store_true",
+                    help="time the automatic launch plan of several shapes against every built alternative, "
+                         "print JSON, exit")
+    ap.add_argument("--plan-sweep-report", metavar="JSON",
+                    help="markdown tables of a --plan-sweep result (with --trace DIR: and of its kernel trace)")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="markdown table of a rocprofv3 --kernel-trace --marker-trace run of this script")
+    ap.add_argument("--trace", metavar="DIR", help="the kernel trace of the --plan-sweep run (for the report)")
+    ap.add_argument("--top", type=int, default=0, help="report: per shape the fastest N plans, the planner's and "
+                                                       "the slowest")
     ap.add_argument("--prime-ms", type=float, default=PRIME_MS,
                     help="the workload's own launches before each line (shorter for counter runs)")
     ap.add_argument("--replay-ms", type=float, default=MIN_REPLAY_MS,
@@ -623,6 +881,14 @@ def main():
               "rows are independent, so more GPUs would each run the same kernel on their own rows.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return
+    if args.plan_sweep_report:
+        sweep = json.loads(open(args.plan_sweep_report).read().strip().splitlines()[-1])["plan_sweep"]
+        print(plan_sweep_report(sweep, args.trace, args.top))
+        return
 
     import torch
 
@@ -637,6 +903,9 @@ def main():
         return
     if args.ceiling_sweep:
         print(json.dumps({"ceiling_sweep": ceiling_sweep(args.steps, dev)}), flush=True)
+        return
+    if args.plan_sweep:
+        print(json.dumps({"plan_sweep": plan_sweep(dev, args.steps)}), flush=True)
         return
 
     w = workloads.C5

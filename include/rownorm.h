@@ -246,6 +246,42 @@ int rn_forward_noalloc(int op, const void* x, const void* residual, const void* 
                        void* residual_out, float* mean, float* rstd, int64_t rows, int64_t N, float eps, int dtype,
                        const rn_row_strides* strides, hipStream_t stream);
 
+/*
+ * Launch choices that replace the planner's own (rn_forward_tuned, rn_plan_tuned): for
+ * measuring the automatic plan against its alternatives on a given device, and for
+ * autotuning. A field at its "automatic" value (0, or -1 where stated) changes nothing. They
+ * apply to the vectorized variants (RN_VARIANT_WAVE / RN_VARIANT_WORKGROUP, or
+ * RN_VARIANT_AUTO where it picks one of them); a tuning that changes anything for another
+ * variant returns RN_ERR_UNSUPPORTED.
+ */
+typedef struct rn_tuning {
+    int waves_per_row;    /* 1, 2, 4, 8 or 16 wavefronts per row (0: automatic); rows per workgroup
+                             follow (4 / waves_per_row up to 4 waves, else 1) */
+    int chunks_per_lane;  /* 16-byte chunks each lane holds, 64 * waves_per_row * chunks_per_lane
+                             covering the row (0: the fewest power of two that covers it) */
+    int persistent;       /* 1: persistent launch (rows that exactly fill the row group, up to 4096
+                             chunks), 0: one workgroup per row block, -1: automatic */
+    int prefetch;         /* persistent launches: 1 the instance that loads a workgroup's next row
+                             before it reduces the current one, 0 the one that does not, -1: the
+                             grid rule's choice. Rows of 16 waves, and one-wave rows of 8 or more
+                             chunks per lane, have only the second; of the other shapes only rows
+                             of 4 or more waves with parameters have both */
+    int64_t grid_blocks;  /* workgroups to launch (at most one per row block; each loops over the
+                             row blocks left), 0: automatic */
+} rn_tuning;
+
+/*
+ * rn_forward_ex with a tuning (nullable: then exactly rn_forward_ex). Results are those of
+ * rn_forward_ex, bit for bit, when only persistent, prefetch or grid_blocks change; another
+ * row-group shape changes the order of the fp32 partial sums, not the tolerance the results
+ * meet. RN_ERR_UNSUPPORTED when the library holds no kernel for the resulting shape (nothing
+ * is enqueued then), or for a tuning outside the ranges above.
+ */
+int rn_forward_tuned(int op, const void* x, const void* residual, const void* gamma, const void* beta, void* y,
+                     void* residual_out, float* mean, float* rstd, int64_t rows, int64_t N, float eps, int dtype,
+                     const rn_row_strides* strides, int variant, const rn_tuning* tuning, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace bytes rn_forward_ex needs for the split-row paths of this shape, 0 when N <= 16384
  * (such rows are never split). Otherwise the larger of the two-launch layout, rows *
  * ceil(N / 8192) * 16 bytes (16-byte records), and the one-pass layout, 256 + rows *
@@ -341,6 +377,14 @@ int rn_plan(int op, const void* x, const void* residual, const void* gamma, cons
             const void* residual_out, const void* mean, const void* rstd, int64_t rows, int64_t N, float eps,
             int dtype, int variant, const rn_row_strides* strides, const void* workspace, size_t workspace_bytes,
             rn_plan_info* out);
+
+/* rn_plan with a tuning (see rn_tuning), also host only: the plan rn_forward_tuned would launch
+ * (grid_blocks: the tuning's grid when it sets one), and RN_ERR_UNSUPPORTED when the library
+ * holds no kernel of that shape. */
+int rn_plan_tuned(int op, const void* x, const void* residual, const void* gamma, const void* beta, const void* y,
+                  const void* residual_out, const void* mean, const void* rstd, int64_t rows, int64_t N, float eps,
+                  int dtype, int variant, const rn_row_strides* strides, const rn_tuning* tuning,
+                  const void* workspace, size_t workspace_bytes, rn_plan_info* out);
 
 /* The same for a backward call (op: RN_OP_LAYER_NORM or RN_OP_RMS_NORM); grid_blocks is the
  * row kernel's workgroup count before the launch caps it at what the device keeps resident

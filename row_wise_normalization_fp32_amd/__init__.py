@@ -13,6 +13,11 @@ Function names follow the C ABI: ``ln_forward``, ``rms_norm``, ``fused_add_rms_n
 [rows, N] with rows the product of the leading dimensions; they must be contiguous, except
 that a 2-D tensor may have a row stride larger than N (e.g. a column slice of a wider
 buffer), which the kernels read and write in place.
+
+Every forward function also takes ``tuning=``, a dict of the fields of ``rn_tuning``
+(waves_per_row, chunks_per_lane, persistent, prefetch, grid_blocks), to launch a
+caller-chosen plan instead of the automatic one: for autotuning, and for measuring the
+planner's choices against their alternatives.
 """
 
 from __future__ import annotations
@@ -50,6 +55,18 @@ class PlanInfo(ctypes.Structure):
                 ("lds_bytes", _ci), ("pairs", _ci)]
 
 
+class Tuning(ctypes.Structure):
+    _fields_ = [("waves_per_row", _ci), ("chunks_per_lane", _ci), ("persistent", _ci), ("prefetch", _ci),
+                ("grid_blocks", _i64)]
+
+
+_lib.rn_forward_tuned.argtypes = [_ci, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci,
+                                  ctypes.POINTER(RowStrides), _ci, ctypes.POINTER(Tuning), _vp, ctypes.c_size_t, _vp]
+_lib.rn_forward_tuned.restype = _ci
+_lib.rn_plan_tuned.argtypes = [_ci, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci, _ci,
+                               ctypes.POINTER(RowStrides), ctypes.POINTER(Tuning), _vp, ctypes.c_size_t,
+                               ctypes.POINTER(PlanInfo)]
+_lib.rn_plan_tuned.restype = _ci
 _lib.rn_forward_ex.argtypes = [_ci, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _f32, _ci,
                                ctypes.POINTER(RowStrides), _ci, _vp, ctypes.c_size_t, _vp]
 _lib.rn_forward_ex.restype = _ci
@@ -198,8 +215,23 @@ _ELEM_BYTES = {torch.float32: 4, torch.float16: 2, torch.bfloat16: 2}
 _NO_STRIDES = RowStrides(0, 0, 0, 0)
 
 
+_TUNING_DEFAULTS = {"waves_per_row": 0, "chunks_per_lane": 0, "persistent": -1, "prefetch": -1, "grid_blocks": 0}
+
+
+def _tuning(tuning: Optional[dict]):
+    """An rn_tuning from a dict of its fields (missing fields: automatic)."""
+    if tuning is None:
+        return None
+    bad = set(tuning) - set(_TUNING_DEFAULTS)
+    if bad:
+        raise ValueError(f"unknown tuning fields {sorted(bad)}; known: {sorted(_TUNING_DEFAULTS)}")
+    f = dict(_TUNING_DEFAULTS)
+    f.update({k: int(v) for k, v in tuning.items()})
+    return Tuning(**f)
+
+
 def _call(op: str, what: str, x, residual, gamma, beta, y, ro, mean, rstd, rows, N, eps, strides, variant, stream,
-          workspace=None):
+          workspace=None, tuning=None):
     # Host time per call matters for small launches: the common case (dense rows, current
     # device, no workspace) takes no context manager and builds no ctypes structure.
     st_obj = _NO_STRIDES if not any(strides) else RowStrides(*strides)
@@ -214,13 +246,17 @@ def _call(op: str, what: str, x, residual, gamma, beta, y, ro, mean, rstd, rows,
             workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     if workspace is not None:
         ws_bytes = workspace.numel() * workspace.element_size()
-    args = (OPS[op], _ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(ro), _ptr(mean), _ptr(rstd),
-            rows, N, float(eps), DTYPE_CODE[x.dtype], ctypes.byref(st_obj), v, _ptr(workspace), ws_bytes)
+    head = (OPS[op], _ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(ro), _ptr(mean), _ptr(rstd),
+            rows, N, float(eps), DTYPE_CODE[x.dtype], ctypes.byref(st_obj), v)
+    if tuning is None:
+        fn, args = _lib.rn_forward_ex, head + (_ptr(workspace), ws_bytes)
+    else:
+        fn, args = _lib.rn_forward_tuned, head + (ctypes.byref(_tuning(tuning)), _ptr(workspace), ws_bytes)
     if x.get_device() == torch.cuda.current_device():
-        st = _lib.rn_forward_ex(*args, _stream(x, stream))
+        st = fn(*args, _stream(x, stream))
     else:
         with torch.cuda.device(x.device):
-            st = _lib.rn_forward_ex(*args, _stream(x, stream))
+            st = fn(*args, _stream(x, stream))
     if st != 0:
         raise RowNormError(st, what)
 
@@ -232,7 +268,7 @@ def _new_like(x: torch.Tensor) -> torch.Tensor:
 def ln_forward(x: torch.Tensor, gamma: Optional[torch.Tensor] = None, beta: Optional[torch.Tensor] = None,
                eps: float = 1e-5, *, out: Optional[torch.Tensor] = None, mean: Optional[torch.Tensor] = None,
                rstd: Optional[torch.Tensor] = None, return_stats: bool = False, variant: Union[str, int] = "auto",
-               stream=None):
+               stream=None, tuning: Optional[dict] = None):
     """LayerNorm forward over the last dimension.
 
     Returns ``y`` (same shape and dtype as ``x``), or ``(y, mean, rstd)`` with fp32
@@ -248,7 +284,7 @@ def ln_forward(x: torch.Tensor, gamma: Optional[torch.Tensor] = None, beta: Opti
     mean = _stats("mean", mean, x, rows, want)
     rstd = _stats("rstd", rstd, x, rows, want)
     _call("ln", "ln_forward", x, None, gamma, beta, y, None, mean, rstd, rows, N, eps, (ldx, 0, ldy, 0), variant,
-          stream)
+          stream, tuning=tuning)
     return (y, mean, rstd) if want else y
 
 
@@ -258,7 +294,7 @@ layer_norm = ln_forward
 
 def rms_norm(x: torch.Tensor, weight: Optional[torch.Tensor] = None, eps: float = 1e-6, *,
              out: Optional[torch.Tensor] = None, rstd: Optional[torch.Tensor] = None, return_rstd: bool = False,
-             variant: Union[str, int] = "auto", stream=None):
+             variant: Union[str, int] = "auto", stream=None, tuning: Optional[dict] = None):
     """RMSNorm forward over the last dimension. Returns ``y`` or ``(y, rstd)``."""
     rows, N, ldx = _prep(x)
     _check_vector("weight", weight, x)
@@ -267,14 +303,15 @@ def rms_norm(x: torch.Tensor, weight: Optional[torch.Tensor] = None, eps: float 
     want = return_rstd or rstd is not None
     rstd = _stats("rstd", rstd, x, rows, want)
     _call("rms", "rms_norm", x, None, weight, None, y, None, None, rstd, rows, N, eps, (ldx, 0, ldy, 0), variant,
-          stream)
+          stream, tuning=tuning)
     return (y, rstd) if want else y
 
 
 def fused_add_rms_norm(x: torch.Tensor, residual: torch.Tensor, weight: Optional[torch.Tensor] = None,
                        eps: float = 1e-6, *, out: Optional[torch.Tensor] = None,
                        residual_out: Optional[torch.Tensor] = None, rstd: Optional[torch.Tensor] = None,
-                       return_rstd: bool = False, variant: Union[str, int] = "auto", stream=None):
+                       return_rstd: bool = False, variant: Union[str, int] = "auto", stream=None,
+                       tuning: Optional[dict] = None):
     """Fused residual add + RMSNorm.
 
     ``residual_out = x + residual`` rounded to the dtype; ``y = rms_norm(residual_out) *
@@ -290,7 +327,7 @@ def fused_add_rms_norm(x: torch.Tensor, residual: torch.Tensor, weight: Optional
     want = return_rstd or rstd is not None
     rstd = _stats("rstd", rstd, x, rows, want)
     _call("fused_add_rms", "fused_add_rms_norm", x, residual, weight, None, y, ro, None, rstd, rows, N, eps,
-          (ldx, ldr, ldy, ldo), variant, stream)
+          (ldx, ldr, ldy, ldo), variant, stream, tuning=tuning)
     return (y, ro, rstd) if want else (y, ro)
 
 
@@ -298,7 +335,7 @@ def fused_add_layer_norm(x: torch.Tensor, residual: torch.Tensor, gamma: Optiona
                          beta: Optional[torch.Tensor] = None, eps: float = 1e-5, *, out: Optional[torch.Tensor] = None,
                          residual_out: Optional[torch.Tensor] = None, mean: Optional[torch.Tensor] = None,
                          rstd: Optional[torch.Tensor] = None, return_stats: bool = False,
-                         variant: Union[str, int] = "auto", stream=None):
+                         variant: Union[str, int] = "auto", stream=None, tuning: Optional[dict] = None):
     """Fused residual add + LayerNorm.
 
     ``residual_out = x + residual`` rounded to the dtype; ``y = layer_norm(residual_out)``.
@@ -316,13 +353,13 @@ def fused_add_layer_norm(x: torch.Tensor, residual: torch.Tensor, gamma: Optiona
     mean = _stats("mean", mean, x, rows, want)
     rstd = _stats("rstd", rstd, x, rows, want)
     _call("fused_add_ln", "fused_add_layer_norm", x, residual, gamma, beta, y, ro, mean, rstd, rows, N, eps,
-          (ldx, ldr, ldy, ldo), variant, stream)
+          (ldx, ldr, ldy, ldo), variant, stream, tuning=tuning)
     return (y, ro, mean, rstd) if want else (y, ro)
 
 
 def softmax_forward(x: torch.Tensor, *, out: Optional[torch.Tensor] = None, row_max: Optional[torch.Tensor] = None,
                     row_sum: Optional[torch.Tensor] = None, return_stats: bool = False,
-                    variant: Union[str, int] = "auto", stream=None):
+                    variant: Union[str, int] = "auto", stream=None, tuning: Optional[dict] = None):
     """Softmax over the last dimension. Returns ``y``, or ``(y, row_max, row_sum)`` with
     row_sum = sum(exp(x - row_max)) (fp32)."""
     rows, N, ldx = _prep(x)
@@ -332,7 +369,7 @@ def softmax_forward(x: torch.Tensor, *, out: Optional[torch.Tensor] = None, row_
     row_max = _stats("row_max", row_max, x, rows, want)
     row_sum = _stats("row_sum", row_sum, x, rows, want)
     _call("softmax", "softmax_forward", x, None, None, None, y, None, row_max, row_sum, rows, N, 0.0,
-          (ldx, 0, ldy, 0), variant, stream)
+          (ldx, 0, ldy, 0), variant, stream, tuning=tuning)
     return (y, row_max, row_sum) if want else y
 
 
@@ -449,12 +486,14 @@ def plan_backward(op: str, rows: int, N: int, dtype: torch.dtype, *, ptrs: Optio
 
 def plan(op: str, rows: int, N: int, dtype: torch.dtype, *, ptrs: Optional[dict] = None, eps: float = 1e-5,
          variant: Union[str, int] = "auto", strides: Optional[dict] = None,
-         workspace_bytes: int = 0) -> Tuple[int, dict]:
+         workspace_bytes: int = 0, tuning: Optional[dict] = None) -> Tuple[int, dict]:
     """Host-only launch plan (no GPU needed). ``ptrs`` maps buffer names (x, residual,
     gamma, beta, y, residual_out, mean, rstd) to integer addresses; missing required
     buffers default to 256-byte-aligned placeholders that never overlap. ``strides`` maps
     x / residual / y / residual_out to row strides in elements; ``workspace_bytes`` > 0
-    stands for a workspace of that size (the split-row path). Returns ``(status, info)``."""
+    stands for a workspace of that size (the split-row path); ``tuning`` (fields of
+    rn_tuning) gives the plan rn_forward_tuned would launch, with status RN_ERR_UNSUPPORTED
+    when no kernel of that shape is built. Returns ``(status, info)``."""
     s = torch.tensor([], dtype=dtype).element_size()
     ld = max([N] + list((strides or {}).values()))
     span = max(1, rows * ld * s)
@@ -469,11 +508,14 @@ def plan(op: str, rows: int, N: int, dtype: torch.dtype, *, ptrs: Optional[dict]
         p.update(ptrs)
     st_obj = RowStrides(**(strides or {}))
     info = PlanInfo()
-    st = _lib.rn_plan(OPS[op], p.get("x"), p.get("residual"), p.get("gamma"), p.get("beta"), p.get("y"),
-                      p.get("residual_out"), p.get("mean"), p.get("rstd"), rows, N, float(eps),
-                      DTYPE_CODE.get(dtype, 99), _variant(variant), ctypes.byref(st_obj),
-                      p.get("workspace", (1 << 47) if workspace_bytes else None), workspace_bytes,
-                      ctypes.byref(info))
+    head = (OPS[op], p.get("x"), p.get("residual"), p.get("gamma"), p.get("beta"), p.get("y"), p.get("residual_out"),
+            p.get("mean"), p.get("rstd"), rows, N, float(eps), DTYPE_CODE.get(dtype, 99), _variant(variant),
+            ctypes.byref(st_obj))
+    tail = (p.get("workspace", (1 << 47) if workspace_bytes else None), workspace_bytes, ctypes.byref(info))
+    if tuning is None:
+        st = _lib.rn_plan(*head, *tail)
+    else:
+        st = _lib.rn_plan_tuned(*head, ctypes.byref(_tuning(tuning)), *tail)
     return st, {"variant": VARIANT_NAMES.get(info.variant, info.variant), "waves_per_row": info.waves_per_row,
                 "rows_per_block": info.rows_per_block, "block_threads": info.block_threads,
                 "chunks_per_lane": info.chunks_per_lane, "grid_blocks": info.grid_blocks,

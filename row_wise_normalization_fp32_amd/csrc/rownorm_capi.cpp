@@ -65,7 +65,14 @@ struct Args {
     int64_t ldx, ldr, ldy, ldro;  // resolved row strides (elements)
     void* ws;                     // split-row workspace, nullable
     size_t ws_bytes;
+    const rn_tuning* tune;        // caller-chosen launch choices, nullable
 };
+
+// A tuning that changes anything (fields at their "automatic" values change nothing).
+bool tuned(const rn_tuning* t) {
+    return t != nullptr && (t->waves_per_row != 0 || t->chunks_per_lane != 0 || t->persistent != -1 ||
+                            t->prefetch != -1 || t->grid_blocks != 0);
+}
 
 // Split-row paths: rows longer than a workgroup's registers hold. Segments of 2048 16-byte
 // chunks (whole-chunk rows) or of 8192 elements (any rows); one 16-byte record per segment.
@@ -143,6 +150,15 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     const bool fused = is_fused(a.op);
     const bool ln = is_ln(a.op);
     const bool sm = a.op == RN_OP_SOFTMAX;
+    const bool tune = tuned(a.tune);
+    if (tune) {
+        const rn_tuning& t = *a.tune;
+        const int w = t.waves_per_row;
+        if (w != 0 && w != 1 && w != 2 && w != 4 && w != 8 && w != 16) return RN_ERR_UNSUPPORTED;
+        if (t.chunks_per_lane < 0 || t.chunks_per_lane > 64 || t.persistent < -1 || t.persistent > 1 ||
+            t.prefetch < -1 || t.prefetch > 1 || t.grid_blocks < 0)
+            return RN_ERR_UNSUPPORTED;
+    }
     plan->variant = rn::V_GENERAL;
     plan->waves_per_row = 0;
     plan->rows_per_block = 0;
@@ -255,6 +271,8 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
         else
             v = RN_VARIANT_GENERAL;
     }
+    // a tuning applies to the vectorized variants only
+    if (tune && !(v == RN_VARIANT_WAVE || v == RN_VARIANT_WORKGROUP)) return RN_ERR_UNSUPPORTED;
     if (v == RN_VARIANT_WIDE_ELEMENT) {
         if (N <= elem_cap) return RN_ERR_UNSUPPORTED;
         if (!ws_given) return RN_ERR_WORKSPACE;
@@ -344,12 +362,21 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
         // 5.41 -> 4.04 us. Hot cache: 64-192 rows gain 10-16%, 256-448 rows lose 0-12% (the
         // persistent kernel's streaming loads); single-wave rows stay as they are (64 x 1024
         // fp32 LayerNorm: 2.16 us, widened 2.28-2.33 us).
-        if (plan->variant == rn::V_WORKGROUP && W < 4 && C >= int64_t(64) * 4 &&
-            (rows + 4 / W - 1) / (4 / W) < rn::kPersistentVecBlocks)
+        if (tune && a.tune->waves_per_row > 0) {
+            W = a.tune->waves_per_row;
+            plan->variant = W == 1 ? rn::V_WAVE : rn::V_WORKGROUP;
+        } else if (plan->variant == rn::V_WORKGROUP && W < 4 && C >= int64_t(64) * 4 &&
+                   (rows + 4 / W - 1) / (4 / W) < rn::kPersistentVecBlocks) {
             W = 4;
+        }
         plan->waves_per_row = W;
         plan->rows_per_block = W <= 4 ? 4 / W : 1;
         plan->chunks_per_lane = next_pow2((C + 64 * W - 1) / (64 * W));
+        if (tune && a.tune->chunks_per_lane > 0) {
+            // the row group must cover the row
+            if (int64_t(64) * W * a.tune->chunks_per_lane < C) return RN_ERR_UNSUPPORTED;
+            plan->chunks_per_lane = a.tune->chunks_per_lane;
+        }
         plan->block_threads = 64 * W * plan->rows_per_block;
     }
     const int64_t blocks = (rows + plan->rows_per_block - 1) / plan->rows_per_block;
@@ -368,17 +395,28 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     const bool has_params = a.gamma != nullptr || (ln && a.beta != nullptr);
     plan->persistent = (vec && plan->exact && C <= group_cap && blocks >= rn::kPersistentVecBlocks) ||
                        (plan->variant == rn::V_ELEMENT && blocks >= rn::kPersistentBlocks);
+    if (tune) {
+        const rn_tuning& t = *a.tune;
+        if (t.persistent == 1 && !(plan->exact && C <= group_cap)) return RN_ERR_UNSUPPORTED;
+        if (t.persistent >= 0) plan->persistent = t.persistent == 1;
+        if (t.prefetch >= 0 && !plan->persistent) return RN_ERR_UNSUPPORTED;
+        plan->prefetch = t.prefetch;
+        if (t.grid_blocks > 0) {
+            const int64_t g = t.grid_blocks < plan->grid ? t.grid_blocks : plan->grid;
+            if (plan->persistent)
+                plan->grid_force = g;  // the launch caps nothing further
+            else
+                plan->grid = g;  // the grid-per-row kernels loop over the remaining row blocks
+        }
+    }
     plan->lds_bytes = 0;
     if (plan->persistent && vec && has_params) plan->lds_bytes = static_cast<int>(C * 16);  // one parameter vector in LDS
     *chunks = C;
     return RN_OK;
 }
 
-int run(Args a, const rn_row_strides* strides, hipStream_t stream) {
-    Plan plan;
-    int64_t C = 0;
-    const int st = validate_and_plan(a, strides, &plan, &C);
-    if (st != RN_OK || a.rows == 0) return st;
+// Kernel arguments of a validated call (C: 16-byte chunks per row, vectorized variants).
+Params make_params(const Args& a, int64_t C) {
     const int64_t s = a.dtype == RN_F32 ? 4 : 2;
     Params p;
     p.x = a.x;
@@ -402,9 +440,34 @@ int run(Args a, const rn_row_strides* strides, hipStream_t stream) {
     p.cro = a.ldro * s / 16;
     p.eps = a.eps;
     p.inv_n = static_cast<float>(1.0 / static_cast<double>(a.N));
-    // Persistent vectorized launches have instances of their own (parameters staged on
-    // chip); the element kernel is the same instance in both launch modes.
+    return p;
+}
+
+// The per-dtype launch of a planned vectorized, element or general call (not split rows).
+// Persistent vectorized launches have instances of their own (parameters staged on chip);
+// the element kernel is the same instance in both launch modes.
+hipError_t launch_rows(const Args& a, const Plan& plan, const Params& p, hipStream_t stream) {
     const bool pers_vec = plan.persistent && plan.variant != rn::V_ELEMENT;
+    switch (a.dtype) {
+    case RN_F32: return pers_vec ? rn::launch_f32_persistent(a.op, plan, p, stream) : rn::launch_f32(a.op, plan, p, stream);
+    case RN_F16: return pers_vec ? rn::launch_f16_persistent(a.op, plan, p, stream) : rn::launch_f16(a.op, plan, p, stream);
+    case RN_BF16:
+        return pers_vec ? rn::launch_bf16_persistent(a.op, plan, p, stream) : rn::launch_bf16(a.op, plan, p, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// hipErrorNotSupported from a launch: no kernel instance of the (tuned) shape is built.
+int launch_status(hipError_t e) {
+    return e == hipSuccess ? RN_OK : (e == hipErrorNotSupported ? RN_ERR_UNSUPPORTED : RN_ERR_HIP);
+}
+
+int run(Args a, const rn_row_strides* strides, hipStream_t stream) {
+    Plan plan;
+    int64_t C = 0;
+    const int st = validate_and_plan(a, strides, &plan, &C);
+    if (st != RN_OK || a.rows == 0) return st;
+    const Params p = make_params(a, C);
     if (plan.variant == rn::V_WIDE || plan.variant == rn::V_WIDE_ELEM) {
         rn::WideArgs wa{};
         wa.ws = a.ws;
@@ -431,17 +494,7 @@ int run(Args a, const rn_row_strides* strides, hipStream_t stream) {
         }
         return e == hipSuccess ? RN_OK : RN_ERR_HIP;
     }
-    hipError_t e = hipErrorInvalidValue;
-    switch (a.dtype) {
-    case RN_F32: e = pers_vec ? rn::launch_f32_persistent(a.op, plan, p, stream)
-                              : rn::launch_f32(a.op, plan, p, stream); break;
-    case RN_F16: e = pers_vec ? rn::launch_f16_persistent(a.op, plan, p, stream)
-                              : rn::launch_f16(a.op, plan, p, stream); break;
-    case RN_BF16: e = pers_vec ? rn::launch_bf16_persistent(a.op, plan, p, stream)
-                               : rn::launch_bf16(a.op, plan, p, stream); break;
-    default: break;
-    }
-    return e == hipSuccess ? RN_OK : RN_ERR_HIP;
+    return launch_status(launch_rows(a, plan, p, stream));
 }
 
 Args make_args(int op, const void* x, const void* residual, const void* gamma, const void* beta, const void* y,
@@ -465,6 +518,7 @@ Args make_args(int op, const void* x, const void* residual, const void* gamma, c
     a.ldx = a.ldr = a.ldy = a.ldro = N;
     a.ws = nullptr;
     a.ws_bytes = 0;
+    a.tune = nullptr;
     return a;
 }
 
@@ -729,6 +783,17 @@ int rn_forward_ex(int op, const void* x, const void* residual, const void* gamma
     return run(a, strides, stream);
 }
 
+int rn_forward_tuned(int op, const void* x, const void* residual, const void* gamma, const void* beta, void* y,
+                     void* residual_out, float* mean, float* rstd, int64_t rows, int64_t N, float eps, int dtype,
+                     const rn_row_strides* strides, int variant, const rn_tuning* tuning, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+    Args a = make_args(op, x, residual, gamma, beta, y, residual_out, mean, rstd, rows, N, eps, dtype, variant);
+    a.ws = workspace;
+    a.ws_bytes = workspace_bytes;
+    a.tune = tuning;
+    return run(a, strides, stream);
+}
+
 size_t rn_forward_workspace_bytes(int op, int64_t rows, int64_t N, int dtype) {
     if (op < RN_OP_LAYER_NORM || op > RN_OP_SOFTMAX) return 0;
     if (dtype != RN_F32 && dtype != RN_F16 && dtype != RN_BF16) return 0;
@@ -791,6 +856,37 @@ int rn_plan_backward(int op, const void* dy, const void* x, const void* gamma, c
         out->block_threads = plan.block_threads;
         out->chunks_per_lane = plan.chunks_per_lane;
         out->grid_blocks = plan.grid;
+        out->exact = plan.exact ? 1 : 0;
+        out->persistent = plan.persistent ? 1 : 0;
+        out->lds_bytes = plan.lds_bytes;
+        out->pairs = plan.pairs ? 1 : 0;
+    }
+    return st;
+}
+
+int rn_plan_tuned(int op, const void* x, const void* residual, const void* gamma, const void* beta, const void* y,
+                  const void* residual_out, const void* mean, const void* rstd, int64_t rows, int64_t N, float eps,
+                  int dtype, int variant, const rn_row_strides* strides, const rn_tuning* tuning,
+                  const void* workspace, size_t workspace_bytes, rn_plan_info* out) {
+    Plan plan{};
+    int64_t C = 0;
+    Args a = make_args(op, x, residual, gamma, beta, y, residual_out, mean, rstd, rows, N, eps, dtype, variant);
+    a.ws = const_cast<void*>(workspace);
+    a.ws_bytes = workspace_bytes;
+    a.tune = tuning;
+    int st = validate_and_plan(a, strides, &plan, &C);
+    // a tuned shape must be one the library holds a kernel for: resolved without launching
+    if (st == RN_OK && rows > 0 && tuned(tuning)) {
+        plan.dry = true;
+        st = launch_status(launch_rows(a, plan, make_params(a, C), nullptr));
+    }
+    if (out) {
+        out->variant = plan.variant;
+        out->waves_per_row = plan.waves_per_row;
+        out->rows_per_block = plan.rows_per_block;
+        out->block_threads = plan.block_threads;
+        out->chunks_per_lane = plan.chunks_per_lane;
+        out->grid_blocks = plan.grid_force > 0 ? plan.grid_force : plan.grid;
         out->exact = plan.exact ? 1 : 0;
         out->persistent = plan.persistent ? 1 : 0;
         out->lds_bytes = plan.lds_bytes;

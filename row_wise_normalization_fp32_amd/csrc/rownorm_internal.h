@@ -97,6 +97,13 @@ struct Plan {
     bool persistent;      // parameters staged on chip once, grid sized to resident capacity
     int lds_bytes;        // dynamic LDS of a persistent launch
     bool pairs;           // element variant, 16-bit: slots of two adjacent elements (pair kernel)
+    // Caller-chosen launch (rn_forward_tuned / rn_plan_tuned); the automatic plan leaves these
+    // at their defaults.
+    int64_t grid_force = 0;  // persistent vectorized launches: workgroups to launch (0: the grid rule)
+    int prefetch = -1;       // persistent vectorized launches: 1 the prefetching instance, 0 the
+                             // looping one, -1 the grid rule's choice
+    bool dry = false;        // resolve the kernel instance only, with no HIP call: hipSuccess if
+                             // it is built, hipErrorNotSupported if not
 };
 
 // Shapes the vectorized kernels are built for.

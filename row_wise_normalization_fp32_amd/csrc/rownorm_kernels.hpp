@@ -2101,8 +2101,18 @@ inline hipError_t resident(int block_threads, int lds_bytes, int* cus_out, int* 
     return hipSuccess;
 }
 
+// grid > 0: that many workgroups (at most the row blocks) instead of the resident count.
 template <auto KERNEL>
-inline hipError_t go_persistent(const Plan& plan, const Params& p, hipStream_t stream, int row_bytes_per_wave = 0) {
+inline hipError_t go_persistent(const Plan& plan, const Params& p, hipStream_t stream, int row_bytes_per_wave = 0,
+                                int64_t grid_set = 0) {
+    if (grid_set > 0) {
+        Params args = p;
+        void* argv[] = {&args};
+        return hipLaunchKernel(reinterpret_cast<const void*>(KERNEL),
+                               dim3(static_cast<unsigned>(grid_set < plan.grid ? grid_set : plan.grid)),
+                               dim3(static_cast<unsigned>(plan.block_threads)), argv,
+                               static_cast<size_t>(plan.lds_bytes), stream);
+    }
     int cus = 0, per_cu = 0;
     hipError_t e = resident<KERNEL>(plan.block_threads, plan.lds_bytes, &cus, &per_cu);
     if (e != hipSuccess) return e;
@@ -2142,9 +2152,12 @@ inline hipError_t go_persistent(const Plan& plan, const Params& p, hipStream_t s
 //           stores the first (FL_PREFETCH);
 //   R >  3: one workgroup per block again (the hardware starts a workgroup whenever one ends,
 //           which keeps rows in flight without holding a second row in registers), except
-//           for rows of 4 or more waves with parameters, whose staged parameters are as large
-//           as the block or larger: two workgroups per CU loop over the rows without
-//           prefetching, staging the parameters once.
+//           for rows of 4 or more waves with parameters. Of those, LayerNorm and RMSNorm rows,
+//           whose staged parameters are as large as the block or larger, loop over the rows
+//           on two workgroups per CU without prefetching, staging the parameters once; the
+//           fused ops (two row tensors in, two out) keep one workgroup per block, with the
+//           looping instance from 8 waves per row (whose prefetching instance holds two rows
+//           in fewer registers per lane).
 // The thresholds come from a sweep on MI355X (cold cache, device time per launch of replayed
 // HIP graphs) over LayerNorm, RMSNorm, fused add + RMSNorm / LayerNorm and softmax, 256 to
 // 65536 rows of 1024 to 16384 elements, at grids of 1 to 8 workgroups per CU, half and full:
@@ -2155,12 +2168,22 @@ inline hipError_t go_persistent(const Plan& plan, const Params& p, hipStream_t s
 // 13.74 -> 11.64 us, 32768 x 4096 184.1 -> 174.2 us; RMSNorm fp16 2048 x 4096 8.01 -> 6.96
 // us; fused add + LayerNorm bf16 32768 x 4096 184.8 -> 171.8 us; softmax fp32 32768 x 4096
 // 182.1 -> 169.9 us; LayerNorm bf16 4096 x 16384 unchanged at 46.3 us.
+// Measured on MI355X for the R > 3 exceptions (cold cache, device time per launch; every
+// alternative in the launch-plan sweep of the benchmark): LayerNorm bf16 4096 x 16384 looping
+// on 512 workgroups 46.4 us, prefetching one per block 49.5 us; LayerNorm bf16 16384 x 8192
+// 88.3 against 90.5 us; fused add + LayerNorm bf16 16384 x 8192 prefetching one per block
+// 171.9 us, looping on 512 182.2 us; fused add + RMSNorm fp16 16384 x 8192 174.5 against
+// 182.8 us; fused add + LayerNorm bf16 4096 x 16384 (8 waves) looping one per block 90.7 us,
+// prefetching one per block 94.5 us, looping on the resident grid 94.2 us.
 struct GridRule {
     bool two_tensors;  // fused ops: x and the residual
     bool ln16;         // LayerNorm of 16-bit rows
-    bool loop_wide;    // 4 or more waves per row, with parameters
+    bool loop_wide;    // R > 3: the looping instance on the resident grid
+    bool loop_blocks;  // R > 3: the looping instance, one workgroup per block
 };
 
+// The grid of a persistent vectorized launch and its instance: *loop_out selects the looping
+// instance, on *grid_out workgroups, or on the resident grid when *grid_out is 0.
 template <auto PF_KERNEL>
 inline hipError_t persistent_grid(const Plan& plan, const GridRule& rule, int* grid_out, bool* loop_out) {
     int cus = 0, per_cu = 0;
@@ -2174,8 +2197,11 @@ inline hipError_t persistent_grid(const Plan& plan, const GridRule& rule, int* g
     if (!one_round) {
         if (blocks <= 3 * res) {
             grid = (blocks + 1) / 2;
+        } else if (rule.loop_wide) {
+            loop = true;
+            grid = 0;
         } else {
-            loop = rule.loop_wide;
+            loop = rule.loop_blocks;
         }
     }
     if (grid > kMaxGrid) grid = kMaxGrid;
@@ -2205,21 +2231,33 @@ inline hipError_t go_v(const Plan& plan, const Params& p, hipStream_t s) {
         // without prefetching, as do wide rows with parameters when R > 2.
         constexpr bool NOPF = W >= 16 || (W == 1 && V >= 8);
         constexpr bool WIDE_PARAMS = W >= 4 && AFF != 0 && !OpTraits<OP>::SM;
+        // A caller-chosen instance (plan.prefetch 0 / 1) must be one that is built: the looping
+        // instance exists for NOPF shapes and wide rows with parameters only.
         if constexpr (NOPF) {
-            return go_persistent<rownorm_vec_kernel<DT, OP, W, V, RPB, EXACT, AFF, FL>>(plan, p, s);
+            if (plan.prefetch == 1) return hipErrorNotSupported;
+            if (plan.dry) return hipSuccess;
+            return go_persistent<rownorm_vec_kernel<DT, OP, W, V, RPB, EXACT, AFF, FL>>(plan, p, s, 0, plan.grid_force);
         } else {
+            if (plan.prefetch == 0 && !WIDE_PARAMS) return hipErrorNotSupported;
+            if (plan.dry) return hipSuccess;
             constexpr auto PFK = rownorm_vec_kernel<DT, OP, W, V, RPB, EXACT, AFF, FL | FL_PREFETCH>;
-            constexpr GridRule rule{OpTraits<OP>::RES, OP == OP_LN && DT != DT_F32, WIDE_PARAMS};
+            constexpr bool RES = OpTraits<OP>::RES;
+            constexpr GridRule rule{RES, OP == OP_LN && DT != DT_F32, WIDE_PARAMS && !RES,
+                                    WIDE_PARAMS && RES && W >= 8};
             int grid = 0;
             bool loop = false;
             hipError_t e = persistent_grid<PFK>(plan, rule, &grid, &loop);
             if (e != hipSuccess) return e;
+            if (plan.prefetch >= 0) loop = plan.prefetch == 0;
+            if (plan.grid_force > 0) grid = static_cast<int>(plan.grid_force < plan.grid ? plan.grid_force : plan.grid);
             if constexpr (WIDE_PARAMS) {
-                if (loop) return go_persistent<rownorm_vec_kernel<DT, OP, W, V, RPB, EXACT, AFF, FL>>(plan, p, s);
+                if (loop) return go_persistent<rownorm_vec_kernel<DT, OP, W, V, RPB, EXACT, AFF, FL>>(plan, p, s, 0, grid);
             }
+            if (grid <= 0) grid = static_cast<int>(plan.grid);  // the prefetching instance chosen over a looping rule
             return launch_grid<PFK>(plan, p, s, grid);
         }
     } else {
+        if (plan.dry) return hipSuccess;
         // 1024-lane workgroups have 128 VGPRs per lane: LayerNorm rows there keep no fp32 copy.
         constexpr int FL = W >= 16 && OpTraits<OP>::LN ? FL_NOFLOAT : 0;
         return go(rownorm_vec_kernel<DT, OP, W, V, RPB, EXACT, AFF, FL>, plan, p, s);
@@ -2258,7 +2296,7 @@ inline hipError_t launch_v(const Plan& plan, const Params& p, hipStream_t s) {
         if (plan.chunks_per_lane == 16) return RN_GO(16);
     }
 #undef RN_GO
-    return hipErrorInvalidValue;
+    return hipErrorNotSupported;  // no instance of this shape is built
 }
 
 template <int DT, int OP, bool EXACT, int AFF, bool PERS>
@@ -2269,7 +2307,7 @@ inline hipError_t launch_w(const Plan& plan, const Params& p, hipStream_t s) {
     case 4: return launch_v<DT, OP, 4, EXACT, AFF, PERS>(plan, p, s);
     case 8: return launch_v<DT, OP, 8, EXACT, AFF, PERS>(plan, p, s);
     case 16: return launch_v<DT, OP, 16, EXACT, AFF, PERS>(plan, p, s);
-    default: return hipErrorInvalidValue;
+    default: return hipErrorNotSupported;
     }
 }
 
@@ -2277,7 +2315,7 @@ template <int DT, int OP, int AFF, bool PERS>
 inline hipError_t launch_e(const Plan& plan, const Params& p, hipStream_t s) {
     if constexpr (PERS) {
         // persistent launches are planned only for exact shapes
-        if (!plan.exact) return hipErrorInvalidValue;
+        if (!plan.exact) return hipErrorNotSupported;
         return launch_w<DT, OP, true, AFF, true>(plan, p, s);
     } else {
         return plan.exact ? launch_w<DT, OP, true, AFF, false>(plan, p, s)

@@ -75,3 +75,54 @@ def test_replay_spread():
     s = bench.spread({"repeats_ms": [0.047, 0.046, 0.0465, 0.0462, 0.048]})
     assert s["n"] == 5 and s["median_ms"] == 0.0465 and s["q1_ms"] == 0.0462 and s["q3_ms"] == 0.047
     assert bench.spread({"repeats_ms": None}) is None
+
+
+def _write_trace(d, marks, kernels):
+    import csv as _csv
+
+    with open(d / "trace_marker_api_trace.csv", "w", newline="") as f:
+        w = _csv.writer(f)
+        w.writerow(["Function", "Start_Timestamp", "End_Timestamp"])
+        for name, a, b in marks:
+            w.writerow([name, a, b])
+    with open(d / "trace_kernel_trace.csv", "w", newline="") as f:
+        w = _csv.writer(f)
+        w.writerow(["Kernel_Name", "Start_Timestamp", "End_Timestamp", "Workgroup_Size_X", "Workgroup_Size_Y",
+                    "Workgroup_Size_Z", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"])
+        for name, t, dur, wg, grid in kernels:
+            w.writerow([name, t, t + dur, wg, 1, 1, grid, 1, 1])
+
+
+def test_trace_by_range_attributes_dispatches_to_their_range(tmp_path):
+    k = "void rn::rownorm_vec_kernel<2, 0, 8, 4, 1, true, 3, 62>(rn::Params)"
+    kernels = [(k, 1000 + 10 * i, 5000 + i, 512, 512 * 512) for i in range(30)]  # in range a
+    kernels += [(k, 3000 + 10 * i, 7000, 512, 512 * 1024) for i in range(25)]  # in range b, another grid
+    kernels += [("void at::native::elementwise_kernel<128, 4>(int)", 1005, 100, 128, 128),  # torch: dropped
+                (k, 2500, 100, 512, 512)]  # between the ranges: dropped
+    _write_trace(tmp_path, [("bench:plan:s:a", 900, 2000), ("bench:plan:s:b", 2900, 4000),
+                            ("other", 1000, 5000)], kernels)
+    by = bench.trace_by_range(str(tmp_path))
+    assert set(by) == {"plan:s:a", "plan:s:b"}
+    (name, n, us, wg), = by["plan:s:a"]
+    assert name == "rn::rownorm_vec_kernel<2, 0, 8, 4, 1, true, 3, 62>" and n == 30 and wg == 512
+    assert us == pytest.approx(5.0145)  # median of 5000..5029 ns
+    (name, n, us, wg), = by["plan:s:b"]
+    assert n == 25 and wg == 1024 and us == pytest.approx(7.0)
+    assert "plan:s:a" in bench.trace_summary(str(tmp_path))
+
+
+def test_plan_sweep_report():
+    cand = lambda label, us, W: {"label": label, "tuning": None, "us": us, "q1_us": us, "q3_us": us,  # noqa: E731
+                                  "replays": 5, "pct_of_peak": 50.0, "vs_best": us / 10.0,
+                                  "plan": {"waves_per_row": W, "chunks_per_lane": 4, "persistent": True}}
+    sweep = {"shapes": {
+        "s1": {"op": "ln", "dtype": "bf16", "rows": 4, "N": 8, "why": "w", "planner_vs_best": 1.1, "planner_rank": 2,
+               "candidates": [cand("auto", 11.0, 2), cand("W4xV2 persistent", 10.0, 4), cand("x", 30.0, 1)]},
+        "s2": {"op": "ln", "dtype": "bf16", "rows": 4, "N": 8, "why": "w", "planner_vs_best": 1.0, "planner_rank": 1,
+               "candidates": [cand("auto", 10.0, 2)]}}}
+    md = bench.plan_sweep_report(sweep)
+    assert "geometric mean 1.049x, worst 1.100x" in md
+    assert "**planner** (W2xV4 persistent, grid rule)" in md
+    # top=1 keeps the fastest, the planner's and the slowest
+    md1 = bench.plan_sweep_report(sweep, top=1)
+    assert md1.count("| x |") == 1 and md1.count("W4xV2 persistent") == 1
