@@ -178,8 +178,15 @@ def kernel_name(w, plan):
 
 
 def launch(rn, w, s, tuning=None):
-    """One call of workload `w` on buffer set `s` (forward ops: with an optional tuning)."""
-    kw = {} if tuning is None else {"tuning": tuning}
+    """One call of workload `w` on buffer set `s` (forward ops: with an optional tuning, whose
+    "variant" key, if any, forces a kernel variant)."""
+    kw = {}
+    if tuning is not None:
+        t = dict(tuning)
+        if "variant" in t:
+            kw["variant"] = t.pop("variant")
+        if t:
+            kw["tuning"] = t
     if w.op == "ln":
         rn.ln_forward(s["x"], s.get("gamma"), s.get("beta"), w.eps, out=s["y"], mean=s["mean"], rstd=s["rstd"], **kw)
     elif w.op == "rms":
@@ -618,6 +625,27 @@ def plan_sweep_shapes():
         (ln4k(256), "persistent threshold: 256 rows (widened to 4 waves: 256 row blocks)"),
         (ln4k(384), "persistent threshold: 384 rows (widened to 4 waves: 384 row blocks)"),
         (ln4k(1024), "persistent threshold: 1024 rows (2 waves: 512 row blocks)"),
+        (sm.scaled(rows=512, N=32768, name="softmax_fp32_512x32768"), "128 KiB softmax rows: one 16-wave "
+                                                                       "workgroup per row against split rows"),
+        (workloads.C3.scaled(rows=1024, N=65536, name="rms_fp16_1024x65536"), "128 KiB RMSNorm rows: one "
+                                                                               "16-wave workgroup against split "
+                                                                               "rows"),
+        (c5.scaled(rows=1024, N=65536, name="ln_bf16_1024x65536"), "128 KiB LayerNorm rows: one 16-wave "
+                                                                   "workgroup against split rows and the general "
+                                                                   "kernel"),
+        (workloads.C2.scaled(rows=1024, N=32768, name="ln_fp32_1024x32768"), "128 KiB fp32 LayerNorm rows"),
+        (workloads.C4_FP16.scaled(rows=1024, N=65536, name="fused_fp16_1024x65536"), "128 KiB fused add + "
+                                                                                      "RMSNorm rows"),
+        (workloads.C4_BF16.scaled(rows=4096, N=65536, name="fused_bf16_4096x65536"), "128 KiB fused add + "
+                                                                                     "RMSNorm rows, more rows"),
+        (c5.scaled(rows=4096, N=65536, name="ln_bf16_4096x65536"), "128 KiB LayerNorm rows, more rows"),
+        (sm.scaled(rows=512, N=65536, name="softmax_fp32_512x65536"), "256 KiB fp32 softmax rows: one 16-wave "
+                                                                      "workgroup against split rows"),
+        (workloads.C1.scaled(rows=8192, N=4095, name="ln_fp32_8192x4095"), "ragged fp32 rows: element kernel "
+                                                                           "against the general kernel"),
+        (workloads.C1.scaled(rows=1024, N=65537, name="ln_fp32_1024x65537"), "long ragged rows: element-granular "
+                                                                             "split rows against the general "
+                                                                             "kernel"),
         (workloads.C4_FP16, "persistent threshold: fused add + RMSNorm fp16 256 rows"),
         (fln.scaled(rows=384, name="fused_ln_bf16_384x4096"), "persistent threshold: fused add + LayerNorm "
                                                               "384 rows"),
@@ -646,7 +674,8 @@ def plan_candidates(rn, w, s0, cus):
 
     td = workloads.TORCH_DTYPES[w.dtype]
     ptrs = _plan_ptrs(w, s0)
-    st, auto = rn.plan(w.op, w.rows, w.N, td, ptrs=ptrs, eps=w.eps)
+    st, auto = rn.plan(w.op, w.rows, w.N, td, ptrs=ptrs, eps=w.eps,
+                       workspace_bytes=rn.forward_workspace_bytes(w.op, w.rows, w.N, td))
     if st != 0:
         raise RuntimeError(f"{w.name}: automatic plan failed ({rn.STATUS.get(st, st)})")
     blocks = auto["grid_blocks"]
@@ -658,9 +687,24 @@ def plan_candidates(rn, w, s0, cus):
         tries += [{"prefetch": pf, "grid_blocks": g} for pf in (1, 0) for g in grids]
     else:
         tries.append({"persistent": 1})
-    key = lambda i, t: (i["waves_per_row"], i["chunks_per_lane"], i["rows_per_block"], i["persistent"],  # noqa
-                        i["grid_blocks"], (t or {}).get("prefetch", -1))
+    key = lambda i, t: (i["variant"], i["waves_per_row"], i["chunks_per_lane"], i["rows_per_block"],  # noqa
+                        i["persistent"], i["grid_blocks"], (t or {}).get("prefetch", -1))
     out, seen = [("auto", None, auto)], {key(auto, None)}
+    # the other kernel variants (forced through rn_forward_ex's variant argument), each with
+    # its own automatic launch
+    # (as the binding calls them: a workspace only for the split-row variants)
+    ws = rn.forward_workspace_bytes(w.op, w.rows, w.N, td)
+    vec = auto["variant"] in ("wave", "workgroup")
+    for v in ("element", "general", "wide", "wide_element") if vec else \
+            ("wave", "workgroup", "element", "general", "wide", "wide_element"):
+        wsv = ws if v in ("wide", "wide_element") else 0
+        st, info = rn.plan(w.op, w.rows, w.N, td, ptrs=ptrs, eps=w.eps, variant=v, workspace_bytes=wsv)
+        if st != 0 or key(info, None) in seen or v == auto["variant"]:
+            continue
+        seen.add(key(info, None))
+        out.append((f"variant {v}", {"variant": v}, info))
+    if not vec:
+        return out  # the tunings below apply to the vectorized variants
     for t in tries:
         st, info = rn.plan(w.op, w.rows, w.N, td, ptrs=ptrs, eps=w.eps, tuning=t)
         if st != 0 or key(info, t) in seen:
@@ -677,7 +721,7 @@ def plan_candidates(rn, w, s0, cus):
     return out
 
 
-def plan_sweep(dev, steps):
+def plan_sweep(dev, steps, only=None):
     import torch
 
     import row_wise_normalization_fp32_amd as rn
@@ -686,6 +730,8 @@ def plan_sweep(dev, steps):
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     res = {}
     for w, why in plan_sweep_shapes():
+        if only and w.name not in only:
+            continue
         nbytes = workloads.algorithmic_bytes(w.op, w.rows, w.N, w.elem_bytes, with_stats=True)
         set_bytes = SET_TENSORS[w.op] * w.rows * w.N * w.elem_bytes
         nsets = max(MIN_COLD_SETS, min(64, math.ceil(COLD_FOOTPRINT / set_bytes)))
@@ -763,14 +809,127 @@ def trace_by_range(trace_dir):
 
 
 def trace_summary(trace_dir):
-    """Markdown table of trace_by_range: kernels launched at least 20 times in a range."""
-    lines = ["| range | kernel (template arguments) | workgroups | dispatches | median us (last 100) |",
-             "|---|---|---|---|---|"]
+    """Markdown table of trace_by_range: the kernels launched at least 20 times in a range (a
+    range's other kernels prepare its inputs), and for a bench line the sum per step with the
+    line's algorithmic bytes per second."""
+    import workloads
+
+    wl = bench_workloads()
+    lines = ["| range | kernel (template arguments) | workgroups | dispatches | median µs (last 100) | "
+             "µs per step | GB/s | % of 8 TB/s |", "|---|---|---|---|---|---|---|---|"]
     for rng, ks in trace_by_range(trace_dir).items():
-        for name, c, us, wg in ks:
-            if c >= 20:
-                lines.append(f"| {rng} | `{name}` | {wg} | {c} | {us:.2f} |")
+        ks = [k for k in ks if k[1] >= 20]
+        if not ks:
+            continue
+        line = rng.partition(":")[0]
+        b = None
+        if line.startswith("ceiling_"):
+            b = int(line.split("_")[1])
+        elif line in wl and not rng.startswith("plan:"):
+            w = wl[line]
+            b = workloads.algorithmic_bytes(w.op, w.rows, w.N, w.elem_bytes, with_stats=True)
+        tot = sum(k[2] for k in ks)
+        for i, (name, c, us, wg) in enumerate(ks):
+            tail = " | | |"
+            if i == len(ks) - 1:
+                gbs = b / (tot * 1e-6) / 1e9 if b else None
+                tail = (f" {tot:.2f} | " + (f"{gbs:.0f} | {100 * gbs / PEAK_HBM_GBS:.1f} |" if gbs else " | |"))
+            lines.append(f"| {rng} | `{name}` | {wg} | {c} | {us:.2f} |" + tail)
     return "\n".join(lines)
+
+
+def _csv_rows(path):
+    """Rows of a rocprofv3 CSV, read from `path` or from `path`.gz."""
+    import csv
+    import gzip
+
+    f = gzip.open(path + ".gz", "rt") if not os.path.exists(path) and os.path.exists(path + ".gz") else open(path)
+    with f:
+        return list(csv.DictReader(f))
+
+
+def _counter_medians(run_dir, prefix):
+    """Median counter value per (kernel template name, workgroups) of a --pmc run."""
+    import statistics
+
+    by = {}
+    for r in _csv_rows(os.path.join(run_dir, f"{prefix}_counter_collection.csv")):
+        name = re.sub(r"\(.*$", "", r["Kernel_Name"].replace("void ", "").replace("(anonymous namespace)::", ""))
+        wg = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+        by.setdefault((name, wg), []).append(float(r["Counter_Value"]))
+    return {k: statistics.median(v) for k, v in by.items()}
+
+
+def bench_workloads():
+    """Every workload a default run of this script times, by line name (as line_marker names
+    its roctx range without the cache suffix)."""
+    import workloads
+
+    ws = [workloads.C5, workloads.FUSED_8192] + [x for _, x, _ in _more()] + list(workloads.CONFIGS)
+    ws += [workloads.C4_FP16.scaled(rows=r, name=f"fused_fp16_{r}x4096") for r in (2048, 8192, 32768)]
+    ws += [workloads.C4_BF16.scaled(rows=r, name=f"fused_bf16_{r}x4096") for r in (2048, 8192, 32768)]
+    ws += [workloads.C5.scaled(rows=2048, N=4096, name="ln_bf16_2048x4096"),
+           workloads.C5.scaled(name="ln_bf16_4096x16384_hot")]
+    return {w.name: w for w in ws}
+
+
+def traffic_summary(fetch_dir, write_dir, cal_fetch_dir, cal_write_dir, trace_dir):
+    """HBM traffic per call of each bench line from two --pmc runs of this script (FETCH_SIZE,
+    WRITE_SIZE, KiB per dispatch), scaled by what the same counters read for the streaming
+    copy kernel of --copy-calibration (256 MiB read and written per dispatch), with each
+    kernel attributed to its line through a --kernel-trace --marker-trace run. The text is the
+    record counter_traffic() reads."""
+    import statistics
+    import workloads
+
+    cal = {}
+    for c, d in (("FETCH_SIZE", cal_fetch_dir), ("WRITE_SIZE", cal_write_dir)):
+        v = [float(r["Counter_Value"]) for r in _csv_rows(os.path.join(d, "cal_counter_collection.csv"))
+             if "stream_copy" in r["Kernel_Name"]]
+        cal[c] = (256 * 1024) / statistics.median(v)
+    cnt = {"FETCH_SIZE": _counter_medians(fetch_dir, "pmc"), "WRITE_SIZE": _counter_medians(write_dir, "pmc")}
+    by = trace_by_range(trace_dir)
+    wl = bench_workloads()
+    out = [f"kernel_source_sha256_16: {kernel_source_hash()}",
+           "# (sha256 of rownorm_kernels.hpp + rownorm_backward.hpp + rownorm_capi.cpp with comments",
+           "# and whitespace removed; bench.py reports traffic only while it matches)",
+           f"# fetch scale {cal['FETCH_SIZE']:.5f}, write scale {cal['WRITE_SIZE']:.5f} (streaming copy: "
+           f"FETCH_SIZE {256 * 1024 / cal['FETCH_SIZE']:.1f} KiB, WRITE_SIZE {256 * 1024 / cal['WRITE_SIZE']:.1f} KiB "
+           "per 262144 KiB read and written)", ""]
+    seen = set()
+    for rng, ks in by.items():
+        if rng.startswith("plan:"):
+            continue
+        line, _, cache = rng.partition(":")
+        key = "ln_bf16_4096x16384" if line in ("C5_ln_bf16_4096x16384", "ln_bf16_4096x16384_hot") else line
+        if cache == "hot" or key in seen:
+            continue
+        seen.add(key)
+        if line.startswith("ceiling_"):
+            b = int(line.split("_")[1])
+        elif line in wl:
+            w = wl[line]
+            b = workloads.algorithmic_bytes(w.op, w.rows, w.N, w.elem_bytes, with_stats=True)
+        else:
+            continue
+        t, desc = 0.0, []
+        for name, n, _, wg in ks:
+            if n < 20:
+                continue  # launched only to prepare a line's inputs
+            f, w_ = cnt["FETCH_SIZE"].get((name, wg)), cnt["WRITE_SIZE"].get((name, wg))
+            if f is None or w_ is None:
+                desc.append(f"#   {name} ({wg} workgroups): no counter record")
+                t = None
+                break
+            t += (f * cal["FETCH_SIZE"] + w_ * cal["WRITE_SIZE"]) * 1024
+            desc.append(f"#   {name} ({wg} workgroups): FETCH_SIZE {f:.1f} KiB, WRITE_SIZE {w_:.1f} KiB")
+        out.append(f"# {key}" + (" (streaming copy, bytes read + written)" if line.startswith("ceiling_") else ""))
+        out.extend(desc)
+        if t is not None:
+            out.append(f"#   algorithmic bytes {b}; measured/algorithmic = {t / b:.4f}")
+            out.append(f"{key} traffic_bytes_per_launch: {t:.0f}")
+        out.append("")
+    return "\n".join(out)
 
 
 def plan_sweep_report(sweep, trace_dir=None, top=0):
@@ -812,6 +971,8 @@ def plan_sweep_report(sweep, trace_dir=None, top=0):
 
 
 def _plan_label(info):
+    if info["variant"] not in ("wave", "workgroup"):
+        return f"{info['variant']} variant"
     s = f"W{info['waves_per_row']}xV{info['chunks_per_lane']}"
     return s + (" persistent, grid rule" if info["persistent"] else " grid per row")
 
@@ -862,11 +1023,16 @@ def main():
     ap.add_argument("--plan-sweep", action="store_true",
                     help="time the automatic launch plan of several shapes against every built alternative, "
                          "print JSON, exit")
+    ap.add_argument("--shapes", metavar="NAMES", help="--plan-sweep: only these shapes (comma-separated names)")
     ap.add_argument("--plan-sweep-report", metavar="JSON",
                     help="markdown tables of a --plan-sweep result (with --trace DIR: and of its kernel trace)")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="markdown table of a rocprofv3 --kernel-trace --marker-trace run of this script")
     ap.add_argument("--trace", metavar="DIR", help="the kernel trace of the --plan-sweep run (for the report)")
+    ap.add_argument("--traffic-summary", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "CAL_FETCH_DIR", "CAL_WRITE_DIR",
+                                                            "TRACE_DIR"),
+                    help="HBM traffic per bench line from --pmc FETCH_SIZE / WRITE_SIZE runs of this script, the "
+                         "--copy-calibration runs and a --kernel-trace --marker-trace run")
     ap.add_argument("--top", type=int, default=0, help="report: per shape the fastest N plans, the planner's and "
                                                        "the slowest")
     ap.add_argument("--prime-ms", type=float, default=PRIME_MS,
@@ -884,6 +1050,9 @@ def main():
 
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
+        return
+    if args.traffic_summary:
+        print(traffic_summary(*args.traffic_summary))
         return
     if args.plan_sweep_report:
         sweep = json.loads(open(args.plan_sweep_report).read().strip().splitlines()[-1])["plan_sweep"]
@@ -905,7 +1074,8 @@ def main():
         print(json.dumps({"ceiling_sweep": ceiling_sweep(args.steps, dev)}), flush=True)
         return
     if args.plan_sweep:
-        print(json.dumps({"plan_sweep": plan_sweep(dev, args.steps)}), flush=True)
+        only = set(args.shapes.split(",")) if args.shapes else None
+        print(json.dumps({"plan_sweep": plan_sweep(dev, args.steps, only)}), flush=True)
         return
 
     w = workloads.C5

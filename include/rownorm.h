@@ -104,7 +104,7 @@ typedef enum rn_variant {
     RN_VARIANT_AUTO = 0,      /* choose from N, dtype, alignment and rows (what the plain entry points do) */
     RN_VARIANT_WAVE = 1,      /* one 64-lane wavefront per row, row held in VGPRs (rows up to 16 KiB) */
     RN_VARIANT_WORKGROUP = 2, /* 2-16 wavefronts per row, partial moments combined in LDS (rows up to 64 KiB;
-                                 softmax and RMSNorm up to 128 KiB, LayerNorm and fused add + RMSNorm
+                                 softmax, RMSNorm and LayerNorm up to 128 KiB, fused add + RMSNorm
                                  too when no workspace is given) */
     RN_VARIANT_GENERAL = 3,   /* any N, any element-aligned pointers; re-reads the row */
     RN_VARIANT_ELEMENT = 4,   /* rows up to 16384 elements held in VGPRs one element per slot;
@@ -214,13 +214,14 @@ int softmax_forward(const void* x, void* y, float* row_max, float* row_sum, int6
  * statistics record as tagged 64-bit words, wait a bounded time for the row's other records
  * and compute any still missing themselves from the inputs, with the same bits, so the result
  * never depends on which workgroups run at the same time. The environment variable
- * RN_FWD_WAIT_POLLS (a non-negative integer, read at every call) sets the wait; 0 computes
- * every other record locally. In-place calls (y == x, residual_out == residual, ...), rows
+ * RN_FWD_WAIT_POLLS (a non-negative integer, read at every call) sets the wait; 0 waits for
+ * nothing and computes every record of a row in each of its workgroups. In-place calls (y == x, residual_out == residual, ...), rows
  * of more than 256 segments, and a workspace of only the two-launch size (rows * ceil(N /
  * 8192) * 16 bytes) take two launches: records, then normalization, which reads x (for the
- * fused ops: residual_out) a second time. Both forms give the same bits. Without a
- * workspace, LayerNorm and fused add + RMSNorm rows of whole chunks up to 128 KiB take one
- * 16-wave workgroup; other such rows take the general kernel.
+ * fused ops: residual_out) a second time. Both forms give the same bits. Softmax, RMSNorm
+ * and LayerNorm rows of whole chunks up to 128 KiB (fp32 softmax: 256 KiB) never split: one
+ * 16-wave workgroup holds them. Without a workspace, fused add + RMSNorm rows of whole chunks
+ * up to 128 KiB take one 16-wave workgroup too; other such rows take the general kernel.
  */
 int rn_forward_ex(int op, const void* x, const void* residual, const void* gamma, const void* beta, void* y,
                   void* residual_out, float* mean, float* rstd, int64_t rows, int64_t N, float eps, int dtype,

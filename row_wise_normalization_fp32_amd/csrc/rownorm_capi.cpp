@@ -110,8 +110,9 @@ size_t wide_workspace_bytes_any(int64_t rows, int64_t N, int64_t s) {
 
 // Polls of a missing segment record before the one-pass split-row forward computes it in the
 // waiting workgroup: rn::kWideWaitPolls, or RN_FWD_WAIT_POLLS from the environment (a
-// non-negative integer; 0 computes every other segment's record locally, which tests use to
-// check that both ways give the same bits). Read at every call.
+// non-negative integer; 0 waits for nothing and computes every record of each row in every
+// workgroup of the row, which tests use to check that both ways give the same bits). Read at
+// every call.
 int fwd_wait_polls() {
     const char* v = getenv("RN_FWD_WAIT_POLLS");
     if (v == nullptr || *v == '\0') return rn::kWideWaitPolls;
@@ -236,20 +237,22 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     // Softmax keeps no parameters in registers: its element / pair kernels hold rows of up to
     // 65536 elements in one 16-wave workgroup (x read once) instead of splitting them.
     const int64_t elem_cap_op = sm ? int64_t(64) * rn::kMaxGroupWaves * rn::kSoftmaxElemMaxPerLane : elem_cap;
-    // Softmax and RMSNorm: 16 waves x 8 chunks hold rows up to 8192 chunks in one workgroup
-    // (grid per row). Measured on MI355X against the split-row path: softmax 51-54% -> 55-61%,
-    // RMSNorm 59% -> 61%; the LayerNorm ops (42-50% vs 51-57%) and fused add + RMSNorm (66%
-    // vs 67%) stay split.
+    // Softmax, RMSNorm and LayerNorm: 16 waves x 8 chunks hold rows up to 8192 chunks in one
+    // workgroup (grid per row). Measured on MI355X against the split-row paths (cold cache,
+    // graph replays): softmax 51-54% -> 55-61%, RMSNorm 59% -> 61%; LayerNorm against the
+    // one-pass split rows bf16 1024 x 65536 68.8 -> 61.3 us, 4096 x 65536 240.1 -> 223.9 us,
+    // fp32 1024 x 32768 64.5 -> 59.0 us. Fused add + RMSNorm stays split when a workspace is
+    // given (fp16 1024 x 65536 105.5 against 101.0 us one workgroup, bf16 4096 x 65536 371.4
+    // against 377.1 us), fused add + LayerNorm always (its 16 x 8 instance would spill).
     // fp32 softmax, which holds nothing else in registers, takes 16 chunks per lane: rows of
     // 65536 elements (256 KiB); 16-bit softmax rows of that length fit 8 chunks per lane.
-    // Without a workspace (no split rows possible) LayerNorm and fused add + RMSNorm rows of
-    // up to 8192 chunks also take one 16-wave workgroup instead of the general kernel (which
-    // reads the row up to three times, element by element).
-    const bool big_instead_of_general =
-        !ws_given && (a.op == RN_OP_LAYER_NORM || a.op == RN_OP_FUSED_ADD_RMS_NORM);
+    // Without a workspace (no split rows possible) fused add + RMSNorm rows of up to 8192
+    // chunks also take one 16-wave workgroup instead of the general kernel (which reads the
+    // row up to three times, element by element).
+    const bool big_instead_of_general = !ws_given && a.op == RN_OP_FUSED_ADD_RMS_NORM;
     const int64_t big_cap = a.op == RN_OP_SOFTMAX
                                 ? int64_t(64) * rn::kMaxGroupWaves * (s == 4 ? rn::kMaxSoftmaxChunks : rn::kMaxBigChunks)
-                            : (a.op == RN_OP_RMS_NORM || big_instead_of_general)
+                            : (a.op == RN_OP_RMS_NORM || a.op == RN_OP_LAYER_NORM || big_instead_of_general)
                                 ? int64_t(64) * rn::kMaxGroupWaves * rn::kMaxBigChunks
                                 : group_cap;
 

@@ -44,7 +44,9 @@ struct WideArgs {
     unsigned* sync;
     unsigned long long* rec64;
     int P;           // row blocks
-    int R;           // rows per block (one ticket = one block of one segment)
+    int R;           // rows per block (one ticket = one block of one segment) ...
+    int P1;          // ... for the first P1 blocks; the rest have R2 rows (the last one fewer)
+    int R2;
     int wait_polls;  // polls of a missing record before the waiting workgroup computes it
 };
 

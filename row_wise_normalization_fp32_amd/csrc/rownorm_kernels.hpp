@@ -1529,9 +1529,9 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_norm_kernel(Params p,
 // ---------------------------------------------------------------------------------------
 // One-pass split rows (whole 16-byte chunks): x (for the fused ops, x and the residual) is
 // read once, the walkthrough's single-read layout (sections 3-4) carried over to a row that
-// outgrows one workgroup (section 1.1). The rows are cut into P blocks of R rows; a ticket is
-// one (block, segment) pair, ticket = block * S + segment, and workgroups take tickets from a
-// counter in the workspace in increasing order. For each row of its block the workgroup
+// outgrows one workgroup (section 1.1). The rows are cut into P blocks, P1 of R rows and
+// then blocks of R2 rows; a ticket is one (block, segment) pair, ticket = block * S + segment,
+// and workgroups take tickets from a counter in the workspace in increasing order. For each row of its block the workgroup
 // holding a ticket keeps its segment in registers, forms the segment's statistics record
 // (wide_record, as the two-launch path does) and publishes it as four 64-bit words (tag 1 in
 // the upper half, the float's bits in the lower half; single-copy atomic, device scope), loads
@@ -1665,8 +1665,10 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_onepass_kernel(Params
             };
             return wide_record<DT, OP, EXACT>(get, Cs2, t, lane, wr, part, buf);
         };
-        const int64_t r0 = blk * wa.R;
-        const int64_t r1 = r0 + wa.R < p.rows ? r0 + wa.R : p.rows;
+        const int64_t r0 = blk < wa.P1 ? blk * wa.R
+                                       : static_cast<int64_t>(wa.P1) * wa.R + (blk - wa.P1) * wa.R2;
+        const int64_t rn = r0 + (blk < wa.P1 ? wa.R : wa.R2);
+        const int64_t r1 = rn < p.rows ? rn : p.rows;
         // three rows in flight: row (record posted, waiting), row + 1 (posted before the wait
         // for row), row + 2 (loads issued before that wait)
         u32x4 cx[V], cr[NR], nx[V], nr[NR];
@@ -1686,7 +1688,8 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_onepass_kernel(Params
                     const int k = lane + 64 * j;
                     if (k < S) {
                         bool got = false;
-                        for (int n = 0;; ++n) {
+                        // wait_polls 0: no wait at all, every record of the row is computed here
+                        for (int n = 0; wa.wait_polls > 0; ++n) {
                             const unsigned long long w0 = __hip_atomic_load(w + 4 * k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                             const unsigned long long w1 = __hip_atomic_load(w + 4 * k + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                             const unsigned long long w2 = __hip_atomic_load(w + 4 * k + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2505,16 +2508,32 @@ inline hipError_t go_wide_onepass(const Plan& plan, const Params& p, const WideA
     // Blocks of about kWideOnePassRows rows (at least enough blocks to fill the resident
     // grid): measured on MI355X, LayerNorm fp32 1024 x 65536: 16 rows per block 114.3 us, 8
     // 109.0, 4 107.9; 512 rows: 8 rows 62.5 us, 4 63.3; 2048 rows: 32 rows 214.0 us, 8 201.6,
-    // 4 200.0.
+    // 4 200.0. Rejected (same shapes): three rows loaded ahead instead of two (1024 rows:
+    // 112.9 us), each workgroup on one segment for the whole launch with per-segment block
+    // counters (134 us: a row's segments were no longer processed together), and tickets
+    // claimed a row ahead with the row pipeline running across tickets (112.6 us).
     WideArgs wa = wa0;
     int64_t P = (p.rows + kWideOnePassRows - 1) / kWideOnePassRows;
     if (P < res / wa.S) P = res / wa.S;
     if (P > p.rows) P = p.rows;
     const int64_t R = (p.rows + P - 1) / P;
     P = (p.rows + R - 1) / R;
+    // The last rows, about one round of the resident grid (res / S, at most a quarter of
+    // the rows), in tickets of one row, so that the workgroups run out of work together:
+    // measured on MI355X, LayerNorm fp32 x 65536: 512 rows 63.3 -> 61.5 us, 1024 rows 109.2 ->
+    // 106.6 us, 2048 rows 204.4 -> 201.3 us (tails of 128-256 rows in 2-row tickets: 0-2 us).
+    int64_t P1 = P;
+    const int64_t R2 = 1;
+    const int64_t tail = res / wa.S < p.rows / 4 ? res / wa.S : p.rows / 4;
+    if (R > 1 && tail > 0) {
+        P1 = (p.rows - tail) / R;
+        P = P1 + (p.rows - P1 * R + R2 - 1) / R2;
+    }
     if (P * wa.S > INT32_MAX) return hipErrorNotSupported;  // tickets come from a 32-bit counter
     wa.P = static_cast<int>(P);
     wa.R = static_cast<int>(R);
+    wa.P1 = static_cast<int>(P1);
+    wa.R2 = static_cast<int>(R2);
     // header (counter, count) and records: 256 + rows * S * 32 bytes
     const int64_t n16 = (256 + p.rows * wa.S * 32) / 16;
     int64_t gc = (n16 + 255) / 256;

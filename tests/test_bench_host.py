@@ -114,7 +114,8 @@ def test_trace_by_range_attributes_dispatches_to_their_range(tmp_path):
 def test_plan_sweep_report():
     cand = lambda label, us, W: {"label": label, "tuning": None, "us": us, "q1_us": us, "q3_us": us,  # noqa: E731
                                   "replays": 5, "pct_of_peak": 50.0, "vs_best": us / 10.0,
-                                  "plan": {"waves_per_row": W, "chunks_per_lane": 4, "persistent": True}}
+                                  "plan": {"variant": "workgroup", "waves_per_row": W, "chunks_per_lane": 4,
+                                           "persistent": True}}
     sweep = {"shapes": {
         "s1": {"op": "ln", "dtype": "bf16", "rows": 4, "N": 8, "why": "w", "planner_vs_best": 1.1, "planner_rank": 2,
                "candidates": [cand("auto", 11.0, 2), cand("W4xV2 persistent", 10.0, 4), cand("x", 30.0, 1)]},

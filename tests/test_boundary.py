@@ -254,11 +254,18 @@ def test_plan_forced_variants():
     assert rn.plan("softmax", 4, 65536, torch.float32, variant="workgroup")[1]["chunks_per_lane"] == 16
     assert rn.plan("softmax", 4, 65540, torch.float32, variant="workgroup")[0] == UNSUP
     assert rn.plan("softmax", 4, 65544, torch.bfloat16, variant="workgroup")[0] == UNSUP
-    # LayerNorm rows of 8192 chunks: one workgroup without a workspace, split rows with one
+    # LayerNorm rows of 8192 chunks: one workgroup, with or without a workspace (split rows
+    # only when forced); fused add + RMSNorm rows: one workgroup without a workspace, split
+    # rows with one
     assert rn.plan("ln", 4, 32768, torch.float32, variant="workgroup")[1]["chunks_per_lane"] == 8
     need = rn.forward_workspace_bytes("ln", 4, 32768, torch.float32)
-    assert rn.plan("ln", 4, 32768, torch.float32, workspace_bytes=need)[1]["variant"] == "wide"
-    assert rn.plan("ln", 4, 32768, torch.float32, variant="workgroup", workspace_bytes=need)[0] == UNSUP
+    assert rn.plan("ln", 4, 32768, torch.float32, workspace_bytes=need)[1]["variant"] == "workgroup"
+    assert rn.plan("ln", 4, 32768, torch.float32, variant="wide", workspace_bytes=need)[1]["variant"] == "wide"
+    assert rn.plan("ln", 4, 32768, torch.float32, variant="workgroup", workspace_bytes=need)[0] == OK
+    assert rn.plan("fused_add_rms", 4, 65536, torch.float16, variant="workgroup")[1]["chunks_per_lane"] == 8
+    need = rn.forward_workspace_bytes("fused_add_rms", 4, 65536, torch.float16)
+    assert rn.plan("fused_add_rms", 4, 65536, torch.float16, workspace_bytes=need)[1]["variant"] == "wide"
+    assert rn.plan("fused_add_rms", 4, 65536, torch.float16, variant="workgroup", workspace_bytes=need)[0] == UNSUP
     assert rn.plan("ln", 4, 32772, torch.float32, variant="workgroup")[0] == UNSUP  # 8193 chunks
     assert rn.plan("ln", 4, 64, torch.float32, variant="general")[1]["variant"] == "general"
     assert rn.plan("ln", 4, 4096, torch.float32, variant="element")[1]["variant"] == "element"
@@ -423,11 +430,12 @@ def test_plan_split_rows():
     assert st == OK and info["variant"] == "wide" and info["grid_blocks"] == 64 * 8 and info["exact"]
     st, info = rn.plan("softmax", 8, 65544, bf16, workspace_bytes=8 * 9 * 16)
     assert st == OK and info["variant"] == "wide" and not info["exact"] and info["grid_blocks"] == 8 * 5
-    # softmax and RMSNorm rows up to 128 KiB stay in one workgroup (16 waves x 8 chunks)
+    # softmax, RMSNorm and LayerNorm rows up to 128 KiB stay in one workgroup (16 waves x 8
+    # chunks); the fused ops split them
     ws = rn.forward_workspace_bytes("ln", 8, 32776, bf16)
-    assert rn.plan("softmax", 8, 32776, bf16, workspace_bytes=ws)[1]["variant"] == "workgroup"
-    assert rn.plan("rms", 8, 32776, bf16, workspace_bytes=ws)[1]["variant"] == "workgroup"
-    for op in ("ln", "fused_add_rms", "fused_add_ln"):
+    for op in ("softmax", "rms", "ln"):
+        assert rn.plan(op, 8, 32776, bf16, workspace_bytes=ws)[1]["variant"] == "workgroup"
+    for op in ("fused_add_rms", "fused_add_ln"):
         assert rn.plan(op, 8, 32776, bf16, workspace_bytes=ws)[1]["variant"] == "wide"
     # bf16 rows of whole chunks up to 32768 elements stay in one workgroup, workspace or not
     assert rn.plan("ln", 8, 32768, bf16, workspace_bytes=8 * 8 * 16)[1]["variant"] == "workgroup"

@@ -164,12 +164,12 @@ BIG_SHAPES = {"fp32": [(3, 16388), (4, 24576), (2, 32768)], "bf16": [(3, 32776),
 @pytest.mark.parametrize("op", ["ln", "rms", "fused_add_rms", "fused_add_ln", "softmax"])
 @pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
 def test_workgroup_path_128k_rows(op, dtype):
-    # rows of 64-128 KiB: softmax and RMSNorm in one 16-wave workgroup holding 8 chunks per
-    # lane (x read once); the other ops take the split-row path there
+    # rows of 64-128 KiB: softmax, RMSNorm and LayerNorm in one 16-wave workgroup holding 8
+    # chunks per lane (x read once); the fused ops take the split-row path there
     for rows, N in BIG_SHAPES[dtype]:
         td = TD[dtype]
         st, info = rn.plan(op, rows, N, td, workspace_bytes=rn.forward_workspace_bytes(op, rows, N, td))
-        if op in ("softmax", "rms"):
+        if op in ("softmax", "rms", "ln"):
             assert st == 0 and info["variant"] == "workgroup" and info["chunks_per_lane"] == 8, info
         else:
             assert st == 0 and info["variant"] == "wide", info

@@ -2,7 +2,7 @@
 workgroup holds): x is read once, the segments of a row exchange their statistics records
 through the workspace. Checked bit for bit against the two-launch form (the same records,
 combined in the same order; chosen by giving a workspace too small for the one-pass layout),
-with records forced to be computed by the waiting workgroups (RN_FWD_WAIT_POLLS=0), and
+with every record computed from memory by every workgroup of its row (RN_FWD_WAIT_POLLS=0), and
 against the fp64 oracle. Calls go through rn_forward_ex with device pointers."""
 
 import ctypes
@@ -107,13 +107,14 @@ def test_one_pass_matches_two_launches_and_oracle(base, dtype, rows, N, monkeypa
     two = _forward(w, g, torch.empty(_two_pass_bytes(rows, N), dtype=torch.uint8, device=DEV))
     for k in one:
         assert torch.equal(_bits(one[k]), _bits(two[k])), k
-    # every other segment's record computed by the waiting workgroups: the same bits again
+    # every record of a row computed by each of the row's workgroups from memory: the same
+    # bits again
     monkeypatch.setenv("RN_FWD_WAIT_POLLS", "0")
     local = _forward(w, g, ws)
     computed = int(ws[4:8].view(torch.int32).item())
     monkeypatch.delenv("RN_FWD_WAIT_POLLS")
     S = -(-(N * ESZ[dtype]) // 32768)
-    assert 0 < computed <= rows * S * (S - 1)
+    assert computed == rows * S * S
     for k in one:
         assert torch.equal(_bits(one[k]), _bits(local[k])), k
     _oracle_check(w, inp, one)
