@@ -120,6 +120,24 @@ def test_one_pass_matches_two_launches_and_oracle(base, dtype, rows, N, monkeypa
     _oracle_check(w, inp, one)
 
 
+@pytest.mark.parametrize("base,dtype,rows,N", [
+    (workloads.C2, "fp32", 333, 65536),        # blocks of 4 rows, then 65 rows in single-row tickets
+    (workloads.FUSED_LN, "bf16", 320, 65536),  # 4 segments; blocks of several rows and a tail
+], ids=lambda v: getattr(v, "name", str(v)))
+def test_one_pass_blocks_and_tail_tickets(base, dtype, rows, N):
+    # enough rows that blocks hold several rows (about rows / 4 blocks against the resident
+    # grid's res / S) and the last round goes in single-row tickets
+    w = base.scaled(rows=rows, N=N, seed=1660 + rows, dtype=dtype)
+    inp = workloads.make_inputs(w)
+    g = {k: v.to(DEV) for k, v in inp.items()}
+    need = rn.forward_workspace_bytes(w.op, rows, N, g["x"].dtype)
+    one = _forward(w, g, torch.empty(need, dtype=torch.uint8, device=DEV))
+    two = _forward(w, g, torch.empty(_two_pass_bytes(rows, N), dtype=torch.uint8, device=DEV))
+    for k in one:
+        assert torch.equal(_bits(one[k]), _bits(two[k])), k
+    _oracle_check(w, inp, one)
+
+
 def test_in_place_split_rows_take_two_launches(monkeypatch):
     # In place (y over x; residual_out over the residual and y over x) a waiting workgroup
     # could compute another segment's record from data its owner has already overwritten,
