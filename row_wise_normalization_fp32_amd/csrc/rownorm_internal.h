@@ -138,7 +138,7 @@ constexpr int kBwdWaitPolls = 1 << 12;   // one-pass split rows: polls of a miss
 constexpr int kBwdOnePassMaxSeg = 256;   // one-pass split rows: at most this many segments per row
 constexpr int kWideOnePassMaxSeg = 256;  // forward one-pass split rows: at most this many segments per row
 constexpr int kWideWaitPolls = 1 << 12;  // forward one-pass split rows: polls of a missing record
-constexpr int kWideOnePassRows = 4;      // forward one-pass split rows: rows per ticket (row block)
+constexpr int kWideOnePassRows = 8;      // forward one-pass split rows: rows per ticket (row block)
 constexpr int kBwdTargetChunks = 2;    // backward: about 2 chunks of x and of dy per lane (1 measured slower)
 
 // Enqueue the planned kernel for one I/O dtype (one translation unit per dtype and mode).

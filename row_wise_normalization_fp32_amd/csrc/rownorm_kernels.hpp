@@ -2506,9 +2506,11 @@ inline hipError_t go_wide_onepass(const Plan& plan, const Params& p, const WideA
     const int64_t res = static_cast<int64_t>(cus) * per_cu;
     if (res < 2 * static_cast<int64_t>(wa0.S)) return hipErrorNotSupported;
     // Blocks of about kWideOnePassRows rows (at least enough blocks to fill the resident
-    // grid): measured on MI355X, LayerNorm fp32 1024 x 65536: 16 rows per block 114.3 us, 8
-    // 109.0, 4 107.9; 512 rows: 8 rows 62.5 us, 4 63.3; 2048 rows: 32 rows 214.0 us, 8 201.6,
-    // 4 200.0. Rejected (same shapes): three rows loaded ahead instead of two (1024 rows:
+    // grid). Measured on MI355X with the single-row tail below, rows per block 4 / 8:
+    // LayerNorm fp32 x 65536, 512 rows 61.8 / 61.1 us, 1024 rows 106.2 / 107.6 us, 2048 rows
+    // 200.7 / 200.6 us; LayerNorm bf16 1024 x 131072 119.9 / 114.9 us; fused add + RMSNorm
+    // fp16 1024 x 65536 116.1 / 97.8 us (6 and 12 rows: 5-16% slower). Without the tail,
+    // LayerNorm fp32 1024 x 65536: 16 rows per block 114.3 us, 8 109.0, 4 107.9. Rejected (same shapes): three rows loaded ahead instead of two (1024 rows:
     // 112.9 us), each workgroup on one segment for the whole launch with per-segment block
     // counters (134 us: a row's segments were no longer processed together), and tickets
     // claimed a row ahead with the row pipeline running across tickets (112.6 us).
