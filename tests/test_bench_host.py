@@ -127,3 +127,35 @@ def test_plan_sweep_report():
     # top=1 keeps the fastest, the planner's and the slowest
     md1 = bench.plan_sweep_report(sweep, top=1)
     assert md1.count("| x |") == 1 and md1.count("W4xV2 persistent") == 1
+
+
+def test_traffic_summary_scales_and_attributes(tmp_path, monkeypatch):
+    import csv as _csv
+
+    def counters(d, prefix, rows):
+        d.mkdir()
+        with open(d / f"{prefix}_counter_collection.csv", "w", newline="") as f:
+            w = _csv.writer(f)
+            w.writerow(["Kernel_Name", "Grid_Size", "Workgroup_Size", "Counter_Value"])
+            w.writerows(rows)
+
+    copy = "void (anonymous namespace)::stream_copy_kernel<512, 2, true>(char const*, char*, long)"
+    k = "void rn::rownorm_vec_kernel<2, 0, 8, 4, 1, true, 3, 62>(rn::Params)"
+    # the copy reads 262144 KiB and writes 262144 KiB: FETCH_SIZE counts half, WRITE_SIZE all
+    counters(tmp_path / "cf", "cal", [[copy, 1024, 512, 131072.0]] * 3)
+    counters(tmp_path / "cw", "cal", [[copy, 1024, 512, 262144.0]] * 3)
+    counters(tmp_path / "pf", "pmc", [[k, 512 * 512, 512, 65536.0]] * 5)
+    counters(tmp_path / "pw", "pmc", [[k, 512 * 512, 512, 131072.0]] * 5)
+    tr = tmp_path / "tr"
+    tr.mkdir()
+    _write_trace(tr, [("bench:C5_ln_bf16_4096x16384:cold", 0, 10 ** 6)],
+                 [(k, 10 + i, 45000, 512, 512 * 512) for i in range(30)])
+    out = bench.traffic_summary(str(tmp_path / "pf"), str(tmp_path / "pw"), str(tmp_path / "cf"),
+                                str(tmp_path / "cw"), str(tr))
+    # 65536 KiB * 2 + 131072 KiB = 262144 KiB per launch, recorded under the headline's key
+    assert "ln_bf16_4096x16384 traffic_bytes_per_launch: 268435456" in out
+    assert f"kernel_source_sha256_16: {bench.kernel_source_hash()}" in out
+    rec = tmp_path / "rec.txt"
+    rec.write_text(out)
+    monkeypatch.setattr(bench, "COUNTERS_FILE", str(rec))
+    assert bench.counter_traffic("ln_bf16_4096x16384") == 268435456
