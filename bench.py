@@ -641,8 +641,30 @@ def plan_sweep_shapes():
         (c5.scaled(rows=4096, N=65536, name="ln_bf16_4096x65536"), "128 KiB LayerNorm rows, more rows"),
         (sm.scaled(rows=512, N=65536, name="softmax_fp32_512x65536"), "256 KiB fp32 softmax rows: one 16-wave "
                                                                       "workgroup against split rows"),
-        (workloads.C1.scaled(rows=8192, N=4095, name="ln_fp32_8192x4095"), "ragged fp32 rows: element kernel "
-                                                                           "against the general kernel"),
+        (workloads.C1.scaled(rows=8192, N=4095, name="ln_fp32_8192x4095"), "ragged fp32 rows: byte-addressed "
+                                                                           "vectorized kernel against the element "
+                                                                           "and general kernels"),
+        (c5.scaled(rows=16384, N=4095, name="ln_bf16_16384x4095"), "ragged 16-bit rows: byte-addressed vectorized "
+                                                                   "kernel against the pair kernel"),
+        (workloads.C3.scaled(rows=16384, N=4095, name="rms_fp16_16384x4095"), "ragged RMSNorm fp16 rows"),
+        (workloads.C4_BF16.scaled(rows=8192, N=4095, name="fused_bf16_8192x4095"), "ragged fused add + RMSNorm "
+                                                                                  "bf16 rows"),
+        (sm.scaled(rows=8192, N=4097, name="softmax_fp32_8192x4097"), "ragged fp32 softmax rows (8 waves)"),
+        (c5.scaled(rows=4096, N=16383, name="ln_bf16_4096x16383"), "ragged 8-wave LayerNorm rows"),
+        (workloads.C1.scaled(rows=16384, N=1023, name="ln_fp32_16384x1023"), "ragged one-wave LayerNorm rows"),
+        (workloads.C3.scaled(rows=8192, N=8191, dtype="bf16", name="rms_bf16_8192x8191"), "ragged 4-wave RMSNorm "
+                                                                                          "bf16 rows"),
+        (workloads.C3.scaled(rows=4096, N=16383, name="rms_fp16_4096x16383"), "ragged 8-wave RMSNorm fp16 rows"),
+        (workloads.C4_FP16.scaled(rows=8192, N=8191, name="fused_fp16_8192x8191"), "ragged 4-wave fused add + "
+                                                                                   "RMSNorm rows"),
+        (fln.scaled(rows=8192, N=8191, name="fused_ln_bf16_8192x8191"), "ragged 4-wave fused add + LayerNorm rows"),
+        (sm.scaled(rows=8192, N=8191, dtype="bf16", name="softmax_bf16_8192x8191"), "ragged 4-wave bf16 softmax "
+                                                                                    "rows"),
+        (c5.scaled(rows=16384, N=4088, name="ln_bf16_16384x4088"), "whole-chunk rows that do not fill the row group "
+                                                                   "(511 of 512 chunks): byte-addressed persistent "
+                                                                   "against grid per row"),
+        (workloads.C3.scaled(rows=8192, N=4092, dtype="fp32", name="rms_fp32_8192x4092"), "fp32 rows of 1023 of "
+                                                                                          "1024 chunks"),
         (workloads.C1.scaled(rows=1024, N=65537, name="ln_fp32_1024x65537"), "long ragged rows: element-granular "
                                                                              "split rows against the general "
                                                                              "kernel"),
@@ -695,7 +717,9 @@ def plan_candidates(rn, w, s0, cus):
     # (as the binding calls them: a workspace only for the split-row variants)
     ws = rn.forward_workspace_bytes(w.op, w.rows, w.N, td)
     vec = auto["variant"] in ("wave", "workgroup")
-    for v in ("element", "general", "wide", "wide_element") if vec else \
+    # (byte-addressed rows are an automatic choice: forcing the wave / workgroup variant gives the
+    # grid-per-row kernel of whole-chunk rows, when the rows are whole chunks)
+    for v in ("element", "general", "wide", "wide_element") if vec and not auto.get("ragged") else \
             ("wave", "workgroup", "element", "general", "wide", "wide_element"):
         wsv = ws if v in ("wide", "wide_element") else 0
         st, info = rn.plan(w.op, w.rows, w.N, td, ptrs=ptrs, eps=w.eps, variant=v, workspace_bytes=wsv)

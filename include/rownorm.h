@@ -372,6 +372,13 @@ typedef struct rn_plan_info {
     int pairs;             /* element variant: 1 if each lane slot holds two adjacent 16-bit
                               elements moved as one 4-byte word (chunks_per_lane then counts
                               such slots) */
+    int ragged;            /* vectorized variants: 1 if rows are addressed by byte (persistent
+                              launches of many rows whose rows, row strides or tensors are not
+                              whole 16-byte chunks, or whose rows do not fill the row group
+                              exactly): 16-byte accesses at element alignment, the row's partial
+                              last chunk moved by its whole dwords and, for an odd-length 16-bit
+                              row, one 2-byte access; chunks_per_lane counts 16-byte chunks, the
+                              last one partial, and exact is 1 when they fill the row group */
 } rn_plan_info;
 
 int rn_plan(int op, const void* x, const void* residual, const void* gamma, const void* beta, const void* y,

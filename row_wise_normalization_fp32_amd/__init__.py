@@ -52,7 +52,7 @@ class RowStrides(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [("variant", _ci), ("waves_per_row", _ci), ("rows_per_block", _ci), ("block_threads", _ci),
                 ("chunks_per_lane", _ci), ("grid_blocks", _i64), ("exact", _ci), ("persistent", _ci),
-                ("lds_bytes", _ci), ("pairs", _ci)]
+                ("lds_bytes", _ci), ("pairs", _ci), ("ragged", _ci)]
 
 
 class Tuning(ctypes.Structure):
@@ -520,4 +520,4 @@ def plan(op: str, rows: int, N: int, dtype: torch.dtype, *, ptrs: Optional[dict]
                 "rows_per_block": info.rows_per_block, "block_threads": info.block_threads,
                 "chunks_per_lane": info.chunks_per_lane, "grid_blocks": info.grid_blocks,
                 "exact": bool(info.exact), "persistent": bool(info.persistent), "lds_bytes": info.lds_bytes,
-                "pairs": bool(info.pairs)}
+                "pairs": bool(info.pairs), "ragged": bool(info.ragged)}

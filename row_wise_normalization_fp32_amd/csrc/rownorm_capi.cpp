@@ -170,6 +170,7 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     plan->persistent = false;
     plan->lds_bytes = 0;
     plan->pairs = false;
+    plan->ragged = false;
     *chunks = 0;
     if (rows == 0) return RN_OK;
 
@@ -230,9 +231,28 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
         if (reinterpret_cast<uintptr_t>(bufs[i].p) % 16 != 0) vec_ok = false;
         if ((bufs[i].stride * s) % 16 != 0) vec_ok = false;
     }
-    const int64_t C = vec_ok ? (N * s) / 16 : 0;
     const int64_t wave_cap = int64_t(64) * rn::kMaxWaveChunks;                         // 1024 chunks
     const int64_t group_cap = int64_t(64) * rn::kMaxGroupWaves * rn::kMaxGroupChunks;  // 4096 chunks
+    // Ragged rows (rows, tensors or row strides that are not whole 16-byte chunks; every
+    // tensor element-aligned), many of them: the persistent vectorized kernel with rows
+    // addressed by byte (16-byte accesses at element alignment, which the hardware performs,
+    // and the row's partial last chunk by its whole dwords and one 2-byte access), for rows of
+    // up to 4096 chunks. The same kernel takes aligned rows of whole chunks that do not fill
+    // their row group exactly (the grid-per-row kernel would take them otherwise). Fewer rows
+    // (under kPersistentVecBlocks row blocks) take the element / pair kernels, or the
+    // grid-per-row kernel.
+    const int64_t Cr = (N * s + 15) / 16;
+    bool ragged = false;
+    if (Cr <= group_cap && a.variant == RN_VARIANT_AUTO) {
+        int wr = next_pow2((Cr + 64 * rn::kTargetChunks - 1) / (64 * rn::kTargetChunks));
+        if (wr > rn::kMaxGroupWaves) wr = rn::kMaxGroupWaves;
+        const int64_t rpb = wr <= 4 ? 4 / wr : 1;
+        const int64_t vr = next_pow2((Cr + 64 * wr - 1) / (64 * wr));
+        const bool fills = Cr == int64_t(64) * wr * vr;  // the row group holds the row exactly
+        ragged = (!vec_ok || !fills) && (rows + rpb - 1) / rpb >= rn::kPersistentVecBlocks;
+    }
+    if (tune && ragged) return RN_ERR_UNSUPPORTED;  // a tuning applies to whole-chunk rows only
+    const int64_t C = vec_ok ? (N * s) / 16 : (ragged ? Cr : 0);
     const int64_t elem_cap = int64_t(64) * rn::kMaxGroupWaves * rn::kElemMaxPerLane;   // 16384 elements
     // Softmax keeps no parameters in registers: its element / pair kernels hold rows of up to
     // 65536 elements in one 16-wave workgroup (x read once) instead of splitting them.
@@ -263,7 +283,7 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
 
     int v = a.variant;
     if (v == RN_VARIANT_AUTO) {
-        if (vec_ok && C <= big_cap)
+        if ((vec_ok && C <= big_cap) || ragged)
             v = w_auto == 1 ? RN_VARIANT_WAVE : RN_VARIANT_WORKGROUP;
         else if (vec_ok && ws_given)
             v = RN_VARIANT_WIDE;
@@ -307,11 +327,11 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     }
     int W = 0;
     if (v == RN_VARIANT_WAVE) {
-        if (!vec_ok || C > wave_cap) return RN_ERR_UNSUPPORTED;
+        if (!(vec_ok || ragged) || C > wave_cap) return RN_ERR_UNSUPPORTED;
         W = 1;
         plan->variant = rn::V_WAVE;
     } else if (v == RN_VARIANT_WORKGROUP) {
-        if (!vec_ok || C > big_cap) return RN_ERR_UNSUPPORTED;
+        if (!(vec_ok || ragged) || C > big_cap) return RN_ERR_UNSUPPORTED;
         W = w_auto < 2 ? 2 : w_auto;
         plan->variant = rn::V_WORKGROUP;
     } else if (v == RN_VARIANT_ELEMENT) {
@@ -386,6 +406,7 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     plan->grid = blocks < rn::kMaxGrid ? blocks : rn::kMaxGrid;
     const bool vec = plan->variant == rn::V_WAVE || plan->variant == rn::V_WORKGROUP;
     plan->exact = vec && C == int64_t(64) * W * plan->chunks_per_lane;
+    plan->ragged = ragged;
     // Persistent launch: for exact shapes with enough rows that workgroups would otherwise
     // be launched many times over, and for the element / pair kernels with many rows.
     // Measured on MI355X (cold cache): vectorized launches gain from 256 workgroups up
@@ -396,7 +417,7 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     // Parameters go to LDS once per workgroup; the LayerNorm ops with both keep gamma in
     // VGPRs and stage only beta, so the LDS need is at most one row (64 KiB).
     const bool has_params = a.gamma != nullptr || (ln && a.beta != nullptr);
-    plan->persistent = (vec && plan->exact && C <= group_cap && blocks >= rn::kPersistentVecBlocks) ||
+    plan->persistent = (vec && plan->exact && C <= group_cap && blocks >= rn::kPersistentVecBlocks) || ragged ||
                        (plan->variant == rn::V_ELEMENT && blocks >= rn::kPersistentBlocks);
     if (tune) {
         const rn_tuning& t = *a.tune;
@@ -863,6 +884,7 @@ int rn_plan_backward(int op, const void* dy, const void* x, const void* gamma, c
         out->persistent = plan.persistent ? 1 : 0;
         out->lds_bytes = plan.lds_bytes;
         out->pairs = plan.pairs ? 1 : 0;
+        out->ragged = plan.ragged ? 1 : 0;
     }
     return st;
 }
@@ -894,6 +916,7 @@ int rn_plan_tuned(int op, const void* x, const void* residual, const void* gamma
         out->persistent = plan.persistent ? 1 : 0;
         out->lds_bytes = plan.lds_bytes;
         out->pairs = plan.pairs ? 1 : 0;
+        out->ragged = plan.ragged ? 1 : 0;
     }
     return st;
 }
@@ -919,6 +942,7 @@ int rn_plan(int op, const void* x, const void* residual, const void* gamma, cons
         out->persistent = plan.persistent ? 1 : 0;
         out->lds_bytes = plan.lds_bytes;
         out->pairs = plan.pairs ? 1 : 0;
+        out->ragged = plan.ragged ? 1 : 0;
     }
     return st;
 }

@@ -99,6 +99,8 @@ struct Plan {
     bool persistent;      // parameters staged on chip once, grid sized to resident capacity
     int lds_bytes;        // dynamic LDS of a persistent launch
     bool pairs;           // element variant, 16-bit: slots of two adjacent elements (pair kernel)
+    bool ragged = false;  // vectorized variants, persistent: rows addressed by byte (row starts,
+                          // tensors or row lengths that are not whole 16-byte chunks)
     // Caller-chosen launch (rn_forward_tuned / rn_plan_tuned); the automatic plan leaves these
     // at their defaults.
     int64_t grid_force = 0;  // persistent vectorized launches: workgroups to launch (0: the grid rule)

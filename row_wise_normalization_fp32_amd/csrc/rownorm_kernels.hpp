@@ -384,6 +384,8 @@ enum {
                          // once per workgroup), only beta is staged in LDS (half the LDS)
     FL_PREFETCH = 64,    // grid-stride loop: the next row's loads are issued before the current
                          // row's reductions and stores (two rows of registers per lane)
+    FL_RAGGED = 128,     // rows addressed by byte: row starts and tensors need only element
+                         // alignment, and the row's last chunk may be partial (see VecRow)
 };
 
 template <int FL>
@@ -531,6 +533,89 @@ struct VecRow {
     static constexpr int NG = HG ? V : 1;
     static constexpr int NB = HB ? V : 1;
 
+    // FL_RAGGED: row r of a row tensor starts at byte r * ld * s, at any element-aligned
+    // address. The lane layout stays the aligned one (chunk c holds elements E c to E c + E - 1),
+    // and every chunk moves as one 16-byte access, which the hardware performs at any alignment,
+    // through a buffer resource that ends with the row. The hardware checks such a resource's
+    // range per dword (a dword of an access moves only if all of its 4 bytes lie inside), so
+    // the row's partial last chunk (N not a multiple of E) moves its whole dwords and reads 0
+    // for the rest, and nothing past the row is touched. What is left is the row's last element
+    // when a 16-bit row has an odd length: the low half of a dword that straddles the row's
+    // end. One 2-byte access moves it (issued by the waves holding that chunk, with an offset
+    // past the row on every lane but its own), and it joins the chunk where the row is first
+    // used, so that no load waits inside the row's batch of loads. The partial chunk's missing
+    // elements are masked out of the statistics.
+    static constexpr bool RAG = (FL & FL_RAGGED) != 0;
+    static constexpr int SB = 16 / E;                            // bytes per element
+    static constexpr int CPL = (FL & FL_NT_LOAD) != 0 ? 2 : 0;   // buffer cache policy: non-temporal
+    static constexpr int CPS = (FL & FL_NT_STORE) != 0 ? 2 : 0;
+    struct Rag {
+        uint32_t rb;  // bytes of the row
+        int te;       // elements of the partial chunk (0: none)
+        int ti;       // its slot (-1: none)
+        int tt;       // its lane in the row group
+        int hd;       // 16-bit rows of odd length: the partial chunk's dword holding the last
+                      // element in its low half; -1 otherwise
+    };
+    __device__ static __forceinline__ Rag rag(const Params& p) {
+        Rag g;
+        const int n = static_cast<int>(p.N);  // N <= 64 * W * V * E fits in 32 bits here
+        const int full = n / E;
+        g.rb = static_cast<uint32_t>(n) * SB;
+        g.te = n - full * E;
+        g.ti = g.te != 0 ? full / LANES : -1;
+        g.tt = full % LANES;
+        g.hd = SB == 2 && (n & 1) != 0 ? (g.te - 1) >> 1 : -1;
+        return g;
+    }
+    // The waves that hold the partial chunk's lane (the 2-byte access is issued by them only).
+    __device__ static __forceinline__ bool tail_wave(const Rag& g, int t) {
+        return g.hd >= 0 && __builtin_amdgcn_readfirstlane(t >> 6) == (g.tt >> 6);
+    }
+    // The last element of an odd-length 16-bit row, in the low half (0 on other lanes).
+    template <int CP>
+    __device__ static __forceinline__ unsigned tail_half(Rsrc r, const Rag& g, int t) {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(t == g.tt ? g.rb - 2u : g.rb), 0, CP);
+    }
+    __device__ static __forceinline__ u32x4 with_half(u32x4 v, unsigned h, const Rag& g) {
+        v.x |= g.hd == 0 ? h : 0u;
+        v.y |= g.hd == 1 ? h : 0u;
+        v.z |= g.hd == 2 ? h : 0u;
+        v.w |= g.hd == 3 ? h : 0u;
+        return v;
+    }
+    // The row at byte address `base`: its chunks into v, the last element of an odd-length
+    // 16-bit row into th on the lane that holds it (th is read only on that lane).
+    __device__ static __forceinline__ void rag_load_row(const char* base, const Rag& g, int t, int Ci, u32x4 (&v)[V],
+                                                        u32x4& th) {
+        const Rsrc r = make_rsrc(base, g.rb);
+#pragma unroll
+        for (int i = 0; i < V; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(r, chunk(i, t, Ci) * 16, 0, CPL);
+        if (tail_wave(g, t)) th.x = tail_half<CPL>(r, g, t);
+    }
+    __device__ static __forceinline__ void rag_store_row(char* base, const Rag& g, int i, int t, int Ci,
+                                                         const u32x4& v) {
+        const Rsrc r = make_rsrc(base, g.rb);
+        if (valid(i, t, Ci))  // the partial chunk: its whole dwords
+            __builtin_amdgcn_raw_buffer_store_b128(v, r, (i * LANES + t) * 16, 0, CPS);
+        if (i == g.ti && tail_wave(g, t)) {  // and the half dword of an odd-length 16-bit row
+            const unsigned h = g.hd == 0 ? v.x : g.hd == 1 ? v.y : g.hd == 2 ? v.z : v.w;
+            bstore16<CPS>(r, t == g.tt ? g.rb - 2u : g.rb, h);
+        }
+    }
+    // Chunk c of a parameter vector (element-aligned, N elements).
+    __device__ static __forceinline__ u32x4 param_chunk(const void* base, int c, const Rag& g) {
+        if constexpr (!RAG) {
+            return static_cast<const u32x4*>(base)[c];
+        } else {
+            const Rsrc r = make_rsrc(base, g.rb);
+            u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, c * 16, 0, 0);
+            if (g.hd >= 0 && c == g.ti * LANES + g.tt)
+                v = with_half(v, __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(g.rb - 2u), 0, 0), g);
+            return v;
+        }
+    }
+
     // Chunk of slot i for lane t, clamped into the row for idle lanes of a ragged tail.
     __device__ static __forceinline__ int chunk(int i, int t, int Ci) {
         const int c = i * LANES + t;
@@ -540,7 +625,13 @@ struct VecRow {
 
     // a1: issue every load of the row (and of the residual). Row strides are in chunks.
     __device__ static __forceinline__ void load_row(const Params& p, int64_t row, int t, int Ci, u32x4 (&xv)[V],
-                                                    u32x4 (&rv)[NR]) {
+                                                    u32x4 (&rv)[NR], u32x4& xt, u32x4& rt) {
+        if constexpr (RAG) {
+            const Rag g = rag(p);
+            rag_load_row(static_cast<const char*>(p.x) + row * p.ldx * SB, g, t, Ci, xv, xt);
+            if constexpr (OT::RES) rag_load_row(static_cast<const char*>(p.residual) + row * p.ldr * SB, g, t, Ci, rv, rt);
+            return;
+        }
         const u32x4* xr = static_cast<const u32x4*>(p.x) + row * p.cx;
 #pragma unroll
         for (int i = 0; i < V; ++i) xv[i] = ld<FL>(xr + chunk(i, t, Ci));
@@ -553,10 +644,11 @@ struct VecRow {
 
     __device__ static __forceinline__ void load_params(const Params& p, int t, int Ci, u32x4 (&gv)[NG],
                                                        u32x4 (&bv)[NB]) {
+        const Rag g = RAG ? rag(p) : Rag{};
 #pragma unroll
         for (int i = 0; i < V; ++i) {
-            if constexpr (HG) gv[i] = static_cast<const u32x4*>(p.gamma)[chunk(i, t, Ci)];
-            if constexpr (HB) bv[i] = static_cast<const u32x4*>(p.beta)[chunk(i, t, Ci)];
+            if constexpr (HG) gv[i] = param_chunk(p.gamma, chunk(i, t, Ci), g);
+            if constexpr (HB) bv[i] = param_chunk(p.beta, chunk(i, t, Ci), g);
         }
     }
 
@@ -581,27 +673,66 @@ struct VecRow {
     // form; the output is exp(x - max_w) * (exp(max_w - max) / sum).
     template <int PSRC>
     __device__ static __forceinline__ void norm_row(const Params& p, int64_t row, int lane, int wr, int t, int Ci,
-                                                    const u32x4 (&xv)[V], const u32x4 (&rv)[NR], u32x4 (&gv)[NG],
-                                                    u32x4 (&bv)[NB], const u32x4* lds, WavePart (*part)[WS],
-                                                    int& buf) {
+                                                    const u32x4 (&xv)[V], const u32x4 (&rv)[NR], const u32x4& xt,
+                                                    const u32x4& rt, u32x4 (&gv)[NG], u32x4 (&bv)[NB],
+                                                    const u32x4* lds, WavePart (*part)[WS], int& buf) {
+        const Rag g = RAG ? rag(p) : Rag{};
+        // RAG: the partial chunk joins its slot here, at the row's first use.
+        auto xin = [&](int i) {
+            u32x4 v = xv[i];
+            if constexpr (RAG) {
+                if (i == g.ti && g.hd >= 0 && t == g.tt) v = with_half(v, xt.x, g);
+            }
+            return v;
+        };
+        auto rin = [&](int i) {
+            u32x4 v = rv[OT::RES ? i : 0];
+            if constexpr (RAG) {
+                if (i == g.ti && g.hd >= 0 && t == g.tt) v = with_half(v, rt.x, g);
+            }
+            return v;
+        };
+        // RAG: in the slot that holds the partial chunk (a uniform branch), its missing
+        // elements take the value `fill` on the lane that holds it, so that they add exactly 0
+        // to a sum of (f - fill) terms; the other slots are left alone
+        auto fill_tail = [&](int i, float(&f)[E], float fill) {
+            if constexpr (RAG) {
+                if (i == g.ti) {
+                    const bool me = t == g.tt;
+#pragma unroll
+                    for (int e = 0; e < E; ++e) f[e] = (me && e >= g.te) ? fill : f[e];
+                }
+            }
+        };
+        // element e of slot i is part of the row
+        auto ok = [&](int i, int e) {
+            if constexpr (RAG)
+                return valid(i, t, Ci) && !(i == g.ti && t == g.tt && e >= g.te);
+            else
+                return valid(i, t, Ci);
+        };
         // Chunk i as the kernel sees it: the input, or for the fused ops the rounded sum.
         u32x4 src[V];
         if constexpr (OT::RES) {
             // ---- a2: t = round(x + residual), stored as residual_out; t is what gets normalized.
             u32x4* ro = static_cast<u32x4*>(p.residual_out) + row * p.cro;
+            char* rob = static_cast<char*>(p.residual_out) + row * p.ldro * SB;
 #pragma unroll
             for (int i = 0; i < V; ++i) {
                 float a[E], b[E];
-                IO::unpack(xv[i], a);
-                IO::unpack(rv[i], b);
+                IO::unpack(xin(i), a);
+                IO::unpack(rin(i), b);
 #pragma unroll
                 for (int e = 0; e < E; ++e) a[e] += b[e];
                 src[i] = IO::pack(a);
-                if (valid(i, t, Ci)) st<FL>(ro + i * LANES + t, src[i]);
+                if constexpr (RAG)
+                    rag_store_row(rob, g, i, t, Ci, src[i]);
+                else if (valid(i, t, Ci))
+                    st<FL>(ro + i * LANES + t, src[i]);
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < V; ++i) src[i] = xv[i];
+            for (int i = 0; i < V; ++i) src[i] = xin(i);
         }
         if constexpr (!EXACT && !OT::SM) {
 #pragma unroll
@@ -613,6 +744,9 @@ struct VecRow {
             n_w = static_cast<float>(p.N);
         } else if constexpr (EXACT) {
             n_w = static_cast<float>(V * 64 * E);
+            if constexpr (RAG) {
+                if (g.ti >= 0 && (g.tt >> 6) == wr) n_w -= static_cast<float>(E - g.te);  // the partial chunk's wave
+            }
         } else {
             int cnt = 0;
 #pragma unroll
@@ -620,7 +754,13 @@ struct VecRow {
                 const int k = Ci - (i * LANES + wr * 64);
                 cnt += k <= 0 ? 0 : (k >= 64 ? 64 : k);
             }
-            n_w = static_cast<float>(cnt * E);
+            if constexpr (RAG) {
+                if (g.ti >= 0 && (g.tt >> 6) == wr) cnt = cnt * E - (E - g.te);  // the partial chunk's wave
+                else cnt *= E;
+                n_w = static_cast<float>(cnt);
+            } else {
+                n_w = static_cast<float>(cnt * E);
+            }
         }
 
         // NOFLOAT: the widened row is not kept; the epilogue widens the packed row again.
@@ -639,6 +779,7 @@ struct VecRow {
                 for (int i = 0; i < V; ++i) {
                     float f[E];
                     IO::unpack(src[i], f);
+                    fill_tail(i, f, K);
 #pragma unroll
                     for (int e = 0; e < E; ++e) s1 += valid(i, t, Ci) ? f[e] - K : 0.f;
                 }
@@ -654,9 +795,10 @@ struct VecRow {
             for (int i = 0; i < V; ++i) {
                 float f[E];
                 IO::unpack(src[i], f);
+                if constexpr (DT == DT_F32) fill_tail(i, f, a);  // (16-bit rows: fewer VGPRs masked)
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    const float d = valid(i, t, Ci) ? f[e] - a : 0.f;
+                    const float d = (DT == DT_F32 ? valid(i, t, Ci) : ok(i, e)) ? f[e] - a : 0.f;
                     if constexpr (!NOFLOAT) v[i][e] = d;
                     c += d;
                     q = fmaf(d, d, q);
@@ -668,7 +810,8 @@ struct VecRow {
             const float cw = Cw * inv_w;
             // ---- a5: per-wave (n, a, mean - a, M2), combined across the row group in LDS.
             float rel, m2, mean;
-            group_moments<W, EXACT>(part, buf, lane, wr, n_w, a, cw, fmaxf(Qw - Cw * cw, 0.f), rel, m2, mean);
+            // (ragged rows: the partial chunk's wave holds fewer elements, so the general combine)
+            group_moments<W, EXACT && !RAG>(part, buf, lane, wr, n_w, a, cw, fmaxf(Qw - Cw * cw, 0.f), rel, m2, mean);
             if (t == 0 && p.mean) p.mean[row] = mean;
             // ---- a6: finalize.
             scale = inv_sqrt(fmaf(m2, p.inv_n, p.eps));
@@ -681,7 +824,7 @@ struct VecRow {
                 float f[E];
                 IO::unpack(src[i], f);
 #pragma unroll
-                for (int e = 0; e < E; ++e) mx = valid(i, t, Ci) ? max_nan(mx, f[e]) : mx;
+                for (int e = 0; e < E; ++e) mx = ok(i, e) ? max_nan(mx, f[e]) : mx;
             }
             const float mw = wave_max(mx);
             // exp(x - m_w): x - m_w is exact for the elements near the maximum.
@@ -692,7 +835,7 @@ struct VecRow {
                 IO::unpack(src[i], f);
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
-                    const float ex = valid(i, t, Ci) ? exp_neg(f[e] - mw) : 0.f;
+                    const float ex = ok(i, e) ? exp_neg(f[e] - mw) : 0.f;
                     v[i][e] = ex;
                     s += ex;
                 }
@@ -728,9 +871,10 @@ struct VecRow {
             }
         }
         u32x4* yr = static_cast<u32x4*>(p.y) + row * p.cy;
+        char* yb = static_cast<char*>(p.y) + row * p.ldy * SB;
 #pragma unroll
         for (int i = 0; i < V; ++i) {
-            float g[E], b[E], o[E];
+            float gm[E], b[E], o[E];
             float w[E];  // NOFLOAT: x - a of this chunk
             if constexpr (NOFLOAT) {
                 IO::unpack(src[i], w);
@@ -741,14 +885,14 @@ struct VecRow {
                 const int c = chunk(i, t, Ci);
                 constexpr bool GREG = (FL & FL_GAMMA_REG) != 0 && HG && HB;
                 if constexpr (GREG) {
-                    IO::unpack(gv[i], g);
+                    IO::unpack(gv[i], gm);
                     IO::unpack(lds[c], b);
                 } else {
-                    if constexpr (HG) IO::unpack(lds[c], g);
+                    if constexpr (HG) IO::unpack(lds[c], gm);
                     if constexpr (HB) IO::unpack(lds[(HG ? Ci : 0) + c], b);
                 }
             } else {
-                if constexpr (HG) IO::unpack(gv[i], g);
+                if constexpr (HG) IO::unpack(gv[i], gm);
                 if constexpr (HB) IO::unpack(bv[i], b);
             }
 #pragma unroll
@@ -760,15 +904,18 @@ struct VecRow {
                     z = OT::LN ? fmaf(v[i][e], scale, offset) : v[i][e] * scale;
                 }
                 if constexpr (HG && HB) {
-                    z = fmaf(z, g[e], b[e]);
+                    z = fmaf(z, gm[e], b[e]);
                 } else if constexpr (HG) {
-                    z = z * g[e];
+                    z = z * gm[e];
                 } else if constexpr (HB) {
                     z = z + b[e];
                 }
                 o[e] = z;
             }
-            if (valid(i, t, Ci)) st<FL>(yr + i * LANES + t, IO::pack(o));
+            if constexpr (RAG)
+                rag_store_row(yb, g, i, t, Ci, IO::pack(o));
+            else if (valid(i, t, Ci))
+                st<FL>(yr + i * LANES + t, IO::pack(o));
         }
     }
 };
@@ -801,18 +948,20 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_vec_kernel(Params p) {
     int64_t base = static_cast<int64_t>(blockIdx.x) * RPB;
     // Row registers: xa / ra hold the row being processed; with FL_PREFETCH, xb / rb the next.
     u32x4 xa[V], ra[R::NR], xb[PF ? V : 1], rb[PF ? R::NR : 1];
+    u32x4 xta, rta, xtb, rtb;  // FL_RAGGED: the partial chunk of the rows in xa / ra and xb / rb
     if constexpr (PLDS) {
+        const typename R::Rag g = R::RAG ? R::rag(p) : typename R::Rag{};
         for (int c = threadIdx.x; c < Ci; c += 64 * W * RPB) {
             if constexpr (GREG) {
-                prm[c] = static_cast<const u32x4*>(p.beta)[c];
+                prm[c] = R::param_chunk(p.beta, c, g);
             } else {
-                if constexpr (R::HG) prm[c] = static_cast<const u32x4*>(p.gamma)[c];
-                if constexpr (R::HB) prm[(R::HG ? Ci : 0) + c] = static_cast<const u32x4*>(p.beta)[c];
+                if constexpr (R::HG) prm[c] = R::param_chunk(p.gamma, c, g);
+                if constexpr (R::HB) prm[(R::HG ? Ci : 0) + c] = R::param_chunk(p.beta, c, g);
             }
         }
         if constexpr (GREG) {
 #pragma unroll
-            for (int i = 0; i < V; ++i) gkeep[i] = static_cast<const u32x4*>(p.gamma)[R::chunk(i, t, Ci)];
+            for (int i = 0; i < V; ++i) gkeep[i] = R::param_chunk(p.gamma, R::chunk(i, t, Ci), g);
         }
         __syncthreads();
     }
@@ -832,28 +981,29 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_vec_kernel(Params p) {
             int tl = t;
             asm volatile("" : "+v"(tl));
             u32x4 gv[R::NG], bv[R::NB];
-            R::load_row(p, row, tl, Ci, xa, ra);
+            R::load_row(p, row, tl, Ci, xa, ra, xta, rta);
             if constexpr (PSRC == R::PARAMS_REG) R::load_params(p, tl, Ci, gv, bv);
             if constexpr (GREG) {
 #pragma unroll
                 for (int i = 0; i < V; ++i) gv[i] = gkeep[i];
             }
             __builtin_amdgcn_sched_barrier(0);  // every load of the row is issued before any use
-            R::template norm_row<PSRC>(p, row, lane, wr, tl, Ci, xa, ra, gv, bv, prm, part[rg], buf);
+            R::template norm_row<PSRC>(p, row, lane, wr, tl, Ci, xa, ra, xta, rta, gv, bv, prm, part[rg], buf);
         }
     } else {
         static_assert(PSRC == R::PARAMS_LDS || !(R::HG || R::HB), "the prefetching loop stages the parameters");
         {
             int tl = t;
             asm volatile("" : "+v"(tl));
-            if (base + rg < p.rows) R::load_row(p, base + rg, tl, Ci, xa, ra);
+            if (base + rg < p.rows) R::load_row(p, base + rg, tl, Ci, xa, ra, xta, rta);
         }
         // One row: its registers (xc, rc) are already loaded; the row one stride further is
         // loaded into (xn, rn) first.
-        auto one = [&](int64_t row, u32x4(&xc)[V], u32x4(&rc)[R::NR], u32x4(&xn)[V], u32x4(&rn)[R::NR]) {
+        auto one = [&](int64_t row, u32x4(&xc)[V], u32x4(&rc)[R::NR], u32x4& xtc, u32x4& rtc, u32x4(&xn)[V],
+                       u32x4(&rn)[R::NR], u32x4& xtn, u32x4& rtn) {
             int tl = t;
             asm volatile("" : "+v"(tl));
-            if (row + stride < p.rows) R::load_row(p, row + stride, tl, Ci, xn, rn);
+            if (row + stride < p.rows) R::load_row(p, row + stride, tl, Ci, xn, rn, xtn, rtn);
             u32x4 gv[R::NG], bv[R::NB];
             if constexpr (GREG) {
 #pragma unroll
@@ -861,17 +1011,17 @@ __global__ __launch_bounds__(64 * W * RPB) void rownorm_vec_kernel(Params p) {
             }
             __builtin_amdgcn_sched_barrier(0);
             if (row < p.rows) {
-                R::template norm_row<PSRC>(p, row, lane, wr, tl, Ci, xc, rc, gv, bv, prm, part[rg], buf);
+                R::template norm_row<PSRC>(p, row, lane, wr, tl, Ci, xc, rc, xtc, rtc, gv, bv, prm, part[rg], buf);
             } else if constexpr (W > 1) {
                 __syncthreads();  // a row group without a row still takes part in the barrier
                 buf ^= 1;
             }
         };
         while (base < p.rows) {
-            one(base + rg, xa, ra, xb, rb);
+            one(base + rg, xa, ra, xta, rta, xb, rb, xtb, rtb);
             base += stride;
             if (base >= p.rows) break;
-            one(base + rg, xb, rb, xa, ra);
+            one(base + rg, xb, rb, xtb, rtb, xa, ra, xta, rta);
             base += stride;
         }
     }
@@ -2224,11 +2374,11 @@ inline hipError_t launch_grid(const Plan& plan, const Params& p, hipStream_t str
 
 // One vectorized launch: persistent (the prefetching instance, or the looping one for wide
 // rows with parameters when R > 3) or grid per row.
-template <int DT, int OP, int W, int V, bool EXACT, int AFF, bool PERS>
+template <int DT, int OP, int W, int V, bool EXACT, int AFF, bool PERS, bool RAG = false>
 inline hipError_t go_v(const Plan& plan, const Params& p, hipStream_t s) {
     constexpr int RPB = rows_per_block_for(W);
     if constexpr (PERS) {
-        constexpr int FL = persistent_flags<OP, AFF>();
+        constexpr int FL = persistent_flags<OP, AFF>() | (RAG ? FL_RAGGED : 0);
         // 1024-lane workgroups have no registers for a second row, nor have one-wave rows of 8
         // or more chunks per lane (reached only by forcing the wave variant): they loop
         // without prefetching, as do wide rows with parameters when R > 2.
@@ -2267,11 +2417,24 @@ inline hipError_t go_v(const Plan& plan, const Params& p, hipStream_t s) {
     }
 }
 
-template <int DT, int OP, int W, bool EXACT, int AFF, bool PERS>
+template <int DT, int OP, int W, bool EXACT, int AFF, bool PERS, bool RAG = false>
 inline hipError_t launch_v(const Plan& plan, const Params& p, hipStream_t s) {
     constexpr int RPB = rows_per_block_for(W);
     if (plan.rows_per_block != RPB) return hipErrorInvalidValue;
-#define RN_GO(VV) go_v<DT, OP, W, VV, EXACT, AFF, PERS>(plan, p, s)
+#define RN_GO(VV) go_v<DT, OP, W, VV, EXACT, AFF, PERS, RAG>(plan, p, s)
+    // Ragged rows (persistent only): the planner's shapes, about 4 chunks per lane (fewer
+    // only for one-wave rows).
+    if constexpr (RAG) {
+        if (plan.chunks_per_lane == 4) return RN_GO(4);
+        if constexpr (W == 1) {
+            switch (plan.chunks_per_lane) {
+            case 1: return RN_GO(1);
+            case 2: return RN_GO(2);
+            default: break;
+            }
+        }
+        return hipErrorNotSupported;
+    }
     // The planner gives rows of 8 and 16 waves 4 chunks per lane (or 8 / 16 for the one-
     // workgroup rows below); fewer chunks per lane occur only with 1, 2 and 4 waves.
     if constexpr (W <= 4) {
@@ -2302,14 +2465,14 @@ inline hipError_t launch_v(const Plan& plan, const Params& p, hipStream_t s) {
     return hipErrorNotSupported;  // no instance of this shape is built
 }
 
-template <int DT, int OP, bool EXACT, int AFF, bool PERS>
+template <int DT, int OP, bool EXACT, int AFF, bool PERS, bool RAG = false>
 inline hipError_t launch_w(const Plan& plan, const Params& p, hipStream_t s) {
     switch (plan.waves_per_row) {
-    case 1: return launch_v<DT, OP, 1, EXACT, AFF, PERS>(plan, p, s);
-    case 2: return launch_v<DT, OP, 2, EXACT, AFF, PERS>(plan, p, s);
-    case 4: return launch_v<DT, OP, 4, EXACT, AFF, PERS>(plan, p, s);
-    case 8: return launch_v<DT, OP, 8, EXACT, AFF, PERS>(plan, p, s);
-    case 16: return launch_v<DT, OP, 16, EXACT, AFF, PERS>(plan, p, s);
+    case 1: return launch_v<DT, OP, 1, EXACT, AFF, PERS, RAG>(plan, p, s);
+    case 2: return launch_v<DT, OP, 2, EXACT, AFF, PERS, RAG>(plan, p, s);
+    case 4: return launch_v<DT, OP, 4, EXACT, AFF, PERS, RAG>(plan, p, s);
+    case 8: return launch_v<DT, OP, 8, EXACT, AFF, PERS, RAG>(plan, p, s);
+    case 16: return launch_v<DT, OP, 16, EXACT, AFF, PERS, RAG>(plan, p, s);
     default: return hipErrorNotSupported;
     }
 }
@@ -2317,10 +2480,15 @@ inline hipError_t launch_w(const Plan& plan, const Params& p, hipStream_t s) {
 template <int DT, int OP, int AFF, bool PERS>
 inline hipError_t launch_e(const Plan& plan, const Params& p, hipStream_t s) {
     if constexpr (PERS) {
-        // persistent launches are planned only for exact shapes
+        // persistent launches are planned for exact shapes and for ragged rows (byte-addressed
+        // rows; exact when the row's chunks, the last one partial, fill the row group)
+        if (plan.ragged)
+            return plan.exact ? launch_w<DT, OP, true, AFF, true, true>(plan, p, s)
+                              : launch_w<DT, OP, false, AFF, true, true>(plan, p, s);
         if (!plan.exact) return hipErrorNotSupported;
         return launch_w<DT, OP, true, AFF, true>(plan, p, s);
     } else {
+        if (plan.ragged) return hipErrorNotSupported;
         return plan.exact ? launch_w<DT, OP, true, AFF, false>(plan, p, s)
                           : launch_w<DT, OP, false, AFF, false>(plan, p, s);
     }

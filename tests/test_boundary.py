@@ -93,8 +93,10 @@ def test_status_strings_and_version():
     ("softmax", torch.float32, 8192, 4096, "workgroup", 4, 4, True),   # persistent without parameters
     ("softmax", torch.float16, 64, 333, "element", 1, 4, False),
     ("softmax", torch.float32, 64, 333, "element", 1, 8, False),
-    ("ln", torch.bfloat16, 16384, 4095, "element", 4, 8, True),        # many ragged rows: persistent
-    ("ln", torch.float32, 16384, 4095, "element", 8, 8, True),
+    ("ln", torch.bfloat16, 16384, 4095, "workgroup", 2, 4, True),      # many ragged rows: byte-addressed,
+    ("ln", torch.float32, 16384, 4095, "workgroup", 4, 4, True),       # persistent
+    ("ln", torch.bfloat16, 200, 4095, "element", 4, 8, False),         # few ragged rows: element / pair
+    ("ln", torch.bfloat16, 16384, 4088, "workgroup", 2, 4, True),      # whole chunks, 511 of 512: byte-addressed
 ])
 def test_plan_variant_choice(op, dtype, rows, N, variant, W, V, persistent):
     ptrs = {"gamma": 1 << 44, "beta": (1 << 44) + (1 << 30)}
@@ -122,10 +124,13 @@ def test_plan_variant_choice(op, dtype, rows, N, variant, W, V, persistent):
     assert info["block_threads"] == 64 * W * rpb
     assert info["grid_blocks"] == (rows + rpb - 1) // rpb
     s = torch.tensor([], dtype=dtype).element_size()
-    assert info["exact"] == (N * s // 16 == 64 * W * V)
+    C = (N * s + 15) // 16  # chunks per row, the last one partial when N * s is not a multiple of 16
+    assert info["exact"] == (C == 64 * W * V)
+    # rows that are not whole chunks, or that do not fill the row group, run byte-addressed
+    assert info["ragged"] == (persistent and (N * s % 16 != 0 or C != 64 * W * V))
     if persistent:
         # one parameter vector staged in LDS (softmax has none)
-        assert info["lds_bytes"] == (0 if op == "softmax" else N * s)
+        assert info["lds_bytes"] == (0 if op == "softmax" else C * 16)
 
 
 def test_plan_persistent_launches():
@@ -145,11 +150,19 @@ def test_plan_persistent_launches():
     st, info = rn.plan("softmax", 512, 4096, torch.bfloat16)
     assert info["persistent"] and info["rows_per_block"] == 2 and info["waves_per_row"] == 2
     assert not rn.plan("softmax", 255, 4096, torch.bfloat16)[1]["persistent"]  # 255 workgroups of 1 row
-    assert not rn.plan("ln", 2047, 4095, torch.float32)[1]["persistent"]  # element kernel, 2047 workgroups
-    assert rn.plan("ln", 2048, 4095, torch.float32)[1]["persistent"]
-    # ragged rows of the vectorized kernels are never persistent
+    # ragged rows: the byte-addressed vectorized kernel from 256 row blocks (fp32 4095: 4-wave
+    # rows, one per workgroup), the element kernel (forced) from 2048 workgroups
+    assert not rn.plan("ln", 255, 4095, torch.float32)[1]["persistent"]
+    st, info = rn.plan("ln", 256, 4095, torch.float32)
+    assert info["persistent"] and info["ragged"] and info["variant"] == "workgroup"
+    assert not rn.plan("ln", 2047, 4095, torch.float32, variant="element")[1]["persistent"]
+    assert rn.plan("ln", 2048, 4095, torch.float32, variant="element")[1]["persistent"]
+    # whole-chunk rows that do not fill the row group (250 of 256 chunks): byte-addressed from
+    # 256 row blocks, grid per row below
     st, info = rn.plan("rms", 1 << 15, 1000, torch.float32, ptrs={"gamma": 1 << 44})
-    assert st == OK and not info["exact"] and not info["persistent"]
+    assert st == OK and not info["exact"] and info["persistent"] and info["ragged"]
+    st, info = rn.plan("rms", 1020, 1000, torch.float32, ptrs={"gamma": 1 << 44})
+    assert st == OK and not info["exact"] and not info["persistent"] and not info["ragged"]
 
 
 def test_plan_grid_is_capped():

@@ -38,13 +38,14 @@ def _rows_to_check(rows, N, s=2):
     return sorted({0, 1, rows // 2, first_beyond - 1, first_beyond, rows - 2, rows - 1})
 
 
-def _forward_case(rows, N, seed, expect):
+def _forward_case(rows, N, seed, expect, variant="auto"):
     x, gamma, beta = _inputs(rows, N, seed)
     assert x.numel() * 2 > (1 << 32)
     st, info = rn.plan("ln", rows, N, BF16, ptrs={"x": x.data_ptr(), "gamma": gamma.data_ptr(),
-                                                  "beta": beta.data_ptr()})
-    assert st == 0 and info["variant"] == expect[0] and info["persistent"] and info["pairs"] == expect[1], info
-    y, mean, rstd = rn.ln_forward(x, gamma, beta, EPS, return_stats=True)
+                                                  "beta": beta.data_ptr()}, variant=variant)
+    assert st == 0 and info["persistent"], info
+    assert (info["variant"], info["pairs"], info["ragged"]) == expect, info
+    y, mean, rstd = rn.ln_forward(x, gamma, beta, EPS, return_stats=True, variant=variant)
     torch.cuda.synchronize()
     idx = torch.tensor(_rows_to_check(rows, N), device=DEV)
     ref = oracle.layer_norm(x[idx].cpu(), gamma.cpu(), beta.cpu(), EPS)
@@ -54,11 +55,16 @@ def _forward_case(rows, N, seed, expect):
 
 
 def test_layer_norm_beyond_4gib_vectorized():
-    _forward_case(131075, 16384, 7001, ("workgroup", False))  # 4.3 GB per tensor
+    _forward_case(131075, 16384, 7001, ("workgroup", False, False))  # 4.3 GB per tensor
+
+
+def test_layer_norm_beyond_4gib_ragged():
+    # ragged rows, 4.3 GB per tensor: the byte-addressed vectorized kernel
+    _forward_case(524420, 4095, 7002, ("workgroup", False, True))
 
 
 def test_layer_norm_beyond_4gib_pairs():
-    _forward_case(524420, 4095, 7002, ("element", True))  # ragged rows, 4.3 GB per tensor
+    _forward_case(524420, 4095, 7003, ("element", True, False), variant="element")  # the pair kernel
 
 
 def test_split_rows_beyond_4gib():

@@ -114,7 +114,7 @@ def test_new_ops_full_size(w):
     check_case(w)
 
 
-@pytest.mark.parametrize("w,variant", [(workloads.LN_RAGGED, "element"), (workloads.LN_SPLIT, "wide"),
+@pytest.mark.parametrize("w,variant", [(workloads.LN_RAGGED, "workgroup"), (workloads.LN_SPLIT, "wide"),
                                        (workloads.SOFTMAX_VOCAB, "element")], ids=lambda v: getattr(v, "name", v))
 def test_general_shapes_full_size(w, variant):
     # the benchmark's general-shape workloads at full size, in the launch configuration it
@@ -322,10 +322,14 @@ def test_odd_widths(N):
                                   ("rms", "fp32", 16384, 101), ("fused_add_rms", "bf16", 2048, 16383),
                                   ("softmax", "fp32", 16384, 333)], ids=lambda c: f"{c[0]}-{c[1]}-{c[2]}x{c[3]}")
 def test_element_kernel_persistent(case):
+    # many ragged rows go to the byte-addressed vectorized kernel by default; forced, the
+    # element / pair kernels run persistent
     op, dtype, rows, N = case
     st, info = rn.plan(op, rows, N, TD[dtype])
+    assert st == 0 and info["variant"] in ("wave", "workgroup") and info["ragged"], info
+    st, info = rn.plan(op, rows, N, TD[dtype], variant="element")
     assert st == 0 and info["variant"] == "element" and info["persistent"], info
-    check_case(BASES[op].scaled(rows=rows, N=N, seed=720 + N, dtype=dtype))
+    check_case(BASES[op].scaled(rows=rows, N=N, seed=720 + N, dtype=dtype), "element")
 
 
 ROW_TENSORS = ("x", "residual", "y", "residual_out")
