@@ -169,6 +169,8 @@ def kernel_name(w, plan):
         return (f"rn::rownorm_wide_elem_stats_kernel + rn::rownorm_wide_elem_norm_kernel ({w.dtype}, {w.op}, one "
                 f"512-lane workgroup per row segment, {plan['grid_blocks']} segments)")
     mode = "persistent" if plan["persistent"] else "grid per row"
+    if plan.get("ragged"):
+        mode += ", byte-addressed rows"
     if plan["variant"] == "element":
         k = "rownorm_pair_kernel" if plan.get("pairs") else "rownorm_elem_kernel"
     else:
@@ -665,6 +667,19 @@ def plan_sweep_shapes():
                                                                    "against grid per row"),
         (workloads.C3.scaled(rows=8192, N=4092, dtype="fp32", name="rms_fp32_8192x4092"), "fp32 rows of 1023 of "
                                                                                           "1024 chunks"),
+        (workloads.C3.scaled(rows=16384, N=4088, dtype="bf16", name="rms_bf16_16384x4088"), "16-bit RMSNorm rows of "
+                                                                                            "511 of 512 chunks"),
+        (sm.scaled(rows=16384, N=4088, dtype="bf16", name="softmax_bf16_16384x4088"), "16-bit softmax rows of 511 of "
+                                                                                      "512 chunks"),
+        (workloads.C4_FP16.scaled(rows=8192, N=4088, name="fused_fp16_8192x4088"), "fused add + RMSNorm rows of 511 "
+                                                                                   "of 512 chunks"),
+        (workloads.C1.scaled(rows=8192, N=4092, name="ln_fp32_8192x4092"), "fp32 LayerNorm rows of 1023 of 1024 "
+                                                                           "chunks"),
+        (c5.scaled(rows=4096, N=16376, name="ln_bf16_4096x16376"), "8-wave LayerNorm rows of 2047 of 2048 chunks"),
+        (workloads.C4_FP16.scaled(rows=16384, N=4095, name="fused_fp16_16384x4095"), "ragged 2-wave fused add + "
+                                                                                     "RMSNorm fp16 rows"),
+        (workloads.C3.scaled(rows=4096, N=16383, dtype="fp32", name="rms_fp32_4096x16383"), "ragged 16-wave fp32 "
+                                                                                            "RMSNorm rows"),
         (workloads.C1.scaled(rows=1024, N=65537, name="ln_fp32_1024x65537"), "long ragged rows: element-granular "
                                                                              "split rows against the general "
                                                                              "kernel"),
@@ -1014,7 +1029,8 @@ def _more():
         ("rms_norm_backward", workloads.RMS_BWD.scaled(rows=8192, name="rms_bwd_fp16_8192x4096"),
          "RMSNorm backward, fp16 I/O, 8192 x 4096: dx, dweight from fp32 rstd"),
         ("layer_norm_ragged", workloads.LN_RAGGED,
-         "LayerNorm, bf16 I/O, 16384 x 4095 (rows not whole 16-byte chunks: element-pair kernel), y + mean + rstd"),
+         "LayerNorm, bf16 I/O, 16384 x 4095 (rows not whole 16-byte chunks: the vectorized kernel with "
+         "byte-addressed rows, 16-byte accesses at 2-byte alignment), y + mean + rstd"),
         ("layer_norm_split_rows", workloads.LN_SPLIT,
          "LayerNorm, fp32 I/O, 1024 x 65536 (rows beyond a workgroup's registers: one-pass split rows, the "
          "segments of a row exchanging their statistics through the workspace, x read once)"),

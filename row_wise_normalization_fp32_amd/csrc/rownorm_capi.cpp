@@ -250,6 +250,28 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
         const int64_t vr = next_pow2((Cr + 64 * wr - 1) / (64 * wr));
         const bool fills = Cr == int64_t(64) * wr * vr;  // the row group holds the row exactly
         ragged = (!vec_ok || !fills) && (rows + rpb - 1) / rpb >= rn::kPersistentVecBlocks;
+        // 16-bit rows that start at odd 2-byte positions (an odd N or row stride, or a tensor at
+        // an odd element offset): their 16-byte accesses cost the most there, and light kernels
+        // with several row tensors go faster through the element / pair kernels' aligned 4-byte
+        // words. Measured on MI355X (cold cache, graph replays, byte-addressed against the
+        // element / pair kernel): fused add + RMSNorm fp16 8192 x 8191 (4 waves) 112.4 against
+        // 100.9 us, fused add + LayerNorm bf16 8192 x 8191 118.9 against 112.0, RMSNorm fp16
+        // 4096 x 16383 (8 waves) 60.1 against 57.0, RMSNorm bf16 8192 x 8191 (4 waves) 53.1
+        // against 52.6; at 2 waves the byte-addressed kernel is faster (fused add + RMSNorm fp16
+        // 16384 x 4095 99.2 against 103.3 us, RMSNorm fp16 16384 x 4095 47.8 against 54.0), and
+        // so it is for LayerNorm and softmax at every width (LayerNorm bf16 4096 x 16383 64.1
+        // against 81.2, softmax bf16 8192 x 8191 53.3 against 78.5).
+        bool odd2 = false;
+        if (s == 2) {
+            const void* rowp[] = {a.x, a.residual, a.y, a.residual_out};
+            const int64_t lds[] = {a.ldx, a.ldr, a.ldy, a.ldro};
+            for (int i = 0; i < 4; ++i) {
+                if (!rowp[i]) continue;
+                if ((reinterpret_cast<uintptr_t>(rowp[i]) >> 1) & 1) odd2 = true;
+                if (rows > 1 && (lds[i] & 1)) odd2 = true;
+            }
+        }
+        if (odd2 && ((fused && wr >= 4) || (a.op == RN_OP_RMS_NORM && wr >= 8))) ragged = false;
     }
     if (tune && ragged) return RN_ERR_UNSUPPORTED;  // a tuning applies to whole-chunk rows only
     const int64_t C = vec_ok ? (N * s) / 16 : (ragged ? Cr : 0);

@@ -483,3 +483,21 @@ def test_python_wrapper_names():
     for n in ("ln_forward", "layer_norm", "rms_norm", "fused_add_rms_norm", "fused_add_layer_norm",
               "softmax_forward", "ln_backward", "rms_norm_backward"):
         assert callable(getattr(rn, n)) and n in rn.__all__
+
+
+def test_plan_ragged_rows_rule():
+    # many rows that are not whole 16-byte chunks, or that do not fill the row group: the
+    # byte-addressed vectorized kernel, except 16-bit rows at odd 2-byte positions of the fused
+    # ops from 4 waves per row and of RMSNorm from 8 (the element / pair kernels)
+    f16, bf16, f32 = torch.float16, torch.bfloat16, torch.float32
+    rag = lambda *a, **k: rn.plan(*a, **k)[1]["ragged"]  # noqa: E731
+    assert rag("fused_add_rms", 16384, 4095, f16)                  # 2 waves
+    assert not rag("fused_add_rms", 8192, 8191, f16)               # 4 waves, odd N
+    assert not rag("fused_add_ln", 8192, 8191, bf16)
+    assert rag("fused_add_rms", 8192, 8190, f16)                   # even N: rows at 4-byte positions
+    assert not rag("fused_add_rms", 8192, 8192, f16, ptrs={"x": (1 << 44) + 2})  # x at an odd element
+    assert rag("rms", 8192, 8191, bf16) and not rag("rms", 4096, 16383, f16)     # 4 and 8 waves
+    assert rag("ln", 4096, 16383, bf16) and rag("softmax", 8192, 8191, bf16)
+    assert rag("rms", 4096, 16383, f32) and rag("fused_add_rms", 8192, 8191, f32)  # fp32: always
+    st, info = rn.plan("fused_add_rms", 8192, 8191, f16)
+    assert info["variant"] == "element" and info["pairs"] and info["persistent"]
