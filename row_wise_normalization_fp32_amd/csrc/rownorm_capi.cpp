@@ -93,11 +93,10 @@ size_t wide_workspace_bytes(int64_t rows, int64_t N) {
 // records computed by waiting workgroups), then four 64-bit words per (row, chunk segment).
 size_t wide_onepass_bytes(int64_t rows, int64_t C) { return 256 + static_cast<size_t>(rows * wide_segments(C) * 32); }
 
-// The one-pass layout's bytes for rows of N elements of s bytes (0 when N * s is not whole
-// chunks: such rows never take it).
+// The one-pass layout's bytes for rows of N elements of s bytes.
 template <class A>
 size_t vec_layout_bytes(const A&, int64_t rows, int64_t N, int64_t s) {
-    return (N * s) % 16 == 0 ? wide_onepass_bytes(rows, N * s / 16) : 0;
+    return wide_onepass_bytes(rows, (N * s + 15) / 16);  // byte-addressed rows: the last chunk partial
 }
 
 // What rn_forward_workspace_bytes reports: room for either form.
@@ -274,7 +273,21 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
         if (odd2 && ((fused && wr >= 4) || (a.op == RN_OP_RMS_NORM && wr >= 8))) ragged = false;
     }
     if (tune && ragged) return RN_ERR_UNSUPPORTED;  // a tuning applies to whole-chunk rows only
-    const int64_t C = vec_ok ? (N * s) / 16 : (ragged ? Cr : 0);
+    // Long ragged rows (beyond what the element kernels hold) with a workspace of the one-pass
+    // layout, out of place, in at most kWideOnePassMaxSeg segments: the one-pass split rows with
+    // byte-addressed segments (x read once) instead of the element-granular two launches (x read
+    // twice).
+    const int64_t elem_cap_rows = int64_t(64) * rn::kMaxGroupWaves *
+                                  (sm ? rn::kSoftmaxElemMaxPerLane : rn::kElemMaxPerLane);
+    bool wide_rag = false;
+    if (!vec_ok && !ragged && ws_given && a.variant == RN_VARIANT_AUTO && N > elem_cap_rows) {
+        const bool in_place = a.y == a.x || (a.residual_out != nullptr &&
+                                             (a.residual_out == a.residual || a.residual_out == a.x)) ||
+                              (a.residual != nullptr && a.y == a.residual);
+        wide_rag = !in_place && wide_segments(Cr) <= rn::kWideOnePassMaxSeg &&
+                   a.ws_bytes >= wide_onepass_bytes(rows, Cr);
+    }
+    const int64_t C = vec_ok ? (N * s) / 16 : (ragged || wide_rag ? Cr : 0);
     const int64_t elem_cap = int64_t(64) * rn::kMaxGroupWaves * rn::kElemMaxPerLane;   // 16384 elements
     // Softmax keeps no parameters in registers: its element / pair kernels hold rows of up to
     // 65536 elements in one 16-wave workgroup (x read once) instead of splitting them.
@@ -307,7 +320,7 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     if (v == RN_VARIANT_AUTO) {
         if ((vec_ok && C <= big_cap) || ragged)
             v = w_auto == 1 ? RN_VARIANT_WAVE : RN_VARIANT_WORKGROUP;
-        else if (vec_ok && ws_given)
+        else if ((vec_ok && ws_given) || wide_rag)
             v = RN_VARIANT_WIDE;
         else if (N <= elem_cap_op)
             v = RN_VARIANT_ELEMENT;
@@ -334,7 +347,7 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
         return RN_OK;
     }
     if (v == RN_VARIANT_WIDE) {
-        if (!vec_ok || C <= group_cap) return RN_ERR_UNSUPPORTED;
+        if (!wide_rag && (!vec_ok || C <= group_cap)) return RN_ERR_UNSUPPORTED;
         if (!ws_given) return RN_ERR_WORKSPACE;
         const int64_t S = wide_segments(C);
         plan->variant = rn::V_WIDE;
@@ -343,7 +356,8 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
         plan->chunks_per_lane = 4;
         plan->block_threads = 512;
         plan->grid = rows * S < rn::kMaxGrid ? rows * S : rn::kMaxGrid;
-        plan->exact = C % rn::kWideSegChunks == 0;
+        plan->exact = !wide_rag && C % rn::kWideSegChunks == 0;
+        plan->ragged = wide_rag;
         *chunks = C;
         return RN_OK;
     }

@@ -1434,21 +1434,32 @@ static_assert(kWideChunks == kWideSegChunks, "segment size shared with the plann
 // wave takes part (one barrier). The two-launch statistics kernel, the one-pass kernel and a
 // workgroup that computes another segment's record in its place all go through this, so the
 // records have the same bits.
+// The partial last chunk of a byte-addressed split row's last segment: its slot, its lane and
+// its element count (ti = -1: the segment ends with a whole chunk).
+struct WideTail {
+    int ti = -1;
+    int tt = 0;
+    int te = 0;
+};
+
 template <int DT, int OP, bool EXACT, class Get>
 __device__ __forceinline__ float4 wide_record(Get get, int Cs, int t, int lane, int wr, WavePart (*part)[kWideW],
-                                              int& buf) {
+                                              int& buf, const WideTail& tl = WideTail{}) {
     using IO = Io<DT>;
     using OT = OpTraits<OP>;
     constexpr int E = IO::E;
     constexpr int V = kWideV;
     auto valid = [&](int i) { return EXACT || i * kWideLanes + t < Cs; };
+    // element e of slot i is part of the row (the partial chunk's missing elements read 0)
+    auto ok = [&](int i, int e) { return valid(i) && !(i == tl.ti && t == tl.tt && e >= tl.te); };
     int cnt = 0;  // chunks of this wave
 #pragma unroll
     for (int i = 0; i < V; ++i) {
         const int k = Cs - (i * kWideLanes + wr * 64);
         cnt += k <= 0 ? 0 : (k >= 64 ? 64 : k);
     }
-    const float n_w = static_cast<float>(cnt * E);
+    const int missing = tl.ti >= 0 ? E - tl.te : 0;  // elements the partial chunk lacks
+    const float n_w = static_cast<float>(cnt * E - ((tl.tt >> 6) == wr ? missing : 0));
     if constexpr (OT::LN) {
         const float K = uniform(IO::first(get(0)));
         float s1 = 0.f;
@@ -1457,7 +1468,7 @@ __device__ __forceinline__ float4 wide_record(Get get, int Cs, int t, int lane, 
             float f[E];
             IO::unpack(get(i), f);
 #pragma unroll
-            for (int e = 0; e < E; ++e) s1 += valid(i) ? f[e] - K : 0.f;
+            for (int e = 0; e < E; ++e) s1 += ok(i, e) ? f[e] - K : 0.f;
         }
         const float inv_w = n_w > 0.f ? 1.0f / n_w : 0.f;
         const float a = K + wave_sum(s1) * inv_w;
@@ -1468,7 +1479,7 @@ __device__ __forceinline__ float4 wide_record(Get get, int Cs, int t, int lane, 
             IO::unpack(get(i), f);
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                const float d = valid(i) ? f[e] - a : 0.f;
+                const float d = ok(i, e) ? f[e] - a : 0.f;
                 c += d;
                 q = fmaf(d, d, q);
             }
@@ -1479,7 +1490,7 @@ __device__ __forceinline__ float4 wide_record(Get get, int Cs, int t, int lane, 
         group_moments<kWideW, false>(part, buf, lane, wr, n_w, a, cw, fmaxf(Qw - Cw * cw, 0.f), rel, m2, mean);
         // relative to wave 0's rough mean R: rel is the mean minus this wave's a, so
         // mean - R = rel + (a - R); wave 0 (a == R) writes the record
-        return make_float4(static_cast<float>(Cs * E), a, rel, m2);
+        return make_float4(static_cast<float>(Cs * E - missing), a, rel, m2);
     } else if constexpr (OT::SM) {
         float mx = -INFINITY;
 #pragma unroll
@@ -1487,7 +1498,7 @@ __device__ __forceinline__ float4 wide_record(Get get, int Cs, int t, int lane, 
             float f[E];
             IO::unpack(get(i), f);
 #pragma unroll
-            for (int e = 0; e < E; ++e) mx = valid(i) ? max_nan(mx, f[e]) : mx;
+            for (int e = 0; e < E; ++e) mx = ok(i, e) ? max_nan(mx, f[e]) : mx;
         }
         const float mw = wave_max(mx);
         float sm = 0.f;
@@ -1496,7 +1507,7 @@ __device__ __forceinline__ float4 wide_record(Get get, int Cs, int t, int lane, 
             float f[E];
             IO::unpack(get(i), f);
 #pragma unroll
-            for (int e = 0; e < E; ++e) sm += valid(i) ? exp_neg(f[e] - mw) : 0.f;
+            for (int e = 0; e < E; ++e) sm += ok(i, e) ? exp_neg(f[e] - mw) : 0.f;
         }
         float M, Ssum;
         group_softmax<kWideW>(part, buf, lane, wr, mw, wave_sum(sm), M, Ssum);
@@ -1705,12 +1716,19 @@ __global__ __launch_bounds__(256) void rownorm_wide_clear_kernel(u32x4* p, int64
         p[i] = z;
 }
 
-template <int DT, int OP, bool EXACT, int AFF>
+// RAG: rows addressed by byte (rows, tensors or strides that are not whole 16-byte chunks):
+// each segment of a row moves through a buffer resource that ends with the segment (the last
+// one with the row), in 16-byte accesses at element alignment; the row's partial last chunk
+// moves by its whole dwords (the hardware checks the range per dword) and, for an odd-length
+// 16-bit row, its last element by one 2-byte access (the low half of `h` on the lane that holds
+// that chunk), merged into the chunk where the segment is first used.
+template <int DT, int OP, bool EXACT, int AFF, bool RAG = false>
 __global__ __launch_bounds__(kWideLanes) void rownorm_wide_onepass_kernel(Params p, WideArgs wa) {
     using IO = Io<DT>;
     using OT = OpTraits<OP>;
     constexpr int E = IO::E;
     constexpr int V = kWideV;
+    constexpr int SB = 16 / E;  // bytes per element
     constexpr bool HG = !OT::SM && (AFF & AFF_G) != 0;
     constexpr bool HB = OT::LN && (AFF & AFF_B) != 0;
     constexpr int NR = OT::RES ? V : 1;
@@ -1744,14 +1762,81 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_onepass_kernel(Params
             const int c = i * kWideLanes + t;
             return c0 + (EXACT ? c : (c < Cs ? c : Cs - 1));
         };
+        // RAG geometry of segment s: its first byte in the row, its bytes, its partial chunk
+        const int64_t row_bytes = p.N * SB;
+        auto seg_bytes = [&](int s_) {
+            const int64_t b0 = static_cast<int64_t>(s_) * kWideChunks * 16;
+            const int64_t rem = row_bytes - b0;
+            return static_cast<uint32_t>(rem < kWideChunks * 16 ? rem : kWideChunks * 16);
+        };
+        auto seg_tail = [&](int s_) {
+            WideTail tl;
+            const int te = static_cast<int>(p.N % E);
+            if (RAG && te != 0 && s_ == S - 1) {
+                const int idx = static_cast<int>(p.C - 1 - static_cast<int64_t>(s_) * kWideChunks);
+                tl.ti = idx / kWideLanes;
+                tl.tt = idx % kWideLanes;
+                tl.te = te;
+            }
+            return tl;
+        };
+        const uint32_t sb = seg_bytes(seg);
+        const WideTail tail = seg_tail(seg);
+        const bool odd16 = RAG && SB == 2 && (p.N & 1) != 0;  // a last element to move by 2 bytes
+        const bool hseg = odd16 && tail.ti >= 0;               // ... in this segment
+        const int hd = (tail.te - 1) >> 1;                      // the dword holding it (low half)
+        // (the half's wave and lane; the waves without it issue nothing for it)
+        auto half_wave = [&]() { return hseg && wr == (tail.tt >> 6); };
+        auto with_half = [&](u32x4 v, unsigned h) {
+            v.x |= hd == 0 ? h : 0u;
+            v.y |= hd == 1 ? h : 0u;
+            v.z |= hd == 2 ? h : 0u;
+            v.w |= hd == 3 ? h : 0u;
+            return v;
+        };
+        auto rsrc_seg = [&](const void* base, int64_t ld, int64_t row) {
+            return make_rsrc(static_cast<const char*>(base) + (row * ld + c0 * E) * SB, sb);
+        };
         // the segment's parameters, for all the block's rows (read after the first row's
         // wait, which is past at least one barrier)
         for (int c = t; c < kWideChunks; c += kWideLanes) {
             const int64_t cc = c0 + (c < Cs ? c : Cs - 1);
-            if constexpr (HG) prm[c] = static_cast<const u32x4*>(p.gamma)[cc];
-            if constexpr (HB) prm[(HG ? kWideChunks : 0) + c] = static_cast<const u32x4*>(p.beta)[cc];
+            if constexpr (RAG) {
+                const int cl = c < Cs ? c : Cs - 1;
+                auto pchunk = [&](const void* base) {
+                    const Rsrc r = rsrc_seg(base, 0, 0);
+                    u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, cl * 16, 0, 0);
+                    if (hseg && cl == tail.ti * kWideLanes + tail.tt)
+                        v = with_half(v, __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(sb - 2u), 0, 0));
+                    return v;
+                };
+                if constexpr (HG) prm[c] = pchunk(p.gamma);
+                if constexpr (HB) prm[(HG ? kWideChunks : 0) + c] = pchunk(p.beta);
+            } else {
+                if constexpr (HG) prm[c] = static_cast<const u32x4*>(p.gamma)[cc];
+                if constexpr (HB) prm[(HG ? kWideChunks : 0) + c] = static_cast<const u32x4*>(p.beta)[cc];
+            }
         }
-        auto load = [&](int64_t row, u32x4(&xv)[V], u32x4(&rv)[NR]) {
+        // xh / rh: RAG, the last element of an odd-length 16-bit row (see above)
+        auto load = [&](int64_t row, u32x4(&xv)[V], u32x4(&rv)[NR], unsigned& xh, unsigned& rh) {
+            if constexpr (RAG) {
+                const Rsrc rx = rsrc_seg(p.x, p.ldx, row);
+#pragma unroll
+                for (int i = 0; i < V; ++i)
+                    xv[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, static_cast<int>((chunk(i) - c0) * 16), 0, 2);
+                if (half_wave())
+                    xh = __builtin_amdgcn_raw_buffer_load_b16(rx, static_cast<int>(t == tail.tt ? sb - 2u : sb), 0, 2);
+                if constexpr (OT::RES) {
+                    const Rsrc rr = rsrc_seg(p.residual, p.ldr, row);
+#pragma unroll
+                    for (int i = 0; i < V; ++i)
+                        rv[i] = __builtin_amdgcn_raw_buffer_load_b128(rr, static_cast<int>((chunk(i) - c0) * 16), 0, 2);
+                    if (half_wave())
+                        rh = __builtin_amdgcn_raw_buffer_load_b16(rr, static_cast<int>(t == tail.tt ? sb - 2u : sb), 0,
+                                                                  2);
+                }
+                return;
+            }
             const u32x4* xr = static_cast<const u32x4*>(p.x) + row * p.cx;
 #pragma unroll
             for (int i = 0; i < V; ++i) xv[i] = __builtin_nontemporal_load(xr + chunk(i));
@@ -1759,6 +1844,19 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_onepass_kernel(Params
                 const u32x4* rr = static_cast<const u32x4*>(p.residual) + row * p.cr;
 #pragma unroll
                 for (int i = 0; i < V; ++i) rv[i] = __builtin_nontemporal_load(rr + chunk(i));
+            }
+        };
+        // one output chunk of the segment (RAG: the partial chunk's whole dwords, then the half)
+        auto store_seg = [&](void* base, int64_t ld, int64_t row, int i, const u32x4& v) {
+            if constexpr (RAG) {
+                const Rsrc r = rsrc_seg(base, ld, row);
+                if (valid(i)) __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>((chunk(i) - c0) * 16), 0, 2);
+                if (i == tail.ti && half_wave()) {
+                    const unsigned hv = hd == 0 ? v.x : hd == 1 ? v.y : hd == 2 ? v.z : v.w;
+                    bstore16<2>(r, t == tail.tt ? sb - 2u : sb, hv);
+                }
+            } else {
+                if (valid(i)) __builtin_nontemporal_store(v, static_cast<u32x4*>(base) + row * (ld * SB / 16) + chunk(i));
             }
         };
         auto publish = [&](int64_t row, int sgm, const float4& rec) {
@@ -1773,9 +1871,20 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_onepass_kernel(Params
         };
         // this workgroup's segment of one row: the fused ops form the rounded sum (kept in xv)
         // and store residual_out; then the record, published as record `seg` of the row
-        auto post = [&](int64_t row, u32x4(&xv)[V], const u32x4(&rv)[NR]) {
+        // (RAG: the row's last element of an odd-length 16-bit row joins its chunk here)
+        auto post = [&](int64_t row, u32x4(&xv)[V], u32x4(&rv)[NR], unsigned xh, unsigned rh) {
+            if constexpr (RAG) {
+                if (hseg && t == tail.tt) {
+#pragma unroll
+                    for (int i = 0; i < V; ++i) {
+                        if (i == tail.ti) {
+                            xv[i] = with_half(xv[i], xh);
+                            if constexpr (OT::RES) rv[i] = with_half(rv[i], rh);
+                        }
+                    }
+                }
+            }
             if constexpr (OT::RES) {
-                u32x4* ro = static_cast<u32x4*>(p.residual_out) + row * p.cro;
 #pragma unroll
                 for (int i = 0; i < V; ++i) {
                     float a[E], c[E];
@@ -1784,10 +1893,11 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_onepass_kernel(Params
 #pragma unroll
                     for (int e = 0; e < E; ++e) a[e] += c[e];
                     xv[i] = IO::pack(a);
-                    if (valid(i)) __builtin_nontemporal_store(xv[i], ro + chunk(i));
+                    store_seg(p.residual_out, p.ldro, row, i, xv[i]);
                 }
             }
-            const float4 rec = wide_record<DT, OP, EXACT>([&](int i) { return xv[i]; }, Cs, t, lane, wr, part, buf);
+            const float4 rec =
+                wide_record<DT, OP, EXACT>([&](int i) { return xv[i]; }, Cs, t, lane, wr, part, buf, tail);
             publish(row, seg, rec);
         };
         // segment s2's record of one row, computed here from memory, one chunk per tensor at a
@@ -1795,14 +1905,40 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_onepass_kernel(Params
         auto other_record = [&](int64_t row, int s2) {
             const int64_t c2 = static_cast<int64_t>(s2) * kWideChunks;
             const int Cs2 = static_cast<int>(p.C - c2 < kWideChunks ? p.C - c2 : kWideChunks);
+            const WideTail tl2 = seg_tail(s2);
+            const uint32_t sb2 = seg_bytes(s2);
+            // RAG: the segment's resource, and the byte offset of its 2-byte last element
+            // (sb2 - 2 on the lane holding that chunk, past the segment elsewhere)
+            const Rsrc rx2 = make_rsrc(static_cast<const char*>(p.x) + (row * p.ldx + c2 * E) * SB, sb2);
+            const Rsrc rr2 = make_rsrc(OT::RES ? static_cast<const char*>(p.residual) + (row * p.ldr + c2 * E) * SB
+                                               : nullptr,
+                                       OT::RES ? sb2 : 0u);
+            const bool h2 = odd16 && tl2.ti >= 0;
+            const int hd2 = (tl2.te - 1) >> 1;
             const u32x4* xr = static_cast<const u32x4*>(p.x) + row * p.cx + c2;
             const u32x4* rr = OT::RES ? static_cast<const u32x4*>(p.residual) + row * p.cr + c2 : nullptr;
+            auto ld2 = [&](const u32x4* gp, Rsrc r, int cc, int i) {
+                if constexpr (RAG) {
+                    u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, cc * 16, 0, 0);
+                    if (h2 && i == tl2.ti) {
+                        const unsigned h = __builtin_amdgcn_raw_buffer_load_b16(
+                            r, static_cast<int>(t == tl2.tt ? sb2 - 2u : sb2), 0, 0);
+                        v.x |= hd2 == 0 ? h : 0u;
+                        v.y |= hd2 == 1 ? h : 0u;
+                        v.z |= hd2 == 2 ? h : 0u;
+                        v.w |= hd2 == 3 ? h : 0u;
+                    }
+                    return v;
+                } else {
+                    return gp[cc];
+                }
+            };
             auto get = [&](int i) {
                 const int c = i * kWideLanes + t;
                 const int cc = EXACT ? c : (c < Cs2 ? c : Cs2 - 1);
-                u32x4 v = xr[cc];
+                u32x4 v = ld2(xr, rx2, cc, i);
                 if constexpr (OT::RES) {
-                    const u32x4 r = rr[cc];
+                    const u32x4 r = ld2(rr, rr2, cc, i);
                     float a[E], b[E];
                     IO::unpack(v, a);
                     IO::unpack(r, b);
@@ -1813,7 +1949,7 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_onepass_kernel(Params
                 asm volatile("" ::: "memory");  // one chunk per tensor in flight
                 return v;
             };
-            return wide_record<DT, OP, EXACT>(get, Cs2, t, lane, wr, part, buf);
+            return wide_record<DT, OP, EXACT>(get, Cs2, t, lane, wr, part, buf, tl2);
         };
         const int64_t r0 = blk < wa.P1 ? blk * wa.R
                                        : static_cast<int64_t>(wa.P1) * wa.R + (blk - wa.P1) * wa.R2;
@@ -1822,14 +1958,16 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_onepass_kernel(Params
         // three rows in flight: row (record posted, waiting), row + 1 (posted before the wait
         // for row), row + 2 (loads issued before that wait)
         u32x4 cx[V], cr[NR], nx[V], nr[NR];
-        load(r0, cx, cr);
-        if (r0 + 1 < r1) load(r0 + 1, nx, nr);
-        post(r0, cx, cr);
+        unsigned cxh = 0, crh = 0, nxh = 0, nrh = 0;  // RAG: the rows' 2-byte last elements
+        load(r0, cx, cr, cxh, crh);
+        if (r0 + 1 < r1) load(r0 + 1, nx, nr, nxh, nrh);
+        post(r0, cx, cr, cxh, crh);
         for (int64_t row = r0; row < r1; ++row) {
             const int par = static_cast<int>(row & 1);
             u32x4 mx[V], mr[NR];
-            if (row + 2 < r1) load(row + 2, mx, mr);
-            if (row + 1 < r1) post(row + 1, nx, nr);
+            unsigned mxh = 0, mrh = 0;
+            if (row + 2 < r1) load(row + 2, mx, mr, mxh, mrh);
+            if (row + 1 < r1) post(row + 1, nx, nr, nxh, nrh);
             if (wr == POLLER) {
                 const unsigned long long* w = wa.rec64 + 4 * row * S;
                 unsigned miss = 0;
@@ -1881,7 +2019,6 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_onepass_kernel(Params
             const float4 tot = combine_records<OP>(s_rec[par], S, lane);
             const WideScale ws = wide_scale<OP>(tot, p);
             if (seg == 0 && t == 0) wide_store_stats<OP>(p, row, tot, ws);
-            u32x4* yr = static_cast<u32x4*>(p.y) + row * p.cy;
 #pragma unroll
             for (int i = 0; i < V; ++i) {
                 const int c = i * kWideLanes + t;
@@ -1889,7 +2026,7 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_onepass_kernel(Params
                 const u32x4 gv = HG ? prm[cl] : u32x4{0u, 0u, 0u, 0u};
                 const u32x4 bv = HB ? prm[(HG ? kWideChunks : 0) + cl] : u32x4{0u, 0u, 0u, 0u};
                 const u32x4 o = wide_out<DT, OP, HG, HB>(cx[i], gv, bv, ws);
-                if (valid(i)) __builtin_nontemporal_store(o, yr + chunk(i));
+                store_seg(p.y, p.ldy, row, i, o);
             }
 #pragma unroll
             for (int i = 0; i < V; ++i) {
@@ -1900,6 +2037,8 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_onepass_kernel(Params
                     nr[i] = mr[i];
                 }
             }
+            nxh = mxh;
+            nrh = mrh;
         }
     }
 }
@@ -2664,9 +2803,9 @@ inline hipError_t launch_wide_elem_op(const Plan& plan, const Params& p, const W
 // blocks (at most 256 segments and room for two workgroups per segment on the device;
 // otherwise, or for lack of the layout, the two launches). Returns hipErrorNotSupported when
 // the one pass does not apply.
-template <int DT, int OP, bool EXACT, int AFF>
+template <int DT, int OP, bool EXACT, int AFF, bool RAG = false>
 inline hipError_t go_wide_onepass(const Plan& plan, const Params& p, const WideArgs& wa0, hipStream_t s) {
-    constexpr auto K = rownorm_wide_onepass_kernel<DT, OP, EXACT, AFF>;
+    constexpr auto K = rownorm_wide_onepass_kernel<DT, OP, EXACT, AFF, RAG>;
     if (wa0.sync == nullptr || wa0.rec64 == nullptr || wa0.S > kWideOnePassMaxSeg) return hipErrorNotSupported;
     int cus = 0, per_cu = 0;
     hipError_t e = resident<K>(kWideLanes, 0, &cus, &per_cu);
@@ -2721,17 +2860,17 @@ inline hipError_t go_wide_onepass(const Plan& plan, const Params& p, const WideA
                            s);
 }
 
-template <int DT, int OP, bool EXACT>
+template <int DT, int OP, bool EXACT, bool RAG = false>
 inline hipError_t launch_wide_onepass(const Plan& plan, const Params& p, const WideArgs& wa, hipStream_t s) {
     if constexpr (OpTraits<OP>::SM) {
-        return go_wide_onepass<DT, OP, EXACT, 0>(plan, p, wa, s);
+        return go_wide_onepass<DT, OP, EXACT, 0, RAG>(plan, p, wa, s);
     } else {
         const int aff = (p.gamma ? AFF_G : 0) | (OpTraits<OP>::LN && p.beta ? AFF_B : 0);
-        if (aff == 0) return go_wide_onepass<DT, OP, EXACT, 0>(plan, p, wa, s);
-        if (aff == AFF_G) return go_wide_onepass<DT, OP, EXACT, AFF_G>(plan, p, wa, s);
+        if (aff == 0) return go_wide_onepass<DT, OP, EXACT, 0, RAG>(plan, p, wa, s);
+        if (aff == AFF_G) return go_wide_onepass<DT, OP, EXACT, AFF_G, RAG>(plan, p, wa, s);
         if constexpr (OpTraits<OP>::LN) {
-            if (aff == AFF_B) return go_wide_onepass<DT, OP, EXACT, AFF_B>(plan, p, wa, s);
-            return go_wide_onepass<DT, OP, EXACT, AFF_G | AFF_B>(plan, p, wa, s);
+            if (aff == AFF_B) return go_wide_onepass<DT, OP, EXACT, AFF_B, RAG>(plan, p, wa, s);
+            return go_wide_onepass<DT, OP, EXACT, AFF_G | AFF_B, RAG>(plan, p, wa, s);
         }
         return hipErrorInvalidValue;
     }
@@ -2740,6 +2879,23 @@ inline hipError_t launch_wide_onepass(const Plan& plan, const Params& p, const W
 template <int DT, int OP>
 inline hipError_t launch_wide_op(const Plan& plan, const Params& p, const WideArgs& wa, hipStream_t s) {
     if (plan.variant == V_WIDE_ELEM) return launch_wide_elem_op<DT, OP>(plan, p, wa, s);
+    if (plan.ragged) {
+        // byte-addressed rows: the one-pass kernel, or (when the device cannot hold it) the
+        // element-granular two launches over the same workspace, which the planner sized for both
+        const hipError_t e1 = launch_wide_onepass<DT, OP, false, true>(plan, p, wa, s);
+        if (e1 != hipErrorNotSupported) return e1;
+        Plan pe = plan;
+        pe.variant = V_WIDE_ELEM;
+        pe.ragged = false;
+        const int64_t S2 = (p.N + kWideElemSeg - 1) / kWideElemSeg;
+        pe.grid = p.rows * S2 < kMaxGrid ? p.rows * S2 : kMaxGrid;
+        pe.exact = p.N % kWideElemSeg == 0;
+        WideArgs we = wa;
+        we.S = static_cast<int>(S2);
+        we.sync = nullptr;
+        we.rec64 = nullptr;
+        return launch_wide_elem_op<DT, OP>(pe, p, we, s);
+    }
     {
         const hipError_t e1 = plan.exact ? launch_wide_onepass<DT, OP, true>(plan, p, wa, s)
                                          : launch_wide_onepass<DT, OP, false>(plan, p, wa, s);

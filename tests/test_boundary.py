@@ -228,8 +228,8 @@ def test_plan_long_softmax_rows_stay_in_one_workgroup():
     assert st == OK and info["variant"] == "element" and info["pairs"] and info["chunks_per_lane"] == 32
     # up to 65536 elements; the other ops split such rows
     assert rn.plan("softmax", 8, 65536, f32, ptrs={"x": (1 << 40) + 4}, workspace_bytes=ws)[1]["variant"] == "element"
-    assert rn.plan("softmax", 8, 65537, f32, workspace_bytes=ws)[1]["variant"] == "wide_element"
-    assert rn.plan("rms", 8, 50257, f32, workspace_bytes=ws)[1]["variant"] == "wide_element"
+    assert rn.plan("softmax", 8, 65537, f32, workspace_bytes=ws)[1]["variant"] == "wide"  # byte-addressed one pass
+    assert rn.plan("rms", 8, 50257, f32, workspace_bytes=ws)[1]["variant"] == "wide"
     assert rn.plan("softmax", 8, 65537, f32, variant="element")[0] == UNSUP
     assert rn.plan("ln", 8, 16385, f32, variant="element")[0] == UNSUP
 
@@ -452,15 +452,27 @@ def test_plan_split_rows():
         assert rn.plan(op, 8, 32776, bf16, workspace_bytes=ws)[1]["variant"] == "wide"
     # bf16 rows of whole chunks up to 32768 elements stay in one workgroup, workspace or not
     assert rn.plan("ln", 8, 32768, bf16, workspace_bytes=8 * 8 * 16)[1]["variant"] == "workgroup"
-    # other rows longer than 16384 elements: segments of 8192 elements
+    # other rows longer than 16384 elements: with room for the one-pass layout, byte-addressed
+    # segments of 2048 chunks (the last chunk partial); with only the two-launch form's records,
+    # or in place, segments of 8192 elements
     for N, dt, ptrs, strides in [(65537, f32, None, None), (50257, bf16, None, None),
                                  (65536, f32, {"x": (1 << 40) + 4}, None), (20000, bf16, None, {"x": 20001})]:
         ws = rn.forward_workspace_bytes("ln", 8, N, dt)
         st, info = rn.plan("ln", 8, N, dt, workspace_bytes=ws, ptrs=ptrs, strides=strides)
+        C = (N * (4 if dt == f32 else 2) + 15) // 16
+        assert st == OK and info["variant"] == "wide" and info["ragged"] and not info["exact"], (N, info)
+        assert info["grid_blocks"] == 8 * ((C + 2047) // 2048) and info["chunks_per_lane"] == 4
         S = (N + 8191) // 8192
-        assert st == OK and info["variant"] == "wide_element", (N, info)
-        assert info["grid_blocks"] == 8 * S and info["block_threads"] == 512 and info["chunks_per_lane"] == 16
-        assert info["exact"] == (N % 8192 == 0)
+        for kw in ({"workspace_bytes": 8 * S * 16}, {"workspace_bytes": ws, "in_place": True}):
+            pp, sd = dict(ptrs or {}), dict(strides or {})
+            if kw.pop("in_place", False):  # y over x: same address, same row stride
+                pp["y"] = pp["x"] = pp.get("x", 1 << 42)
+                if "x" in sd:
+                    sd["y"] = sd["x"]
+            st, info = rn.plan("ln", 8, N, dt, ptrs=pp, strides=sd or None, **kw)
+            assert st == OK and info["variant"] == "wide_element", (N, kw, info)
+            assert info["grid_blocks"] == 8 * S and info["block_threads"] == 512 and info["chunks_per_lane"] == 16
+            assert info["exact"] == (N % 8192 == 0) and not info["ragged"]
         # below the two-launch form's records (one per 8192 elements): no split rows
         assert rn.plan("ln", 8, N, dt, workspace_bytes=8 * S * 16 - 16, ptrs=ptrs,
                        strides=strides)[1]["variant"] == "general"

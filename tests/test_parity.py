@@ -209,13 +209,16 @@ ELEM_WIDE_SHAPES = {"fp32": [(3, 16385), (2, 50257), (3, 65537)], "bf16": [(3, 2
 @pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
 def test_split_rows_element(op, dtype):
     # rows of more than 16384 elements that are not whole 16-byte chunks (a vocabulary-sized
-    # softmax, 50257): statistics per 8192-element segment, then the same fixed-order combine
-    # (softmax rows of up to 65536 elements stay in one workgroup: the element / pair kernels)
+    # softmax, 50257): by default byte-addressed one-pass segments; forced, statistics per
+    # 8192-element segment, then the same fixed-order combine (softmax rows of up to 65536
+    # elements stay in one workgroup: the element / pair kernels)
     for rows, N in ELEM_WIDE_SHAPES[dtype]:
         st, info = rn.plan(op, rows, N, TD[dtype], workspace_bytes=rn.forward_workspace_bytes(op, rows, N, TD[dtype]))
-        expect = "element" if op == "softmax" and N <= 65536 else "wide_element"
+        expect = "element" if op == "softmax" and N <= 65536 else "wide"
         assert st == 0 and info["variant"] == expect, info
         check_case(BASES[op].scaled(rows=rows, N=N, seed=660 + N, dtype=dtype))
+        if expect == "wide":
+            check_case(BASES[op].scaled(rows=rows, N=N, seed=660 + N, dtype=dtype), "wide_element")
     # forced on rows of whole chunks (segments end exactly on the row's end)
     check_case(BASES[op].scaled(rows=2, N=65536, seed=661, dtype=dtype), "wide_element")
 
@@ -253,7 +256,7 @@ def test_split_rows_element_offsets_strides_constant_and_in_place():
         inp = workloads.make_inputs(w)
         ref = run_oracle(w, inp)
         for off, ld in [({n: 1 for n in ROW_TENSORS}, None), ({"x": 3, "y": 0}, {n: 20003 for n in ROW_TENSORS})]:
-            out = run_placed(w, inp, offset=off, ld=ld, expect_variant="element" if op == "softmax" else "wide_element")
+            out = run_placed(w, inp, offset=off, ld=ld, expect_variant="element" if op == "softmax" else "wide")
             check_outputs(w, ref, *out)
     w = workloads.C5.scaled(rows=3, N=50257, seed=673)
     inp = workloads.make_inputs(w)
@@ -318,15 +321,16 @@ def test_odd_widths(N):
         check_case(base.scaled(rows=3, N=N, seed=700 + N))
 
 
-@pytest.mark.parametrize("case", [("ln", "bf16", 16384, 4095), ("fused_add_ln", "fp16", 8192, 1001),
-                                  ("rms", "fp32", 16384, 101), ("fused_add_rms", "bf16", 2048, 16383),
-                                  ("softmax", "fp32", 16384, 333)], ids=lambda c: f"{c[0]}-{c[1]}-{c[2]}x{c[3]}")
+@pytest.mark.parametrize("case", [("ln", "bf16", 16384, 4095, "workgroup"), ("fused_add_ln", "fp16", 8192, 1001, "wave"),
+                                  ("rms", "fp32", 16384, 101, "wave"), ("fused_add_rms", "bf16", 2048, 16383, "element"),
+                                  ("softmax", "fp32", 16384, 333, "wave")], ids=lambda c: f"{c[0]}-{c[1]}-{c[2]}x{c[3]}")
 def test_element_kernel_persistent(case):
-    # many ragged rows go to the byte-addressed vectorized kernel by default; forced, the
-    # element / pair kernels run persistent
-    op, dtype, rows, N = case
+    # many ragged rows go to the byte-addressed vectorized kernel by default (16-bit fused rows
+    # of 8 waves at odd 2-byte positions to the pair kernel); forced, the element / pair kernels
+    # run persistent
+    op, dtype, rows, N, auto = case
     st, info = rn.plan(op, rows, N, TD[dtype])
-    assert st == 0 and info["variant"] in ("wave", "workgroup") and info["ragged"], info
+    assert st == 0 and info["variant"] == auto and info["ragged"] == (auto != "element"), info
     st, info = rn.plan(op, rows, N, TD[dtype], variant="element")
     assert st == 0 and info["variant"] == "element" and info["persistent"], info
     check_case(BASES[op].scaled(rows=rows, N=N, seed=720 + N, dtype=dtype), "element")

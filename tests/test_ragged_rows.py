@@ -9,7 +9,9 @@ the elements before and after the tensors) are checked to be left as they were.
 Cases cover every partial-chunk length of each dtype (fp32: 1-3 elements, 16-bit: 1-7),
 rows of one chunk or less, every row-group width (1 to 16 waves), all five operations with
 and without parameters, misaligned tensors with whole-chunk rows, odd row strides, and
-outputs written over their inputs."""
+outputs written over their inputs. (16-bit rows at odd 2-byte positions of the fused ops from
+4 waves per row and of RMSNorm from 8 take the pair kernel instead, by measurement: those
+shapes are left to the planner tests.)"""
 
 import os
 
@@ -143,7 +145,8 @@ SHAPES = [
     ("ln", "fp32", 2048, 3, True, True),         # rows shorter than a chunk: only a partial chunk
     ("ln", "fp32", 1100, 1022, False, True),     # 1 wave x 4 chunks, 2 of 4, beta only
     ("rms", "fp16", 1100, 2047, True, False),    # 1 wave x 4 chunks, 7 of 8
-    ("rms", "bf16", 280, 16383, False, False),   # 8 waves, 7 of 8, no weight
+    ("rms", "fp32", 280, 8191, False, False),    # 8 waves, 3 of 4, no weight
+    ("rms", "bf16", 280, 16382, False, False),   # 8 waves, 6 of 8 (rows at 4-byte positions)
     ("rms", "bf16", 1024, 9, True, False),       # one whole chunk and 1 element
     ("rms", "fp32", 520, 2049, True, False),     # 4 waves: 513 chunks of 1024 slots, 1 of 4
     ("fused_add_rms", "fp16", 520, 4094, True, False),   # 6 of 8
@@ -169,7 +172,8 @@ def test_ragged_rows_against_the_oracle(op, dtype, rows, N, gamma, beta):
     ("rms", "fp32", 1024, 1024, None, {"x": 1025, "y": 1027}),          # odd row strides
     ("rms", "fp16", 2048, 1000, {"x": 7, "y": 5}, {"x": 1001}),          # whole chunks per row, odd stride
     ("fused_add_rms", "bf16", 520, 4000, {"x": 1, "residual": 2, "y": 3, "residual_out": 5}, None),
-    ("fused_add_ln", "fp16", 270, 8191, {"x": 3, "residual": 1}, {"y": 8195, "residual_out": 8193}),
+    ("fused_add_ln", "fp16", 270, 8190, {"x": 2, "residual": 4}, {"y": 8194, "residual_out": 8192}),
+    ("fused_add_ln", "fp32", 270, 4095, {"x": 3, "residual": 1}, {"y": 4099, "residual_out": 4097}),
     ("softmax", "fp32", 300, 8192, {"x": 2, "y": 1}, None),
 ])
 def test_misaligned_tensors_and_strides(op, dtype, rows, N, off, ld):
