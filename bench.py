@@ -680,9 +680,14 @@ def plan_sweep_shapes():
                                                                                      "RMSNorm fp16 rows"),
         (workloads.C3.scaled(rows=4096, N=16383, dtype="fp32", name="rms_fp32_4096x16383"), "ragged 16-wave fp32 "
                                                                                             "RMSNorm rows"),
-        (workloads.C1.scaled(rows=1024, N=65537, name="ln_fp32_1024x65537"), "long ragged rows: element-granular "
-                                                                             "split rows against the general "
-                                                                             "kernel"),
+        (workloads.C1.scaled(rows=1024, N=65537, name="ln_fp32_1024x65537"), "long ragged rows: byte-addressed "
+                                                                             "one-pass split rows against the "
+                                                                             "element-granular two launches and "
+                                                                             "the general kernel"),
+        (c5.scaled(rows=1024, N=65539, name="ln_bf16_1024x65539"), "long ragged 16-bit rows (odd length)"),
+        (workloads.C4_FP16.scaled(rows=1024, N=65537, name="fused_fp16_1024x65537"), "long ragged fused add + "
+                                                                                     "RMSNorm rows"),
+        (sm.scaled(rows=1024, N=100003, name="softmax_fp32_1024x100003"), "long ragged fp32 softmax rows"),
         (workloads.C4_FP16, "persistent threshold: fused add + RMSNorm fp16 256 rows"),
         (fln.scaled(rows=384, name="fused_ln_bf16_384x4096"), "persistent threshold: fused add + LayerNorm "
                                                               "384 rows"),

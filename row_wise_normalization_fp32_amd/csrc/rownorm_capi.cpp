@@ -241,6 +241,18 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     // (under kPersistentVecBlocks row blocks) take the element / pair kernels, or the
     // grid-per-row kernel.
     const int64_t Cr = (N * s + 15) / 16;
+    // 16-bit rows that start at odd 2-byte positions (an odd N or row stride, or a row tensor at
+    // an odd element offset): their 16-byte accesses cost the most (see the rules below)
+    bool odd2 = false;
+    if (s == 2) {
+        const void* rowp[] = {a.x, a.residual, a.y, a.residual_out};
+        const int64_t lds[] = {a.ldx, a.ldr, a.ldy, a.ldro};
+        for (int i = 0; i < 4; ++i) {
+            if (!rowp[i]) continue;
+            if ((reinterpret_cast<uintptr_t>(rowp[i]) >> 1) & 1) odd2 = true;
+            if (rows > 1 && (lds[i] & 1)) odd2 = true;
+        }
+    }
     bool ragged = false;
     if (Cr <= group_cap && a.variant == RN_VARIANT_AUTO) {
         int wr = next_pow2((Cr + 64 * rn::kTargetChunks - 1) / (64 * rn::kTargetChunks));
@@ -249,10 +261,8 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
         const int64_t vr = next_pow2((Cr + 64 * wr - 1) / (64 * wr));
         const bool fills = Cr == int64_t(64) * wr * vr;  // the row group holds the row exactly
         ragged = (!vec_ok || !fills) && (rows + rpb - 1) / rpb >= rn::kPersistentVecBlocks;
-        // 16-bit rows that start at odd 2-byte positions (an odd N or row stride, or a tensor at
-        // an odd element offset): their 16-byte accesses cost the most there, and light kernels
-        // with several row tensors go faster through the element / pair kernels' aligned 4-byte
-        // words. Measured on MI355X (cold cache, graph replays, byte-addressed against the
+        // At odd 2-byte positions light kernels with several row tensors go faster through the
+        // element / pair kernels' aligned 4-byte words. Measured on MI355X (cold cache, graph replays, byte-addressed against the
         // element / pair kernel): fused add + RMSNorm fp16 8192 x 8191 (4 waves) 112.4 against
         // 100.9 us, fused add + LayerNorm bf16 8192 x 8191 118.9 against 112.0, RMSNorm fp16
         // 4096 x 16383 (8 waves) 60.1 against 57.0, RMSNorm bf16 8192 x 8191 (4 waves) 53.1
@@ -260,27 +270,21 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
         // 16384 x 4095 99.2 against 103.3 us, RMSNorm fp16 16384 x 4095 47.8 against 54.0), and
         // so it is for LayerNorm and softmax at every width (LayerNorm bf16 4096 x 16383 64.1
         // against 81.2, softmax bf16 8192 x 8191 53.3 against 78.5).
-        bool odd2 = false;
-        if (s == 2) {
-            const void* rowp[] = {a.x, a.residual, a.y, a.residual_out};
-            const int64_t lds[] = {a.ldx, a.ldr, a.ldy, a.ldro};
-            for (int i = 0; i < 4; ++i) {
-                if (!rowp[i]) continue;
-                if ((reinterpret_cast<uintptr_t>(rowp[i]) >> 1) & 1) odd2 = true;
-                if (rows > 1 && (lds[i] & 1)) odd2 = true;
-            }
-        }
         if (odd2 && ((fused && wr >= 4) || (a.op == RN_OP_RMS_NORM && wr >= 8))) ragged = false;
     }
     if (tune && ragged) return RN_ERR_UNSUPPORTED;  // a tuning applies to whole-chunk rows only
     // Long ragged rows (beyond what the element kernels hold) with a workspace of the one-pass
     // layout, out of place, in at most kWideOnePassMaxSeg segments: the one-pass split rows with
     // byte-addressed segments (x read once) instead of the element-granular two launches (x read
-    // twice).
+    // twice). Not for 16-bit rows at odd 2-byte positions, whose 16-byte accesses cost the split
+    // rows more than reading x twice does. Measured on MI355X (cold cache, graph replays):
+    // LayerNorm fp32 1024 x 65537 134.2 against 160.9 us, softmax fp32 1024 x 100003 205.4
+    // against 239.4 us, fused add + RMSNorm fp16 1024 x 65537 134.0 against 134.2 us; bf16
+    // 1024 x 65539 (odd positions) 113.1 against 107.9 us.
     const int64_t elem_cap_rows = int64_t(64) * rn::kMaxGroupWaves *
                                   (sm ? rn::kSoftmaxElemMaxPerLane : rn::kElemMaxPerLane);
     bool wide_rag = false;
-    if (!vec_ok && !ragged && ws_given && a.variant == RN_VARIANT_AUTO && N > elem_cap_rows) {
+    if (!vec_ok && !ragged && !odd2 && ws_given && a.variant == RN_VARIANT_AUTO && N > elem_cap_rows) {
         const bool in_place = a.y == a.x || (a.residual_out != nullptr &&
                                              (a.residual_out == a.residual || a.residual_out == a.x)) ||
                               (a.residual != nullptr && a.y == a.residual);

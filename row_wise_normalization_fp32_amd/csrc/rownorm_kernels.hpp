@@ -1748,6 +1748,10 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_onepass_kernel(Params
     int buf = 0;
     const int S = wa.S;
     const unsigned total = static_cast<unsigned>(wa.P) * static_cast<unsigned>(S);
+    // chunks per segment: 2048; byte-addressed rows split evenly instead (ceil(C / S) each, at
+    // most 2048), so that a row's last segment is not a sliver whose workgroup idles while
+    // the row waits for its record
+    const int64_t L = RAG ? (p.C + S - 1) / S : kWideChunks;
     for (;;) {
         if (t == 0) s_ticket = __hip_atomic_fetch_add(wa.sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();
@@ -1755,8 +1759,8 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_onepass_kernel(Params
         if (ticket >= total) break;        // uniform over the workgroup
         const int64_t blk = ticket / static_cast<unsigned>(S);
         const int seg = static_cast<int>(ticket % static_cast<unsigned>(S));
-        const int64_t c0 = static_cast<int64_t>(seg) * kWideChunks;
-        const int Cs = static_cast<int>(p.C - c0 < kWideChunks ? p.C - c0 : kWideChunks);
+        const int64_t c0 = static_cast<int64_t>(seg) * L;
+        const int Cs = static_cast<int>(p.C - c0 < L ? p.C - c0 : L);
         auto valid = [&](int i) { return EXACT || i * kWideLanes + t < Cs; };
         auto chunk = [&](int i) {
             const int c = i * kWideLanes + t;
@@ -1765,15 +1769,15 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_onepass_kernel(Params
         // RAG geometry of segment s: its first byte in the row, its bytes, its partial chunk
         const int64_t row_bytes = p.N * SB;
         auto seg_bytes = [&](int s_) {
-            const int64_t b0 = static_cast<int64_t>(s_) * kWideChunks * 16;
+            const int64_t b0 = static_cast<int64_t>(s_) * L * 16;
             const int64_t rem = row_bytes - b0;
-            return static_cast<uint32_t>(rem < kWideChunks * 16 ? rem : kWideChunks * 16);
+            return static_cast<uint32_t>(rem < L * 16 ? rem : L * 16);
         };
         auto seg_tail = [&](int s_) {
             WideTail tl;
             const int te = static_cast<int>(p.N % E);
             if (RAG && te != 0 && s_ == S - 1) {
-                const int idx = static_cast<int>(p.C - 1 - static_cast<int64_t>(s_) * kWideChunks);
+                const int idx = static_cast<int>(p.C - 1 - static_cast<int64_t>(s_) * L);
                 tl.ti = idx / kWideLanes;
                 tl.tt = idx % kWideLanes;
                 tl.te = te;
@@ -1903,8 +1907,8 @@ __global__ __launch_bounds__(kWideLanes) void rownorm_wide_onepass_kernel(Params
         // segment s2's record of one row, computed here from memory, one chunk per tensor at a
         // time (the rows in flight keep their registers)
         auto other_record = [&](int64_t row, int s2) {
-            const int64_t c2 = static_cast<int64_t>(s2) * kWideChunks;
-            const int Cs2 = static_cast<int>(p.C - c2 < kWideChunks ? p.C - c2 : kWideChunks);
+            const int64_t c2 = static_cast<int64_t>(s2) * L;
+            const int Cs2 = static_cast<int>(p.C - c2 < L ? p.C - c2 : L);
             const WideTail tl2 = seg_tail(s2);
             const uint32_t sb2 = seg_bytes(s2);
             // RAG: the segment's resource, and the byte offset of its 2-byte last element

@@ -453,15 +453,21 @@ def test_plan_split_rows():
     # bf16 rows of whole chunks up to 32768 elements stay in one workgroup, workspace or not
     assert rn.plan("ln", 8, 32768, bf16, workspace_bytes=8 * 8 * 16)[1]["variant"] == "workgroup"
     # other rows longer than 16384 elements: with room for the one-pass layout, byte-addressed
-    # segments of 2048 chunks (the last chunk partial); with only the two-launch form's records,
-    # or in place, segments of 8192 elements
-    for N, dt, ptrs, strides in [(65537, f32, None, None), (50257, bf16, None, None),
-                                 (65536, f32, {"x": (1 << 40) + 4}, None), (20000, bf16, None, {"x": 20001})]:
+    # segments of up to 2048 chunks (the last chunk partial); 16-bit rows at odd 2-byte
+    # positions, and with only the two-launch form's records or in place any rows, segments of
+    # 8192 elements
+    for N, dt, ptrs, strides, one in [(65537, f32, None, None, True), (50257, bf16, None, None, False),
+                                      (50258, bf16, None, None, True), (65536, f32, {"x": (1 << 40) + 4}, None, True),
+                                      (20000, bf16, None, {"x": 20001}, False),
+                                      (20000, bf16, {"x": (1 << 40) + 4}, None, True)]:
         ws = rn.forward_workspace_bytes("ln", 8, N, dt)
         st, info = rn.plan("ln", 8, N, dt, workspace_bytes=ws, ptrs=ptrs, strides=strides)
         C = (N * (4 if dt == f32 else 2) + 15) // 16
-        assert st == OK and info["variant"] == "wide" and info["ragged"] and not info["exact"], (N, info)
-        assert info["grid_blocks"] == 8 * ((C + 2047) // 2048) and info["chunks_per_lane"] == 4
+        if one:
+            assert st == OK and info["variant"] == "wide" and info["ragged"] and not info["exact"], (N, info)
+            assert info["grid_blocks"] == 8 * ((C + 2047) // 2048) and info["chunks_per_lane"] == 4
+        else:
+            assert st == OK and info["variant"] == "wide_element" and not info["ragged"], (N, info)
         S = (N + 8191) // 8192
         for kw in ({"workspace_bytes": 8 * S * 16}, {"workspace_bytes": ws, "in_place": True}):
             pp, sd = dict(ptrs or {}), dict(strides or {})

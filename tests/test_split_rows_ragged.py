@@ -84,25 +84,32 @@ def _check(w, ref, o):
 
 
 CASES = [
-    # (base workload, dtype, rows, N): the last segment ends with a chunk of N mod E elements
+    # (base workload, dtype, rows, N): the last segment ends with a chunk of N mod E elements.
+    # 16-bit rows of odd length take this path only as a single row (several such rows sit at
+    # odd 2-byte positions, which the planner gives to the element-granular two launches):
+    # those cases move the row's last element by the 2-byte access.
     (workloads.C2, "fp32", 40, 65537),        # 1 of 4; the last segment holds only that chunk
     (workloads.C2, "fp32", 40, 65538),        # 2 of 4
     (workloads.C1, "fp32", 40, 65539),        # 3 of 4
-    (workloads.C5, "bf16", 32, 65537),        # 1 of 8 (the 2-byte access alone)
+    (workloads.C5, "bf16", 1, 65537),         # 1 of 8 (the 2-byte access alone)
     (workloads.C5, "bf16", 32, 65538),        # 2 of 8
-    (workloads.C5, "bf16", 32, 65539),        # 3 of 8
+    (workloads.C5, "bf16", 1, 65539),         # 3 of 8
     (workloads.C5, "fp16", 32, 65540),        # 4 of 8
-    (workloads.C5, "bf16", 32, 65541),        # 5 of 8
+    (workloads.C5, "bf16", 1, 65541),         # 5 of 8
     (workloads.C5, "fp16", 32, 65542),        # 6 of 8
-    (workloads.C5, "bf16", 32, 65543),        # 7 of 8
-    (workloads.C5, "bf16", 24, 20001),        # two segments, the second of 453 chunks
-    (workloads.C3, "fp16", 32, 50001),
-    (workloads.C4_FP16, "fp16", 24, 70001),
-    (workloads.C4_BF16, "bf16", 24, 65539),
-    (workloads.FUSED_LN, "bf16", 24, 50003),
+    (workloads.C5, "bf16", 1, 65543),         # 7 of 8
+    (workloads.C5, "bf16", 24, 20002),        # two segments
+    (workloads.C3, "fp16", 32, 50002),
+    (workloads.C3, "fp16", 1, 50001),
+    (workloads.C4_FP16, "fp16", 24, 70002),
+    (workloads.C4_FP16, "fp16", 1, 70001),
+    (workloads.C4_BF16, "bf16", 24, 65538),
+    (workloads.FUSED_LN, "bf16", 1, 50003),
+    (workloads.FUSED_LN, "bf16", 24, 50006),
     (workloads.FUSED_LN.scaled(dtype="fp32"), "fp32", 16, 40001),
     (workloads.SOFTMAX, "fp32", 16, 100003),
-    (workloads.SOFTMAX, "bf16", 16, 70001),
+    (workloads.SOFTMAX, "bf16", 16, 70002),
+    (workloads.SOFTMAX, "bf16", 1, 70001),
 ]
 
 
@@ -142,11 +149,12 @@ def _placed(rows, N, dtype, off, ld, src=None):
 
 
 @pytest.mark.parametrize("op,dtype,rows,N,off,ld", [
-    ("ln", "bf16", 16, 65536, {"x": 1, "y": 3}, {}),                     # whole chunks, misaligned tensors
+    ("ln", "bf16", 16, 65536, {"x": 2, "y": 6}, {}),                     # whole chunks, misaligned tensors
     ("ln", "fp32", 12, 50000, {"x": 1}, {"y": 50003}),                  # padded odd stride
-    ("rms", "fp16", 16, 40001, {"x": 2, "y": 5}, {"x": 40003}),
-    ("fused_add_rms", "bf16", 12, 65536, {"x": 1, "residual": 2, "y": 3, "residual_out": 5}, {}),
-    ("fused_add_ln", "fp16", 12, 33333, {"x": 3, "residual": 1}, {"y": 33337, "residual_out": 33335}),
+    ("ln", "fp32", 12, 50001, {"x": 3, "y": 2}, {"x": 50005}),
+    ("rms", "fp16", 16, 40002, {"x": 2, "y": 4}, {"x": 40004}),
+    ("fused_add_rms", "bf16", 12, 65536, {"x": 2, "residual": 4, "y": 6, "residual_out": 10}, {}),
+    ("fused_add_ln", "fp16", 12, 33334, {"x": 2, "residual": 6}, {"y": 33338, "residual_out": 33336}),
     ("softmax", "fp32", 8, 70000, {"x": 2, "y": 1}, {}),
 ])
 def test_byte_addressed_one_pass_placement(op, dtype, rows, N, off, ld):
@@ -194,3 +202,18 @@ def test_byte_addressed_one_pass_placement(op, dtype, rows, N, off, ld):
         v = views[k]
         mask[v.storage_offset():v.storage_offset() + rows * v.stride(0)].view(rows, v.stride(0))[:, :N] = False
         assert torch.equal(_bits(bufs[k])[mask], _bits(b0)[mask]), k
+
+
+@pytest.mark.parametrize("op,dtype,rows,N", [("ln", "bf16", 24, 65539), ("fused_add_rms", "fp16", 16, 50001),
+                                             ("softmax", "bf16", 8, 70001)])
+def test_odd_position_16bit_rows_take_element_segments(op, dtype, rows, N):
+    # several 16-bit rows of odd length sit at odd 2-byte positions: the element-granular two
+    # launches (measured faster there than 16-byte accesses at those positions)
+    base = {"ln": workloads.C5, "fused_add_rms": workloads.C4_FP16, "softmax": workloads.SOFTMAX}[op]
+    w = base.scaled(rows=rows, N=N, seed=1790 + rows, dtype=dtype)
+    inp = workloads.make_inputs(w)
+    g = {k: v.to(DEV) for k, v in inp.items()}
+    need = rn.forward_workspace_bytes(w.op, rows, N, g["x"].dtype)
+    st, info = rn.plan(w.op, rows, N, g["x"].dtype, workspace_bytes=need)
+    assert st == 0 and info["variant"] == "wide_element" and not info["ragged"], info
+    _check(w, _oracle(w, inp), _forward(w, g, torch.empty(need, dtype=torch.uint8, device=DEV)))
