@@ -54,12 +54,21 @@
  *     by one 64-lane wavefront (rows of up to 4 KiB, or 16 KiB when forced) or by a group of
  *     up to 16 wavefronts (rows of up to 64 KiB: 16384 fp32 or 32768 fp16 / bf16 elements;
  *     softmax and RMSNorm rows of up to 128 KiB, and LayerNorm and fused add + RMSNorm rows
- *     of up to 128 KiB when no workspace is given).
+ * *     of up to 128 KiB when no workspace is given).
+ *     Other rows of up to 64 KiB (not whole chunks, or tensors / strides only element-
+ *     aligned), when there are at least 256 row blocks, run the same vectorized kernel with
+ *     rows addressed by byte: 16-byte accesses at element alignment through a buffer
+ *     resource that ends with the row, the row's partial last chunk by its whole 4-byte
+ *     words, and the last element of an odd-length 16-bit row by one 2-byte access; rows of
+ *     whole chunks that do not fill their group of wavefronts exactly take it too (16-bit
+ *     rows at odd 2-byte positions of the fused ops from 4 wavefronts per row and of
+ *     RMSNorm from 8 keep the element / pair kernels, which measure faster there).
  *     Otherwise rows of up to 16384 elements are held in registers one element per slot
  *     (the element kernel, still one read of x; 16-bit rows whose tensors share their
  *     position within 4-byte words move as element pairs). Longer rows take the split-row
- *     kernels (whole-chunk rows: 16-byte chunks; other rows: elements) when rn_forward_ex is
- *     given a workspace; without one (and beyond the 128 KiB rows above) they take a general
+ *     kernels (16-byte chunks, rows addressed by byte when they are not whole chunks; 16-bit
+ *     rows at odd 2-byte positions and in-place calls: elements) when rn_forward_ex is given
+ *     a workspace; without one (and beyond the 128 KiB rows above) they take a general
  *     kernel that reads the row up to three times.
  *   - Launches use the current HIP device (the device of the buffers and of `stream`). The
  *     first call of a kernel configuration on a device queries its occupancy once.
@@ -109,11 +118,15 @@ typedef enum rn_variant {
     RN_VARIANT_GENERAL = 3,   /* any N, any element-aligned pointers; re-reads the row */
     RN_VARIANT_ELEMENT = 4,   /* rows up to 16384 elements held in VGPRs one element per slot;
                                  any element-aligned pointers and strides */
-    RN_VARIANT_WIDE = 5,      /* rows longer than RN_VARIANT_WORKGROUP holds (whole 16-byte
-                                 chunks): split into 32 KiB segments, one workgroup each, that
-                                 exchange statistics through the workspace; x is read once
-                                 (two launches, x read twice, for in-place calls or a workspace
-                                 of only the two-launch size); needs a workspace (rn_forward_ex) */
+    RN_VARIANT_WIDE = 5,      /* rows longer than RN_VARIANT_WORKGROUP holds: split into 32 KiB
+                                 segments, one workgroup each, that exchange statistics through
+                                 the workspace; x is read once (two launches, x read twice, for
+                                 in-place calls or a workspace of only the two-launch size).
+                                 Rows of whole 16-byte chunks; under RN_VARIANT_AUTO also other
+                                 long rows (byte-addressed segments of ceil(C / S) chunks, C the
+                                 row's chunks rounded up, S the segments of 32 KiB), out of
+                                 place with a one-pass workspace, except 16-bit rows at odd
+                                 2-byte positions; needs a workspace (rn_forward_ex) */
     RN_VARIANT_WIDE_ELEMENT = 6 /* rows of more than 16384 elements with any element-aligned
                                  pointers and strides: split into segments of 8192 elements (one
                                  per register slot), one workgroup each, in two launches; needs a
@@ -195,8 +208,11 @@ int softmax_forward(const void* x, void* y, float* row_max, float* row_sum, int6
  *   strides    nullable (all rows dense); see rn_row_strides.
  *   variant    an rn_variant; RN_VARIANT_AUTO chooses as the plain entry points do, except
  *              that rows too long for one workgroup's registers take RN_VARIANT_WIDE (whole
- *              16-byte chunks) or RN_VARIANT_WIDE_ELEMENT (any other rows of more than 16384
- *              elements) when a large enough workspace is given. A forced variant that cannot
+ *              16-byte chunks; other rows of more than 16384 elements when the workspace has
+ *              the one-pass size, the call is out of place and, for 16-bit rows, no row
+ *              tensor or stride sits at an odd 2-byte position) or RN_VARIANT_WIDE_ELEMENT
+ *              (the remaining rows of more than 16384 elements) when a large enough
+ *              workspace is given. A forced variant that cannot
  *              run the shape / alignment returns RN_ERR_UNSUPPORTED (the split-row variants
  *              without a large enough workspace: RN_ERR_WORKSPACE).
  *   workspace  nullable device memory of workspace_bytes, 16-byte aligned, owned by the
@@ -205,8 +221,9 @@ int softmax_forward(const void* x, void* y, float* row_max, float* row_sum, int6
  *              share it must be ordered (same stream).
  * Unknown op codes return RN_ERR_SHAPE.
  *
- * Split rows (walkthrough section 1.1: a row that outgrows one block). Rows of whole 16-byte
- * chunks with up to 256 segments, called out of place with a workspace of
+ * Split rows (walkthrough section 1.1: a row that outgrows one block). Rows with up to 256
+ * segments (whole 16-byte chunks, or under RN_VARIANT_AUTO the byte-addressed rows named at
+ * RN_VARIANT_WIDE), called out of place with a workspace of
  * rn_forward_workspace_bytes, take one pass that reads x (and the residual) once: a small
  * kernel first clears a 256-byte header (a ticket counter; at byte offset 4 a 32-bit count of
  * records computed by waiting workgroups, left there as a diagnostic) and the records; the

@@ -2577,7 +2577,7 @@ inline hipError_t launch_v(const Plan& plan, const Params& p, hipStream_t s) {
             }
         }
         return hipErrorNotSupported;
-    }
+    } else {
     // The planner gives rows of 8 and 16 waves 4 chunks per lane (or 8 / 16 for the one-
     // workgroup rows below); fewer chunks per lane occur only with 1, 2 and 4 waves.
     if constexpr (W <= 4) {
@@ -2604,8 +2604,9 @@ inline hipError_t launch_v(const Plan& plan, const Params& p, hipStream_t s) {
     if constexpr (W == 16 && !PERS && OP == OP_SOFTMAX && DT == DT_F32) {  // fp32 softmax rows up to 256 KiB
         if (plan.chunks_per_lane == 16) return RN_GO(16);
     }
-#undef RN_GO
     return hipErrorNotSupported;  // no instance of this shape is built
+    }
+#undef RN_GO
 }
 
 template <int DT, int OP, bool EXACT, int AFF, bool PERS, bool RAG = false>

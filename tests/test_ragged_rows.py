@@ -1,8 +1,10 @@
 """GPU parity of ragged rows on the vectorized kernel: persistent launches of many rows whose
 length is not a whole number of 16-byte chunks, or whose row tensors start at addresses or
-row strides that are only element-aligned. Those rows are addressed by byte: whole chunks as
-16-byte accesses at element alignment, the row's partial last chunk in 8-, 4- and 2-byte
-pieces. Every case is checked against the fp64 oracle (the same bars as the aligned rows),
+row strides that are only element-aligned. Those rows are addressed by byte: every chunk as a
+16-byte access at element alignment through a buffer resource that ends with the row (the
+partial last chunk moves its whole dwords), and the last element of an odd-length 16-bit row
+by one 2-byte access. Every case is checked against the fp64 oracle (the same bars as the
+aligned rows),
 the plan is checked to be that path, and the bytes around every output row (row padding,
 the elements before and after the tensors) are checked to be left as they were.
 
