@@ -688,6 +688,24 @@ def plan_sweep_shapes():
         (workloads.C4_FP16.scaled(rows=1024, N=65537, name="fused_fp16_1024x65537"), "long ragged fused add + "
                                                                                      "RMSNorm rows"),
         (sm.scaled(rows=1024, N=100003, name="softmax_fp32_1024x100003"), "long ragged fp32 softmax rows"),
+        # hidden sizes that are whole chunks but no power-of-two number of them (640 = 64 x 10
+        # chunks, 896 = 64 x 14, ...): the row group of a power-of-two width and depth holds them
+        # with idle slots
+        (c5.scaled(rows=8192, N=5120, name="ln_bf16_8192x5120"), "hidden size 5120: 640 chunks = 64 x 2 x 5"),
+        (workloads.C3.scaled(rows=8192, N=7168, dtype="bf16", name="rms_bf16_8192x7168"),
+         "hidden size 7168: 896 chunks = 64 x 2 x 7"),
+        (workloads.C4_BF16.scaled(rows=8192, N=5120, name="fused_bf16_8192x5120"),
+         "fused add + RMSNorm, hidden size 5120"),
+        (c5.scaled(rows=16384, N=3072, name="ln_bf16_16384x3072"), "hidden size 3072: 384 chunks = 64 x 2 x 3"),
+        (workloads.C3.scaled(rows=16384, N=1536, dtype="bf16", name="rms_bf16_16384x1536"),
+         "hidden size 1536: 192 chunks = 64 x 3"),
+        (workloads.C1.scaled(rows=8192, N=5120, name="ln_fp32_8192x5120"), "fp32 hidden size 5120: 1280 chunks = "
+                                                                           "64 x 4 x 5"),
+        (fln.scaled(rows=8192, N=6144, name="fused_ln_bf16_8192x6144"), "fused add + LayerNorm, hidden size 6144: "
+                                                                        "768 chunks = 64 x 4 x 3"),
+        (workloads.C3.scaled(rows=4096, N=14336, dtype="bf16", name="rms_bf16_4096x14336"),
+         "width 14336: 1792 chunks = 64 x 4 x 7"),
+        (c5.scaled(rows=16384, N=2560, name="ln_bf16_16384x2560"), "hidden size 2560: 320 chunks = 64 x 5"),
         (workloads.C4_FP16, "persistent threshold: fused add + RMSNorm fp16 256 rows"),
         (fln.scaled(rows=384, name="fused_ln_bf16_384x4096"), "persistent threshold: fused add + LayerNorm "
                                                               "384 rows"),

@@ -51,6 +51,23 @@ int next_pow2(int64_t v) {
     return p;
 }
 
+// Rows of C = 64 * 2^k * o chunks with o = 3, 5 or 7 and 2^k <= kMaxGroupWaves (o * 2^k * 64 <=
+// the row-group capacity): returns o and sets *w = 2^k; otherwise 0.
+int odd_lane_chunks(int64_t C, int* w) {
+    *w = 0;
+    if (C <= 0 || C % 64 != 0) return 0;
+    int64_t m = C / 64;
+    int k = 1;
+    while (m % 2 == 0 && k < rn::kMaxGroupWaves) {
+        m /= 2;
+        k *= 2;
+    }
+    if (!(m == 3 || m == 5 || m == 7) || int64_t(64) * k * m > int64_t(64) * rn::kMaxGroupWaves * rn::kMaxGroupChunks)
+        return 0;
+    *w = k;
+    return static_cast<int>(m);
+}
+
 bool is_ln(int op) { return op == RN_OP_LAYER_NORM || op == RN_OP_FUSED_ADD_LAYER_NORM; }
 bool is_fused(int op) { return op == RN_OP_FUSED_ADD_RMS_NORM || op == RN_OP_FUSED_ADD_LAYER_NORM; }
 
@@ -253,8 +270,22 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
             if (rows > 1 && (lds[i] & 1)) odd2 = true;
         }
     }
+    // Whole-chunk rows of 64 x 2^k x o chunks, o = 3, 5 or 7 (16-bit rows of 1536, 2560, 3072,
+    // 3584, 5120, 6144, 7168, 14336 elements; fp32 rows of 2560, 3072, 5120, 7168, ...): a row
+    // group of 2^k waves holding o chunks per lane holds them exactly, with no idle slot, where
+    // the power-of-two row group would leave a quarter to a half of its slots idle and mask
+    // every element. Persistent launches only (the instances built), many rows.
+    int odd_w = 0, odd_v = 0;
+    if (vec_ok && a.variant == RN_VARIANT_AUTO) {
+        const int vo = odd_lane_chunks(Cr, &odd_w);
+        if (vo > 0) {
+            const int64_t rpb = odd_w <= 4 ? 4 / odd_w : 1;
+            if ((rows + rpb - 1) / rpb >= rn::kPersistentVecBlocks) odd_v = vo;
+        }
+        if (odd_v == 0) odd_w = 0;
+    }
     bool ragged = false;
-    if (Cr <= group_cap && a.variant == RN_VARIANT_AUTO) {
+    if (Cr <= group_cap && a.variant == RN_VARIANT_AUTO && odd_v == 0) {
         int wr = next_pow2((Cr + 64 * rn::kTargetChunks - 1) / (64 * rn::kTargetChunks));
         if (wr > rn::kMaxGroupWaves) wr = rn::kMaxGroupWaves;
         const int64_t rpb = wr <= 4 ? 4 / wr : 1;
@@ -319,6 +350,7 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     // chunks (measured on MI355X: 4 chunks per lane balances bytes in flight against VGPRs).
     int w_auto = next_pow2((C + 64 * rn::kTargetChunks - 1) / (64 * rn::kTargetChunks));
     if (w_auto > rn::kMaxGroupWaves) w_auto = rn::kMaxGroupWaves;
+    if (odd_v > 0) w_auto = odd_w;
 
     int v = a.variant;
     if (v == RN_VARIANT_AUTO) {
@@ -435,6 +467,15 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
         plan->waves_per_row = W;
         plan->rows_per_block = W <= 4 ? 4 / W : 1;
         plan->chunks_per_lane = next_pow2((C + 64 * W - 1) / (64 * W));
+        if (odd_v > 0) {
+            // 3, 5 or 7 chunks per lane when W waves hold the row exactly so (persistent
+            // instances only: not for a caller-chosen launch of one workgroup per row block)
+            int wo = 0;
+            const int vo = odd_lane_chunks(C, &wo);
+            if (vo > 0 && wo == W && (rows + plan->rows_per_block - 1) / plan->rows_per_block >=
+                                         rn::kPersistentVecBlocks && !(tune && a.tune->persistent == 0))
+                plan->chunks_per_lane = vo;
+        }
         if (tune && a.tune->chunks_per_lane > 0) {
             // the row group must cover the row
             if (int64_t(64) * W * a.tune->chunks_per_lane < C) return RN_ERR_UNSUPPORTED;

@@ -2588,6 +2588,15 @@ inline hipError_t launch_v(const Plan& plan, const Params& p, hipStream_t s) {
         }
     }
     if (plan.chunks_per_lane == 4) return RN_GO(4);
+    // Rows of 64 * W * o chunks, o = 3, 5, 7, held exactly (persistent launches only; rows of
+    // 16 waves: o = 3, the rest exceed 4096 chunks)
+    if constexpr (PERS && EXACT) {
+        if (plan.chunks_per_lane == 3) return RN_GO(3);
+        if constexpr (W <= 8) {
+            if (plan.chunks_per_lane == 5) return RN_GO(5);
+            if (plan.chunks_per_lane == 7) return RN_GO(7);
+        }
+    }
     if constexpr (W == 1) {
         switch (plan.chunks_per_lane) {
         case 8: return RN_GO(8);

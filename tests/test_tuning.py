@@ -29,6 +29,10 @@ SHAPES = [
     workloads.FUSED_LN.scaled(rows=131, N=8192, seed=1705, name="fused_ln_bf16_131x8192"),
     workloads.SOFTMAX.scaled(rows=270, seed=1706, name="softmax_fp32_270x4096"),
     workloads.C1.scaled(rows=517, seed=1707, name="ln_fp32_517x1024"),
+    # rows held exactly by 3, 5 or 7 chunks per lane (2 waves x 5, 4 x 3, 4 x 7)
+    workloads.C5.scaled(rows=523, N=5120, seed=1708, name="ln_bf16_523x5120"),
+    workloads.FUSED_LN.scaled(rows=263, N=6144, seed=1709, name="fused_ln_bf16_263x6144"),
+    workloads.C3.scaled(rows=259, N=14336, seed=1710, name="rms_fp16_259x14336"),
 ]
 
 TUNINGS = ([{"waves_per_row": w} for w in (1, 2, 4, 8, 16)] +

@@ -110,3 +110,40 @@ def test_tuned_entry_point_rejects_before_launch():
     st = rn._lib.rn_forward_tuned(0, 0x100000, None, None, None, 0x200000, None, None, None, 4, 4096, 1e-5, 2,
                                   None, 0, ctypes.byref(t), None, 0, None)
     assert st == UNSUP
+
+
+@pytest.mark.parametrize("op,rows,N,dtype,W,V", [
+    ("ln", 16384, 1536, BF16, 1, 3), ("rms", 16384, 2560, F16, 1, 5), ("ln", 16384, 3584, BF16, 1, 7),
+    ("ln", 8192, 3072, BF16, 2, 3), ("ln", 8192, 5120, BF16, 2, 5), ("rms", 8192, 7168, BF16, 2, 7),
+    ("fused_add_ln", 8192, 6144, BF16, 4, 3), ("ln", 8192, 5120, F32, 4, 5), ("fused_add_rms", 4096, 14336, F16, 4, 7),
+    ("softmax", 4096, 12288, BF16, 8, 3), ("ln", 4096, 20480, BF16, 8, 5), ("ln", 4096, 7168 * 2, F32, 8, 7),
+    ("ln", 2048, 24576, BF16, 16, 3),
+])
+def test_rows_held_exactly_by_odd_chunk_counts(op, rows, N, dtype, W, V):
+    # rows of 64 x W x V chunks, V = 3, 5, 7: W waves with V chunks per lane, exact and
+    # persistent, automatically and when the caller names W
+    for t in (None, {"waves_per_row": W}, {"waves_per_row": W, "persistent": 1}):
+        st, info = plan(op, rows, N, dtype, t)
+        assert st == OK, (t, st)
+        assert (info["waves_per_row"], info["chunks_per_lane"]) == (W, V), (t, info)
+        assert info["exact"] and info["persistent"] and not info["ragged"], (t, info)
+
+
+def test_odd_chunk_counts_fall_back_where_not_built():
+    # few rows (under 256 row blocks of the exact row group): the power-of-two plan
+    st, info = plan("ln", 300, 5120, BF16, None)
+    assert st == OK and (info["waves_per_row"], info["chunks_per_lane"]) == (4, 4) and info["ragged"], info
+    st, info = plan("ln", 100, 5120, BF16, None)
+    assert st == OK and not info["persistent"] and not info["exact"], info
+    # a caller-chosen grid-per-row launch, or another width: power-of-two chunks per lane
+    st, info = plan("ln", 8192, 5120, BF16, {"waves_per_row": 4})
+    assert st == OK and (info["chunks_per_lane"], info["exact"], info["persistent"]) == (4, False, False), info
+    assert plan("ln", 8192, 5120, BF16, {"waves_per_row": 2, "persistent": 0})[0] == UNSUP  # 2 x 8 not built
+    st, info = plan("ln", 8192, 5120, BF16, {"waves_per_row": 1, "persistent": 0})
+    assert st == OK and (info["chunks_per_lane"], info["persistent"]) == (16, False), info
+    # 9 and 11 chunks per 64 lanes: no exact odd row group
+    for N in (4608, 5632):
+        st, info = plan("ln", 8192, N, BF16, None)
+        assert st == OK and info["chunks_per_lane"] in (1, 2, 4) and not info["exact"], (N, info)
+    # a caller-chosen odd count on a grid-per-row launch is not built
+    assert plan("ln", 8192, 5120, BF16, {"waves_per_row": 2, "chunks_per_lane": 5, "persistent": 0})[0] == UNSUP
