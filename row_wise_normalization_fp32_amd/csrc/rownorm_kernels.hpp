@@ -87,9 +87,20 @@ __device__ __forceinline__ To bit_cast(From v) {
 using Rsrc = __amdgpu_buffer_rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;  // 32-bit data format, no swizzle (untyped accesses)
 
+//
+// Every resource here describes memory of one row (or segment, or parameter vector) that the
+// whole wave works on: base and size are the same on every lane. They are taken from the
+// first active lane so that the compiler keeps the descriptor in SGPRs even where it cannot
+// prove it uniform (a value defined inside a loop that lanes leave at different times counts
+// as divergent after it); a descriptor in VGPRs would wrap each access in a loop over the
+// distinct descriptors of the lanes.
 __device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
-                                             kRsrcWord3);
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+    void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, static_cast<short>(0), static_cast<int>(n), kRsrcWord3);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -598,7 +609,7 @@ struct VecRow {
         const Rsrc r = make_rsrc(base, g.rb);
         if (valid(i, t, Ci))  // the partial chunk: its whole dwords
             __builtin_amdgcn_raw_buffer_store_b128(v, r, (i * LANES + t) * 16, 0, CPS);
-        if (i == g.ti && tail_wave(g, t)) {  // and the half dword of an odd-length 16-bit row
+        if (tail_slot(i, g) && tail_wave(g, t)) {  // and the half dword of an odd-length 16-bit row
             const unsigned h = g.hd == 0 ? v.x : g.hd == 1 ? v.y : g.hd == 2 ? v.z : v.w;
             bstore16<CPS>(r, t == g.tt ? g.rb - 2u : g.rb, h);
         }
@@ -622,6 +633,18 @@ struct VecRow {
         return EXACT ? c : (c < Ci ? c : Ci - 1);
     }
     __device__ static __forceinline__ bool valid(int i, int t, int Ci) { return EXACT || i * LANES + t < Ci; }
+    // Uniform slot classes of a row of Ci chunks (chunk-exact rows: every slot full). A full
+    // slot holds a chunk of the row on every lane, a live one on some lane.
+    __device__ static __forceinline__ bool full_slot(int i, int Ci) { return EXACT || (i + 1) * LANES <= Ci; }
+    __device__ static __forceinline__ bool live_slot(int i, int Ci) { return EXACT || i * LANES < Ci; }
+    // RAG: slot i holds the row's partial last chunk. In chunk-exact rows that chunk is the last
+    // slot's, so the test is a constant false for the other slots.
+    __device__ static __forceinline__ bool tail_slot(int i, const Rag& g) {
+        if constexpr (!RAG)
+            return false;
+        else
+            return (!EXACT || i == V - 1) && i == g.ti;
+    }
 
     // a1: issue every load of the row (and of the residual). Row strides are in chunks.
     __device__ static __forceinline__ void load_row(const Params& p, int64_t row, int t, int Ci, u32x4 (&xv)[V],
@@ -681,14 +704,14 @@ struct VecRow {
         auto xin = [&](int i) {
             u32x4 v = xv[i];
             if constexpr (RAG) {
-                if (i == g.ti && g.hd >= 0 && t == g.tt) v = with_half(v, xt.x, g);
+                if (tail_slot(i, g) && g.hd >= 0 && t == g.tt) v = with_half(v, xt.x, g);
             }
             return v;
         };
         auto rin = [&](int i) {
             u32x4 v = rv[OT::RES ? i : 0];
             if constexpr (RAG) {
-                if (i == g.ti && g.hd >= 0 && t == g.tt) v = with_half(v, rt.x, g);
+                if (tail_slot(i, g) && g.hd >= 0 && t == g.tt) v = with_half(v, rt.x, g);
             }
             return v;
         };
@@ -697,7 +720,7 @@ struct VecRow {
         // to a sum of (f - fill) terms; the other slots are left alone
         auto fill_tail = [&](int i, float(&f)[E], float fill) {
             if constexpr (RAG) {
-                if (i == g.ti) {
+                if (tail_slot(i, g)) {
                     const bool me = t == g.tt;
 #pragma unroll
                     for (int e = 0; e < E; ++e) f[e] = (me && e >= g.te) ? fill : f[e];
@@ -707,10 +730,13 @@ struct VecRow {
         // element e of slot i is part of the row
         auto ok = [&](int i, int e) {
             if constexpr (RAG)
-                return valid(i, t, Ci) && !(i == g.ti && t == g.tt && e >= g.te);
+                return valid(i, t, Ci) && !(tail_slot(i, g) && t == g.tt && e >= g.te);
             else
                 return valid(i, t, Ci);
         };
+        // Slot i needs no per-element mask (a uniform branch): every lane holds a whole chunk
+        // of the row there (fp32: the partial chunk's missing elements are filled instead).
+        auto plain = [&](int i) { return full_slot(i, Ci) && (DT == DT_F32 || !tail_slot(i, g)); };
         // Chunk i as the kernel sees it: the input, or for the fused ops the rounded sum.
         u32x4 src[V];
         if constexpr (OT::RES) {
@@ -719,6 +745,10 @@ struct VecRow {
             char* rob = static_cast<char*>(p.residual_out) + row * p.ldro * SB;
 #pragma unroll
             for (int i = 0; i < V; ++i) {
+                if (!live_slot(i, Ci)) {  // (uniform) no lane holds a chunk of the row here
+                    src[i] = u32x4{0u, 0u, 0u, 0u};
+                    continue;
+                }
                 float a[E], b[E];
                 IO::unpack(xin(i), a);
                 IO::unpack(rin(i), b);
@@ -737,7 +767,7 @@ struct VecRow {
         if constexpr (!EXACT && !OT::SM) {
 #pragma unroll
             for (int i = 0; i < V; ++i)
-                if (!valid(i, t, Ci)) src[i] = u32x4{0u, 0u, 0u, 0u};  // idle lanes contribute zeros
+                if (!full_slot(i, Ci) && !valid(i, t, Ci)) src[i] = u32x4{0u, 0u, 0u, 0u};  // idle lanes: zeros
         }
         float n_w;  // elements held by this wave
         if constexpr (W == 1) {
@@ -780,8 +810,14 @@ struct VecRow {
                     float f[E];
                     IO::unpack(src[i], f);
                     fill_tail(i, f, K);
+                    if (plain(i)) {
 #pragma unroll
-                    for (int e = 0; e < E; ++e) s1 += valid(i, t, Ci) ? f[e] - K : 0.f;
+                        for (int e = 0; e < E; ++e) s1 += f[e] - K;
+                    } else {
+                        const bool vl = valid(i, t, Ci);
+#pragma unroll
+                        for (int e = 0; e < E; ++e) s1 += vl ? f[e] - K : 0.f;
+                    }
                 }
             } else {
 #pragma unroll
@@ -796,12 +832,22 @@ struct VecRow {
                 float f[E];
                 IO::unpack(src[i], f);
                 if constexpr (DT == DT_F32) fill_tail(i, f, a);  // (16-bit rows: fewer VGPRs masked)
+                if (plain(i)) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float d = (DT == DT_F32 ? valid(i, t, Ci) : ok(i, e)) ? f[e] - a : 0.f;
-                    if constexpr (!NOFLOAT) v[i][e] = d;
-                    c += d;
-                    q = fmaf(d, d, q);
+                    for (int e = 0; e < E; ++e) {
+                        const float d = f[e] - a;
+                        if constexpr (!NOFLOAT) v[i][e] = d;
+                        c += d;
+                        q = fmaf(d, d, q);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const float d = (DT == DT_F32 ? valid(i, t, Ci) : ok(i, e)) ? f[e] - a : 0.f;
+                        if constexpr (!NOFLOAT) v[i][e] = d;
+                        c += d;
+                        q = fmaf(d, d, q);
+                    }
                 }
             }
             a_keep = a;
@@ -823,8 +869,13 @@ struct VecRow {
             for (int i = 0; i < V; ++i) {
                 float f[E];
                 IO::unpack(src[i], f);
+                if (full_slot(i, Ci) && !tail_slot(i, g)) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) mx = ok(i, e) ? max_nan(mx, f[e]) : mx;
+                    for (int e = 0; e < E; ++e) mx = max_nan(mx, f[e]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) mx = ok(i, e) ? max_nan(mx, f[e]) : mx;
+                }
             }
             const float mw = wave_max(mx);
             // exp(x - m_w): x - m_w is exact for the elements near the maximum.
@@ -833,11 +884,20 @@ struct VecRow {
             for (int i = 0; i < V; ++i) {
                 float f[E];
                 IO::unpack(src[i], f);
+                if (full_slot(i, Ci) && !tail_slot(i, g)) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float ex = ok(i, e) ? exp_neg(f[e] - mw) : 0.f;
-                    v[i][e] = ex;
-                    s += ex;
+                    for (int e = 0; e < E; ++e) {
+                        const float ex = exp_neg(f[e] - mw);
+                        v[i][e] = ex;
+                        s += ex;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const float ex = ok(i, e) ? exp_neg(f[e] - mw) : 0.f;
+                        v[i][e] = ex;
+                        s += ex;
+                    }
                 }
             }
             float M, S;
@@ -874,6 +934,7 @@ struct VecRow {
         char* yb = static_cast<char*>(p.y) + row * p.ldy * SB;
 #pragma unroll
         for (int i = 0; i < V; ++i) {
+            if (!live_slot(i, Ci)) continue;  // (uniform) nothing of the row to store here
             float gm[E], b[E], o[E];
             float w[E];  // NOFLOAT: x - a of this chunk
             if constexpr (NOFLOAT) {
