@@ -706,6 +706,13 @@ def plan_sweep_shapes():
         (workloads.C3.scaled(rows=4096, N=14336, dtype="bf16", name="rms_bf16_4096x14336"),
          "width 14336: 1792 chunks = 64 x 4 x 7"),
         (c5.scaled(rows=16384, N=2560, name="ln_bf16_16384x2560"), "hidden size 2560: 320 chunks = 64 x 5"),
+        # rows of 16 waves (64 KiB): 1024-lane workgroups, looping (no second row in registers)
+        (workloads.C3.scaled(rows=4096, N=16384, dtype="fp32", name="rms_fp32_4096x16384"),
+         "16-wave fp32 RMSNorm rows, persistent"),
+        (workloads.C1.scaled(rows=4096, N=16384, name="ln_fp32_4096x16384"), "16-wave fp32 LayerNorm rows, "
+                                                                             "persistent"),
+        (sm.scaled(rows=4096, N=32768, dtype="bf16", name="softmax_bf16_4096x32768"), "16-wave bf16 softmax "
+                                                                                       "rows, persistent"),
         (workloads.C4_FP16, "persistent threshold: fused add + RMSNorm fp16 256 rows"),
         (fln.scaled(rows=384, name="fused_ln_bf16_384x4096"), "persistent threshold: fused add + LayerNorm "
                                                               "384 rows"),

@@ -238,11 +238,14 @@ def _call(op: str, what: str, x, residual, gamma, beta, y, ro, mean, rstd, rows,
     v = _variant(variant)
     ws_bytes = 0
     nb = N * _ELEM_BYTES[x.dtype]
-    # only rows beyond a workgroup's registers use a workspace (rows of whole 16-byte chunks
-    # up to 64 KiB, and any rows up to 16384 elements, never do)
-    if N > 16384 and (nb > 65536 or nb % 16 != 0):
-        need = forward_workspace_bytes(op, rows, N, x.dtype)
-        if need and workspace is None and v in (VARIANTS["auto"], VARIANTS["wide"], VARIANTS["wide_element"]):
+    # only split rows use a workspace: the automatic plan splits rows beyond a workgroup's
+    # registers (rows of whole 16-byte chunks up to 64 KiB, and any rows up to 16384
+    # elements, never split), a forced split-row variant any rows of more than 16384 elements
+    if N > 16384 and workspace is None:
+        split = v in (VARIANTS["wide"], VARIANTS["wide_element"]) or (
+            v == VARIANTS["auto"] and (nb > 65536 or nb % 16 != 0))
+        need = forward_workspace_bytes(op, rows, N, x.dtype) if split else 0
+        if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     if workspace is not None:
         ws_bytes = workspace.numel() * workspace.element_size()

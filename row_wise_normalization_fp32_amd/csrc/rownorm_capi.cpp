@@ -303,7 +303,6 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
         // against 81.2, softmax bf16 8192 x 8191 53.3 against 78.5).
         if (odd2 && ((fused && wr >= 4) || (a.op == RN_OP_RMS_NORM && wr >= 8))) ragged = false;
     }
-    if (tune && ragged) return RN_ERR_UNSUPPORTED;  // a tuning applies to whole-chunk rows only
     // Long ragged rows (beyond what the element kernels hold) with a workspace of the one-pass
     // layout, out of place, in at most kWideOnePassMaxSeg segments: the one-pass split rows with
     // byte-addressed segments (x read once) instead of the element-granular two launches (x read
@@ -502,7 +501,9 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
                        (plan->variant == rn::V_ELEMENT && blocks >= rn::kPersistentBlocks);
     if (tune) {
         const rn_tuning& t = *a.tune;
-        if (t.persistent == 1 && !(plan->exact && C <= group_cap)) return RN_ERR_UNSUPPORTED;
+        // (byte-addressed rows: persistent launches only, built with 4 chunks per lane, and 1 or
+        // 2 on one wave; the launch resolves which)
+        if (t.persistent == 1 && !((plan->exact || plan->ragged) && C <= group_cap)) return RN_ERR_UNSUPPORTED;
         if (t.persistent >= 0) plan->persistent = t.persistent == 1;
         if (t.prefetch >= 0 && !plan->persistent) return RN_ERR_UNSUPPORTED;
         plan->prefetch = t.prefetch;

@@ -2532,11 +2532,15 @@ inline hipError_t go_persistent(const Plan& plan, const Params& p, hipStream_t s
 // 171.9 us, looping on 512 182.2 us; fused add + RMSNorm fp16 16384 x 8192 174.5 against
 // 182.8 us; fused add + LayerNorm bf16 4096 x 16384 (8 waves) looping one per block 90.7 us,
 // prefetching one per block 94.5 us, looping on the resident grid 94.2 us.
+// Byte-addressed 16-bit LayerNorm rows of 1 or 2 waves keep half as many workgroups for R > 3
+// as well (their accesses at 2-byte alignment take longer, and a second row in flight per
+// workgroup covers that): LayerNorm bf16 16384 x 4095 54.3 -> 51.2 us (one per block 54.5).
 struct GridRule {
     bool two_tensors;  // fused ops: x and the residual
     bool ln16;         // LayerNorm of 16-bit rows
     bool loop_wide;    // R > 3: the looping instance on the resident grid
     bool loop_blocks;  // R > 3: the looping instance, one workgroup per block
+    bool half_many;    // R > 3: half as many workgroups, prefetching
 };
 
 // The grid of a persistent vectorized launch and its instance: *loop_out selects the looping
@@ -2557,6 +2561,8 @@ inline hipError_t persistent_grid(const Plan& plan, const GridRule& rule, int* g
         } else if (rule.loop_wide) {
             loop = true;
             grid = 0;
+        } else if (rule.half_many) {
+            grid = (blocks + 1) / 2;
         } else {
             loop = rule.loop_blocks;
         }
@@ -2593,14 +2599,29 @@ inline hipError_t go_v(const Plan& plan, const Params& p, hipStream_t s) {
         if constexpr (NOPF) {
             if (plan.prefetch == 1) return hipErrorNotSupported;
             if (plan.dry) return hipSuccess;
-            return go_persistent<rownorm_vec_kernel<DT, OP, W, V, RPB, EXACT, AFF, FL>>(plan, p, s, 0, plan.grid_force);
+            constexpr auto K = rownorm_vec_kernel<DT, OP, W, V, RPB, EXACT, AFF, FL>;
+            int64_t grid = plan.grid_force;
+            if (grid <= 0) {
+                // Up to kLoopWorkgroupsPerCu workgroups per CU, more than stay resident: each
+                // loops over fewer rows, and the hardware hands the later ones to whichever
+                // CU finishes first, which evens out the CUs' finishing times. Measured on
+                // MI355X against two looping workgroups per CU (cold cache, graph replays):
+                // RMSNorm fp32 4096 x 16384 92.7 -> 89.1 us, 4096 x 16383 (byte-addressed)
+                // 99.5 -> 95.8 us, LayerNorm fp32 4096 x 16384 91.0 -> 89.8 us, softmax bf16
+                // 4096 x 32768 115.2 -> 112.1 us.
+                int cus = 0, per_cu = 0;
+                hipError_t e = resident<K>(plan.block_threads, plan.lds_bytes, &cus, &per_cu);
+                if (e != hipSuccess) return e;
+                grid = static_cast<int64_t>(cus) * kLoopWorkgroupsPerCu;
+            }
+            return go_persistent<K>(plan, p, s, 0, grid);
         } else {
             if (plan.prefetch == 0 && !WIDE_PARAMS) return hipErrorNotSupported;
             if (plan.dry) return hipSuccess;
             constexpr auto PFK = rownorm_vec_kernel<DT, OP, W, V, RPB, EXACT, AFF, FL | FL_PREFETCH>;
             constexpr bool RES = OpTraits<OP>::RES;
             constexpr GridRule rule{RES, OP == OP_LN && DT != DT_F32, WIDE_PARAMS && !RES,
-                                    WIDE_PARAMS && RES && W >= 8};
+                                    WIDE_PARAMS && RES && W >= 8, RAG && OP == OP_LN && DT != DT_F32};
             int grid = 0;
             bool loop = false;
             hipError_t e = persistent_grid<PFK>(plan, rule, &grid, &loop);

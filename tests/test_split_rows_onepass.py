@@ -181,3 +181,29 @@ def test_many_segments_take_two_launches():
     check_y(y, ref["y"], op="ln")
     check_mean(mean, ref["mean"], ref["rstd"], w.eps)
     check_rstd(rstd, ref["rstd"])
+
+
+@pytest.mark.parametrize("op,dtype,N,variants", [("softmax", "bf16", 32768, ("wide_element",)),
+                                                  ("rms", "fp16", 32768, ("wide_element",)),
+                                                  ("ln", "bf16", 32768, ("wide_element",)),
+                                                  ("rms", "fp16", 65536, ("wide", "wide_element"))])
+def test_forced_split_rows_through_the_binding(op, dtype, N, variants):
+    # rows of whole chunks that the automatic plan holds in one workgroup (64 and 128 KiB): a
+    # forced split-row variant through the Python binding gets its workspace from the binding
+    # (16-byte segments only for rows of more than 4096 chunks)
+    base = {"softmax": workloads.SOFTMAX, "rms": workloads.C3, "ln": workloads.C5}[op]
+    w = base.scaled(rows=37, N=N, seed=2250 + N % 7, dtype=dtype)
+    inp = workloads.make_inputs(w)
+    g = {k: v.to(DEV) for k, v in inp.items()}
+    for variant in variants:
+        if op == "softmax":
+            y, mx, sm = rn.softmax_forward(g["x"], return_stats=True, variant=variant)
+            o = {"y": y, "mean": mx, "rstd": sm}
+        elif op == "rms":
+            y, r = rn.rms_norm(g["x"], g.get("weight"), w.eps, return_rstd=True, variant=variant)
+            o = {"y": y, "rstd": r}
+        else:
+            y, m, r = rn.ln_forward(g["x"], g.get("gamma"), g.get("beta"), w.eps, return_stats=True, variant=variant)
+            o = {"y": y, "mean": m, "rstd": r}
+        torch.cuda.synchronize()
+        _oracle_check(w, inp, o)

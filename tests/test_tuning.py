@@ -33,6 +33,9 @@ SHAPES = [
     workloads.C5.scaled(rows=523, N=5120, seed=1708, name="ln_bf16_523x5120"),
     workloads.FUSED_LN.scaled(rows=263, N=6144, seed=1709, name="fused_ln_bf16_263x6144"),
     workloads.C3.scaled(rows=259, N=14336, seed=1710, name="rms_fp16_259x14336"),
+    # byte-addressed rows (2 and 8 waves), launch tunings only
+    workloads.C5.scaled(rows=523, N=4095, seed=1711, name="ln_bf16_523x4095"),
+    workloads.C5.scaled(rows=263, N=16383, seed=1712, name="ln_bf16_263x16383"),
 ]
 
 TUNINGS = ([{"waves_per_row": w} for w in (1, 2, 4, 8, 16)] +

@@ -56,8 +56,8 @@ def test_invalid_tunings():
 
 
 def test_tuning_applies_to_vectorized_variants_only():
-    # ragged rows (element / pair kernels), split rows and the general kernel take no tuning
-    assert plan("ln", 8192, 4095, BF16, {"grid_blocks": 64})[0] == UNSUP
+    # few ragged rows (element / pair kernels), split rows and the general kernel take no tuning
+    assert plan("ln", 300, 4095, BF16, {"grid_blocks": 64})[0] == UNSUP
     assert plan("ln", 64, 65536, F32, {"grid_blocks": 64}, workspace_bytes=1 << 24)[0] == UNSUP
     assert plan("ln", 64, 64, F32, {"persistent": 0}, variant="general")[0] == UNSUP
     # ... but an all-automatic tuning is accepted everywhere
@@ -94,8 +94,10 @@ def test_launch_mode():
     # grid-per-row launches with fewer workgroups than row blocks loop over the rest
     st, info = plan("ln", 8192, 4096, BF16, {"persistent": 0, "grid_blocks": 100})
     assert st == OK and info["grid_blocks"] == 100
-    # non-exact rows cannot be persistent
-    assert plan("rms", 8192, 1000, F32, {"persistent": 1})[0] == UNSUP
+    # non-exact rows are persistent only as byte-addressed rows (from 256 row blocks)
+    assert plan("rms", 500, 1000, F32, {"persistent": 1})[0] == UNSUP
+    st, info = plan("rms", 8192, 1000, F32, {"persistent": 1})
+    assert st == OK and info["ragged"] and not info["exact"], info
 
 
 def test_tuned_entry_point_rejects_before_launch():
@@ -147,3 +149,24 @@ def test_odd_chunk_counts_fall_back_where_not_built():
         assert st == OK and info["chunks_per_lane"] in (1, 2, 4) and not info["exact"], (N, info)
     # a caller-chosen odd count on a grid-per-row launch is not built
     assert plan("ln", 8192, 5120, BF16, {"waves_per_row": 2, "chunks_per_lane": 5, "persistent": 0})[0] == UNSUP
+
+
+def test_byte_addressed_rows_take_launch_tunings():
+    # many ragged rows (byte-addressed, persistent): grid size and instance, and widths whose
+    # chunks per lane are built (4; 1 or 2 on one wave); never grid per row
+    auto = plan("ln", 8192, 4095, BF16, None)[1]
+    assert auto["ragged"] and auto["persistent"] and (auto["waves_per_row"], auto["chunks_per_lane"]) == (2, 4)
+    for t in ({"grid_blocks": 64}, {"prefetch": 1, "grid_blocks": 1000}, {"persistent": 1}):
+        st, info = plan("ln", 8192, 4095, BF16, t)
+        assert st == OK and info["ragged"] and info["persistent"], (t, info)
+        assert (info["waves_per_row"], info["chunks_per_lane"]) == (2, 4), (t, info)
+    st, info = plan("ln", 8192, 4095, BF16, {"grid_blocks": 64})
+    assert info["grid_blocks"] == 64
+    assert plan("ln", 8192, 4095, BF16, {"persistent": 0})[0] == UNSUP
+    assert plan("ln", 8192, 4095, BF16, {"prefetch": 0})[0] == UNSUP  # 2 waves: the prefetching instance only
+    st, info = plan("ln", 4096, 16383, BF16, {"prefetch": 0})  # 8 waves with parameters: both instances
+    assert st == OK and info["ragged"] and (info["waves_per_row"], info["chunks_per_lane"]) == (8, 4), info
+    st, info = plan("ln", 8192, 4095, BF16, {"waves_per_row": 4})  # 4 x 2 chunks: not built
+    assert st == UNSUP, info
+    st, info = plan("ln", 8192, 4095, BF16, {"waves_per_row": 1})  # 1 x 8 chunks: not built
+    assert st == UNSUP, info
