@@ -713,6 +713,10 @@ def plan_sweep_shapes():
                                                                              "persistent"),
         (sm.scaled(rows=4096, N=32768, dtype="bf16", name="softmax_bf16_4096x32768"), "16-wave bf16 softmax "
                                                                                        "rows, persistent"),
+        # vocabulary-sized softmax rows: ragged (50257) and padded to whole chunks (50304)
+        (sm.scaled(rows=1024, N=50257, name="softmax_fp32_1024x50257"), "vocabulary rows, not whole chunks"),
+        (sm.scaled(rows=1024, N=50304, name="softmax_fp32_1024x50304"), "vocabulary rows padded to whole chunks: "
+                                                                        "one 16-wave workgroup, 16 chunks per lane"),
         (workloads.C4_FP16, "persistent threshold: fused add + RMSNorm fp16 256 rows"),
         (fln.scaled(rows=384, name="fused_ln_bf16_384x4096"), "persistent threshold: fused add + LayerNorm "
                                                               "384 rows"),
@@ -1065,7 +1069,7 @@ def _more():
          "LayerNorm, fp32 I/O, 1024 x 65536 (rows beyond a workgroup's registers: one-pass split rows, the "
          "segments of a row exchanging their statistics through the workspace, x read once)"),
         ("softmax_vocab", workloads.SOFTMAX_VOCAB,
-         "row-wise softmax, fp32 I/O, 1024 x 50257 (vocabulary-sized rows, not whole chunks: element kernel, "
+         "row-wise softmax, fp32 I/O, 1024 x 50257 (vocabulary-sized rows, not whole chunks: byte-addressed rows, "
          "one 16-wave workgroup per row)"),
         ("ln_backward_split_rows", workloads.LN_BWD.scaled(rows=1024, N=65536, name="ln_bwd_bf16_1024x65536"),
          "LayerNorm backward, bf16 I/O, 1024 x 65536 (rows beyond one workgroup: one launch in which the "

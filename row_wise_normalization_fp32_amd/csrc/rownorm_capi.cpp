@@ -311,17 +311,26 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     // LayerNorm fp32 1024 x 65537 134.2 against 160.9 us, softmax fp32 1024 x 100003 205.4
     // against 239.4 us, fused add + RMSNorm fp16 1024 x 65537 134.0 against 134.2 us; bf16
     // 1024 x 65539 (odd positions) 113.1 against 107.9 us.
+    // Softmax rows beyond 4096 chunks that are not whole chunks (vocabulary rows such as 50257
+    // elements), up to what one 16-wave workgroup holds (fp32: 16 chunks per lane, 256 KiB;
+    // 16-bit: 8, 128 KiB): byte-addressed rows on one workgroup each, grid per row, instead of
+    // the element kernel. Measured on MI355X (cold cache, graph replays): softmax fp32 1024 x
+    // 50304 (whole chunks) 90.1 us on 16 waves x 16 chunks against 97.8 us on the element
+    // kernel; the ragged 1024 x 50257 104.8 us on the element kernel.
+    const int64_t sm_big_cap = int64_t(64) * rn::kMaxGroupWaves * (s == 4 ? rn::kMaxSoftmaxChunks : rn::kMaxBigChunks);
+    const bool ragged_big = sm && !vec_ok && !ragged && a.variant == RN_VARIANT_AUTO && Cr > group_cap &&
+                            Cr <= sm_big_cap;
     const int64_t elem_cap_rows = int64_t(64) * rn::kMaxGroupWaves *
                                   (sm ? rn::kSoftmaxElemMaxPerLane : rn::kElemMaxPerLane);
     bool wide_rag = false;
-    if (!vec_ok && !ragged && !odd2 && ws_given && a.variant == RN_VARIANT_AUTO && N > elem_cap_rows) {
+    if (!vec_ok && !ragged && !ragged_big && !odd2 && ws_given && a.variant == RN_VARIANT_AUTO && N > elem_cap_rows) {
         const bool in_place = a.y == a.x || (a.residual_out != nullptr &&
                                              (a.residual_out == a.residual || a.residual_out == a.x)) ||
                               (a.residual != nullptr && a.y == a.residual);
         wide_rag = !in_place && wide_segments(Cr) <= rn::kWideOnePassMaxSeg &&
                    a.ws_bytes >= wide_onepass_bytes(rows, Cr);
     }
-    const int64_t C = vec_ok ? (N * s) / 16 : (ragged || wide_rag ? Cr : 0);
+    const int64_t C = vec_ok ? (N * s) / 16 : (ragged || ragged_big || wide_rag ? Cr : 0);
     const int64_t elem_cap = int64_t(64) * rn::kMaxGroupWaves * rn::kElemMaxPerLane;   // 16384 elements
     // Softmax keeps no parameters in registers: its element / pair kernels hold rows of up to
     // 65536 elements in one 16-wave workgroup (x read once) instead of splitting them.
@@ -353,7 +362,7 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
 
     int v = a.variant;
     if (v == RN_VARIANT_AUTO) {
-        if ((vec_ok && C <= big_cap) || ragged)
+        if ((vec_ok && C <= big_cap) || ragged || ragged_big)
             v = w_auto == 1 ? RN_VARIANT_WAVE : RN_VARIANT_WORKGROUP;
         else if ((vec_ok && ws_given) || wide_rag)
             v = RN_VARIANT_WIDE;
@@ -402,7 +411,7 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
         W = 1;
         plan->variant = rn::V_WAVE;
     } else if (v == RN_VARIANT_WORKGROUP) {
-        if (!(vec_ok || ragged) || C > big_cap) return RN_ERR_UNSUPPORTED;
+        if (!(vec_ok || ragged || ragged_big) || C > big_cap) return RN_ERR_UNSUPPORTED;
         W = w_auto < 2 ? 2 : w_auto;
         plan->variant = rn::V_WORKGROUP;
     } else if (v == RN_VARIANT_ELEMENT) {
@@ -486,7 +495,7 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
     plan->grid = blocks < rn::kMaxGrid ? blocks : rn::kMaxGrid;
     const bool vec = plan->variant == rn::V_WAVE || plan->variant == rn::V_WORKGROUP;
     plan->exact = vec && C == int64_t(64) * W * plan->chunks_per_lane;
-    plan->ragged = ragged;
+    plan->ragged = ragged || ragged_big;
     // Persistent launch: for exact shapes with enough rows that workgroups would otherwise
     // be launched many times over, and for the element / pair kernels with many rows.
     // Measured on MI355X (cold cache): vectorized launches gain from 256 workgroups up

@@ -2637,7 +2637,7 @@ inline hipError_t go_v(const Plan& plan, const Params& p, hipStream_t s) {
     } else {
         if (plan.dry) return hipSuccess;
         // 1024-lane workgroups have 128 VGPRs per lane: LayerNorm rows there keep no fp32 copy.
-        constexpr int FL = W >= 16 && OpTraits<OP>::LN ? FL_NOFLOAT : 0;
+        constexpr int FL = (W >= 16 && OpTraits<OP>::LN ? FL_NOFLOAT : 0) | (RAG ? FL_RAGGED : 0);
         return go(rownorm_vec_kernel<DT, OP, W, V, RPB, EXACT, AFF, FL>, plan, p, s);
     }
 }
@@ -2647,9 +2647,18 @@ inline hipError_t launch_v(const Plan& plan, const Params& p, hipStream_t s) {
     constexpr int RPB = rows_per_block_for(W);
     if (plan.rows_per_block != RPB) return hipErrorInvalidValue;
 #define RN_GO(VV) go_v<DT, OP, W, VV, EXACT, AFF, PERS, RAG>(plan, p, s)
-    // Ragged rows (persistent only): the planner's shapes, about 4 chunks per lane (fewer
-    // only for one-wave rows).
-    if constexpr (RAG) {
+    // Ragged rows: persistent, the planner's shapes, about 4 chunks per lane (fewer only for
+    // one-wave rows); grid per row, softmax rows of more than 4096 chunks on one 16-wave
+    // workgroup (8 chunks per lane, fp32 up to 16).
+    if constexpr (RAG && !PERS) {
+        if constexpr (W == 16 && OP == OP_SOFTMAX) {
+            if (plan.chunks_per_lane == 8) return RN_GO(8);
+            if constexpr (DT == DT_F32) {
+                if (plan.chunks_per_lane == 16) return RN_GO(16);
+            }
+        }
+        return hipErrorNotSupported;
+    } else if constexpr (RAG) {
         if (plan.chunks_per_lane == 4) return RN_GO(4);
         if constexpr (W == 1) {
             switch (plan.chunks_per_lane) {
@@ -2723,7 +2732,14 @@ inline hipError_t launch_e(const Plan& plan, const Params& p, hipStream_t s) {
         if (!plan.exact) return hipErrorNotSupported;
         return launch_w<DT, OP, true, AFF, true>(plan, p, s);
     } else {
-        if (plan.ragged) return hipErrorNotSupported;
+        // grid per row: byte-addressed softmax rows of more than 4096 chunks (the instance
+        // that is not chunk-exact serves every such row)
+        if (plan.ragged) {
+            if constexpr (OP == OP_SOFTMAX)
+                return launch_w<DT, OP, false, AFF, false, true>(plan, p, s);
+            else
+                return hipErrorNotSupported;
+        }
         return plan.exact ? launch_w<DT, OP, true, AFF, false>(plan, p, s)
                           : launch_w<DT, OP, false, AFF, false>(plan, p, s);
     }

@@ -222,12 +222,22 @@ def test_plan_element_pairs():
 def test_plan_long_softmax_rows_stay_in_one_workgroup():
     f32, bf = torch.float32, torch.bfloat16
     ws = 1 << 24
-    st, info = rn.plan("softmax", 8, 50257, f32, workspace_bytes=ws)
+    # byte-addressed rows on one 16-wave workgroup, grid per row (fp32: 16 chunks per lane, up
+    # to 16384 chunks; 16-bit: 8, up to 8192)
+    for dt, V in ((f32, 16), (bf, 8)):
+        st, info = rn.plan("softmax", 8, 50257, dt, workspace_bytes=ws)
+        assert st == OK and info["variant"] == "workgroup" and info["ragged"] and not info["persistent"], info
+        assert (info["waves_per_row"], info["chunks_per_lane"]) == (16, V), info
+    st, info = rn.plan("softmax", 8, 16385, f32)  # 4097 chunks: 8 per lane
+    assert st == OK and info["ragged"] and (info["waves_per_row"], info["chunks_per_lane"]) == (16, 8), info
+    # the element kernel when forced
+    st, info = rn.plan("softmax", 8, 50257, f32, variant="element")
     assert st == OK and info["variant"] == "element" and info["waves_per_row"] == 16 and info["chunks_per_lane"] == 64
-    st, info = rn.plan("softmax", 8, 50257, bf, workspace_bytes=ws)
+    st, info = rn.plan("softmax", 8, 50257, bf, variant="element")
     assert st == OK and info["variant"] == "element" and info["pairs"] and info["chunks_per_lane"] == 32
     # up to 65536 elements; the other ops split such rows
-    assert rn.plan("softmax", 8, 65536, f32, ptrs={"x": (1 << 40) + 4}, workspace_bytes=ws)[1]["variant"] == "element"
+    st, info = rn.plan("softmax", 8, 65536, f32, ptrs={"x": (1 << 40) + 4}, workspace_bytes=ws)
+    assert info["variant"] == "workgroup" and info["ragged"] and info["chunks_per_lane"] == 16, info
     assert rn.plan("softmax", 8, 65537, f32, workspace_bytes=ws)[1]["variant"] == "wide"  # byte-addressed one pass
     assert rn.plan("rms", 8, 50257, f32, workspace_bytes=ws)[1]["variant"] == "wide"
     assert rn.plan("softmax", 8, 65537, f32, variant="element")[0] == UNSUP

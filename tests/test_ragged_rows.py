@@ -196,3 +196,20 @@ def test_few_ragged_rows_keep_the_element_kernels():
     for op, dtype, rows, N in (("ln", "bf16", 300, 4095), ("rms", "fp32", 200, 4095), ("softmax", "fp16", 1000, 999)):
         info = run_case(op, dtype, rows, N, seed=2000 + rows)
         assert info["variant"] == "element" and not info["ragged"], info
+
+
+@pytest.mark.parametrize("dtype,rows,N,V,off,in_place", [
+    ("fp32", 300, 50257, 16, None, False),   # vocabulary rows: 12565 chunks, the last 1 of 4
+    ("bf16", 200, 40001, 8, None, False),    # 5001 chunks, the last 1 of 8 (an odd length)
+    ("fp16", 64, 65535, 8, None, False),     # 8192 chunks, the last 7 of 8
+    ("fp32", 7, 16385, 8, None, False),      # 4097 chunks, few rows
+    ("fp32", 9, 65535, 16, None, False),     # 16384 chunks, the last 3 of 4
+    ("fp32", 100, 50304, 16, {"x": 1, "y": 3}, False),  # whole chunks at element-aligned addresses
+    ("bf16", 50, 50257, 8, {"x": 1}, True),  # in place, rows at odd 2-byte positions
+])
+def test_vocabulary_softmax_rows(dtype, rows, N, V, off, in_place):
+    # softmax rows of more than 4096 chunks that are not whole chunks: byte-addressed rows on
+    # one 16-wave workgroup each, grid per row
+    info = run_case("softmax", dtype, rows, N, seed=2300 + N % 101, off=off, in_place=in_place)
+    assert info["ragged"] and not info["persistent"], info
+    assert (info["waves_per_row"], info["chunks_per_lane"]) == (16, V), info
