@@ -115,7 +115,7 @@ def test_new_ops_full_size(w):
 
 
 @pytest.mark.parametrize("w,variant", [(workloads.LN_RAGGED, "workgroup"), (workloads.LN_SPLIT, "wide"),
-                                       (workloads.SOFTMAX_VOCAB, "element")], ids=lambda v: getattr(v, "name", v))
+                                       (workloads.SOFTMAX_VOCAB, "workgroup")], ids=lambda v: getattr(v, "name", v))
 def test_general_shapes_full_size(w, variant):
     # the benchmark's general-shape workloads at full size, in the launch configuration it
     # times (automatic choice; the binding supplies the split-row workspace)
@@ -211,11 +211,16 @@ def test_split_rows_element(op, dtype):
     # rows of more than 16384 elements that are not whole 16-byte chunks (a vocabulary-sized
     # softmax, 50257): by default byte-addressed one-pass segments; forced, statistics per
     # 8192-element segment, then the same fixed-order combine (softmax rows of up to 65536
-    # elements stay in one workgroup: the element / pair kernels)
+    # elements stay in one workgroup: byte-addressed 16-wave rows beyond 4096 chunks, else the
+    # element / pair kernels)
     for rows, N in ELEM_WIDE_SHAPES[dtype]:
         st, info = rn.plan(op, rows, N, TD[dtype], workspace_bytes=rn.forward_workspace_bytes(op, rows, N, TD[dtype]))
         # (these 16-bit rows have odd lengths: at odd 2-byte positions, element segments)
-        expect = "element" if op == "softmax" and N <= 65536 else ("wide" if dtype == "fp32" else "wide_element")
+        chunks = -(-N * (4 if dtype == "fp32" else 2) // 16)
+        if op == "softmax" and N <= 65536:
+            expect = "workgroup" if chunks > 4096 else "element"
+        else:
+            expect = "wide" if dtype == "fp32" else "wide_element"
         assert st == 0 and info["variant"] == expect, info
         check_case(BASES[op].scaled(rows=rows, N=N, seed=660 + N, dtype=dtype))
         if expect == "wide":
@@ -227,13 +232,26 @@ def test_split_rows_element(op, dtype):
 @pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp16"])
 def test_softmax_long_rows_one_workgroup(dtype):
     # softmax rows of 16385-65536 elements that are not whole chunks (or unaligned): one
-    # 16-wave workgroup per row holding up to 64 elements (32 pairs) per lane
+    # 16-wave workgroup per row, byte-addressed 16-byte chunks beyond 4096 chunks (8 per lane,
+    # fp32 up to 16), else the element / pair kernels; forced, the element / pair kernels
+    # holding up to 64 elements (32 pairs) per lane
     for rows, N, v in [(3, 16385, 32), (2, 32768 + 7, 64), (2, 50257, 64), (2, 65535, 64)]:
         td = TD[dtype]
+        esz = 4 if dtype == "fp32" else 2
+        chunks = -(-N * esz // 16)
         st, info = rn.plan("softmax", rows, N, td, workspace_bytes=rn.forward_workspace_bytes("softmax", rows, N, td))
+        assert st == 0 and info["waves_per_row"] == 16, info
+        if chunks > 4096:
+            assert info["variant"] == "workgroup" and info["ragged"], info
+            assert info["chunks_per_lane"] == (8 if chunks <= 8192 else 16), info
+        else:
+            assert info["variant"] == "element", info
+        w = workloads.SOFTMAX.scaled(rows=rows, N=N, seed=690 + N, dtype=dtype)
+        check_case(w)
+        st, info = rn.plan("softmax", rows, N, td, variant="element")
         assert st == 0 and info["variant"] == "element" and info["waves_per_row"] == 16, info
         assert info["chunks_per_lane"] == (v if dtype == "fp32" else v // 2) and info["pairs"] == (dtype != "fp32")
-        check_case(workloads.SOFTMAX.scaled(rows=rows, N=N, seed=690 + N, dtype=dtype))
+        check_case(w, "element")
     # large logits (spread +-160) on the longest rows
     check_case(workloads.SOFTMAX.scaled(rows=2, N=65535, seed=699, dtype="fp32", x_scale=80.0))
     if dtype == "fp32":
