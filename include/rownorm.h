@@ -64,7 +64,9 @@
  *     words, and the last element of an odd-length 16-bit row by one 2-byte access; rows of
  *     whole chunks that do not fill their group of wavefronts exactly take it too (16-bit
  *     rows at odd 2-byte positions of the fused ops from 4 wavefronts per row and of
- *     RMSNorm from 8 keep the element / pair kernels, which measure faster there).
+ *     RMSNorm from 8 keep the element / pair kernels, which measure faster there). Softmax
+ *     rows of such kinds beyond 64 KiB, up to 256 KiB fp32 / 128 KiB 16-bit, are addressed
+ *     by byte on one 16-wavefront workgroup per row, any number of rows.
  *     Otherwise rows of up to 16384 elements are held in registers one element per slot
  *     (the element kernel, still one read of x; 16-bit rows whose tensors share their
  *     position within 4-byte words move as element pairs). Longer rows take the split-row
