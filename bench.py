@@ -8,9 +8,9 @@ The same measurement is also taken for fused residual-add + RMSNorm at 8192 x 40
 "more", for fused residual-add + LayerNorm (8192 x 4096 bf16), softmax (8192 x 4096 fp32),
 the LayerNorm backward (4096 x 16384 bf16: dx, dgamma, dbeta), the RMSNorm backward
 (8192 x 4096 fp16: dx, dweight), ragged LayerNorm rows (16384 x 4095 bf16), split rows
-(LayerNorm 1024 x 65536 fp32), a vocabulary-sized softmax (1024 x 50257 fp32, element
-kernel) and the split-row LayerNorm backward (1024 x 65536 bf16); under "scale_up_sweep", fused add + RMSNorm at
-N = 4096 over 2048 / 8192 / 32768 rows (fp16 and bf16), LayerNorm bf16 2048 x 4096, and the
+(LayerNorm 1024 x 65536 fp32), a vocabulary-sized softmax (1024 x 50257 fp32, byte-addressed
+rows) and the split-row LayerNorm backward (1024 x 65536 bf16); under "scale_up_sweep", fused add + RMSNorm at
+N = 4096 over 2048 / 8192 / 32768 rows (fp16 and bf16), LayerNorm bf16 at N = 4096 over 2048 / 4096 / 8192 rows, and the
 headline workload with a hot cache; under "configs", every listed configuration (cold and
 hot, events and graph replay, next to the oracle's host throughput). Small launches (tens of microseconds) are shorter than
 the Python binding's per-call host time, so the sweep also replays its launches from a HIP
@@ -606,6 +606,8 @@ def plan_sweep_shapes():
         (c5.scaled(rows=16384, N=8192, name="ln_bf16_16384x8192"), "4-wave rows with parameters, many rows: "
                                                                    "the looping instance"),
         (ln4k(2048), "2-wave rows, few rows per resident workgroup: one workgroup per row block"),
+        (ln4k(4096), "2-wave rows, 16M elements"),
+        (ln4k(8192), "2-wave rows, 32M elements"),
         (ln4k(16384), "2-wave rows, 1 to 3 row blocks per resident workgroup: half as many workgroups, "
                       "prefetching"),
         (ln4k(32768), "2-wave rows, more than 3 row blocks per resident workgroup: one workgroup per row "
@@ -941,8 +943,8 @@ def bench_workloads():
     ws = [workloads.C5, workloads.FUSED_8192] + [x for _, x, _ in _more()] + list(workloads.CONFIGS)
     ws += [workloads.C4_FP16.scaled(rows=r, name=f"fused_fp16_{r}x4096") for r in (2048, 8192, 32768)]
     ws += [workloads.C4_BF16.scaled(rows=r, name=f"fused_bf16_{r}x4096") for r in (2048, 8192, 32768)]
-    ws += [workloads.C5.scaled(rows=2048, N=4096, name="ln_bf16_2048x4096"),
-           workloads.C5.scaled(name="ln_bf16_4096x16384_hot")]
+    ws += [workloads.C5.scaled(rows=r, N=4096, name=f"ln_bf16_{r}x4096") for r in (2048, 4096, 8192)]
+    ws += [workloads.C5.scaled(name="ln_bf16_4096x16384_hot")]
     return {w.name: w for w in ws}
 
 
@@ -1256,13 +1258,14 @@ def main():
         out["configs"] = confs
     if not args.no_sweep:
         # The scale-up sweep of the 8M-element target clause (fused add + RMSNorm at N = 4096,
-        # fp16 and bf16, 2048 / 8192 / 32768 rows; LayerNorm bf16 2048 x 4096), cold cache,
-        # and the headline workload hot (one buffer set, re-launched back to back).
+        # fp16 and bf16, 2048 / 8192 / 32768 rows; LayerNorm bf16 at N = 4096, 2048 / 4096 /
+        # 8192 rows), cold cache, and the headline workload hot (one buffer set, re-launched
+        # back to back).
         sweep = {}
         cases = [(workloads.C4_FP16.scaled(rows=r, name=f"fused_fp16_{r}x4096"), "cold") for r in (2048, 8192, 32768)]
         cases += [(workloads.C4_BF16.scaled(rows=r, name=f"fused_bf16_{r}x4096"), "cold") for r in (2048, 8192, 32768)]
-        cases += [(workloads.C5.scaled(rows=2048, N=4096, name="ln_bf16_2048x4096"), "cold"),
-                  (workloads.C5.scaled(name="ln_bf16_4096x16384_hot"), "hot")]
+        cases += [(workloads.C5.scaled(rows=r, N=4096, name=f"ln_bf16_{r}x4096"), "cold") for r in (2048, 4096, 8192)]
+        cases += [(workloads.C5.scaled(name="ln_bf16_4096x16384_hot"), "hot")]
         for x, cache in cases:
             log(f"[bench] sweep {x.name} ({cache}) ...")
             rx = measure(x, min(args.steps, 100), min(args.warmup, 10), cache, dev, graph=True)
