@@ -708,6 +708,8 @@ def plan_sweep_shapes():
         (workloads.C3.scaled(rows=4096, N=14336, dtype="bf16", name="rms_bf16_4096x14336"),
          "width 14336: 1792 chunks = 64 x 4 x 7"),
         (c5.scaled(rows=16384, N=2560, name="ln_bf16_16384x2560"), "hidden size 2560: 320 chunks = 64 x 5"),
+        (c5.scaled(rows=8192, N=4608, name="ln_bf16_8192x4608"), "hidden size 4608: 576 chunks = 64 x 9 (no exact "
+                                                                  "row group: 4 waves x 4 chunks, byte-addressed)"),
         # rows of 16 waves (64 KiB): 1024-lane workgroups, looping (no second row in registers)
         (workloads.C3.scaled(rows=4096, N=16384, dtype="fp32", name="rms_fp32_4096x16384"),
          "16-wave fp32 RMSNorm rows, persistent"),

@@ -126,6 +126,7 @@ constexpr int kSoftmaxElemMaxPerLane = 64;  // softmax rows (no parameters in re
 constexpr int kSoftmaxPairMaxPerLane = 32;  // elements / 32 pairs per lane, rows up to 65536
 constexpr int kElemCuRowBytes = 32768; // element kernels, persistent: row bytes held per CU
 constexpr int kLoopWorkgroupsPerCu = 8;  // looping-only persistent launches (1024-lane workgroups): grid per CU
+constexpr int64_t kLoopCuRowBytes = 40960;  // looping persistent launches with parameters: row bytes in flight per CU
 constexpr int64_t kMaxGrid = 1 << 20;  // grid cap; kernels loop over the remaining rows
 constexpr int64_t kPersistentBlocks = 2048;  // element / pair kernels: persistent launch from this many workgroups
 constexpr int64_t kPersistentVecBlocks = 256;  // vectorized kernels: persistent launch from this many workgroups

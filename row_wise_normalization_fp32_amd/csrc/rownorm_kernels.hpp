@@ -2482,13 +2482,20 @@ inline hipError_t go_persistent(const Plan& plan, const Params& p, hipStream_t s
     // kElemCuRowBytes of row data per CU (measured on MI355X, persistent grids of 1 to 6
     // workgroups per CU: 16 waves of 2 KiB or 32 of 1 KiB are the best or within noise of
     // it; fp32 LayerNorm 8192 x 4095: 60% resident-limited -> 68%).
+    // Rows shorter than half of kLoopCuRowBytes keep more workgroups, so that a CU still has
+    // about that many row bytes in flight (measured on MI355X, cold cache, graph replays:
+    // byte-addressed LayerNorm bf16 8192 x 4608, rows of 9 KiB on 4 waves, 51.1 us on two
+    // workgroups per CU, 37.5 on four, 35.2 on six; rows of 16 KiB and more measured best on
+    // two).
     int cap = per_cu;
     if (row_bytes_per_wave > 0) {
         const int waves = kElemCuRowBytes / row_bytes_per_wave;
         const int wg = waves / (plan.block_threads / 64);
         cap = wg < 1 ? 1 : (wg < per_cu ? wg : per_cu);
     } else if (plan.chunks_per_lane >= 4 && per_cu > 2 && plan.lds_bytes > 0) {
-        cap = 2;
+        const int64_t rb = p.C * 16 * plan.rows_per_block;  // row bytes per workgroup
+        const int64_t want = rb > 0 ? kLoopCuRowBytes / rb : 2;
+        cap = want <= 2 ? 2 : (want < per_cu ? static_cast<int>(want) : per_cu);
     }
     int64_t grid = static_cast<int64_t>(cus) * cap;
     if (grid > plan.grid) grid = plan.grid;
