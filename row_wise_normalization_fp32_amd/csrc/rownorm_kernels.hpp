@@ -2686,13 +2686,16 @@ inline hipError_t launch_v(const Plan& plan, const Params& p, hipStream_t s) {
         }
     }
     if (plan.chunks_per_lane == 4) return RN_GO(4);
-    // Rows of 64 * W * o chunks, o = 3, 5, 7, held exactly (persistent launches only; rows of
-    // 16 waves: o = 3, the rest exceed 4096 chunks)
+    // Rows of 64 * W * o chunks, o = 3, 5, 7, 9, held exactly (persistent launches only; rows
+    // of 16 waves: o = 3, of 8 waves up to 7; the rest exceed 4096 chunks)
     if constexpr (PERS && EXACT) {
         if (plan.chunks_per_lane == 3) return RN_GO(3);
         if constexpr (W <= 8) {
             if (plan.chunks_per_lane == 5) return RN_GO(5);
             if (plan.chunks_per_lane == 7) return RN_GO(7);
+        }
+        if constexpr (W <= 4) {
+            if (plan.chunks_per_lane == 9) return RN_GO(9);
         }
     }
     if constexpr (W == 1) {
