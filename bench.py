@@ -708,8 +708,12 @@ def plan_sweep_shapes():
         (workloads.C3.scaled(rows=4096, N=14336, dtype="bf16", name="rms_bf16_4096x14336"),
          "width 14336: 1792 chunks = 64 x 4 x 7"),
         (c5.scaled(rows=16384, N=2560, name="ln_bf16_16384x2560"), "hidden size 2560: 320 chunks = 64 x 5"),
-        (c5.scaled(rows=8192, N=4608, name="ln_bf16_8192x4608"), "hidden size 4608: 576 chunks = 64 x 9 (no exact "
-                                                                  "row group: 4 waves x 4 chunks, byte-addressed)"),
+        (c5.scaled(rows=8192, N=4608, name="ln_bf16_8192x4608"), "hidden size 4608: 576 chunks = 64 x 9"),
+        (c5.scaled(rows=8192, N=6656, name="ln_bf16_8192x6656"), "hidden size 6656: 832 chunks = 64 x 13"),
+        (workloads.C4_BF16.scaled(rows=8192, N=5632, name="fused_bf16_8192x5632"),
+         "fused add + RMSNorm, hidden size 5632: 704 chunks = 64 x 11"),
+        (workloads.C3.scaled(rows=8192, N=7680, dtype="bf16", name="rms_bf16_8192x7680"),
+         "hidden size 7680: 960 chunks = 64 x 15"),
         # rows of 16 waves (64 KiB): 1024-lane workgroups, looping (no second row in registers)
         (workloads.C3.scaled(rows=4096, N=16384, dtype="fp32", name="rms_fp32_4096x16384"),
          "16-wave fp32 RMSNorm rows, persistent"),

@@ -55,8 +55,8 @@
  *     up to 16 wavefronts (rows of up to 64 KiB: 16384 fp32 or 32768 fp16 / bf16 elements;
  *     softmax and RMSNorm rows of up to 128 KiB, and LayerNorm and fused add + RMSNorm rows
  *     of up to 128 KiB when no workspace is given). A row group of 2^k wavefronts holds
- *     16-byte chunks per lane in a power of two, or 3, 5, 7 or 9 of them when that holds the row
- *     exactly (rows of 64 * 2^k * 3, 5, 7 or 9 chunks, at least 256 row blocks).
+ *     16-byte chunks per lane in a power of two, or an odd number from 3 to 15 when that holds
+ *     the row exactly (rows of 64 * 2^k * 3, 5, ..., 15 chunks, at least 256 row blocks).
  *     Other rows of up to 64 KiB (not whole chunks, or tensors / strides only element-
  *     aligned), when there are at least 256 row blocks, run the same vectorized kernel with
  *     rows addressed by byte: 16-byte accesses at element alignment through a buffer
@@ -280,9 +280,10 @@ typedef struct rn_tuning {
     int waves_per_row;    /* 1, 2, 4, 8 or 16 wavefronts per row (0: automatic); rows per workgroup
                              follow (4 / waves_per_row up to 4 waves, else 1) */
     int chunks_per_lane;  /* 16-byte chunks each lane holds, 64 * waves_per_row * chunks_per_lane
-                             covering the row (0: the fewest power of two that covers it, or 3, 5,
-                             7 or 9 when that many hold the row exactly and the launch can be
-                             persistent); 3, 5, 7 and 9 are built for exact persistent launches only */
+                             covering the row (0: the fewest power of two that covers it, or an
+                             odd number from 3 to 15 when that many hold the row exactly and the
+                             launch can be persistent); the odd counts are built for exact
+                             persistent launches only */
     int persistent;       /* 1: persistent launch (rows that exactly fill the row group, up to 4096
                              chunks), 0: one workgroup per row block, -1: automatic */
     int prefetch;         /* persistent launches: 1 the instance that loads a workgroup's next row
@@ -383,8 +384,8 @@ typedef struct rn_plan_info {
     int waves_per_row;     /* wavefronts cooperating on one row (split-row variant: on one segment) */
     int rows_per_block;    /* rows one workgroup processes per iteration */
     int block_threads;     /* workgroup size */
-    int chunks_per_lane;   /* 16-byte chunks (vectorized variants: 1, 2, 4, 8, 16, or 3, 5, 7, 9 for
-                              rows of 64 * waves_per_row * 3, 5, 7 or 9 chunks, persistent) or
+    int chunks_per_lane;   /* 16-byte chunks (vectorized variants: 1, 2, 4, 8, 16, or an odd number from
+                              3 to 15 for rows of 64 * waves_per_row * that many chunks, persistent) or
                               elements (element variant) each lane holds */
     int64_t grid_blocks;   /* workgroups launched (persistent launches: an upper bound; the launch
                               caps it at what the current device keeps resident) */

@@ -51,7 +51,7 @@ int next_pow2(int64_t v) {
     return p;
 }
 
-// Rows of C = 64 * 2^k * o chunks with o = 3, 5, 7 or 9 and 2^k <= kMaxGroupWaves (o * 2^k * 64 <=
+// Rows of C = 64 * 2^k * o chunks with o odd, 3 to 15, and 2^k <= kMaxGroupWaves (o * 2^k * 64 <=
 // the row-group capacity): returns o and sets *w = 2^k; otherwise 0.
 int odd_lane_chunks(int64_t C, int* w) {
     *w = 0;
@@ -62,7 +62,8 @@ int odd_lane_chunks(int64_t C, int* w) {
         m /= 2;
         k *= 2;
     }
-    if (!(m == 3 || m == 5 || m == 7 || m == 9) || int64_t(64) * k * m > int64_t(64) * rn::kMaxGroupWaves * rn::kMaxGroupChunks)
+    if (!(m == 3 || m == 5 || m == 7 || m == 9 || m == 11 || m == 13 || m == 15) ||
+        int64_t(64) * k * m > int64_t(64) * rn::kMaxGroupWaves * rn::kMaxGroupChunks)
         return 0;
     *w = k;
     return static_cast<int>(m);
@@ -270,9 +271,9 @@ int validate_and_plan(Args& a, const rn_row_strides* strides, Plan* plan, int64_
             if (rows > 1 && (lds[i] & 1)) odd2 = true;
         }
     }
-    // Whole-chunk rows of 64 x 2^k x o chunks, o = 3, 5, 7 or 9 (16-bit rows of 1536, 2560,
-    // 3072, 3584, 4608, 5120, 6144, 7168, 14336 elements; fp32 rows of 2304, 2560, 3072, 5120,
-    // 7168, ...): a row group of 2^k waves holding o chunks per lane holds them exactly, with no idle slot, where
+    // Whole-chunk rows of 64 x 2^k x o chunks, o odd from 3 to 15 (16-bit rows of 1536, 2560,
+    // 3072, 3584, 4608, 5120, 5632, 6144, 6656, 7168, 7680, 14336 elements; fp32 rows of 2304,
+    // 2560, 3072, 5120, 7168, ...): a row group of 2^k waves holding o chunks per lane holds them exactly, with no idle slot, where
     // the power-of-two row group would leave a quarter to a half of its slots idle and mask
     // every element. Persistent launches only (the instances built), many rows.
     int odd_w = 0, odd_v = 0;

@@ -2686,8 +2686,8 @@ inline hipError_t launch_v(const Plan& plan, const Params& p, hipStream_t s) {
         }
     }
     if (plan.chunks_per_lane == 4) return RN_GO(4);
-    // Rows of 64 * W * o chunks, o = 3, 5, 7, 9, held exactly (persistent launches only; rows
-    // of 16 waves: o = 3, of 8 waves up to 7; the rest exceed 4096 chunks)
+    // Rows of 64 * W * o chunks, o odd from 3 to 15, held exactly (persistent launches only;
+    // rows of 16 waves: o = 3, of 8 waves up to 7; the rest exceed 4096 chunks)
     if constexpr (PERS && EXACT) {
         if (plan.chunks_per_lane == 3) return RN_GO(3);
         if constexpr (W <= 8) {
@@ -2696,6 +2696,9 @@ inline hipError_t launch_v(const Plan& plan, const Params& p, hipStream_t s) {
         }
         if constexpr (W <= 4) {
             if (plan.chunks_per_lane == 9) return RN_GO(9);
+            if (plan.chunks_per_lane == 11) return RN_GO(11);
+            if (plan.chunks_per_lane == 13) return RN_GO(13);
+            if (plan.chunks_per_lane == 15) return RN_GO(15);
         }
     }
     if constexpr (W == 1) {

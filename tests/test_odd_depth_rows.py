@@ -1,10 +1,10 @@
-"""GPU parity of rows held exactly by row groups of 3, 5, 7 or 9 chunks per lane: whole-chunk rows
-of 64 x 2^k x o chunks (o = 3, 5, 7, 9), such as 16-bit rows of 1536, 2560, 3072, 3584, 5120,
+"""GPU parity of rows held exactly by row groups of 3 to 15 (odd) chunks per lane: whole-chunk
+rows of 64 x 2^k x o chunks (o = 3, 5, ..., 15), such as 16-bit rows of 1536, 2560, 3072, 3584, 5120,
 6144, 7168 or 14336 elements and fp32 rows of 5120 or 7168, launched persistent on a row group
 of 2^k waves with no idle slot. Every case is checked against the fp64 oracle (the bars of the
 other parity tests), the plan is checked to be that row group, and the bytes around every
 output row are checked to be left as they were. Cases cover o = 3, 5, 7 on 1, 2, 4 and 8 waves
-(o = 3 also on 16, o = 9 on 1, 2 and 4), every operation, each dtype, with and without parameters, in place, and
+(o = 3 also on 16; o = 9 to 15 on 1, 2 and 4), every operation, each dtype, with and without parameters, in place, and
 padded row strides."""
 
 import pytest
@@ -40,6 +40,12 @@ SHAPES = [
     ("fused_add_rms", "fp16", 515, 9216, 2, 9),
     ("fused_add_ln", "bf16", 259, 18432, 4, 9),
     ("rms", "fp32", 261, 9216, 4, 9),
+    ("ln", "bf16", 1025, 5632, 1, 11),
+    ("fused_add_ln", "fp16", 513, 13312, 2, 13),
+    ("rms", "bf16", 1027, 7680, 1, 15),
+    ("softmax", "fp32", 259, 15360, 4, 15),
+    ("ln", "fp32", 257, 11264, 4, 11),
+    ("fused_add_rms", "bf16", 1029, 6656, 1, 13),
 ]
 
 

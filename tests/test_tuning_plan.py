@@ -122,6 +122,8 @@ def test_tuned_entry_point_rejects_before_launch():
     ("ln", 2048, 24576, BF16, 16, 3),
     ("ln", 16384, 4608, BF16, 1, 9), ("ln", 16384, 2304, F32, 1, 9), ("rms", 8192, 9216, F16, 2, 9),
     ("fused_add_ln", 4096, 18432, BF16, 4, 9),
+    ("ln", 16384, 5632, BF16, 1, 11), ("ln", 16384, 6656, BF16, 1, 13), ("rms", 16384, 7680, F16, 1, 15),
+    ("softmax", 4096, 15360, F32, 4, 15),
 ])
 def test_rows_held_exactly_by_odd_chunk_counts(op, rows, N, dtype, W, V):
     # rows of 64 x W x V chunks, V = 3, 5, 7: W waves with V chunks per lane, exact and
@@ -145,8 +147,8 @@ def test_odd_chunk_counts_fall_back_where_not_built():
     assert plan("ln", 8192, 5120, BF16, {"waves_per_row": 2, "persistent": 0})[0] == UNSUP  # 2 x 8 not built
     st, info = plan("ln", 8192, 5120, BF16, {"waves_per_row": 1, "persistent": 0})
     assert st == OK and (info["chunks_per_lane"], info["persistent"]) == (16, False), info
-    # 11 and 13 chunks per 64 lanes: no exact odd row group
-    for N in (5632, 6656):
+    # 17 and 19 chunks per 64 lanes (and 9 at 8 waves): no exact odd row group
+    for N in (8704, 9728):
         st, info = plan("ln", 8192, N, BF16, None)
         assert st == OK and info["chunks_per_lane"] in (1, 2, 4) and not info["exact"], (N, info)
     # a caller-chosen odd count on a grid-per-row launch is not built
